@@ -1,0 +1,397 @@
+"""Plain float64 CPU oracle for DeepSeek-V4 Compressed Sparse Attention (CSA)
+and Heavily Compressed Attention (HCA).
+
+TEST INFRASTRUCTURE ONLY.  This module is the independent checker of the HIP
+path: only the tests, the smoke check and the CPU-baseline leg of the
+benchmark may import it.  It imports nothing from the GPU package and shares
+no code with it.  Every function is written for readability, not speed: plain
+NumPy float64 (one library matmul or sort per step at most), loops where the
+definition is a loop.
+
+Sources (web pages on DeepSeek-V4; cited by page title and section):
+  [P1] "DeepSeek V4 Inside: One Token Through Every Block"
+  [P2] "DeepSeek-v4 Beyond Basics: A Practical Guide to mHC, CSA, HCA, and Muon"
+  [P3] "07 The Model" (DS4 course, Phase 1 Module 1)
+  [P4] Hugging Face transformers documentation page "DeepSeek-V4"
+
+Readings taken where the pages are silent or ambiguous (each is listed in the
+design notes of the repository):
+  * overlap direction: entry i pools block i from stream a and block i-1 from
+    stream b (the only direction under which a CSA query at t < m-1 sees no
+    entry, as [P4] "Tata letak attention mask" states);
+  * softmax per channel over the available rows, biases shaped [m, D];
+  * a partial last block pools only the tokens that exist; a missing previous
+    block contributes no rows;
+  * an entry is RoPE-rotated at the position of its block's first token;
+  * RoPE base 10000, no YaRN scaling; angles in float64;
+  * RMSNorm eps 1e-6, a single gain shared by the head;
+  * the indexer applies no scale, norm or RoPE; ReLU before the head weights;
+  * mask first, then top-k; ties go to the lower entry index;
+  * selected and window rows are concatenated without de-duplication;
+  * an empty key set gives a zero output and lse equal to the sink logit;
+  * all positions are 0-based.
+
+Parity status: every function here is pinned by tests/test_oracle_pins.py
+against printed values, closed forms, invariants or library routines, except
+where a function docstring says "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "rope",
+    "sink_softmax_weights",
+    "compress",
+    "visible_count",
+    "window_positions",
+    "index_scores",
+    "select_topk",
+    "attend",
+    "csa_compress",
+    "csa_index_topk",
+    "csa_sparse_attn",
+    "hca_attn",
+]
+
+
+# ---------------------------------------------------------------------------
+# RoPE
+# ---------------------------------------------------------------------------
+def rope(x, pos, rope_dims: int, base: float = 10000.0) -> np.ndarray:
+    """Partial rotary embedding on interleaved pairs of the last ``rope_dims``
+    channels.
+
+    [P4] "Arsitektur": partial RoPE with interleaved pairs on the last
+    qk_rope_head_dim channels of every head; the same rotation with position
+    -i is applied to the rope slice of the attention output.  [P1] "What does
+    layer 0 sliding-window attention do to p?": the pair (x, y) at position i
+    becomes (x cos i - y sin i, x sin i + y cos i) for the pair whose
+    frequency is 1.  [P2] section 3.3 (quoting the paper's section 2.3.3): RoPE
+    acts on the last 64 dimensions.
+
+    Pair j (0 <= j < R/2) covers channels u = D-R+2j and u+1 and turns with
+    angle pos * base**(-2j/R), computed in float64.
+
+    x: [..., D] array; pos: scalar or array broadcastable to x.shape[:-1].
+    """
+    x = np.array(x, dtype=np.float64, copy=True)
+    if rope_dims == 0:
+        return x
+    D = x.shape[-1]
+    R = int(rope_dims)
+    assert R % 2 == 0 and 0 < R <= D
+    half = R // 2
+    j = np.arange(half, dtype=np.float64)
+    theta = np.power(float(base), -2.0 * j / R)
+    phi = np.asarray(pos, dtype=np.float64)[..., None] * theta
+    u = D - R + 2 * np.arange(half)
+    v = u + 1
+    xu = x[..., u].copy()
+    xv = x[..., v].copy()
+    c = np.cos(phi)
+    s = np.sin(phi)
+    x[..., u] = xu * c - xv * s
+    x[..., v] = xu * s + xv * c
+    return x
+
+
+# ---------------------------------------------------------------------------
+# Softmax with a per-head sink in the denominator
+# ---------------------------------------------------------------------------
+def sink_softmax_weights(z, sink: float):
+    """Weights exp(z_j) / (sum_k exp(z_k) + exp(sink)) and the left-over sink
+    mass.  [P1] "What does layer 0 sliding-window attention do to p?", eq.(27):
+    the sink logit enters the denominator only, so the key weights may sum to
+    less than one and a head can put its mass on no key at all.
+
+    The largest logit (sink included) is subtracted first; that changes no
+    value of the quotient.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    mx = max(float(z.max()) if z.size else -math.inf, float(sink))
+    e = np.exp(z - mx)
+    es = math.exp(float(sink) - mx)
+    denom = e.sum() + es
+    return e / denom, es / denom
+
+
+# ---------------------------------------------------------------------------
+# Token-level compressor (CSA: m, overlapped, two streams; HCA: m', one stream)
+# ---------------------------------------------------------------------------
+def compress(c_a, z_a, bias_a, m: int, *, c_b=None, z_b=None, bias_b=None,
+             prev_c_b=None, prev_z_b=None, gain=None, eps: float = 1e-6,
+             rope_dims: int = 0, rope_base: float = 10000.0, pos0: int = 0,
+             overlap: bool | None = None) -> np.ndarray:
+    """Compress one sequence's token streams into ceil(T/m) entries.
+
+    [P2] section 3.2.2 (eqs. 9-12): two token streams C^a, C^b with logits
+    Z^a, Z^b; every m tokens become one entry as a Hadamard (per-channel)
+    softmax-weighted sum, the softmax running over the rows drawn from both
+    Z^a and Z^b plus the learned position biases B^a, B^b.  [P1] "How does CSA
+    compress 8 tokens into 4 KV entries?" (GOTCHA): 2m weights per block,
+    normalised by a softmax, adjacent blocks overlap.  [P2] section 3.3
+    (eqs. 20-23) and [P4] "Arsitektur": HCA uses m' = 128, one stream, no
+    overlap.  [P2] section 3.3 (quoting section 2.3.3): RMSNorm on the single
+    compressed KV head, then RoPE on its last 64 channels.
+
+    Entry i (tokens m*i .. m*i+m-1 relative to ``pos0``) takes stream a from
+    block i and, when overlapped, stream b from block i-1 (for i == 0 the
+    b rows come from ``prev_*`` if given, otherwise block i has no b rows).
+    ``gain`` None means no RMSNorm; ``rope_dims`` 0 means no RoPE.  The entry
+    is rotated at absolute position pos0 + m*i.
+
+    Inputs are [T, D] (``prev_*`` [m, D]; biases [m, D]; gain [D]).
+    The pages print no pooled value of the real operator, so the pins are
+    closed forms, invariants and a library-softmax brute force on tiny inputs.
+    """
+    c_a = np.asarray(c_a, dtype=np.float64)
+    T, D = c_a.shape
+    z_a = np.zeros((T, D)) if z_a is None else np.asarray(z_a, dtype=np.float64)
+    bias_a = np.zeros((m, D)) if bias_a is None else np.asarray(bias_a, dtype=np.float64)
+    if overlap is None:
+        overlap = c_b is not None
+    if overlap:
+        c_b = np.asarray(c_b, dtype=np.float64)
+        z_b = np.asarray(z_b, dtype=np.float64)
+        bias_b = np.zeros((m, D)) if bias_b is None else np.asarray(bias_b, dtype=np.float64)
+    n_entries = -(-T // m)
+    out = np.zeros((n_entries, D))
+    for i in range(n_entries):
+        logits = []
+        values = []
+        for r in range(m):
+            tok = m * i + r
+            if tok < T:
+                logits.append(z_a[tok] + bias_a[r])
+                values.append(c_a[tok])
+        if overlap:
+            for r in range(m):
+                if i >= 1:
+                    tok = m * (i - 1) + r
+                    logits.append(z_b[tok] + bias_b[r])
+                    values.append(c_b[tok])
+                elif prev_c_b is not None:
+                    logits.append(np.asarray(prev_z_b[r], dtype=np.float64) + bias_b[r])
+                    values.append(np.asarray(prev_c_b[r], dtype=np.float64))
+        L = np.stack(logits)            # [rows, D]
+        V = np.stack(values)            # [rows, D]
+        w = np.exp(L - L.max(axis=0))   # per-channel softmax over the rows
+        w = w / w.sum(axis=0)
+        pooled = (w * V).sum(axis=0)
+        if gain is not None:
+            g = np.asarray(gain, dtype=np.float64)
+            pooled = pooled / np.sqrt(np.mean(pooled * pooled) + eps) * g
+        if rope_dims:
+            pooled = rope(pooled, pos0 + m * i, rope_dims, rope_base)
+        out[i] = pooled
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Causal visibility and the sliding window
+# ---------------------------------------------------------------------------
+def visible_count(t_pos: int, m: int, n_entries: int) -> int:
+    """Number of compressed entries a query at absolute position t may see.
+
+    [P1] "How does CSA compress 8 tokens into 4 KV entries?": an entry is
+    visible only when every token in it sits at or before the query.  [P4]
+    "Tata letak attention mask": HCA entry w becomes visible once its window
+    has closed, w < (t+1) // m; CSA queries before the first closed window
+    (t < m-1) see nothing.  Entries beyond the cache (``n_entries``) do not
+    exist.
+    """
+    return max(0, min(int(n_entries), (int(t_pos) + 1) // int(m)))
+
+
+def window_positions(t_pos: int, W: int) -> range:
+    """Absolute token positions of the uncompressed sliding-window branch for
+    a query at t: the last W tokens up to and including t.  [P2] section 3.2.2:
+    the most recent 128 uncompressed tokens; [P1] "What does layer 0
+    sliding-window attention do to p?": the window includes the query's own
+    token."""
+    return range(max(0, int(t_pos) - int(W) + 1), int(t_pos) + 1)
+
+
+# ---------------------------------------------------------------------------
+# Lightning indexer and top-k selection
+# ---------------------------------------------------------------------------
+def index_scores(q_idx, w_idx, k_idx) -> np.ndarray:
+    """Index scores of one query against every compressed indexer key.
+
+    [P2] section 3.2.2 (eq. 16): I[t,s] = sum_h w[t,h] * ReLU(q[t,h] . K[s]).
+    [P3] "The indexer: a learned retrieval mechanism": every compressed row is
+    scored against all 64 indexer query heads; each head's dot product passes
+    a ReLU and the heads are mixed by learned per-head weights.
+
+    q_idx [Hi, Di], w_idx [Hi], k_idx [N, Di] -> float64 [N].
+    """
+    q = np.asarray(q_idx, dtype=np.float64)
+    w = np.asarray(w_idx, dtype=np.float64)
+    k = np.asarray(k_idx, dtype=np.float64)
+    dots = q @ k.T                          # [Hi, N]
+    return (w[:, None] * np.maximum(dots, 0.0)).sum(axis=0)
+
+
+def select_topk(scores, n_visible: int, K: int) -> np.ndarray:
+    """Top-k selector over the visible entries 0 .. n_visible-1.
+
+    [P2] section 3.2.2 (eq. 17): keep the entries whose index score is among
+    the top k.  [P1] "How does CSA compress 8 tokens into 4 KV entries?": the
+    causal mask applies before the ranking.  [P3] "The indexer: a learned
+    retrieval mechanism": with no more rows than k, every row is kept.  [P4]
+    "Tata letak attention mask": empty slots carry the sentinel -1.
+
+    The decision is taken on the scores as given (float32 for the parity
+    rule); ties go to the lower index.  Returns int32 [K]: the chosen indices
+    in ascending order, then -1 padding.
+    """
+    s = np.asarray(scores)
+    n = int(n_visible)
+    if n <= K:
+        chosen = np.arange(n)
+    else:
+        idx = np.arange(n)
+        vals = s[:n]
+        # primary key: descending score; secondary: ascending index
+        order = np.lexsort((idx, -vals.astype(np.float64)))
+        chosen = np.sort(order[:K])
+    out = np.full(K, -1, dtype=np.int32)
+    out[: len(chosen)] = chosen
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Shared-K=V multi-query attention with a per-head sink
+# ---------------------------------------------------------------------------
+def attend(q, t_pos: int, rows, sink, scale: float, rope_dims: int,
+           rope_base: float = 10000.0):
+    """Core attention of one query token over a list of K=V rows.
+
+    [P2] section 3.2.2 (eq. 19) and [P4] "Arsitektur": the selected compressed
+    entries (concatenated with the window rows) serve as both key and value of
+    a multi-query attention with one KV head.  [P1] "What does layer 0
+    sliding-window attention do to p?": logits scaled by 1/sqrt(head_dim),
+    sink logit in the denominator (eq. 27).  [P1] "How does CSA compress 8
+    tokens into 4 KV entries?" and [P4] "Arsitektur": the rope slice of the
+    output is rotated by position -t.
+
+    q [H, D] (already RMS-normalised, not yet rotated), rows [n, D],
+    sink [H] -> (out [H, D], lse [H]) in float64.  lse includes the sink.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.float64).reshape(-1, q.shape[-1])
+    sink = np.asarray(sink, dtype=np.float64)
+    H, D = q.shape
+    if rows.shape[0] == 0:
+        return np.zeros((H, D)), sink.copy()
+    qr = rope(q, t_pos, rope_dims, rope_base)
+    z = scale * (qr @ rows.T)                       # [H, n]
+    mx = np.maximum(z.max(axis=1), sink)
+    denom = np.exp(z - mx[:, None]).sum(axis=1) + np.exp(sink - mx)
+    lse = mx + np.log(denom)
+    p = np.exp(z - lse[:, None])                    # key weights
+    o = p @ rows                                    # [H, D]
+    return rope(o, -t_pos, rope_dims, rope_base), lse
+
+
+# ---------------------------------------------------------------------------
+# Batched drivers with the same argument meaning as the library's calls
+# ---------------------------------------------------------------------------
+def csa_compress(c_a, z_a, bias_a, m, *, c_b=None, z_b=None, bias_b=None,
+                 prev_c_b=None, prev_z_b=None, gain=None, eps=1e-6,
+                 rope_dims=0, rope_base=10000.0, pos0=None, overlap=None):
+    """Batched ``compress``: streams [B, T, D], prev [B, m, D] -> [B, ceil(T/m), D]."""
+    c_a = np.asarray(c_a)
+    B = c_a.shape[0]
+    pos0 = np.zeros(B, dtype=np.int64) if pos0 is None else np.asarray(pos0)
+    outs = []
+    for b in range(B):
+        outs.append(compress(
+            c_a[b], None if z_a is None else z_a[b], bias_a, m,
+            c_b=None if c_b is None else c_b[b], z_b=None if z_b is None else z_b[b],
+            bias_b=bias_b,
+            prev_c_b=None if prev_c_b is None else prev_c_b[b],
+            prev_z_b=None if prev_z_b is None else prev_z_b[b],
+            gain=gain, eps=eps, rope_dims=rope_dims, rope_base=rope_base,
+            pos0=int(pos0[b]), overlap=overlap))
+    return np.stack(outs)
+
+
+def csa_index_topk(q_idx, w_idx, k_idx, n_entries, q_pos0, K, m, queries=None):
+    """Scores and selections for every query (or the listed (b, t) pairs).
+
+    q_idx [B, Tq, Hi, Di], w_idx [B, Tq, Hi], k_idx [B, N_cap, Di],
+    n_entries [B], q_pos0 [B].  Returns (idx int32 [B, Tq, K] with -1 where not
+    computed, scores float32 [B, Tq, N_cap] with NaN beyond the visible
+    entries).  The float64 scores are rounded to float32 before selection.
+    """
+    q_idx = np.asarray(q_idx)
+    B, Tq = q_idx.shape[:2]
+    N_cap = np.asarray(k_idx).shape[1]
+    idx = np.full((B, Tq, K), -1, dtype=np.int32)
+    scores = np.full((B, Tq, N_cap), np.nan, dtype=np.float32)
+    pairs = queries if queries is not None else [(b, t) for b in range(B) for t in range(Tq)]
+    for b, t in pairs:
+        t_pos = int(q_pos0[b]) + t
+        n_vis = visible_count(t_pos, m, int(n_entries[b]))
+        s64 = index_scores(q_idx[b, t], w_idx[b, t], k_idx[b, :n_vis])
+        s32 = s64.astype(np.float32)
+        scores[b, t, :n_vis] = s32
+        idx[b, t] = select_topk(s32, n_vis, K)
+    return idx, scores
+
+
+def _window_rows(win, win_pos0, t_pos, W):
+    r = [p - int(win_pos0) for p in window_positions(t_pos, W)]
+    if r and (r[0] < 0 or r[-1] >= win.shape[0]):
+        raise ValueError("window buffer does not cover the query's window")
+    return np.asarray(win, dtype=np.float64)[r] if r else np.zeros((0, win.shape[1]))
+
+
+def csa_sparse_attn(q, pool, idx, win, win_pos0, W, sink, q_pos0, scale,
+                    rope_dims, rope_base=10000.0, queries=None):
+    """Sparse attention over idx-selected pool rows and the window rows.
+
+    q [B, Tq, H, D], pool [B, N_cap, D], idx [B, Tq, K] (-1 = empty slot),
+    win [B, L_win, D] with win[b, r] the token at win_pos0[b] + r.
+    Returns (out [B, Tq, H, D], lse [B, Tq, H]); entries not computed are NaN.
+    """
+    q = np.asarray(q)
+    B, Tq, H, D = q.shape
+    out = np.full((B, Tq, H, D), np.nan)
+    lse = np.full((B, Tq, H), np.nan)
+    pairs = queries if queries is not None else [(b, t) for b in range(B) for t in range(Tq)]
+    for b, t in pairs:
+        t_pos = int(q_pos0[b]) + t
+        sel = [int(s) for s in idx[b, t] if s >= 0]
+        rows = np.concatenate([np.asarray(pool[b], dtype=np.float64)[sel].reshape(-1, D),
+                               _window_rows(win[b], win_pos0[b], t_pos, W)])
+        out[b, t], lse[b, t] = attend(q[b, t], t_pos, rows, sink, scale, rope_dims, rope_base)
+    return out, lse
+
+
+def hca_attn(q, pool, n_entries, m, win, win_pos0, W, sink, q_pos0, scale,
+             rope_dims, rope_base=10000.0, queries=None):
+    """Dense attention over every visible compressed entry and the window.
+
+    [P2] section 3.3 (eq. 26): no top-k selection, every heavily compressed
+    entry is attended.  [P1] "What does HCA change?": same MQA, window, RoPE
+    and sink as CSA.  Argument meaning as ``csa_sparse_attn`` with the
+    selection replaced by the entries w < visible_count(t, m, n_entries[b]).
+    """
+    q = np.asarray(q)
+    B, Tq, H, D = q.shape
+    out = np.full((B, Tq, H, D), np.nan)
+    lse = np.full((B, Tq, H), np.nan)
+    pairs = queries if queries is not None else [(b, t) for b in range(B) for t in range(Tq)]
+    for b, t in pairs:
+        t_pos = int(q_pos0[b]) + t
+        n_vis = visible_count(t_pos, m, int(n_entries[b]))
+        rows = np.concatenate([np.asarray(pool[b][:n_vis], dtype=np.float64).reshape(-1, D),
+                               _window_rows(win[b], win_pos0[b], t_pos, W)])
+        out[b, t], lse[b, t] = attend(q[b, t], t_pos, rows, sink, scale, rope_dims, rope_base)
+    return out, lse
