@@ -1,0 +1,195 @@
+/*
+ * csa.h - C ABI of the MI355X (gfx950) library for DeepSeek-V4 Compressed
+ * Sparse Attention (CSA) and Heavily Compressed Attention (HCA).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P1] "DeepSeek V4 Inside: One Token Through Every Block"
+ *   [P2] "DeepSeek-v4 Beyond Basics: A Practical Guide to mHC, CSA, HCA, and Muon"
+ *   [P3] "07 The Model" (DS4 course, Phase 1 Module 1)
+ *   [P4] Hugging Face transformers documentation "DeepSeek-V4"
+ *
+ * Conventions shared by every call
+ *   - Tensors are device memory, contiguous and row-major, 16-byte aligned,
+ *     owned by the caller.  The library never allocates, frees or
+ *     synchronises; it launches only on the given stream (a hipStream_t
+ *     passed as void*, NULL = the null stream).
+ *   - `dt` is the storage type of activations, pools and outputs
+ *     (CSA_F32 or CSA_BF16).  Small parameter vectors (biases, gains, head
+ *     weights, sinks) are always float32.  bf16 outputs are rounded once,
+ *     round-to-nearest-even, from float32 results.
+ *   - Positions are absolute, 0-based token positions (int64, device).
+ *   - Return value: CSA_OK or a negative csa_status.  Argument and shape
+ *     errors are reported before anything is launched.  CSA_ERR_HIP means a
+ *     launch failed.  Faults of running kernels surface at the caller's next
+ *     synchronisation.  Nothing is printed.
+ *   - Kernels clamp every index they read (pool index, window position) to
+ *     the buffers described by the arguments; data that violates a stated
+ *     precondition gives unspecified values, never an out-of-bounds access.
+ *   - The library is stateless and re-entrant; results are deterministic
+ *     (same inputs, same bits).
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_ARG = -1,         /* null pointer, negative size, inconsistent sizes */
+  CSA_ERR_UNSUPPORTED = -2, /* shape outside what the kernels implement      */
+  CSA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required     */
+  CSA_ERR_HIP = -4          /* a kernel launch failed                          */
+} csa_status;
+
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
+
+/* ---------------------------------------------------------------------------
+ * csa_compress - token-level compressor.
+ *
+ * [P2] section 3.2.2 (eqs. 9-12): two token streams C^a, C^b and logits Z^a,
+ * Z^b; each block of m tokens becomes one entry, a per-channel softmax over
+ * the rows of both streams (plus position biases B^a, B^b) weighting the
+ * rows.  Adjacent blocks overlap.  [P2] section 3.3 (eqs. 20-23): HCA uses one
+ * stream, m' = 128, no overlap.  [P2] section 3.3 (quoting section 2.3.3):
+ * RMSNorm on the compressed KV head and RoPE on its last 64 channels.  [P3]
+ * "The indexer: a learned retrieval mechanism" and [P2] section 3.2.2: the
+ * indexer keys are produced by the same operation on their own streams
+ * (no norm, no RoPE).  With m = 1, no overlap, RMSNorm and RoPE, the call
+ * produces the uncompressed sliding-window rows.
+ *
+ * Entry i of the call pools tokens pos0[b] + m*i .. + m-1 of stream a
+ * (c_a/z_a rows m*i .. m*i+m-1; a partial last block pools the rows that
+ * exist) and, if overlap != 0, the previous block's m rows of stream b:
+ * c_b/z_b rows m*(i-1) .. for i >= 1, prev_c_b/prev_z_b for i == 0 (when
+ * prev_c_b is NULL, entry 0 has no b rows, as at the start of a sequence).
+ * Logit of a row = z + bias[offset in block].  Then, if gain != NULL,
+ * y = y / sqrt(mean(y^2) + eps) * gain; then, if rope_dims > 0, RoPE with
+ * interleaved pairs on the last rope_dims channels at position pos0[b] + m*i
+ * (angles pos * rope_base^(-2j/rope_dims) in float64).
+ *
+ *   c_a, z_a        [B, T, D]   (z_a may be NULL: all logits zero)
+ *   c_b, z_b        [B, T, D]   required iff overlap != 0, else NULL
+ *   prev_c_b/_z_b   [B, m, D]   optional iff overlap != 0, else NULL
+ *   bias_a, bias_b  [m, D] f32  (NULL = zero)
+ *   gain            [D] f32     (NULL = no RMSNorm)
+ *   pos0            [B] int64   device; required if rope_dims > 0
+ *   out             [B, ceil(T/m), D] with batch stride out_bstride elements
+ *                   (0 = contiguous); may point into a larger pool buffer
+ * Supported: 1 <= m <= 1024, D a power of two with 8 <= D <= 1024 (bf16) or
+ * 4 <= D <= 1024 (f32), rope_dims even and <= D.
+ * ------------------------------------------------------------------------- */
+int csa_compress(int dt, int B, int T, int D, int m, int overlap,
+                 const void* c_a, const void* z_a, const void* c_b, const void* z_b,
+                 const void* prev_c_b, const void* prev_z_b,
+                 const float* bias_a, const float* bias_b,
+                 const float* gain, float eps,
+                 int rope_dims, double rope_base, const int64_t* pos0,
+                 void* out, int64_t out_bstride, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * csa_index_topk - lightning indexer scores and top-K selection.
+ *
+ * [P2] section 3.2.2 (eqs. 13-17) and [P3] "The indexer: a learned retrieval
+ * mechanism": I[t,s] = sum_h w[t,h] * ReLU(q[t,h] . K[s]); the K entries with
+ * the highest scores are kept.  [P1] "How does CSA compress 8 tokens into 4
+ * KV entries?": only causally closed entries may be chosen (mask first, then
+ * rank).  [P3] (same section): when no more than K entries are visible,
+ * all of them are kept.  [P4] "Tata letak attention mask": empty slots
+ * carry -1.
+ *
+ * Query t of sequence b sits at position q_pos0[b] + t and sees entries
+ * s < min(n_entries[b], (q_pos0[b] + t + 1) / m).  Scores are float32 (bf16
+ * products accumulated in float32); ties go to the lower entry index.
+ *
+ *   q_idx      [B, Tq, Hi, Di]     dt
+ *   w_idx      [B, Tq, Hi]         f32
+ *   k_idx      [B, N_cap, Di]      dt (compressed indexer keys)
+ *   n_entries  [B] int32 device    live entries, <= N_cap
+ *   q_pos0     [B] int64 device
+ *   idx_out    [B, Tq, K] int32    chosen entries in ascending order, then -1
+ *   score_out  [B, Tq, K] f32      score of each chosen entry, -inf on -1
+ *                                  slots (may be NULL)
+ *   all_scores [B, Tq, N_cap] f32  every score of the visible entries;
+ *                                  later columns unspecified (may be NULL)
+ *   ws         workspace of csa_index_topk_ws_bytes(B, Tq, Hi, N_cap, K)
+ * Supported: Hi <= 64, Di <= 256, 1 <= K <= 4096, N_cap <= 2^26.
+ * ------------------------------------------------------------------------- */
+int csa_index_topk(int dt, int B, int Tq, int Hi, int Di, int N_cap, int K, int m,
+                   const void* q_idx, const float* w_idx, const void* k_idx,
+                   const int32_t* n_entries, const int64_t* q_pos0,
+                   int32_t* idx_out, float* score_out, float* all_scores,
+                   void* ws, size_t ws_bytes, void* stream);
+size_t csa_index_topk_ws_bytes(int B, int Tq, int Hi, int N_cap, int K);
+
+/* ---------------------------------------------------------------------------
+ * csa_sparse_attn - shared-K=V multi-query attention with a per-head sink
+ * over the selected pool rows and the sliding-window rows.
+ *
+ * [P2] section 3.2.2 (eq. 19) and [P4] "Arsitektur": the selected entries are
+ * both key and value of a multi-query attention with one KV head; the
+ * window's uncompressed rows are concatenated with them.  [P1] "What does
+ * layer 0 sliding-window attention do to p?" (eq. 27): a per-head sink
+ * logit sits in the softmax denominator only.  [P1] "How does CSA compress 8
+ * tokens into 4 KV entries?" and [P4] "Arsitektur": the query's rope slice
+ * is rotated at its position t and the output's rope slice by -t.
+ *
+ * For query t (position q_pos0[b] + t) and head h:
+ *   rows  = pool[b, idx[b,t,j]] for every idx >= 0 (no de-duplication),
+ *           then win[b, p - win_pos0[b]] for p in [max(0, t-W+1), t] that
+ *           lie inside the window buffer;
+ *   q'    = RoPE(q[b,t,h], t);  z_j = scale * q' . row_j;
+ *   lse   = log(sum_j exp z_j + exp sink[h]);
+ *   out   = RoPE(sum_j exp(z_j - lse) row_j, -t).
+ * With no rows, out = 0 and lse = sink[h].
+ *
+ *   q       [B, Tq, H, D] dt (RMS-normalised, not rotated)
+ *   pool    [B, N_cap, D] dt;  idx [B, Tq, K] int32 (-1 = empty slot)
+ *   win     [B, L_win, D] dt;  win_pos0 [B] int64 device (NULL iff W == 0)
+ *   sink    [H] f32; q_pos0 [B] int64 device
+ *   out     [B, Tq, H, D] dt;  lse [B, Tq, H] f32 natural log (may be NULL)
+ *   ws      workspace of csa_attn_ws_bytes(B, Tq, H, D, K + W)
+ * Supported: D <= 1024, H <= 128, rope_dims even and <= D.
+ * ------------------------------------------------------------------------- */
+int csa_sparse_attn(int dt, int B, int Tq, int H, int D, int rope_dims, double rope_base,
+                    float scale, const void* q, const void* pool, int N_cap,
+                    const int32_t* idx, int K, const void* win, int L_win,
+                    const int64_t* win_pos0, int W, const float* sink,
+                    const int64_t* q_pos0, void* out, float* lse,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * hca_attn - the same attention with every visible compressed entry as a
+ * key (no indexer).
+ *
+ * [P2] section 3.3 (eqs. 24-26) and [P1] "What does HCA change?": no top-k,
+ * dense attention over the heavily compressed entries plus the window.
+ * [P4] "Tata letak attention mask": entry w is visible to t iff
+ * w < (t + 1) / m.
+ *
+ * rows = pool[b, w] for w < min(n_entries[b], (q_pos0[b] + t + 1) / m), then
+ * the window rows as in csa_sparse_attn.  Other arguments as there.
+ *   ws      workspace of csa_attn_ws_bytes(B, Tq, H, D, N_cap + W)
+ * ------------------------------------------------------------------------- */
+int hca_attn(int dt, int B, int Tq, int H, int D, int rope_dims, double rope_base,
+             float scale, const void* q, const void* pool, int N_cap,
+             const int32_t* n_entries, int m, const void* win, int L_win,
+             const int64_t* win_pos0, int W, const float* sink,
+             const int64_t* q_pos0, void* out, float* lse,
+             void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace (bytes) for csa_sparse_attn / hca_attn with at most
+ * keys_per_query rows per query (K + W, or N_cap + W). */
+size_t csa_attn_ws_bytes(int B, int Tq, int H, int D, int keys_per_query);
+
+/* Human-readable name of a csa_status value (static string). */
+const char* csa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H */

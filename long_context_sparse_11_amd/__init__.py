@@ -1,0 +1,17 @@
+"""MI355X-native DeepSeek-V4 Compressed Sparse Attention (CSA) and Heavily
+Compressed Attention (HCA).
+
+The computation lives in the HIP library ``libcsa.so`` (C ABI in
+include/csa.h); ``binding`` marshals torch tensors into it.  ``synth`` holds
+the seeded synthetic workloads.
+"""
+from .binding import (  # noqa: F401
+    CsaError,
+    csa_attn_ws_bytes,
+    csa_compress,
+    csa_index_topk,
+    csa_index_topk_ws_bytes,
+    csa_sparse_attn,
+    hca_attn,
+    lib,
+)

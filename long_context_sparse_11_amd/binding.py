@@ -1,0 +1,212 @@
+"""Thin ctypes binding of libcsa.so (declared in include/csa.h).
+
+Argument marshalling only: every step runs in the HIP library.  Tensors are
+torch tensors on the GPU (PyTorch supplies device memory and the current HIP
+stream); outputs and workspaces are allocated here with torch and handed to
+the library.  There is no fallback: if the library is missing or a call
+fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
+_lib = None
+
+CSA_F32, CSA_BF16 = 0, 1
+
+_c = ctypes
+_SIGS = {
+    "csa_compress": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                _c.c_void_p, _c.c_float, _c.c_int, _c.c_double, _c.c_void_p,
+                                _c.c_void_p, _c.c_int64, _c.c_void_p]),
+    "csa_index_topk": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                  _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                  _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                  _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "csa_index_topk_ws_bytes": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int]),
+    "csa_sparse_attn": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                   _c.c_double, _c.c_float, _c.c_void_p, _c.c_void_p, _c.c_int,
+                                   _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int, _c.c_void_p,
+                                   _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                   _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "hca_attn": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                            _c.c_double, _c.c_float, _c.c_void_p, _c.c_void_p, _c.c_int,
+                            _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int,
+                            _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                            _c.c_size_t, _c.c_void_p]),
+    "csa_attn_ws_bytes": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int]),
+    "csa_status_string": (_c.c_char_p, [_c.c_int]),
+}
+
+
+class CsaError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libcsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise CsaError(f"{_LIB_PATH} is missing; run long_context_sparse_11_amd.build.build()")
+        h = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = h
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = lib().csa_status_string(status).decode()
+        raise CsaError(f"{what} failed: {msg}")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    if t.dtype == torch.float32:
+        return CSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must live on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _f32(t):
+    if t is not None and t.dtype != torch.float32:
+        raise TypeError("parameter vectors are float32")
+    return t
+
+
+def _i64(t):
+    if t is not None and t.dtype != torch.int64:
+        raise TypeError("positions are int64")
+    return t
+
+
+# ---------------------------------------------------------------------------
+def csa_compress(c_a, m, *, z_a=None, c_b=None, z_b=None, prev_c_b=None, prev_z_b=None,
+                 bias_a=None, bias_b=None, gain=None, eps=1e-6, rope_dims=0,
+                 rope_base=10000.0, pos0=None, out=None, out_bstride=0, stream=None):
+    """Compressor (see include/csa.h).  c_a [B, T, D]; returns out [B, ceil(T/m), D]
+    (or writes the caller's ``out`` with batch stride ``out_bstride``)."""
+    B, T, D = c_a.shape
+    overlap = c_b is not None
+    _dev(c_a, z_a, c_b, z_b, prev_c_b, prev_z_b, bias_a, bias_b, gain, pos0)
+    _f32(bias_a), _f32(bias_b), _f32(gain), _i64(pos0)
+    n_out = -(-T // m)
+    if out is None:
+        out = torch.empty((B, n_out, D), dtype=c_a.dtype, device=c_a.device)
+    st = lib().csa_compress(_dt(c_a), B, T, D, m, int(overlap), _p(c_a), _p(z_a), _p(c_b), _p(z_b),
+                            _p(prev_c_b), _p(prev_z_b), _p(bias_a), _p(bias_b), _p(gain),
+                            float(eps), int(rope_dims), float(rope_base), _p(pos0), _p(out),
+                            int(out_bstride), _stream(stream))
+    _check(st, "csa_compress")
+    return out
+
+
+def csa_index_topk_ws_bytes(B, Tq, Hi, N_cap, K):
+    return int(lib().csa_index_topk_ws_bytes(B, Tq, Hi, N_cap, K))
+
+
+def csa_index_topk(q_idx, w_idx, k_idx, n_entries, q_pos0, K, m, *, want_scores=False,
+                   want_all_scores=False, ws=None, idx_out=None, stream=None):
+    """Indexer scores + top-K.  Returns (idx [B,Tq,K] int32, score_out or None,
+    all_scores or None)."""
+    B, Tq, Hi, Di = q_idx.shape
+    N_cap = k_idx.shape[1]
+    _dev(q_idx, w_idx, k_idx, n_entries, q_pos0)
+    _f32(w_idx), _i64(q_pos0)
+    if n_entries.dtype != torch.int32:
+        raise TypeError("n_entries is int32")
+    dev = q_idx.device
+    if idx_out is None:
+        idx_out = torch.empty((B, Tq, K), dtype=torch.int32, device=dev)
+    score_out = torch.empty((B, Tq, K), dtype=torch.float32, device=dev) if want_scores else None
+    all_scores = (torch.empty((B, Tq, N_cap), dtype=torch.float32, device=dev)
+                  if want_all_scores else None)
+    need = csa_index_topk_ws_bytes(B, Tq, Hi, N_cap, K)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = lib().csa_index_topk(_dt(q_idx), B, Tq, Hi, Di, N_cap, K, m, _p(q_idx), _p(w_idx),
+                              _p(k_idx), _p(n_entries), _p(q_pos0), _p(idx_out), _p(score_out),
+                              _p(all_scores), _p(ws), 0 if ws is None else ws.numel(),
+                              _stream(stream))
+    _check(st, "csa_index_topk")
+    return idx_out, score_out, all_scores
+
+
+def csa_attn_ws_bytes(B, Tq, H, D, keys_per_query):
+    return int(lib().csa_attn_ws_bytes(B, Tq, H, D, keys_per_query))
+
+
+def csa_sparse_attn(q, pool, idx, win, win_pos0, W, sink, q_pos0, *, rope_dims, rope_base=10000.0,
+                    scale=None, want_lse=False, out=None, ws=None, stream=None):
+    """Sparse attention over idx-selected pool rows + window.  Returns (out, lse)."""
+    B, Tq, H, D = q.shape
+    N_cap = pool.shape[1]
+    K = idx.shape[2]
+    L_win = 0 if win is None else win.shape[1]
+    _dev(q, pool, idx, win, win_pos0, sink, q_pos0)
+    _f32(sink), _i64(q_pos0), _i64(win_pos0)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device) if want_lse else None
+    need = csa_attn_ws_bytes(B, Tq, H, D, K + W)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib().csa_sparse_attn(_dt(q), B, Tq, H, D, int(rope_dims), float(rope_base), float(scale),
+                               _p(q), _p(pool), N_cap, _p(idx), K, _p(win), L_win, _p(win_pos0),
+                               int(W), _p(sink), _p(q_pos0), _p(out), _p(lse), _p(ws),
+                               0 if ws is None else ws.numel(), _stream(stream))
+    _check(st, "csa_sparse_attn")
+    return out, lse
+
+
+def hca_attn(q, pool, n_entries, m, win, win_pos0, W, sink, q_pos0, *, rope_dims,
+             rope_base=10000.0, scale=None, want_lse=False, out=None, ws=None, stream=None):
+    """Dense attention over every visible pool entry + window.  Returns (out, lse)."""
+    B, Tq, H, D = q.shape
+    N_cap = pool.shape[1]
+    L_win = 0 if win is None else win.shape[1]
+    _dev(q, pool, n_entries, win, win_pos0, sink, q_pos0)
+    _f32(sink), _i64(q_pos0), _i64(win_pos0)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device) if want_lse else None
+    need = csa_attn_ws_bytes(B, Tq, H, D, N_cap + W)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib().hca_attn(_dt(q), B, Tq, H, D, int(rope_dims), float(rope_base), float(scale), _p(q),
+                        _p(pool), N_cap, _p(n_entries), int(m), _p(win), L_win, _p(win_pos0),
+                        int(W), _p(sink), _p(q_pos0), _p(out), _p(lse), _p(ws),
+                        0 if ws is None else ws.numel(), _stream(stream))
+    _check(st, "hca_attn")
+    return out, lse

@@ -1,0 +1,195 @@
+// C ABI of the library (declarations and contracts in include/csa.h):
+// argument validation, workspace sizing and dispatch to the kernels.  No
+// call allocates, frees or synchronises.
+#include "../../include/csa.h"
+#include "kernels.h"
+
+#define CSA_EXPORT extern "C" __attribute__((visibility("default")))
+
+using namespace csa;
+
+namespace {
+
+inline bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline int status_of(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_ERR_HIP; }
+
+// Candidate lists of the two-level selection for rows longer than kTopkCap.
+inline int topk_chunks(int N_cap) { return N_cap > kTopkCap ? (N_cap + kTopkCap - 1) / kTopkCap : 0; }
+
+}  // namespace
+
+CSA_EXPORT const char* csa_status_string(int status) {
+  switch (status) {
+    case CSA_OK: return "CSA_OK";
+    case CSA_ERR_ARG: return "CSA_ERR_ARG: invalid argument";
+    case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED: shape not implemented";
+    case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE: workspace missing or too small";
+    case CSA_ERR_HIP: return "CSA_ERR_HIP: kernel launch failed";
+    default: return "unknown csa_status";
+  }
+}
+
+// ---------------------------------------------------------------- compressor
+CSA_EXPORT int csa_compress(int dt, int B, int T, int D, int m, int overlap, const void* c_a,
+                            const void* z_a, const void* c_b, const void* z_b,
+                            const void* prev_c_b, const void* prev_z_b, const float* bias_a,
+                            const float* bias_b, const float* gain, float eps, int rope_dims,
+                            double rope_base, const int64_t* pos0, void* out,
+                            int64_t out_bstride, void* stream) {
+  if (dt != CSA_F32 && dt != CSA_BF16) return CSA_ERR_ARG;
+  if (B < 0 || T < 0 || D <= 0 || m <= 0) return CSA_ERR_ARG;
+  if (B == 0 || T == 0) return CSA_OK;
+  if (!c_a || !out) return CSA_ERR_ARG;
+  if (overlap) {
+    if (!c_b || !z_b) return CSA_ERR_ARG;
+    if ((prev_c_b == nullptr) != (prev_z_b == nullptr)) return CSA_ERR_ARG;
+  } else if (c_b || z_b || prev_c_b || prev_z_b) {
+    return CSA_ERR_ARG;
+  }
+  if (rope_dims < 0 || rope_dims > D || (rope_dims & 1)) return CSA_ERR_ARG;
+  if (rope_dims > 0 && (!pos0 || !(rope_base > 0.0))) return CSA_ERR_ARG;
+  if (gain && !(eps >= 0.f)) return CSA_ERR_ARG;
+  const int n_out = (T + m - 1) / m;
+  if (out_bstride != 0 && out_bstride < (int64_t)n_out * D) return CSA_ERR_ARG;
+  if (m > 1024 || !is_pow2(D) || D > 1024 || D < (dt == CSA_BF16 ? 8 : 4)) return CSA_ERR_UNSUPPORTED;
+  CompressArgs a{dt, B, T, D, m, overlap ? 1 : 0, n_out, c_a, z_a, c_b, z_b, prev_c_b, prev_z_b,
+                 bias_a, bias_b, gain, eps, rope_dims, rope_base, pos0, out, out_bstride};
+  return status_of(launch_compress(a, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------- index + top-k
+CSA_EXPORT size_t csa_index_topk_ws_bytes(int B, int Tq, int Hi, int N_cap, int K) {
+  (void)Hi;
+  if (B <= 0 || Tq <= 0 || N_cap <= 0 || K <= 0) return 0;
+  const size_t q = (size_t)B * Tq;
+  size_t bytes = align256(q * N_cap * sizeof(float));
+  const int nc = topk_chunks(N_cap);
+  if (nc) bytes += 2 * align256(q * nc * K * sizeof(float));
+  return bytes;
+}
+
+CSA_EXPORT int csa_index_topk(int dt, int B, int Tq, int Hi, int Di, int N_cap, int K, int m,
+                              const void* q_idx, const float* w_idx, const void* k_idx,
+                              const int32_t* n_entries, const int64_t* q_pos0, int32_t* idx_out,
+                              float* score_out, float* all_scores, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (dt != CSA_F32 && dt != CSA_BF16) return CSA_ERR_ARG;
+  if (B < 0 || Tq < 0 || Hi <= 0 || Di <= 0 || N_cap < 0 || K <= 0 || m <= 0) return CSA_ERR_ARG;
+  if (B == 0 || Tq == 0) return CSA_OK;
+  if (!q_idx || !w_idx || !n_entries || !q_pos0 || !idx_out) return CSA_ERR_ARG;
+  if (N_cap > 0 && !k_idx) return CSA_ERR_ARG;
+  if (Hi > 64 || Di > 256 || Hi * Di > 8192 || K > 4096 || N_cap > (1 << 26))
+    return CSA_ERR_UNSUPPORTED;
+  if ((int64_t)topk_chunks(N_cap) * K > kTopkCap) return CSA_ERR_UNSUPPORTED;
+  const size_t need = csa_index_topk_ws_bytes(B, Tq, Hi, N_cap, K);
+  if (N_cap > 0 && (!ws || ws_bytes < need)) return CSA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t q = (size_t)B * Tq;
+  char* w = (char*)ws;
+  float* scores = all_scores ? all_scores : (float*)w;
+  w += align256(q * (size_t)N_cap * sizeof(float));
+
+  if (N_cap > 0) {
+    IndexArgs ia{dt, B, Tq, Hi, Di, N_cap, m, q_idx, w_idx, k_idx, n_entries, q_pos0, scores};
+    hipError_t e = launch_index_scores(ia, s);
+    if (e != hipSuccess) return CSA_ERR_HIP;
+  }
+  const int nc = topk_chunks(N_cap);
+  TopkArgs ta{};
+  ta.B = B; ta.Tq = Tq; ta.N_cap = N_cap; ta.m = m; ta.K = K;
+  ta.n_entries = n_entries; ta.q_pos0 = q_pos0;
+  if (nc == 0) {
+    ta.mode = 0;
+    ta.nchunks = 1;
+    ta.scores = scores;
+    ta.out_idx = idx_out;
+    ta.out_scores = score_out;
+    return status_of(launch_topk(ta, (int)q, s));
+  }
+  float* cand_s = (float*)w;
+  int32_t* cand_i = (int32_t*)(w + align256(q * nc * K * sizeof(float)));
+  ta.mode = 1;
+  ta.nchunks = nc;
+  ta.chunk = kTopkCap;
+  ta.scores = scores;
+  ta.out_idx = cand_i;
+  ta.out_scores = cand_s;
+  hipError_t e = launch_topk(ta, (int)(q * nc), s);
+  if (e != hipSuccess) return CSA_ERR_HIP;
+  TopkArgs tb = ta;
+  tb.mode = 2;
+  tb.scores = cand_s;
+  tb.in_idx = cand_i;
+  tb.out_idx = idx_out;
+  tb.out_scores = score_out;
+  return status_of(launch_topk(tb, (int)q, s));
+}
+
+// ------------------------------------------------------------------ attention
+CSA_EXPORT size_t csa_attn_ws_bytes(int B, int Tq, int H, int D, int keys_per_query) {
+  if (B <= 0 || Tq <= 0 || H <= 0 || D <= 0 || keys_per_query <= 0) return 0;
+  return attn_ws_bytes(CSA_BF16, B, Tq, H, D, keys_per_query);
+}
+
+namespace {
+
+int attn_common(AttnArgs& a, int keys_per_query, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (a.dt != CSA_F32 && a.dt != CSA_BF16) return CSA_ERR_ARG;
+  if (a.B < 0 || a.Tq < 0 || a.H <= 0 || a.D <= 0 || a.N_cap < 0 || a.W < 0 || a.L_win < 0)
+    return CSA_ERR_ARG;
+  if (a.B == 0 || a.Tq == 0) return CSA_OK;
+  if (!a.q || !a.sink || !a.q_pos0 || !a.out) return CSA_ERR_ARG;
+  if (a.N_cap > 0 && !a.pool) return CSA_ERR_ARG;
+  if (a.W > 0 && a.L_win > 0 && (!a.win || !a.win_pos0)) return CSA_ERR_ARG;
+  if (a.R < 0 || a.R > a.D || (a.R & 1) || (a.R > 0 && !(a.rope_base > 0.0))) return CSA_ERR_ARG;
+  if (a.D > 1024 || a.H > 128 || (a.D & 1)) return CSA_ERR_UNSUPPORTED;
+  if (attn_uses_mfma(a.dt, a.H, a.D, a.R)) {
+    a.splits = attn_splits(a.dt, a.B, a.Tq, a.H, a.D, keys_per_query);
+    if (a.splits > 1) {
+      const size_t need = attn_ws_bytes(a.dt, a.B, a.Tq, a.H, a.D, keys_per_query);
+      if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
+      a.part_o = (float*)ws;
+      a.part_ml = a.part_o + (size_t)a.B * a.Tq * a.splits * a.H * a.D;
+    }
+  } else {
+    a.splits = 1;
+  }
+  return status_of(launch_attn(a, s));
+}
+
+}  // namespace
+
+CSA_EXPORT int csa_sparse_attn(int dt, int B, int Tq, int H, int D, int rope_dims,
+                               double rope_base, float scale, const void* q, const void* pool,
+                               int N_cap, const int32_t* idx, int K, const void* win, int L_win,
+                               const int64_t* win_pos0, int W, const float* sink,
+                               const int64_t* q_pos0, void* out, float* lse, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (K < 0) return CSA_ERR_ARG;
+  if (K > 0 && !idx) return CSA_ERR_ARG;
+  AttnArgs a{};
+  a.dt = dt; a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.R = rope_dims;
+  a.rope_base = rope_base; a.scale = scale;
+  a.q = q; a.pool = pool; a.N_cap = N_cap; a.csa = 1; a.idx = idx; a.K = K;
+  a.n_entries = nullptr; a.m = 1;
+  a.win = win; a.L_win = L_win; a.win_pos0 = win_pos0; a.W = W;
+  a.sink = sink; a.q_pos0 = q_pos0; a.out = out; a.lse = lse;
+  return attn_common(a, K + W, ws, ws_bytes, (hipStream_t)stream);
+}
+
+CSA_EXPORT int hca_attn(int dt, int B, int Tq, int H, int D, int rope_dims, double rope_base,
+                        float scale, const void* q, const void* pool, int N_cap,
+                        const int32_t* n_entries, int m, const void* win, int L_win,
+                        const int64_t* win_pos0, int W, const float* sink, const int64_t* q_pos0,
+                        void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (m <= 0 || !n_entries) return CSA_ERR_ARG;
+  AttnArgs a{};
+  a.dt = dt; a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.R = rope_dims;
+  a.rope_base = rope_base; a.scale = scale;
+  a.q = q; a.pool = pool; a.N_cap = N_cap; a.csa = 0; a.idx = nullptr; a.K = 0;
+  a.n_entries = n_entries; a.m = m;
+  a.win = win; a.L_win = L_win; a.win_pos0 = win_pos0; a.W = W;
+  a.sink = sink; a.q_pos0 = q_pos0; a.out = out; a.lse = lse;
+  return attn_common(a, N_cap + W, ws, ws_bytes, (hipStream_t)stream);
+}

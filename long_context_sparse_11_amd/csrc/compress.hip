@@ -1,0 +1,182 @@
+// Token-level compressor: softmax-weighted pooling of m-token blocks (two
+// overlapped streams for CSA, one stream for HCA), then optional RMSNorm and
+// partial RoPE.  "DeepSeek-v4 Beyond Basics" section 3.2.2 (eqs. 9-12) and
+// section 3.3 (eqs. 20-23); RMSNorm/RoPE placement from the same page's
+// section 3.3 (its quote of the paper's section 2.3.3).
+//
+// One workgroup per (sequence, entry).  A row of D channels is covered by
+// L = D / VEC lanes holding VEC contiguous channels each (16-byte loads, so
+// a row is one coalesced read).  The block's rows are spread over G lane
+// groups; each group keeps a per-channel online softmax (max, denominator,
+// weighted sum) in registers, the groups are merged through LDS, and group 0
+// finishes the entry (normalise, gain, rotate, store).
+#include "kernels.h"
+
+namespace csa {
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(1024) void compress_kernel(CompressArgs a) {
+  extern __shared__ float smem[];
+  const int i = blockIdx.x;  // entry within the call
+  const int b = blockIdx.y;
+  const int D = a.D;
+  const int L = D / VEC;
+  const int G = blockDim.x / L;
+  const int tid = threadIdx.x;
+  const int g = tid / L;
+  const int lane = tid - g * L;
+  const int c0 = lane * VEC;
+  const int m = a.m;
+
+  const int64_t a_row0 = (int64_t)m * i;
+  const int na = (int)min((int64_t)m, (int64_t)a.T - a_row0);
+  const T* cb_base = nullptr;
+  const T* zb_base = nullptr;
+  int nb = 0;
+  if (a.overlap) {
+    if (i >= 1) {
+      nb = m;
+      const int64_t off = ((int64_t)b * a.T + (int64_t)m * (i - 1)) * D;
+      cb_base = (const T*)a.c_b + off;
+      zb_base = (const T*)a.z_b + off;
+    } else if (a.prev_c_b) {
+      nb = m;
+      const int64_t off = (int64_t)b * m * D;
+      cb_base = (const T*)a.prev_c_b + off;
+      zb_base = (const T*)a.prev_z_b + off;
+    }
+  }
+  const int nr = na + nb;
+
+  float mx[VEC], den[VEC], acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) { mx[e] = -INFINITY; den[e] = 0.f; acc[e] = 0.f; }
+
+  const int64_t a_off = ((int64_t)b * a.T + a_row0) * D;
+#pragma unroll 4
+  for (int r = g; r < nr; r += G) {
+    const T* cp;
+    const T* zp;
+    const float* bp;
+    if (r < na) {
+      cp = (const T*)a.c_a + a_off + (int64_t)r * D + c0;
+      zp = a.z_a ? (const T*)a.z_a + a_off + (int64_t)r * D + c0 : nullptr;
+      bp = a.bias_a ? a.bias_a + (int64_t)r * D + c0 : nullptr;
+    } else {
+      const int rr = r - na;
+      cp = cb_base + (int64_t)rr * D + c0;
+      zp = zb_base + (int64_t)rr * D + c0;
+      bp = a.bias_b ? a.bias_b + (int64_t)rr * D + c0 : nullptr;
+    }
+    float cv[VEC], lv[VEC];
+    Elem<T>::template load<VEC>(cp, cv);
+    if (zp) {
+      Elem<T>::template load<VEC>(zp, lv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) lv[e] = 0.f;
+    }
+    if (bp) {
+      float bv[VEC];
+      Elem<float>::template load<VEC>(bp, bv);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) lv[e] += bv[e];
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const float nm = fmaxf(mx[e], lv[e]);
+      const float sc = expf(mx[e] - nm);
+      const float p = expf(lv[e] - nm);
+      den[e] = den[e] * sc + p;
+      acc[e] = acc[e] * sc + p * cv[e];
+      mx[e] = nm;
+    }
+  }
+
+  // merge the G groups: LDS layout [3][G][D]
+  float* s_mx = smem;
+  float* s_den = smem + G * D;
+  float* s_acc = smem + 2 * G * D;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    s_mx[g * D + c0 + e] = mx[e];
+    s_den[g * D + c0 + e] = den[e];
+    s_acc[g * D + c0 + e] = acc[e];
+  }
+  __syncthreads();
+  if (g != 0) return;
+
+  float y[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    float M = -INFINITY;
+    for (int gg = 0; gg < G; ++gg) M = fmaxf(M, s_mx[gg * D + c0 + e]);
+    float dsum = 0.f, asum = 0.f;
+    for (int gg = 0; gg < G; ++gg) {
+      const float w = expf(s_mx[gg * D + c0 + e] - M);
+      dsum += s_den[gg * D + c0 + e] * w;
+      asum += s_acc[gg * D + c0 + e] * w;
+    }
+    y[e] = asum / dsum;
+  }
+
+  if (a.gain) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) ss += y[e] * y[e];
+    for (int off = L >> 1; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+    float gv[VEC];
+    Elem<float>::template load<VEC>(a.gain + c0, gv);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) y[e] = y[e] * inv * gv[e];
+  }
+
+  const int R = a.rope_dims;
+  if (R > 0 && c0 + VEC > D - R) {
+    const int64_t pos = a.pos0[b] + (int64_t)m * i;
+#pragma unroll
+    for (int e = 0; e < VEC; e += 2) {
+      const int c = c0 + e;
+      if (c >= D - R) {
+        float cs, sn;
+        rope_cos_sin(pos, (c - (D - R)) >> 1, R, a.rope_base, cs, sn);
+        const float x0 = y[e], x1 = y[e + 1];
+        y[e] = x0 * cs - x1 * sn;
+        y[e + 1] = x0 * sn + x1 * cs;
+      }
+    }
+  }
+
+  const int64_t bstride = a.out_bstride ? a.out_bstride : (int64_t)a.n_out * D;
+  T* op = (T*)a.out + (int64_t)b * bstride + (int64_t)i * D + c0;
+  Elem<T>::template store<VEC>(op, y);
+}
+
+template <typename T, int VEC>
+static hipError_t launch_compress_t(const CompressArgs& a, hipStream_t stream) {
+  const int L = a.D / VEC;
+  const int rows = a.m * (a.overlap ? 2 : 1);
+  int G = 1;
+  while (G < rows) G <<= 1;
+  const int g_threads = 1024 / L;                       // at most 1024 threads
+  const int g_lds = (48 * 1024) / (3 * 4 * a.D);        // merge buffer <= 48 KiB
+  G = min(G, min(g_threads, max(g_lds, 1)));
+  while (G * L < 64 && G * L < 1024 && G < 64) G <<= 1;  // at least one full wave
+  const size_t lds = (size_t)3 * G * a.D * sizeof(float);
+  dim3 grid(a.n_out, a.B), block(G * L);
+  hipLaunchKernelGGL((compress_kernel<T, VEC>), grid, block, lds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress(const CompressArgs& a, hipStream_t stream) {
+  if (a.dt == 1) {
+    if (a.D <= 512) return launch_compress_t<bf16_t, 8>(a, stream);
+    return launch_compress_t<bf16_t, 16>(a, stream);
+  }
+  if (a.D <= 256) return launch_compress_t<float, 4>(a, stream);
+  if (a.D == 512) return launch_compress_t<float, 8>(a, stream);
+  return launch_compress_t<float, 16>(a, stream);
+}
+
+}  // namespace csa

@@ -1,0 +1,233 @@
+// Lightning-indexer scores I[t,s] = sum_h w[t,h] * ReLU(q[t,h] . K[s]) for
+// every compressed key s visible to query t ("DeepSeek-v4 Beyond Basics"
+// section 3.2.2, eq. 16; "07 The Model", "The indexer: a learned retrieval
+// mechanism").  Scores are float32; bf16 products accumulate in float32.
+//
+// Three kernels:
+//  * index_generic   any shape/dtype, one thread per (query, key), VALU.
+//  * index_decode    bf16, 64 heads x 128, few queries: every wave streams its
+//                    own 32-key tiles straight from HBM into MFMA operands;
+//                    the query's 64x128 head matrix stays in registers.
+//  * index_prefill   bf16, 64 heads x 128, many queries: 8 waves = 8 queries
+//                    share 64-key tiles staged in LDS (double buffered).
+//
+// MFMA layout (v_mfma_f32_32x32x16_bf16, C[32x32] += A[32x16] B[16x32]):
+// lane l feeds A row (l % 32) and B column (l % 32) with 8 consecutive K
+// slots starting at 8 * (l / 32); accumulator element r of lane l is
+// C[8*(r/4) + 4*(l/32) + r%4][l % 32].  Here A = query heads (M = 32 heads),
+// B = keys (N = 32 keys) and the 128-long contraction runs in 8 steps; at
+// step s the K slots of lane half g map to key channels 64*g + 8*s .. +7,
+// the same map on both operands, so each lane reads 128 contiguous bytes of
+// its key row.  After the 16 MFMAs of a tile a lane holds 32 of the 64 head
+// dots of one key: ReLU, weight, sum, and one cross-half shuffle finish it.
+#include "kernels.h"
+
+namespace csa {
+
+// ------------------------------------------------------------------ generic
+template <typename T>
+__global__ __launch_bounds__(256) void index_generic(IndexArgs a) {
+  extern __shared__ float sq[];  // [Hi*Di] query, then [Hi] weights
+  const int query = blockIdx.y;
+  const int b = query / a.Tq;
+  const int t = query - b * a.Tq;
+  const int n_vis = visible_entries(a.q_pos0[b] + t, a.m, min(a.n_entries[b], a.N_cap));
+  const int HD = a.Hi * a.Di;
+  const T* qp = (const T*)a.q + (int64_t)query * HD;
+  for (int e = threadIdx.x; e < HD; e += blockDim.x) sq[e] = Elem<T>::get(qp + e);
+  for (int e = threadIdx.x; e < a.Hi; e += blockDim.x) sq[HD + e] = a.w[(int64_t)query * a.Hi + e];
+  __syncthreads();
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= n_vis) return;
+  const T* kp = (const T*)a.k + ((int64_t)b * a.N_cap + s) * a.Di;
+  float score = 0.f;
+  for (int h = 0; h < a.Hi; ++h) {
+    float dot = 0.f;
+    for (int c = 0; c < a.Di; ++c) dot += sq[h * a.Di + c] * Elem<T>::get(kp + c);
+    score += sq[HD + h] * fmaxf(dot, 0.f);
+  }
+  a.scores[(int64_t)query * a.N_cap + s] = score;
+}
+
+// --------------------------------------------------------------- MFMA common
+// Query operand: lane (g, j) holds heads j and 32+j, channels 64g + 8s .. +7.
+__device__ __forceinline__ void load_query_operand(const bf16_t* qp, int lane, bf16x8_t (&qa)[2][8]) {
+  const int j = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qa[mt][s] = *reinterpret_cast<const bf16x8_t*>(qp + (mt * 32 + j) * 128 + g * 64 + 8 * s);
+}
+
+// Head weights matching the accumulator rows held by this lane.
+__device__ __forceinline__ void load_head_weights(const float* wp, int lane, float (&wv)[2][16]) {
+  const int g = lane >> 5;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wv[mt][r] = wp[mt * 32 + 8 * (r >> 2) + 4 * g + (r & 3)];
+}
+
+__device__ __forceinline__ float tile_score(const bf16x8_t (&qa)[2][8], const bf16x8_t (&kb)[8],
+                                            const float (&wv)[2][16]) {
+  f32x16_t c0 = {}, c1 = {};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], kb[s], c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], kb[s], c1, 0, 0, 0);
+  }
+  float sc = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sc += wv[0][r] * fmaxf(c0[r], 0.f);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sc += wv[1][r] * fmaxf(c1[r], 0.f);
+  return sc + __shfl_xor(sc, 32);
+}
+
+// ------------------------------------------------------------------- decode
+// grid (chunks, B*Tq); 4 waves; chunk = 4 * tiles_per_wave tiles of 32 keys,
+// tiles interleaved over the waves so the WG reads one contiguous range.
+__global__ __launch_bounds__(256) void index_decode(IndexArgs a, int tiles_per_wave) {
+  const int query = blockIdx.y;
+  const int b = query / a.Tq;
+  const int t = query - b * a.Tq;
+  const int n_vis = visible_entries(a.q_pos0[b] + t, a.m, min(a.n_entries[b], a.N_cap));
+  const int chunk_tiles = 4 * tiles_per_wave;
+  const int tile0 = blockIdx.x * chunk_tiles;
+  if (tile0 * 32 >= n_vis) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = lane & 31, g = lane >> 5;
+
+  bf16x8_t qa[2][8];
+  load_query_operand((const bf16_t*)a.q + (int64_t)query * 64 * 128, lane, qa);
+  float wv[2][16];
+  load_head_weights(a.w + (int64_t)query * 64, lane, wv);
+
+  const bf16_t* kbase = (const bf16_t*)a.k + (int64_t)b * a.N_cap * 128 + g * 64;
+  float* out = a.scores + (int64_t)query * a.N_cap;
+
+  int tile = tile0 + wave;
+  const int tile_end = min(tile0 + chunk_tiles, (n_vis + 31) >> 5);
+  bf16x8_t kb[8], kn[8];
+  if (tile < tile_end) {
+    const int key = min(tile * 32 + j, n_vis - 1);
+    const bf16_t* kp = kbase + (int64_t)key * 128;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kb[s] = *reinterpret_cast<const bf16x8_t*>(kp + 8 * s);
+  }
+  for (; tile < tile_end; tile += 4) {
+    const int nxt = tile + 4;
+    if (nxt < tile_end) {
+      const int key = min(nxt * 32 + j, n_vis - 1);
+      const bf16_t* kp = kbase + (int64_t)key * 128;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) kn[s] = *reinterpret_cast<const bf16x8_t*>(kp + 8 * s);
+    }
+    const float sc = tile_score(qa, kb, wv);
+    const int key = tile * 32 + j;
+    if (g == 0 && key < n_vis) out[key] = sc;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kb[s] = kn[s];
+  }
+}
+
+// ------------------------------------------------------------------ prefill
+// grid (ceil(Tq/8), B); 8 waves, wave w scores query 8*blockIdx.x + w
+// against 64-key tiles in LDS (row pitch 272 bytes: the 16-byte column
+// reads of 16 consecutive rows fall in distinct banks).
+constexpr int kPfKeys = 64;
+constexpr int kPfPitch = 136;  // bf16 elements per LDS row
+
+__global__ __launch_bounds__(512) void index_prefill(IndexArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t kt[2][kPfKeys * kPfPitch];
+  const int b = blockIdx.y;
+  const int t0 = blockIdx.x * 8;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = lane & 31, g = lane >> 5;
+  const int t = t0 + wave;
+  const bool live = t < a.Tq;
+  const int64_t pos_base = a.q_pos0[b];
+  const int n_live = min(a.n_entries[b], a.N_cap);
+  const int n_vis = live ? visible_entries(pos_base + t, a.m, n_live) : 0;
+  const int t_last = min(t0 + 7, a.Tq - 1);
+  const int n_max = visible_entries(pos_base + t_last, a.m, n_live);
+  const int64_t query = (int64_t)b * a.Tq + (live ? t : t_last);
+
+  bf16x8_t qa[2][8];
+  load_query_operand((const bf16_t*)a.q + query * 64 * 128, lane, qa);
+  float wv[2][16];
+  load_head_weights(a.w + query * 64, lane, wv);
+
+  const bf16_t* kbase = (const bf16_t*)a.k + (int64_t)b * a.N_cap * 128;
+  float* out = a.scores + query * a.N_cap;
+
+  // cooperative tile load: 64 keys x 256 B = 1024 x 16 B pieces, 2 per thread
+  const int p0 = threadIdx.x, p1 = threadIdx.x + 512;
+  auto fetch = [&](int k0, uint4& v0, uint4& v1) {
+    const int r0 = p0 >> 4, r1 = p1 >> 4;
+    const int key0 = min(k0 + r0, max(n_max - 1, 0));
+    const int key1 = min(k0 + r1, max(n_max - 1, 0));
+    v0 = *reinterpret_cast<const uint4*>(kbase + (int64_t)key0 * 128 + (p0 & 15) * 8);
+    v1 = *reinterpret_cast<const uint4*>(kbase + (int64_t)key1 * 128 + (p1 & 15) * 8);
+  };
+  auto stash = [&](int buf, const uint4& v0, const uint4& v1) {
+    *reinterpret_cast<uint4*>(&kt[buf][(p0 >> 4) * kPfPitch + (p0 & 15) * 8]) = v0;
+    *reinterpret_cast<uint4*>(&kt[buf][(p1 >> 4) * kPfPitch + (p1 & 15) * 8]) = v1;
+  };
+
+  if (n_max <= 0) return;
+  uint4 v0, v1;
+  fetch(0, v0, v1);
+  stash(0, v0, v1);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = 0; k0 < n_max; k0 += kPfKeys) {
+    const bool more = k0 + kPfKeys < n_max;
+    if (more) fetch(k0 + kPfKeys, v0, v1);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      bf16x8_t kb[8];
+      const bf16_t* row = &kt[buf][(nt * 32 + j) * kPfPitch + g * 64];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) kb[s] = *reinterpret_cast<const bf16x8_t*>(row + 8 * s);
+      const float sc = tile_score(qa, kb, wv);
+      const int key = k0 + nt * 32 + j;
+      if (g == 0 && key < n_vis) out[key] = sc;
+    }
+    if (more) stash(buf ^ 1, v0, v1);
+    __syncthreads();
+    buf ^= 1;
+  }
+}
+
+bool index_uses_mfma(const IndexArgs& a) { return a.dt == 1 && a.Hi == 64 && a.Di == 128; }
+
+hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream) {
+  const int queries = a.B * a.Tq;
+  if (queries == 0 || a.N_cap == 0) return hipSuccess;
+  if (index_uses_mfma(a)) {
+    if (a.Tq >= 8) {
+      dim3 grid((a.Tq + 7) / 8, a.B);
+      hipLaunchKernelGGL(index_prefill, grid, dim3(512), 0, stream, a);
+    } else {
+      // ~1.5k workgroups in flight: enough to cover 256 CUs several times
+      const int64_t keys = (int64_t)queries * a.N_cap;
+      int tpw = (int)((keys + 1536LL * 128 - 1) / (1536LL * 128));
+      tpw = max(1, min(tpw, 32));
+      const int chunk = 4 * tpw * 32;
+      dim3 grid((a.N_cap + chunk - 1) / chunk, queries);
+      hipLaunchKernelGGL(index_decode, grid, dim3(256), 0, stream, a, tpw);
+    }
+    return hipGetLastError();
+  }
+  const size_t lds = ((size_t)a.Hi * a.Di + a.Hi) * sizeof(float);
+  dim3 grid((a.N_cap + 255) / 256, queries);
+  if (a.dt == 1)
+    hipLaunchKernelGGL(index_generic<bf16_t>, grid, dim3(256), lds, stream, a);
+  else
+    hipLaunchKernelGGL(index_generic<float>, grid, dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,91 @@
+// Internal interface between the C ABI layer (abi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace csa {
+
+// ---------------------------------------------------------------- compressor
+struct CompressArgs {
+  int dt;  // 0 f32, 1 bf16
+  int B, T, D, m, overlap, n_out;
+  const void *c_a, *z_a, *c_b, *z_b, *prev_c_b, *prev_z_b;
+  const float *bias_a, *bias_b, *gain;
+  float eps;
+  int rope_dims;
+  double rope_base;
+  const int64_t* pos0;
+  void* out;
+  int64_t out_bstride;
+};
+hipError_t launch_compress(const CompressArgs& a, hipStream_t stream);
+
+// ------------------------------------------------------------------- indexer
+struct IndexArgs {
+  int dt;
+  int B, Tq, Hi, Di, N_cap, m;
+  const void* q;        // [B, Tq, Hi, Di]
+  const float* w;       // [B, Tq, Hi]
+  const void* k;        // [B, N_cap, Di]
+  const int32_t* n_entries;
+  const int64_t* q_pos0;
+  float* scores;        // [B*Tq, N_cap]
+};
+// True when the MFMA kernels cover this shape (bf16, 64 heads x 128).
+bool index_uses_mfma(const IndexArgs& a);
+hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
+
+// --------------------------------------------------------------------- top-k
+// Largest score row that one workgroup selects from in LDS.
+constexpr int kTopkCap = 16384;
+
+struct TopkArgs {
+  int mode;             // 0: direct rows, 1: chunk of a row, 2: merge of candidates
+  int B, Tq, N_cap, m, K;
+  int nchunks;          // chunks per query (mode 1); chunks merged (mode 2)
+  int chunk;            // elements per chunk (mode 1)
+  const float* scores;  // mode 0/1: [B*Tq, N_cap]; mode 2: candidates [B*Tq, nchunks*K]
+  const int32_t* in_idx;  // mode 2: candidate indices [B*Tq, nchunks*K]
+  const int32_t* n_entries;
+  const int64_t* q_pos0;
+  int32_t* out_idx;     // [segments, K]
+  float* out_scores;    // [segments, K] or null
+};
+hipError_t launch_topk(const TopkArgs& a, int segments, hipStream_t stream);
+
+// ----------------------------------------------------------------- attention
+struct AttnArgs {
+  int dt;
+  int B, Tq, H, D, R;
+  double rope_base;
+  float scale;
+  const void* q;        // [B, Tq, H, D]
+  const void* pool;     // [B, N_cap, D]
+  int N_cap;
+  int csa;              // 1: rows = idx-selected pool rows; 0: visible prefix (HCA)
+  const int32_t* idx;   // CSA: [B, Tq, K] (may be null when K == 0)
+  int K;
+  const int32_t* n_entries;  // HCA
+  int m;                     // HCA
+  const void* win;      // [B, L_win, D]
+  int L_win;
+  const int64_t* win_pos0;
+  int W;
+  const float* sink;    // [H]
+  const int64_t* q_pos0;
+  void* out;            // [B, Tq, H, D]
+  float* lse;           // [B, Tq, H] or null
+  int splits;           // key-range splits per query (1 = no combine pass)
+  float* part_o;        // [B*Tq, splits, H, D] when splits > 1
+  float* part_ml;       // [B*Tq, splits, H, 2]
+};
+bool attn_uses_mfma(int dt, int H, int D, int R);
+int attn_splits(int dt, int B, int Tq, int H, int D, int keys_per_query);
+size_t attn_ws_bytes(int dt, int B, int Tq, int H, int D, int keys_per_query);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace csa

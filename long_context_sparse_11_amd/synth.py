@@ -2,10 +2,11 @@
 
 This module draws random numbers and rounds them to bfloat16; it holds none
 of the method's arithmetic, so both the GPU tests and the CPU oracle can be
-fed from it.  Every array is generated in float32 with NumPy's PCG64
-(``default_rng(seed)``) in a fixed order, then (for bf16 workloads) rounded
-once to bfloat16, round-to-nearest-even; the float32 view of the rounded
-values and the raw uint16 bits describe the same numbers.
+fed from it.  Every array is generated in float32 with NumPy's PCG64 from its own stream,
+``default_rng([seed, crc32(workload), crc32(array name)])``, so any subset of
+a workload can be drawn without drawing the rest, then (for bf16 workloads)
+rounded once to bfloat16, round-to-nearest-even; the float32 view of the
+rounded values and the raw uint16 bits describe the same numbers.
 
 Workloads (shapes after DeepSeek-V4-Flash: 64 query heads x head_dim 512, one
 shared K=V head, RoPE on the last 64 channels, indexer 64 heads x 128, top-k
@@ -22,6 +23,8 @@ shared K=V head, RoPE on the last 64 channels, indexer 64 heads x 128, top-k
              indexer keys with 10% of rows scaled by 4 (heavy-tailed mixture)
 """
 from __future__ import annotations
+
+import zlib
 
 import numpy as np
 
@@ -71,6 +74,23 @@ class Tensor:
         return self.bits if self.dt == "bf16" else self._f32
 
 
+def _rng(seed, workload, name):
+    return np.random.default_rng([int(seed), zlib.crc32(workload.encode()), zlib.crc32(name.encode())])
+
+
+class _Draw:
+    """Per-array streams of one workload and seed."""
+
+    def __init__(self, seed, workload):
+        self.seed, self.workload = seed, workload
+
+    def __call__(self, name, shape, std=1.0, mean=0.0):
+        return _normal(_rng(self.seed, self.workload, name), shape, std, mean)
+
+    def rng(self, name):
+        return _rng(self.seed, self.workload, name)
+
+
 def _normal(rng, shape, std=1.0, mean=0.0):
     x = rng.standard_normal(size=shape, dtype=np.float32)
     if std != 1.0:
@@ -85,108 +105,111 @@ def _normal(rng, shape, std=1.0, mean=0.0):
 # ---------------------------------------------------------------------------
 def toy(seed: int = 0):
     """Toy CSA layer in fp32: every stream a full causal prefill of 256 tokens."""
-    rng = np.random.default_rng(seed)
+    dr = _Draw(seed, "toy")
     T, H, D, R, Hi, Di, m, K, W = 256, 4, 64, 16, 4, 32, 4, 16, 16
     s = 1.0 / np.sqrt(D)
     si = 1.0 / np.sqrt(Di)
     d = dict(name="toy", dt="f32", B=1, T=T, Tq=T, H=H, D=D, R=R, Hi=Hi, Di=Di, m=m, K=K, W=W,
-             q_pos0=np.array([0], np.int64), base=10000.0, eps=1e-6)
-    d["q"] = Tensor(_normal(rng, (1, T, H, D), s), "f32")
-    d["kv"] = Tensor(_normal(rng, (1, T, D), s), "f32")
-    d["c_a"] = Tensor(_normal(rng, (1, T, D), s), "f32")
-    d["c_b"] = Tensor(_normal(rng, (1, T, D), s), "f32")
-    d["z_a"] = Tensor(_normal(rng, (1, T, D)), "f32")
-    d["z_b"] = Tensor(_normal(rng, (1, T, D)), "f32")
-    d["bias_a"] = _normal(rng, (m, D), 0.02)
-    d["bias_b"] = _normal(rng, (m, D), 0.02)
-    d["gain"] = _normal(rng, (D,), 0.02, 1.0)
-    d["gain_win"] = _normal(rng, (D,), 0.02, 1.0)
-    d["ic_a"] = Tensor(_normal(rng, (1, T, Di), si), "f32")
-    d["ic_b"] = Tensor(_normal(rng, (1, T, Di), si), "f32")
-    d["iz_a"] = Tensor(_normal(rng, (1, T, Di)), "f32")
-    d["iz_b"] = Tensor(_normal(rng, (1, T, Di)), "f32")
-    d["ibias_a"] = _normal(rng, (m, Di), 0.02)
-    d["ibias_b"] = _normal(rng, (m, Di), 0.02)
-    d["q_idx"] = Tensor(_normal(rng, (1, T, Hi, Di), si), "f32")
-    d["w_idx"] = _normal(rng, (1, T, Hi), 0.02)
-    d["sink"] = _normal(rng, (H,), 0.02)
+             N=T // m, q_pos0=np.array([0], np.int64), n_entries=np.array([T // m], np.int32),
+             win_pos0=np.array([0], np.int64), base=10000.0, eps=1e-6)
+    f = lambda n, shape, std=1.0: Tensor(dr(n, shape, std), "f32")
+    d["q"] = f("q", (1, T, H, D), s)
+    d["kv"] = f("kv", (1, T, D), s)
+    for n in ("c_a", "c_b"):
+        d[n] = f(n, (1, T, D), s)
+    for n in ("z_a", "z_b"):
+        d[n] = f(n, (1, T, D))
+    d["bias_a"] = dr("bias_a", (m, D), 0.02)
+    d["bias_b"] = dr("bias_b", (m, D), 0.02)
+    d["gain"] = dr("gain", (D,), 0.02, 1.0)
+    d["gain_win"] = dr("gain_win", (D,), 0.02, 1.0)
+    for n in ("ic_a", "ic_b"):
+        d[n] = f(n, (1, T, Di), si)
+    for n in ("iz_a", "iz_b"):
+        d[n] = f(n, (1, T, Di))
+    d["ibias_a"] = dr("ibias_a", (m, Di), 0.02)
+    d["ibias_b"] = dr("ibias_b", (m, Di), 0.02)
+    d["q_idx"] = f("q_idx", (1, T, Hi, Di), si)
+    d["w_idx"] = dr("w_idx", (1, T, Hi), 0.02)
+    d["sink"] = dr("sink", (H,), 0.02)
     return d
 
 
-def decode(kind: str, seed: int = 0, B: int | None = None, N: int | None = None,
-           heavy_tail: bool | None = None):
-    """Decode-step inputs (one new query per sequence) for 'csa64k', 'csa1m'
-    or 'hca1m'.  ``B`` / ``N`` override the batch and the pool length for
-    reduced-size parity cases; positions then follow from ``N``.
+DECODE = {  # m, batch, pool entries, heavy-tailed indexer keys
+    "csa64k": (4, 4, 16384, False),
+    "csa1m": (4, 8, 262144, True),
+    "hca1m": (128, 16, 8192, False),
+}
 
-    The pool and window rows are drawn directly (they stand for already
-    normalised, rotated entries); the closing block's compressor streams are
-    drawn separately so the step can run the compressor too.
+
+def decode(kind: str, seed: int = 0, B: int | None = None, N: int | None = None,
+           heavy_tail: bool | None = None, skip=()):
+    """Decode-step inputs (one new query per sequence at the last position of
+    a context of N*m tokens) for 'csa64k', 'csa1m' or 'hca1m'.  ``B`` / ``N``
+    override batch and pool length for reduced-size cases; ``skip`` names
+    arrays not to draw (e.g. the 2 GiB pool when only the indexer is tested).
+
+    Pool and window rows are drawn directly (they stand for entries already
+    normalised and rotated); the closing block's compressor streams are drawn
+    separately so a step can run the compressor too.
     """
-    rng = np.random.default_rng(seed)
+    dr = _Draw(seed, kind)
     F = FLASH
     H, D, R, Hi, Di, K, W = F["H"], F["D"], F["R"], F["Hi"], F["Di"], F["K"], F["W"]
-    if kind == "csa64k":
-        m, B0, N0, ht = 4, 4, 16384, False
-    elif kind == "csa1m":
-        m, B0, N0, ht = 4, 8, 262144, True
-    elif kind == "hca1m":
-        m, B0, N0, ht = 128, 16, 8192, False
-    else:
-        raise ValueError(kind)
+    m, B0, N0, ht = DECODE[kind]
     B = B0 if B is None else B
     N = N0 if N is None else N
     ht = ht if heavy_tail is None else heavy_tail
     ctx = N * m
-    t = ctx - 1
     d = dict(name=kind, dt="bf16", B=B, Tq=1, H=H, D=D, R=R, Hi=Hi, Di=Di, m=m, K=K, W=W,
              N=N, base=10000.0, eps=1e-6,
-             q_pos0=np.full(B, t, np.int64),
+             q_pos0=np.full(B, ctx - 1, np.int64),
              n_entries=np.full(B, N, np.int32),
              win_pos0=np.full(B, ctx - W, np.int64),
              block_pos0=np.full(B, ctx - m, np.int64))
-    d["q"] = Tensor(_normal(rng, (B, 1, H, D)), "bf16")
-    d["pool"] = Tensor(_normal(rng, (B, N, D)), "bf16")
-    d["win"] = Tensor(_normal(rng, (B, W, D)), "bf16")
-    d["sink"] = _normal(rng, (H,), 0.02)
-    # closing block of the compressor (entry N-1): block i (stream a) and,
-    # for CSA, block i-1 (stream b) as the overlap state
-    d["c_a"] = Tensor(_normal(rng, (B, m, D)), "bf16")
-    d["z_a"] = Tensor(_normal(rng, (B, m, D)), "bf16")
-    d["bias_a"] = _normal(rng, (m, D), 0.02)
-    d["gain"] = _normal(rng, (D,), 0.02, 1.0)
-    if kind != "hca1m":
-        d["c_b"] = Tensor(_normal(rng, (B, m, D)), "bf16")
-        d["z_b"] = Tensor(_normal(rng, (B, m, D)), "bf16")
-        d["prev_c_b"] = Tensor(_normal(rng, (B, m, D)), "bf16")
-        d["prev_z_b"] = Tensor(_normal(rng, (B, m, D)), "bf16")
-        d["bias_b"] = _normal(rng, (m, D), 0.02)
-        d["q_idx"] = Tensor(_normal(rng, (B, 1, Hi, Di)), "bf16")
-        d["w_idx"] = _normal(rng, (B, 1, Hi), 0.02)
-        kk = _normal(rng, (B, N, Di))
-        if ht:
+
+    def bf(name, shape, std=1.0):
+        if name not in skip:
+            d[name] = Tensor(dr(name, shape, std), "bf16")
+
+    bf("q", (B, 1, H, D))
+    bf("pool", (B, N, D))
+    bf("win", (B, W, D))
+    d["sink"] = dr("sink", (H,), 0.02)
+    # closing block of the compressor (entry N-1): block i in stream a and,
+    # for CSA, block i-1 in stream b (the overlap state)
+    bf("c_a", (B, m, D))
+    bf("z_a", (B, m, D))
+    d["bias_a"] = dr("bias_a", (m, D), 0.02)
+    d["gain"] = dr("gain", (D,), 0.02, 1.0)
+    if kind == "hca1m":
+        return d
+    for n in ("c_b", "z_b", "prev_c_b", "prev_z_b"):
+        bf(n, (B, m, D))
+    d["bias_b"] = dr("bias_b", (m, D), 0.02)
+    bf("q_idx", (B, 1, Hi, Di))
+    d["w_idx"] = dr("w_idx", (B, 1, Hi), 0.02)
+    if "k_idx" not in skip:
+        kk = dr("k_idx", (B, N, Di))
+        if ht:  # exactly floor(0.1 N) rows per sequence scaled by 4
+            prng = dr.rng("heavy_rows")
             n_heavy = int(0.1 * N)
             for b in range(B):
-                rows = rng.permutation(N)[:n_heavy]
-                kk[b, rows] *= np.float32(4.0)
+                kk[b, prng.permutation(N)[:n_heavy]] *= np.float32(4.0)
         d["k_idx"] = Tensor(kk, "bf16")
-        # indexer-key compressor streams for the closing block (Di wide)
-        d["ic_a"] = Tensor(_normal(rng, (B, m, Di)), "bf16")
-        d["iz_a"] = Tensor(_normal(rng, (B, m, Di)), "bf16")
-        d["ic_b"] = Tensor(_normal(rng, (B, m, Di)), "bf16")
-        d["iz_b"] = Tensor(_normal(rng, (B, m, Di)), "bf16")
-        d["iprev_c_b"] = Tensor(_normal(rng, (B, m, Di)), "bf16")
-        d["iprev_z_b"] = Tensor(_normal(rng, (B, m, Di)), "bf16")
-        d["ibias_a"] = _normal(rng, (m, Di), 0.02)
-        d["ibias_b"] = _normal(rng, (m, Di), 0.02)
+    # indexer-key compressor streams of the closing block (Di wide)
+    for n in ("ic_a", "iz_a", "ic_b", "iz_b", "iprev_c_b", "iprev_z_b"):
+        bf(n, (B, m, Di))
+    d["ibias_a"] = dr("ibias_a", (m, Di), 0.02)
+    d["ibias_b"] = dr("ibias_b", (m, Di), 0.02)
     return d
 
 
-def prefill(seed: int = 0, Tq: int = 4096, prefix: int = 15360):
+def prefill(seed: int = 0, Tq: int = 4096, prefix: int = 15360, skip=()):
     """CSA chunked prefill: ``Tq`` new tokens after a cached prefix of
-    ``prefix`` entries (m = 4).  The chunk's compressor streams carry 4 extra
+    ``prefix`` entries (m = 4).  The chunk's compressor streams carry m extra
     leading rows: the previous block's b-stream (overlap state)."""
-    rng = np.random.default_rng(seed)
+    dr = _Draw(seed, "prefill")
     F = FLASH
     H, D, R, Hi, Di, K, W = F["H"], F["D"], F["R"], F["Hi"], F["Di"], F["K"], F["W"]
     m = 4
@@ -197,19 +220,24 @@ def prefill(seed: int = 0, Tq: int = 4096, prefix: int = 15360):
              N=N, prefix=prefix, base=10000.0, eps=1e-6,
              q_pos0=np.array([p0], np.int64), n_entries=np.array([N], np.int32),
              win_pos0=np.array([p0 - W + 1], np.int64), chunk_pos0=np.array([p0], np.int64))
-    d["pool_prefix"] = Tensor(_normal(rng, (1, prefix, D)), "bf16")
-    d["kidx_prefix"] = Tensor(_normal(rng, (1, prefix, Di)), "bf16")
+
+    def bf(name, shape, std=1.0):
+        if name not in skip:
+            d[name] = Tensor(dr(name, shape, std), "bf16")
+
+    bf("pool_prefix", (1, prefix, D))
+    bf("kidx_prefix", (1, prefix, Di))
     for name, width in (("c_a", D), ("z_a", D), ("c_b", D), ("z_b", D),
                         ("ic_a", Di), ("iz_a", Di), ("ic_b", Di), ("iz_b", Di)):
-        d[name] = Tensor(_normal(rng, (1, Tq + m, width)), "bf16")
-    d["bias_a"] = _normal(rng, (m, D), 0.02)
-    d["bias_b"] = _normal(rng, (m, D), 0.02)
-    d["ibias_a"] = _normal(rng, (m, Di), 0.02)
-    d["ibias_b"] = _normal(rng, (m, Di), 0.02)
-    d["gain"] = _normal(rng, (D,), 0.02, 1.0)
-    d["win"] = Tensor(_normal(rng, (1, L_win, D)), "bf16")
-    d["q"] = Tensor(_normal(rng, (1, Tq, H, D)), "bf16")
-    d["q_idx"] = Tensor(_normal(rng, (1, Tq, Hi, Di)), "bf16")
-    d["w_idx"] = _normal(rng, (1, Tq, Hi), 0.02)
-    d["sink"] = _normal(rng, (H,), 0.02)
+        bf(name, (1, Tq + m, width))
+    d["bias_a"] = dr("bias_a", (m, D), 0.02)
+    d["bias_b"] = dr("bias_b", (m, D), 0.02)
+    d["ibias_a"] = dr("ibias_a", (m, Di), 0.02)
+    d["ibias_b"] = dr("ibias_b", (m, Di), 0.02)
+    d["gain"] = dr("gain", (D,), 0.02, 1.0)
+    bf("win", (1, L_win, D))
+    bf("q", (1, Tq, H, D))
+    bf("q_idx", (1, Tq, Hi, Di))
+    d["w_idx"] = dr("w_idx", (1, Tq, Hi), 0.02)
+    d["sink"] = dr("sink", (H,), 0.02)
     return d

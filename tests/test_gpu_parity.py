@@ -1,0 +1,439 @@
+"""GPU parity of every library call against the CPU oracle, at sizes the
+oracle finishes in seconds that still span several tiles and a ragged tail,
+plus the edge cases of the method.  Calls go through the C ABI (ctypes
+binding); stage isolation: each call gets the same inputs as the oracle.
+
+Tolerances: attention and compressor outputs use the row-wise rule
+max_rows ||gpu - oracle||_inf / ||oracle||_inf <= 1e-5 (fp32) or 2e-2 (bf16);
+index sets follow the band rule (symmetric difference only within 1e-4 of
+the K-th oracle score); integer selection from the GPU's own scores must be
+bit-exact against the oracle's selector.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_11_amd as L
+from long_context_sparse_11_amd import synth
+from oracle import csa_oracle as O
+from tests.helpers import (BAND, TOL_BF16, TOL_F32, bf16_dev_from_f32, check_band, dev, host,
+                           rowwise_rel_err)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    L.lib()
+
+
+def i64(a):
+    return dev(np.asarray(a, dtype=np.int64))
+
+
+def i32(a):
+    return dev(np.asarray(a, dtype=np.int32))
+
+
+# ======================================================================
+# compressor
+# ======================================================================
+def test_compress_toy_fp32():
+    d = synth.toy(0)
+    m, R = d["m"], d["R"]
+    pos0 = i64([0])
+    pool = L.csa_compress(dev(d["c_a"]), m, z_a=dev(d["z_a"]), c_b=dev(d["c_b"]), z_b=dev(d["z_b"]),
+                          bias_a=dev(d["bias_a"]), bias_b=dev(d["bias_b"]), gain=dev(d["gain"]),
+                          rope_dims=R, pos0=pos0)
+    ref = O.csa_compress(d["c_a"].f32, d["z_a"].f32, d["bias_a"], m, c_b=d["c_b"].f32,
+                         z_b=d["z_b"].f32, bias_b=d["bias_b"], gain=d["gain"], rope_dims=R,
+                         pos0=[0])
+    assert pool.shape == (1, 64, 64)
+    assert rowwise_rel_err(host(pool), ref) <= TOL_F32
+    keys = L.csa_compress(dev(d["ic_a"]), m, z_a=dev(d["iz_a"]), c_b=dev(d["ic_b"]),
+                          z_b=dev(d["iz_b"]), bias_a=dev(d["ibias_a"]), bias_b=dev(d["ibias_b"]))
+    kref = O.csa_compress(d["ic_a"].f32, d["iz_a"].f32, d["ibias_a"], m, c_b=d["ic_b"].f32,
+                          z_b=d["iz_b"].f32, bias_b=d["ibias_b"])
+    assert rowwise_rel_err(host(keys), kref) <= TOL_F32
+    win = L.csa_compress(dev(d["kv"]), 1, gain=dev(d["gain_win"]), rope_dims=R, pos0=pos0)
+    wref = O.csa_compress(d["kv"].f32, None, None, 1, gain=d["gain_win"], rope_dims=R, pos0=[0])
+    assert rowwise_rel_err(host(win), wref) <= TOL_F32
+
+
+CASES = [  # D, m, T, overlap, prev, norm+rope, pos0
+    (512, 4, 100, True, True, True, [61440, 8]),
+    (512, 4, 101, True, False, True, [0, 0]),        # ragged partial block, sequence start
+    (128, 4, 101, True, True, False, [400, 4]),      # indexer keys
+    (512, 128, 300, False, False, True, [1048192, 0]),  # HCA, ragged
+    (512, 1, 50, False, False, True, [77, 1000]),    # window rows
+    (64, 8, 37, True, True, True, [16, 0]),          # small head
+]
+
+
+@pytest.mark.parametrize("D,m,T,overlap,prev,normrope,pos", CASES)
+def test_compress_bf16(D, m, T, overlap, prev, normrope, pos):
+    rng = np.random.default_rng(D * 7 + m * 3 + T)
+    B = 2
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)
+    ca, za, cb, zb = (synth.Tensor(f(B, T, D), "bf16") for _ in range(4))
+    pcb, pzb = (synth.Tensor(f(B, m, D), "bf16") for _ in range(2))
+    ba, bb = 0.02 * f(m, D), 0.02 * f(m, D)
+    gain = 1 + 0.02 * f(D) if normrope else None
+    R = min(64, D) if normrope else 0
+    kw = dict(z_a=dev(za), bias_a=dev(ba), rope_dims=R, pos0=i64(pos))
+    okw = dict(rope_dims=R, pos0=pos)
+    if gain is not None:
+        kw["gain"] = dev(gain)
+        okw["gain"] = gain
+    if overlap:
+        kw.update(c_b=dev(cb), z_b=dev(zb), bias_b=dev(bb))
+        okw.update(c_b=cb.f32, z_b=zb.f32, bias_b=bb)
+        if prev:
+            kw.update(prev_c_b=dev(pcb), prev_z_b=dev(pzb))
+            okw.update(prev_c_b=pcb.f32, prev_z_b=pzb.f32)
+    out = L.csa_compress(dev(ca), m, **kw)
+    ref = O.csa_compress(ca.f32, za.f32, ba, m, **okw)
+    assert out.shape == ref.shape == (B, -(-T // m), D)
+    assert rowwise_rel_err(host(out), ref) <= TOL_BF16
+
+
+def test_compress_closing_block_into_pool():
+    """Decode: the closing block's entry is written in place into row N-1 of
+    a [B, N, D] pool through the batch stride; nothing else changes."""
+    d = synth.decode("csa64k", 0, B=3, N=64)
+    B, N, D, m = d["B"], d["N"], d["D"], d["m"]
+    pool = dev(d["pool"])
+    before = pool.clone()
+    L.csa_compress(dev(d["c_a"]), m, z_a=dev(d["z_a"]), c_b=dev(d["c_b"]), z_b=dev(d["z_b"]),
+                   prev_c_b=dev(d["prev_c_b"]), prev_z_b=dev(d["prev_z_b"]),
+                   bias_a=dev(d["bias_a"]), bias_b=dev(d["bias_b"]), gain=dev(d["gain"]),
+                   rope_dims=d["R"], pos0=i64(d["block_pos0"]), out=pool[:, N - 1:],
+                   out_bstride=N * D)
+    ref = O.csa_compress(d["c_a"].f32, d["z_a"].f32, d["bias_a"], m, c_b=d["c_b"].f32,
+                         z_b=d["z_b"].f32, bias_b=d["bias_b"], prev_c_b=d["prev_c_b"].f32,
+                         prev_z_b=d["prev_z_b"].f32, gain=d["gain"], rope_dims=d["R"],
+                         pos0=d["block_pos0"])
+    assert torch.equal(pool[:, : N - 1], before[:, : N - 1])
+    assert rowwise_rel_err(host(pool[:, N - 1]), ref[:, 0]) <= TOL_BF16
+
+
+# ======================================================================
+# indexer + top-k
+# ======================================================================
+def _index_case(q_idx, w_idx, k_idx, n_entries, q_pos0, K, m):
+    idx, sc, alls = L.csa_index_topk(dev(q_idx), dev(w_idx), dev(k_idx), i32(n_entries),
+                                     i64(q_pos0), K, m, want_scores=True, want_all_scores=True)
+    return host(idx).astype(np.int64), host(sc), host(alls)
+
+
+def _check_index(q_idx, w_idx, k_idx, n_entries, q_pos0, K, m, score_atol):
+    qf = q_idx.f32 if isinstance(q_idx, synth.Tensor) else q_idx
+    kf = k_idx.f32 if isinstance(k_idx, synth.Tensor) else k_idx
+    B, Tq = qf.shape[:2]
+    gidx, gsc, gall = _index_case(q_idx, w_idx, k_idx, n_entries, q_pos0, K, m)
+    ridx, rsc = O.csa_index_topk(qf, w_idx, kf, n_entries, q_pos0, K, m)
+    excused = 0
+    for b in range(B):
+        for t in range(Tq):
+            nv = O.visible_count(q_pos0[b] + t, m, n_entries[b])
+            # scores of every visible entry
+            if nv:
+                err = np.abs(gall[b, t, :nv].astype(np.float64) - rsc[b, t, :nv]).max()
+                assert err <= score_atol, (b, t, err)
+            excused += check_band(gidx[b, t], ridx[b, t], rsc[b, t], nv, K)
+            # selection from the GPU's own float32 scores is exact
+            want = O.select_topk(gall[b, t, :nv], nv, K)
+            assert np.array_equal(gidx[b, t], want), (b, t)
+            sel = gidx[b, t]
+            assert np.array_equal(gsc[b, t][sel >= 0], gall[b, t][sel[sel >= 0]])
+            assert np.all(np.isneginf(gsc[b, t][sel < 0]))
+    return excused
+
+
+def test_index_toy_fp32():
+    d = synth.toy(0)
+    keys = O.csa_compress(d["ic_a"].f32, d["iz_a"].f32, d["ibias_a"], 4, c_b=d["ic_b"].f32,
+                          z_b=d["iz_b"].f32, bias_b=d["ibias_b"]).astype(np.float32)
+    ex = _check_index(d["q_idx"], d["w_idx"], keys, d["n_entries"], d["q_pos0"], d["K"], d["m"],
+                      score_atol=1e-7)
+    assert ex == 0
+
+
+# Worst-case float32 rounding of a 64-head, 128-term score with these value
+# ranges is ~1e-3; observed errors are ~1e-6.
+SCORE_ATOL_BF16 = 1e-3
+
+
+@pytest.mark.parametrize("N", [300, 513, 5000, 20000])
+def test_index_decode_bf16(N):
+    d = synth.decode("csa64k", 1, B=2, N=N, skip=("pool", "q", "win"))
+    _check_index(d["q_idx"], d["w_idx"], d["k_idx"], d["n_entries"], d["q_pos0"], d["K"], d["m"],
+                 SCORE_ATOL_BF16)
+
+
+@pytest.mark.parametrize("Tq,pos0", [(40, 2040), (37, 0), (8, 100000)])
+def test_index_prefill_bf16(Tq, pos0):
+    rng = np.random.default_rng(Tq)
+    N = 700
+    q = synth.Tensor(rng.standard_normal((1, Tq, 64, 128)).astype(np.float32), "bf16")
+    w = (0.02 * rng.standard_normal((1, Tq, 64))).astype(np.float32)
+    k = synth.Tensor(rng.standard_normal((1, N, 128)).astype(np.float32), "bf16")
+    _check_index(q, w, k, np.array([N], np.int32), np.array([pos0]), 512, 4, SCORE_ATOL_BF16)
+
+
+def test_index_heavy_tail_two_level_select():
+    """Rows longer than one workgroup's LDS go through chunk winners + merge."""
+    d = synth.decode("csa1m", 2, B=2, N=40000, skip=("pool", "q", "win"))
+    _check_index(d["q_idx"], d["w_idx"], d["k_idx"], d["n_entries"], d["q_pos0"], d["K"], d["m"],
+                 SCORE_ATOL_BF16)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_index_all_zero_scores_take_lowest_indices(dt):
+    """Every dot negative -> every score 0 -> ties -> the K lowest indices."""
+    rng = np.random.default_rng(3)
+    Hi, Di = (64, 128) if dt == "bf16" else (4, 32)
+    N, K = 3000, 512
+    q = np.abs(rng.standard_normal((1, 1, Hi, Di))).astype(np.float32)
+    k = -np.abs(rng.standard_normal((1, N, Di))).astype(np.float32)
+    w = rng.standard_normal((1, 1, Hi)).astype(np.float32)   # mixed signs: -0 and +0 scores
+    qq, kk = synth.Tensor(q, dt), synth.Tensor(k, dt)
+    gidx, gsc, _ = _index_case(qq, w, kk, [N], [4 * N - 1], K, 4)
+    assert np.array_equal(gidx[0, 0], np.arange(K))
+    assert np.all(gsc[0, 0] == 0)
+
+
+def test_index_nothing_visible():
+    rng = np.random.default_rng(4)
+    q = synth.Tensor(rng.standard_normal((2, 3, 64, 128)).astype(np.float32), "bf16")
+    w = rng.standard_normal((2, 3, 64)).astype(np.float32)
+    k = synth.Tensor(rng.standard_normal((2, 50, 128)).astype(np.float32), "bf16")
+    # b=0: no entries at all; b=1: positions 0..2 < m-1 with m = 4
+    gidx, gsc, _ = _index_case(q, w, k, [0, 50], [100, 0], 16, 4)
+    assert np.all(gidx == -1) and np.all(np.isneginf(gsc))
+
+
+def test_index_p4_sentinel_example():
+    """The transformers page's 16-token CSA example (m = 4, index_topk = 2):
+    queries before the first closed window get only -1, then slots fill."""
+    rng = np.random.default_rng(5)
+    T, m, K = 16, 4, 2
+    q = rng.standard_normal((1, T, 4, 32)).astype(np.float32)
+    w = rng.standard_normal((1, T, 4)).astype(np.float32)
+    k = rng.standard_normal((1, T // m, 32)).astype(np.float32)
+    gidx, _, _ = _index_case(q, w, k, [T // m], [0], K, m)
+    filled = (gidx[0] >= 0).sum(1)
+    assert list(filled[:3]) == [0, 0, 0] and list(filled[3:7]) == [1] * 4 and filled[7:].min() == 2
+    for t in range(T):
+        assert all(m * (s + 1) - 1 <= t for s in gidx[0, t] if s >= 0)
+
+
+# ======================================================================
+# attention
+# ======================================================================
+def _attn_ref(kind, q, pool, sel, win, win_pos0, W, sink, q_pos0, R, m=4, n_entries=None):
+    D = q.shape[-1]
+    if kind == "csa":
+        return O.csa_sparse_attn(q, pool, sel, win, win_pos0, W, sink, q_pos0, 1 / math.sqrt(D), R)
+    return O.hca_attn(q, pool, n_entries, m, win, win_pos0, W, sink, q_pos0, 1 / math.sqrt(D), R)
+
+
+def _run_attn(kind, q, pool, sel, win, win_pos0, W, sink, q_pos0, R, m=4, n_entries=None):
+    if kind == "csa":
+        return L.csa_sparse_attn(q, pool, sel, win, win_pos0, W, sink, q_pos0, rope_dims=R,
+                                 want_lse=True)
+    return L.hca_attn(q, pool, n_entries, m, win, win_pos0, W, sink, q_pos0, rope_dims=R,
+                      want_lse=True)
+
+
+def test_attn_toy_fp32():
+    d = synth.toy(0)
+    m, R, W, K = d["m"], d["R"], d["W"], d["K"]
+    pool = O.csa_compress(d["c_a"].f32, d["z_a"].f32, d["bias_a"], m, c_b=d["c_b"].f32,
+                          z_b=d["z_b"].f32, bias_b=d["bias_b"], gain=d["gain"], rope_dims=R,
+                          pos0=[0]).astype(np.float32)
+    win = O.csa_compress(d["kv"].f32, None, None, 1, gain=d["gain_win"], rope_dims=R,
+                         pos0=[0]).astype(np.float32)
+    keys = O.csa_compress(d["ic_a"].f32, d["iz_a"].f32, d["ibias_a"], m, c_b=d["ic_b"].f32,
+                          z_b=d["iz_b"].f32, bias_b=d["ibias_b"])
+    sel, _ = O.csa_index_topk(d["q_idx"].f32, d["w_idx"], keys, d["n_entries"], d["q_pos0"], K, m)
+    out, lse = L.csa_sparse_attn(dev(d["q"]), dev(pool), dev(sel), dev(win), i64([0]), W,
+                                 dev(d["sink"]), i64([0]), rope_dims=R, want_lse=True)
+    ro, rl = O.csa_sparse_attn(d["q"].f32, pool, sel, win, [0], W, d["sink"], [0],
+                               1 / math.sqrt(d["D"]), R)
+    assert rowwise_rel_err(host(out), ro) <= TOL_F32
+    assert np.abs(host(lse) - rl).max() <= 1e-5
+
+
+def _rand_sel(rng, B, Tq, K, n_vis_list, n_empty=0, dups=False):
+    sel = np.full((B, Tq, K), -1, np.int32)
+    for b in range(B):
+        for t in range(Tq):
+            nv = n_vis_list[b][t]
+            k = min(K - n_empty, nv)
+            ch = rng.choice(nv, size=k, replace=dups)
+            sel[b, t, :k] = np.sort(ch)
+            rng.shuffle(sel[b, t])
+    return sel
+
+
+# Worst-case effect of rounding the rotated query to bfloat16 on the
+# natural-log normaliser for unit-variance inputs is well below this.
+LSE_ATOL_BF16 = 2e-2
+
+
+@pytest.mark.parametrize("N,K,W,Tq,n_empty", [(2000, 512, 128, 1, 7), (300, 64, 16, 24, 0),
+                                              (5000, 512, 128, 3, 0), (100, 512, 128, 1, 0)])
+def test_attn_csa_bf16(N, K, W, Tq, n_empty):
+    rng = np.random.default_rng(N + Tq)
+    B, H, D, R, m = 2, 64, 512, 64, 4
+    ctx = N * m
+    q_pos0 = np.array([ctx - Tq, ctx - Tq - 5 * m])
+    L_win = Tq + W - 1 + 5 * m
+    win_pos0 = q_pos0 - W + 1 - 5 * m
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)
+    q, pool, win = (synth.Tensor(f(*s), "bf16") for s in [(B, Tq, H, D), (B, N, D), (B, L_win, D)])
+    sink = 0.5 * f(H)
+    nv = [[O.visible_count(q_pos0[b] + t, m, N) for t in range(Tq)] for b in range(B)]
+    sel = _rand_sel(rng, B, Tq, K, nv, n_empty)
+    out, lse = _run_attn("csa", dev(q), dev(pool), dev(sel), dev(win), i64(win_pos0), W, dev(sink),
+                         i64(q_pos0), R)
+    ro, rl = _attn_ref("csa", q.f32, pool.f32, sel, win.f32, win_pos0, W, sink, q_pos0, R)
+    assert rowwise_rel_err(host(out), ro) <= TOL_BF16
+    assert np.abs(host(lse) - rl).max() <= LSE_ATOL_BF16
+
+
+@pytest.mark.parametrize("N,n_ent,Tq,W", [(300, [300, 250, 1], 1, 128), (64, [64, 10, 0], 2, 16),
+                                          (2000, [2000, 1999, 1000], 1, 128)])
+def test_attn_hca_bf16(N, n_ent, Tq, W):
+    rng = np.random.default_rng(N + 1)
+    B, H, D, R, m = 3, 64, 512, 64, 128
+    ctx = N * m
+    q_pos0 = np.full(B, ctx - Tq)
+    L_win = Tq + W - 1
+    win_pos0 = q_pos0 - W + 1
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)
+    q, pool, win = (synth.Tensor(f(*s), "bf16") for s in [(B, Tq, H, D), (B, N, D), (B, L_win, D)])
+    sink = f(H)
+    n_entries = np.array(n_ent, np.int32)
+    out, lse = _run_attn("hca", dev(q), dev(pool), None, dev(win), i64(win_pos0), W, dev(sink),
+                         i64(q_pos0), R, m=m, n_entries=i32(n_entries))
+    ro, rl = _attn_ref("hca", q.f32, pool.f32, None, win.f32, win_pos0, W, sink, q_pos0, R, m=m,
+                       n_entries=n_entries)
+    assert rowwise_rel_err(host(out), ro) <= TOL_BF16
+    assert np.abs(host(lse) - rl).max() <= LSE_ATOL_BF16
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_attn_empty_key_set_is_sink_only(dt):
+    """No selected rows and no window: output 0, lse = sink."""
+    rng = np.random.default_rng(6)
+    H, D, R = (64, 512, 64) if dt == "bf16" else (4, 64, 16)
+    B, Tq, K = 2, 3, 16
+    q = synth.Tensor(rng.standard_normal((B, Tq, H, D)).astype(np.float32), dt)
+    pool = synth.Tensor(rng.standard_normal((B, 8, D)).astype(np.float32), dt)
+    sel = np.full((B, Tq, K), -1, np.int32)
+    sink = rng.standard_normal(H).astype(np.float32)
+    out, lse = L.csa_sparse_attn(dev(q), dev(pool), dev(sel), None, None, 0, dev(sink),
+                                 i64([5, 9]), rope_dims=R, want_lse=True)
+    assert torch.count_nonzero(out).item() == 0
+    assert np.allclose(host(lse), np.broadcast_to(sink, (B, Tq, H)), atol=1e-6)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_attn_duplicates_window_clip_and_window_only(dt):
+    """Duplicate selections count twice; window rows outside the buffer are
+    skipped; K = 0 attends to the window only."""
+    rng = np.random.default_rng(7)
+    H, D, R = (64, 512, 64) if dt == "bf16" else (4, 64, 16)
+    B, Tq, K, N, W = 1, 2, 6, 40, 8
+    q = synth.Tensor(rng.standard_normal((B, Tq, H, D)).astype(np.float32), dt)
+    pool = synth.Tensor(rng.standard_normal((B, N, D)).astype(np.float32), dt)
+    win = synth.Tensor(rng.standard_normal((B, 5, D)).astype(np.float32), dt)
+    sink = rng.standard_normal(H).astype(np.float32)
+    q_pos0, win_pos0 = np.array([150]), np.array([148])   # window wants 143..150/151
+    sel = np.array([[[3, 3, 3, 9, -1, 0], [1, 1, 2, 2, 5, 5]]], np.int32)
+    tol = TOL_BF16 if dt == "bf16" else TOL_F32
+    out, _ = L.csa_sparse_attn(dev(q), dev(pool), dev(sel), dev(win), i64(win_pos0), W, dev(sink),
+                               i64(q_pos0), rope_dims=R)
+    # the oracle needs every window row, so give it the clipped set explicitly
+    ro = np.zeros((B, Tq, H, D))
+    for t in range(Tq):
+        tp = 150 + t
+        rows = [pool.f32[0, s] for s in sel[0, t] if s >= 0]
+        rows += [win.f32[0, p - 148] for p in O.window_positions(tp, W) if 0 <= p - 148 < 5]
+        ro[0, t], _ = O.attend(q.f32[0, t], tp, np.array(rows), sink, 1 / math.sqrt(D), R)
+    assert rowwise_rel_err(host(out), ro) <= tol
+    # window only
+    sel0 = np.zeros((B, Tq, 0), np.int32)
+    out0, _ = L.csa_sparse_attn(dev(q), dev(pool), dev(sel0), dev(win), i64(win_pos0), W,
+                                dev(sink), i64(q_pos0), rope_dims=R)
+    for t in range(Tq):
+        tp = 150 + t
+        rows = [win.f32[0, p - 148] for p in O.window_positions(tp, W) if 0 <= p - 148 < 5]
+        ro[0, t], _ = O.attend(q.f32[0, t], tp, np.array(rows), sink, 1 / math.sqrt(D), R)
+    assert rowwise_rel_err(host(out0), ro) <= tol
+
+
+def test_attn_csa_with_all_visible_equals_hca_on_gpu():
+    rng = np.random.default_rng(8)
+    B, H, D, R, m, N, W = 2, 64, 512, 64, 4, 400, 128
+    q_pos0 = np.array([4 * N - 1, 4 * N - 1])
+    q = bf16_dev_from_f32(rng.standard_normal((B, 1, H, D)))
+    pool = bf16_dev_from_f32(rng.standard_normal((B, N, D)))
+    win = bf16_dev_from_f32(rng.standard_normal((B, W, D)))
+    sink = dev(rng.standard_normal(H).astype(np.float32))
+    sel = np.tile(np.arange(N, dtype=np.int32), (B, 1, 1))
+    a, la = L.csa_sparse_attn(q, pool, dev(sel), win, i64(q_pos0 - W + 1), W, sink, i64(q_pos0),
+                              rope_dims=R, want_lse=True)
+    h, lh = L.hca_attn(q, pool, i32([N, N]), m, win, i64(q_pos0 - W + 1), W, sink, i64(q_pos0),
+                       rope_dims=R, want_lse=True)
+    assert torch.equal(a, h) and torch.equal(la, lh)
+
+
+# ======================================================================
+# whole toy layer on the GPU, and determinism
+# ======================================================================
+def test_toy_layer_chain_on_gpu():
+    d = synth.toy(1)
+    m, R, W, K = d["m"], d["R"], d["W"], d["K"]
+    p0 = i64([0])
+    pool = L.csa_compress(dev(d["c_a"]), m, z_a=dev(d["z_a"]), c_b=dev(d["c_b"]), z_b=dev(d["z_b"]),
+                          bias_a=dev(d["bias_a"]), bias_b=dev(d["bias_b"]), gain=dev(d["gain"]),
+                          rope_dims=R, pos0=p0)
+    keys = L.csa_compress(dev(d["ic_a"]), m, z_a=dev(d["iz_a"]), c_b=dev(d["ic_b"]),
+                          z_b=dev(d["iz_b"]), bias_a=dev(d["ibias_a"]), bias_b=dev(d["ibias_b"]))
+    win = L.csa_compress(dev(d["kv"]), 1, gain=dev(d["gain_win"]), rope_dims=R, pos0=p0)
+    idx, _, _ = L.csa_index_topk(dev(d["q_idx"]), dev(d["w_idx"]), keys, i32(d["n_entries"]), p0,
+                                 K, m)
+    out, _ = L.csa_sparse_attn(dev(d["q"]), pool, idx, win, p0, W, dev(d["sink"]), p0, rope_dims=R)
+    rpool = O.csa_compress(d["c_a"].f32, d["z_a"].f32, d["bias_a"], m, c_b=d["c_b"].f32,
+                           z_b=d["z_b"].f32, bias_b=d["bias_b"], gain=d["gain"], rope_dims=R,
+                           pos0=[0])
+    rkeys = O.csa_compress(d["ic_a"].f32, d["iz_a"].f32, d["ibias_a"], m, c_b=d["ic_b"].f32,
+                           z_b=d["iz_b"].f32, bias_b=d["ibias_b"])
+    rwin = O.csa_compress(d["kv"].f32, None, None, 1, gain=d["gain_win"], rope_dims=R, pos0=[0])
+    ridx, rsc = O.csa_index_topk(d["q_idx"].f32, d["w_idx"], rkeys, d["n_entries"], [0], K, m)
+    gidx = host(idx)
+    for t in range(d["T"]):
+        check_band(gidx[0, t], ridx[0, t], rsc[0, t], O.visible_count(t, m, 64), K)
+    ro, _ = O.csa_sparse_attn(d["q"].f32, rpool, gidx, rwin, [0], W, d["sink"], [0],
+                              1 / math.sqrt(d["D"]), R)
+    assert rowwise_rel_err(host(out), ro) <= TOL_F32
+
+
+def test_decode_step_is_deterministic():
+    d = synth.decode("csa64k", 3, B=2, N=3000)
+    args = [dev(d["q_idx"]), dev(d["w_idx"]), dev(d["k_idx"]), i32(d["n_entries"]),
+            i64(d["q_pos0"]), d["K"], d["m"]]
+    a1 = L.csa_index_topk(*args)[0]
+    a2 = L.csa_index_topk(*args)[0]
+    assert torch.equal(a1, a2)
+    att = [dev(d["q"]), dev(d["pool"]), a1, dev(d["win"]), i64(d["win_pos0"]), d["W"],
+           dev(d["sink"]), i64(d["q_pos0"])]
+    o1, _ = L.csa_sparse_attn(*att, rope_dims=d["R"])
+    o2, _ = L.csa_sparse_attn(*att, rope_dims=d["R"])
+    assert torch.equal(o1, o2)

@@ -1,0 +1,141 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+include/csa.h declares, sizes workspaces, and rejects bad arguments before
+launching anything (no GPU needed; no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+LIB = os.path.join(ROOT, "long_context_sparse_11_amd", "libcsa.so")
+
+CSA_OK, CSA_ERR_ARG, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE = 0, -1, -2, -3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libcsa.so not built (run __graft_entry__.build())")
+    from long_context_sparse_11_amd import binding
+    return binding.lib()
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("csa_compress", "csa_index_topk", "csa_sparse_attn", "hca_attn",
+              "csa_index_topk_ws_bytes", "csa_attn_ws_bytes", "csa_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(LIB)
+    for n in declared_functions():
+        assert hasattr(raw, n), n
+
+
+def test_no_internal_symbols_leak():
+    out = os.popen(f"nm -D --defined-only {LIB}").read()
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(declared_functions()) <= exported
+    assert not [s for s in exported if s.startswith("_ZN3csa")]
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4):
+        assert lib.csa_status_string(s).decode().startswith("CSA_")
+    assert b"unknown" in lib.csa_status_string(7)
+
+
+def test_workspace_sizes(lib):
+    # scores + nothing else below the single-pass limit
+    assert lib.csa_index_topk_ws_bytes(4, 1, 64, 16384, 512) >= 4 * 16384 * 4
+    # two-level selection needs candidate lists too
+    small = lib.csa_index_topk_ws_bytes(8, 1, 64, 16384, 512)
+    big = lib.csa_index_topk_ws_bytes(8, 1, 64, 262144, 512)
+    assert big >= 8 * 262144 * 4 + 2 * 8 * 16 * 512 * 4 and big > small
+    assert lib.csa_index_topk_ws_bytes(0, 1, 64, 10, 5) == 0
+    # the MFMA attention splits a few long queries and needs partials
+    assert lib.csa_attn_ws_bytes(16, 1, 64, 512, 8320) > 0
+    assert lib.csa_attn_ws_bytes(1, 4096, 64, 512, 640) == 0   # many queries: no split
+    assert lib.csa_attn_ws_bytes(1, 256, 4, 64, 32) == 0       # generic path: no split
+
+
+P = ctypes.c_void_p(64)  # a non-null dummy: validation never dereferences it
+N = None
+
+
+def _compress(lib, **kw):
+    a = dict(dt=1, B=2, T=8, D=512, m=4, overlap=1, c_a=P, z_a=P, c_b=P, z_b=P, prev_c_b=N,
+             prev_z_b=N, bias_a=N, bias_b=N, gain=N, eps=1e-6, rope=0, base=10000.0, pos0=N,
+             out=P, ostride=0)
+    a.update(kw)
+    return lib.csa_compress(a["dt"], a["B"], a["T"], a["D"], a["m"], a["overlap"], a["c_a"],
+                            a["z_a"], a["c_b"], a["z_b"], a["prev_c_b"], a["prev_z_b"],
+                            a["bias_a"], a["bias_b"], a["gain"], a["eps"], a["rope"], a["base"],
+                            a["pos0"], a["out"], a["ostride"], N)
+
+
+def test_compress_validation(lib):
+    assert _compress(lib, dt=7) == CSA_ERR_ARG
+    assert _compress(lib, B=-1) == CSA_ERR_ARG
+    assert _compress(lib, B=0) == CSA_OK                 # nothing to do, nothing launched
+    assert _compress(lib, T=0) == CSA_OK
+    assert _compress(lib, c_b=N) == CSA_ERR_ARG          # overlap needs stream b
+    assert _compress(lib, overlap=0) == CSA_ERR_ARG      # stream b given without overlap
+    assert _compress(lib, prev_c_b=P) == CSA_ERR_ARG     # prev c without prev z
+    assert _compress(lib, rope=3) == CSA_ERR_ARG         # odd rope dims
+    assert _compress(lib, rope=64) == CSA_ERR_ARG        # rope without positions
+    assert _compress(lib, ostride=100) == CSA_ERR_ARG    # stride shorter than one batch
+    assert _compress(lib, D=384) == CSA_ERR_UNSUPPORTED  # not a power of two
+    assert _compress(lib, m=2048) == CSA_ERR_UNSUPPORTED
+
+
+def _index(lib, **kw):
+    a = dict(dt=1, B=2, Tq=1, Hi=64, Di=128, N=1000, K=512, m=4, ws=P, wsb=1 << 40)
+    a.update(kw)
+    return lib.csa_index_topk(a["dt"], a["B"], a["Tq"], a["Hi"], a["Di"], a["N"], a["K"], a["m"],
+                              P, P, P, P, P, P, N, N, a["ws"], a["wsb"], N)
+
+
+def test_index_validation(lib):
+    assert _index(lib, K=0) == CSA_ERR_ARG
+    assert _index(lib, m=0) == CSA_ERR_ARG
+    assert _index(lib, B=0) == CSA_OK
+    assert _index(lib, Hi=65) == CSA_ERR_UNSUPPORTED
+    assert _index(lib, K=5000) == CSA_ERR_UNSUPPORTED
+    assert _index(lib, ws=N) == CSA_ERR_WORKSPACE
+    assert _index(lib, wsb=16) == CSA_ERR_WORKSPACE
+
+
+def _attn(lib, fn="csa_sparse_attn", **kw):
+    a = dict(dt=1, B=4, Tq=1, H=64, D=512, R=64, base=10000.0, scale=0.044, N=16384, K=512,
+             L_win=128, W=128, ws=P, wsb=1 << 40, idx=P, n_ent=P, m=4)
+    a.update(kw)
+    if fn == "csa_sparse_attn":
+        return lib.csa_sparse_attn(a["dt"], a["B"], a["Tq"], a["H"], a["D"], a["R"], a["base"],
+                                   a["scale"], P, P, a["N"], a["idx"], a["K"], P, a["L_win"], P,
+                                   a["W"], P, P, P, N, a["ws"], a["wsb"], N)
+    return lib.hca_attn(a["dt"], a["B"], a["Tq"], a["H"], a["D"], a["R"], a["base"], a["scale"],
+                        P, P, a["N"], a["n_ent"], a["m"], P, a["L_win"], P, a["W"], P, P, P, N,
+                        a["ws"], a["wsb"], N)
+
+
+def test_attn_validation(lib):
+    assert _attn(lib, K=-1) == CSA_ERR_ARG
+    assert _attn(lib, idx=N) == CSA_ERR_ARG
+    assert _attn(lib, R=63) == CSA_ERR_ARG
+    assert _attn(lib, R=1024) == CSA_ERR_ARG
+    assert _attn(lib, D=2048) == CSA_ERR_UNSUPPORTED
+    assert _attn(lib, ws=N) == CSA_ERR_WORKSPACE          # 4 long queries are split
+    assert _attn(lib, B=0) == CSA_OK
+    assert _attn(lib, "hca_attn", m=0) == CSA_ERR_ARG
+    assert _attn(lib, "hca_attn", n_ent=N) == CSA_ERR_ARG
+    assert _attn(lib, "hca_attn", wsb=1) == CSA_ERR_WORKSPACE
