@@ -1,0 +1,453 @@
+"""Benchmark of one decode step of DeepSeek-V4 Compressed Sparse Attention on
+one MI355X.
+
+Default workload (the headline metric's configuration): CSA decode, batch 4,
+one new query per sequence at context 65,536 (16,384 compressed entries),
+64 heads x 512, RoPE 64, indexer 64 x 128, top-k 512, window 128.  A step is
+the whole hot path for that batch: compress the closing block (KV entry and
+indexer key, written in place into the caches), lightning-indexer scores +
+top-512 selection, sparse gather attention with the sink.  Other workloads
+(--workload): csa1m (batch 8, context 1,048,576), hca1m (HCA decode, batch
+16, context 1,048,576: compress + hca_attn), prefill (CSA chunk of 4,096
+queries on a 61,440-token prefix).
+
+Timing: inputs resident in HBM; the step is captured once per input copy in
+a HIP graph and replayed; enough copies of the inputs are rotated that no
+step finds its data in the 256 MB Infinity Cache.  Warmup steps are untimed,
+then exactly --steps steps are timed, bracketed by device synchronisation.
+Per-call durations come from HIP events on the library's stream.  The CPU
+oracle is timed on a bounded sample of the same workload (rank 0, N = 1).
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA/HCA attention decode tokens/s at 64K & 1M ctx; % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="csa64k", choices=["csa64k", "csa1m", "hca1m", "prefill"])
+    p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
+    p.add_argument("--no-cpu", action="store_true")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# workload setup
+# ---------------------------------------------------------------------------
+def upload(d, torch):
+    from long_context_sparse_11_amd.device import to_device
+    out = {}
+    for k, v in d.items():
+        if hasattr(v, "storage") or isinstance(v, np.ndarray):
+            out[k] = to_device(v)
+        else:
+            out[k] = v
+    return out
+
+
+class Step:
+    """Buffers of one input copy plus the closure that runs one step."""
+
+    def __init__(self, kind, g, L, torch):
+        self.kind, self.g, self.L, self.torch = kind, g, L, torch
+        B, D, m = g["B"], g["D"], g["m"]
+        self.B = B
+        if kind in ("csa64k", "csa1m"):
+            N, K, W = g["N"], g["K"], g["W"]
+            self.idx = torch.empty((B, 1, K), dtype=torch.int32, device="cuda")
+            self.out = torch.empty_like(g["q"])
+            self.ws_i = torch.empty(L.csa_index_topk_ws_bytes(B, 1, 64, N, K), dtype=torch.uint8,
+                                    device="cuda")
+            n = L.csa_attn_ws_bytes(B, 1, 64, D, K + W)
+            self.ws_a = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+        elif kind == "hca1m":
+            N, W = g["N"], g["W"]
+            self.out = torch.empty_like(g["q"])
+            n = L.csa_attn_ws_bytes(B, 1, 64, D, N + W)
+            self.ws_a = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+        else:  # prefill
+            Tq, N, K, W = g["Tq"], g["N"], g["K"], g["W"]
+            self.idx = torch.empty((1, Tq, K), dtype=torch.int32, device="cuda")
+            self.out = torch.empty_like(g["q"])
+            self.ws_i = torch.empty(L.csa_index_topk_ws_bytes(1, Tq, 64, N, K), dtype=torch.uint8,
+                                    device="cuda")
+            n = L.csa_attn_ws_bytes(1, Tq, 64, D, K + W)
+            self.ws_a = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+
+    def calls(self):
+        """The step as a list of (name, thunk) library calls."""
+        g, L = self.g, self.L
+        kind = self.kind
+        if kind in ("csa64k", "csa1m"):
+            N, D, Di, m = g["N"], g["D"], g["Di"], g["m"]
+            pool, kidx = g["pool"], g["k_idx"]
+            return [
+                ("compress", lambda: (
+                    L.csa_compress(g["c_a"], m, z_a=g["z_a"], c_b=g["c_b"], z_b=g["z_b"],
+                                   prev_c_b=g["prev_c_b"], prev_z_b=g["prev_z_b"],
+                                   bias_a=g["bias_a"], bias_b=g["bias_b"], gain=g["gain"],
+                                   rope_dims=g["R"], pos0=g["block_pos0"], out=pool[:, N - 1:],
+                                   out_bstride=N * D),
+                    L.csa_compress(g["ic_a"], m, z_a=g["iz_a"], c_b=g["ic_b"], z_b=g["iz_b"],
+                                   prev_c_b=g["iprev_c_b"], prev_z_b=g["iprev_z_b"],
+                                   bias_a=g["ibias_a"], bias_b=g["ibias_b"], out=kidx[:, N - 1:],
+                                   out_bstride=N * Di))),
+                ("index_topk", lambda: L.csa_index_topk(g["q_idx"], g["w_idx"], kidx,
+                                                        g["n_entries"], g["q_pos0"], g["K"], m,
+                                                        ws=self.ws_i, idx_out=self.idx)),
+                ("sparse_attn", lambda: L.csa_sparse_attn(g["q"], pool, self.idx, g["win"],
+                                                          g["win_pos0"], g["W"], g["sink"],
+                                                          g["q_pos0"], rope_dims=g["R"],
+                                                          out=self.out, ws=self.ws_a)),
+            ]
+        if kind == "hca1m":
+            N, D, m = g["N"], g["D"], g["m"]
+            pool = g["pool"]
+            return [
+                ("compress", lambda: L.csa_compress(g["c_a"], m, z_a=g["z_a"], bias_a=g["bias_a"],
+                                                    gain=g["gain"], rope_dims=g["R"],
+                                                    pos0=g["block_pos0"], out=pool[:, N - 1:],
+                                                    out_bstride=N * D)),
+                ("hca_attn", lambda: L.hca_attn(g["q"], pool, g["n_entries"], m, g["win"],
+                                                g["win_pos0"], g["W"], g["sink"], g["q_pos0"],
+                                                rope_dims=g["R"], out=self.out, ws=self.ws_a)),
+            ]
+        # prefill
+        N, D, Di, m, P = g["N"], g["D"], g["Di"], g["m"], g["prefix"]
+        pool, kidx = g["pool"], g["k_idx"]
+        return [
+            ("compress", lambda: (
+                L.csa_compress(g["c_a"][:, m:], m, z_a=g["z_a"][:, m:], c_b=g["c_b"][:, m:],
+                               z_b=g["z_b"][:, m:], prev_c_b=g["c_b"][:, :m],
+                               prev_z_b=g["z_b"][:, :m], bias_a=g["bias_a"], bias_b=g["bias_b"],
+                               gain=g["gain"], rope_dims=g["R"], pos0=g["chunk_pos0"],
+                               out=pool[:, P:]),
+                L.csa_compress(g["ic_a"][:, m:], m, z_a=g["iz_a"][:, m:], c_b=g["ic_b"][:, m:],
+                               z_b=g["iz_b"][:, m:], prev_c_b=g["ic_b"][:, :m],
+                               prev_z_b=g["iz_b"][:, :m], bias_a=g["ibias_a"],
+                               bias_b=g["ibias_b"], out=kidx[:, P:]))),
+            ("index_topk", lambda: L.csa_index_topk(g["q_idx"], g["w_idx"], kidx, g["n_entries"],
+                                                    g["q_pos0"], g["K"], m, ws=self.ws_i,
+                                                    idx_out=self.idx)),
+            ("sparse_attn", lambda: L.csa_sparse_attn(g["q"], pool, self.idx, g["win"],
+                                                      g["win_pos0"], g["W"], g["sink"],
+                                                      g["q_pos0"], rope_dims=g["R"], out=self.out,
+                                                      ws=self.ws_a)),
+        ]
+
+
+def make_inputs(kind):
+    from long_context_sparse_11_amd import synth
+    if kind == "prefill":
+        d = synth.prefill(0)
+    else:
+        d = synth.decode(kind, 0)
+    return d
+
+
+def prefill_buffers(g, torch):
+    """Pool / key caches of the prefill workload: cached prefix + room for the chunk."""
+    B, P, N, D, Di = 1, g["prefix"], g["N"], g["D"], g["Di"]
+    pool = torch.empty((B, N, D), dtype=torch.bfloat16, device="cuda")
+    pool[:, :P] = g.pop("pool_prefix")
+    kidx = torch.empty((B, N, Di), dtype=torch.bfloat16, device="cuda")
+    kidx[:, :P] = g.pop("kidx_prefix")
+    g["pool"], g["k_idx"] = pool, kidx
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work per step (what the method must move / compute)
+# ---------------------------------------------------------------------------
+def algorithmic(kind, d):
+    H, D, Hi, Di, K, W, m = d["H"], d["D"], d["Hi"], d["Di"], d["K"], d["W"], d["m"]
+    B, Tq = d["B"], d["Tq"]
+    bf = 2
+    out = {}
+    if kind in ("csa64k", "csa1m"):
+        N = d["N"]
+        comp = B * ((4 * m) * D * bf + D * bf + (4 * m) * Di * bf + Di * bf)
+        idx_bytes = B * (N * Di * bf + Hi * Di * bf + Hi * 4 + K * 4)
+        rows = min(K, N) + W
+        attn_bytes = B * (rows * D * bf + 2 * H * D * bf + K * 4)
+        out["bytes"] = {"compress": comp, "index_topk": idx_bytes, "sparse_attn": attn_bytes}
+        out["flops"] = {"index_topk": B * 2 * Hi * Di * N, "sparse_attn": B * 4 * H * D * rows}
+    elif kind == "hca1m":
+        N = d["N"]
+        comp = B * (2 * m * D * bf + D * bf)
+        rows = N + W
+        out["bytes"] = {"compress": comp, "hca_attn": B * (rows * D * bf + 2 * H * D * bf)}
+        out["flops"] = {"hca_attn": B * 4 * H * D * rows}
+    else:
+        N, P = d["N"], d["prefix"]
+        T = Tq + m
+        comp = 4 * T * D * bf + (Tq // m) * D * bf + 4 * T * Di * bf + (Tq // m) * Di * bf
+        p0 = P * m
+        vis = [min(N, (p0 + t + 1) // m) for t in range(Tq)]
+        idx_bytes = N * Di * bf + Tq * (Hi * Di * bf + Hi * 4 + K * 4)
+        attn_bytes = Tq * (2 * H * D * bf + K * 4) + (Tq + W - 1) * D * bf + N * D * bf
+        out["bytes"] = {"compress": comp, "index_topk": idx_bytes, "sparse_attn": attn_bytes}
+        out["flops"] = {"index_topk": 2 * Hi * Di * sum(vis),
+                        "sparse_attn": 4 * H * D * (K + W) * Tq}
+    return out
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample of the same step)
+# ---------------------------------------------------------------------------
+def cpu_baseline(kind, d, budget_s):
+    from long_context_sparse_11_amd.synth import bf16_to_f32
+    from oracle import csa_oracle as O
+
+    def rows_of(t, b, sel):  # float32 rows of one sequence, converted on demand
+        return bf16_to_f32(t.bits[b][sel]) if t.dt == "bf16" else t.f32[b][sel]
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    B, Tq = d["B"], d["Tq"]
+    scale = 1.0 / math.sqrt(d["D"])
+    done = 0
+    t0 = time.perf_counter()
+    if kind == "prefill":
+        # compress the chunk once, then queries one at a time
+        m = d["m"]
+        pool = np.concatenate([d["pool_prefix"].f32[0], O.compress(
+            d["c_a"].f32[0, m:], d["z_a"].f32[0, m:], d["bias_a"], m, c_b=d["c_b"].f32[0, m:],
+            z_b=d["z_b"].f32[0, m:], bias_b=d["bias_b"], prev_c_b=d["c_b"].f32[0, :m],
+            prev_z_b=d["z_b"].f32[0, :m], gain=d["gain"], rope_dims=d["R"],
+            pos0=int(d["chunk_pos0"][0]))])
+        keys = np.concatenate([d["kidx_prefix"].f32[0], O.compress(
+            d["ic_a"].f32[0, m:], d["iz_a"].f32[0, m:], d["ibias_a"], m, c_b=d["ic_b"].f32[0, m:],
+            z_b=d["iz_b"].f32[0, m:], bias_b=d["ibias_b"], prev_c_b=d["ic_b"].f32[0, :m],
+            prev_z_b=d["iz_b"].f32[0, :m])])
+        t = 0
+        while time.perf_counter() - t0 < budget_s and t < Tq:
+            tp = int(d["q_pos0"][0]) + t
+            nv = O.visible_count(tp, m, d["N"])
+            s = O.index_scores(d["q_idx"].f32[0, t], d["w_idx"][0, t], keys[:nv]).astype(np.float32)
+            sel = O.select_topk(s, nv, d["K"])
+            rows = np.concatenate([pool[[v for v in sel if v >= 0]],
+                                   d["win"].f32[0][[p - int(d["win_pos0"][0]) for p in O.window_positions(tp, d["W"])]]])
+            O.attend(d["q"].f32[0, t], tp, rows, d["sink"], scale, d["R"])
+            t += 1
+            done += 1
+        sample = f"chunk compress + {done} of {Tq} queries"
+    else:
+        b = 0
+        while time.perf_counter() - t0 < budget_s or done == 0:
+            bb = b % B
+            m = d["m"]
+            tp = int(d["q_pos0"][bb])
+            kv = O.compress(d["c_a"].f32[bb], d["z_a"].f32[bb], d["bias_a"], m,
+                            c_b=None if kind == "hca1m" else d["c_b"].f32[bb],
+                            z_b=None if kind == "hca1m" else d["z_b"].f32[bb],
+                            bias_b=d.get("bias_b"),
+                            prev_c_b=None if kind == "hca1m" else d["prev_c_b"].f32[bb],
+                            prev_z_b=None if kind == "hca1m" else d["prev_z_b"].f32[bb],
+                            gain=d["gain"], rope_dims=d["R"], pos0=int(d["block_pos0"][bb]))
+            win = d["win"].f32[bb]
+            wr = [p - int(d["win_pos0"][bb]) for p in O.window_positions(tp, d["W"])]
+            if kind == "hca1m":
+                nv = O.visible_count(tp, m, d["N"])
+                pool = rows_of(d["pool"], bb, slice(0, nv)).astype(np.float64)
+                pool[-1] = kv[0]
+                rows = np.concatenate([pool, win[wr]])
+            else:
+                O.compress(d["ic_a"].f32[bb], d["iz_a"].f32[bb], d["ibias_a"], m,
+                           c_b=d["ic_b"].f32[bb], z_b=d["iz_b"].f32[bb], bias_b=d["ibias_b"],
+                           prev_c_b=d["iprev_c_b"].f32[bb], prev_z_b=d["iprev_z_b"].f32[bb])
+                nv = O.visible_count(tp, m, d["N"])
+                s = O.index_scores(d["q_idx"].f32[bb, 0], d["w_idx"][bb, 0],
+                                   rows_of(d["k_idx"], bb, slice(0, nv))).astype(np.float32)
+                sel = O.select_topk(s, nv, d["K"])
+                rows = np.concatenate([rows_of(d["pool"], bb, [v for v in sel if v >= 0]), win[wr]])
+            O.attend(d["q"].f32[bb, 0], tp, rows, d["sink"], scale, d["R"])
+            done += 1
+            b += 1
+        sample = f"{done} decode queries (full step per query) of batch {B}"
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": sample, "seconds": round(el, 2),
+            "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
+# ---------------------------------------------------------------------------
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {a.gpus}); the path shards by sequence "
+              "across GPUs with no exchange, so the whole-job rate is N times this line", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import long_context_sparse_11_amd as L
+    L.lib()
+    if not torch.cuda.is_available():
+        print("no GPU", file=sys.stderr)
+        sys.exit(1)
+
+    kind = a.workload
+    d = make_inputs(kind)
+    work = algorithmic(kind, d)
+    step_bytes = sum(work["bytes"].values())
+    n_copies = max(1, min(64, math.ceil(2 * MALL_BYTES / max(step_bytes, 1)) + 1))
+
+    # one copy uploaded from host, the rest cloned on the device
+    base = upload({k: v for k, v in d.items() if k not in ("name", "dt")}, torch)
+    if kind == "prefill":
+        prefill_buffers(base, torch)
+    copies = [base]
+    big = [k for k, v in base.items() if isinstance(v, torch.Tensor) and v.numel() * v.element_size() > 4096]
+    for _ in range(n_copies - 1):
+        c = dict(base)
+        for k in big:
+            c[k] = base[k].clone()
+        copies.append(c)
+    steps = [Step(kind, c, L, torch) for c in copies]
+
+    # calibration copy kernel of known size (also flushes the Infinity Cache)
+    cal_src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    names = [n for n, _ in steps[0].calls()]
+    use_graph = not a.no_graph
+    # eager warm-up (loads the code objects)
+    for st in steps[:2]:
+        for _, f in st.calls():
+            f()
+    torch.cuda.synchronize()
+    graphs, call_graphs = [], []
+    if use_graph:
+        # one graph per input copy for the whole step, and one per library call
+        for st in steps:
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gph):
+                for _, f in st.calls():
+                    f()
+            graphs.append(gph)
+            per = []
+            for _, f in st.calls():
+                cg = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(cg):
+                    f()
+                per.append(cg)
+            call_graphs.append(per)
+        torch.cuda.synchronize()
+
+    def run_step(i):
+        if use_graph:
+            graphs[i % n_copies].replay()
+        else:
+            for _, f in steps[i % n_copies].calls():
+                f()
+
+    for i in range(a.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        run_step(a.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / a.steps
+    tokens = d["B"] * d["Tq"]
+    value = tokens * a.steps / elapsed
+
+    # device time per step and per library call: HIP events on the library's
+    # stream around graph replays, queued behind a spin kernel so the device
+    # never waits for the host between them
+    reps = min(a.steps, 100)
+
+    def timed(thunks):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in thunks]
+        torch.cuda._sleep(20_000_000)
+        for (e0, e1), th in zip(evs, thunks):
+            e0.record(stream)
+            th()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]  # us
+
+    dev_step_us = float(np.median(timed([(lambda i=i: run_step(i)) for i in range(reps)])))
+    per_call = {}
+    for k, n in enumerate(names):
+        if use_graph:
+            th = [(lambda i=i, k=k: call_graphs[i % n_copies][k].replay()) for i in range(reps)]
+        else:
+            th = [(lambda i=i, k=k: steps[i % n_copies].calls()[k][1]()) for i in range(reps)]
+        per_call[n] = float(np.median(timed(th)))
+    call_us = per_call
+
+    # roofline of the dominant call: the one moving the most algorithmic bytes
+    if kind == "prefill":
+        dom = max(work["flops"], key=lambda n: work["flops"][n])
+    else:
+        dom = max(work["bytes"], key=lambda n: work["bytes"][n])
+    dom_bytes = work["bytes"][dom]
+    dom_flops = work["flops"].get(dom, 0)
+    if kind == "prefill":
+        ach = work["flops"][dom] / (call_us[dom] * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        ach = dom_bytes / (call_us[dom] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    roof["kernel"] = dom
+    roof["algorithmic_bytes"] = int(dom_bytes)
+    roof["algorithmic_flops"] = int(dom_flops)
+    roof["avg_us"] = round(call_us[dom], 2)
+
+    cpu = None
+    if not a.no_cpu:
+        cpu = cpu_baseline(kind, d, a.cpu_seconds)
+
+    cfgs = {
+        "csa64k": dict(workload="csa_decode_64k", batch=4, context=65536, entries=16384),
+        "csa1m": dict(workload="csa_decode_1m", batch=8, context=1048576, entries=262144),
+        "hca1m": dict(workload="hca_decode_1m", batch=16, context=1048576, entries=8192),
+        "prefill": dict(workload="csa_prefill_4k_on_60k", batch=1, queries=4096, context=65536,
+                        entries=16384),
+    }[kind]
+    cfgs.update(heads=64, head_dim=512, rope_dims=64, index_heads=64, index_dim=128,
+                index_topk=512, window=128, m=d["m"], step_calls=names,
+                graph=use_graph, input_copies=n_copies)
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic", "config": cfgs, "roofline": roof, "cpu_baseline": cpu,
+        "device_us_per_step": round(dev_step_us, 2),
+        "per_call_us": {k: round(v, 2) for k, v in call_us.items()},
+        "step_algorithmic_bytes": int(step_bytes),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

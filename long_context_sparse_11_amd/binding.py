@@ -122,6 +122,13 @@ def csa_compress(c_a, m, *, z_a=None, c_b=None, z_b=None, prev_c_b=None, prev_z_
     n_out = -(-T // m)
     if out is None:
         out = torch.empty((B, n_out, D), dtype=c_a.dtype, device=c_a.device)
+    else:  # may be a view into a larger cache: [B, n_out, D] with batch stride out_bstride
+        bs = out_bstride if out_bstride else n_out * D
+        if (tuple(out.shape) != (B, n_out, D) or out.dtype != c_a.dtype or not out.is_cuda
+                or out.stride(2) != 1 or (n_out > 1 and out.stride(1) != D)
+                or (B > 1 and out.stride(0) != bs)):
+            raise ValueError("out must be [B, ceil(T/m), D] with row stride D and batch stride "
+                             "out_bstride")
     st = lib().csa_compress(_dt(c_a), B, T, D, m, int(overlap), _p(c_a), _p(z_a), _p(c_b), _p(z_b),
                             _p(prev_c_b), _p(prev_z_b), _p(bias_a), _p(bias_b), _p(gain),
                             float(eps), int(rope_dims), float(rope_base), _p(pos0), _p(out),

@@ -4,6 +4,8 @@
 #include "../../include/csa.h"
 #include "kernels.h"
 
+#include <math.h>
+
 #define CSA_EXPORT extern "C" __attribute__((visibility("default")))
 
 using namespace csa;
@@ -53,8 +55,9 @@ CSA_EXPORT int csa_compress(int dt, int B, int T, int D, int m, int overlap, con
   const int n_out = (T + m - 1) / m;
   if (out_bstride != 0 && out_bstride < (int64_t)n_out * D) return CSA_ERR_ARG;
   if (m > 1024 || !is_pow2(D) || D > 1024 || D < (dt == CSA_BF16 ? 8 : 4)) return CSA_ERR_UNSUPPORTED;
+  const double theta1 = rope_dims > 0 ? pow(rope_base, -2.0 / rope_dims) : 0.0;
   CompressArgs a{dt, B, T, D, m, overlap ? 1 : 0, n_out, c_a, z_a, c_b, z_b, prev_c_b, prev_z_b,
-                 bias_a, bias_b, gain, eps, rope_dims, rope_base, pos0, out, out_bstride};
+                 bias_a, bias_b, gain, eps, rope_dims, theta1, pos0, out, out_bstride};
   return status_of(launch_compress(a, (hipStream_t)stream));
 }
 
@@ -134,7 +137,8 @@ CSA_EXPORT size_t csa_attn_ws_bytes(int B, int Tq, int H, int D, int keys_per_qu
 
 namespace {
 
-int attn_common(AttnArgs& a, int keys_per_query, void* ws, size_t ws_bytes, hipStream_t s) {
+int attn_common(AttnArgs& a, double rope_base, int keys_per_query, void* ws, size_t ws_bytes,
+                hipStream_t s) {
   if (a.dt != CSA_F32 && a.dt != CSA_BF16) return CSA_ERR_ARG;
   if (a.B < 0 || a.Tq < 0 || a.H <= 0 || a.D <= 0 || a.N_cap < 0 || a.W < 0 || a.L_win < 0)
     return CSA_ERR_ARG;
@@ -142,8 +146,9 @@ int attn_common(AttnArgs& a, int keys_per_query, void* ws, size_t ws_bytes, hipS
   if (!a.q || !a.sink || !a.q_pos0 || !a.out) return CSA_ERR_ARG;
   if (a.N_cap > 0 && !a.pool) return CSA_ERR_ARG;
   if (a.W > 0 && a.L_win > 0 && (!a.win || !a.win_pos0)) return CSA_ERR_ARG;
-  if (a.R < 0 || a.R > a.D || (a.R & 1) || (a.R > 0 && !(a.rope_base > 0.0))) return CSA_ERR_ARG;
+  if (a.R < 0 || a.R > a.D || (a.R & 1) || (a.R > 0 && !(rope_base > 0.0))) return CSA_ERR_ARG;
   if (a.D > 1024 || a.H > 128 || (a.D & 1)) return CSA_ERR_UNSUPPORTED;
+  a.rope_theta1 = a.R > 0 ? pow(rope_base, -2.0 / a.R) : 0.0;
   if (attn_uses_mfma(a.dt, a.H, a.D, a.R)) {
     a.splits = attn_splits(a.dt, a.B, a.Tq, a.H, a.D, keys_per_query);
     if (a.splits > 1) {
@@ -170,12 +175,12 @@ CSA_EXPORT int csa_sparse_attn(int dt, int B, int Tq, int H, int D, int rope_dim
   if (K > 0 && !idx) return CSA_ERR_ARG;
   AttnArgs a{};
   a.dt = dt; a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.R = rope_dims;
-  a.rope_base = rope_base; a.scale = scale;
+  a.scale = scale;
   a.q = q; a.pool = pool; a.N_cap = N_cap; a.csa = 1; a.idx = idx; a.K = K;
   a.n_entries = nullptr; a.m = 1;
   a.win = win; a.L_win = L_win; a.win_pos0 = win_pos0; a.W = W;
   a.sink = sink; a.q_pos0 = q_pos0; a.out = out; a.lse = lse;
-  return attn_common(a, K + W, ws, ws_bytes, (hipStream_t)stream);
+  return attn_common(a, rope_base, K + W, ws, ws_bytes, (hipStream_t)stream);
 }
 
 CSA_EXPORT int hca_attn(int dt, int B, int Tq, int H, int D, int rope_dims, double rope_base,
@@ -186,10 +191,10 @@ CSA_EXPORT int hca_attn(int dt, int B, int Tq, int H, int D, int rope_dims, doub
   if (m <= 0 || !n_entries) return CSA_ERR_ARG;
   AttnArgs a{};
   a.dt = dt; a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.R = rope_dims;
-  a.rope_base = rope_base; a.scale = scale;
+  a.scale = scale;
   a.q = q; a.pool = pool; a.N_cap = N_cap; a.csa = 0; a.idx = nullptr; a.K = 0;
   a.n_entries = n_entries; a.m = m;
   a.win = win; a.L_win = L_win; a.win_pos0 = win_pos0; a.W = W;
   a.sink = sink; a.q_pos0 = q_pos0; a.out = out; a.lse = lse;
-  return attn_common(a, N_cap + W, ws, ws_bytes, (hipStream_t)stream);
+  return attn_common(a, rope_base, N_cap + W, ws, ws_bytes, (hipStream_t)stream);
 }

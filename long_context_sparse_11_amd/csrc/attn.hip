@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void attn_generic(AttnArgs a) {
     cs[k] = 1.f;
     sn[k] = 0.f;
     if (rot[k]) {
-      rope_cos_sin(tpos, (c - (D - R)) >> 1, R, a.rope_base, cs[k], sn[k]);
+      rope_cos_sin(tpos, (c - (D - R)) >> 1, a.rope_theta1, cs[k], sn[k]);
       const float x0 = q0[k], x1 = q1[k];
       q0[k] = x0 * cs[k] - x1 * sn[k];
       q1[k] = x0 * sn[k] + x1 * cs[k];
@@ -161,15 +161,26 @@ __global__ __launch_bounds__(256) void attn_generic(AttnArgs a) {
 
 // --------------------------------------------------------------------- MFMA
 constexpr int kAtRows = 32;       // rows per tile
-constexpr int kRtPitch = 136;     // bf16 per LDS row of the transposition copy (272 B)
+constexpr int kRtPitch = 128;     // bf16 per LDS row of a wave's row copy (256 B, swizzled)
+
+// The wave's copy of a tile row (its 256-byte slice, sixteen 16-byte chunks)
+// stores chunk c at position c ^ rt_swz(row): the 16-byte stash writes of 16
+// consecutive rows and the 8-byte transposing reads of 4 consecutive rows
+// then fall on distinct LDS banks.
+__device__ __forceinline__ int rt_swz(int row) { return (4 * row + (row >> 2)) & 15; }
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr;
 constexpr int kAtD = 512;
 constexpr int kAtH = 64;
+constexpr int kAtMaxSplitRows = 4096;  // rows of one key split (LDS index stage)
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_mfma(AttnArgs a) {
   __shared__ float s_cos[kAtD / 2], s_sin[kAtD / 2];
   __shared__ __attribute__((aligned(16))) f32x4_t sx[2][4][2][4][64];  // [buf][wave][ht][rq][lane]
   __shared__ __attribute__((aligned(16))) bf16_t rt[4][kAtRows * kRtPitch];
+  __shared__ int32_t s_idx[kAtMaxSplitRows];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -180,13 +191,19 @@ void attn_mfma(AttnArgs a) {
   const int R = a.R;
   const int rope0 = kAtD - R;
 
-  for (int p = tid; p < R / 2; p += 256) rope_cos_sin(tpos, p, R, a.rope_base, s_cos[p], s_sin[p]);
+  for (int p = tid; p < R / 2; p += 256) rope_cos_sin(tpos, p, a.rope_theta1, s_cos[p], s_sin[p]);
 
   const KeyRange kr = key_range(a, b, qi, tpos);
   const int L = kr.nsel + kr.nwin;
   const int per = (((L + S - 1) / S) + kAtRows - 1) / kAtRows * kAtRows;
   const int start = min(L, sp * per);
   const int end = min(L, start + per);
+  // the split's selected pool indices, staged once (row addresses then need
+  // no dependent global load inside the tile loop)
+  if (a.csa) {
+    const int sel_end = min(end, kr.nsel);
+    for (int jj = start + tid; jj < sel_end; jj += 256) s_idx[jj - start] = a.idx[(int64_t)qi * a.K + jj];
+  }
   __syncthreads();
 
   // query operand, rotated at +tpos: lane (g, j) holds head j (+32) at
@@ -229,12 +246,24 @@ void attn_mfma(AttnArgs a) {
   const float sl2 = a.scale * kLog2e;
   bf16_t* myrt = rt[wave];
 
-  bf16x8_t ra[8], rn[8];
-  bool va = false, vn = false;
+  bf16x8_t ra[8];
+  bool va = false;
   auto load_rows = [&](int j0, bf16x8_t(&dst)[8], bool& valid) {
     const int jj = j0 + j;
-    bool rv;
-    const bf16_t* p = key_row<bf16_t>(a, b, qi, kr, jj < end ? jj : start, rv);
+    const int jr = jj < end ? jj : start;
+    const bf16_t* p;
+    bool rv = true;
+    if (jr < kr.nsel) {
+      int srow = jr;
+      if (a.csa) {
+        srow = s_idx[jr - start];
+        rv = srow >= 0 && srow < a.N_cap;
+        if (!rv) srow = 0;
+      }
+      p = (const bf16_t*)a.pool + ((int64_t)b * a.N_cap + srow) * kAtD;
+    } else {
+      p = (const bf16_t*)a.win + ((int64_t)b * a.L_win + kr.win_r0 + (jr - kr.nsel)) * kAtD;
+    }
     valid = rv && jj < end;
     p += fbase;
 #pragma unroll
@@ -244,9 +273,6 @@ void attn_mfma(AttnArgs a) {
   int buf = 0;
   if (start < end) load_rows(start, ra, va);
   for (int j0 = start; j0 < end; j0 += kAtRows) {
-    const bool more = j0 + kAtRows < end;
-    if (more) load_rows(j0 + kAtRows, rn, vn);
-
     // partial logits over this wave's 128 channels
     f32x16_t s0 = {}, s1 = {};
 #pragma unroll
@@ -257,13 +283,16 @@ void attn_mfma(AttnArgs a) {
     // wave-private copy of the rows for the transposed PV operand
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      *reinterpret_cast<bf16x8_t*>(&myrt[j * kRtPitch + g * 64 + 8 * s]) = ra[s];
+      *reinterpret_cast<bf16x8_t*>(&myrt[j * kRtPitch + 8 * ((8 * g + s) ^ rt_swz(j))]) = ra[s];
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       sx[buf][wave][0][rq][lane] = f32x4_t{s0[4 * rq], s0[4 * rq + 1], s0[4 * rq + 2], s0[4 * rq + 3]};
       sx[buf][wave][1][rq][lane] = f32x4_t{s1[4 * rq], s1[4 * rq + 1], s1[4 * rq + 2], s1[4 * rq + 3]};
     }
     const uint64_t vmask = __ballot(va);
+    // the rows now live in LDS: reuse their registers for the next tile's
+    // loads, which then overlap this tile's softmax and PV
+    if (j0 + kAtRows < end) load_rows(j0 + kAtRows, ra, va);
     __syncthreads();
 
     float p[2][16];
@@ -283,31 +312,44 @@ void attn_mfma(AttnArgs a) {
       }
     buf ^= 1;
 
+    // Online softmax with a lazily moved reference: a head's running max
+    // only moves when a tile exceeds it by more than 2^8 (log2 units), so
+    // exp2(s - mrun) stays below 256 and the accumulator is rescaled only on
+    // those (rare) tiles.  The first tile with a valid row always moves it.
+    float tm[2];
+    bool move = false;
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      float x = p[ht][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) x = fmaxf(x, p[ht][r]);
+      tm[ht] = fmaxf(x, __shfl_xor(x, 32));
+      move |= tm[ht] > mrun[ht] + 8.f;
+    }
+    if (__ballot(move)) {
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        const float mnew = fmaxf(mrun[ht], tm[ht]);
+        if (mnew > mrun[ht]) {
+          const float alpha = exp2f(mrun[ht] - mnew);
+          lrun[ht] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) oacc[dt][ht] *= alpha;
+          mrun[ht] = mnew;
+        }
+      }
+    }
     bf16x8_t pb[2][2];
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
-      float tm = p[ht][0];
+      const bool none = mrun[ht] == -INFINITY;  // no valid row seen yet
 #pragma unroll
-      for (int r = 1; r < 16; ++r) tm = fmaxf(tm, p[ht][r]);
-      tm = fmaxf(tm, __shfl_xor(tm, 32));
-      const float mnew = fmaxf(mrun[ht], tm);
-      float alpha = 1.f;
-      if (mnew == -INFINITY) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[ht][r] = 0.f;
-      } else {
-        alpha = exp2f(mrun[ht] - mnew);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[ht][r] = exp2f(p[ht][r] - mnew);
-      }
+      for (int r = 0; r < 16; ++r) p[ht][r] = none ? 0.f : exp2f(p[ht][r] - mrun[ht]);
       float rs = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) rs += p[ht][r];
       rs += __shfl_xor(rs, 32);
-      lrun[ht] = lrun[ht] * alpha + rs;
-      mrun[ht] = mnew;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) oacc[dt][ht] *= alpha;
+      lrun[ht] += rs;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         u32x4_t pk;
@@ -319,32 +361,32 @@ void attn_mfma(AttnArgs a) {
       }
     }
 
-    // O^T[channel][head] += R^T[channel][row] P^T[row][head]
+    // O^T[channel][head] += R^T[channel][row] P^T[row][head].  The R^T
+    // operand comes from ds_read_b64_tr_b16: in each 16-lane group, lane c
+    // points at 4 consecutive channels of row (c / 4) of a 4-row block and
+    // lane i receives channel i of all 4 rows, i.e. 4 consecutive K slots of
+    // its own M row; two reads (rows +0..3 and +8..11) make one operand.
+    const int tr_row = 4 * g + ((lane & 15) >> 2);
+    const int tr_q = lane & 3;
+    const int tr_h = (lane >> 4) & 1;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const int col = dt * 32 + j;
+      const int chunk = dt * 4 + 2 * tr_h + (tr_q >> 1);   // 16-byte chunk of the channel
+      const int sub = 4 * (tr_q & 1);                       // bf16 offset inside it
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int n0 = 16 * ks + 4 * g;
-        uint32_t w4[4];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const uint32_t lo = myrt[(n0 + 2 * e) * kRtPitch + col];
-          const uint32_t hi = myrt[(n0 + 2 * e + 1) * kRtPitch + col];
-          w4[e] = lo | (hi << 16);
-          const uint32_t lo2 = myrt[(n0 + 8 + 2 * e) * kRtPitch + col];
-          const uint32_t hi2 = myrt[(n0 + 8 + 2 * e + 1) * kRtPitch + col];
-          w4[2 + e] = lo2 | (hi2 << 16);
-        }
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, u32x4_t{w4[0], w4[1], w4[2], w4[3]});
+        const int r0 = 16 * ks + tr_row, r1 = r0 + 8;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_ptr)(&myrt[r0 * kRtPitch + 8 * (chunk ^ rt_swz(r0)) + sub]));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_ptr)(&myrt[r1 * kRtPitch + 8 * (chunk ^ rt_swz(r1)) + sub]));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, u32x4_t{l2.x, l2.y, h2.x, h2.y});
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht)
           oacc[dt][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ht][ks], oacc[dt][ht], 0, 0, 0);
       }
     }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) ra[s] = rn[s];
-    va = vn;
   }
 
   // ---- epilogue
@@ -406,46 +448,69 @@ void attn_mfma(AttnArgs a) {
 
 // Merge of the key-range splits: partial maxima are in log2 units of the
 // scaled logits, partial sums and outputs unnormalised.  grid (B*Tq, H),
-// 128 threads, 4 channels per thread per step.
+// 128 threads, 4 channels per thread per step.  The per-split weights are
+// computed once into LDS; the split loop is unrolled so the loads of several
+// splits are in flight together.
+constexpr int kMaxSplits = 256;
+
 template <typename T>
 __global__ __launch_bounds__(128) void attn_combine(AttnArgs a) {
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_lse;
   const int qi = blockIdx.x, h = blockIdx.y;
   const int S = a.splits, D = a.D, R = a.R;
   const int b = qi / a.Tq, t = qi - b * a.Tq;
   const int64_t tpos = a.q_pos0[b] + t;
-  const float skl2 = a.sink[h] * kLog2e;
   const int64_t slot0 = (int64_t)qi * S * a.H + h;
-  float M = skl2;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_ml[2 * (slot0 + (int64_t)s * a.H)]);
-  float Ls = exp2f(skl2 - M);
-  for (int s = 0; s < S; ++s) {
-    const int64_t sl = slot0 + (int64_t)s * a.H;
-    Ls += a.part_ml[2 * sl + 1] * exp2f(a.part_ml[2 * sl] - M);
-  }
-  if (threadIdx.x == 0 && a.lse) a.lse[(int64_t)qi * a.H + h] = (M + log2f(Ls)) * kLn2;
-  const float inv = 1.f / Ls;
-  for (int c = threadIdx.x * 4; c < D; c += 512) {
-    float o[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < S; ++s) {
-      const int64_t sl = slot0 + (int64_t)s * a.H;
-      const float w = exp2f(a.part_ml[2 * sl] - M) * inv;
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(a.part_o + sl * D + c);
+  if (threadIdx.x < 64) {  // one wave merges the (max, sum) pairs
+    const int lane = threadIdx.x;
+    const float skl2 = a.sink[h] * kLog2e;
+    float M = skl2;
+    for (int s = lane; s < S; s += 64) M = fmaxf(M, a.part_ml[2 * (slot0 + (int64_t)s * a.H)]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] += w * v[e];
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float Ls = 0.f;
+    for (int s = lane; s < S; s += 64) {
+      const int64_t sl = slot0 + (int64_t)s * a.H;
+      Ls += a.part_ml[2 * sl + 1] * exp2f(a.part_ml[2 * sl] - M);
     }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) Ls += __shfl_xor(Ls, off);
+    Ls += exp2f(skl2 - M);
+    const float inv = 1.f / Ls;
+    for (int s = lane; s < S; s += 64)
+      s_w[s] = exp2f(a.part_ml[2 * (slot0 + (int64_t)s * a.H)] - M) * inv;
+    if (lane == 0) s_lse = (M + log2f(Ls)) * kLn2;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && a.lse) a.lse[(int64_t)qi * a.H + h] = s_lse;
+  for (int c = threadIdx.x * 4; c < D; c += 512) {
+    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+    int s = 0;
+    for (; s + 8 <= S; s += 8) {
+      f32x4_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = *reinterpret_cast<const f32x4_t*>(a.part_o + (slot0 + (int64_t)(s + u) * a.H) * D + c);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) o += s_w[s + u] * v[u];
+    }
+    for (; s < S; ++s)
+      o += s_w[s] * *reinterpret_cast<const f32x4_t*>(a.part_o + (slot0 + (int64_t)s * a.H) * D + c);
+    float r[4] = {o[0], o[1], o[2], o[3]};
 #pragma unroll
     for (int e = 0; e < 4; e += 2) {
       if (c + e >= D - R) {
         float cs, sn;
-        rope_cos_sin(tpos, (c + e - (D - R)) >> 1, R, a.rope_base, cs, sn);
-        const float x0 = o[e], x1 = o[e + 1];
-        o[e] = x0 * cs + x1 * sn;
-        o[e + 1] = -x0 * sn + x1 * cs;
+        rope_cos_sin(tpos, (c + e - (D - R)) >> 1, a.rope_theta1, cs, sn);
+        const float x0 = r[e], x1 = r[e + 1];
+        r[e] = x0 * cs + x1 * sn;
+        r[e + 1] = -x0 * sn + x1 * cs;
       }
     }
     T* op = (T*)a.out + ((int64_t)qi * a.H + h) * D + c;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) Elem<T>::put(op + e, o[e]);
+    for (int e = 0; e < 4; ++e) Elem<T>::put(op + e, r[e]);
   }
 }
 
@@ -458,10 +523,11 @@ int attn_splits(int dt, int B, int Tq, int H, int D, int keys_per_query) {
   if (!(dt == 1 && H == kAtH && D == kAtD)) return 1;
   const int64_t q = (int64_t)B * Tq;
   const int tiles = (keys_per_query + kAtRows - 1) / kAtRows;
-  if (q >= 512 || tiles < 4) return 1;
-  int s = (int)((512 + q - 1) / q);
-  s = min(s, tiles / 2);
-  return max(s, 1);
+  int s = 1;
+  if (q < 256 && tiles >= 4) s = min((int)((256 + q - 1) / q), tiles / 2);
+  // a split holds at most kAtMaxSplitRows rows (its index stage lives in LDS)
+  s = max(s, (keys_per_query + kAtMaxSplitRows - 1) / kAtMaxSplitRows);
+  return min(s, kMaxSplits);
 }
 
 size_t attn_ws_bytes(int dt, int B, int Tq, int H, int D, int keys_per_query) {

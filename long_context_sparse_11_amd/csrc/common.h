@@ -94,17 +94,32 @@ struct Elem<bf16_t> {
 };
 
 // ---------------------------------------------------------------------------
-// RoPE angle of pair j (of R/2) at an absolute position, float64 throughout:
-// theta_j = base^(-2j/R), phi = pos * theta_j.
+// RoPE angle of pair j (of R/2) at an absolute position.  theta_j =
+// base^(-2j/R) = theta1^j with theta1 = base^(-2/R) computed once on the host
+// (float64 libm); theta1^j by binary powering in float64 (relative error
+// ~j * 1e-16).  phi = pos * theta_j in float64, reduced modulo 2*pi in
+// float64 (2*pi split into a double and its remainder, Cody-Waite style,
+// exact to far below float precision for |phi| < 2^40); sin/cos of the
+// reduced angle in float32.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void rope_cos_sin(int64_t pos, int j, int R, double base, float& c,
-                                             float& s) {
-  const double theta = pow(base, -2.0 * (double)j / (double)R);
-  const double phi = (double)pos * theta;
-  double sd, cd;
-  sincos(phi, &sd, &cd);
-  c = (float)cd;
-  s = (float)sd;
+__device__ __forceinline__ double rope_theta(double theta1, int j) {
+  double th = 1.0, b = theta1;
+  for (int e = j; e; e >>= 1) {
+    if (e & 1) th *= b;
+    b *= b;
+  }
+  return th;
+}
+
+__device__ __forceinline__ void rope_cos_sin(int64_t pos, int j, double theta1, float& c, float& s) {
+  constexpr double kTwoPiHi = 6.283185307179586;        // nearest double to 2*pi
+  constexpr double kTwoPiLo = 2.4492935982947064e-16;   // 2*pi - kTwoPiHi
+  constexpr double kInvTwoPi = 0.15915494309189535;
+  const double phi = (double)pos * rope_theta(theta1, j);
+  const double k = rint(phi * kInvTwoPi);
+  double r = fma(-k, kTwoPiHi, phi);
+  r = fma(-k, kTwoPiLo, r);
+  sincosf((float)r, &s, &c);
 }
 
 // ---------------------------------------------------------------------------
@@ -122,6 +137,11 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of score_key (a -0 score comes back as +0).
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
 // Visible compressed entries for a query at absolute position tpos.

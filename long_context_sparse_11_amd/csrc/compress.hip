@@ -14,9 +14,9 @@
 
 namespace csa {
 
-template <typename T, int VEC>
-__global__ __launch_bounds__(1024) void compress_kernel(CompressArgs a) {
-  extern __shared__ float smem[];
+template <typename T, int VEC, int GMAX>
+__global__ __launch_bounds__(GMAX * 64) void compress_kernel(CompressArgs a) {
+  __shared__ float smem[3 * (GMAX / 2) * 64 * VEC];
   const int i = blockIdx.x;  // entry within the call
   const int b = blockIdx.y;
   const int D = a.D;
@@ -53,72 +53,91 @@ __global__ __launch_bounds__(1024) void compress_kernel(CompressArgs a) {
   for (int e = 0; e < VEC; ++e) { mx[e] = -INFINITY; den[e] = 0.f; acc[e] = 0.f; }
 
   const int64_t a_off = ((int64_t)b * a.T + a_row0) * D;
-#pragma unroll 4
-  for (int r = g; r < nr; r += G) {
-    const T* cp;
-    const T* zp;
-    const float* bp;
-    if (r < na) {
-      cp = (const T*)a.c_a + a_off + (int64_t)r * D + c0;
-      zp = a.z_a ? (const T*)a.z_a + a_off + (int64_t)r * D + c0 : nullptr;
-      bp = a.bias_a ? a.bias_a + (int64_t)r * D + c0 : nullptr;
-    } else {
-      const int rr = r - na;
-      cp = cb_base + (int64_t)rr * D + c0;
-      zp = zb_base + (int64_t)rr * D + c0;
-      bp = a.bias_b ? a.bias_b + (int64_t)rr * D + c0 : nullptr;
-    }
-    float cv[VEC], lv[VEC];
-    Elem<T>::template load<VEC>(cp, cv);
-    if (zp) {
-      Elem<T>::template load<VEC>(zp, lv);
-    } else {
+  // rows g, g+G, ... in batches of 4 whose loads are all issued first
+  for (int r0 = g; r0 < nr; r0 += 4 * G) {
+    float cv[4][VEC], lv[4][VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) lv[e] = 0.f;
-    }
-    if (bp) {
-      float bv[VEC];
-      Elem<float>::template load<VEC>(bp, bv);
+    for (int u = 0; u < 4; ++u) {
+      const int r = r0 + u * G;
+      if (r >= nr) continue;
+      const T* cp;
+      const T* zp;
+      const float* bp;
+      if (r < na) {
+        cp = (const T*)a.c_a + a_off + (int64_t)r * D + c0;
+        zp = a.z_a ? (const T*)a.z_a + a_off + (int64_t)r * D + c0 : nullptr;
+        bp = a.bias_a ? a.bias_a + (int64_t)r * D + c0 : nullptr;
+      } else {
+        const int rr = r - na;
+        cp = cb_base + (int64_t)rr * D + c0;
+        zp = zb_base + (int64_t)rr * D + c0;
+        bp = a.bias_b ? a.bias_b + (int64_t)rr * D + c0 : nullptr;
+      }
+      Elem<T>::template load<VEC>(cp, cv[u]);
+      if (zp) {
+        Elem<T>::template load<VEC>(zp, lv[u]);
+      } else {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) lv[e] += bv[e];
+        for (int e = 0; e < VEC; ++e) lv[u][e] = 0.f;
+      }
+      if (bp) {
+        float bv[VEC];
+        Elem<float>::template load<VEC>(bp, bv);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) lv[u][e] += bv[e];
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) lv[u][e] *= kLog2e;  // softmax in base 2
     }
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const float nm = fmaxf(mx[e], lv[e]);
-      const float sc = expf(mx[e] - nm);
-      const float p = expf(lv[e] - nm);
-      den[e] = den[e] * sc + p;
-      acc[e] = acc[e] * sc + p * cv[e];
-      mx[e] = nm;
+    for (int u = 0; u < 4; ++u) {
+      if (r0 + u * G >= nr) continue;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float nm = fmaxf(mx[e], lv[u][e]);
+        const float sc = exp2f(mx[e] - nm);
+        const float p = exp2f(lv[u][e] - nm);
+        den[e] = den[e] * sc + p;
+        acc[e] = acc[e] * sc + p * cv[u][e];
+        mx[e] = nm;
+      }
     }
   }
 
-  // merge the G groups: LDS layout [3][G][D]
+  // merge the G groups pairwise through LDS (log2 G steps, all groups busy):
+  // the upper half of the live groups posts its partials, the lower half
+  // folds them in.  LDS layout [3][G/2][D].
+  float gv[VEC];
+  if (g == 0 && a.gain) Elem<float>::template load<VEC>(a.gain + c0, gv);  // in flight meanwhile
   float* s_mx = smem;
-  float* s_den = smem + G * D;
-  float* s_acc = smem + 2 * G * D;
+  float* s_den = smem + (GMAX / 2) * 64 * VEC;
+  float* s_acc = smem + 2 * (GMAX / 2) * 64 * VEC;
+  for (int half = G >> 1; half >= 1; half >>= 1) {
+    if (g >= half && g < 2 * half) {
+      const int o = (g - half) * D + c0;
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) {
-    s_mx[g * D + c0 + e] = mx[e];
-    s_den[g * D + c0 + e] = den[e];
-    s_acc[g * D + c0 + e] = acc[e];
+      for (int e = 0; e < VEC; ++e) { s_mx[o + e] = mx[e]; s_den[o + e] = den[e]; s_acc[o + e] = acc[e]; }
+    }
+    __syncthreads();
+    if (g < half) {
+      const int o = g * D + c0;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float om = s_mx[o + e];
+        const float M = fmaxf(mx[e], om);
+        const float w0 = mx[e] == -INFINITY ? 0.f : exp2f(mx[e] - M);
+        const float w1 = om == -INFINITY ? 0.f : exp2f(om - M);
+        den[e] = den[e] * w0 + s_den[o + e] * w1;
+        acc[e] = acc[e] * w0 + s_acc[o + e] * w1;
+        mx[e] = M;
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
   if (g != 0) return;
-
   float y[VEC];
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) {
-    float M = -INFINITY;
-    for (int gg = 0; gg < G; ++gg) M = fmaxf(M, s_mx[gg * D + c0 + e]);
-    float dsum = 0.f, asum = 0.f;
-    for (int gg = 0; gg < G; ++gg) {
-      const float w = expf(s_mx[gg * D + c0 + e] - M);
-      dsum += s_den[gg * D + c0 + e] * w;
-      asum += s_acc[gg * D + c0 + e] * w;
-    }
-    y[e] = asum / dsum;
-  }
+  for (int e = 0; e < VEC; ++e) y[e] = acc[e] / den[e];
 
   if (a.gain) {
     float ss = 0.f;
@@ -126,8 +145,6 @@ __global__ __launch_bounds__(1024) void compress_kernel(CompressArgs a) {
     for (int e = 0; e < VEC; ++e) ss += y[e] * y[e];
     for (int off = L >> 1; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
     const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
-    float gv[VEC];
-    Elem<float>::template load<VEC>(a.gain + c0, gv);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) y[e] = y[e] * inv * gv[e];
   }
@@ -140,7 +157,7 @@ __global__ __launch_bounds__(1024) void compress_kernel(CompressArgs a) {
       const int c = c0 + e;
       if (c >= D - R) {
         float cs, sn;
-        rope_cos_sin(pos, (c - (D - R)) >> 1, R, a.rope_base, cs, sn);
+        rope_cos_sin(pos, (c - (D - R)) >> 1, a.rope_theta1, cs, sn);
         const float x0 = y[e], x1 = y[e + 1];
         y[e] = x0 * cs - x1 * sn;
         y[e + 1] = x0 * sn + x1 * cs;
@@ -153,20 +170,26 @@ __global__ __launch_bounds__(1024) void compress_kernel(CompressArgs a) {
   Elem<T>::template store<VEC>(op, y);
 }
 
+template <typename T, int VEC, int GMAX>
+static hipError_t launch_compress_g(const CompressArgs& a, int G, hipStream_t stream) {
+  const int L = a.D / VEC;
+  dim3 grid(a.n_out, a.B), block(G * L);
+  hipLaunchKernelGGL((compress_kernel<T, VEC, GMAX>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+// Row groups: about 4 rows per group (one batch of loads each; a merge step
+// costs more than streaming 4 more rows), at most 16 groups / 1024 threads,
+// at least one full wave; more than 8 groups take the 16-group variant.
 template <typename T, int VEC>
 static hipError_t launch_compress_t(const CompressArgs& a, hipStream_t stream) {
   const int L = a.D / VEC;
   const int rows = a.m * (a.overlap ? 2 : 1);
   int G = 1;
-  while (G < rows) G <<= 1;
-  const int g_threads = 1024 / L;                       // at most 1024 threads
-  const int g_lds = (48 * 1024) / (3 * 4 * a.D);        // merge buffer <= 48 KiB
-  G = min(G, min(g_threads, max(g_lds, 1)));
-  while (G * L < 64 && G * L < 1024 && G < 64) G <<= 1;  // at least one full wave
-  const size_t lds = (size_t)3 * G * a.D * sizeof(float);
-  dim3 grid(a.n_out, a.B), block(G * L);
-  hipLaunchKernelGGL((compress_kernel<T, VEC>), grid, block, lds, stream, a);
-  return hipGetLastError();
+  while (4 * G < rows && G * L < 1024 && G < 16) G <<= 1;
+  while (G * L < 64 && G < 16) G <<= 1;
+  if (G <= 8 || VEC > 8) return launch_compress_g<T, VEC, 8>(a, min(G, 8), stream);
+  return launch_compress_g<T, VEC, (VEC > 8 ? 8 : 16)>(a, G, stream);
 }
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t stream) {

@@ -89,6 +89,8 @@ __device__ __forceinline__ float tile_score(const bf16x8_t (&qa)[2][8], const bf
 // grid (chunks, B*Tq); 4 waves; chunk = 4 * tiles_per_wave tiles of 32 keys,
 // tiles interleaved over the waves so the WG reads one contiguous range.
 __global__ __launch_bounds__(256) void index_decode(IndexArgs a, int tiles_per_wave) {
+  __shared__ __attribute__((aligned(16))) bf16_t sq[64 * 128];
+  __shared__ __attribute__((aligned(16))) float sw[64];
   const int query = blockIdx.y;
   const int b = query / a.Tq;
   const int t = query - b * a.Tq;
@@ -99,36 +101,54 @@ __global__ __launch_bounds__(256) void index_decode(IndexArgs a, int tiles_per_w
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 31, g = lane >> 5;
 
+  // the query's 64 x 128 head matrix and head weights, fetched once per
+  // workgroup (4 + 1 vector loads per thread) and shared by its waves
+  {
+    const uint4* qg = reinterpret_cast<const uint4*>((const bf16_t*)a.q + (int64_t)query * 64 * 128);
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = qg[threadIdx.x + 256 * u];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) reinterpret_cast<uint4*>(sq)[threadIdx.x + 256 * u] = v[u];
+    if (threadIdx.x < 16)
+      reinterpret_cast<f32x4_t*>(sw)[threadIdx.x] =
+          reinterpret_cast<const f32x4_t*>(a.w + (int64_t)query * 64)[threadIdx.x];
+  }
+  __syncthreads();
   bf16x8_t qa[2][8];
-  load_query_operand((const bf16_t*)a.q + (int64_t)query * 64 * 128, lane, qa);
+  load_query_operand(sq, lane, qa);
   float wv[2][16];
-  load_head_weights(a.w + (int64_t)query * 64, lane, wv);
+  load_head_weights(sw, lane, wv);
 
   const bf16_t* kbase = (const bf16_t*)a.k + (int64_t)b * a.N_cap * 128 + g * 64;
   float* out = a.scores + (int64_t)query * a.N_cap;
 
   int tile = tile0 + wave;
   const int tile_end = min(tile0 + chunk_tiles, (n_vis + 31) >> 5);
-  bf16x8_t kb[8], kn[8];
-  if (tile < tile_end) {
-    const int key = min(tile * 32 + j, n_vis - 1);
+  auto load = [&](int tl, bf16x8_t(&dst)[8]) {
+    const int key = min(tl * 32 + j, n_vis - 1);
     const bf16_t* kp = kbase + (int64_t)key * 128;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) kb[s] = *reinterpret_cast<const bf16x8_t*>(kp + 8 * s);
-  }
-  for (; tile < tile_end; tile += 4) {
-    const int nxt = tile + 4;
-    if (nxt < tile_end) {
-      const int key = min(nxt * 32 + j, n_vis - 1);
-      const bf16_t* kp = kbase + (int64_t)key * 128;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) kn[s] = *reinterpret_cast<const bf16x8_t*>(kp + 8 * s);
-    }
+    for (int s = 0; s < 8; ++s) dst[s] = *reinterpret_cast<const bf16x8_t*>(kp + 8 * s);
+  };
+  auto score = [&](int tl, const bf16x8_t(&kb)[8]) {
     const float sc = tile_score(qa, kb, wv);
-    const int key = tile * 32 + j;
+    const int key = tl * 32 + j;
     if (g == 0 && key < n_vis) out[key] = sc;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) kb[s] = kn[s];
+  };
+  // two key buffers in turn: the next tile's loads are in flight while the
+  // current tile is scored, with no register copy between them
+  bf16x8_t k0[8], k1[8];
+  if (tile < tile_end) load(tile, k0);
+  while (tile < tile_end) {
+    const int t1 = tile + 4;
+    if (t1 < tile_end) load(t1, k1);
+    score(tile, k0);
+    if (t1 >= tile_end) break;
+    const int t2 = t1 + 4;
+    if (t2 < tile_end) load(t2, k0);
+    score(t1, k1);
+    tile = t2;
   }
 }
 

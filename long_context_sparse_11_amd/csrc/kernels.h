@@ -17,7 +17,7 @@ struct CompressArgs {
   const float *bias_a, *bias_b, *gain;
   float eps;
   int rope_dims;
-  double rope_base;
+  double rope_theta1;   // rope_base^(-2/rope_dims), computed on the host
   const int64_t* pos0;
   void* out;
   int64_t out_bstride;
@@ -61,7 +61,7 @@ hipError_t launch_topk(const TopkArgs& a, int segments, hipStream_t stream);
 struct AttnArgs {
   int dt;
   int B, Tq, H, D, R;
-  double rope_base;
+  double rope_theta1;   // rope_base^(-2/R), computed on the host
   float scale;
   const void* q;        // [B, Tq, H, D]
   const void* pool;     // [B, N_cap, D]

@@ -5,33 +5,64 @@
 // learned retrieval mechanism"; -1 for empty slots per the transformers
 // "DeepSeek-V4" page, "Tata letak attention mask").
 //
-// One 512-thread workgroup selects from one segment held in LDS (at most
-// kTopkCap scores) by an exact most-significant-digit radix select on
-// order-preserving uint32 keys: four 8-bit digits, an LDS histogram per
-// digit, the digit holding the K-th largest found by a suffix scan, early
-// exit as soon as the threshold bin is taken whole.  Elements above the
-// threshold are all kept; among those equal to it the lowest indices are
-// kept.  The output is compacted in index order with wave ballots, so the
-// chosen indices come out ascending and the result is deterministic.
+// One 512-thread workgroup selects from one segment of at most kTopkCap
+// scores, each thread holding 32 consecutive ones as order-preserving uint32
+// keys in registers (element e lives in thread e / 32, slot e % 32).  The select is
+// an exact most-significant-digit radix select with adaptive 12-bit digits:
+// every pass takes the 12 bits just below the common prefix of the keys
+// still in play (block min/max), histograms them in LDS (4096 bins, fine
+// enough that lanes seldom collide on a bin), and a block-wide suffix scan
+// finds the bin holding the K-th largest.  It stops when that bin is taken
+// whole or all 32 bits are fixed (three passes at most for distinct keys).
+// Keys above the bin are all kept; keys inside it are kept in index order
+// until K are chosen, so ties go to the lower index.  Output positions come
+// from one block-wide prefix count over the threads' (above, inside) tallies:
+// the chosen indices come out ascending and the result is deterministic.
 //
-// Rows longer than kTopkCap are handled in two launches: mode 1 selects K
-// from every kTopkCap-long chunk, mode 2 selects K from the concatenated
-// chunk winners (still in ascending index order, so ties resolve the same).
+// Rows longer than kTopkCap go through two launches: mode 1 selects K per
+// chunk, mode 2 selects K from the concatenated chunk winners (still in
+// ascending index order, so ties resolve identically).
 #include "kernels.h"
 
 namespace csa {
 
 constexpr int kTkThreads = 512;
 constexpr int kTkWaves = kTkThreads / 64;
-constexpr int kTkRounds = kTopkCap / kTkThreads;
+constexpr int kTkRounds = kTopkCap / kTkThreads;  // keys per thread
+constexpr int kDigitBits = 12;
+constexpr int kBins = 1 << kDigitBits;
+constexpr int kBinsPerThread = kBins / kTkThreads;
+
+struct TkShared {
+  uint32_t hist[kBins];
+  uint32_t red[2][kTkWaves];
+  uint32_t sel_digit, sel_above;
+};
+
+__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, TkShared& S, int wave,
+                                             int lane) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+  }
+  if (lane == 0) {
+    S.red[0][wave] = mn;
+    S.red[1][wave] = mx;
+  }
+  __syncthreads();
+  mn = S.red[0][0];
+  mx = S.red[1][0];
+#pragma unroll
+  for (int w = 1; w < kTkWaves; ++w) {
+    mn = min(mn, S.red[0][w]);
+    mx = max(mx, S.red[1][w]);
+  }
+  __syncthreads();
+}
 
 __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkArgs a) {
-  __shared__ uint32_t keys[kTopkCap];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t cnt_gt[kTkRounds * kTkWaves];
-  __shared__ uint32_t cnt_eq[kTkRounds * kTkWaves];
-  __shared__ uint32_t sel_digit, sel_above;
-
+  __shared__ TkShared S;
   const int seg = blockIdx.x;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -69,111 +100,157 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkArgs a) {
     return;
   }
 
-  // ---- load keys, first-digit histogram
-  for (int e = tid; e < 256; e += kTkThreads) hist[e] = 0;
-  __syncthreads();
-  for (int e = tid; e < n; e += kTkThreads) {
-    uint32_t key = score_key(src[e]);
-    if (src_idx && src_idx[e] < 0) key = 0;  // empty candidate slot ranks last
-    keys[e] = key;
-    atomicAdd(&hist[key >> 24], 1u);
+  // ---- keys in registers; every load issued before any is consumed.  A
+  // slot beyond n, or an empty candidate slot (index -1), takes no part.
+  uint32_t key[kTkRounds];
+  int32_t vi[kTkRounds];  // candidate indices (mode 2)
+  uint32_t live = 0;      // bit i: slot i holds a key
+  const int e0 = tid * kTkRounds;
+  {
+    float v[kTkRounds];
+    const bool vec = ((((uintptr_t)src) | ((uintptr_t)src_idx)) & 15) == 0 && e0 + kTkRounds <= n;
+    if (vec) {
+#pragma unroll
+      for (int u = 0; u < kTkRounds / 4; ++u) {
+        const f32x4_t x = reinterpret_cast<const f32x4_t*>(src + e0)[u];
+        v[4 * u] = x[0]; v[4 * u + 1] = x[1]; v[4 * u + 2] = x[2]; v[4 * u + 3] = x[3];
+      }
+      if (src_idx) {
+#pragma unroll
+        for (int u = 0; u < kTkRounds / 4; ++u) {
+          const int4 x = reinterpret_cast<const int4*>(src_idx + e0)[u];
+          vi[4 * u] = x.x; vi[4 * u + 1] = x.y; vi[4 * u + 2] = x.z; vi[4 * u + 3] = x.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kTkRounds; ++i) {
+        const int e = e0 + i;
+        v[i] = e < n ? src[e] : 0.f;
+        vi[i] = (src_idx && e < n) ? src_idx[e] : 0;
+      }
+    }
+    if (!src_idx) {
+#pragma unroll
+      for (int i = 0; i < kTkRounds; ++i) vi[i] = 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kTkRounds; ++i) {
+      key[i] = score_key(v[i]);
+      if (e0 + i < n && vi[i] >= 0) live |= 1u << i;
+    }
   }
-  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kBinsPerThread; ++k) S.hist[tid * kBinsPerThread + k] = 0;
 
+  // ---- radix select with adaptive 12-bit digits (the histogram is zero on
+  // entry to every pass; the barriers of the min/max reduction order the
+  // zeroing before the counting)
   uint32_t prefix = 0, mask = 0;
   int remaining = K;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    if (pass > 0) {
-      for (int e = tid; e < 256; e += kTkThreads) hist[e] = 0;
-      __syncthreads();
-      for (int e = tid; e < n; e += kTkThreads) {
-        const uint32_t key = keys[e];
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+  for (;;) {
+    uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int i = 0; i < kTkRounds; ++i) {
+      if (((live >> i) & 1) && (key[i] & mask) == prefix) {
+        mn = min(mn, key[i]);
+        mx = max(mx, key[i]);
       }
-      __syncthreads();
     }
-    // wave 0: find the digit d with above(d) < remaining <= above(d) + hist[d]
-    if (wave == 0) {
-      uint32_t h[4], local = 0;
+    block_minmax(mn, mx, S, wave, lane);
+    const uint32_t diff = mn ^ mx;
+    if (diff == 0) {  // every key in play is equal: take them in index order
+      prefix = mn;
+      mask = 0xffffffffu;
+      break;
+    }
+    const int hb = 31 - __clz(diff);
+    const uint32_t common = hb == 31 ? 0u : ~((2u << hb) - 1u);
+    mask |= common;
+    prefix = mn & mask;
+    const int shift = max(hb + 1 - kDigitBits, 0);
+    const uint32_t dmask = (1u << (hb + 1 - shift)) - 1u;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) { h[k] = hist[4 * lane + k]; local += h[k]; }
-      uint32_t suffix = local;  // inclusive suffix sum over lanes >= lane
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_down(suffix, off);
-        if (lane + off < 64) suffix += o;
-      }
-      uint32_t above = suffix - local;  // bins of higher lanes
-#pragma unroll
-      for (int k = 3; k >= 0; --k) {
-        if (above < (uint32_t)remaining && (uint32_t)remaining <= above + h[k]) {
-          sel_digit = 4 * lane + k;
-          sel_above = above;
-        }
-        above += h[k];
-      }
+    for (int i = 0; i < kTkRounds; ++i) {
+      if (((live >> i) & 1) && (key[i] & mask) == prefix)
+        atomicAdd(&S.hist[(key[i] >> shift) & dmask], 1u);
     }
     __syncthreads();
-    const uint32_t d = sel_digit;
-    remaining -= (int)sel_above;
+    // bins 8t .. 8t+7 belong to thread t; suffix sums run from the top bin down
+    uint32_t h[kBinsPerThread], local = 0;
+#pragma unroll
+    for (int k = 0; k < kBinsPerThread; ++k) {
+      h[k] = S.hist[tid * kBinsPerThread + k];
+      local += h[k];
+    }
+    uint32_t suffix = local;  // inclusive, over lanes >= lane of this wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_down(suffix, off);
+      if (lane + off < 64) suffix += o;
+    }
+    if (lane == 0) S.red[0][wave] = suffix;  // wave total
+    __syncthreads();
+    uint32_t above = suffix - local;
+    for (int w = wave + 1; w < kTkWaves; ++w) above += S.red[0][w];
+#pragma unroll
+    for (int k = kBinsPerThread - 1; k >= 0; --k) {
+      if (above < (uint32_t)remaining && (uint32_t)remaining <= above + h[k]) {
+        S.sel_digit = tid * kBinsPerThread + k;
+        S.sel_above = above;
+      }
+      above += h[k];
+    }
+    __syncthreads();
+    const uint32_t d = S.sel_digit;
+    remaining -= (int)S.sel_above;
+    mask |= dmask << shift;
     prefix |= d << shift;
-    mask |= 255u << shift;
-    const bool whole = hist[d] == (uint32_t)remaining;
-    __syncthreads();  // hist is rewritten by the next pass
-    if (whole) break;
+    const bool whole = S.hist[d] == (uint32_t)remaining;
+    __syncthreads();  // every thread has read hist[d]
+#pragma unroll
+    for (int k = 0; k < kBinsPerThread; ++k) S.hist[tid * kBinsPerThread + k] = 0;
+    if (whole || shift == 0) break;
   }
 
-  // ---- compaction in index order: key above the threshold bin -> kept;
-  // in the bin -> kept if among the first `remaining` of the bin.
-  const int rounds = (n + kTkThreads - 1) / kTkThreads;
-  for (int r = 0; r < rounds; ++r) {
-    const int e = r * kTkThreads + tid;
-    const uint32_t key = e < n ? (keys[e] & mask) : 0u;
-    const bool valid = e < n;
-    const uint64_t bgt = __ballot(valid && key > prefix);
-    const uint64_t beq = __ballot(valid && key == prefix);
-    if (lane == 0) {
-      cnt_gt[r * kTkWaves + wave] = __popcll(bgt);
-      cnt_eq[r * kTkWaves + wave] = __popcll(beq);
-    }
-  }
-  __syncthreads();
-  // exclusive scan of the (round, wave) counts; wave 0 does both arrays
-  if (wave == 0) {
-    const int total = rounds * kTkWaves;
-    uint32_t run_gt = 0, run_eq = 0;
-    for (int base = 0; base < total; base += 64) {
-      const int e = base + lane;
-      const uint32_t vg = e < total ? cnt_gt[e] : 0u;
-      const uint32_t ve = e < total ? cnt_eq[e] : 0u;
-      uint32_t ig = vg, ie = ve;
+  // ---- emit in index order: above the threshold bin -> kept; inside it ->
+  // kept if among the first `remaining` of the bin.  One block-wide
+  // exclusive prefix of the per-thread tallies gives every thread its start.
+  uint32_t ngt = 0, neq = 0;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t og = __shfl_up(ig, off);
-        const uint32_t oe = __shfl_up(ie, off);
-        if (lane >= off) { ig += og; ie += oe; }
-      }
-      if (e < total) { cnt_gt[e] = run_gt + ig - vg; cnt_eq[e] = run_eq + ie - ve; }
-      run_gt += __shfl(ig, 63);
-      run_eq += __shfl(ie, 63);
-    }
+  for (int i = 0; i < kTkRounds; ++i) {
+    const bool v = (live >> i) & 1;
+    const uint32_t k = key[i] & mask;
+    ngt += (v && k > prefix) ? 1u : 0u;
+    neq += (v && k == prefix) ? 1u : 0u;
   }
+  uint32_t igt = ngt, ieq = neq;  // inclusive prefix within the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t og = __shfl_up(igt, off);
+    const uint32_t oe = __shfl_up(ieq, off);
+    if (lane >= off) { igt += og; ieq += oe; }
+  }
+  if (lane == 63) { S.red[0][wave] = igt; S.red[1][wave] = ieq; }
   __syncthreads();
-  for (int r = 0; r < rounds; ++r) {
-    const int e = r * kTkThreads + tid;
-    const uint32_t key = e < n ? (keys[e] & mask) : 0u;
-    const bool valid = e < n;
-    const bool gt = valid && key > prefix;
-    const bool eq = valid && key == prefix;
-    const uint64_t bgt = __ballot(gt);
-    const uint64_t beq = __ballot(eq);
-    const uint32_t before_gt = cnt_gt[r * kTkWaves + wave] + lanes_below(bgt);
-    const uint32_t before_eq = cnt_eq[r * kTkWaves + wave] + lanes_below(beq);
-    if (gt || (eq && before_eq < (uint32_t)remaining)) {
-      const uint32_t pos = before_gt + min(before_eq, (uint32_t)remaining);
-      oidx[pos] = src_idx ? src_idx[e] : base_index + e;
-      if (osc) osc[pos] = src[e];
+  uint32_t before_gt = igt - ngt, before_eq = ieq - neq;
+  for (int w = 0; w < wave; ++w) { before_gt += S.red[0][w]; before_eq += S.red[1][w]; }
+#pragma unroll
+  for (int i = 0; i < kTkRounds; ++i) {
+    const bool v = (live >> i) & 1;
+    const uint32_t k = key[i] & mask;
+    if (v && k > prefix) {
+      const uint32_t p = before_gt + min(before_eq, (uint32_t)remaining);
+      oidx[p] = src_idx ? vi[i] : base_index + e0 + i;
+      if (osc) osc[p] = key_score(key[i]);
+      ++before_gt;
+    } else if (v && k == prefix) {
+      if (before_eq < (uint32_t)remaining) {
+        const uint32_t p = before_gt + before_eq;
+        oidx[p] = src_idx ? vi[i] : base_index + e0 + i;
+        if (osc) osc[p] = key_score(key[i]);
+      }
+      ++before_eq;
     }
   }
 }

@@ -4,6 +4,7 @@ import numpy as np
 import torch
 
 from long_context_sparse_11_amd import synth
+from long_context_sparse_11_amd.device import to_device
 
 # Parity bars (attention/compress: max over rows of ||gpu - ref||_inf / ||ref||_inf)
 TOL_F32 = 1e-5
@@ -13,12 +14,7 @@ BAND = 1e-4   # top-k: symmetric difference only within this of the K-th score
 
 def dev(x, dtype=None):
     """Host array / synth.Tensor -> contiguous CUDA tensor (bf16 bits kept)."""
-    if isinstance(x, synth.Tensor):
-        if x.dt == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(x.bits).view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(np.ascontiguousarray(x.f32)).cuda()
-    a = np.ascontiguousarray(x)
-    t = torch.from_numpy(a).cuda()
+    t = to_device(x)
     return t if dtype is None else t.to(dtype)
 
 

@@ -437,3 +437,70 @@ def test_decode_step_is_deterministic():
     o1, _ = L.csa_sparse_attn(*att, rope_dims=d["R"])
     o2, _ = L.csa_sparse_attn(*att, rope_dims=d["R"])
     assert torch.equal(o1, o2)
+
+
+def test_graph_replay_matches_eager():
+    """A captured decode step (compress + index/top-k + attention) replayed
+    several times, with eager work and synchronisation between replays,
+    reproduces the eager result every time."""
+    d = synth.decode("csa64k", 4, B=2, N=2500)
+    B, N, D, Di, m = d["B"], d["N"], d["D"], d["Di"], d["m"]
+    g = {k: (dev(v) if hasattr(v, "storage") or isinstance(v, np.ndarray) else v)
+         for k, v in d.items() if k not in ("name", "dt")}
+    idx = torch.empty((B, 1, d["K"]), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(g["q"])
+    ws_i = torch.empty(L.csa_index_topk_ws_bytes(B, 1, 64, N, d["K"]), dtype=torch.uint8,
+                       device="cuda")
+    ws_a = torch.empty(max(1, L.csa_attn_ws_bytes(B, 1, 64, D, d["K"] + d["W"])),
+                       dtype=torch.uint8, device="cuda")
+
+    def step():
+        L.csa_compress(g["c_a"], m, z_a=g["z_a"], c_b=g["c_b"], z_b=g["z_b"],
+                       prev_c_b=g["prev_c_b"], prev_z_b=g["prev_z_b"], bias_a=g["bias_a"],
+                       bias_b=g["bias_b"], gain=g["gain"], rope_dims=d["R"], pos0=g["block_pos0"],
+                       out=g["pool"][:, N - 1:], out_bstride=N * D)
+        L.csa_compress(g["ic_a"], m, z_a=g["iz_a"], c_b=g["ic_b"], z_b=g["iz_b"],
+                       prev_c_b=g["iprev_c_b"], prev_z_b=g["iprev_z_b"], bias_a=g["ibias_a"],
+                       bias_b=g["ibias_b"], out=g["k_idx"][:, N - 1:], out_bstride=N * Di)
+        L.csa_index_topk(g["q_idx"], g["w_idx"], g["k_idx"], g["n_entries"], g["q_pos0"], d["K"],
+                         m, ws=ws_i, idx_out=idx)
+        L.csa_sparse_attn(g["q"], g["pool"], idx, g["win"], g["win_pos0"], d["W"], g["sink"],
+                          g["q_pos0"], rope_dims=d["R"], out=out, ws=ws_a)
+
+    step()
+    torch.cuda.synchronize()
+    want_idx, want_out, want_pool = idx.clone(), out.clone(), g["pool"].clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(4):
+        idx.fill_(-7)
+        out.zero_()
+        g["pool"][:, N - 1].zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, want_idx), r
+        assert torch.equal(out, want_out), r
+        assert torch.equal(g["pool"], want_pool), r
+        step()   # eager work between replays
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("N", [10000, 20000])
+def test_index_ties_overflow_candidate_filter(N):
+    """A few positive scores and thousands of exact zeros: the sampled
+    threshold lands on 0, too many keys pass it, and the selector falls back
+    to the exact full-segment path; ties at 0 go to the lowest indices."""
+    rng = np.random.default_rng(N)
+    K = 512
+    q = np.abs(rng.standard_normal((1, 1, 64, 128))).astype(np.float32)
+    k = -np.abs(rng.standard_normal((1, N, 128))).astype(np.float32)
+    pos_rows = rng.choice(N, size=100, replace=False)
+    k[0, pos_rows] *= -1.0
+    w = np.abs(rng.standard_normal((1, 1, 64))).astype(np.float32) * 0.02
+    qq, kk = synth.Tensor(q, "bf16"), synth.Tensor(k, "bf16")
+    _check_index(qq, w, kk, np.array([N], np.int32), np.array([4 * N - 1]), K, 4, SCORE_ATOL_BF16)
+    gidx, gsc, _ = _index_case(qq, w, kk, [N], [4 * N - 1], K, 4)
+    zeros = sorted(set(range(N)) - set(pos_rows.tolist()))[: K - 100]
+    assert sorted(gidx[0, 0].tolist()) == sorted(pos_rows.tolist() + zeros)
