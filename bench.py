@@ -341,37 +341,41 @@ def main():
         for _, f in st.calls():
             f()
     torch.cuda.synchronize()
+    # steps per graph replay: several decode steps are captured together
+    # (each on its own input copy), as a serving loop would capture them
+    per_graph = next(p for p in (10, 8, 5, 4, 2, 1) if a.steps % p == 0 and a.warmup % p == 0) \
+        if use_graph else 1
+    reps_call = 20  # repetitions of one call per timing graph (distinct copies)
     graphs, call_graphs = [], []
     if use_graph:
-        # one graph per input copy for the whole step, and one per library call
-        for st in steps:
+        for gi in range(n_copies):
             gph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gph):
-                for _, f in st.calls():
-                    f()
+                for r in range(per_graph):
+                    for _, f in steps[(gi * per_graph + r) % n_copies].calls():
+                        f()
             graphs.append(gph)
-            per = []
-            for _, f in st.calls():
-                cg = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(cg):
-                    f()
-                per.append(cg)
-            call_graphs.append(per)
+        for k in range(len(names)):
+            cg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(cg):
+                for r in range(reps_call):
+                    steps[r % n_copies].calls()[k][1]()
+            call_graphs.append(cg)
         torch.cuda.synchronize()
 
-    def run_step(i):
+    def run(i):  # replay i covers steps i*per_graph .. (i+1)*per_graph-1
         if use_graph:
             graphs[i % n_copies].replay()
         else:
             for _, f in steps[i % n_copies].calls():
                 f()
 
-    for i in range(a.warmup):
-        run_step(i)
+    for i in range(a.warmup // per_graph):
+        run(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(a.steps):
-        run_step(a.warmup + i)
+    for i in range(a.steps // per_graph):
+        run(a.warmup // per_graph + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / a.steps
@@ -381,8 +385,6 @@ def main():
     # device time per step and per library call: HIP events on the library's
     # stream around graph replays, queued behind a spin kernel so the device
     # never waits for the host between them
-    reps = min(a.steps, 100)
-
     def timed(thunks):
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in thunks]
         torch.cuda._sleep(20_000_000)
@@ -393,15 +395,14 @@ def main():
         torch.cuda.synchronize()
         return [e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]  # us
 
-    dev_step_us = float(np.median(timed([(lambda i=i: run_step(i)) for i in range(reps)])))
-    per_call = {}
-    for k, n in enumerate(names):
-        if use_graph:
-            th = [(lambda i=i, k=k: call_graphs[i % n_copies][k].replay()) for i in range(reps)]
-        else:
-            th = [(lambda i=i, k=k: steps[i % n_copies].calls()[k][1]()) for i in range(reps)]
-        per_call[n] = float(np.median(timed(th)))
-    call_us = per_call
+    if use_graph:
+        dev_step_us = float(np.median(timed([(lambda i=i: run(i)) for i in range(20)]))) / per_graph
+        call_us = {n: float(np.median(timed([call_graphs[k].replay] * 10))) / reps_call
+                   for k, n in enumerate(names)}
+    else:
+        dev_step_us = float(np.median(timed([(lambda i=i: run(i)) for i in range(20)])))
+        call_us = {n: float(np.median(timed([(lambda i=i, k=k: steps[i % n_copies].calls()[k][1]())
+                                             for i in range(20)]))) for k, n in enumerate(names)}
 
     # roofline of the dominant call: the one moving the most algorithmic bytes
     if kind == "prefill":
@@ -436,7 +437,7 @@ def main():
     }[kind]
     cfgs.update(heads=64, head_dim=512, rope_dims=64, index_heads=64, index_dim=128,
                 index_topk=512, window=128, m=d["m"], step_calls=names,
-                graph=use_graph, input_copies=n_copies)
+                graph=use_graph, steps_per_graph=per_graph, input_copies=n_copies)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 5),

@@ -127,6 +127,33 @@ __device__ __forceinline__ void rope_cos_sin(int64_t pos, int j, double theta1, 
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Inclusive scan over the 64 lanes of a wave with DPP moves (no LDS
+// traffic): shifts by 1, 2, 4 and 8 inside each 16-lane row, then row
+// broadcasts of lane 15 and lane 31 into the rows above.  Lanes without a
+// source read the operation's identity.
+template <typename F>
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t x, uint32_t id, F f) {
+  x = f(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x111, 0xf, 0xf, false));
+  x = f(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x112, 0xf, 0xf, false));
+  x = f(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x114, 0xf, 0xf, false));
+  x = f(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x118, 0xf, 0xf, false));
+  x = f(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x142, 0xa, 0xf, false));
+  x = f(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x143, 0xc, 0xf, false));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+  return wave_scan_dpp(x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+// Whole-wave min / max, uniform result (lane 63 of the inclusive scan).
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+  x = wave_scan_dpp(x, 0xffffffffu, [](uint32_t a, uint32_t b) { return min(a, b); });
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  x = wave_scan_dpp(x, 0u, [](uint32_t a, uint32_t b) { return max(a, b); });
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));

@@ -5,19 +5,28 @@
 // learned retrieval mechanism"; -1 for empty slots per the transformers
 // "DeepSeek-V4" page, "Tata letak attention mask").
 //
-// One 512-thread workgroup selects from one segment of at most kTopkCap
-// scores, each thread holding 32 consecutive ones as order-preserving uint32
-// keys in registers (element e lives in thread e / 32, slot e % 32).  The select is
-// an exact most-significant-digit radix select with adaptive 12-bit digits:
-// every pass takes the 12 bits just below the common prefix of the keys
-// still in play (block min/max), histograms them in LDS (4096 bins, fine
-// enough that lanes seldom collide on a bin), and a block-wide suffix scan
-// finds the bin holding the K-th largest.  It stops when that bin is taken
-// whole or all 32 bits are fixed (three passes at most for distinct keys).
-// Keys above the bin are all kept; keys inside it are kept in index order
-// until K are chosen, so ties go to the lower index.  Output positions come
-// from one block-wide prefix count over the threads' (above, inside) tallies:
-// the chosen indices come out ascending and the result is deterministic.
+// One 1024-thread workgroup selects from one segment of at most kTopkCap
+// scores, each thread holding 16 consecutive ones as order-preserving uint32
+// keys in registers (element e lives in thread e / 16, slot e % 16).  The
+// select is exact and deterministic:
+//  1. the first digit of a key is a monotone linear map of its score over
+//     the segment's [min, max] onto 4096 bins (a larger score never gets a
+//     smaller digit, so every key in a higher bin beats every key in a lower
+//     one); one LDS histogram and a block suffix scan find the bin holding
+//     the K-th largest.  Spreading the range linearly keeps both same-bin
+//     atomic collisions and the threshold bin's population small, unlike
+//     digits taken from the float bits, which pile a smooth distribution
+//     into a few dozen bins;
+//  2. the keys of that bin are compacted into LDS and one wave finds the
+//     exact threshold key among them: by direct ranking when there are at
+//     most 64, else by a barrier-free radix select on 8-bit digits;
+//  3. keys in higher bins and keys above the threshold are all kept, keys
+//     equal to it are kept in index order until K are chosen (ties go to the
+//     lower index); output positions come from one block-wide prefix count,
+//     so the chosen indices come out ascending.
+// A degenerate or non-finite score range, or a threshold bin too full for
+// one wave (heavy ties), falls back to an adaptive block-level radix select
+// on the keys themselves (same answer, slower).
 //
 // Rows longer than kTopkCap go through two launches: mode 1 selects K per
 // chunk, mode 2 selects K from the concatenated chunk winners (still in
@@ -26,26 +35,26 @@
 
 namespace csa {
 
-constexpr int kTkThreads = 512;
+constexpr int kTkThreads = 1024;
 constexpr int kTkWaves = kTkThreads / 64;
 constexpr int kTkRounds = kTopkCap / kTkThreads;  // keys per thread
 constexpr int kDigitBits = 12;
 constexpr int kBins = 1 << kDigitBits;
 constexpr int kBinsPerThread = kBins / kTkThreads;
+constexpr int kBinCap = 2048;  // most keys of the threshold bin one wave resolves
+static_assert(kTkRounds <= 32, "slot masks are 32 bits");
 
 struct TkShared {
   uint32_t hist[kBins];
-  uint32_t red[2][kTkWaves];
-  uint32_t sel_digit, sel_above;
+  uint32_t bin[kBinCap];
+  uint32_t red[3][kTkWaves];
+  uint32_t sel_digit, sel_above, sel_count, fill;
 };
 
 __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, TkShared& S, int wave,
                                              int lane) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
-  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
   if (lane == 0) {
     S.red[0][wave] = mn;
     S.red[1][wave] = mx;
@@ -59,6 +68,25 @@ __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, TkShare
     mx = max(mx, S.red[1][w]);
   }
   __syncthreads();
+}
+
+// Exclusive block prefix of x (all threads take part); also returns the
+// block total.  Uses S.red[0] and two barriers.
+__device__ __forceinline__ uint32_t block_excl_sum(uint32_t x, uint32_t& total, TkShared& S,
+                                                   int wave, int lane) {
+  const uint32_t incl = wave_incl_sum(x);
+  if (lane == 63) S.red[0][wave] = incl;
+  __syncthreads();
+  uint32_t before = incl - x, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) {
+    const uint32_t t = S.red[0][w];
+    before += w < wave ? t : 0u;
+    tot += t;
+  }
+  total = tot;
+  __syncthreads();
+  return before;
 }
 
 __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkArgs a) {
@@ -142,115 +170,309 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkArgs a) {
   }
 #pragma unroll
   for (int k = 0; k < kBinsPerThread; ++k) S.hist[tid * kBinsPerThread + k] = 0;
+  if (tid == 0) S.fill = 0;
 
-  // ---- radix select with adaptive 12-bit digits (the histogram is zero on
-  // entry to every pass; the barriers of the min/max reduction order the
-  // zeroing before the counting)
-  uint32_t prefix = 0, mask = 0;
-  int remaining = K;
-  for (;;) {
-    uint32_t mn = 0xffffffffu, mx = 0u;
+  // ---- radix select with adaptive 12-bit digits over the register slots in
+  // `act`: returns (prefix, mask, remaining) such that the chosen keys are
+  // those with (key & mask) > prefix plus the first `remaining` (in index
+  // order) with (key & mask) == prefix.  The histogram is zero on entry to
+  // every pass; the barriers of the min/max reduction order the zeroing
+  // before the counting.
+  auto select = [&](uint32_t act, int want, uint32_t& prefix, uint32_t& mask, int& remaining) {
+    prefix = 0;
+    mask = 0;
+    remaining = want;
+    for (;;) {
+      uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
-    for (int i = 0; i < kTkRounds; ++i) {
-      if (((live >> i) & 1) && (key[i] & mask) == prefix) {
-        mn = min(mn, key[i]);
-        mx = max(mx, key[i]);
+      for (int i = 0; i < kTkRounds; ++i) {
+        if (((act >> i) & 1) && (key[i] & mask) == prefix) {
+          mn = min(mn, key[i]);
+          mx = max(mx, key[i]);
+        }
       }
-    }
-    block_minmax(mn, mx, S, wave, lane);
-    const uint32_t diff = mn ^ mx;
-    if (diff == 0) {  // every key in play is equal: take them in index order
-      prefix = mn;
-      mask = 0xffffffffu;
-      break;
-    }
-    const int hb = 31 - __clz(diff);
-    const uint32_t common = hb == 31 ? 0u : ~((2u << hb) - 1u);
-    mask |= common;
-    prefix = mn & mask;
-    const int shift = max(hb + 1 - kDigitBits, 0);
-    const uint32_t dmask = (1u << (hb + 1 - shift)) - 1u;
+      block_minmax(mn, mx, S, wave, lane);
+      const uint32_t diff = mn ^ mx;
+      if (diff == 0) {  // every key in play is equal: take them in index order
+        prefix = mn;
+        mask = 0xffffffffu;
+        return;
+      }
+      const int hb = 31 - __clz(diff);
+      const uint32_t common = hb == 31 ? 0u : ~((2u << hb) - 1u);
+      mask |= common;
+      prefix = mn & mask;
+      const int shift = max(hb + 1 - kDigitBits, 0);
+      const uint32_t dmask = (1u << (hb + 1 - shift)) - 1u;
 #pragma unroll
-    for (int i = 0; i < kTkRounds; ++i) {
-      if (((live >> i) & 1) && (key[i] & mask) == prefix)
-        atomicAdd(&S.hist[(key[i] >> shift) & dmask], 1u);
+      for (int i = 0; i < kTkRounds; ++i) {
+        if (((act >> i) & 1) && (key[i] & mask) == prefix)
+          atomicAdd(&S.hist[(key[i] >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      // bins kBinsPerThread*t .. +kBinsPerThread-1 belong to thread t; the
+      // suffix sums run from the top bin down
+      uint32_t h[kBinsPerThread], local = 0;
+#pragma unroll
+      for (int k = 0; k < kBinsPerThread; ++k) {
+        h[k] = S.hist[tid * kBinsPerThread + k];
+        local += h[k];
+      }
+      uint32_t total;
+      const uint32_t below = block_excl_sum(local, total, S, wave, lane);
+      uint32_t above = total - below - local;
+#pragma unroll
+      for (int k = kBinsPerThread - 1; k >= 0; --k) {
+        if (above < (uint32_t)remaining && (uint32_t)remaining <= above + h[k]) {
+          S.sel_digit = tid * kBinsPerThread + k;
+          S.sel_above = above;
+        }
+        above += h[k];
+      }
+      __syncthreads();
+      const uint32_t d = S.sel_digit;
+      remaining -= (int)S.sel_above;
+      mask |= dmask << shift;
+      prefix |= d << shift;
+      const bool whole = S.hist[d] == (uint32_t)remaining;
+      __syncthreads();  // every thread has read hist[d]
+#pragma unroll
+      for (int k = 0; k < kBinsPerThread; ++k) S.hist[tid * kBinsPerThread + k] = 0;
+      if (whole || shift == 0) return;
+    }
+  };
+
+  // ---- 1. key range and live count, then the histogram of the linear
+  // first digit
+  uint32_t kmn = 0xffffffffu, kmx = 0u;
+#pragma unroll
+  for (int i = 0; i < kTkRounds; ++i) {
+    if ((live >> i) & 1) {
+      kmn = min(kmn, key[i]);
+      kmx = max(kmx, key[i]);
+    }
+  }
+  uint32_t n_live;
+  {
+    kmn = wave_min(kmn);
+    kmx = wave_max(kmx);
+    const uint32_t cnt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(__popc(live)), 63);
+    if (lane == 0) {
+      S.red[0][wave] = kmn;
+      S.red[1][wave] = kmx;
+      S.red[2][wave] = cnt;
+    }
+    __syncthreads();  // also orders the zeroing above before the counting
+    n_live = 0;
+#pragma unroll
+    for (int w = 0; w < kTkWaves; ++w) {
+      kmn = min(kmn, S.red[0][w]);
+      kmx = max(kmx, S.red[1][w]);
+      n_live += S.red[2][w];
     }
     __syncthreads();
-    // bins 8t .. 8t+7 belong to thread t; suffix sums run from the top bin down
+  }
+  const float fmn = key_score(kmn), fmx = key_score(kmx);
+  const float range = fmx - fmn;
+  const float scale = (float)kBins / range;
+  const bool linear = kmn < kmx && isfinite(fmn) && isfinite(fmx) && isfinite(range) &&
+                      isfinite(scale) && scale > 0.f;
+
+  uint32_t prefix = 0, mask = 0;   // threshold among the keys of in_bin
+  int remaining = K;
+  uint32_t above_m = 0;            // slots in a bin above the threshold bin: always kept
+  uint32_t in_bin = live;          // slots competing at the threshold
+  if (n_live <= (uint32_t)K) {
+    // at most K candidates (mode 2 with few visible entries): keep them all
+    above_m = live;
+    in_bin = 0;
+    remaining = 0;
+    for (int e = (int)n_live + tid; e < K; e += kTkThreads) {
+      oidx[e] = -1;
+      if (osc) osc[e] = -INFINITY;
+    }
+  } else if (linear) {
+    uint32_t dg[kTkRounds];
+#pragma unroll
+    for (int i = 0; i < kTkRounds; ++i) {
+      dg[i] = (uint32_t)fminf((key_score(key[i]) - fmn) * scale, (float)(kBins - 1));
+      if ((live >> i) & 1) atomicAdd(&S.hist[dg[i]], 1u);
+    }
+    __syncthreads();
     uint32_t h[kBinsPerThread], local = 0;
 #pragma unroll
     for (int k = 0; k < kBinsPerThread; ++k) {
       h[k] = S.hist[tid * kBinsPerThread + k];
       local += h[k];
     }
-    uint32_t suffix = local;  // inclusive, over lanes >= lane of this wave
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t o = __shfl_down(suffix, off);
-      if (lane + off < 64) suffix += o;
-    }
-    if (lane == 0) S.red[0][wave] = suffix;  // wave total
-    __syncthreads();
-    uint32_t above = suffix - local;
-    for (int w = wave + 1; w < kTkWaves; ++w) above += S.red[0][w];
+    uint32_t total;
+    const uint32_t below = block_excl_sum(local, total, S, wave, lane);
+    uint32_t above = total - below - local;
 #pragma unroll
     for (int k = kBinsPerThread - 1; k >= 0; --k) {
-      if (above < (uint32_t)remaining && (uint32_t)remaining <= above + h[k]) {
+      if (above < (uint32_t)K && (uint32_t)K <= above + h[k]) {
         S.sel_digit = tid * kBinsPerThread + k;
         S.sel_above = above;
+        S.sel_count = h[k];
       }
       above += h[k];
     }
     __syncthreads();
-    const uint32_t d = S.sel_digit;
-    remaining -= (int)S.sel_above;
-    mask |= dmask << shift;
-    prefix |= d << shift;
-    const bool whole = S.hist[d] == (uint32_t)remaining;
-    __syncthreads();  // every thread has read hist[d]
+    const uint32_t d1 = S.sel_digit;
+    const uint32_t c1 = S.sel_count;
+    remaining = K - (int)S.sel_above;
+    in_bin = 0;
 #pragma unroll
-    for (int k = 0; k < kBinsPerThread; ++k) S.hist[tid * kBinsPerThread + k] = 0;
-    if (whole || shift == 0) break;
+    for (int i = 0; i < kTkRounds; ++i) {
+      const bool v = (live >> i) & 1;
+      above_m |= (v && dg[i] > d1) ? (1u << i) : 0u;
+      in_bin |= (v && dg[i] == d1) ? (1u << i) : 0u;
+    }
+    __syncthreads();  // sel_* are rewritten below
+
+    if (c1 == (uint32_t)remaining) {
+      // the whole bin is taken: every key of in_bin is "equal" and all fit
+    } else if (c1 <= (uint32_t)kBinCap) {
+      // ---- 2. compact the bin's keys (any order), one wave finishes
+      const uint32_t mine = __popc(in_bin);
+      const uint32_t incl = wave_incl_sum(mine);
+      uint32_t base = 0;
+      if (lane == 63) base = atomicAdd(&S.fill, incl);
+      uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)base, 63) + incl - mine;
+#pragma unroll
+      for (int i = 0; i < kTkRounds; ++i) {
+        if ((in_bin >> i) & 1) S.bin[pos++] = key[i];
+      }
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t pre, msk;
+        int rem = remaining;
+        if (c1 <= 64) {
+          // rank the (at most 64) keys against each other
+          const bool valid = (uint32_t)lane < c1;
+          const uint32_t k = valid ? S.bin[lane] : 0u;
+          uint32_t gt = 0, ge = 0;
+          for (uint32_t j = 0; j < c1; ++j) {
+            const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)k, (int)j);
+            gt += kj > k ? 1u : 0u;
+            ge += kj >= k ? 1u : 0u;
+          }
+          const bool hit = valid && gt < (uint32_t)rem && (uint32_t)rem <= ge;
+          const uint64_t hm = __ballot(hit);
+          const int src_lane = __ffsll((long long)hm) - 1;
+          pre = (uint32_t)__builtin_amdgcn_readlane((int)k, src_lane);
+          rem -= (int)(uint32_t)__builtin_amdgcn_readlane((int)gt, src_lane);
+          msk = 0xffffffffu;
+        } else {
+          // barrier-free radix select on 8-bit digits below the bin's common
+          // prefix; LDS operations of one wave complete in order
+          uint32_t bmn = 0xffffffffu, bmx = 0u;
+          for (uint32_t e = lane; e < c1; e += 64) {
+            const uint32_t k = S.bin[e];
+            bmn = min(bmn, k);
+            bmx = max(bmx, k);
+          }
+          bmn = wave_min(bmn);
+          bmx = wave_max(bmx);
+          const uint32_t diff = bmn ^ bmx;
+          if (diff == 0) {
+            pre = bmn;
+            msk = 0xffffffffu;
+          } else {
+            const int hb = 31 - __clz(diff);
+            msk = hb == 31 ? 0u : ~((2u << hb) - 1u);
+            pre = bmn & msk;
+            uint32_t* wh = S.hist;  // 256 bins, 4 per lane
+            for (int top = hb; top >= 0; top -= 8) {
+              const int shift = max(top - 7, 0);
+              const uint32_t dm = (1u << (top + 1 - shift)) - 1u;
+#pragma unroll
+              for (int k = 0; k < 4; ++k) wh[4 * lane + k] = 0;
+              __builtin_amdgcn_wave_barrier();
+              for (uint32_t e = lane; e < c1; e += 64) {
+                const uint32_t k = S.bin[e];
+                if ((k & msk) == pre) atomicAdd(&wh[(k >> shift) & dm], 1u);
+              }
+              __builtin_amdgcn_wave_barrier();
+              uint32_t hh[4], loc = 0;
+#pragma unroll
+              for (int k = 0; k < 4; ++k) { hh[k] = wh[4 * lane + k]; loc += hh[k]; }
+              const uint32_t inc = wave_incl_sum(loc);
+              const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+              uint32_t abv = tot - inc;  // bins of higher lanes
+              uint32_t dsel = 0, asel = 0, csel = 0;
+              bool hit = false;
+#pragma unroll
+              for (int k = 3; k >= 0; --k) {
+                if (!hit && abv < (uint32_t)rem && (uint32_t)rem <= abv + hh[k]) {
+                  hit = true; dsel = 4 * lane + k; asel = abv; csel = hh[k];
+                }
+                abv += hh[k];
+              }
+              const uint64_t hm = __ballot(hit);
+              const int src_lane = __ffsll((long long)hm) - 1;
+              dsel = (uint32_t)__builtin_amdgcn_readlane((int)dsel, src_lane);
+              asel = (uint32_t)__builtin_amdgcn_readlane((int)asel, src_lane);
+              csel = (uint32_t)__builtin_amdgcn_readlane((int)csel, src_lane);
+              __builtin_amdgcn_wave_barrier();
+              rem -= (int)asel;
+              pre |= dsel << shift;
+              msk |= dm << shift;
+              if (csel == (uint32_t)rem) break;  // the whole digit bin is taken
+            }
+          }
+        }
+        if (lane == 0) {
+          S.sel_digit = pre;
+          S.sel_above = msk;
+          S.sel_count = (uint32_t)rem;
+        }
+      }
+      __syncthreads();
+      prefix = S.sel_digit;
+      mask = S.sel_above;
+      remaining = (int)S.sel_count;
+    } else {
+      // ---- heavy ties: adaptive block-level radix inside the bin
+#pragma unroll
+      for (int k = 0; k < kBinsPerThread; ++k) S.hist[tid * kBinsPerThread + k] = 0;
+      select(in_bin, remaining, prefix, mask, remaining);
+    }
+  } else {
+    select(live, K, prefix, mask, remaining);
   }
 
-  // ---- emit in index order: above the threshold bin -> kept; inside it ->
-  // kept if among the first `remaining` of the bin.  One block-wide
-  // exclusive prefix of the per-thread tallies gives every thread its start.
-  uint32_t ngt = 0, neq = 0;
+  // ---- 3. emit in index order: chosen are the keys of higher bins, the
+  // bin's keys above the threshold and, in index order, the first
+  // `remaining` equal to it.  A thread's chosen keys fill one contiguous run
+  // of the output, starting after everything chosen by lower threads.
+  uint32_t gt_m = above_m, eq_m = 0;
 #pragma unroll
   for (int i = 0; i < kTkRounds; ++i) {
-    const bool v = (live >> i) & 1;
+    const bool v = (in_bin >> i) & 1;
     const uint32_t k = key[i] & mask;
-    ngt += (v && k > prefix) ? 1u : 0u;
-    neq += (v && k == prefix) ? 1u : 0u;
+    gt_m |= (v && k > prefix) ? (1u << i) : 0u;
+    eq_m |= (v && k == prefix) ? (1u << i) : 0u;
   }
-  uint32_t igt = ngt, ieq = neq;  // inclusive prefix within the wave
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t og = __shfl_up(igt, off);
-    const uint32_t oe = __shfl_up(ieq, off);
-    if (lane >= off) { igt += og; ieq += oe; }
-  }
-  if (lane == 63) { S.red[0][wave] = igt; S.red[1][wave] = ieq; }
-  __syncthreads();
-  uint32_t before_gt = igt - ngt, before_eq = ieq - neq;
-  for (int w = 0; w < wave; ++w) { before_gt += S.red[0][w]; before_eq += S.red[1][w]; }
+  const uint32_t ngt = __popc(gt_m), neq = __popc(eq_m);
+  uint32_t total;  // counts packed as gt | eq << 16 (each at most kTopkCap)
+  const uint32_t before = block_excl_sum(ngt | (neq << 16), total, S, wave, lane);
+  const uint32_t before_gt = before & 0xffffu, before_eq = before >> 16;
+  // the first `take` of this thread's equal keys are chosen; the clamp comes
+  // before the subtraction so that no intermediate can wrap
+  const uint32_t eq_before = min(before_eq, (uint32_t)remaining);
+  const uint32_t take = min(neq, (uint32_t)remaining - eq_before);
+  uint32_t p = before_gt + eq_before;
+  uint32_t seen_eq = 0;
 #pragma unroll
   for (int i = 0; i < kTkRounds; ++i) {
-    const bool v = (live >> i) & 1;
-    const uint32_t k = key[i] & mask;
-    if (v && k > prefix) {
-      const uint32_t p = before_gt + min(before_eq, (uint32_t)remaining);
+    const bool g = (gt_m >> i) & 1, e = (eq_m >> i) & 1;
+    const bool c = g || (e && seen_eq < take);
+    seen_eq += e ? 1u : 0u;
+    if (c) {
       oidx[p] = src_idx ? vi[i] : base_index + e0 + i;
       if (osc) osc[p] = key_score(key[i]);
-      ++before_gt;
-    } else if (v && k == prefix) {
-      if (before_eq < (uint32_t)remaining) {
-        const uint32_t p = before_gt + before_eq;
-        oidx[p] = src_idx ? vi[i] : base_index + e0 + i;
-        if (osc) osc[p] = key_score(key[i]);
-      }
-      ++before_eq;
+      ++p;
     }
   }
 }

@@ -504,3 +504,53 @@ def test_index_ties_overflow_candidate_filter(N):
     gidx, gsc, _ = _index_case(qq, w, kk, [N], [4 * N - 1], K, 4)
     zeros = sorted(set(range(N)) - set(pos_rows.tolist()))[: K - 100]
     assert sorted(gidx[0, 0].tolist()) == sorted(pos_rows.tolist() + zeros)
+
+
+def test_index_two_level_with_few_visible():
+    """Rows longer than one workgroup's share, queried early: fewer than K
+    chunk winners survive into the merge, which then keeps them all and pads
+    with -1; a third query spans two chunks."""
+    rng = np.random.default_rng(11)
+    N, K, m = 20000, 512, 4
+    q = synth.Tensor(rng.standard_normal((3, 2, 64, 128)).astype(np.float32), "bf16")
+    w = (0.02 * rng.standard_normal((3, 2, 64))).astype(np.float32)
+    k = synth.Tensor(rng.standard_normal((3, N, 128)).astype(np.float32), "bf16")
+    pos0 = np.array([0, 4 * 300, 4 * 17000])   # visible 0..1, ~300, ~17000
+    n_ent = np.array([N, N, N], np.int32)
+    _check_index(q, w, k, n_ent, pos0, K, m, SCORE_ATOL_BF16)
+    gidx, _, _ = _index_case(q, w, k, n_ent, pos0, K, m)
+    assert np.all(gidx[0, 0] == -1)
+    assert (gidx[1, 0] >= 0).sum() == O.visible_count(pos0[1], m, N)
+
+
+def _linear_bin_count(scores, K):
+    """Population of the threshold bin of a 4096-bin linear map of the score
+    range (float32, as the selector computes it): tells which way the exact
+    finish goes."""
+    s = scores.astype(np.float32)
+    mn, mx = s.min(), s.max()
+    scale = np.float32(4096) / np.float32(mx - mn)
+    d = np.minimum(((s - mn) * scale).astype(np.float32), np.float32(4095)).astype(np.int64)
+    h = np.bincount(d, minlength=4096)
+    above = np.cumsum(h[::-1])[::-1] - h   # count in higher bins
+    b = int(np.nonzero((above < K) & (K <= above + h))[0][0])
+    return int(h[b])
+
+
+@pytest.mark.parametrize("N,outlier", [(16000, 3000.0), (16000, 40.0), (40000, 3000.0)])
+def test_index_outlier_stretches_range(N, outlier):
+    """One key row scaled far beyond the rest stretches the score range, so
+    the threshold bin of the linear first digit holds many keys and the exact
+    finish takes its radix path (or, for a mild outlier, the ranking path)."""
+    rng = np.random.default_rng(int(outlier) + N)
+    Hi, Di, K = 4, 32, 512
+    q = rng.standard_normal((1, 1, Hi, Di)).astype(np.float32)
+    w = np.abs(rng.standard_normal((1, 1, Hi))).astype(np.float32)
+    k = rng.standard_normal((1, N, Di)).astype(np.float32)
+    k[0, 77] = np.abs(q[0, 0, 0]) * np.sign(q[0, 0, 0]) * outlier / np.linalg.norm(q[0, 0, 0])
+    _check_index(q, w, k, np.array([N], np.int32), np.array([4 * N - 1]), K, 4,
+                 score_atol=1e-5 * outlier)   # float32 rounding at the outlier's magnitude
+    _, _, alls = _index_case(q, w, k, [N], [4 * N - 1], K, 4)
+    if N <= 16384:
+        c1 = _linear_bin_count(alls[0, 0, :N], K)
+        assert (c1 > 64) if outlier > 1000 else (c1 <= 64), c1
