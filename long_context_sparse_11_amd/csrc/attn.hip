@@ -12,10 +12,11 @@
 //
 // attn_generic  any shape/dtype; one wave per (query, head), VALU.
 // attn_mfma     bf16, 64 heads x 512 (the Flash shape).  One workgroup of 4
-//               waves per (query, key split).  Wave w owns channels
-//               128w .. 128w+127 of every row: it gathers its 256-byte slice
-//               of 32 rows per tile straight from HBM into MFMA operands
-//               (each row is read once and serves all 64 heads), computes
+//               waves per (query, key split).  Wave w owns 128 channels of
+//               every row (16 of each 64-channel stretch): it gathers its
+//               share of 32 rows per tile straight from HBM into MFMA
+//               operands (each row is read once and serves all 64 heads),
+//               computes
 //               the partial logits S^T[row][head] over its channels,
 //               the four partials are summed through LDS, every wave runs
 //               the same online softmax (running max/sum per head, seeded
@@ -169,70 +170,151 @@ constexpr int kRtPitch = 128;     // bf16 per LDS row of a wave's row copy (256 
 // then fall on distinct LDS banks.
 __device__ __forceinline__ int rt_swz(int row) { return (4 * row + (row >> 2)) & 15; }
 
+constexpr int kAtMaxSplitRows = 4096;  // rows of a multi-tile CSA split (LDS index stage)
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr;
 constexpr int kAtD = 512;
 constexpr int kAtH = 64;
-constexpr int kAtMaxSplitRows = 4096;  // rows of one key split (LDS index stage)
 
+// Value of lane (l ^ 32): the two halves of the wave swap through
+// v_permlane32_swap (a VALU move; no LDS round trip).
+__device__ __forceinline__ float half_swap(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(__lane_id() < 32 ? r[1] : r[0]);
+}
+
+// CSA: rows come from the selected index list (else every visible entry).
+// MULTI: a split may hold more than one 32-row tile (else exactly one, and
+// the kernel is straight-line code with no prefetch).
+template <bool CSA, bool MULTI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_mfma(AttnArgs a) {
   __shared__ float s_cos[kAtD / 2], s_sin[kAtD / 2];
   __shared__ __attribute__((aligned(16))) f32x4_t sx[2][4][2][4][64];  // [buf][wave][ht][rq][lane]
   __shared__ __attribute__((aligned(16))) bf16_t rt[4][kAtRows * kRtPitch];
-  __shared__ int32_t s_idx[kAtMaxSplitRows];
+  __shared__ int32_t s_idx[MULTI && CSA ? kAtMaxSplitRows : 1];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int j = lane & 31, g = lane >> 5;
   const int qi = blockIdx.y, sp = blockIdx.x, S = gridDim.x;
   const int b = qi / a.Tq, t = qi - b * a.Tq;
-  const int64_t tpos = a.q_pos0[b] + t;
   const int R = a.R;
   const int rope0 = kAtD - R;
+  // Channel ownership: lane (g, j) of wave w holds, in its slot s (0..7),
+  // 8 consecutive channels of row / head j (+32); the wave's local channel
+  // 64g + 8s + e (its LDS row copy, its PV rows) is global channel
+  // 8 * blk(s, g) + e.  Multi-tile splits stream rows, and there each lane
+  // reads one contiguous 128-byte stretch (blocks 16w + 8g + s).  A
+  // single-tile split is latency-bound instead, and there the blocks are
+  // 8s + 2w + g: the eight lane groups each own one block of every
+  // 64-channel stretch, so the rope channels at the end of the row are
+  // spread over all of them rather than piled on one half-wave, whose
+  // rotation would otherwise hold up the whole workgroup.
+  auto blk = [&](int s, int gg) { return MULTI ? 16 * wave + 8 * gg + s : 8 * s + 2 * wave + gg; };
+  auto chan = [&](int s) { return 8 * blk(s, g); };
 
-  for (int p = tid; p < R / 2; p += 256) rope_cos_sin(tpos, p, a.rope_theta1, s_cos[p], s_sin[p]);
-
-  const KeyRange kr = key_range(a, b, qi, tpos);
-  const int L = kr.nsel + kr.nwin;
-  const int per = (((L + S - 1) / S) + kAtRows - 1) / kAtRows * kAtRows;
-  const int start = min(L, sp * per);
-  const int end = min(L, start + per);
-  // the split's selected pool indices, staged once (row addresses then need
-  // no dependent global load inside the tile loop)
-  if (a.csa) {
-    const int sel_end = min(end, kr.nsel);
-    for (int jj = start + tid; jj < sel_end; jj += 256) s_idx[jj - start] = a.idx[(int64_t)qi * a.K + jj];
+  // ---- Every global load below is unconditional (clamped or redirected
+  // addresses), so the compiler can count outstanding loads exactly and
+  // waits only for the one it needs.  Order: the selected indices of tiles
+  // 0 and 1 (the row loads wait on them), the query slice, then tile 0's
+  // rows.  A CSA split covers a fixed range of the list [K selected rows,
+  // then up to min(W, L_win) window rows], so its bounds are known before
+  // the query position is.
+  int start = 0, end = 0;
+  if (CSA) {
+    const int wc = (a.W > 0 && a.L_win > 0) ? min(a.W, a.L_win) : 0;
+    const int Lmax = a.K + wc;
+    const int per = (((Lmax + S - 1) / S) + kAtRows - 1) / kAtRows * kAtRows;
+    start = min(Lmax, sp * per);
+    end = min(Lmax, start + per);
   }
-  __syncthreads();
-
-  // query operand, rotated at +tpos: lane (g, j) holds head j (+32) at
-  // channels fbase + 8s .. +7
-  const int fbase = wave * 128 + g * 64;
+  // selected index of this lane's row at list position j0 + j (a harmless
+  // word when there is none: a position past K, or K == 0)
+  const bool has_idx = CSA && a.K > 0;
+  const int32_t* idx_q = has_idx ? a.idx + (int64_t)qi * a.K : (const int32_t*)a.q_pos0;
+  auto load_idx = [&](int j0) -> int32_t {
+    return idx_q[has_idx ? min(max(j0 + j, 0), a.K - 1) : 0];
+  };
+  const int32_t idx0 = CSA ? load_idx(start) : 0;  // tile 0
   bf16x8_t qb[2][8];
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
-    const bf16_t* qp = (const bf16_t*)a.q + ((int64_t)qi * kAtH + ht * 32 + j) * kAtD + fbase;
+    const bf16_t* qp = (const bf16_t*)a.q + ((int64_t)qi * kAtH + ht * 32 + j) * kAtD;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      float v[8];
-      Elem<bf16_t>::load<8>(qp + 8 * s, v);
+    for (int s = 0; s < 8; ++s) qb[ht][s] = *reinterpret_cast<const bf16x8_t*>(qp + chan(s));
+  }
+  const bf16_t* q_slice = (const bf16_t*)a.q + ((int64_t)qi * kAtH + j) * kAtD;
+  const int64_t tpos = a.q_pos0[b] + t;
+  const KeyRange kr = key_range(a, b, qi, tpos);
+  if (!CSA) {
+    const int L = kr.nsel + kr.nwin;
+    const int per = (((L + S - 1) / S) + kAtRows - 1) / kAtRows * kAtRows;
+    start = min(L, sp * per);
+    end = min(L, start + per);
+  }
+
+  // Row at list position j0 + j into this wave's operand registers (its 128
+  // channels of the row).  An absent row (empty index slot, window row
+  // beyond the buffer, or past the split) reads the lane's own query slice
+  // instead: `valid` masks it out of the softmax, so its (finite) values
+  // meet a zero weight in the PV product.
+  const bf16_t* pool_b = (const bf16_t*)a.pool + (int64_t)b * a.N_cap * kAtD;
+  const bf16_t* win_b = (const bf16_t*)a.win + ((int64_t)b * a.L_win + kr.win_r0) * kAtD;
+  auto load_rows = [&](int j0, int sidx, bf16x8_t(&dst)[8], bool& valid) {
+    const int jj = j0 + j;
+    const bool in_sel = jj < kr.nsel;
+    const int srow = CSA ? sidx : jj;
+    const int wrow = jj - kr.nsel;
+    valid = jj < end && (in_sel ? (srow >= 0 && srow < a.N_cap) : wrow < kr.nwin);
+    const bf16_t* pb = pool_b;  // values, so the selects below are of pointers, not of
+    const bf16_t* wb = win_b;   // the captured variables (which would put them in scratch)
+    const bf16_t* p = (in_sel ? pb : wb) + (int64_t)(in_sel ? srow : wrow) * kAtD;
+    p = valid ? p : q_slice;
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const int c = fbase + 8 * s + e;
-        if (c >= rope0) {
-          const int pj = (c - rope0) >> 1;
-          const float cs = s_cos[pj], sn = s_sin[pj];
-          const float x0 = v[e], x1 = v[e + 1];
-          v[e] = x0 * cs - x1 * sn;
-          v[e + 1] = x0 * sn + x1 * cs;
-        }
-      }
+    for (int s = 0; s < 8; ++s) dst[s] = *reinterpret_cast<const bf16x8_t*>(p + chan(s));
+  };
+
+  // rope table at +tpos (computed while tile 0's indices are in flight)
+  for (int p = tid; p < R / 2; p += 256) rope_cos_sin(tpos, p, a.rope_theta1, s_cos[p], s_sin[p]);
+
+  bf16x8_t ra[8];
+  bool va = false;
+  load_rows(start, idx0, ra, va);
+  if constexpr (MULTI && CSA) {
+    // later tiles' indices, staged once for the whole split (after tile 0's
+    // rows are requested: waiting on these loads then costs nothing extra)
+    const int sel_end = min(end, a.K);
+    for (int jj = start + kAtRows + tid; jj < sel_end; jj += 256)
+      s_idx[jj - start] = a.idx[(int64_t)qi * a.K + jj];
+  }
+  __syncthreads();  // rope table, staged indices
+
+  // rotate the query's rope channels at +tpos: only the lane's slots that
+  // reach the rope part
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int c0 = chan(s);
+    if (c0 + 8 <= rope0) continue;
+    float cs[4], sn[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = c0 + 2 * k;
+      const int pj = max(c - rope0, 0) >> 1;
+      const bool rot = c >= rope0;
+      cs[k] = rot ? s_cos[pj] : 1.f;
+      sn[k] = rot ? s_sin[pj] : 0.f;
+    }
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const u32x4_t w = __builtin_bit_cast(u32x4_t, qb[ht][s]);
       u32x4_t pk;
-      pk.x = pack_bf16x2(v[0], v[1]);
-      pk.y = pack_bf16x2(v[2], v[3]);
-      pk.z = pack_bf16x2(v[4], v[5]);
-      pk.w = pack_bf16x2(v[6], v[7]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float x0 = __uint_as_float(w[k] << 16), x1 = __uint_as_float(w[k] & 0xffff0000u);
+        pk[k] = pack_bf16x2(x0 * cs[k] - x1 * sn[k], x0 * sn[k] + x1 * cs[k]);
+      }
       qb[ht][s] = __builtin_bit_cast(bf16x8_t, pk);
     }
   }
@@ -246,32 +328,7 @@ void attn_mfma(AttnArgs a) {
   const float sl2 = a.scale * kLog2e;
   bf16_t* myrt = rt[wave];
 
-  bf16x8_t ra[8];
-  bool va = false;
-  auto load_rows = [&](int j0, bf16x8_t(&dst)[8], bool& valid) {
-    const int jj = j0 + j;
-    const int jr = jj < end ? jj : start;
-    const bf16_t* p;
-    bool rv = true;
-    if (jr < kr.nsel) {
-      int srow = jr;
-      if (a.csa) {
-        srow = s_idx[jr - start];
-        rv = srow >= 0 && srow < a.N_cap;
-        if (!rv) srow = 0;
-      }
-      p = (const bf16_t*)a.pool + ((int64_t)b * a.N_cap + srow) * kAtD;
-    } else {
-      p = (const bf16_t*)a.win + ((int64_t)b * a.L_win + kr.win_r0 + (jr - kr.nsel)) * kAtD;
-    }
-    valid = rv && jj < end;
-    p += fbase;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) dst[s] = *reinterpret_cast<const bf16x8_t*>(p + 8 * s);
-  };
-
   int buf = 0;
-  if (start < end) load_rows(start, ra, va);
   for (int j0 = start; j0 < end; j0 += kAtRows) {
     // partial logits over this wave's 128 channels
     f32x16_t s0 = {}, s1 = {};
@@ -292,7 +349,13 @@ void attn_mfma(AttnArgs a) {
     const uint64_t vmask = __ballot(va);
     // the rows now live in LDS: reuse their registers for the next tile's
     // loads, which then overlap this tile's softmax and PV
-    if (j0 + kAtRows < end) load_rows(j0 + kAtRows, ra, va);
+    if constexpr (MULTI) {
+      if (j0 + kAtRows < end) {
+        const int jn = j0 + kAtRows + j;
+        const int idx_n = (CSA && jn < min(end, a.K)) ? s_idx[jn - start] : 0;
+        load_rows(j0 + kAtRows, idx_n, ra, va);
+      }
+    }
     __syncthreads();
 
     float p[2][16];
@@ -323,7 +386,7 @@ void attn_mfma(AttnArgs a) {
       float x = p[ht][0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) x = fmaxf(x, p[ht][r]);
-      tm[ht] = fmaxf(x, __shfl_xor(x, 32));
+      tm[ht] = fmaxf(x, half_swap(x));
       move |= tm[ht] > mrun[ht] + 8.f;
     }
     if (__ballot(move)) {
@@ -348,7 +411,7 @@ void attn_mfma(AttnArgs a) {
       float rs = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) rs += p[ht][r];
-      rs += __shfl_xor(rs, 32);
+      rs += half_swap(rs);
       lrun[ht] += rs;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -389,7 +452,13 @@ void attn_mfma(AttnArgs a) {
     }
   }
 
-  // ---- epilogue
+  // ---- epilogue.  Accumulator element (dt, rq, e) of lane (g, j) is the
+  // wave's local channel 32dt + 8rq + 4g + e, i.e. global channel
+  // out_chan(dt, rq) + e (4 consecutive channels).
+  auto out_chan = [&](int dt, int rq) {
+    const int sl = 4 * (dt & 1) + rq;  // slot and lane half of the local channel
+    return 8 * blk(sl, dt >> 1) + 4 * g;
+  };
   if (S == 1) {
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
@@ -399,7 +468,7 @@ void attn_mfma(AttnArgs a) {
       const float lf = lrun[ht] * exp2f(mrun[ht] - mf) + exp2f(skl2 - mf);
       const float fac = exp2f(mrun[ht] - mf) / lf;
       if (wave == 0 && g == 0 && a.lse) a.lse[(int64_t)qi * kAtH + h] = (mf + log2f(lf)) * kLn2;
-      bf16_t* op = (bf16_t*)a.out + ((int64_t)qi * kAtH + h) * kAtD + wave * 128;
+      bf16_t* op = (bf16_t*)a.out + ((int64_t)qi * kAtH + h) * kAtD;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
@@ -407,7 +476,7 @@ void attn_mfma(AttnArgs a) {
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = oacc[dt][ht][4 * rq + e] * fac;
-          const int c = wave * 128 + dt * 32 + 8 * rq + 4 * g;
+          const int c = out_chan(dt, rq);
 #pragma unroll
           for (int e = 0; e < 4; e += 2) {
             if (c + e >= rope0) {
@@ -421,7 +490,7 @@ void attn_mfma(AttnArgs a) {
           uint2 pk;
           pk.x = pack_bf16x2(o[0], o[1]);
           pk.y = pack_bf16x2(o[2], o[3]);
-          *reinterpret_cast<uint2*>(op + dt * 32 + 8 * rq + 4 * g) = pk;
+          *reinterpret_cast<uint2*>(op + c) = pk;
         }
       }
     }
@@ -434,34 +503,58 @@ void attn_mfma(AttnArgs a) {
         a.part_ml[2 * slot] = mrun[ht];
         a.part_ml[2 * slot + 1] = lrun[ht];
       }
-      float* po = a.part_o + slot * kAtD + wave * 128;
+      // the output's rope slice is rotated back by -tpos here (the rotation
+      // is linear, so the merge of the splits commutes with it)
+      float* po = a.part_o + slot * kAtD;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq)
-          *reinterpret_cast<f32x4_t*>(po + dt * 32 + 8 * rq + 4 * g) =
-              f32x4_t{oacc[dt][ht][4 * rq], oacc[dt][ht][4 * rq + 1], oacc[dt][ht][4 * rq + 2],
-                      oacc[dt][ht][4 * rq + 3]};
+        for (int rq = 0; rq < 4; ++rq) {
+          float o[4] = {oacc[dt][ht][4 * rq], oacc[dt][ht][4 * rq + 1], oacc[dt][ht][4 * rq + 2],
+                        oacc[dt][ht][4 * rq + 3]};
+          const int c = out_chan(dt, rq);
+          if (c + 4 > rope0) {
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+              if (c + e >= rope0) {
+                const int pj = (c + e - rope0) >> 1;
+                const float cs = s_cos[pj], sn = s_sin[pj];
+                const float x0 = o[e], x1 = o[e + 1];
+                o[e] = x0 * cs + x1 * sn;
+                o[e + 1] = -x0 * sn + x1 * cs;
+              }
+            }
+          }
+          *reinterpret_cast<f32x4_t*>(po + c) = f32x4_t{o[0], o[1], o[2], o[3]};
+        }
     }
   }
 }
 
 // Merge of the key-range splits: partial maxima are in log2 units of the
-// scaled logits, partial sums and outputs unnormalised.  grid (B*Tq, H),
-// 128 threads, 4 channels per thread per step.  The per-split weights are
-// computed once into LDS; the split loop is unrolled so the loads of several
-// splits are in flight together.
+// scaled logits, partial sums and outputs unnormalised (outputs already
+// rotated back by -tpos on their rope slice).  grid (B*Tq, H),
+// 128 threads of 4 channels each (the 512-wide Flash rows).  The partial
+// outputs of the first kCbPre splits are requested before the per-split
+// weights are known, so the two dependent reads overlap; the weights go
+// through LDS.
 constexpr int kMaxSplits = 256;
+constexpr int kCbPre = 16;
 
 template <typename T>
 __global__ __launch_bounds__(128) void attn_combine(AttnArgs a) {
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_lse;
   const int qi = blockIdx.x, h = blockIdx.y;
-  const int S = a.splits, D = a.D, R = a.R;
-  const int b = qi / a.Tq, t = qi - b * a.Tq;
-  const int64_t tpos = a.q_pos0[b] + t;
+  const int S = a.splits;
   const int64_t slot0 = (int64_t)qi * S * a.H + h;
+  const int c = threadIdx.x * 4;
+  const float* po = a.part_o + slot0 * kAtD + c;
+  const int64_t sstride = (int64_t)a.H * kAtD;
+  f32x4_t v[kCbPre];
+#pragma unroll
+  for (int u = 0; u < kCbPre; ++u)
+    v[u] = u < S ? *reinterpret_cast<const f32x4_t*>(po + u * sstride) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   if (threadIdx.x < 64) {  // one wave merges the (max, sum) pairs
     const int lane = threadIdx.x;
     const float skl2 = a.sink[h] * kLog2e;
@@ -484,34 +577,23 @@ __global__ __launch_bounds__(128) void attn_combine(AttnArgs a) {
   }
   __syncthreads();
   if (threadIdx.x == 0 && a.lse) a.lse[(int64_t)qi * a.H + h] = s_lse;
-  for (int c = threadIdx.x * 4; c < D; c += 512) {
-    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-    int s = 0;
-    for (; s + 8 <= S; s += 8) {
-      f32x4_t v[8];
+  f32x4_t o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        v[u] = *reinterpret_cast<const f32x4_t*>(a.part_o + (slot0 + (int64_t)(s + u) * a.H) * D + c);
+  for (int u = 0; u < kCbPre; ++u)
+    if (u < S) o += s_w[u] * v[u];
+  for (int s = kCbPre; s < S; s += 8) {
+    f32x4_t w8[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) o += s_w[s + u] * v[u];
-    }
-    for (; s < S; ++s)
-      o += s_w[s] * *reinterpret_cast<const f32x4_t*>(a.part_o + (slot0 + (int64_t)s * a.H) * D + c);
-    float r[4] = {o[0], o[1], o[2], o[3]};
+    for (int u = 0; u < 8; ++u)
+      w8[u] = s + u < S ? *reinterpret_cast<const f32x4_t*>(po + (s + u) * sstride) : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 4; e += 2) {
-      if (c + e >= D - R) {
-        float cs, sn;
-        rope_cos_sin(tpos, (c + e - (D - R)) >> 1, a.rope_theta1, cs, sn);
-        const float x0 = r[e], x1 = r[e + 1];
-        r[e] = x0 * cs + x1 * sn;
-        r[e + 1] = -x0 * sn + x1 * cs;
-      }
-    }
-    T* op = (T*)a.out + ((int64_t)qi * a.H + h) * D + c;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Elem<T>::put(op + e, r[e]);
+    for (int u = 0; u < 8; ++u)
+      if (s + u < S) o += s_w[s + u] * w8[u];
   }
+  float r[4] = {o[0], o[1], o[2], o[3]};
+  T* op = (T*)a.out + ((int64_t)qi * a.H + h) * kAtD + c;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) Elem<T>::put(op + e, r[e]);
 }
 
 // ------------------------------------------------------------------- launch
@@ -523,9 +605,12 @@ int attn_splits(int dt, int B, int Tq, int H, int D, int keys_per_query) {
   if (!(dt == 1 && H == kAtH && D == kAtD)) return 1;
   const int64_t q = (int64_t)B * Tq;
   const int tiles = (keys_per_query + kAtRows - 1) / kAtRows;
+  // few queries: spread each one's tiles over splits until there are about
+  // as many workgroups as compute units (one tile per split at most)
   int s = 1;
-  if (q < 256 && tiles >= 4) s = min((int)((256 + q - 1) / q), tiles / 2);
-  // a split holds at most kAtMaxSplitRows rows (its index stage lives in LDS)
+  if (q < 256 && tiles >= 2) s = min((int)((256 + q - 1) / q), tiles);
+  // a multi-tile split holds at most kAtMaxSplitRows rows (its CSA index
+  // stage lives in LDS)
   s = max(s, (keys_per_query + kAtMaxSplitRows - 1) / kAtMaxSplitRows);
   return min(s, kMaxSplits);
 }
@@ -551,7 +636,17 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.B * a.Tq == 0) return hipSuccess;
   if (attn_uses_mfma(a.dt, a.H, a.D, a.R)) {
     dim3 grid(a.splits, a.B * a.Tq);
-    hipLaunchKernelGGL(attn_mfma, grid, dim3(256), 0, stream, a);
+    // most rows a split can hold: the list length bound over the split count
+    const int wc = (a.W > 0 && a.L_win > 0) ? min(a.W, a.L_win) : 0;
+    const int64_t lmax = (a.csa ? (int64_t)a.K : (int64_t)a.N_cap) + wc;
+    const bool multi = (lmax + a.splits - 1) / a.splits > kAtRows;
+    if (a.csa) {
+      if (multi) hipLaunchKernelGGL((attn_mfma<true, true>), grid, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((attn_mfma<true, false>), grid, dim3(256), 0, stream, a);
+    } else {
+      if (multi) hipLaunchKernelGGL((attn_mfma<false, true>), grid, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((attn_mfma<false, false>), grid, dim3(256), 0, stream, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
     hipLaunchKernelGGL(attn_combine<bf16_t>, dim3(a.B * a.Tq, a.H), dim3(128), 0, stream, a);

@@ -23,17 +23,15 @@ constexpr float kLn2 = 0.6931471805599453f;
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// Round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// float32 -> bfloat16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
 }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
 // Element access for the two storage types.  VEC elements per call, VEC a
 // multiple of (16 bytes / element size) so every access is a 16-byte vector.
@@ -56,6 +54,20 @@ struct Elem<float> {
 #pragma unroll
     for (int c = 0; c < VEC / 4; ++c)
       reinterpret_cast<float4*>(p)[c] = make_float4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
+  }
+  // raw 16-byte words (VEC / 4 of them) and their conversion, kept apart so
+  // a load can be issued long before its value is needed
+  template <int VEC>
+  __device__ __forceinline__ static void load_raw(const float* p, u32x4_t* w) {
+#pragma unroll
+    for (int c = 0; c < VEC / 4; ++c) w[c] = reinterpret_cast<const u32x4_t*>(p)[c];
+  }
+  template <int VEC>
+  __device__ __forceinline__ static void from_raw(const u32x4_t* w, float* v) {
+#pragma unroll
+    for (int c = 0; c < VEC / 4; ++c)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[4 * c + k] = __uint_as_float(w[c][k]);
   }
   __device__ __forceinline__ static float get(const float* p) { return *p; }
   __device__ __forceinline__ static void put(float* p, float v) { *p = v; }
@@ -88,6 +100,21 @@ struct Elem<bf16_t> {
       x.w = pack_bf16x2(v[8 * c + 6], v[8 * c + 7]);
       reinterpret_cast<uint4*>(p)[c] = x;
     }
+  }
+  template <int VEC>
+  __device__ __forceinline__ static void load_raw(const bf16_t* p, u32x4_t* w) {
+#pragma unroll
+    for (int c = 0; c < VEC / 8; ++c) w[c] = reinterpret_cast<const u32x4_t*>(p)[c];
+  }
+  template <int VEC>
+  __device__ __forceinline__ static void from_raw(const u32x4_t* w, float* v) {
+#pragma unroll
+    for (int c = 0; c < VEC / 8; ++c)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[8 * c + 2 * k] = __uint_as_float(w[c][k] << 16);
+        v[8 * c + 2 * k + 1] = __uint_as_float(w[c][k] & 0xffff0000u);
+      }
   }
   __device__ __forceinline__ static float get(const bf16_t* p) { return bf16_to_f32(*p); }
   __device__ __forceinline__ static void put(bf16_t* p, float v) { *p = (bf16_t)f32_to_bf16(v); }

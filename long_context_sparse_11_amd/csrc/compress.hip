@@ -53,52 +53,57 @@ __global__ __launch_bounds__(GMAX * 64) void compress_kernel(CompressArgs a) {
   for (int e = 0; e < VEC; ++e) { mx[e] = -INFINITY; den[e] = 0.f; acc[e] = 0.f; }
 
   const int64_t a_off = ((int64_t)b * a.T + a_row0) * D;
-  // rows g, g+G, ... in batches of 4 whose loads are all issued first
+  // rows g, g+G, ... in batches of 4.  Every load of a batch is issued before
+  // any arithmetic: a row past the block reads a valid row (its own group's
+  // first) and is skipped afterwards, and the optional z / bias loads go
+  // into zero-initialised registers, so no load is waited on before the
+  // batch's last one is in flight.
+  constexpr int NW = VEC * (int)sizeof(T) / 16;  // 16-byte words per lane per row
+  // the optional streams' words are initialised once (a skipped load then
+  // leaves a defined value that a select discards), never inside the loop,
+  // where a fresh write could be made to wait for an older load
+  u32x4_t cw[4][NW], zw[4][NW], bw[4][VEC / 4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+#pragma unroll
+    for (int k = 0; k < NW; ++k) zw[u][k] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < VEC / 4; ++k) bw[u][k] = u32x4_t{0u, 0u, 0u, 0u};
+  }
   for (int r0 = g; r0 < nr; r0 += 4 * G) {
-    float cv[4][VEC], lv[4][VEC];
+    bool hz[4], hb[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int r = r0 + u * G;
-      if (r >= nr) continue;
-      const T* cp;
-      const T* zp;
-      const float* bp;
-      if (r < na) {
-        cp = (const T*)a.c_a + a_off + (int64_t)r * D + c0;
-        zp = a.z_a ? (const T*)a.z_a + a_off + (int64_t)r * D + c0 : nullptr;
-        bp = a.bias_a ? a.bias_a + (int64_t)r * D + c0 : nullptr;
-      } else {
-        const int rr = r - na;
-        cp = cb_base + (int64_t)rr * D + c0;
-        zp = zb_base + (int64_t)rr * D + c0;
-        bp = a.bias_b ? a.bias_b + (int64_t)rr * D + c0 : nullptr;
-      }
-      Elem<T>::template load<VEC>(cp, cv[u]);
-      if (zp) {
-        Elem<T>::template load<VEC>(zp, lv[u]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) lv[u][e] = 0.f;
-      }
-      if (bp) {
-        float bv[VEC];
-        Elem<float>::template load<VEC>(bp, bv);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) lv[u][e] += bv[e];
-      }
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) lv[u][e] *= kLog2e;  // softmax in base 2
+      const int rr = r < nr ? r : r0;
+      const bool in_a = rr < na;
+      const int64_t rb = rr - na;
+      const T* cp = in_a ? (const T*)a.c_a + a_off + (int64_t)rr * D + c0 : cb_base + rb * D + c0;
+      const T* zb = in_a ? (const T*)a.z_a : zb_base;
+      const T* zp = in_a ? (const T*)a.z_a + a_off + (int64_t)rr * D + c0 : zb_base + rb * D + c0;
+      const float* bb = in_a ? a.bias_a : a.bias_b;
+      const float* bp = bb + (int64_t)(in_a ? rr : (int)rb) * D + c0;
+      hz[u] = zb != nullptr;
+      hb[u] = bb != nullptr;
+      Elem<T>::template load_raw<VEC>(cp, cw[u]);
+      if (hz[u]) Elem<T>::template load_raw<VEC>(zp, zw[u]);
+      if (hb[u]) Elem<float>::template load_raw<VEC>(bp, bw[u]);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (r0 + u * G >= nr) continue;
+      float cv[VEC], zv[VEC], bv[VEC];
+      Elem<T>::template from_raw<VEC>(cw[u], cv);
+      Elem<T>::template from_raw<VEC>(zw[u], zv);
+      Elem<float>::template from_raw<VEC>(bw[u], bv);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        const float nm = fmaxf(mx[e], lv[u][e]);
+        const float l = ((hz[u] ? zv[e] : 0.f) + (hb[u] ? bv[e] : 0.f)) * kLog2e;  // base 2
+        const float nm = fmaxf(mx[e], l);
         const float sc = exp2f(mx[e] - nm);
-        const float p = exp2f(lv[u][e] - nm);
+        const float p = exp2f(l - nm);
         den[e] = den[e] * sc + p;
-        acc[e] = acc[e] * sc + p * cv[u][e];
+        acc[e] = acc[e] * sc + p * cv[e];
         mx[e] = nm;
       }
     }
