@@ -181,6 +181,14 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
+// Sum over the 64 lanes of a wave (DPP moves; the result is uniform).
+__device__ __forceinline__ float wave_sum(float x) {
+  const uint32_t r = wave_scan_dpp(__float_as_uint(x), 0u, [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  });
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)r, 63));
+}
+
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));

@@ -28,6 +28,7 @@ __global__ __launch_bounds__(GMAX * 64) void compress_kernel(CompressArgs a) {
   const int c0 = lane * VEC;
   const int m = a.m;
 
+  const int64_t pos = a.pos0 ? a.pos0[b] + (int64_t)m * i : 0;  // requested early (rope)
   const int64_t a_row0 = (int64_t)m * i;
   const int na = (int)min((int64_t)m, (int64_t)a.T - a_row0);
   const T* cb_base = nullptr;
@@ -148,7 +149,11 @@ __global__ __launch_bounds__(GMAX * 64) void compress_kernel(CompressArgs a) {
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) ss += y[e] * y[e];
-    for (int off = L >> 1; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    if (L == 64) {
+      ss = wave_sum(ss);
+    } else {
+      for (int off = L >> 1; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    }
     const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) y[e] = y[e] * inv * gv[e];
@@ -156,7 +161,6 @@ __global__ __launch_bounds__(GMAX * 64) void compress_kernel(CompressArgs a) {
 
   const int R = a.rope_dims;
   if (R > 0 && c0 + VEC > D - R) {
-    const int64_t pos = a.pos0[b] + (int64_t)m * i;
 #pragma unroll
     for (int e = 0; e < VEC; e += 2) {
       const int c = c0 + e;

@@ -368,7 +368,7 @@ def csa_sparse_attn(q, pool, idx, win, win_pos0, W, sink, q_pos0, scale,
     for b, t in pairs:
         t_pos = int(q_pos0[b]) + t
         sel = [int(s) for s in idx[b, t] if s >= 0]
-        rows = np.concatenate([np.asarray(pool[b], dtype=np.float64)[sel].reshape(-1, D),
+        rows = np.concatenate([np.asarray(pool[b][sel], dtype=np.float64).reshape(-1, D),
                                _window_rows(win[b], win_pos0[b], t_pos, W)])
         out[b, t], lse[b, t] = attend(q[b, t], t_pos, rows, sink, scale, rope_dims, rope_base)
     return out, lse
