@@ -38,6 +38,7 @@ METRIC = "CSA/HCA attention decode tokens/s at 64K & 1M ctx; % HBM/MFMA roofline
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
+CAL_BYTES = 512 << 20
 
 
 def parse():
@@ -94,6 +95,20 @@ class Step:
                                     device="cuda")
             n = L.csa_attn_ws_bytes(1, Tq, 64, D, K + W)
             self.ws_a = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+
+    def dominant(self):
+        """(name, thunk) of the kernel that carries the step's algorithmic
+        work: the indexer scoring (CSA; one kernel, the scoring half of
+        index_topk) or the whole HCA attention call (attention + split merge)."""
+        g, L = self.g, self.L
+        if self.kind == "hca1m":
+            return self.calls()[1]
+        if not hasattr(self, "scores"):
+            B, Tq, N = g["B"], g["Tq"], g["N"]
+            self.scores = self.torch.empty((B, Tq, N), dtype=self.torch.float32, device="cuda")
+        return ("index_scores", lambda: L.csa_index_scores(g["q_idx"], g["w_idx"], g["k_idx"],
+                                                           g["n_entries"], g["q_pos0"], g["m"],
+                                                           out=self.scores))
 
     def calls(self):
         """The step as a list of (name, thunk) library calls."""
@@ -188,6 +203,9 @@ def algorithmic(kind, d):
         N = d["N"]
         comp = B * ((4 * m) * D * bf + D * bf + (4 * m) * Di * bf + Di * bf)
         idx_bytes = B * (N * Di * bf + Hi * Di * bf + Hi * 4 + K * 4)
+        # the scoring kernel alone: visible keys, query heads and weights
+        out["index_scores"] = {"bytes": B * (N * Di * bf + Hi * Di * bf + Hi * 4),
+                               "flops": B * 2 * Hi * Di * N}
         rows = min(K, N) + W
         attn_bytes = B * (rows * D * bf + 2 * H * D * bf + K * 4)
         out["bytes"] = {"compress": comp, "index_topk": idx_bytes, "sparse_attn": attn_bytes}
@@ -198,6 +216,7 @@ def algorithmic(kind, d):
         rows = N + W
         out["bytes"] = {"compress": comp, "hca_attn": B * (rows * D * bf + 2 * H * D * bf)}
         out["flops"] = {"hca_attn": B * 4 * H * D * rows}
+        out["hca_attn"] = {"bytes": out["bytes"]["hca_attn"], "flops": out["flops"]["hca_attn"]}
     else:
         N, P = d["N"], d["prefix"]
         T = Tq + m
@@ -209,7 +228,46 @@ def algorithmic(kind, d):
         out["bytes"] = {"compress": comp, "index_topk": idx_bytes, "sparse_attn": attn_bytes}
         out["flops"] = {"index_topk": 2 * Hi * Di * sum(vis),
                         "sparse_attn": 4 * H * D * (K + W) * Tq}
+        out["index_scores"] = {"bytes": N * Di * bf + Tq * (Hi * Di * bf + Hi * 4),
+                               "flops": 2 * Hi * Di * sum(vis)}
     return out
+
+
+# ---------------------------------------------------------------------------
+# measured HBM traffic of the dominant kernel (hardware counters, committed)
+# ---------------------------------------------------------------------------
+DOMINANT_KERNELS = {
+    "index_scores": ["index_decode (decode) / index_prefill (prefill)"],
+    "hca_attn": ["attn_mfma<false, true>", "attn_combine<bf16>"],
+}
+KERNEL_SOURCES = {
+    "index_scores": ["indexer.hip", "common.h", "kernels.h"],
+    "hca_attn": ["attn.hip", "common.h", "kernels.h"],
+}
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+
+
+def kernel_source_hash(dom):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[dom]:
+        with open(os.path.join(ROOT, "long_context_sparse_11_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kind, dom):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, each scaled by what it
+    reads for the calibration kernel), from the committed counter record of
+    this workload; None when there is none or the kernel source changed since."""
+    try:
+        with open(COUNTERS) as fh:
+            rec = json.load(fh).get(kind)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel") != dom or rec.get("source_sha256") != kernel_source_hash(dom):
+        return None
+    return int(rec["hbm_bytes_per_launch"])
 
 
 # ---------------------------------------------------------------------------
@@ -327,10 +385,11 @@ def main():
         copies.append(c)
     steps = [Step(kind, c, L, torch) for c in copies]
 
-    # calibration copy kernel of known size (also flushes the Infinity Cache)
-    cal_src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    # calibration kernel of known traffic for the hardware byte counters
+    # (reads and writes 512 MiB; also flushes the Infinity Cache)
+    cal_src = torch.zeros(CAL_BYTES, dtype=torch.uint8, device="cuda")
     cal_dst = torch.empty_like(cal_src)
-    cal_dst.copy_(cal_src)
+    torch.bitwise_not(cal_src, out=cal_dst)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -361,6 +420,13 @@ def main():
                 for r in range(reps_call):
                     steps[r % n_copies].calls()[k][1]()
             call_graphs.append(cg)
+        dom_graph = torch.cuda.CUDAGraph()
+        for st in steps[:2]:
+            st.dominant()[1]()   # allocates its output before capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(dom_graph):
+            for r in range(reps_call):
+                steps[r % n_copies].dominant()[1]()
         torch.cuda.synchronize()
 
     def run(i):  # replay i covers steps i*per_graph .. (i+1)*per_graph-1
@@ -404,25 +470,30 @@ def main():
         call_us = {n: float(np.median(timed([(lambda i=i, k=k: steps[i % n_copies].calls()[k][1]())
                                              for i in range(20)]))) for k, n in enumerate(names)}
 
-    # roofline of the dominant call: the one moving the most algorithmic bytes
-    if kind == "prefill":
-        dom = max(work["flops"], key=lambda n: work["flops"][n])
+    # roofline of the dominant kernel: its per-launch duration from HIP
+    # events around replays of a graph of reps_call launches (rotating input
+    # copies), on the library's stream
+    dom = steps[0].dominant()[0]
+    if use_graph:
+        dom_us = float(np.median(timed([dom_graph.replay] * 10))) / reps_call
     else:
-        dom = max(work["bytes"], key=lambda n: work["bytes"][n])
-    dom_bytes = work["bytes"][dom]
-    dom_flops = work["flops"].get(dom, 0)
+        dom_us = float(np.median(timed([(lambda i=i: steps[i % n_copies].dominant()[1]())
+                                        for i in range(20)])))
+    dw = work[dom]
     if kind == "prefill":
-        ach = work["flops"][dom] / (call_us[dom] * 1e-6) / 1e12
+        ach = dw["flops"] / (dom_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
     else:
-        ach = dom_bytes / (call_us[dom] * 1e-6) / 1e9
+        ach = dw["bytes"] / (dom_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = measured_traffic(kind, dom)
     roof["kernel"] = dom
-    roof["algorithmic_bytes"] = int(dom_bytes)
-    roof["algorithmic_flops"] = int(dom_flops)
-    roof["avg_us"] = round(call_us[dom], 2)
+    roof["device_kernels"] = DOMINANT_KERNELS[dom]
+    roof["algorithmic_bytes_per_launch"] = int(dw["bytes"])
+    roof["algorithmic_flops_per_launch"] = int(dw["flops"])
+    roof["avg_launch_us"] = round(dom_us, 2)
 
     cpu = None
     if not a.no_cpu:

@@ -117,7 +117,8 @@ int csa_compress(int dt, int B, int T, int D, int m, int overlap,
  *   all_scores [B, Tq, N_cap] f32  every score of the visible entries;
  *                                  later columns unspecified (may be NULL)
  *   ws         workspace of csa_index_topk_ws_bytes(B, Tq, Hi, N_cap, K)
- * Supported: Hi <= 64, Di <= 256, 1 <= K <= 4096, N_cap <= 2^26.
+ * Supported: Hi <= 64, Di <= 256, Hi * Di <= 8192, 1 <= K <= 4096,
+ * N_cap <= 2^26.
  * ------------------------------------------------------------------------- */
 int csa_index_topk(int dt, int B, int Tq, int Hi, int Di, int N_cap, int K, int m,
                    const void* q_idx, const float* w_idx, const void* k_idx,
@@ -125,6 +126,21 @@ int csa_index_topk(int dt, int B, int Tq, int Hi, int Di, int N_cap, int K, int 
                    int32_t* idx_out, float* score_out, float* all_scores,
                    void* ws, size_t ws_bytes, void* stream);
 size_t csa_index_topk_ws_bytes(int B, int Tq, int Hi, int N_cap, int K);
+
+/* ---------------------------------------------------------------------------
+ * csa_index_scores - the lightning indexer scores alone (the scoring half
+ * of csa_index_topk, same kernels, no selection).
+ *
+ * [P2] section 3.2.2 (eqs. 13-16): I[t,s] = sum_h w[t,h] * ReLU(q[t,h] .
+ * K[s]) for every entry s visible to query t (visibility as in
+ * csa_index_topk).  Arguments as csa_index_topk; scores [B, Tq, N_cap] f32
+ * receives the visible columns of every row, later columns are left
+ * untouched.  No workspace.  Supported shapes as csa_index_topk.
+ * ------------------------------------------------------------------------- */
+int csa_index_scores(int dt, int B, int Tq, int Hi, int Di, int N_cap, int m,
+                     const void* q_idx, const float* w_idx, const void* k_idx,
+                     const int32_t* n_entries, const int64_t* q_pos0, float* scores,
+                     void* stream);
 
 /* ---------------------------------------------------------------------------
  * csa_sparse_attn - shared-K=V multi-query attention with a per-head sink

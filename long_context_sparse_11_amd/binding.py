@@ -30,6 +30,9 @@ _SIGS = {
                                   _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                   _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                   _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "csa_index_scores": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                     _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                     _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "csa_index_topk_ws_bytes": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int]),
     "csa_sparse_attn": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                    _c.c_double, _c.c_float, _c.c_void_p, _c.c_void_p, _c.c_int,
@@ -166,6 +169,26 @@ def csa_index_topk(q_idx, w_idx, k_idx, n_entries, q_pos0, K, m, *, want_scores=
                               _stream(stream))
     _check(st, "csa_index_topk")
     return idx_out, score_out, all_scores
+
+
+def csa_index_scores(q_idx, w_idx, k_idx, n_entries, q_pos0, m, *, out=None, stream=None):
+    """Indexer scores of the visible entries (no selection).  Returns scores
+    [B, Tq, N_cap] float32; columns past a query's visible count are left as
+    they were (uninitialised when ``out`` is not given)."""
+    B, Tq, Hi, Di = q_idx.shape
+    N_cap = k_idx.shape[1]
+    _dev(q_idx, w_idx, k_idx, n_entries, q_pos0)
+    _f32(w_idx), _i64(q_pos0)
+    if n_entries.dtype != torch.int32:
+        raise TypeError("n_entries is int32")
+    if out is None:
+        out = torch.empty((B, Tq, N_cap), dtype=torch.float32, device=q_idx.device)
+    elif tuple(out.shape) != (B, Tq, N_cap) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out is a contiguous float32 [B, Tq, N_cap] tensor")
+    st = lib().csa_index_scores(_dt(q_idx), B, Tq, Hi, Di, N_cap, m, _p(q_idx), _p(w_idx),
+                                _p(k_idx), _p(n_entries), _p(q_pos0), _p(out), _stream(stream))
+    _check(st, "csa_index_scores")
+    return out
 
 
 def csa_attn_ws_bytes(B, Tq, H, D, keys_per_query):

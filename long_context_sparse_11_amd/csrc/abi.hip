@@ -129,6 +129,19 @@ CSA_EXPORT int csa_index_topk(int dt, int B, int Tq, int Hi, int Di, int N_cap, 
   return status_of(launch_topk(tb, (int)q, s));
 }
 
+CSA_EXPORT int csa_index_scores(int dt, int B, int Tq, int Hi, int Di, int N_cap, int m,
+                                const void* q_idx, const float* w_idx, const void* k_idx,
+                                const int32_t* n_entries, const int64_t* q_pos0, float* scores,
+                                void* stream) {
+  if (dt != CSA_F32 && dt != CSA_BF16) return CSA_ERR_ARG;
+  if (B < 0 || Tq < 0 || Hi <= 0 || Di <= 0 || N_cap < 0 || m <= 0) return CSA_ERR_ARG;
+  if (B == 0 || Tq == 0 || N_cap == 0) return CSA_OK;
+  if (!q_idx || !w_idx || !k_idx || !n_entries || !q_pos0 || !scores) return CSA_ERR_ARG;
+  if (Hi > 64 || Di > 256 || Hi * Di > 8192 || N_cap > (1 << 26)) return CSA_ERR_UNSUPPORTED;
+  IndexArgs ia{dt, B, Tq, Hi, Di, N_cap, m, q_idx, w_idx, k_idx, n_entries, q_pos0, scores};
+  return status_of(launch_index_scores(ia, (hipStream_t)stream));
+}
+
 // ------------------------------------------------------------------ attention
 CSA_EXPORT size_t csa_attn_ws_bytes(int B, int Tq, int H, int D, int keys_per_query) {
   if (B <= 0 || Tq <= 0 || H <= 0 || D <= 0 || keys_per_query <= 0) return 0;

@@ -554,3 +554,28 @@ def test_index_outlier_stretches_range(N, outlier):
     if N <= 16384:
         c1 = _linear_bin_count(alls[0, 0, :N], K)
         assert (c1 > 64) if outlier > 1000 else (c1 <= 64), c1
+
+
+@pytest.mark.parametrize("Tq,pos0", [(1, 4 * 5000 - 1), (12, 4 * 900)])
+def test_index_scores_alone_match_index_topk_and_oracle(Tq, pos0):
+    """csa_index_scores is the scoring half of csa_index_topk: the same
+    float32 scores (bitwise), the oracle's within the score tolerance, and
+    columns past a query's visible count untouched."""
+    rng = np.random.default_rng(Tq)
+    N, K, m = 5000, 512, 4
+    q = synth.Tensor(rng.standard_normal((2, Tq, 64, 128)).astype(np.float32), "bf16")
+    w = (0.02 * rng.standard_normal((2, Tq, 64))).astype(np.float32)
+    k = synth.Tensor(rng.standard_normal((2, N, 128)).astype(np.float32), "bf16")
+    n_ent = np.array([N, N - 7], np.int32)
+    p0 = np.array([pos0, pos0 + 3])
+    out = torch.full((2, Tq, N), 123.0, dtype=torch.float32, device="cuda")
+    L.csa_index_scores(dev(q), dev(w), dev(k), i32(n_ent), i64(p0), m, out=out)
+    _, _, alls = _index_case(q, w, k, n_ent, p0, K, m)
+    got = host(out)
+    _, rsc = O.csa_index_topk(q.f32, w, k.f32, n_ent, p0, K, m)
+    for b in range(2):
+        for t in range(Tq):
+            nv = O.visible_count(int(p0[b]) + t, m, int(n_ent[b]))
+            assert np.array_equal(got[b, t, :nv], alls[b, t, :nv])
+            assert np.abs(got[b, t, :nv].astype(np.float64) - rsc[b, t, :nv]).max() <= SCORE_ATOL_BF16
+            assert np.all(got[b, t, nv:] == 123.0)

@@ -30,7 +30,7 @@ def lib():
 
 def test_header_declares_the_four_calls():
     names = declared_functions()
-    for n in ("csa_compress", "csa_index_topk", "csa_sparse_attn", "hca_attn",
+    for n in ("csa_compress", "csa_index_topk", "csa_index_scores", "csa_sparse_attn", "hca_attn",
               "csa_index_topk_ws_bytes", "csa_attn_ws_bytes", "csa_status_string"):
         assert n in names
 
@@ -113,6 +113,23 @@ def test_index_validation(lib):
     assert _index(lib, K=5000) == CSA_ERR_UNSUPPORTED
     assert _index(lib, ws=N) == CSA_ERR_WORKSPACE
     assert _index(lib, wsb=16) == CSA_ERR_WORKSPACE
+
+
+def _scores(lib, **kw):
+    a = dict(dt=1, B=2, Tq=1, Hi=64, Di=128, N=1000, m=4, out=P)
+    a.update(kw)
+    return lib.csa_index_scores(a["dt"], a["B"], a["Tq"], a["Hi"], a["Di"], a["N"], a["m"],
+                                P, P, P, P, P, a["out"], N)
+
+
+def test_index_scores_validation(lib):
+    assert _scores(lib, m=0) == CSA_ERR_ARG
+    assert _scores(lib, dt=3) == CSA_ERR_ARG
+    assert _scores(lib, out=N) == CSA_ERR_ARG
+    assert _scores(lib, B=0) == CSA_OK
+    assert _scores(lib, N=0) == CSA_OK                   # no entries: nothing to score
+    assert _scores(lib, Hi=65) == CSA_ERR_UNSUPPORTED
+    assert _scores(lib, Hi=64, Di=256) == CSA_ERR_UNSUPPORTED   # Hi * Di > 8192
 
 
 def _attn(lib, fn="csa_sparse_attn", **kw):
