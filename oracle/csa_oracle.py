@@ -147,6 +147,10 @@ def compress(c_a, z_a, bias_a, m: int, *, c_b=None, z_b=None, bias_b=None,
     Inputs are [T, D] (``prev_*`` [m, D]; biases [m, D]; gain [D]).
     The pages print no pooled value of the real operator, so the pins are
     closed forms, invariants and a library-softmax brute force on tiny inputs.
+    Two parts rest on readings the pages do not fix and are parity unpinned
+    against them (the tests pin them only to the reading): the overlap
+    direction (stream b from block i-1) and the entry's RoPE position
+    (pos0 + m*i).
     """
     c_a = np.asarray(c_a, dtype=np.float64)
     T, D = c_a.shape
