@@ -27,6 +27,10 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
+# attention keeps its output accumulators in ordinary VGPRs (MFMA VGPR form):
+# the online-softmax rescale touches them with VALU ops, and the AGPR form
+# made the allocator shuttle them between register files on every tile
+SOURCE_FLAGS = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _run(cmd):
@@ -43,7 +47,8 @@ def build(verbose: bool = True, extra_flags: list[str] | None = None) -> str:
 
     def compile_one(src):
         obj = os.path.join(OBJ, src.replace(".hip", ".o"))
-        rc, out = _run([HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
+        rc, out = _run([HIPCC, *flags, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+                        "-o", obj])
         return src, obj, rc, out
 
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:

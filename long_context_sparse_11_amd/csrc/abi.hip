@@ -163,6 +163,7 @@ int attn_common(AttnArgs& a, double rope_base, int keys_per_query, void* ws, siz
   if (a.D > 1024 || a.H > 128 || (a.D & 1)) return CSA_ERR_UNSUPPORTED;
   a.rope_theta1 = a.R > 0 ? pow(rope_base, -2.0 / a.R) : 0.0;
   if (attn_uses_mfma(a.dt, a.H, a.D, a.R)) {
+    if (a.csa && (int64_t)keys_per_query > attn_max_csa_keys()) return CSA_ERR_UNSUPPORTED;
     a.splits = attn_splits(a.dt, a.B, a.Tq, a.H, a.D, keys_per_query);
     if (a.splits > 1) {
       const size_t need = attn_ws_bytes(a.dt, a.B, a.Tq, a.H, a.D, keys_per_query);

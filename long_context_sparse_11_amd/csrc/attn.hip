@@ -11,20 +11,13 @@
 //   the query, rotation by -t of the output's rope slice.
 //
 // attn_generic  any shape/dtype; one wave per (query, head), VALU.
-// attn_mfma     bf16, 64 heads x 512 (the Flash shape).  One workgroup of 4
-//               waves per (query, key split).  Wave w owns 128 channels of
-//               every row (16 of each 64-channel stretch): it gathers its
-//               share of 32 rows per tile straight from HBM into MFMA
-//               operands (each row is read once and serves all 64 heads),
-//               computes
-//               the partial logits S^T[row][head] over its channels,
-//               the four partials are summed through LDS, every wave runs
-//               the same online softmax (running max/sum per head, seeded
-//               empty; the sink enters once at the end), and the wave
-//               accumulates O^T[channel][head] for its own channels.
-//               v_mfma_f32_32x32x16_bf16 throughout; the PV step reads its
-//               row operand transposed from a wave-private LDS copy of the
-//               tile, and its P operand is the lane's own softmax output.
+// attn_hs       bf16, 64 heads x 512 (the Flash shape).  One workgroup of 4
+//               waves per (query, key split); wave w owns heads 16w .. 16w+15
+//               over all 512 channels.  A tile's 32 rows are copied HBM ->
+//               LDS once (each row serves all 64 heads); QK^T and PV run on
+//               v_mfma_f32_16x16x32_bf16 with an online softmax per head
+//               (running max/sum, seeded empty; the sink enters once at the
+//               end).
 // combine       merges key-range splits and adds the sink once.
 #include "kernels.h"
 
@@ -161,16 +154,6 @@ __global__ __launch_bounds__(256) void attn_generic(AttnArgs a) {
 }
 
 // --------------------------------------------------------------------- MFMA
-constexpr int kAtRows = 32;       // rows per tile
-constexpr int kRtPitch = 128;     // bf16 per LDS row of a wave's row copy (256 B, swizzled)
-
-// The wave's copy of a tile row (its 256-byte slice, sixteen 16-byte chunks)
-// stores chunk c at position c ^ rt_swz(row): the 16-byte stash writes of 16
-// consecutive rows and the 8-byte transposing reads of 4 consecutive rows
-// then fall on distinct LDS banks.
-__device__ __forceinline__ int rt_swz(int row) { return (4 * row + (row >> 2)) & 15; }
-
-constexpr int kAtMaxSplitRows = 4096;  // rows of a multi-tile CSA split (LDS index stage)
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr;
 constexpr int kAtD = 512;
@@ -184,349 +167,349 @@ __device__ __forceinline__ float half_swap(float x) {
   return __uint_as_float(__lane_id() < 32 ? r[1] : r[0]);
 }
 
-// CSA: rows come from the selected index list (else every visible entry).
-// MULTI: a split may hold more than one 32-row tile (else exactly one, and
-// the kernel is straight-line code with no prefetch).
+// ------------------------------------------------------------- head split
+// attn_hs: bf16, 64 heads x 512 (the Flash shape).  One workgroup of 4 waves
+// per (query, key split); wave w owns heads 16w .. 16w+15 over all 512
+// channels, so each head's logits are complete inside one wave: no partial
+// logits cross waves and each head's online softmax runs once.
+//
+// A tile's 32 rows are copied HBM -> LDS once (global_load_lds, 16 bytes per
+// lane, a whole 1 KiB row per wave instruction) and serve the four waves;
+// tiles are double-buffered.  MFMA v_mfma_f32_16x16x32_bf16 throughout
+// (lane l feeds A[l % 16][8(l/16) .. +7] and B[8(l/16) .. +7][l % 16];
+// accumulator element r is C[4(l/16) + r][l % 16]):
+//   S^T[key][head] += R[key][ch] Q^T[ch][head]: A = 16 rows x 32 channels
+//     from LDS, B = the lane's query slice held in registers;
+//   O^T[ch][head] += R^T[ch][key] P^T[key][head]: B = the lane's own
+//     softmax values (the contraction's key slots are permuted so that the
+//     accumulator layout of S^T is the operand layout of P^T: slot e < 4 is
+//     key 4(l/16) + e, slot e >= 4 is key 16 + 4(l/16) + e - 4), A = rows
+//     read transposed from LDS (ds_read_b64_tr_b16, the same key permutation).
+// Row r of a tile stores its 16-byte chunk c at position c ^ hs_swz(r): the
+// QK reads (16 rows, one chunk) and the transposing PV reads (4 rows, two
+// chunks) then fall on distinct banks.
+constexpr int kHsRows = 32;
+constexpr int kHsMaxSplitRows = 2048;  // rows of a multi-tile CSA split (LDS index stage)
+
+// Conflict-free under either bank model of a 16-byte read (8-lane groups
+// on 32 banks, or 16-lane groups on 64): the 16 rows of a QK read differ in
+// bits 0-2 within each half and in bits 0-3 overall, and the 4 rows of a
+// transposing read differ in bits 1-2.
+__device__ __forceinline__ int hs_swz(int r) {
+  return ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3);
+}
+
+// Value of lane (l ^ 16): v_permlane16_swap exchanges 16-lane rows 0<->1, 2<->3.
+__device__ __forceinline__ float row_swap16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(((__lane_id() >> 4) & 1) ? r[0] : r[1]);
+}
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
 template <bool CSA, bool MULTI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_mfma(AttnArgs a) {
+void attn_hs(AttnArgs a) {
+  // two row buffers as distinct objects: with every access naming a fixed
+  // one, the compiler can tell that a copy into one does not touch the other
+  // (it would otherwise wait for the copy before reading)
+  __shared__ __attribute__((aligned(16))) bf16_t s_rows0[kHsRows * kAtD];
+  __shared__ __attribute__((aligned(16))) bf16_t s_rows1[kHsRows * kAtD];
   __shared__ float s_cos[kAtD / 2], s_sin[kAtD / 2];
-  __shared__ __attribute__((aligned(16))) f32x4_t sx[2][4][2][4][64];  // [buf][wave][ht][rq][lane]
-  __shared__ __attribute__((aligned(16))) bf16_t rt[4][kAtRows * kRtPitch];
-  __shared__ int32_t s_idx[MULTI && CSA ? kAtMaxSplitRows : 1];
+  __shared__ __attribute__((aligned(16))) int32_t s_idx[MULTI && CSA ? kHsMaxSplitRows : 4];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int j = lane & 31, g = lane >> 5;
+  const int c16 = lane & 15, G = lane >> 4;
+  const int h = 16 * wave + c16;  // this lane's head
   const int qi = blockIdx.y, sp = blockIdx.x, S = gridDim.x;
   const int b = qi / a.Tq, t = qi - b * a.Tq;
   const int R = a.R;
   const int rope0 = kAtD - R;
-  // Channel ownership: lane (g, j) of wave w holds, in its slot s (0..7),
-  // 8 consecutive channels of row / head j (+32); the wave's local channel
-  // 64g + 8s + e (its LDS row copy, its PV rows) is global channel
-  // 8 * blk(s, g) + e.  Multi-tile splits stream rows, and there each lane
-  // reads one contiguous 128-byte stretch (blocks 16w + 8g + s).  A
-  // single-tile split is latency-bound instead, and there the blocks are
-  // 8s + 2w + g: the eight lane groups each own one block of every
-  // 64-channel stretch, so the rope channels at the end of the row are
-  // spread over all of them rather than piled on one half-wave, whose
-  // rotation would otherwise hold up the whole workgroup.
-  auto blk = [&](int s, int gg) { return MULTI ? 16 * wave + 8 * gg + s : 8 * s + 2 * wave + gg; };
-  auto chan = [&](int s) { return 8 * blk(s, g); };
 
-  // ---- Every global load below is unconditional (clamped or redirected
-  // addresses), so the compiler can count outstanding loads exactly and
-  // waits only for the one it needs.  Order: the selected indices of tiles
-  // 0 and 1 (the row loads wait on them), the query slice, then tile 0's
-  // rows.  A CSA split covers a fixed range of the list [K selected rows,
-  // then up to min(W, L_win) window rows], so its bounds are known before
-  // the query position is.
+  // ---- split bounds (CSA: a fixed range of [K selected, up to
+  // min(W, L_win) window rows], known before the position)
   int start = 0, end = 0;
   if (CSA) {
     const int wc = (a.W > 0 && a.L_win > 0) ? min(a.W, a.L_win) : 0;
     const int Lmax = a.K + wc;
-    const int per = (((Lmax + S - 1) / S) + kAtRows - 1) / kAtRows * kAtRows;
+    const int per = (((Lmax + S - 1) / S) + kHsRows - 1) / kHsRows * kHsRows;
     start = min(Lmax, sp * per);
     end = min(Lmax, start + per);
   }
-  // selected index of this lane's row at list position j0 + j (a harmless
-  // word when there is none: a position past K, or K == 0)
+  // tile 0's selected indices: lane l (< 32) holds row start + l's (a
+  // harmless word when there is none; every load here is unconditional so
+  // the compiler counts outstanding loads exactly)
   const bool has_idx = CSA && a.K > 0;
   const int32_t* idx_q = has_idx ? a.idx + (int64_t)qi * a.K : (const int32_t*)a.q_pos0;
-  auto load_idx = [&](int j0) -> int32_t {
-    return idx_q[has_idx ? min(max(j0 + j, 0), a.K - 1) : 0];
-  };
-  const int32_t idx0 = CSA ? load_idx(start) : 0;  // tile 0
-  bf16x8_t qb[2][8];
+  const int32_t idx0 = idx_q[has_idx ? min(max(start + (lane & 31), 0), a.K - 1) : 0];
+
+  // the lane's query slice: head h, channels 32 ks + 8G .. +7
+  const bf16_t* qrow = (const bf16_t*)a.q + ((int64_t)qi * kAtH + h) * kAtD;
+  bf16x8_t qb[16];
 #pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
-    const bf16_t* qp = (const bf16_t*)a.q + ((int64_t)qi * kAtH + ht * 32 + j) * kAtD;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qb[ht][s] = *reinterpret_cast<const bf16x8_t*>(qp + chan(s));
-  }
-  const bf16_t* q_slice = (const bf16_t*)a.q + ((int64_t)qi * kAtH + j) * kAtD;
+  for (int ks = 0; ks < 16; ++ks) qb[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * ks + 8 * G);
+
   const int64_t tpos = a.q_pos0[b] + t;
   const KeyRange kr = key_range(a, b, qi, tpos);
   if (!CSA) {
     const int L = kr.nsel + kr.nwin;
-    const int per = (((L + S - 1) / S) + kAtRows - 1) / kAtRows * kAtRows;
+    const int per = (((L + S - 1) / S) + kHsRows - 1) / kHsRows * kHsRows;
     start = min(L, sp * per);
     end = min(L, start + per);
   }
-
-  // Row at list position j0 + j into this wave's operand registers (its 128
-  // channels of the row).  An absent row (empty index slot, window row
-  // beyond the buffer, or past the split) reads the lane's own query slice
-  // instead: `valid` masks it out of the softmax, so its (finite) values
-  // meet a zero weight in the PV product.
   const bf16_t* pool_b = (const bf16_t*)a.pool + (int64_t)b * a.N_cap * kAtD;
   const bf16_t* win_b = (const bf16_t*)a.win + ((int64_t)b * a.L_win + kr.win_r0) * kAtD;
-  auto load_rows = [&](int j0, int sidx, bf16x8_t(&dst)[8], bool& valid) {
-    const int jj = j0 + j;
+  const bf16_t* dummy = (const bf16_t*)a.q + (int64_t)qi * kAtH * kAtD;  // 1 KiB always readable
+
+  // Request tile j0's 32 rows into LDS buffer `dst` and return their
+  // validity mask.  Lane l (< 32) resolves row j0 + l (sidx_l: its selected
+  // index) to a source address with selects, not branches (an invalid row
+  // reads a harmless 1 KiB); wave w then copies rows 8w .. 8w+7, one 1 KiB
+  // row per global_load_lds: the row's address is read from its lane into
+  // scalar registers and lane i fetches the 16-byte chunk that belongs at
+  // position i (i ^ hs_swz(row)).
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint64_t pool_a = (uint64_t)pool_b, win_a = (uint64_t)win_b, dummy_a = (uint64_t)dummy;
+  auto load_tile = [&](int j0, int sidx_l, bf16_t* dst) -> uint32_t {
+    const int jj = j0 + (lane & 31);
     const bool in_sel = jj < kr.nsel;
-    const int srow = CSA ? sidx : jj;
+    const int srow = CSA ? sidx_l : jj;
     const int wrow = jj - kr.nsel;
-    valid = jj < end && (in_sel ? (srow >= 0 && srow < a.N_cap) : wrow < kr.nwin);
-    const bf16_t* pb = pool_b;  // values, so the selects below are of pointers, not of
-    const bf16_t* wb = win_b;   // the captured variables (which would put them in scratch)
-    const bf16_t* p = (in_sel ? pb : wb) + (int64_t)(in_sel ? srow : wrow) * kAtD;
-    p = valid ? p : q_slice;
+    const bool valid =
+        lane < 32 && jj < end && (in_sel ? (srow >= 0 && srow < a.N_cap) : wrow < kr.nwin);
+    const uint64_t sa = in_sel ? pool_a + (uint64_t)((int64_t)srow * (kAtD * 2))
+                               : win_a + (uint64_t)((int64_t)wrow * (kAtD * 2));
+    const uint64_t src = valid ? sa : dummy_a;
+    const int lo = (int)(uint32_t)src, hi = (int)(uint32_t)(src >> 32);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) dst[s] = *reinterpret_cast<const bf16x8_t*>(p + chan(s));
+    for (int u = 0; u < 8; ++u) {
+      const int r = 8 * wv + u;
+      const uint64_t rs = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, r) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane(lo, r);
+      const bf16_t* gp = reinterpret_cast<const bf16_t*>(rs) + 8 * (lane ^ hs_swz(r));
+      __builtin_amdgcn_global_load_lds((const void*)gp, (lds_void_ptr)(dst + r * kAtD), 16, 0, 0);
+    }
+    return (uint32_t)__ballot(valid);
   };
 
-  // rope table at +tpos (computed while tile 0's indices are in flight)
+  // ---- prologue: tile 0's rows, the rope table, the split's later indices
+  uint32_t vmask = load_tile(start, idx0, s_rows0);
   for (int p = tid; p < R / 2; p += 256) rope_cos_sin(tpos, p, a.rope_theta1, s_cos[p], s_sin[p]);
-
-  bf16x8_t ra[8];
-  bool va = false;
-  load_rows(start, idx0, ra, va);
   if constexpr (MULTI && CSA) {
-    // later tiles' indices, staged once for the whole split (after tile 0's
-    // rows are requested: waiting on these loads then costs nothing extra)
     const int sel_end = min(end, a.K);
-    for (int jj = start + kAtRows + tid; jj < sel_end; jj += 256)
+    for (int jj = start + kHsRows + tid; jj < sel_end; jj += 256)
       s_idx[jj - start] = a.idx[(int64_t)qi * a.K + jj];
   }
-  __syncthreads();  // rope table, staged indices
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
-  // rotate the query's rope channels at +tpos: only the lane's slots that
-  // reach the rope part
+  // rotate the query slice's rope channels at +tpos (each lane its own pairs)
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int c0 = chan(s);
+  for (int ks = 0; ks < 16; ++ks) {
+    const int c0 = 32 * ks + 8 * G;
     if (c0 + 8 <= rope0) continue;
-    float cs[4], sn[4];
+    const u32x4_t w = __builtin_bit_cast(u32x4_t, qb[ks]);
+    u32x4_t pk;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int c = c0 + 2 * k;
-      const int pj = max(c - rope0, 0) >> 1;
       const bool rot = c >= rope0;
-      cs[k] = rot ? s_cos[pj] : 1.f;
-      sn[k] = rot ? s_sin[pj] : 0.f;
+      const int pj = max(c - rope0, 0) >> 1;
+      const float cs = rot ? s_cos[pj] : 1.f, sn = rot ? s_sin[pj] : 0.f;
+      const float x0 = __uint_as_float(w[k] << 16), x1 = __uint_as_float(w[k] & 0xffff0000u);
+      pk[k] = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
     }
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      const u32x4_t w = __builtin_bit_cast(u32x4_t, qb[ht][s]);
-      u32x4_t pk;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float x0 = __uint_as_float(w[k] << 16), x1 = __uint_as_float(w[k] & 0xffff0000u);
-        pk[k] = pack_bf16x2(x0 * cs[k] - x1 * sn[k], x0 * sn[k] + x1 * cs[k]);
-      }
-      qb[ht][s] = __builtin_bit_cast(bf16x8_t, pk);
-    }
+    qb[ks] = __builtin_bit_cast(bf16x8_t, pk);
   }
 
-  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
-  f32x16_t oacc[4][2];
+  float mrun = -INFINITY, lrun = 0.f;  // this lane's head (shared by its 4 row groups)
+  f32x4_t oacc[32];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) oacc[dt][ht] = f32x16_t{};
+  for (int cb = 0; cb < 32; ++cb) oacc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.scale * kLog2e;
-  bf16_t* myrt = rt[wave];
 
-  int buf = 0;
-  for (int j0 = start; j0 < end; j0 += kAtRows) {
-    // partial logits over this wave's 128 channels
-    f32x16_t s0 = {}, s1 = {};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[s], qb[0][s], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[s], qb[1][s], s1, 0, 0, 0);
-    }
-    // wave-private copy of the rows for the transposed PV operand
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      *reinterpret_cast<bf16x8_t*>(&myrt[j * kRtPitch + 8 * ((8 * g + s) ^ rt_swz(j))]) = ra[s];
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      sx[buf][wave][0][rq][lane] = f32x4_t{s0[4 * rq], s0[4 * rq + 1], s0[4 * rq + 2], s0[4 * rq + 3]};
-      sx[buf][wave][1][rq][lane] = f32x4_t{s1[4 * rq], s1[4 * rq + 1], s1[4 * rq + 2], s1[4 * rq + 3]};
-    }
-    const uint64_t vmask = __ballot(va);
-    // the rows now live in LDS: reuse their registers for the next tile's
-    // loads, which then overlap this tile's softmax and PV
+  // One tile: logits, softmax, PV from `rows`; in multi-tile splits the
+  // next tile's rows are first requested into `next` (the other buffer).
+  auto tile_step = [&](int j0, const bf16_t* rows, bf16_t* next) {
+    uint32_t vnext = 0;
     if constexpr (MULTI) {
-      if (j0 + kAtRows < end) {
-        const int jn = j0 + kAtRows + j;
-        const int idx_n = (CSA && jn < min(end, a.K)) ? s_idx[jn - start] : 0;
-        load_rows(j0 + kAtRows, idx_n, ra, va);
-      }
-    }
-    __syncthreads();
-
-    float p[2][16];
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        f32x4_t x = sx[buf][0][ht][rq][lane];
-        x += sx[buf][1][ht][rq][lane];
-        x += sx[buf][2][ht][rq][lane];
-        x += sx[buf][3][ht][rq][lane];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int n = 8 * rq + 4 * g + e;
-          p[ht][4 * rq + e] = ((vmask >> n) & 1) ? x[e] * sl2 : -INFINITY;
-        }
-      }
-    buf ^= 1;
-
-    // Online softmax with a lazily moved reference: a head's running max
-    // only moves when a tile exceeds it by more than 2^8 (log2 units), so
-    // exp2(s - mrun) stays below 256 and the accumulator is rescaled only on
-    // those (rare) tiles.  The first tile with a valid row always moves it.
-    float tm[2];
-    bool move = false;
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      float x = p[ht][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) x = fmaxf(x, p[ht][r]);
-      tm[ht] = fmaxf(x, half_swap(x));
-      move |= tm[ht] > mrun[ht] + 8.f;
-    }
-    if (__ballot(move)) {
-#pragma unroll
-      for (int ht = 0; ht < 2; ++ht) {
-        const float mnew = fmaxf(mrun[ht], tm[ht]);
-        if (mnew > mrun[ht]) {
-          const float alpha = exp2f(mrun[ht] - mnew);
-          lrun[ht] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) oacc[dt][ht] *= alpha;
-          mrun[ht] = mnew;
-        }
-      }
-    }
-    bf16x8_t pb[2][2];
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      const bool none = mrun[ht] == -INFINITY;  // no valid row seen yet
-#pragma unroll
-      for (int r = 0; r < 16; ++r) p[ht][r] = none ? 0.f : exp2f(p[ht][r] - mrun[ht]);
-      float rs = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) rs += p[ht][r];
-      rs += half_swap(rs);
-      lrun[ht] += rs;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        u32x4_t pk;
-        pk.x = pack_bf16x2(p[ht][8 * ks + 0], p[ht][8 * ks + 1]);
-        pk.y = pack_bf16x2(p[ht][8 * ks + 2], p[ht][8 * ks + 3]);
-        pk.z = pack_bf16x2(p[ht][8 * ks + 4], p[ht][8 * ks + 5]);
-        pk.w = pack_bf16x2(p[ht][8 * ks + 6], p[ht][8 * ks + 7]);
-        pb[ht][ks] = __builtin_bit_cast(bf16x8_t, pk);
+      // the next tile's rows are requested before this one is used
+      if (j0 + kHsRows < end) {
+        const int jn = j0 + kHsRows;
+        // row jn + l's selected index (entries past the selected part are
+        // never used; jn - start + l stays below the split's row count)
+        int sidx_l = 0;
+        if constexpr (CSA) sidx_l = s_idx[jn - start + (lane & 31)];
+        vnext = load_tile(jn, sidx_l, next);
       }
     }
 
-    // O^T[channel][head] += R^T[channel][row] P^T[row][head].  The R^T
-    // operand comes from ds_read_b64_tr_b16: in each 16-lane group, lane c
-    // points at 4 consecutive channels of row (c / 4) of a 4-row block and
-    // lane i receives channel i of all 4 rows, i.e. 4 consecutive K slots of
-    // its own M row; two reads (rows +0..3 and +8..11) make one operand.
-    const int tr_row = 4 * g + ((lane & 15) >> 2);
-    const int tr_q = lane & 3;
-    const int tr_h = (lane >> 4) & 1;
+    // logits S^T[key][head] over all 512 channels, two 16-key blocks; a
+    // block's 16 operand reads are issued before its MFMAs
+    f32x4_t sacc[2];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const int chunk = dt * 4 + 2 * tr_h + (tr_q >> 1);   // 16-byte chunk of the channel
-      const int sub = 4 * (tr_q & 1);                       // bf16 offset inside it
+    for (int kb = 0; kb < 2; ++kb) {
+      const int r = 16 * kb + c16;
+      const bf16_t* rp = rows + r * kAtD;
+      const int sw = hs_swz(r);
+      bf16x8_t av[16];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int r0 = 16 * ks + tr_row, r1 = r0 + 8;
+      for (int ks = 0; ks < 16; ++ks)
+        av[ks] = *reinterpret_cast<const bf16x8_t*>(rp + 8 * ((4 * ks + G) ^ sw));
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks], qb[ks], acc, 0, 0, 0);
+      sacc[kb] = acc;
+    }
+
+    // online softmax of head h over this tile's 32 keys: lane (G, c16) holds
+    // keys 16kb + 4G + r; the other three row groups hold the rest
+    float p[2][4];
+    float tmx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = 16 * kb + 4 * G + r;
+        p[kb][r] = ((vmask >> key) & 1) ? sacc[kb][r] * sl2 : -INFINITY;
+        tmx = fmaxf(tmx, p[kb][r]);
+      }
+    tmx = fmaxf(tmx, row_swap16(tmx));
+    tmx = fmaxf(tmx, half_swap(tmx));
+    // lazily moved reference: rescale only when the tile max exceeds it by
+    // more than 2^8 (log2 units); the first tile with a valid key moves it
+    if (__ballot(tmx > mrun + 8.f)) {
+      const float mnew = fmaxf(mrun, tmx);
+      if (mnew > mrun) {
+        const float alpha = exp2f(mrun - mnew);
+        lrun *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < 32; ++cb) oacc[cb] *= alpha;
+        mrun = mnew;
+      }
+    }
+    const bool none = mrun == -INFINITY;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[kb][r] = none ? 0.f : exp2f(p[kb][r] - mrun);
+        rs += p[kb][r];
+      }
+    rs += row_swap16(rs);
+    rs += half_swap(rs);
+    lrun += rs;
+    u32x4_t pk;
+    pk.x = pack_bf16x2(p[0][0], p[0][1]);
+    pk.y = pack_bf16x2(p[0][2], p[0][3]);
+    pk.z = pack_bf16x2(p[1][0], p[1][1]);
+    pk.w = pack_bf16x2(p[1][2], p[1][3]);
+    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk);
+
+    // O^T[ch][head] += R^T[ch][key] P^T[key][head]: in each 16-lane group,
+    // lane i points at key row 4G + i/4 (and 16 + 4G + i/4), channels
+    // 16cb + 4(i % 4) .. +3, and receives channel 16cb + i of the 4 rows.
+    // The transposing reads of 8 channel blocks go out before their MFMAs.
+    const int kr0 = 4 * G + (c16 >> 2);
+    const int kr1 = kr0 + 16;
+    const bf16_t* rp0 = rows + kr0 * kAtD;
+    const bf16_t* rp1 = rows + kr1 * kAtD;
+    const int sw0 = hs_swz(kr0), sw1 = hs_swz(kr1);
+    const int q4 = c16 & 3;
+#pragma unroll
+    for (int c8 = 0; c8 < 4; ++c8) {
+      bf16x8_t av[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int cb = 8 * c8 + k;
+        const int ch = 2 * cb + (q4 >> 1);          // 16-byte chunk of the channels
+        const int sub = 4 * (q4 & 1);               // bf16 offset inside it
         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_ptr)(&myrt[r0 * kRtPitch + 8 * (chunk ^ rt_swz(r0)) + sub]));
+            (lds_s16x4_ptr)(rp0 + 8 * (ch ^ sw0) + sub));
         const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_ptr)(&myrt[r1 * kRtPitch + 8 * (chunk ^ rt_swz(r1)) + sub]));
+            (lds_s16x4_ptr)(rp1 + 8 * (ch ^ sw1) + sub));
         const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, u32x4_t{l2.x, l2.y, h2.x, h2.y});
-#pragma unroll
-        for (int ht = 0; ht < 2; ++ht)
-          oacc[dt][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ht][ks], oacc[dt][ht], 0, 0, 0);
+        av[k] = __builtin_bit_cast(bf16x8_t, u32x4_t{l2.x, l2.y, h2.x, h2.y});
       }
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        oacc[8 * c8 + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k], pb, oacc[8 * c8 + k], 0, 0, 0);
     }
+
+    if constexpr (MULTI) {
+      // the next tile's rows have landed and every wave is done with this one
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      vmask = vnext;
+    }
+  };
+
+  for (int j0 = start; j0 < end; j0 += 2 * kHsRows) {
+    tile_step(j0, s_rows0, s_rows1);
+    if (j0 + kHsRows >= end) break;
+    tile_step(j0 + kHsRows, s_rows1, s_rows0);
   }
 
-  // ---- epilogue.  Accumulator element (dt, rq, e) of lane (g, j) is the
-  // wave's local channel 32dt + 8rq + 4g + e, i.e. global channel
-  // out_chan(dt, rq) + e (4 consecutive channels).
-  auto out_chan = [&](int dt, int rq) {
-    const int sl = 4 * (dt & 1) + rq;  // slot and lane half of the local channel
-    return 8 * blk(sl, dt >> 1) + 4 * g;
-  };
+  // ---- epilogue: lane (G, c16) holds channels 16cb + 4G + r of head h
   if (S == 1) {
+    const float skl2 = a.sink[h] * kLog2e;
+    const float mf = fmaxf(mrun, skl2);
+    const float lf = lrun * exp2f(mrun - mf) + exp2f(skl2 - mf);
+    const float fac = exp2f(mrun - mf) / lf;
+    if (G == 0 && a.lse) a.lse[(int64_t)qi * kAtH + h] = (mf + log2f(lf)) * kLn2;
+    bf16_t* op = (bf16_t*)a.out + ((int64_t)qi * kAtH + h) * kAtD;
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      const int h = ht * 32 + j;
-      const float skl2 = a.sink[h] * kLog2e;
-      const float mf = fmaxf(mrun[ht], skl2);
-      const float lf = lrun[ht] * exp2f(mrun[ht] - mf) + exp2f(skl2 - mf);
-      const float fac = exp2f(mrun[ht] - mf) / lf;
-      if (wave == 0 && g == 0 && a.lse) a.lse[(int64_t)qi * kAtH + h] = (mf + log2f(lf)) * kLn2;
-      bf16_t* op = (bf16_t*)a.out + ((int64_t)qi * kAtH + h) * kAtD;
+    for (int cb = 0; cb < 32; ++cb) {
+      float o[4];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
+      for (int r = 0; r < 4; ++r) o[r] = oacc[cb][r] * fac;
+      const int c = 16 * cb + 4 * G;
+      if (c + 4 > rope0) {
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          float o[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = oacc[dt][ht][4 * rq + e] * fac;
-          const int c = out_chan(dt, rq);
-#pragma unroll
-          for (int e = 0; e < 4; e += 2) {
-            if (c + e >= rope0) {
-              const int pj = (c + e - rope0) >> 1;
-              const float cs = s_cos[pj], sn = s_sin[pj];
-              const float x0 = o[e], x1 = o[e + 1];
-              o[e] = x0 * cs + x1 * sn;
-              o[e + 1] = -x0 * sn + x1 * cs;
-            }
+        for (int e = 0; e < 4; e += 2) {
+          if (c + e >= rope0) {
+            const int pj = (c + e - rope0) >> 1;
+            const float cs = s_cos[pj], sn = s_sin[pj];
+            const float x0 = o[e], x1 = o[e + 1];
+            o[e] = x0 * cs + x1 * sn;
+            o[e + 1] = -x0 * sn + x1 * cs;
           }
-          uint2 pk;
-          pk.x = pack_bf16x2(o[0], o[1]);
-          pk.y = pack_bf16x2(o[2], o[3]);
-          *reinterpret_cast<uint2*>(op + c) = pk;
         }
       }
+      uint2 pk;
+      pk.x = pack_bf16x2(o[0], o[1]);
+      pk.y = pack_bf16x2(o[2], o[3]);
+      *reinterpret_cast<uint2*>(op + c) = pk;
     }
   } else {
+    const int64_t slot = ((int64_t)qi * S + sp) * kAtH + h;
+    if (G == 0) {
+      a.part_ml[2 * slot] = mrun;
+      a.part_ml[2 * slot + 1] = lrun;
+    }
+    // the output's rope slice is rotated back by -tpos here (the rotation is
+    // linear, so the merge of the splits commutes with it)
+    float* po = a.part_o + slot * kAtD;
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      const int h = ht * 32 + j;
-      const int64_t slot = ((int64_t)qi * S + sp) * kAtH + h;
-      if (wave == 0 && g == 0) {
-        a.part_ml[2 * slot] = mrun[ht];
-        a.part_ml[2 * slot + 1] = lrun[ht];
-      }
-      // the output's rope slice is rotated back by -tpos here (the rotation
-      // is linear, so the merge of the splits commutes with it)
-      float* po = a.part_o + slot * kAtD;
+    for (int cb = 0; cb < 32; ++cb) {
+      float o[4] = {oacc[cb][0], oacc[cb][1], oacc[cb][2], oacc[cb][3]};
+      const int c = 16 * cb + 4 * G;
+      if (c + 4 > rope0) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          float o[4] = {oacc[dt][ht][4 * rq], oacc[dt][ht][4 * rq + 1], oacc[dt][ht][4 * rq + 2],
-                        oacc[dt][ht][4 * rq + 3]};
-          const int c = out_chan(dt, rq);
-          if (c + 4 > rope0) {
-#pragma unroll
-            for (int e = 0; e < 4; e += 2) {
-              if (c + e >= rope0) {
-                const int pj = (c + e - rope0) >> 1;
-                const float cs = s_cos[pj], sn = s_sin[pj];
-                const float x0 = o[e], x1 = o[e + 1];
-                o[e] = x0 * cs + x1 * sn;
-                o[e + 1] = -x0 * sn + x1 * cs;
-              }
-            }
+        for (int e = 0; e < 4; e += 2) {
+          if (c + e >= rope0) {
+            const int pj = (c + e - rope0) >> 1;
+            const float cs = s_cos[pj], sn = s_sin[pj];
+            const float x0 = o[e], x1 = o[e + 1];
+            o[e] = x0 * cs + x1 * sn;
+            o[e + 1] = -x0 * sn + x1 * cs;
           }
-          *reinterpret_cast<f32x4_t*>(po + c) = f32x4_t{o[0], o[1], o[2], o[3]};
         }
+      }
+      *reinterpret_cast<f32x4_t*>(po + c) = f32x4_t{o[0], o[1], o[2], o[3]};
     }
   }
 }
@@ -604,16 +587,20 @@ bool attn_uses_mfma(int dt, int H, int D, int R) {
 int attn_splits(int dt, int B, int Tq, int H, int D, int keys_per_query) {
   if (!(dt == 1 && H == kAtH && D == kAtD)) return 1;
   const int64_t q = (int64_t)B * Tq;
-  const int tiles = (keys_per_query + kAtRows - 1) / kAtRows;
+  const int tiles = (keys_per_query + kHsRows - 1) / kHsRows;
   // few queries: spread each one's tiles over splits until there are about
   // as many workgroups as compute units (one tile per split at most)
   int s = 1;
   if (q < 256 && tiles >= 2) s = min((int)((256 + q - 1) / q), tiles);
-  // a multi-tile split holds at most kAtMaxSplitRows rows (its CSA index
+  // a multi-tile split holds at most kHsMaxSplitRows rows (its CSA index
   // stage lives in LDS)
-  s = max(s, (keys_per_query + kAtMaxSplitRows - 1) / kAtMaxSplitRows);
+  s = max(s, (keys_per_query + kHsMaxSplitRows - 1) / kHsMaxSplitRows);
   return min(s, kMaxSplits);
 }
+
+// every multi-tile CSA split stages its indices in LDS: at most kMaxSplits
+// splits of kHsMaxSplitRows rows each
+int64_t attn_max_csa_keys() { return (int64_t)kMaxSplits * kHsMaxSplitRows; }
 
 size_t attn_ws_bytes(int dt, int B, int Tq, int H, int D, int keys_per_query) {
   const int s = attn_splits(dt, B, Tq, H, D, keys_per_query);
@@ -639,13 +626,13 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
     // most rows a split can hold: the list length bound over the split count
     const int wc = (a.W > 0 && a.L_win > 0) ? min(a.W, a.L_win) : 0;
     const int64_t lmax = (a.csa ? (int64_t)a.K : (int64_t)a.N_cap) + wc;
-    const bool multi = (lmax + a.splits - 1) / a.splits > kAtRows;
+    const bool multi = (lmax + a.splits - 1) / a.splits > kHsRows;
     if (a.csa) {
-      if (multi) hipLaunchKernelGGL((attn_mfma<true, true>), grid, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((attn_mfma<true, false>), grid, dim3(256), 0, stream, a);
+      if (multi) hipLaunchKernelGGL((attn_hs<true, true>), grid, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((attn_hs<true, false>), grid, dim3(256), 0, stream, a);
     } else {
-      if (multi) hipLaunchKernelGGL((attn_mfma<false, true>), grid, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((attn_mfma<false, false>), grid, dim3(256), 0, stream, a);
+      if (multi) hipLaunchKernelGGL((attn_hs<false, true>), grid, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((attn_hs<false, false>), grid, dim3(256), 0, stream, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;

@@ -85,6 +85,8 @@ struct AttnArgs {
 };
 bool attn_uses_mfma(int dt, int H, int D, int R);
 int attn_splits(int dt, int B, int Tq, int H, int D, int keys_per_query);
+// most selected + window rows per query the MFMA path takes (CSA)
+int64_t attn_max_csa_keys();
 size_t attn_ws_bytes(int dt, int B, int Tq, int H, int D, int keys_per_query);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 

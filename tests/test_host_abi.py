@@ -151,6 +151,9 @@ def test_attn_validation(lib):
     assert _attn(lib, R=63) == CSA_ERR_ARG
     assert _attn(lib, R=1024) == CSA_ERR_ARG
     assert _attn(lib, D=2048) == CSA_ERR_UNSUPPORTED
+    # a multi-tile split stages at most 2048 selected indices in LDS and there
+    # are at most 256 splits: more selected + window rows are refused
+    assert _attn(lib, N=1 << 20, K=256 * 2048 - 128 + 1) == CSA_ERR_UNSUPPORTED
     assert _attn(lib, ws=N) == CSA_ERR_WORKSPACE          # 4 long queries are split
     assert _attn(lib, B=0) == CSA_OK
     assert _attn(lib, "hca_attn", m=0) == CSA_ERR_ARG
