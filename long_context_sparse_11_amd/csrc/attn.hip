@@ -173,8 +173,8 @@ __device__ __forceinline__ float half_swap(float x) {
 // channels, so each head's logits are complete inside one wave: no partial
 // logits cross waves and each head's online softmax runs once.
 //
-// A tile's 32 rows are copied HBM -> LDS once (global_load_lds, 16 bytes per
-// lane, a whole 1 KiB row per wave instruction) and serve the four waves;
+// A tile's 32 rows are copied HBM -> LDS once (buffer loads into LDS, 16
+// bytes per lane, a whole 1 KiB row per wave instruction) and serve the four waves;
 // tiles are double-buffered.  MFMA v_mfma_f32_16x16x32_bf16 throughout
 // (lane l feeds A[l % 16][8(l/16) .. +7] and B[8(l/16) .. +7][l % 16];
 // accumulator element r is C[4(l/16) + r][l % 16]):
@@ -189,12 +189,17 @@ __device__ __forceinline__ float half_swap(float x) {
 // QK reads (16 rows, one chunk) and the transposing PV reads (4 rows, two
 // chunks) then fall on distinct banks.
 constexpr int kHsRows = 32;
+// word 3 of a raw (untyped) buffer descriptor: 32-bit data format
+constexpr int kRawBufferWord3 = 0x00020000;
 constexpr int kHsMaxSplitRows = 2048;  // rows of a multi-tile CSA split (LDS index stage)
 
 // Conflict-free under either bank model of a 16-byte read (8-lane groups
 // on 32 banks, or 16-lane groups on 64): the 16 rows of a QK read differ in
 // bits 0-2 within each half and in bits 0-3 overall, and the 4 rows of a
 // transposing read differ in bits 1-2.
+// hs_swz < 16 changes only the low 4 bits of a chunk index, so a read's
+// address is written as a per-lane base (from the low bits) plus a constant
+// offset (from the high bits) that the compiler folds into the instruction.
 __device__ __forceinline__ int hs_swz(int r) {
   return ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3);
 }
@@ -263,16 +268,20 @@ void attn_hs(AttnArgs a) {
   const bf16_t* win_b = (const bf16_t*)a.win + ((int64_t)b * a.L_win + kr.win_r0) * kAtD;
   const bf16_t* dummy = (const bf16_t*)a.q + (int64_t)qi * kAtH * kAtD;  // 1 KiB always readable
 
-  // Request tile j0's 32 rows into LDS buffer `dst` and return their
-  // validity mask.  Lane l (< 32) resolves row j0 + l (sidx_l: its selected
-  // index) to a source address with selects, not branches (an invalid row
-  // reads a harmless 1 KiB); wave w then copies rows 8w .. 8w+7, one 1 KiB
-  // row per global_load_lds: the row's address is read from its lane into
-  // scalar registers and lane i fetches the 16-byte chunk that belongs at
-  // position i (i ^ hs_swz(row)).
+  // A tile's 32 rows reach LDS in two steps.  resolve_tile: lane l (< 32)
+  // turns row j0 + l (sidx_l: its selected index) into a source address with
+  // selects, not branches (an invalid row reads a harmless 1 KiB), and the
+  // tile's validity mask comes back.  issue_row(u): wave w copies row
+  // 8w + u with one buffer load into LDS (1 KiB); the row's address is read from
+  // its lane into scalar registers and lane i fetches the 16-byte chunk that
+  // belongs at position i (i ^ hs_swz(row)).
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const uint64_t pool_a = (uint64_t)pool_b, win_a = (uint64_t)win_b, dummy_a = (uint64_t)dummy;
-  auto load_tile = [&](int j0, int sidx_l, bf16_t* dst) -> uint32_t {
+  struct TileSrc {
+    int lo, hi;  // this lane's row address
+    uint32_t mask;
+  };
+  auto resolve_tile = [&](int j0, int sidx_l) -> TileSrc {
     const int jj = j0 + (lane & 31);
     const bool in_sel = jj < kr.nsel;
     const int srow = CSA ? sidx_l : jj;
@@ -282,20 +291,28 @@ void attn_hs(AttnArgs a) {
     const uint64_t sa = in_sel ? pool_a + (uint64_t)((int64_t)srow * (kAtD * 2))
                                : win_a + (uint64_t)((int64_t)wrow * (kAtD * 2));
     const uint64_t src = valid ? sa : dummy_a;
-    const int lo = (int)(uint32_t)src, hi = (int)(uint32_t)(src >> 32);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int r = 8 * wv + u;
-      const uint64_t rs = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, r) << 32) |
-                          (uint32_t)__builtin_amdgcn_readlane(lo, r);
-      const bf16_t* gp = reinterpret_cast<const bf16_t*>(rs) + 8 * (lane ^ hs_swz(r));
-      __builtin_amdgcn_global_load_lds((const void*)gp, (lds_void_ptr)(dst + r * kAtD), 16, 0, 0);
-    }
-    return (uint32_t)__ballot(valid);
+    return TileSrc{(int)(uint32_t)src, (int)(uint32_t)(src >> 32), (uint32_t)__ballot(valid)};
+  };
+  auto issue_row = [&](const TileSrc& ts, int u, bf16_t* dst) {
+    const int r = 8 * wv + u;
+    const uint64_t rs = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(ts.hi, r) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane(ts.lo, r);
+    // a buffer load (not a global one): it counts on vmcnt only, so the
+    // LDS reads issued around it keep exact lgkmcnt waits
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)rs, (short)0, kAtD * 2, kRawBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)(dst + r * kAtD), 16,
+                                             16 * (lane ^ hs_swz(r)), 0, 0, 0);
   };
 
   // ---- prologue: tile 0's rows, the rope table, the split's later indices
-  uint32_t vmask = load_tile(start, idx0, s_rows0);
+  uint32_t vmask;
+  {
+    const TileSrc t0 = resolve_tile(start, idx0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) issue_row(t0, u, s_rows0);
+    vmask = t0.mask;
+  }
   for (int p = tid; p < R / 2; p += 256) rope_cos_sin(tpos, p, a.rope_theta1, s_cos[p], s_sin[p]);
   if constexpr (MULTI && CSA) {
     const int sel_end = min(end, a.K);
@@ -333,35 +350,47 @@ void attn_hs(AttnArgs a) {
   // One tile: logits, softmax, PV from `rows`; in multi-tile splits the
   // next tile's rows are first requested into `next` (the other buffer).
   auto tile_step = [&](int j0, const bf16_t* rows, bf16_t* next) {
-    uint32_t vnext = 0;
+    // multi-tile splits request the next tile while this one is used; past
+    // the split's end every row is invalid and the copy reads the harmless
+    // row into the idle buffer, so the request is unconditional
+    TileSrc nt{0, 0, 0u};
     if constexpr (MULTI) {
-      // the next tile's rows are requested before this one is used
-      if (j0 + kHsRows < end) {
-        const int jn = j0 + kHsRows;
-        // row jn + l's selected index (entries past the selected part are
-        // never used; jn - start + l stays below the split's row count)
-        int sidx_l = 0;
-        if constexpr (CSA) sidx_l = s_idx[jn - start + (lane & 31)];
-        vnext = load_tile(jn, sidx_l, next);
-      }
+      const int jn = j0 + kHsRows;
+      int sidx_l = 0;
+      // row jn + l's selected index; entries past the selected part (or the
+      // split) are never used, the clamp only keeps the read inside s_idx
+      if constexpr (CSA) sidx_l = s_idx[min(jn - start + (lane & 31), kHsMaxSplitRows - 1)];
+      nt = resolve_tile(jn, sidx_l);
     }
 
-    // logits S^T[key][head] over all 512 channels, two 16-key blocks; a
-    // block's 16 operand reads are issued before its MFMAs
-    f32x4_t sacc[2];
+    // logits S^T[key][head] over all 512 channels for two 16-key blocks (two
+    // independent accumulator chains, interleaved).  The order is pinned:
+    // with one wave per SIMD nothing else hides the LDS latency, so the 32
+    // operand reads run 8 ahead of their MFMAs, and the next tile's 8 row
+    // copies are spread between them instead of stalling issue up front.
+    f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    {
+      const bf16_t* rpk[2] = {rows + c16 * kAtD, rows + (16 + c16) * kAtD};
+      const int swk[2] = {hs_swz(c16), hs_swz(16 + c16)};
+      // step f reads block f % 2, channel slice f / 2
+      auto qk_read = [&](int f) {
+        const int kb = f & 1, ks = f >> 1;
+        return *reinterpret_cast<const bf16x8_t*>(rpk[kb] + 128 * (ks >> 2) +
+                                                  8 * ((4 * (ks & 3) + G) ^ swk[kb]));
+      };
+      bf16x8_t av[8];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int r = 16 * kb + c16;
-      const bf16_t* rp = rows + r * kAtD;
-      const int sw = hs_swz(r);
-      bf16x8_t av[16];
+      for (int f = 0; f < 8; ++f) av[f] = qk_read(f);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks)
-        av[ks] = *reinterpret_cast<const bf16x8_t*>(rp + 8 * ((4 * ks + G) ^ sw));
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks], qb[ks], acc, 0, 0, 0);
-      sacc[kb] = acc;
+      for (int f = 0; f < 32; ++f) {
+        sacc[f & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[f & 7], qb[f >> 1], sacc[f & 1], 0, 0, 0);
+        if (f + 8 < 32) av[f & 7] = qk_read(f + 8);
+        if constexpr (MULTI) {
+          if ((f & 3) == 3) issue_row(nt, f >> 2, next);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 
     // online softmax of head h over this tile's 32 keys: lane (G, c16) holds
@@ -412,7 +441,6 @@ void attn_hs(AttnArgs a) {
     // O^T[ch][head] += R^T[ch][key] P^T[key][head]: in each 16-lane group,
     // lane i points at key row 4G + i/4 (and 16 + 4G + i/4), channels
     // 16cb + 4(i % 4) .. +3, and receives channel 16cb + i of the 4 rows.
-    // The transposing reads of 8 channel blocks go out before their MFMAs.
     const int kr0 = 4 * G + (c16 >> 2);
     const int kr1 = kr0 + 16;
     const bf16_t* rp0 = rows + kr0 * kAtD;
@@ -428,9 +456,9 @@ void attn_hs(AttnArgs a) {
         const int ch = 2 * cb + (q4 >> 1);          // 16-byte chunk of the channels
         const int sub = 4 * (q4 & 1);               // bf16 offset inside it
         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_ptr)(rp0 + 8 * (ch ^ sw0) + sub));
+            (lds_s16x4_ptr)(rp0 + 128 * (ch >> 4) + 8 * ((ch & 15) ^ sw0) + sub));
         const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_ptr)(rp1 + 8 * (ch ^ sw1) + sub));
+            (lds_s16x4_ptr)(rp1 + 128 * (ch >> 4) + 8 * ((ch & 15) ^ sw1) + sub));
         const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
         av[k] = __builtin_bit_cast(bf16x8_t, u32x4_t{l2.x, l2.y, h2.x, h2.y});
       }
@@ -438,12 +466,20 @@ void attn_hs(AttnArgs a) {
       for (int k = 0; k < 8; ++k)
         oacc[8 * c8 + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k], pb, oacc[8 * c8 + k], 0, 0, 0);
     }
+    // 16 transposing reads (8 channel blocks) ahead, then one MFMA per two
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 1);
+#pragma unroll
+    for (int i = 0; i < 24; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
 
     if constexpr (MULTI) {
       // the next tile's rows have landed and every wave is done with this one
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      vmask = vnext;
+      vmask = nt.mask;
     }
   };
 
