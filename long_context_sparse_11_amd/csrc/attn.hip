@@ -185,24 +185,25 @@ __device__ __forceinline__ float half_swap(float x) {
 //     accumulator layout of S^T is the operand layout of P^T: slot e < 4 is
 //     key 4(l/16) + e, slot e >= 4 is key 16 + 4(l/16) + e - 4), A = rows
 //     read transposed from LDS (ds_read_b64_tr_b16, the same key permutation).
-// Row r of a tile stores its 16-byte chunk c at position c ^ hs_swz(r): the
-// QK reads (16 rows, one chunk) and the transposing PV reads (4 rows, two
-// chunks) then fall on distinct banks.
+// Row r of a tile stores its 16-byte chunk c at position c ^ hs_swz(r), which
+// keeps both read patterns free of bank conflicts.
 constexpr int kHsRows = 32;
 // word 3 of a raw (untyped) buffer descriptor: 32-bit data format
 constexpr int kRawBufferWord3 = 0x00020000;
 constexpr int kHsMaxSplitRows = 2048;  // rows of a multi-tile CSA split (LDS index stage)
 
-// Conflict-free under either bank model of a 16-byte read (8-lane groups
-// on 32 banks, or 16-lane groups on 64): the 16 rows of a QK read differ in
-// bits 0-2 within each half and in bits 0-3 overall, and the 4 rows of a
-// transposing read differ in bits 1-2.
+// LDS banks (64 x 4 bytes), as measured with the bank-conflict counter:
+// a 16-byte read serves 16 lanes per cycle, those with equal lane bit 5 and
+// equal parity of lane bits 2-4; a transposing 8-byte read serves 32
+// consecutive lanes per cycle.  With chunk c of row r at c ^ ((r & 7) << 1):
+// in a QK read the 8 lanes of a cycle with even G (l / 16) get the even
+// slots 2(r & 7) (distinct, as r & 7 is) and those with odd G the odd ones;
+// in a transposing read each row's 32 bytes go to the slot pair r & 7,
+// distinct over the 8 rows of a 32-lane half.  No read conflicts.
 // hs_swz < 16 changes only the low 4 bits of a chunk index, so a read's
 // address is written as a per-lane base (from the low bits) plus a constant
 // offset (from the high bits) that the compiler folds into the instruction.
-__device__ __forceinline__ int hs_swz(int r) {
-  return ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3);
-}
+__device__ __forceinline__ int hs_swz(int r) { return (r & 7) << 1; }
 
 // Value of lane (l ^ 16): v_permlane16_swap exchanges 16-lane rows 0<->1, 2<->3.
 __device__ __forceinline__ float row_swap16(float x) {
