@@ -72,6 +72,7 @@ class Step:
 
     def __init__(self, kind, g, L, torch):
         self.kind, self.g, self.L, self.torch = kind, g, L, torch
+        self._cws = {}
         B, D, m = g["B"], g["D"], g["m"]
         self.B = B
         if kind in ("csa64k", "csa1m"):
@@ -95,6 +96,15 @@ class Step:
                                     device="cuda")
             n = L.csa_attn_ws_bytes(1, Tq, 64, D, K + W)
             self.ws_a = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+
+    def cws(self, c, m, overlap=True):
+        """Preallocated compressor workspace for stream tensor c [B, T, D]."""
+        key = (tuple(c.shape), m, overlap)
+        if key not in self._cws:
+            B, T, D = c.shape
+            n = self.L.csa_compress_ws_bytes(1, B, T, D, m, overlap)
+            self._cws[key] = self.torch.empty(max(n, 1), dtype=self.torch.uint8, device="cuda")
+        return self._cws[key]
 
     def dominant(self):
         """(name, thunk) of the kernel that carries the step's algorithmic
@@ -123,11 +133,11 @@ class Step:
                                    prev_c_b=g["prev_c_b"], prev_z_b=g["prev_z_b"],
                                    bias_a=g["bias_a"], bias_b=g["bias_b"], gain=g["gain"],
                                    rope_dims=g["R"], pos0=g["block_pos0"], out=pool[:, N - 1:],
-                                   out_bstride=N * D),
+                                   out_bstride=N * D, ws=self.cws(g["c_a"], m)),
                     L.csa_compress(g["ic_a"], m, z_a=g["iz_a"], c_b=g["ic_b"], z_b=g["iz_b"],
                                    prev_c_b=g["iprev_c_b"], prev_z_b=g["iprev_z_b"],
                                    bias_a=g["ibias_a"], bias_b=g["ibias_b"], out=kidx[:, N - 1:],
-                                   out_bstride=N * Di))),
+                                   out_bstride=N * Di, ws=self.cws(g["ic_a"], m)))),
                 ("index_topk", lambda: L.csa_index_topk(g["q_idx"], g["w_idx"], kidx,
                                                         g["n_entries"], g["q_pos0"], g["K"], m,
                                                         ws=self.ws_i, idx_out=self.idx)),
@@ -143,7 +153,8 @@ class Step:
                 ("compress", lambda: L.csa_compress(g["c_a"], m, z_a=g["z_a"], bias_a=g["bias_a"],
                                                     gain=g["gain"], rope_dims=g["R"],
                                                     pos0=g["block_pos0"], out=pool[:, N - 1:],
-                                                    out_bstride=N * D)),
+                                                    out_bstride=N * D,
+                                                    ws=self.cws(g["c_a"], m, False))),
                 ("hca_attn", lambda: L.hca_attn(g["q"], pool, g["n_entries"], m, g["win"],
                                                 g["win_pos0"], g["W"], g["sink"], g["q_pos0"],
                                                 rope_dims=g["R"], out=self.out, ws=self.ws_a)),
@@ -157,11 +168,11 @@ class Step:
                                z_b=g["z_b"][:, m:], prev_c_b=g["c_b"][:, :m],
                                prev_z_b=g["z_b"][:, :m], bias_a=g["bias_a"], bias_b=g["bias_b"],
                                gain=g["gain"], rope_dims=g["R"], pos0=g["chunk_pos0"],
-                               out=pool[:, P:]),
+                               out=pool[:, P:], ws=self.cws(g["c_a"][:, m:], m)),
                 L.csa_compress(g["ic_a"][:, m:], m, z_a=g["iz_a"][:, m:], c_b=g["ic_b"][:, m:],
                                z_b=g["iz_b"][:, m:], prev_c_b=g["ic_b"][:, :m],
                                prev_z_b=g["iz_b"][:, :m], bias_a=g["ibias_a"],
-                               bias_b=g["ibias_b"], out=kidx[:, P:]))),
+                               bias_b=g["ibias_b"], out=kidx[:, P:], ws=self.cws(g["ic_a"][:, m:], m)))),
             ("index_topk", lambda: L.csa_index_topk(g["q_idx"], g["w_idx"], kidx, g["n_entries"],
                                                     g["q_pos0"], g["K"], m, ws=self.ws_i,
                                                     idx_out=self.idx)),

@@ -80,6 +80,13 @@ typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
  *   pos0            [B] int64   device; required if rope_dims > 0
  *   out             [B, ceil(T/m), D] with batch stride out_bstride elements
  *                   (0 = contiguous); may point into a larger pool buffer
+ *   ws              optional device workspace of csa_compress_ws_bytes(...)
+ *                   bytes (NULL allowed).  A call with few entries spreads
+ *                   each entry over several workgroups; with a gain that
+ *                   needs the workspace, without one it runs one workgroup
+ *                   per entry.  A non-NULL ws smaller than the query gives
+ *                   CSA_ERR_WORKSPACE.  Calls sharing a workspace must not
+ *                   overlap in time.
  * Supported: 1 <= m <= 1024, D a power of two with 8 <= D <= 1024 (bf16) or
  * 4 <= D <= 1024 (f32), rope_dims even and <= D.
  * ------------------------------------------------------------------------- */
@@ -89,7 +96,11 @@ int csa_compress(int dt, int B, int T, int D, int m, int overlap,
                  const float* bias_a, const float* bias_b,
                  const float* gain, float eps,
                  int rope_dims, double rope_base, const int64_t* pos0,
-                 void* out, int64_t out_bstride, void* stream);
+                 void* out, int64_t out_bstride, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace (bytes) csa_compress can use for this shape (overlap as in the
+ * call); 0 when it needs none.  Returns 0 for invalid sizes. */
+size_t csa_compress_ws_bytes(int dt, int B, int T, int D, int m, int overlap);
 
 /* ---------------------------------------------------------------------------
  * csa_index_topk - lightning indexer scores and top-K selection.

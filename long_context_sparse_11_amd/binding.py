@@ -25,7 +25,10 @@ _SIGS = {
                                 _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                 _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                 _c.c_void_p, _c.c_float, _c.c_int, _c.c_double, _c.c_void_p,
-                                _c.c_void_p, _c.c_int64, _c.c_void_p]),
+                                _c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_size_t,
+                                _c.c_void_p]),
+    "csa_compress_ws_bytes": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                            _c.c_int]),
     "csa_index_topk": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                   _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                   _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
@@ -115,9 +118,11 @@ def _i64(t):
 # ---------------------------------------------------------------------------
 def csa_compress(c_a, m, *, z_a=None, c_b=None, z_b=None, prev_c_b=None, prev_z_b=None,
                  bias_a=None, bias_b=None, gain=None, eps=1e-6, rope_dims=0,
-                 rope_base=10000.0, pos0=None, out=None, out_bstride=0, stream=None):
+                 rope_base=10000.0, pos0=None, out=None, out_bstride=0, ws=None, stream=None):
     """Compressor (see include/csa.h).  c_a [B, T, D]; returns out [B, ceil(T/m), D]
-    (or writes the caller's ``out`` with batch stride ``out_bstride``)."""
+    (or writes the caller's ``out`` with batch stride ``out_bstride``).  ``ws``: a
+    device byte tensor of csa_compress_ws_bytes(...) bytes, allocated here when
+    the call can use one and none is given; an empty tensor means no workspace."""
     B, T, D = c_a.shape
     overlap = c_b is not None
     _dev(c_a, z_a, c_b, z_b, prev_c_b, prev_z_b, bias_a, bias_b, gain, pos0)
@@ -132,12 +137,25 @@ def csa_compress(c_a, m, *, z_a=None, c_b=None, z_b=None, prev_c_b=None, prev_z_
                 or (B > 1 and out.stride(0) != bs)):
             raise ValueError("out must be [B, ceil(T/m), D] with row stride D and batch stride "
                              "out_bstride")
+    need = csa_compress_ws_bytes(_dt(c_a), B, T, D, m, overlap)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=c_a.device)
+    if ws is not None and ws.numel() == 0:
+        ws = None
+    if ws is not None:
+        _dev(ws)
     st = lib().csa_compress(_dt(c_a), B, T, D, m, int(overlap), _p(c_a), _p(z_a), _p(c_b), _p(z_b),
                             _p(prev_c_b), _p(prev_z_b), _p(bias_a), _p(bias_b), _p(gain),
                             float(eps), int(rope_dims), float(rope_base), _p(pos0), _p(out),
-                            int(out_bstride), _stream(stream))
+                            int(out_bstride), _p(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+                            _stream(stream))
     _check(st, "csa_compress")
     return out
+
+
+def csa_compress_ws_bytes(dt, B, T, D, m, overlap=False):
+    """Workspace bytes csa_compress can use (dt: 0 float32, 1 bfloat16)."""
+    return int(lib().csa_compress_ws_bytes(dt, B, T, D, m, int(bool(overlap))))
 
 
 def csa_index_topk_ws_bytes(B, Tq, Hi, N_cap, K):

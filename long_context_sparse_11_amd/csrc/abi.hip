@@ -38,7 +38,7 @@ CSA_EXPORT int csa_compress(int dt, int B, int T, int D, int m, int overlap, con
                             const void* prev_c_b, const void* prev_z_b, const float* bias_a,
                             const float* bias_b, const float* gain, float eps, int rope_dims,
                             double rope_base, const int64_t* pos0, void* out,
-                            int64_t out_bstride, void* stream) {
+                            int64_t out_bstride, void* ws, size_t ws_bytes, void* stream) {
   if (dt != CSA_F32 && dt != CSA_BF16) return CSA_ERR_ARG;
   if (B < 0 || T < 0 || D <= 0 || m <= 0) return CSA_ERR_ARG;
   if (B == 0 || T == 0) return CSA_OK;
@@ -55,10 +55,18 @@ CSA_EXPORT int csa_compress(int dt, int B, int T, int D, int m, int overlap, con
   const int n_out = (T + m - 1) / m;
   if (out_bstride != 0 && out_bstride < (int64_t)n_out * D) return CSA_ERR_ARG;
   if (m > 1024 || !is_pow2(D) || D > 1024 || D < (dt == CSA_BF16 ? 8 : 4)) return CSA_ERR_UNSUPPORTED;
+  if (ws && ws_bytes < compress_ws_bytes(dt, B, n_out, D, m * (overlap ? 2 : 1)))
+    return CSA_ERR_WORKSPACE;
   const double theta1 = rope_dims > 0 ? pow(rope_base, -2.0 / rope_dims) : 0.0;
   CompressArgs a{dt, B, T, D, m, overlap ? 1 : 0, n_out, c_a, z_a, c_b, z_b, prev_c_b, prev_z_b,
-                 bias_a, bias_b, gain, eps, rope_dims, theta1, pos0, out, out_bstride};
+                 bias_a, bias_b, gain, eps, rope_dims, theta1, pos0, out, out_bstride,
+                 1, (float*)ws, ws ? ws_bytes : 0};
   return status_of(launch_compress(a, (hipStream_t)stream));
+}
+
+CSA_EXPORT size_t csa_compress_ws_bytes(int dt, int B, int T, int D, int m, int overlap) {
+  if (B <= 0 || T <= 0 || D <= 0 || m <= 0) return 0;
+  return compress_ws_bytes(dt, B, (T + m - 1) / m, D, m * (overlap ? 2 : 1));
 }
 
 // ------------------------------------------------------------- index + top-k

@@ -4,28 +4,38 @@
 // section 3.3 (eqs. 20-23); RMSNorm/RoPE placement from the same page's
 // section 3.3 (its quote of the paper's section 2.3.3).
 //
-// One workgroup per (sequence, entry).  A row of D channels is covered by
-// L = D / VEC lanes holding VEC contiguous channels each (16-byte loads, so
-// a row is one coalesced read).  The block's rows are spread over G lane
-// groups; each group keeps a per-channel online softmax (max, denominator,
-// weighted sum) in registers, the groups are merged through LDS, and group 0
-// finishes the entry (normalise, gain, rotate, store).
+// One workgroup per (sequence, entry, channel slice).  A slice of Ds
+// channels is covered by L = Ds / VEC lanes holding VEC contiguous channels
+// each (16-byte loads, so a row slice is one coalesced read).  The block's
+// rows are spread over G lane groups; each group keeps a per-channel online
+// softmax (max, denominator, weighted sum) in registers, the groups are
+// merged through LDS, and group 0 finishes the entry (normalise, gain,
+// rotate, store).  A call with few entries splits each entry's channels over
+// several workgroups, so that more compute units stream its rows (one
+// workgroup alone pulls its rows at a small fraction of the chip's rate);
+// the pooling is per channel, and only the RMSNorm needs the whole row: with
+// a gain, the slices leave their pooled values in a workspace and
+// compress_finish normalises, rotates and stores.
 #include "kernels.h"
 
 namespace csa {
 
-template <typename T, int VEC, int GMAX>
-__global__ __launch_bounds__(GMAX * 64) void compress_kernel(CompressArgs a) {
-  __shared__ float smem[3 * (GMAX / 2) * 64 * VEC];
+// At most 512 threads: a thread keeps 4 rows' loads in flight, which needs
+// more registers than a 1024-thread bound leaves.
+template <typename T, int VEC>
+__global__ __launch_bounds__(512) void compress_kernel(CompressArgs a) {
+  extern __shared__ float smem[];  // [3][G/2][Ds] merge staging
   const int i = blockIdx.x;  // entry within the call
   const int b = blockIdx.y;
   const int D = a.D;
-  const int L = D / VEC;
+  const int Ds = D / a.slices;  // channels of this workgroup
+  const int L = Ds / VEC;
   const int G = blockDim.x / L;
   const int tid = threadIdx.x;
   const int g = tid / L;
   const int lane = tid - g * L;
-  const int c0 = lane * VEC;
+  const int cl = lane * VEC;                // channel within the slice
+  const int c0 = blockIdx.z * Ds + cl;      // channel within the row
   const int m = a.m;
 
   const int64_t pos = a.pos0 ? a.pos0[b] + (int64_t)m * i : 0;  // requested early (rope)
@@ -116,17 +126,17 @@ __global__ __launch_bounds__(GMAX * 64) void compress_kernel(CompressArgs a) {
   float gv[VEC];
   if (g == 0 && a.gain) Elem<float>::template load<VEC>(a.gain + c0, gv);  // in flight meanwhile
   float* s_mx = smem;
-  float* s_den = smem + (GMAX / 2) * 64 * VEC;
-  float* s_acc = smem + 2 * (GMAX / 2) * 64 * VEC;
+  float* s_den = smem + (G / 2) * Ds;
+  float* s_acc = smem + 2 * (G / 2) * Ds;
   for (int half = G >> 1; half >= 1; half >>= 1) {
     if (g >= half && g < 2 * half) {
-      const int o = (g - half) * D + c0;
+      const int o = (g - half) * Ds + cl;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) { s_mx[o + e] = mx[e]; s_den[o + e] = den[e]; s_acc[o + e] = acc[e]; }
     }
     __syncthreads();
     if (g < half) {
-      const int o = g * D + c0;
+      const int o = g * Ds + cl;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const float om = s_mx[o + e];
@@ -145,6 +155,10 @@ __global__ __launch_bounds__(GMAX * 64) void compress_kernel(CompressArgs a) {
 #pragma unroll
   for (int e = 0; e < VEC; ++e) y[e] = acc[e] / den[e];
 
+  if (a.slices > 1 && a.gain) {  // the norm needs the whole row: compress_finish
+    Elem<float>::template store<VEC>(a.ws_y + ((int64_t)b * a.n_out + i) * D + c0, y);
+    return;
+  }
   if (a.gain) {
     float ss = 0.f;
 #pragma unroll
@@ -179,35 +193,110 @@ __global__ __launch_bounds__(GMAX * 64) void compress_kernel(CompressArgs a) {
   Elem<T>::template store<VEC>(op, y);
 }
 
-template <typename T, int VEC, int GMAX>
-static hipError_t launch_compress_g(const CompressArgs& a, int G, hipStream_t stream) {
-  const int L = a.D / VEC;
-  dim3 grid(a.n_out, a.B), block(G * L);
-  hipLaunchKernelGGL((compress_kernel<T, VEC, GMAX>), grid, block, 0, stream, a);
-  return hipGetLastError();
+// RMSNorm, gain and RoPE of entries whose channel slices were pooled by
+// separate workgroups.  grid (n_out, B), one wave; lane l holds channels
+// VEC l .. VEC l + VEC - 1 (D = 64 VEC).
+template <typename T, int VEC>
+__global__ __launch_bounds__(64) void compress_finish(CompressArgs a) {
+  const int i = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int D = a.D, c0 = lane * VEC;
+  const int64_t pos = a.pos0 ? a.pos0[b] + (int64_t)a.m * i : 0;
+  float y[VEC], gv[VEC];
+  Elem<float>::template load<VEC>(a.ws_y + ((int64_t)b * a.n_out + i) * D + c0, y);
+  Elem<float>::template load<VEC>(a.gain + c0, gv);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) ss += y[e] * y[e];
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) y[e] = y[e] * inv * gv[e];
+  const int R = a.rope_dims;
+  if (R > 0 && c0 + VEC > D - R) {
+#pragma unroll
+    for (int e = 0; e < VEC; e += 2) {
+      const int c = c0 + e;
+      if (c >= D - R) {
+        float cs, sn;
+        rope_cos_sin(pos, (c - (D - R)) >> 1, a.rope_theta1, cs, sn);
+        const float x0 = y[e], x1 = y[e + 1];
+        y[e] = x0 * cs - x1 * sn;
+        y[e + 1] = x0 * sn + x1 * cs;
+      }
+    }
+  }
+  const int64_t bstride = a.out_bstride ? a.out_bstride : (int64_t)a.n_out * D;
+  Elem<T>::template store<VEC>((T*)a.out + (int64_t)b * bstride + (int64_t)i * D + c0, y);
+}
+
+// Calls with fewer entries than this split each entry's channels, when an
+// entry pools at least kCompressSplitRows rows (shorter blocks are a latency
+// matter that a second kernel would only lengthen).
+constexpr int64_t kCompressSplitBelow = 128;
+constexpr int kCompressSplitRows = 32;
+
+static int compress_vec(int dt, int D) {
+  if (dt == 1) return D <= 512 ? 8 : 16;
+  return D <= 256 ? 4 : (D == 512 ? 8 : 16);
+}
+
+// Channel slices per entry: enough workgroups for about 256 in all, slices
+// of at least 8 lanes; with a gain only where the finisher applies (D a
+// multiple of 512, so that one wave holds the row in whole 16-byte bf16
+// words) and a workspace is given.
+static int compress_slices(const CompressArgs& a) {
+  const int64_t entries = (int64_t)a.B * a.n_out;
+  if (entries >= kCompressSplitBelow || a.m * (a.overlap ? 2 : 1) < kCompressSplitRows) return 1;
+  if (a.gain && (a.D % 512 != 0 || !a.ws_y ||
+                 a.ws_bytes < (size_t)entries * a.D * sizeof(float)))
+    return 1;
+  const int vec = compress_vec(a.dt, a.D);
+  int s = 1;
+  while (2 * s * entries <= 256 && a.D / (2 * s) >= 8 * vec) s *= 2;
+  return s;
+}
+
+size_t compress_ws_bytes(int dt, int B, int n_out, int D, int rows) {
+  (void)dt;
+  const int64_t entries = (int64_t)B * n_out;
+  if (entries <= 0 || entries >= kCompressSplitBelow || rows < kCompressSplitRows ||
+      D % 512 != 0)
+    return 0;
+  return (size_t)entries * D * sizeof(float);
 }
 
 // Row groups: about 4 rows per group (one batch of loads each; a merge step
-// costs more than streaming 4 more rows), at most 16 groups / 1024 threads,
-// at least one full wave; more than 8 groups take the 16-group variant.
+// costs more than streaming 4 more rows), at most 512 threads, at least one
+// full wave.
 template <typename T, int VEC>
 static hipError_t launch_compress_t(const CompressArgs& a, hipStream_t stream) {
-  const int L = a.D / VEC;
+  const int L = a.D / a.slices / VEC;
   const int rows = a.m * (a.overlap ? 2 : 1);
-  int G = 1;
-  while (4 * G < rows && G * L < 1024 && G < 16) G <<= 1;
-  while (G * L < 64 && G < 16) G <<= 1;
-  if (G <= 8 || VEC > 8) return launch_compress_g<T, VEC, 8>(a, min(G, 8), stream);
-  return launch_compress_g<T, VEC, (VEC > 8 ? 8 : 16)>(a, G, stream);
+  const size_t ds_bytes = (size_t)(a.D / a.slices) * sizeof(float);
+  int G = 1;  // doubling G grows the merge staging to 3 G Ds floats
+  while (4 * G < rows && 2 * G * L <= 512 && 3 * G * ds_bytes <= 65536) G <<= 1;
+  while (G * L < 64 && 2 * G * L <= 512 && 3 * G * ds_bytes <= 65536) G <<= 1;
+  const size_t smem = 3 * (size_t)(G / 2) * ds_bytes;
+  dim3 grid(a.n_out, a.B, a.slices), block(G * L);
+  hipLaunchKernelGGL((compress_kernel<T, VEC>), grid, block, smem, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.slices == 1 || !a.gain) return e;
+  const int vf = a.D / 64;
+  dim3 fgrid(a.n_out, a.B);
+  if (vf == 8) hipLaunchKernelGGL((compress_finish<T, 8>), fgrid, dim3(64), 0, stream, a);
+  else hipLaunchKernelGGL((compress_finish<T, 16>), fgrid, dim3(64), 0, stream, a);
+  return hipGetLastError();
 }
 
-hipError_t launch_compress(const CompressArgs& a, hipStream_t stream) {
+hipError_t launch_compress(CompressArgs a, hipStream_t stream) {
+  a.slices = compress_slices(a);
+  const int vec = compress_vec(a.dt, a.D);
   if (a.dt == 1) {
-    if (a.D <= 512) return launch_compress_t<bf16_t, 8>(a, stream);
+    if (vec == 8) return launch_compress_t<bf16_t, 8>(a, stream);
     return launch_compress_t<bf16_t, 16>(a, stream);
   }
-  if (a.D <= 256) return launch_compress_t<float, 4>(a, stream);
-  if (a.D == 512) return launch_compress_t<float, 8>(a, stream);
+  if (vec == 4) return launch_compress_t<float, 4>(a, stream);
+  if (vec == 8) return launch_compress_t<float, 8>(a, stream);
   return launch_compress_t<float, 16>(a, stream);
 }
 

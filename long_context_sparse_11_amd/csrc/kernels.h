@@ -21,8 +21,14 @@ struct CompressArgs {
   const int64_t* pos0;
   void* out;
   int64_t out_bstride;
+  int slices;           // channel slices per entry (set by the launcher)
+  float* ws_y;          // [B, n_out, D] f32 pooled values when slices > 1 with a gain
+  size_t ws_bytes;
 };
-hipError_t launch_compress(const CompressArgs& a, hipStream_t stream);
+// Workspace the compressor uses for a call of this shape (0 = none); rows:
+// rows pooled per entry (m, or 2m with overlap).
+size_t compress_ws_bytes(int dt, int B, int n_out, int D, int rows);
+hipError_t launch_compress(CompressArgs a, hipStream_t stream);
 
 // ------------------------------------------------------------------- indexer
 struct IndexArgs {

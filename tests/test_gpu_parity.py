@@ -100,6 +100,35 @@ def test_compress_bf16(D, m, T, overlap, prev, normrope, pos):
     assert rowwise_rel_err(host(out), ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("D,m,T,overlap", [(512, 128, 256, False), (512, 16, 32, True)])
+def test_compress_without_workspace(D, m, T, overlap):
+    """A call with few entries and a gain splits each entry over several
+    workgroups through the workspace; without one it runs one workgroup per
+    entry.  Both match the oracle."""
+    rng = np.random.default_rng(D + m + T)
+    B = 5
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)
+    ca, za, cb, zb = (synth.Tensor(f(B, T, D), "bf16") for _ in range(4))
+    ba, bb = 0.02 * f(m, D), 0.02 * f(m, D)
+    gain = 1 + 0.02 * f(D)
+    pos = [int(x) for x in rng.integers(0, 1 << 20, B)]
+    kw = dict(z_a=dev(za), bias_a=dev(ba), gain=dev(gain), rope_dims=64, pos0=i64(pos))
+    okw = dict(gain=gain, rope_dims=64, pos0=pos)
+    if overlap:
+        kw.update(c_b=dev(cb), z_b=dev(zb), bias_b=dev(bb))
+        okw.update(c_b=cb.f32, z_b=zb.f32, bias_b=bb)
+    need = L.csa_compress_ws_bytes(1, B, T, D, m, overlap)
+    assert need == B * (T // m) * D * 4
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    split = L.csa_compress(dev(ca), m, ws=ws, **kw)
+    whole = L.csa_compress(dev(ca), m, ws=torch.empty(0, dtype=torch.uint8, device="cuda"), **kw)
+    ref = O.csa_compress(ca.f32, za.f32, ba, m, **okw)
+    assert rowwise_rel_err(host(split), ref) <= TOL_BF16
+    assert rowwise_rel_err(host(whole), ref) <= TOL_BF16
+    with pytest.raises(L.CsaError):
+        L.csa_compress(dev(ca), m, ws=ws[:16], **kw)
+
+
 def test_compress_closing_block_into_pool():
     """Decode: the closing block's entry is written in place into row N-1 of
     a [B, N, D] pool through the batch stride; nothing else changes."""

@@ -31,7 +31,8 @@ def lib():
 def test_header_declares_the_four_calls():
     names = declared_functions()
     for n in ("csa_compress", "csa_index_topk", "csa_index_scores", "csa_sparse_attn", "hca_attn",
-              "csa_index_topk_ws_bytes", "csa_attn_ws_bytes", "csa_status_string"):
+              "csa_compress_ws_bytes", "csa_index_topk_ws_bytes", "csa_attn_ws_bytes",
+              "csa_status_string"):
         assert n in names
 
 
@@ -75,12 +76,12 @@ N = None
 def _compress(lib, **kw):
     a = dict(dt=1, B=2, T=8, D=512, m=4, overlap=1, c_a=P, z_a=P, c_b=P, z_b=P, prev_c_b=N,
              prev_z_b=N, bias_a=N, bias_b=N, gain=N, eps=1e-6, rope=0, base=10000.0, pos0=N,
-             out=P, ostride=0)
+             out=P, ostride=0, ws=N, wsb=0)
     a.update(kw)
     return lib.csa_compress(a["dt"], a["B"], a["T"], a["D"], a["m"], a["overlap"], a["c_a"],
                             a["z_a"], a["c_b"], a["z_b"], a["prev_c_b"], a["prev_z_b"],
                             a["bias_a"], a["bias_b"], a["gain"], a["eps"], a["rope"], a["base"],
-                            a["pos0"], a["out"], a["ostride"], N)
+                            a["pos0"], a["out"], a["ostride"], a["ws"], a["wsb"], N)
 
 
 def test_compress_validation(lib):
@@ -96,6 +97,21 @@ def test_compress_validation(lib):
     assert _compress(lib, ostride=100) == CSA_ERR_ARG    # stride shorter than one batch
     assert _compress(lib, D=384) == CSA_ERR_UNSUPPORTED  # not a power of two
     assert _compress(lib, m=2048) == CSA_ERR_UNSUPPORTED
+    # a given workspace must hold what the shape can use (2 entries x 2 x 512 f32)
+    assert _compress(lib, T=32, m=16, ws=P, wsb=100) == CSA_ERR_WORKSPACE
+
+
+def test_compress_workspace_sizes(lib):
+    # few entries with long blocks: each entry's pooled row in f32, so the
+    # channels can be split over workgroups
+    assert lib.csa_compress_ws_bytes(1, 16, 128, 512, 128, 0) == 16 * 512 * 4
+    assert lib.csa_compress_ws_bytes(1, 4, 16, 512, 16, 1) == 4 * 512 * 4
+    # short blocks, enough entries for one workgroup each, or rows the
+    # finisher does not take
+    assert lib.csa_compress_ws_bytes(1, 4, 4, 512, 4, 1) == 0
+    assert lib.csa_compress_ws_bytes(1, 1, 4096, 512, 4, 1) == 0
+    assert lib.csa_compress_ws_bytes(1, 4, 128, 256, 128, 0) == 0
+    assert lib.csa_compress_ws_bytes(1, 0, 4, 512, 4, 1) == 0
 
 
 def _index(lib, **kw):
