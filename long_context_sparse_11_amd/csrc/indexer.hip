@@ -82,7 +82,11 @@ __device__ __forceinline__ float tile_score(const bf16x8_t (&qa)[2][8], const bf
   for (int r = 0; r < 16; ++r) sc += wv[0][r] * fmaxf(c0[r], 0.f);
 #pragma unroll
   for (int r = 0; r < 16; ++r) sc += wv[1][r] * fmaxf(c1[r], 0.f);
-  return sc + __shfl_xor(sc, 32);
+  // the other half of the heads sits in lane l ^ 32: v_permlane32_swap (a
+  // VALU move, no LDS round trip)
+  const uint32_t u = __float_as_uint(sc);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return sc + __uint_as_float(__lane_id() < 32 ? sw[1] : sw[0]);
 }
 
 // ------------------------------------------------------------------- decode
@@ -157,6 +161,9 @@ __global__ __launch_bounds__(256) void index_decode(IndexArgs a, int tiles_per_w
 // against 64-key tiles in LDS (row pitch 272 bytes: the 16-byte column
 // reads of 16 consecutive rows fall in distinct banks).
 constexpr int kPfKeys = 64;
+// s_waitcnt immediate for vmcnt(0) with lgkmcnt and expcnt left at their
+// maxima (vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kPfPitch = 136;  // bf16 elements per LDS row
 
 __global__ __launch_bounds__(512) void index_prefill(IndexArgs a) {
@@ -200,6 +207,10 @@ __global__ __launch_bounds__(512) void index_prefill(IndexArgs a) {
   uint4 v0, v1;
   fetch(0, v0, v1);
   stash(0, v0, v1);
+  // the query operand has landed before the loop: otherwise the compiler's
+  // conservative count makes the loop's MFMAs wait on the next tile's fetch
+  // (the builtin, not inline asm: the compiler's wait counting sees it)
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   int buf = 0;
   for (int k0 = 0; k0 < n_max; k0 += kPfKeys) {
