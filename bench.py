@@ -128,16 +128,16 @@ class Step:
             N, D, Di, m = g["N"], g["D"], g["Di"], g["m"]
             pool, kidx = g["pool"], g["k_idx"]
             return [
-                ("compress", lambda: (
-                    L.csa_compress(g["c_a"], m, z_a=g["z_a"], c_b=g["c_b"], z_b=g["z_b"],
-                                   prev_c_b=g["prev_c_b"], prev_z_b=g["prev_z_b"],
-                                   bias_a=g["bias_a"], bias_b=g["bias_b"], gain=g["gain"],
-                                   rope_dims=g["R"], pos0=g["block_pos0"], out=pool[:, N - 1:],
-                                   out_bstride=N * D, ws=self.cws(g["c_a"], m)),
-                    L.csa_compress(g["ic_a"], m, z_a=g["iz_a"], c_b=g["ic_b"], z_b=g["iz_b"],
-                                   prev_c_b=g["iprev_c_b"], prev_z_b=g["iprev_z_b"],
-                                   bias_a=g["ibias_a"], bias_b=g["ibias_b"], out=kidx[:, N - 1:],
-                                   out_bstride=N * Di, ws=self.cws(g["ic_a"], m)))),
+                # the KV entry and the indexer key of the closing block, one launch
+                ("compress", lambda: L.csa_compress_batch([
+                    dict(c_a=g["c_a"], z_a=g["z_a"], c_b=g["c_b"], z_b=g["z_b"],
+                         prev_c_b=g["prev_c_b"], prev_z_b=g["prev_z_b"], bias_a=g["bias_a"],
+                         bias_b=g["bias_b"], gain=g["gain"], rope_dims=g["R"],
+                         out=pool[:, N - 1:], out_bstride=N * D),
+                    dict(c_a=g["ic_a"], z_a=g["iz_a"], c_b=g["ic_b"], z_b=g["iz_b"],
+                         prev_c_b=g["iprev_c_b"], prev_z_b=g["iprev_z_b"], bias_a=g["ibias_a"],
+                         bias_b=g["ibias_b"], out=kidx[:, N - 1:], out_bstride=N * Di)],
+                    m, pos0=g["block_pos0"])),
                 ("index_topk", lambda: L.csa_index_topk(g["q_idx"], g["w_idx"], kidx,
                                                         g["n_entries"], g["q_pos0"], g["K"], m,
                                                         ws=self.ws_i, idx_out=self.idx)),
@@ -163,16 +163,17 @@ class Step:
         N, D, Di, m, P = g["N"], g["D"], g["Di"], g["m"], g["prefix"]
         pool, kidx = g["pool"], g["k_idx"]
         return [
-            ("compress", lambda: (
-                L.csa_compress(g["c_a"][:, m:], m, z_a=g["z_a"][:, m:], c_b=g["c_b"][:, m:],
-                               z_b=g["z_b"][:, m:], prev_c_b=g["c_b"][:, :m],
-                               prev_z_b=g["z_b"][:, :m], bias_a=g["bias_a"], bias_b=g["bias_b"],
-                               gain=g["gain"], rope_dims=g["R"], pos0=g["chunk_pos0"],
-                               out=pool[:, P:], ws=self.cws(g["c_a"][:, m:], m)),
-                L.csa_compress(g["ic_a"][:, m:], m, z_a=g["iz_a"][:, m:], c_b=g["ic_b"][:, m:],
-                               z_b=g["iz_b"][:, m:], prev_c_b=g["ic_b"][:, :m],
-                               prev_z_b=g["iz_b"][:, :m], bias_a=g["ibias_a"],
-                               bias_b=g["ibias_b"], out=kidx[:, P:], ws=self.cws(g["ic_a"][:, m:], m)))),
+            # the chunk's KV entries and indexer keys, one launch
+            ("compress", lambda: L.csa_compress_batch([
+                dict(c_a=g["c_a"][:, m:], z_a=g["z_a"][:, m:], c_b=g["c_b"][:, m:],
+                     z_b=g["z_b"][:, m:], prev_c_b=g["c_b"][:, :m], prev_z_b=g["z_b"][:, :m],
+                     bias_a=g["bias_a"], bias_b=g["bias_b"], gain=g["gain"], rope_dims=g["R"],
+                     out=pool[:, P:], out_bstride=N * D),
+                dict(c_a=g["ic_a"][:, m:], z_a=g["iz_a"][:, m:], c_b=g["ic_b"][:, m:],
+                     z_b=g["iz_b"][:, m:], prev_c_b=g["ic_b"][:, :m], prev_z_b=g["iz_b"][:, :m],
+                     bias_a=g["ibias_a"], bias_b=g["ibias_b"], out=kidx[:, P:],
+                     out_bstride=N * Di)],
+                m, pos0=g["chunk_pos0"])),
             ("index_topk", lambda: L.csa_index_topk(g["q_idx"], g["w_idx"], kidx, g["n_entries"],
                                                     g["q_pos0"], g["K"], m, ws=self.ws_i,
                                                     idx_out=self.idx)),

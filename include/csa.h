@@ -103,6 +103,44 @@ int csa_compress(int dt, int B, int T, int D, int m, int overlap,
 size_t csa_compress_ws_bytes(int dt, int B, int T, int D, int m, int overlap);
 
 /* ---------------------------------------------------------------------------
+ * csa_compress_batch - up to two compressors over the same token block in
+ * one launch.
+ *
+ * The same operation as csa_compress, once per job, for jobs that share the
+ * block shape and positions: [P2] section 3.2.2 runs the KV compressor and
+ * the indexer-key compressor over the same tokens, so a decode step
+ * compresses its closing block twice.  Each job is what csa_compress takes
+ * after its shared arguments (streams of [B, T, job.D], optional biases,
+ * gain, rope, out with batch stride).  One workgroup per entry and job (no
+ * channel split, no workspace).
+ *
+ *   dt, B, T, m, overlap, pos0   shared by the jobs, as in csa_compress
+ *   jobs[n_jobs], 1 <= n_jobs <= 2
+ * Each job is checked as csa_compress checks its arguments; the first
+ * failing job's status is returned and nothing is launched.
+ * ------------------------------------------------------------------------- */
+typedef struct csa_compress_job {
+  int D;
+  const void* c_a;
+  const void* z_a;
+  const void* c_b;
+  const void* z_b;
+  const void* prev_c_b;
+  const void* prev_z_b;
+  const float* bias_a;
+  const float* bias_b;
+  const float* gain;
+  float eps;
+  int rope_dims;
+  double rope_base;
+  void* out;
+  int64_t out_bstride;
+} csa_compress_job;
+
+int csa_compress_batch(int dt, int B, int T, int m, int overlap, const int64_t* pos0,
+                       const csa_compress_job* jobs, int n_jobs, void* stream);
+
+/* ---------------------------------------------------------------------------
  * csa_index_topk - lightning indexer scores and top-K selection.
  *
  * [P2] section 3.2.2 (eqs. 13-17) and [P3] "The indexer: a learned retrieval

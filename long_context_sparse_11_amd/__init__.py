@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     CsaError,
     csa_attn_ws_bytes,
     csa_compress,
+    csa_compress_batch,
     csa_compress_ws_bytes,
     csa_index_scores,
     csa_index_topk,

@@ -29,6 +29,8 @@ _SIGS = {
                                 _c.c_void_p]),
     "csa_compress_ws_bytes": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                             _c.c_int]),
+    "csa_compress_batch": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                      _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p]),
     "csa_index_topk": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                   _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                   _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
@@ -151,6 +153,54 @@ def csa_compress(c_a, m, *, z_a=None, c_b=None, z_b=None, prev_c_b=None, prev_z_
                             _stream(stream))
     _check(st, "csa_compress")
     return out
+
+
+class CompressJob(ctypes.Structure):
+    """Mirror of csa_compress_job (include/csa.h)."""
+    _fields_ = [("D", _c.c_int), ("c_a", _c.c_void_p), ("z_a", _c.c_void_p),
+                ("c_b", _c.c_void_p), ("z_b", _c.c_void_p), ("prev_c_b", _c.c_void_p),
+                ("prev_z_b", _c.c_void_p), ("bias_a", _c.c_void_p), ("bias_b", _c.c_void_p),
+                ("gain", _c.c_void_p), ("eps", _c.c_float), ("rope_dims", _c.c_int),
+                ("rope_base", _c.c_double), ("out", _c.c_void_p), ("out_bstride", _c.c_int64)]
+
+
+def csa_compress_batch(jobs, m, *, pos0=None, stream=None):
+    """Up to two compressors over the same token block in one launch (see
+    include/csa.h).  ``jobs``: dicts with the keyword arguments of
+    csa_compress plus ``c_a`` and ``out`` (both required here); every job's
+    streams share B, T and, with ``c_b`` given, the overlap."""
+    if not 1 <= len(jobs) <= 2:
+        raise ValueError("one or two jobs")
+    B, T, _ = jobs[0]["c_a"].shape
+    overlap = jobs[0].get("c_b") is not None
+    _i64(pos0)
+    _dev(pos0)
+    arr = (CompressJob * len(jobs))()
+    for k, j in enumerate(jobs):
+        c_a, out = j["c_a"], j["out"]
+        Bj, Tj, D = c_a.shape
+        if (Bj, Tj) != (B, T) or (j.get("c_b") is not None) != overlap or c_a.dtype != jobs[0]["c_a"].dtype:
+            raise ValueError("jobs must share B, T, dtype and overlap")
+        ts = [j.get(n) for n in ("z_a", "c_b", "z_b", "prev_c_b", "prev_z_b", "bias_a", "bias_b", "gain")]
+        _dev(c_a, *ts)
+        _f32(j.get("bias_a")), _f32(j.get("bias_b")), _f32(j.get("gain"))
+        n_out = -(-T // m)
+        bs = j.get("out_bstride", 0) or n_out * D
+        if (tuple(out.shape) != (B, n_out, D) or out.dtype != c_a.dtype or not out.is_cuda
+                or out.stride(2) != 1 or (n_out > 1 and out.stride(1) != D)
+                or (B > 1 and out.stride(0) != bs)):
+            raise ValueError("out must be [B, ceil(T/m), D] with row stride D and batch stride "
+                             "out_bstride")
+        p = lambda t: t.data_ptr() if t is not None else None
+        arr[k] = CompressJob(D, p(c_a), p(j.get("z_a")), p(j.get("c_b")), p(j.get("z_b")),
+                             p(j.get("prev_c_b")), p(j.get("prev_z_b")), p(j.get("bias_a")),
+                             p(j.get("bias_b")), p(j.get("gain")), float(j.get("eps", 1e-6)),
+                             int(j.get("rope_dims", 0)), float(j.get("rope_base", 10000.0)),
+                             out.data_ptr(), int(j.get("out_bstride", 0)))
+    st = lib().csa_compress_batch(_dt(jobs[0]["c_a"]), B, T, m, int(overlap), _p(pos0),
+                                  ctypes.cast(arr, ctypes.c_void_p), len(jobs), _stream(stream))
+    _check(st, "csa_compress_batch")
+    return [j["out"] for j in jobs]
 
 
 def csa_compress_ws_bytes(dt, B, T, D, m, overlap=False):

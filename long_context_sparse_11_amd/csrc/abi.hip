@@ -33,15 +33,18 @@ CSA_EXPORT const char* csa_status_string(int status) {
 }
 
 // ---------------------------------------------------------------- compressor
-CSA_EXPORT int csa_compress(int dt, int B, int T, int D, int m, int overlap, const void* c_a,
-                            const void* z_a, const void* c_b, const void* z_b,
-                            const void* prev_c_b, const void* prev_z_b, const float* bias_a,
-                            const float* bias_b, const float* gain, float eps, int rope_dims,
-                            double rope_base, const int64_t* pos0, void* out,
-                            int64_t out_bstride, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+// Checks one compressor's arguments and fills its launch arguments.
+// Returns CSA_OK, an error, or 1 for "nothing to do" (B or T zero).
+int compress_args(int dt, int B, int T, int D, int m, int overlap, const void* c_a,
+                  const void* z_a, const void* c_b, const void* z_b, const void* prev_c_b,
+                  const void* prev_z_b, const float* bias_a, const float* bias_b,
+                  const float* gain, float eps, int rope_dims, double rope_base,
+                  const int64_t* pos0, void* out, int64_t out_bstride, CompressArgs& a) {
   if (dt != CSA_F32 && dt != CSA_BF16) return CSA_ERR_ARG;
   if (B < 0 || T < 0 || D <= 0 || m <= 0) return CSA_ERR_ARG;
-  if (B == 0 || T == 0) return CSA_OK;
+  if (B == 0 || T == 0) return 1;
   if (!c_a || !out) return CSA_ERR_ARG;
   if (overlap) {
     if (!c_b || !z_b) return CSA_ERR_ARG;
@@ -55,13 +58,49 @@ CSA_EXPORT int csa_compress(int dt, int B, int T, int D, int m, int overlap, con
   const int n_out = (T + m - 1) / m;
   if (out_bstride != 0 && out_bstride < (int64_t)n_out * D) return CSA_ERR_ARG;
   if (m > 1024 || !is_pow2(D) || D > 1024 || D < (dt == CSA_BF16 ? 8 : 4)) return CSA_ERR_UNSUPPORTED;
-  if (ws && ws_bytes < compress_ws_bytes(dt, B, n_out, D, m * (overlap ? 2 : 1)))
-    return CSA_ERR_WORKSPACE;
   const double theta1 = rope_dims > 0 ? pow(rope_base, -2.0 / rope_dims) : 0.0;
-  CompressArgs a{dt, B, T, D, m, overlap ? 1 : 0, n_out, c_a, z_a, c_b, z_b, prev_c_b, prev_z_b,
-                 bias_a, bias_b, gain, eps, rope_dims, theta1, pos0, out, out_bstride,
-                 1, (float*)ws, ws ? ws_bytes : 0};
+  a = CompressArgs{dt, B, T, D, m, overlap ? 1 : 0, n_out, c_a, z_a, c_b, z_b, prev_c_b, prev_z_b,
+                   bias_a, bias_b, gain, eps, rope_dims, theta1, pos0, out, out_bstride,
+                   1, nullptr, 0};
+  return CSA_OK;
+}
+
+}  // namespace
+
+CSA_EXPORT int csa_compress(int dt, int B, int T, int D, int m, int overlap, const void* c_a,
+                            const void* z_a, const void* c_b, const void* z_b,
+                            const void* prev_c_b, const void* prev_z_b, const float* bias_a,
+                            const float* bias_b, const float* gain, float eps, int rope_dims,
+                            double rope_base, const int64_t* pos0, void* out,
+                            int64_t out_bstride, void* ws, size_t ws_bytes, void* stream) {
+  CompressArgs a;
+  const int st = compress_args(dt, B, T, D, m, overlap, c_a, z_a, c_b, z_b, prev_c_b, prev_z_b,
+                               bias_a, bias_b, gain, eps, rope_dims, rope_base, pos0, out,
+                               out_bstride, a);
+  if (st == 1) return CSA_OK;
+  if (st != CSA_OK) return st;
+  if (ws && ws_bytes < compress_ws_bytes(dt, B, a.n_out, D, m * (overlap ? 2 : 1)))
+    return CSA_ERR_WORKSPACE;
+  a.ws_y = (float*)ws;
+  a.ws_bytes = ws ? ws_bytes : 0;
   return status_of(launch_compress(a, (hipStream_t)stream));
+}
+
+CSA_EXPORT int csa_compress_batch(int dt, int B, int T, int m, int overlap, const int64_t* pos0,
+                                  const csa_compress_job* jobs, int n_jobs, void* stream) {
+  if (n_jobs < 1 || n_jobs > 2 || !jobs) return CSA_ERR_ARG;
+  CompressArgs a[2];
+  int nothing = 0;
+  for (int k = 0; k < n_jobs; ++k) {
+    const csa_compress_job& j = jobs[k];
+    const int st = compress_args(dt, B, T, j.D, m, overlap, j.c_a, j.z_a, j.c_b, j.z_b,
+                                 j.prev_c_b, j.prev_z_b, j.bias_a, j.bias_b, j.gain, j.eps,
+                                 j.rope_dims, j.rope_base, pos0, j.out, j.out_bstride, a[k]);
+    if (st == 1) nothing = 1;
+    else if (st != CSA_OK) return st;
+  }
+  if (nothing) return CSA_OK;
+  return status_of(launch_compress_batch(a, n_jobs, (hipStream_t)stream));
 }
 
 CSA_EXPORT size_t csa_compress_ws_bytes(int dt, int B, int T, int D, int m, int overlap) {

@@ -23,8 +23,13 @@ namespace csa {
 // At most 512 threads: a thread keeps 4 rows' loads in flight, which needs
 // more registers than a 1024-thread bound leaves.
 template <typename T, int VEC>
-__global__ __launch_bounds__(512) void compress_kernel(CompressArgs a) {
+__global__ __launch_bounds__(512) void compress_kernel(CompressArgs a0, CompressArgs a1) {
   extern __shared__ float smem[];  // [3][G/2][Ds] merge staging
+  // a launch carries one or two jobs (compressors over the same token
+  // block, say the KV entry and the indexer key): z = job * slices + slice
+  const int job = (int)blockIdx.z / a0.slices;
+  const int slice = (int)blockIdx.z - job * a0.slices;
+  const CompressArgs a = job ? a1 : a0;
   const int i = blockIdx.x;  // entry within the call
   const int b = blockIdx.y;
   const int D = a.D;
@@ -35,7 +40,7 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a) {
   const int g = tid / L;
   const int lane = tid - g * L;
   const int cl = lane * VEC;                // channel within the slice
-  const int c0 = blockIdx.z * Ds + cl;      // channel within the row
+  const int c0 = slice * Ds + cl;           // channel within the row
   const int m = a.m;
 
   const int64_t pos = a.pos0 ? a.pos0[b] + (int64_t)m * i : 0;  // requested early (rope)
@@ -267,20 +272,40 @@ size_t compress_ws_bytes(int dt, int B, int n_out, int D, int rows) {
 
 // Row groups: about 4 rows per group (one batch of loads each; a merge step
 // costs more than streaming 4 more rows), at most 512 threads, at least one
-// full wave.
-template <typename T, int VEC>
-static hipError_t launch_compress_t(const CompressArgs& a, hipStream_t stream) {
-  const int L = a.D / a.slices / VEC;
+// full wave.  Threads of a job whose channel slices take L lanes.
+static int compress_threads(const CompressArgs& a, int L) {
   const int rows = a.m * (a.overlap ? 2 : 1);
   const size_t ds_bytes = (size_t)(a.D / a.slices) * sizeof(float);
   int G = 1;  // doubling G grows the merge staging to 3 G Ds floats
   while (4 * G < rows && 2 * G * L <= 512 && 3 * G * ds_bytes <= 65536) G <<= 1;
   while (G * L < 64 && 2 * G * L <= 512 && 3 * G * ds_bytes <= 65536) G <<= 1;
-  const size_t smem = 3 * (size_t)(G / 2) * ds_bytes;
-  dim3 grid(a.n_out, a.B, a.slices), block(G * L);
-  hipLaunchKernelGGL((compress_kernel<T, VEC>), grid, block, smem, stream, a);
+  return G * L;
+}
+
+// One launch for n (1 or 2) jobs of one VEC; the block is the largest any
+// job asks for, and each job spreads its rows over blockDim / L groups.
+template <typename T, int VEC>
+static hipError_t launch_compress_t(const CompressArgs* jobs, int n, hipStream_t stream) {
+  int threads = 0;
+  for (int k = 0; k < n; ++k)
+    threads = max(threads, compress_threads(jobs[k], jobs[k].D / jobs[k].slices / VEC));
+  size_t smem = 0;
+  for (int k = 0; k < n; ++k) {
+    const int Ds = jobs[k].D / jobs[k].slices;
+    smem = max(smem, 3 * (size_t)(threads / (Ds / VEC) / 2) * Ds * sizeof(float));
+  }
+  if (n > 1 && smem > 65536) {  // too different to share a block shape: one launch each
+    for (int k = 0; k < n; ++k) {
+      const hipError_t e = launch_compress_t<T, VEC>(jobs + k, 1, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  const CompressArgs& a = jobs[0];
+  dim3 grid(a.n_out, a.B, a.slices * n), block(threads);
+  hipLaunchKernelGGL((compress_kernel<T, VEC>), grid, block, smem, stream, a, n > 1 ? jobs[1] : a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.slices == 1 || !a.gain) return e;
+  if (e != hipSuccess || n > 1 || a.slices == 1 || !a.gain) return e;
   const int vf = a.D / 64;
   dim3 fgrid(a.n_out, a.B);
   if (vf == 8) hipLaunchKernelGGL((compress_finish<T, 8>), fgrid, dim3(64), 0, stream, a);
@@ -288,16 +313,32 @@ static hipError_t launch_compress_t(const CompressArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_compress(CompressArgs a, hipStream_t stream) {
-  a.slices = compress_slices(a);
+static hipError_t launch_jobs(const CompressArgs* jobs, int n, hipStream_t stream) {
+  const CompressArgs& a = jobs[0];
   const int vec = compress_vec(a.dt, a.D);
   if (a.dt == 1) {
-    if (vec == 8) return launch_compress_t<bf16_t, 8>(a, stream);
-    return launch_compress_t<bf16_t, 16>(a, stream);
+    if (vec == 8) return launch_compress_t<bf16_t, 8>(jobs, n, stream);
+    return launch_compress_t<bf16_t, 16>(jobs, n, stream);
   }
-  if (vec == 4) return launch_compress_t<float, 4>(a, stream);
-  if (vec == 8) return launch_compress_t<float, 8>(a, stream);
-  return launch_compress_t<float, 16>(a, stream);
+  if (vec == 4) return launch_compress_t<float, 4>(jobs, n, stream);
+  if (vec == 8) return launch_compress_t<float, 8>(jobs, n, stream);
+  return launch_compress_t<float, 16>(jobs, n, stream);
+}
+
+hipError_t launch_compress(CompressArgs a, hipStream_t stream) {
+  a.slices = compress_slices(a);
+  return launch_jobs(&a, 1, stream);
+}
+
+hipError_t launch_compress_batch(const CompressArgs* jobs_in, int n, hipStream_t stream) {
+  CompressArgs jobs[2] = {jobs_in[0], n > 1 ? jobs_in[1] : jobs_in[0]};
+  for (int k = 0; k < 2; ++k) jobs[k].slices = 1;  // one workgroup per entry and job
+  // jobs of different element widths per lane run one launch each
+  if (n > 1 && compress_vec(jobs[0].dt, jobs[0].D) != compress_vec(jobs[1].dt, jobs[1].D)) {
+    const hipError_t e = launch_jobs(jobs, 1, stream);
+    return e != hipSuccess ? e : launch_jobs(jobs + 1, 1, stream);
+  }
+  return launch_jobs(jobs, n, stream);
 }
 
 }  // namespace csa

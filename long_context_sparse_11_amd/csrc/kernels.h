@@ -29,6 +29,9 @@ struct CompressArgs {
 // rows pooled per entry (m, or 2m with overlap).
 size_t compress_ws_bytes(int dt, int B, int n_out, int D, int rows);
 hipError_t launch_compress(CompressArgs a, hipStream_t stream);
+// n (1 or 2) compressors over the same token block (same dt, B, T, m,
+// overlap, pos0) in one launch, one workgroup per entry and job.
+hipError_t launch_compress_batch(const CompressArgs* jobs, int n, hipStream_t stream);
 
 // ------------------------------------------------------------------- indexer
 struct IndexArgs {

@@ -129,6 +129,43 @@ def test_compress_without_workspace(D, m, T, overlap):
         L.csa_compress(dev(ca), m, ws=ws[:16], **kw)
 
 
+@pytest.mark.parametrize("T,m,overlap,prev,pos", [(4, 4, True, True, [65532, 8, 400, 1 << 20]),
+                                                  (101, 4, True, False, [0, 4, 8, 12]),
+                                                  (300, 128, False, False, [1 << 20, 0, 5, 7])])
+def test_compress_batch(T, m, overlap, prev, pos):
+    """The KV compressor (D 512, RMSNorm, RoPE) and the indexer-key compressor
+    (D 128) over the same block in one launch match the oracle, and the
+    single calls."""
+    rng = np.random.default_rng(T * 3 + m)
+    B = 4
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)
+    jobs, refs, singles = [], [], []
+    for D, norm in ((512, True), (128, False)):
+        ca, za, cb, zb = (synth.Tensor(f(B, T, D), "bf16") for _ in range(4))
+        pcb, pzb = (synth.Tensor(f(B, m, D), "bf16") for _ in range(2))
+        ba, bb = 0.02 * f(m, D), 0.02 * f(m, D)
+        kw = dict(z_a=dev(za), bias_a=dev(ba))
+        okw = dict(pos0=pos)
+        if norm:
+            g = 1 + 0.02 * f(D)
+            kw.update(gain=dev(g), rope_dims=64)
+            okw.update(gain=g, rope_dims=64)
+        if overlap:
+            kw.update(c_b=dev(cb), z_b=dev(zb), bias_b=dev(bb))
+            okw.update(c_b=cb.f32, z_b=zb.f32, bias_b=bb)
+            if prev:
+                kw.update(prev_c_b=dev(pcb), prev_z_b=dev(pzb))
+                okw.update(prev_c_b=pcb.f32, prev_z_b=pzb.f32)
+        out = torch.empty((B, -(-T // m), D), dtype=torch.bfloat16, device="cuda")
+        jobs.append(dict(c_a=dev(ca), out=out, **kw))
+        refs.append(O.csa_compress(ca.f32, za.f32, ba, m, **okw))
+        singles.append(L.csa_compress(dev(ca), m, pos0=i64(pos), **kw))
+    outs = L.csa_compress_batch(jobs, m, pos0=i64(pos))
+    for o, r, s1 in zip(outs, refs, singles):
+        assert rowwise_rel_err(host(o), r) <= TOL_BF16
+        assert rowwise_rel_err(host(o), host(s1)) <= 1e-2
+
+
 def test_compress_closing_block_into_pool():
     """Decode: the closing block's entry is written in place into row N-1 of
     a [B, N, D] pool through the batch stride; nothing else changes."""

@@ -30,7 +30,8 @@ def lib():
 
 def test_header_declares_the_four_calls():
     names = declared_functions()
-    for n in ("csa_compress", "csa_index_topk", "csa_index_scores", "csa_sparse_attn", "hca_attn",
+    for n in ("csa_compress", "csa_compress_batch", "csa_index_topk", "csa_index_scores",
+              "csa_sparse_attn", "hca_attn",
               "csa_compress_ws_bytes", "csa_index_topk_ws_bytes", "csa_attn_ws_bytes",
               "csa_status_string"):
         assert n in names
@@ -99,6 +100,54 @@ def test_compress_validation(lib):
     assert _compress(lib, m=2048) == CSA_ERR_UNSUPPORTED
     # a given workspace must hold what the shape can use (2 entries x 2 x 512 f32)
     assert _compress(lib, T=32, m=16, ws=P, wsb=100) == CSA_ERR_WORKSPACE
+
+
+def _job(**kw):
+    from long_context_sparse_11_amd.binding import CompressJob
+    a = dict(D=512, c_a=64, z_a=64, c_b=64, z_b=64, prev_c_b=None, prev_z_b=None, bias_a=None,
+             bias_b=None, gain=None, eps=1e-6, rope_dims=0, rope_base=10000.0, out=64,
+             out_bstride=0)
+    a.update(kw)
+    return CompressJob(**a)
+
+
+def test_compress_batch_validation(lib):
+    from long_context_sparse_11_amd.binding import CompressJob
+    def call(jobs, n=None, B=2, T=8, m=4, overlap=1):
+        arr = (CompressJob * max(len(jobs), 1))(*jobs)
+        return lib.csa_compress_batch(1, B, T, m, overlap, N, ctypes.cast(arr, ctypes.c_void_p),
+                                      len(jobs) if n is None else n, N)
+    assert call([_job(), _job(D=128)], n=3) == CSA_ERR_ARG
+    assert call([_job()], n=0) == CSA_ERR_ARG
+    assert lib.csa_compress_batch(1, 2, 8, 4, 1, N, N, 1, N) == CSA_ERR_ARG      # no jobs
+    assert call([_job(), _job(D=384)]) == CSA_ERR_UNSUPPORTED                   # second job
+    assert call([_job(), _job(c_b=None)]) == CSA_ERR_ARG                        # overlap, no b
+    assert call([_job(rope_dims=64)]) == CSA_ERR_ARG                            # rope, no positions
+    assert call([_job(), _job(D=128)], B=0) == CSA_OK                           # nothing to do
+
+
+def test_compress_job_layout_matches_c():
+    """The ctypes mirror of csa_compress_job has the C compiler's layout."""
+    import shutil
+    import subprocess
+    import tempfile
+    from long_context_sparse_11_amd.binding import CompressJob as J
+    if not shutil.which("gcc"):
+        pytest.skip("no C compiler")
+    src = ('#include <stdio.h>\n#include <stddef.h>\n#include "csa.h"\nint main(void){'
+           'printf("%zu %zu %zu %zu %zu %zu %zu %zu", sizeof(csa_compress_job),'
+           'offsetof(csa_compress_job, c_a), offsetof(csa_compress_job, gain),'
+           'offsetof(csa_compress_job, eps), offsetof(csa_compress_job, rope_dims),'
+           'offsetof(csa_compress_job, rope_base), offsetof(csa_compress_job, out),'
+           'offsetof(csa_compress_job, out_bstride)); return 0;}')
+    with tempfile.TemporaryDirectory() as d:
+        open(os.path.join(d, "t.c"), "w").write(src)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), "-o",
+                        os.path.join(d, "t"), os.path.join(d, "t.c")], check=True)
+        got = subprocess.run([os.path.join(d, "t")], capture_output=True, text=True).stdout.split()
+    want = [ctypes.sizeof(J), J.c_a.offset, J.gain.offset, J.eps.offset, J.rope_dims.offset,
+            J.rope_base.offset, J.out.offset, J.out_bstride.offset]
+    assert [int(x) for x in got] == want
 
 
 def test_compress_workspace_sizes(lib):
