@@ -250,7 +250,7 @@ def algorithmic(kind, d):
 # ---------------------------------------------------------------------------
 DOMINANT_KERNELS = {
     "index_scores": ["index_decode (decode) / index_prefill (prefill)"],
-    "hca_attn": ["attn_hs<false, true>", "attn_combine<bf16>"],
+    "hca_attn": ["attn_hs<false, true, 4>", "attn_combine<bf16>"],
 }
 KERNEL_SOURCES = {
     "index_scores": ["indexer.hip", "common.h", "kernels.h"],

@@ -188,6 +188,9 @@ __device__ __forceinline__ float half_swap(float x) {
 // Row r of a tile stores its 16-byte chunk c at position c ^ hs_swz(r), which
 // keeps both read patterns free of bank conflicts.
 constexpr int kHsRows = 32;
+// single-tile grids of at most this many workgroups after halving the heads
+// take head groups (one workgroup per compute unit)
+constexpr int64_t kHsHeadSplitBelow = 256;
 // word 3 of a raw (untyped) buffer descriptor: 32-bit data format
 constexpr int kRawBufferWord3 = 0x00020000;
 constexpr int kHsMaxSplitRows = 2048;  // rows of a multi-tile CSA split (LDS index stage)
@@ -214,9 +217,16 @@ __device__ __forceinline__ float row_swap16(float x) {
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-template <bool CSA, bool MULTI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// NW: waves per workgroup, 16 heads each.  With NW = 4 the workgroup takes
+// all 64 heads and four waves share each copied tile; with NW = 2 (single-
+// tile splits of few queries, i.e. decode) it takes 32 heads and blockIdx.z
+// is the head group: half the query slice and half the partial output per
+// workgroup, twice the workgroups.  A workgroup's rows and partials go
+// through one compute unit, whose own rate bounds these short workgroups.
+template <bool CSA, bool MULTI, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_hs(AttnArgs a) {
+  constexpr int RPW = kHsRows / NW;  // tile rows each wave copies
   // two row buffers as distinct objects: with every access naming a fixed
   // one, the compiler can tell that a copy into one does not touch the other
   // (it would otherwise wait for the copy before reading)
@@ -228,7 +238,7 @@ void attn_hs(AttnArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, G = lane >> 4;
-  const int h = 16 * wave + c16;  // this lane's head
+  const int h = 16 * (NW * (int)blockIdx.z + wave) + c16;  // this lane's head
   const int qi = blockIdx.y, sp = blockIdx.x, S = gridDim.x;
   const int b = qi / a.Tq, t = qi - b * a.Tq;
   const int R = a.R;
@@ -273,7 +283,7 @@ void attn_hs(AttnArgs a) {
   // turns row j0 + l (sidx_l: its selected index) into a source address with
   // selects, not branches (an invalid row reads a harmless 1 KiB), and the
   // tile's validity mask comes back.  issue_row(u): wave w copies row
-  // 8w + u with one buffer load into LDS (1 KiB); the row's address is read from
+  // RPW w + u with one buffer load into LDS (1 KiB); the row's address is read from
   // its lane into scalar registers and lane i fetches the 16-byte chunk that
   // belongs at position i (i ^ hs_swz(row)).
   const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -295,7 +305,7 @@ void attn_hs(AttnArgs a) {
     return TileSrc{(int)(uint32_t)src, (int)(uint32_t)(src >> 32), (uint32_t)__ballot(valid)};
   };
   auto issue_row = [&](const TileSrc& ts, int u, bf16_t* dst) {
-    const int r = 8 * wv + u;
+    const int r = RPW * wv + u;
     const uint64_t rs = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(ts.hi, r) << 32) |
                         (uint32_t)__builtin_amdgcn_readlane(ts.lo, r);
     // a buffer load (not a global one): it counts on vmcnt only, so the
@@ -311,13 +321,13 @@ void attn_hs(AttnArgs a) {
   {
     const TileSrc t0 = resolve_tile(start, idx0);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) issue_row(t0, u, s_rows0);
+    for (int u = 0; u < RPW; ++u) issue_row(t0, u, s_rows0);
     vmask = t0.mask;
   }
-  for (int p = tid; p < R / 2; p += 256) rope_cos_sin(tpos, p, a.rope_theta1, s_cos[p], s_sin[p]);
+  for (int p = tid; p < R / 2; p += 64 * NW) rope_cos_sin(tpos, p, a.rope_theta1, s_cos[p], s_sin[p]);
   if constexpr (MULTI && CSA) {
     const int sel_end = min(end, a.K);
-    for (int jj = start + kHsRows + tid; jj < sel_end; jj += 256)
+    for (int jj = start + kHsRows + tid; jj < sel_end; jj += 64 * NW)
       s_idx[jj - start] = a.idx[(int64_t)qi * a.K + jj];
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -388,7 +398,7 @@ void attn_hs(AttnArgs a) {
         sacc[f & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[f & 7], qb[f >> 1], sacc[f & 1], 0, 0, 0);
         if (f + 8 < 32) av[f & 7] = qk_read(f + 8);
         if constexpr (MULTI) {
-          if ((f & 3) == 3) issue_row(nt, f >> 2, next);
+          if (f % (32 / RPW) == 32 / RPW - 1) issue_row(nt, f / (32 / RPW), next);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -664,12 +674,18 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
     const int wc = (a.W > 0 && a.L_win > 0) ? min(a.W, a.L_win) : 0;
     const int64_t lmax = (a.csa ? (int64_t)a.K : (int64_t)a.N_cap) + wc;
     const bool multi = (lmax + a.splits - 1) / a.splits > kHsRows;
+    // single-tile splits in head groups of 32 (two waves, grid z) while the
+    // doubled grid still fits the compute units once
+    const bool halves = !multi && 2LL * a.splits * a.B * a.Tq <= kHsHeadSplitBelow;
+    dim3 grid2(a.splits, a.B * a.Tq, 2), block4(256), block2(128);
     if (a.csa) {
-      if (multi) hipLaunchKernelGGL((attn_hs<true, true>), grid, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((attn_hs<true, false>), grid, dim3(256), 0, stream, a);
+      if (multi) hipLaunchKernelGGL((attn_hs<true, true, 4>), grid, block4, 0, stream, a);
+      else if (halves) hipLaunchKernelGGL((attn_hs<true, false, 2>), grid2, block2, 0, stream, a);
+      else hipLaunchKernelGGL((attn_hs<true, false, 4>), grid, block4, 0, stream, a);
     } else {
-      if (multi) hipLaunchKernelGGL((attn_hs<false, true>), grid, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((attn_hs<false, false>), grid, dim3(256), 0, stream, a);
+      if (multi) hipLaunchKernelGGL((attn_hs<false, true, 4>), grid, block4, 0, stream, a);
+      else if (halves) hipLaunchKernelGGL((attn_hs<false, false, 2>), grid2, block2, 0, stream, a);
+      else hipLaunchKernelGGL((attn_hs<false, false, 4>), grid, block4, 0, stream, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;

@@ -41,7 +41,7 @@ CAL_KERNEL = "bitwise_not"
 # device kernels of each dominant unit (substrings of rocprof kernel names)
 UNIT_KERNELS = {
     "index_scores": {"decode": ["index_decode"], "prefill": ["index_prefill"]},
-    "hca_attn": {"decode": ["attn_hs<false, true>", "attn_combine"]},
+    "hca_attn": {"decode": ["attn_hs<false, true, 4>", "attn_combine"]},
 }
 WORKLOAD_NAME = {"csa64k": "csa_decode_64k", "csa1m": "csa_decode_1m",
                  "hca1m": "hca_decode_1m", "prefill": "csa_prefill_4k_on_60k"}
