@@ -207,11 +207,17 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 }
 
 // Visible compressed entries for a query at absolute position tpos.
+// min(floor((tpos + 1) / m), n_entries), at least 0.  Past the cap the
+// division is skipped, and below it the dividend is under m * n_entries, which
+// for any context under 2^32 tokens fits a 32-bit division (a few scalar
+// instructions instead of the 64-bit division's long expansion and branch).
 __device__ __forceinline__ int visible_entries(int64_t tpos, int m, int n_entries) {
-  int64_t v = (tpos + 1) / m;
-  if (v > n_entries) v = n_entries;
-  if (v < 0) v = 0;
-  return (int)v;
+  const int64_t x = tpos + 1;
+  if (x <= 0 || n_entries <= 0) return 0;
+  const int64_t lim = (int64_t)m * n_entries;
+  if (x >= lim) return n_entries;
+  if (lim <= 0xffffffffLL) return (int)((uint32_t)x / (uint32_t)m);
+  return (int)(x / m);
 }
 
 }  // namespace csa

@@ -94,47 +94,54 @@ __device__ __forceinline__ float tile_score(const bf16x8_t (&qa)[2][8], const bf
 // tiles interleaved over the waves so the WG reads one contiguous range.
 __global__ __launch_bounds__(256) void index_decode(IndexArgs a, int tiles_per_wave) {
   __shared__ __attribute__((aligned(16))) bf16_t sq[64 * 128];
-  __shared__ __attribute__((aligned(16))) float sw[64];
+  // head weights: thread i stores a copy of weights 4(i%16) .. +3 in slot i
+  // (a store in every thread: a branch around it would drag its load along)
+  __shared__ __attribute__((aligned(16))) float sw[256 * 4];
   const int query = blockIdx.y;
   const int b = query / a.Tq;
   const int t = query - b * a.Tq;
-  const int n_vis = visible_entries(a.q_pos0[b] + t, a.m, min(a.n_entries[b], a.N_cap));
+  const int64_t tpos = a.q_pos0[b] + t;
+  const int n_ent = a.n_entries[b];
   const int chunk_tiles = 4 * tiles_per_wave;
   const int tile0 = blockIdx.x * chunk_tiles;
-  if (tile0 * 32 >= n_vis) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 31, g = lane >> 5;
+  const bf16_t* kbase = (const bf16_t*)a.k + (int64_t)b * a.N_cap * 128 + g * 64;
+  float* out = a.scores + (int64_t)query * a.N_cap;
+  // key rows past the visible range are read (every row below N_cap is
+  // allocated) but never scored, so no load waits for the visible count
+  auto load = [&](int tl, bf16x8_t(&dst)[8]) {
+    const int key = min(tl * 32 + j, a.N_cap - 1);
+    const bf16_t* kp = kbase + (int64_t)key * 128;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) dst[s] = *reinterpret_cast<const bf16x8_t*>(kp + 8 * s);
+  };
 
   // the query's 64 x 128 head matrix and head weights, fetched once per
-  // workgroup (4 + 1 vector loads per thread) and shared by its waves
-  {
-    const uint4* qg = reinterpret_cast<const uint4*>((const bf16_t*)a.q + (int64_t)query * 64 * 128);
-    uint4 v[4];
+  // workgroup (4 + 1 vector loads per thread) and shared by its waves; the
+  // first key tile is requested behind them, before the visible count is
+  // known, so its latency overlaps theirs.  No branch separates these loads
+  // from their use (a workgroup past the visible range runs through with an
+  // empty tile loop), so the compiler keeps them at the top.
+  uint4 v[4];
+  const uint4* qg = reinterpret_cast<const uint4*>((const bf16_t*)a.q + (int64_t)query * 64 * 128);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = qg[threadIdx.x + 256 * u];
+  for (int u = 0; u < 4; ++u) v[u] = qg[threadIdx.x + 256 * u];
+  const f32x4_t wq = reinterpret_cast<const f32x4_t*>(a.w + (int64_t)query * 64)[threadIdx.x & 15];
+  bf16x8_t k0[8], k1[8];
+  int tile = tile0 + wave;
+  load(tile, k0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) reinterpret_cast<uint4*>(sq)[threadIdx.x + 256 * u] = v[u];
-    if (threadIdx.x < 16)
-      reinterpret_cast<f32x4_t*>(sw)[threadIdx.x] =
-          reinterpret_cast<const f32x4_t*>(a.w + (int64_t)query * 64)[threadIdx.x];
-  }
+  for (int u = 0; u < 4; ++u) reinterpret_cast<uint4*>(sq)[threadIdx.x + 256 * u] = v[u];
+  reinterpret_cast<f32x4_t*>(sw)[threadIdx.x] = wq;
+  const int n_vis = visible_entries(tpos, a.m, min(n_ent, a.N_cap));
   __syncthreads();
   bf16x8_t qa[2][8];
   load_query_operand(sq, lane, qa);
   float wv[2][16];
   load_head_weights(sw, lane, wv);
 
-  const bf16_t* kbase = (const bf16_t*)a.k + (int64_t)b * a.N_cap * 128 + g * 64;
-  float* out = a.scores + (int64_t)query * a.N_cap;
-
-  int tile = tile0 + wave;
   const int tile_end = min(tile0 + chunk_tiles, (n_vis + 31) >> 5);
-  auto load = [&](int tl, bf16x8_t(&dst)[8]) {
-    const int key = min(tl * 32 + j, n_vis - 1);
-    const bf16_t* kp = kbase + (int64_t)key * 128;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) dst[s] = *reinterpret_cast<const bf16x8_t*>(kp + 8 * s);
-  };
   auto score = [&](int tl, const bf16x8_t(&kb)[8]) {
     const float sc = tile_score(qa, kb, wv);
     const int key = tl * 32 + j;
@@ -142,8 +149,6 @@ __global__ __launch_bounds__(256) void index_decode(IndexArgs a, int tiles_per_w
   };
   // two key buffers in turn: the next tile's loads are in flight while the
   // current tile is scored, with no register copy between them
-  bf16x8_t k0[8], k1[8];
-  if (tile < tile_end) load(tile, k0);
   while (tile < tile_end) {
     const int t1 = tile + 4;
     if (t1 < tile_end) load(t1, k1);

@@ -589,6 +589,32 @@ def test_index_two_level_with_few_visible():
     assert (gidx[1, 0] >= 0).sum() == O.visible_count(pos0[1], m, N)
 
 
+# Selection over rows of the float32 toy indexer, one row at a time or many
+# (rows over 16,384 entries: chunk winners, then a merge), K from 16 to the
+# largest supported.  Positions are set so that the rows see slightly
+# different visible counts (ragged tails).  dup: key rows drawn from 24
+# distinct vectors, so scores repeat and ties straddle the cut.
+@pytest.mark.parametrize("rows,N,K,dup", [
+    (3, 20000, 512, True), (136, 20000, 512, True),
+    (2, 40000, 4096, False), (136, 40000, 4096, False),
+    (5, 3000, 16, True), (136, 700, 16, False),
+    (1, 262144, 512, False), (2, 131072, 512, True)])
+def test_topk_selectors(rows, N, K, dup):
+    rng = np.random.default_rng(rows * 1000 + N + K)
+    Hi, Di, m = 4, 32, 4
+    q = rng.standard_normal((1, rows, Hi, Di)).astype(np.float32)
+    w = np.abs(rng.standard_normal((1, rows, Hi))).astype(np.float32)
+    if dup:
+        base = rng.standard_normal((24, Di)).astype(np.float32)
+        k = base[rng.integers(0, 24, size=N)][None]
+    else:
+        k = rng.standard_normal((1, N, Di)).astype(np.float32)
+    pos0 = np.array([m * (N - rows)])
+    # |score| stays below ~250 here (4 heads, 32-term dots, |w| < ~4); float32
+    # accumulation of 36 terms of that size is off by at most ~36 * 2^-24 * 250
+    _check_index(q, w, k, np.array([N], np.int32), pos0, K, m, score_atol=5e-4)
+
+
 def _linear_bin_count(scores, K):
     """Population of the threshold bin of a 4096-bin linear map of the score
     range (float32, as the selector computes it): tells which way the exact
