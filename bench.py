@@ -5,8 +5,9 @@ Default workload (the headline metric's configuration): CSA decode, batch 4,
 one new query per sequence at context 65,536 (16,384 compressed entries),
 64 heads x 512, RoPE 64, indexer 64 x 128, top-k 512, window 128.  A step is
 the whole hot path for that batch: compress the closing block (KV entry and
-indexer key, written in place into the caches), lightning-indexer scores +
-top-512 selection, sparse gather attention with the sink.  Other workloads
+indexer key, written in place into the caches; one launch with the indexer
+scoring), lightning-indexer scores + top-512 selection, sparse gather
+attention with the sink.  Other workloads
 (--workload): csa1m (batch 8, context 1,048,576), hca1m (HCA decode, batch
 16, context 1,048,576: compress + hca_attn), prefill (CSA chunk of 4,096
 queries on a 61,440-token prefix).
@@ -128,19 +129,18 @@ class Step:
             N, D, Di, m = g["N"], g["D"], g["Di"], g["m"]
             pool, kidx = g["pool"], g["k_idx"]
             return [
-                # the KV entry and the indexer key of the closing block, one launch
-                ("compress", lambda: L.csa_compress_batch([
-                    dict(c_a=g["c_a"], z_a=g["z_a"], c_b=g["c_b"], z_b=g["z_b"],
-                         prev_c_b=g["prev_c_b"], prev_z_b=g["prev_z_b"], bias_a=g["bias_a"],
-                         bias_b=g["bias_b"], gain=g["gain"], rope_dims=g["R"],
-                         out=pool[:, N - 1:], out_bstride=N * D),
-                    dict(c_a=g["ic_a"], z_a=g["iz_a"], c_b=g["ic_b"], z_b=g["iz_b"],
-                         prev_c_b=g["iprev_c_b"], prev_z_b=g["iprev_z_b"], bias_a=g["ibias_a"],
-                         bias_b=g["ibias_b"], out=kidx[:, N - 1:], out_bstride=N * Di)],
-                    m, pos0=g["block_pos0"])),
-                ("index_topk", lambda: L.csa_index_topk(g["q_idx"], g["w_idx"], kidx,
-                                                        g["n_entries"], g["q_pos0"], g["K"], m,
-                                                        ws=self.ws_i, idx_out=self.idx)),
+                # the indexer key and the KV entry of the closing block (row
+                # n_entries - 1 of their pools), then the indexer top-K: the
+                # compressors run inside the indexer launch
+                ("compress_index_topk", lambda: L.csa_decode_index_topk(
+                    g["q_idx"], g["w_idx"], g["n_entries"], g["q_pos0"], g["K"], m, [
+                        dict(c_a=g["ic_a"], z_a=g["iz_a"], c_b=g["ic_b"], z_b=g["iz_b"],
+                             prev_c_b=g["iprev_c_b"], prev_z_b=g["iprev_z_b"],
+                             bias_a=g["ibias_a"], bias_b=g["ibias_b"], out=kidx),
+                        dict(c_a=g["c_a"], z_a=g["z_a"], c_b=g["c_b"], z_b=g["z_b"],
+                             prev_c_b=g["prev_c_b"], prev_z_b=g["prev_z_b"], bias_a=g["bias_a"],
+                             bias_b=g["bias_b"], gain=g["gain"], rope_dims=g["R"], out=pool)],
+                    block_pos0=g["block_pos0"], ws=self.ws_i, idx_out=self.idx)),
                 ("sparse_attn", lambda: L.csa_sparse_attn(g["q"], pool, self.idx, g["win"],
                                                           g["win_pos0"], g["W"], g["sink"],
                                                           g["q_pos0"], rope_dims=g["R"],
@@ -220,8 +220,9 @@ def algorithmic(kind, d):
                                "flops": B * 2 * Hi * Di * N}
         rows = min(K, N) + W
         attn_bytes = B * (rows * D * bf + 2 * H * D * bf + K * 4)
-        out["bytes"] = {"compress": comp, "index_topk": idx_bytes, "sparse_attn": attn_bytes}
-        out["flops"] = {"index_topk": B * 2 * Hi * Di * N, "sparse_attn": B * 4 * H * D * rows}
+        out["bytes"] = {"compress_index_topk": comp + idx_bytes, "sparse_attn": attn_bytes}
+        out["flops"] = {"compress_index_topk": B * 2 * Hi * Di * N,
+                        "sparse_attn": B * 4 * H * D * rows}
     elif kind == "hca1m":
         N = d["N"]
         comp = B * (2 * m * D * bf + D * bf)

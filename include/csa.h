@@ -177,6 +177,39 @@ int csa_index_topk(int dt, int B, int Tq, int Hi, int Di, int N_cap, int K, int 
 size_t csa_index_topk_ws_bytes(int B, int Tq, int Hi, int N_cap, int K);
 
 /* ---------------------------------------------------------------------------
+ * csa_decode_index_topk - a decode step's compressors and indexer in one call.
+ *
+ * [P2] section 3.2.2 (eqs. 9-12, then 13-17): the block of m tokens that
+ * closes at this step becomes a new compressed entry, which the indexer
+ * ranks with the older ones.  For each sequence b the entry goes to row
+ * r_b = min(n_entries[b], N_cap) - 1 (nothing when that is negative) of
+ * each job's pool; jobs[0] is the indexer-key compressor and its pool is
+ * the indexer's k_idx.  Then exactly csa_index_topk over k_idx.  The same
+ * results as csa_compress_batch (one entry, written at row r_b) followed by
+ * csa_index_topk; for bf16 with Hi = 64, Di = 128, Tq < 8, job D <= 512
+ * and at most 16 pooled rows the compressors run inside the indexer launch
+ * (one launch fewer, the fresh key scored by the workgroup that built it),
+ * else as a launch of their own.
+ *
+ *   jobs[n_jobs]   n_jobs 1 or 2, as for csa_compress_batch with T = m:
+ *                  c_a, z_a [B, m, D]; prev_c_b, prev_z_b [B, m, D] or NULL
+ *                  (overlap: the previous block's second stream; c_b, z_b
+ *                  must be given and are not read); bias_a, bias_b [m, D];
+ *                  out = the pool base [B, N_cap, D], out_bstride 0 or
+ *                  N_cap * D.  jobs[0].D == Di.
+ *   block_pos0 [B] int64 device  position of the closing block's first token
+ *   other arguments as csa_index_topk (ws of csa_index_topk_ws_bytes).
+ * Errors: as csa_compress_batch and csa_index_topk; CSA_ERR_ARG also for
+ * N_cap == 0, jobs[0].D != Di or another out_bstride.
+ * ------------------------------------------------------------------------- */
+int csa_decode_index_topk(int dt, int B, int Tq, int Hi, int Di, int N_cap, int K, int m,
+                          int overlap, const int64_t* block_pos0, const csa_compress_job* jobs,
+                          int n_jobs, const void* q_idx, const float* w_idx,
+                          const int32_t* n_entries, const int64_t* q_pos0, int32_t* idx_out,
+                          float* score_out, float* all_scores, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* ---------------------------------------------------------------------------
  * csa_index_scores - the lightning indexer scores alone (the scoring half
  * of csa_index_topk, same kernels, no selection).
  *

@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     csa_compress,
     csa_compress_batch,
     csa_compress_ws_bytes,
+    csa_decode_index_topk,
     csa_index_scores,
     csa_index_topk,
     csa_index_topk_ws_bytes,

@@ -35,6 +35,11 @@ _SIGS = {
                                   _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                   _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                   _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "csa_decode_index_topk": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                          _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_void_p,
+                                          _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_void_p,
+                                          _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                          _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "csa_index_scores": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                      _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                      _c.c_void_p, _c.c_void_p, _c.c_void_p]),
@@ -164,6 +169,35 @@ class CompressJob(ctypes.Structure):
                 ("rope_base", _c.c_double), ("out", _c.c_void_p), ("out_bstride", _c.c_int64)]
 
 
+def _job_array(jobs, B, T, overlap, out_shape):
+    """ctypes array of csa_compress_job from job dicts; out_shape(D) is the
+    shape each job's ``out`` must have (row stride D, batch stride
+    ``out_bstride`` or the rows times D)."""
+    arr = (CompressJob * len(jobs))()
+    for k, j in enumerate(jobs):
+        c_a, out = j["c_a"], j["out"]
+        Bj, Tj, D = c_a.shape
+        if (Bj, Tj) != (B, T) or (j.get("c_b") is not None) != overlap or c_a.dtype != jobs[0]["c_a"].dtype:
+            raise ValueError("jobs must share B, T, dtype and overlap")
+        ts = [j.get(n) for n in ("z_a", "c_b", "z_b", "prev_c_b", "prev_z_b", "bias_a", "bias_b", "gain")]
+        _dev(c_a, *ts)
+        _f32(j.get("bias_a")), _f32(j.get("bias_b")), _f32(j.get("gain"))
+        shape = out_shape(D)
+        bs = j.get("out_bstride", 0) or shape[1] * D
+        if (tuple(out.shape) != shape or out.dtype != c_a.dtype or not out.is_cuda
+                or out.stride(2) != 1 or (shape[1] > 1 and out.stride(1) != D)
+                or (B > 1 and out.stride(0) != bs)):
+            raise ValueError(f"out must be {list(shape)} with row stride D and batch stride "
+                             "out_bstride")
+        p = lambda t: t.data_ptr() if t is not None else None
+        arr[k] = CompressJob(D, p(c_a), p(j.get("z_a")), p(j.get("c_b")), p(j.get("z_b")),
+                             p(j.get("prev_c_b")), p(j.get("prev_z_b")), p(j.get("bias_a")),
+                             p(j.get("bias_b")), p(j.get("gain")), float(j.get("eps", 1e-6)),
+                             int(j.get("rope_dims", 0)), float(j.get("rope_base", 10000.0)),
+                             out.data_ptr(), int(j.get("out_bstride", 0)))
+    return arr
+
+
 def csa_compress_batch(jobs, m, *, pos0=None, stream=None):
     """Up to two compressors over the same token block in one launch (see
     include/csa.h).  ``jobs``: dicts with the keyword arguments of
@@ -175,28 +209,7 @@ def csa_compress_batch(jobs, m, *, pos0=None, stream=None):
     overlap = jobs[0].get("c_b") is not None
     _i64(pos0)
     _dev(pos0)
-    arr = (CompressJob * len(jobs))()
-    for k, j in enumerate(jobs):
-        c_a, out = j["c_a"], j["out"]
-        Bj, Tj, D = c_a.shape
-        if (Bj, Tj) != (B, T) or (j.get("c_b") is not None) != overlap or c_a.dtype != jobs[0]["c_a"].dtype:
-            raise ValueError("jobs must share B, T, dtype and overlap")
-        ts = [j.get(n) for n in ("z_a", "c_b", "z_b", "prev_c_b", "prev_z_b", "bias_a", "bias_b", "gain")]
-        _dev(c_a, *ts)
-        _f32(j.get("bias_a")), _f32(j.get("bias_b")), _f32(j.get("gain"))
-        n_out = -(-T // m)
-        bs = j.get("out_bstride", 0) or n_out * D
-        if (tuple(out.shape) != (B, n_out, D) or out.dtype != c_a.dtype or not out.is_cuda
-                or out.stride(2) != 1 or (n_out > 1 and out.stride(1) != D)
-                or (B > 1 and out.stride(0) != bs)):
-            raise ValueError("out must be [B, ceil(T/m), D] with row stride D and batch stride "
-                             "out_bstride")
-        p = lambda t: t.data_ptr() if t is not None else None
-        arr[k] = CompressJob(D, p(c_a), p(j.get("z_a")), p(j.get("c_b")), p(j.get("z_b")),
-                             p(j.get("prev_c_b")), p(j.get("prev_z_b")), p(j.get("bias_a")),
-                             p(j.get("bias_b")), p(j.get("gain")), float(j.get("eps", 1e-6)),
-                             int(j.get("rope_dims", 0)), float(j.get("rope_base", 10000.0)),
-                             out.data_ptr(), int(j.get("out_bstride", 0)))
+    arr = _job_array(jobs, B, T, overlap, lambda D: (B, -(-T // m), D))
     st = lib().csa_compress_batch(_dt(jobs[0]["c_a"]), B, T, m, int(overlap), _p(pos0),
                                   ctypes.cast(arr, ctypes.c_void_p), len(jobs), _stream(stream))
     _check(st, "csa_compress_batch")
@@ -236,6 +249,44 @@ def csa_index_topk(q_idx, w_idx, k_idx, n_entries, q_pos0, K, m, *, want_scores=
                               _p(all_scores), _p(ws), 0 if ws is None else ws.numel(),
                               _stream(stream))
     _check(st, "csa_index_topk")
+    return idx_out, score_out, all_scores
+
+
+def csa_decode_index_topk(q_idx, w_idx, n_entries, q_pos0, K, m, jobs, *, block_pos0=None,
+                          want_scores=False, want_all_scores=False, ws=None, idx_out=None,
+                          stream=None):
+    """A decode step's compressors and indexer in one call (see include/csa.h).
+    ``jobs``: one or two dicts as for csa_compress_batch over the closing
+    block (c_a [B, m, D]); each ``out`` is the whole pool [B, N_cap, D] and
+    the new entry of sequence b lands in row min(n_entries[b], N_cap) - 1;
+    jobs[0] is the indexer-key compressor, its pool the indexer's keys.
+    Returns (idx, score_out or None, all_scores or None) as csa_index_topk."""
+    B, Tq, Hi, Di = q_idx.shape
+    k_idx = jobs[0]["out"]
+    N_cap = k_idx.shape[1]
+    overlap = jobs[0].get("c_b") is not None
+    _dev(q_idx, w_idx, n_entries, q_pos0, block_pos0)
+    _f32(w_idx), _i64(q_pos0), _i64(block_pos0)
+    if n_entries.dtype != torch.int32:
+        raise TypeError("n_entries is int32")
+    if jobs[0]["c_a"].shape[1] != m:
+        raise ValueError("the jobs' streams hold one block of m tokens")
+    arr = _job_array(jobs, B, m, overlap, lambda D: (B, N_cap, D))
+    dev = q_idx.device
+    if idx_out is None:
+        idx_out = torch.empty((B, Tq, K), dtype=torch.int32, device=dev)
+    score_out = torch.empty((B, Tq, K), dtype=torch.float32, device=dev) if want_scores else None
+    all_scores = (torch.empty((B, Tq, N_cap), dtype=torch.float32, device=dev)
+                  if want_all_scores else None)
+    need = csa_index_topk_ws_bytes(B, Tq, Hi, N_cap, K)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = lib().csa_decode_index_topk(_dt(q_idx), B, Tq, Hi, Di, N_cap, K, m, int(overlap),
+                                     _p(block_pos0), ctypes.cast(arr, ctypes.c_void_p), len(jobs),
+                                     _p(q_idx), _p(w_idx), _p(n_entries), _p(q_pos0), _p(idx_out),
+                                     _p(score_out), _p(all_scores), _p(ws),
+                                     0 if ws is None else ws.numel(), _stream(stream))
+    _check(st, "csa_decode_index_topk")
     return idx_out, score_out, all_scores
 
 

@@ -119,11 +119,16 @@ CSA_EXPORT size_t csa_index_topk_ws_bytes(int B, int Tq, int Hi, int N_cap, int 
   return bytes;
 }
 
-CSA_EXPORT int csa_index_topk(int dt, int B, int Tq, int Hi, int Di, int N_cap, int K, int m,
-                              const void* q_idx, const float* w_idx, const void* k_idx,
-                              const int32_t* n_entries, const int64_t* q_pos0, int32_t* idx_out,
-                              float* score_out, float* all_scores, void* ws, size_t ws_bytes,
-                              void* stream) {
+namespace {
+
+// Indexer scores and top-K, optionally preceded by the fresh-entry
+// compressors of a decode step (fused into the indexer launch when its
+// kernel covers the shape, else a compressor launch first).
+int index_topk_run(int dt, int B, int Tq, int Hi, int Di, int N_cap, int K, int m,
+                   const void* q_idx, const float* w_idx, const void* k_idx,
+                   const int32_t* n_entries, const int64_t* q_pos0, int32_t* idx_out,
+                   float* score_out, float* all_scores, void* ws, size_t ws_bytes,
+                   const FreshJobs* fresh, hipStream_t s) {
   if (dt != CSA_F32 && dt != CSA_BF16) return CSA_ERR_ARG;
   if (B < 0 || Tq < 0 || Hi <= 0 || Di <= 0 || N_cap < 0 || K <= 0 || m <= 0) return CSA_ERR_ARG;
   if (B == 0 || Tq == 0) return CSA_OK;
@@ -134,7 +139,6 @@ CSA_EXPORT int csa_index_topk(int dt, int B, int Tq, int Hi, int Di, int N_cap, 
   if ((int64_t)topk_chunks(N_cap) * K > kTopkCap) return CSA_ERR_UNSUPPORTED;
   const size_t need = csa_index_topk_ws_bytes(B, Tq, Hi, N_cap, K);
   if (N_cap > 0 && (!ws || ws_bytes < need)) return CSA_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
   const size_t q = (size_t)B * Tq;
   char* w = (char*)ws;
   float* scores = all_scores ? all_scores : (float*)w;
@@ -142,7 +146,13 @@ CSA_EXPORT int csa_index_topk(int dt, int B, int Tq, int Hi, int Di, int N_cap, 
 
   if (N_cap > 0) {
     IndexArgs ia{dt, B, Tq, Hi, Di, N_cap, m, q_idx, w_idx, k_idx, n_entries, q_pos0, scores};
-    hipError_t e = launch_index_scores(ia, s);
+    hipError_t e;
+    if (fresh && index_fresh_fused(ia, *fresh)) {
+      e = launch_index_fresh(ia, *fresh, s);
+    } else {
+      e = fresh ? launch_compress_batch(fresh->job, fresh->n_jobs, s) : hipSuccess;
+      if (e == hipSuccess) e = launch_index_scores(ia, s);
+    }
     if (e != hipSuccess) return CSA_ERR_HIP;
   }
   const int nc = topk_chunks(N_cap);
@@ -174,6 +184,49 @@ CSA_EXPORT int csa_index_topk(int dt, int B, int Tq, int Hi, int Di, int N_cap, 
   tb.out_idx = idx_out;
   tb.out_scores = score_out;
   return status_of(launch_topk(tb, (int)q, s));
+}
+
+}  // namespace
+
+CSA_EXPORT int csa_index_topk(int dt, int B, int Tq, int Hi, int Di, int N_cap, int K, int m,
+                              const void* q_idx, const float* w_idx, const void* k_idx,
+                              const int32_t* n_entries, const int64_t* q_pos0, int32_t* idx_out,
+                              float* score_out, float* all_scores, void* ws, size_t ws_bytes,
+                              void* stream) {
+  return index_topk_run(dt, B, Tq, Hi, Di, N_cap, K, m, q_idx, w_idx, k_idx, n_entries, q_pos0,
+                        idx_out, score_out, all_scores, ws, ws_bytes, nullptr,
+                        (hipStream_t)stream);
+}
+
+CSA_EXPORT int csa_decode_index_topk(int dt, int B, int Tq, int Hi, int Di, int N_cap, int K,
+                                     int m, int overlap, const int64_t* block_pos0,
+                                     const csa_compress_job* jobs, int n_jobs, const void* q_idx,
+                                     const float* w_idx, const int32_t* n_entries,
+                                     const int64_t* q_pos0, int32_t* idx_out, float* score_out,
+                                     float* all_scores, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  if (n_jobs < 1 || n_jobs > 2 || !jobs) return CSA_ERR_ARG;
+  if (B < 0 || Tq < 0 || N_cap < 0 || m <= 0) return CSA_ERR_ARG;
+  if (jobs[0].D != Di) return CSA_ERR_ARG;
+  if (B == 0 || Tq == 0) return CSA_OK;
+  if (N_cap == 0) return CSA_ERR_ARG;  // the fresh entries need a row
+  FreshJobs f{};
+  f.n_jobs = n_jobs;
+  for (int k = 0; k < n_jobs; ++k) {
+    const csa_compress_job& j = jobs[k];
+    const int64_t pool_stride = (int64_t)N_cap * j.D;
+    if (j.out_bstride != 0 && j.out_bstride != pool_stride) return CSA_ERR_ARG;
+    const int st = compress_args(dt, B, m, j.D, m, overlap, j.c_a, j.z_a, j.c_b, j.z_b,
+                                 j.prev_c_b, j.prev_z_b, j.bias_a, j.bias_b, j.gain, j.eps,
+                                 j.rope_dims, j.rope_base, block_pos0, j.out, pool_stride, f.job[k]);
+    if (st != CSA_OK) return st == 1 ? CSA_ERR_ARG : st;
+    f.job[k].rows_at = n_entries;
+    f.job[k].rows_cap = N_cap;
+    f.job[k].slices = 1;
+  }
+  return index_topk_run(dt, B, Tq, Hi, Di, N_cap, K, m, q_idx, w_idx, jobs[0].out, n_entries,
+                        q_pos0, idx_out, score_out, all_scores, ws, ws_bytes, &f,
+                        (hipStream_t)stream);
 }
 
 CSA_EXPORT int csa_index_scores(int dt, int B, int Tq, int Hi, int Di, int N_cap, int m,

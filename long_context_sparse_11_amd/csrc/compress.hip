@@ -194,7 +194,12 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a0, Compress
   }
 
   const int64_t bstride = a.out_bstride ? a.out_bstride : (int64_t)a.n_out * D;
-  T* op = (T*)a.out + (int64_t)b * bstride + (int64_t)i * D + c0;
+  int64_t ent = i;
+  if (a.rows_at) {
+    ent = (int64_t)min(a.rows_at[b], a.rows_cap) - 1;
+    if (ent < 0) return;
+  }
+  T* op = (T*)a.out + (int64_t)b * bstride + ent * D + c0;
   Elem<T>::template store<VEC>(op, y);
 }
 

@@ -89,10 +89,146 @@ __device__ __forceinline__ float tile_score(const bf16x8_t (&qa)[2][8], const bf
   return sc + __uint_as_float(__lane_id() < 32 ? sw[1] : sw[0]);
 }
 
+// ------------------------------------------------------------ fresh entries
+// The block of m tokens that closes at this decode step, pooled into one
+// entry as the compressor does ("DeepSeek-v4 Beyond Basics" section 3.2.2,
+// eqs. 9-12; compress.hip): per channel, a softmax over the block's rows of
+// z + bias (with overlap, also the previous block's second-stream rows)
+// weights the rows of c; then RMSNorm with the gain, and RoPE of the last
+// rope_dims channels at the block's position.  One workgroup; thread t holds
+// channels 2t and 2t + 1.  The entry goes to row `row` of the job's pool.
+// For the indexer-key job the entry is then scored against every query of
+// the sequence that sees it, from the bf16 value as stored.
+constexpr int kFreshMaxRows = 16;
+
+__device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressArgs& j, int b,
+                                            int row, bool score, float* skey, float* red) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int D = j.D, m = j.m;
+  const int c0 = 2 * tid;
+  const bool act = c0 < D;
+  const int cc = act ? c0 : 0;
+  const bool prev = j.overlap && j.prev_c_b;
+  const int nr = m + (prev ? m : 0);
+  const bf16_t* ca = (const bf16_t*)j.c_a + (int64_t)b * j.T * D;
+  const bool hza = j.z_a != nullptr;
+  const bf16_t* za = hza ? (const bf16_t*)j.z_a + (int64_t)b * j.T * D : ca;
+  const bf16_t* cb = prev ? (const bf16_t*)j.prev_c_b + (int64_t)b * m * D : ca;
+  const bf16_t* zb = prev ? (const bf16_t*)j.prev_z_b + (int64_t)b * m * D : za;
+  // every load first: rows past the block re-read row 0 and are dropped
+  uint32_t cw[kFreshMaxRows], zw[kFreshMaxRows];
+  float2 bw[kFreshMaxRows];
+#pragma unroll
+  for (int r = 0; r < kFreshMaxRows; ++r) {
+    const int rr = r < nr ? r : 0;
+    const bool in_a = rr < m;
+    const int64_t ro = (int64_t)(in_a ? rr : rr - m) * D + cc;
+    cw[r] = *reinterpret_cast<const uint32_t*>((in_a ? ca : cb) + ro);
+    zw[r] = *reinterpret_cast<const uint32_t*>((in_a ? za : zb) + ro);
+    const float* bp = in_a ? j.bias_a : j.bias_b;
+    bw[r] = bp ? *reinterpret_cast<const float2*>(bp + ro) : make_float2(0.f, 0.f);
+  }
+  const float2 gn = j.gain ? *reinterpret_cast<const float2*>(j.gain + cc) : make_float2(1.f, 1.f);
+  const int64_t pos = j.pos0 ? j.pos0[b] : 0;
+
+  auto logit = [&](int r, int e) {  // base-2 logit of row r, channel c0 + e
+    const bool in_a = r < m;
+    const float z = (in_a ? hza : true) ? bf16_to_f32(e ? zw[r] >> 16 : zw[r] & 0xffffu) : 0.f;
+    return (z + (e ? bw[r].y : bw[r].x)) * kLog2e;
+  };
+  float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < kFreshMaxRows; ++r) {
+    if (r < nr) {
+      mx0 = fmaxf(mx0, logit(r, 0));
+      mx1 = fmaxf(mx1, logit(r, 1));
+    }
+  }
+  float den0 = 0.f, den1 = 0.f, acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+  for (int r = 0; r < kFreshMaxRows; ++r) {
+    if (r < nr) {
+      const float p0 = exp2f(logit(r, 0) - mx0), p1 = exp2f(logit(r, 1) - mx1);
+      den0 += p0;
+      den1 += p1;
+      acc0 += p0 * bf16_to_f32(cw[r] & 0xffffu);
+      acc1 += p1 * bf16_to_f32(cw[r] >> 16);
+    }
+  }
+  float y0 = acc0 / den0, y1 = acc1 / den1;
+  if (j.gain) {
+    float ss = act ? y0 * y0 + y1 * y1 : 0.f;
+    ss = wave_sum(ss);
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    ss = red[0] + red[1] + red[2] + red[3];
+    const float inv = 1.0f / sqrtf(ss / (float)D + j.eps);
+    y0 = y0 * inv * gn.x;
+    y1 = y1 * inv * gn.y;
+  }
+  const int R = j.rope_dims;
+  if (R > 0 && act && c0 >= D - R) {
+    float cs, sn;
+    rope_cos_sin(pos, (c0 - (D - R)) >> 1, j.rope_theta1, cs, sn);
+    const float x0 = y0, x1 = y1;
+    y0 = x0 * cs - x1 * sn;
+    y1 = x0 * sn + x1 * cs;
+  }
+  const uint32_t packed = pack_bf16x2(y0, y1);
+  if (act)
+    *reinterpret_cast<uint32_t*>((bf16_t*)j.out + (int64_t)b * j.out_bstride + (int64_t)row * D +
+                                 c0) = packed;
+  if (!score) return;
+
+  // Score the stored entry for every query t of the sequence that sees it:
+  // thread (h = tid / 4, quarter qq = tid % 4) takes head h over channels
+  // 32 qq .. 32 qq + 31, the 4 quarters meet by lane swaps, the 64 heads by a
+  // wave sum and the 4 waves through LDS.
+  if (act) {
+    skey[c0] = bf16_to_f32(packed & 0xffffu);
+    skey[c0 + 1] = bf16_to_f32(packed >> 16);
+  }
+  __syncthreads();
+  const int h = tid >> 2, qq = tid & 3;
+  const int n_ent = min(a.n_entries[b], a.N_cap);
+  for (int t = 0; t < a.Tq; ++t) {
+    const int query = b * a.Tq + t;
+    if (row >= visible_entries(a.q_pos0[b] + t, a.m, n_ent)) continue;
+    const uint4* qp = reinterpret_cast<const uint4*>((const bf16_t*)a.q +
+                                                     ((int64_t)query * 64 + h) * 128 + 32 * qq);
+    uint4 qv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) qv[u] = qp[u];
+    const float wh = a.w[(int64_t)query * 64 + h];
+    float dot = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t wd[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 32 * qq + 8 * u + 2 * e;
+        dot += bf16_to_f32(wd[e] & 0xffffu) * skey[c];
+        dot += bf16_to_f32(wd[e] >> 16) * skey[c + 1];
+      }
+    }
+    dot += __shfl_xor(dot, 1);
+    dot += __shfl_xor(dot, 2);
+    const float v = wave_sum(qq == 0 ? wh * fmaxf(dot, 0.f) : 0.f);
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    if (tid == 0) a.scores[(int64_t)query * a.N_cap + row] = red[0] + red[1] + red[2] + red[3];
+    __syncthreads();
+  }
+}
+
 // ------------------------------------------------------------------- decode
 // grid (chunks, B*Tq); 4 waves; chunk = 4 * tiles_per_wave tiles of 32 keys,
 // tiles interleaved over the waves so the WG reads one contiguous range.
-__global__ __launch_bounds__(256) void index_decode(IndexArgs a, int tiles_per_wave) {
+// FRESH: the last f.n_jobs columns of the grid compress the closing block
+// (fresh_entry, query t = 0 of each sequence) and the other workgroups score
+// the entries stored before it.
+template <bool FRESH>
+__global__ __launch_bounds__(256) void index_decode(IndexArgs a, int tiles_per_wave, FreshJobs f) {
   __shared__ __attribute__((aligned(16))) bf16_t sq[64 * 128];
   // head weights: thread i stores a copy of weights 4(i%16) .. +3 in slot i
   // (a store in every thread: a branch around it would drag its load along)
@@ -102,6 +238,15 @@ __global__ __launch_bounds__(256) void index_decode(IndexArgs a, int tiles_per_w
   const int t = query - b * a.Tq;
   const int64_t tpos = a.q_pos0[b] + t;
   const int n_ent = a.n_entries[b];
+  if constexpr (FRESH) {
+    const int jx = (int)blockIdx.x - ((int)gridDim.x - f.n_jobs);
+    if (jx >= 0) {
+      const int row = min(n_ent, a.N_cap) - 1;
+      if (t == 0 && row >= 0)
+        fresh_entry(a, f.job[jx], b, row, jx == 0, reinterpret_cast<float*>(sq), sw);
+      return;
+    }
+  }
   const int chunk_tiles = 4 * tiles_per_wave;
   const int tile0 = blockIdx.x * chunk_tiles;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -134,7 +279,10 @@ __global__ __launch_bounds__(256) void index_decode(IndexArgs a, int tiles_per_w
 #pragma unroll
   for (int u = 0; u < 4; ++u) reinterpret_cast<uint4*>(sq)[threadIdx.x + 256 * u] = v[u];
   reinterpret_cast<f32x4_t*>(sw)[threadIdx.x] = wq;
-  const int n_vis = visible_entries(tpos, a.m, min(n_ent, a.N_cap));
+  // with fresh entries the last one is scored by its compressing workgroup
+  const int n_vis = FRESH ? max(min(visible_entries(tpos, a.m, min(n_ent, a.N_cap)),
+                                    min(n_ent, a.N_cap) - 1), 0)
+                          : visible_entries(tpos, a.m, min(n_ent, a.N_cap));
   __syncthreads();
   bf16x8_t qa[2][8];
   load_query_operand(sq, lane, qa);
@@ -253,7 +401,7 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream) {
       tpw = max(1, min(tpw, 32));
       const int chunk = 4 * tpw * 32;
       dim3 grid((a.N_cap + chunk - 1) / chunk, queries);
-      hipLaunchKernelGGL(index_decode, grid, dim3(256), 0, stream, a, tpw);
+      hipLaunchKernelGGL(index_decode<false>, grid, dim3(256), 0, stream, a, tpw, FreshJobs{});
     }
     return hipGetLastError();
   }
@@ -263,6 +411,33 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(index_generic<bf16_t>, grid, dim3(256), lds, stream, a);
   else
     hipLaunchKernelGGL(index_generic<float>, grid, dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace csa
+
+namespace csa {
+
+bool index_fresh_fused(const IndexArgs& a, const FreshJobs& f) {
+  if (!index_uses_mfma(a) || a.Tq >= 8 || f.n_jobs < 1 || f.n_jobs > 2) return false;
+  if (f.job[0].D != a.Di) return false;
+  for (int k = 0; k < f.n_jobs; ++k) {
+    const CompressArgs& j = f.job[k];
+    const int rows = j.m * ((j.overlap && j.prev_c_b) ? 2 : 1);
+    if (j.dt != 1 || j.T != j.m || j.D > 512 || (j.D & 1) || rows > kFreshMaxRows) return false;
+  }
+  return true;
+}
+
+hipError_t launch_index_fresh(const IndexArgs& a, const FreshJobs& f, hipStream_t stream) {
+  const int queries = a.B * a.Tq;
+  if (queries == 0) return hipSuccess;
+  const int64_t keys = (int64_t)queries * a.N_cap;
+  int tpw = (int)((keys + 1536LL * 128 - 1) / (1536LL * 128));
+  tpw = max(1, min(tpw, 32));
+  const int chunk = 4 * tpw * 32;
+  dim3 grid((a.N_cap + chunk - 1) / chunk + f.n_jobs, queries);
+  hipLaunchKernelGGL(index_decode<true>, grid, dim3(256), 0, stream, a, tpw, f);
   return hipGetLastError();
 }
 

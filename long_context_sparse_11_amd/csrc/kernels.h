@@ -24,6 +24,10 @@ struct CompressArgs {
   int slices;           // channel slices per entry (set by the launcher)
   float* ws_y;          // [B, n_out, D] f32 pooled values when slices > 1 with a gain
   size_t ws_bytes;
+  // when set (one entry per sequence): sequence b's entry goes to row
+  // min(rows_at[b], rows_cap) - 1 of out (none when that is negative)
+  const int32_t* rows_at;
+  int rows_cap;
 };
 // Workspace the compressor uses for a call of this shape (0 = none); rows:
 // rows pooled per entry (m, or 2m with overlap).
@@ -47,6 +51,18 @@ struct IndexArgs {
 // True when the MFMA kernels cover this shape (bf16, 64 heads x 128).
 bool index_uses_mfma(const IndexArgs& a);
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
+// Decode step with fresh entries: the compressor jobs (bf16, one closing
+// block per sequence, T = m) run in extra workgroups of the indexer launch
+// and write row min(n_entries[b], N_cap) - 1 of their pools; job 0 is the
+// indexer-key compressor, whose fresh entry those workgroups also score.
+struct FreshJobs {
+  CompressArgs job[2];
+  int n_jobs;
+};
+// True when launch_index_fresh covers this shape (otherwise the compressors
+// and the indexer run as separate launches).
+bool index_fresh_fused(const IndexArgs& a, const FreshJobs& f);
+hipError_t launch_index_fresh(const IndexArgs& a, const FreshJobs& f, hipStream_t stream);
 
 // --------------------------------------------------------------------- top-k
 // Largest score row that one workgroup selects from in LDS.

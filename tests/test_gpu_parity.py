@@ -282,6 +282,129 @@ def test_index_nothing_visible():
     assert np.all(gidx == -1) and np.all(np.isneginf(gsc))
 
 
+def _fresh_case(dt, N, Tq, n_ent, key_norm_rope, seed):
+    """Inputs of a decode step whose last query closes a block: the closing
+    block's streams for the indexer-key and KV compressors, pools holding the
+    older entries, queries at positions m n - Tq .. m n - 1."""
+    rng = np.random.default_rng(seed)
+    B = len(n_ent)
+    Hi, Di, D, R, m = (64, 128, 512, 64, 4) if dt == "bf16" else (4, 32, 64, 16, 4)
+    f = lambda *sh: rng.standard_normal(sh).astype(np.float32)
+    T = lambda x: synth.Tensor(x, dt)
+    d = dict(B=B, Hi=Hi, Di=Di, D=D, R=R, m=m, q=T(f(B, Tq, Hi, Di)),
+             w=(0.02 * f(B, Tq, Hi)) if dt == "bf16" else np.abs(f(B, Tq, Hi)),
+             k_idx=T(f(B, N, Di)), pool=T(f(B, N, D)), n_ent=np.asarray(n_ent, np.int32))
+    d["q_pos0"] = m * d["n_ent"].astype(np.int64) - Tq
+    d["block_pos0"] = m * (d["n_ent"].astype(np.int64) - 1)
+    for pre, width in (("k", Di), ("v", D)):
+        for n in ("c_a", "z_a", "c_b", "z_b", "prev_c_b", "prev_z_b"):
+            d[pre + n] = T(f(B, m, width))
+        d[pre + "bias_a"], d[pre + "bias_b"] = 0.02 * f(m, width), 0.02 * f(m, width)
+        d[pre + "gain"] = (1.0 + 0.02 * f(width)).astype(np.float32)
+    d["key_extra"] = dict(gain=d["kgain"], rope_dims=Di // 4) if key_norm_rope else {}
+    return d
+
+
+def _fresh_jobs_and_refs(d, kidx, pool):
+    m = d["m"]
+    jobs, refs = [], []
+    for pre, out, extra in (("k", kidx, d["key_extra"]),
+                            ("v", pool, dict(gain=d["vgain"], rope_dims=d["R"]))):
+        streams = {n: dev(d[pre + n]) for n in ("z_a", "c_b", "z_b", "prev_c_b", "prev_z_b")}
+        kw = dict(bias_a=dev(d[pre + "bias_a"]), bias_b=dev(d[pre + "bias_b"]),
+                  **{k: (dev(v) if isinstance(v, np.ndarray) else v) for k, v in extra.items()})
+        jobs.append(dict(c_a=dev(d[pre + "c_a"]), out=out, **streams, **kw))
+        refs.append(O.csa_compress(d[pre + "c_a"].f32, d[pre + "z_a"].f32, d[pre + "bias_a"], m,
+                                   c_b=d[pre + "c_b"].f32, z_b=d[pre + "z_b"].f32,
+                                   bias_b=d[pre + "bias_b"], prev_c_b=d[pre + "prev_c_b"].f32,
+                                   prev_z_b=d[pre + "prev_z_b"].f32, pos0=d["block_pos0"],
+                                   **extra)[:, 0])
+    return jobs, refs
+
+
+@pytest.mark.parametrize("dt,N,Tq,n_ent,key_norm_rope", [
+    ("bf16", 2000, 1, [2000, 1995], False), ("bf16", 20000, 3, [20000, 20000, 7000], True),
+    ("bf16", 700, 1, [700, 0], False), ("f32", 50, 2, [50, 13], True)])
+def test_decode_index_topk_fused(dt, N, Tq, n_ent, key_norm_rope):
+    """The decode step's compressors and indexer in one call: the closing
+    block's key and KV entries land in row n_entries-1 of their pools (the
+    rest untouched), match the oracle's compressor, and the selection is the
+    indexer top-K over all entries, the fresh one scored from its stored key.
+    bf16 runs the compressors inside the indexer launch; f32 (toy sizes)
+    runs them as a launch of their own."""
+    d = _fresh_case(dt, N, Tq, n_ent, key_norm_rope, seed=N + Tq)
+    B, m, K = d["B"], d["m"], (512 if dt == "bf16" else 8)
+    kidx, pool = dev(d["k_idx"]), dev(d["pool"])
+    k0, p0 = kidx.clone(), pool.clone()
+    jobs, (kref, vref) = _fresh_jobs_and_refs(d, kidx, pool)
+    gidx, gsc, gall = L.csa_decode_index_topk(
+        dev(d["q"]), dev(d["w"]), i32(d["n_ent"]), i64(d["q_pos0"]), K, m, jobs,
+        block_pos0=i64(d["block_pos0"]), want_scores=True, want_all_scores=True)
+    gidx, gsc, gall = host(gidx).astype(np.int64), host(gsc), host(gall)
+    tol = TOL_BF16 if dt == "bf16" else TOL_F32
+    # the oracle ranks the stored older keys plus its own fresh key, stored
+    # at the pool's precision
+    kin = d["k_idx"].f32.copy()
+    for b in range(B):
+        r = int(d["n_ent"][b]) - 1
+        for got, before, ref in ((kidx, k0, kref), (pool, p0, vref)):
+            if r >= 0:
+                assert rowwise_rel_err(host(got[b, r])[None], ref[b][None]) <= tol, b
+            keep = [i for i in range(N) if i != r]
+            assert torch.equal(got[b, keep], before[b, keep]), b
+        if r >= 0:
+            kin[b, r] = synth.Tensor(kref[b].astype(np.float32), dt).f32
+    _, rsc = O.csa_index_topk(d["q"].f32, d["w"], kin, d["n_ent"], d["q_pos0"], K, m)
+    qf = d["q"].f32
+    for b in range(B):
+        r = int(d["n_ent"][b]) - 1
+        for t in range(Tq):
+            nv = O.visible_count(d["q_pos0"][b] + t, m, d["n_ent"][b])
+            old = [i for i in range(nv) if i != r]
+            if old:
+                atol = SCORE_ATOL_BF16 if dt == "bf16" else 5e-4
+                assert np.abs(gall[b, t, old] - rsc[b, t, old]).max() <= atol, (b, t)
+            if 0 <= r < nv:
+                # the fresh key differs from the oracle's by at most tol of
+                # its largest element per channel; bound the score change
+                dk = tol * np.abs(kref[b]).max() * math.sqrt(d["Di"]) * 2
+                bound = float(np.sum(np.abs(d["w"][b, t]) * np.linalg.norm(qf[b, t], axis=1))) * dk
+                assert abs(gall[b, t, r] - rsc[b, t, r]) <= bound + 1e-3, (b, t)
+            want = O.select_topk(gall[b, t, :nv], nv, K)
+            assert np.array_equal(gidx[b, t], want), (b, t)
+            sel = gidx[b, t]
+            assert np.array_equal(gsc[b, t][sel >= 0], gall[b, t][sel[sel >= 0]])
+
+
+def test_decode_index_topk_matches_separate_calls():
+    """Fused and separate (compress batch into row N-1, then index + top-K)
+    give the same pools bitwise and the same selection from scores that
+    agree to float32 rounding."""
+    d = _fresh_case("bf16", 3000, 1, [3000, 3000], False, seed=9)
+    m, K, N = d["m"], 512, 3000
+    kidx, pool = dev(d["k_idx"]), dev(d["pool"])
+    jobs, _ = _fresh_jobs_and_refs(d, kidx, pool)
+    gidx, _, gall = L.csa_decode_index_topk(
+        dev(d["q"]), dev(d["w"]), i32(d["n_ent"]), i64(d["q_pos0"]), K, m, jobs,
+        block_pos0=i64(d["block_pos0"]), want_all_scores=True)
+    kidx2, pool2 = dev(d["k_idx"]), dev(d["pool"])
+    jobs2, _ = _fresh_jobs_and_refs(d, kidx2[:, N - 1:], pool2[:, N - 1:])
+    for j, full in zip(jobs2, (kidx2, pool2)):
+        j["out_bstride"] = full.stride(0)
+    L.csa_compress_batch(jobs2, m, pos0=i64(d["block_pos0"]))
+    idx2, _, all2 = L.csa_index_topk(dev(d["q"]), dev(d["w"]), kidx2, i32(d["n_ent"]),
+                                     i64(d["q_pos0"]), K, m, want_all_scores=True)
+    assert rowwise_rel_err(host(kidx[:, N - 1]), host(kidx2[:, N - 1])) <= 1e-2
+    assert rowwise_rel_err(host(pool[:, N - 1]), host(pool2[:, N - 1])) <= 1e-2
+    assert torch.equal(kidx[:, : N - 1], kidx2[:, : N - 1])
+    # older entries: the same kernel on the same keys; the fresh one: its key
+    # may differ by a bf16 rounding step, and it is scored on another path
+    assert np.array_equal(host(gall)[:, :, : N - 1], host(all2)[:, :, : N - 1])
+    assert np.abs(host(gall)[:, :, N - 1] - host(all2)[:, :, N - 1]).max() <= 1e-2
+    for b in range(2):
+        check_band(host(gidx)[b, 0], host(idx2)[b, 0], host(all2)[b, 0], N, K, band=2e-3)
+
+
 def test_index_p4_sentinel_example():
     """The transformers page's 16-token CSA example (m = 4, index_topk = 2):
     queries before the first closed window get only -1, then slots fill."""

@@ -31,7 +31,7 @@ def lib():
 def test_header_declares_the_four_calls():
     names = declared_functions()
     for n in ("csa_compress", "csa_compress_batch", "csa_index_topk", "csa_index_scores",
-              "csa_sparse_attn", "hca_attn",
+              "csa_decode_index_topk", "csa_sparse_attn", "hca_attn",
               "csa_compress_ws_bytes", "csa_index_topk_ws_bytes", "csa_attn_ws_bytes",
               "csa_status_string"):
         assert n in names
@@ -124,6 +124,26 @@ def test_compress_batch_validation(lib):
     assert call([_job(), _job(c_b=None)]) == CSA_ERR_ARG                        # overlap, no b
     assert call([_job(rope_dims=64)]) == CSA_ERR_ARG                            # rope, no positions
     assert call([_job(), _job(D=128)], B=0) == CSA_OK                           # nothing to do
+
+
+def test_decode_index_topk_validation(lib):
+    from long_context_sparse_11_amd.binding import CompressJob
+    def call(jobs, n=None, B=2, Tq=1, Di=128, N_cap=64, m=4, ws=P, wsb=1 << 30):
+        arr = (CompressJob * max(len(jobs), 1))(*jobs)
+        return lib.csa_decode_index_topk(1, B, Tq, 64, Di, N_cap, 16, m, 1, N,
+                                         ctypes.cast(arr, ctypes.c_void_p),
+                                         len(jobs) if n is None else n, P, P, P, P, P, N, N,
+                                         ws, wsb, N)
+    key, kv = _job(D=128), _job(D=512, out_bstride=64 * 512)
+    assert call([key, kv], n=3) == CSA_ERR_ARG
+    assert call([key], n=0) == CSA_ERR_ARG
+    assert call([kv, key]) == CSA_ERR_ARG                       # jobs[0] is the key job
+    assert call([key, _job(D=512, out_bstride=100)]) == CSA_ERR_ARG   # not the pool stride
+    assert call([key, kv], N_cap=0) == CSA_ERR_ARG              # no row for the fresh entry
+    assert call([key, _job(D=512, c_b=None)]) == CSA_ERR_ARG    # overlap, no stream b
+    assert call([key, _job(D=512, rope_dims=64)]) == CSA_ERR_ARG   # rope, no positions
+    assert call([key, kv], ws=N, wsb=0) == CSA_ERR_WORKSPACE
+    assert call([key, kv], B=0) == CSA_OK                       # nothing to do
 
 
 def test_compress_job_layout_matches_c():
