@@ -130,6 +130,25 @@ __device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressAr
   }
   const float2 gn = j.gain ? *reinterpret_cast<const float2*>(j.gain + cc) : make_float2(1.f, 1.f);
   const int64_t pos = j.pos0 ? j.pos0[b] : 0;
+  // scoring (indexer-key job): thread (h = tid / 4, quarter qq = tid % 4)
+  // takes head h over channels 32 qq .. 32 qq + 31; the first query's slice
+  // and weight are requested with the rows
+  const int h = tid >> 2, qq = tid & 3;
+  auto qslice = [&](int query, uint4 (&qv)[4]) {
+    const uint4* qp = reinterpret_cast<const uint4*>((const bf16_t*)a.q +
+                                                     ((int64_t)query * 64 + h) * 128 + 32 * qq);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) qv[u] = qp[u];
+  };
+  uint4 qv0[4];
+  float wh0 = 0.f;
+  if (score) {
+    qslice(b * a.Tq, qv0);
+    wh0 = a.w[(int64_t)b * a.Tq * 64 + h];
+  }
+  // the sequence's entry count and first query position, requested early too
+  const int n_ent = min(a.n_entries[b], a.N_cap);
+  const int64_t qpos = a.q_pos0[b];
 
   auto logit = [&](int r, int e) {  // base-2 logit of row r, channel c0 + e
     const bool in_a = r < m;
@@ -181,25 +200,25 @@ __device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressAr
   if (!score) return;
 
   // Score the stored entry for every query t of the sequence that sees it:
-  // thread (h = tid / 4, quarter qq = tid % 4) takes head h over channels
-  // 32 qq .. 32 qq + 31, the 4 quarters meet by lane swaps, the 64 heads by a
-  // wave sum and the 4 waves through LDS.
+  // the 4 quarters of a head meet by lane swaps, the 64 heads by a wave sum
+  // and the 4 waves through LDS.
   if (act) {
     skey[c0] = bf16_to_f32(packed & 0xffffu);
     skey[c0 + 1] = bf16_to_f32(packed >> 16);
   }
   __syncthreads();
-  const int h = tid >> 2, qq = tid & 3;
-  const int n_ent = min(a.n_entries[b], a.N_cap);
   for (int t = 0; t < a.Tq; ++t) {
     const int query = b * a.Tq + t;
-    if (row >= visible_entries(a.q_pos0[b] + t, a.m, n_ent)) continue;
-    const uint4* qp = reinterpret_cast<const uint4*>((const bf16_t*)a.q +
-                                                     ((int64_t)query * 64 + h) * 128 + 32 * qq);
+    if (row >= visible_entries(qpos + t, a.m, n_ent)) continue;
     uint4 qv[4];
+    float wh = wh0;
+    if (t == 0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) qv[u] = qp[u];
-    const float wh = a.w[(int64_t)query * 64 + h];
+      for (int u = 0; u < 4; ++u) qv[u] = qv0[u];
+    } else {
+      qslice(query, qv);
+      wh = a.w[(int64_t)query * 64 + h];
+    }
     float dot = 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -222,33 +241,42 @@ __device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressAr
 }
 
 // ------------------------------------------------------------------- decode
-// grid (chunks, B*Tq); 4 waves; chunk = 4 * tiles_per_wave tiles of 32 keys,
-// tiles interleaved over the waves so the WG reads one contiguous range.
-// FRESH: the last f.n_jobs columns of the grid compress the closing block
-// (fresh_entry, query t = 0 of each sequence) and the other workgroups score
-// the entries stored before it.
-template <bool FRESH>
-__global__ __launch_bounds__(256) void index_decode(IndexArgs a, int tiles_per_wave, FreshJobs f) {
+// 1-D grid: [fresh workgroups,] then chunks x (B*Tq) scoring workgroups, 4
+// waves each; chunk = 4 * tiles_per_wave tiles of 32 keys, tiles
+// interleaved over the waves so the WG reads one contiguous range.
+// FRESH: the first n_jobs * B workgroups (dispatched first) compress the
+// closing block of sequence x % B for job x / B (fresh_entry); the scoring
+// workgroups score the entries stored before it.
+// ONE: one tile per wave (tiles_per_wave == 1): a single key buffer, so the
+// kernel fits three waves per SIMD (3 workgroups per CU) and a grid of up
+// to 768 workgroups, fresh ones included, runs in one round.
+template <bool FRESH, bool ONE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONE ? 3 : 1, 8)))
+void index_decode(IndexArgs a, int tiles_per_wave, int chunks, FreshJobs f) {
   __shared__ __attribute__((aligned(16))) bf16_t sq[64 * 128];
   // head weights: thread i stores a copy of weights 4(i%16) .. +3 in slot i
   // (a store in every thread: a branch around it would drag its load along)
   __shared__ __attribute__((aligned(16))) float sw[256 * 4];
-  const int query = blockIdx.y;
+  int id = blockIdx.x;
+  if constexpr (FRESH) {
+    const int fj = f.n_jobs * a.B;
+    if (id < fj) {
+      const int fb = id % a.B;
+      const int row = min(a.n_entries[fb], a.N_cap) - 1;
+      if (row >= 0)
+        fresh_entry(a, f.job[id / a.B], fb, row, id < a.B, reinterpret_cast<float*>(sq), sw);
+      return;
+    }
+    id -= fj;
+  }
+  const int query = id / chunks;
+  const int cx = id - query * chunks;  // chunk of this scoring workgroup
   const int b = query / a.Tq;
   const int t = query - b * a.Tq;
   const int64_t tpos = a.q_pos0[b] + t;
   const int n_ent = a.n_entries[b];
-  if constexpr (FRESH) {
-    const int jx = (int)blockIdx.x - ((int)gridDim.x - f.n_jobs);
-    if (jx >= 0) {
-      const int row = min(n_ent, a.N_cap) - 1;
-      if (t == 0 && row >= 0)
-        fresh_entry(a, f.job[jx], b, row, jx == 0, reinterpret_cast<float*>(sq), sw);
-      return;
-    }
-  }
   const int chunk_tiles = 4 * tiles_per_wave;
-  const int tile0 = blockIdx.x * chunk_tiles;
+  const int tile0 = cx * chunk_tiles;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 31, g = lane >> 5;
   const bf16_t* kbase = (const bf16_t*)a.k + (int64_t)b * a.N_cap * 128 + g * 64;
@@ -273,7 +301,7 @@ __global__ __launch_bounds__(256) void index_decode(IndexArgs a, int tiles_per_w
 #pragma unroll
   for (int u = 0; u < 4; ++u) v[u] = qg[threadIdx.x + 256 * u];
   const f32x4_t wq = reinterpret_cast<const f32x4_t*>(a.w + (int64_t)query * 64)[threadIdx.x & 15];
-  bf16x8_t k0[8], k1[8];
+  bf16x8_t k0[8];
   int tile = tile0 + wave;
   load(tile, k0);
 #pragma unroll
@@ -295,8 +323,13 @@ __global__ __launch_bounds__(256) void index_decode(IndexArgs a, int tiles_per_w
     const int key = tl * 32 + j;
     if (g == 0 && key < n_vis) out[key] = sc;
   };
+  if constexpr (ONE) {
+    if (tile < tile_end) score(tile, k0);
+    return;
+  }
   // two key buffers in turn: the next tile's loads are in flight while the
   // current tile is scored, with no register copy between them
+  bf16x8_t k1[8];
   while (tile < tile_end) {
     const int t1 = tile + 4;
     if (t1 < tile_end) load(t1, k1);
@@ -400,8 +433,12 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream) {
       int tpw = (int)((keys + 1536LL * 128 - 1) / (1536LL * 128));
       tpw = max(1, min(tpw, 32));
       const int chunk = 4 * tpw * 32;
-      dim3 grid((a.N_cap + chunk - 1) / chunk, queries);
-      hipLaunchKernelGGL(index_decode<false>, grid, dim3(256), 0, stream, a, tpw, FreshJobs{});
+      const int chunks = (a.N_cap + chunk - 1) / chunk;
+      dim3 grid(chunks * queries);
+      if (tpw == 1)
+        hipLaunchKernelGGL((index_decode<false, true>), grid, dim3(256), 0, stream, a, tpw, chunks, FreshJobs{});
+      else
+        hipLaunchKernelGGL((index_decode<false, false>), grid, dim3(256), 0, stream, a, tpw, chunks, FreshJobs{});
     }
     return hipGetLastError();
   }
@@ -436,8 +473,12 @@ hipError_t launch_index_fresh(const IndexArgs& a, const FreshJobs& f, hipStream_
   int tpw = (int)((keys + 1536LL * 128 - 1) / (1536LL * 128));
   tpw = max(1, min(tpw, 32));
   const int chunk = 4 * tpw * 32;
-  dim3 grid((a.N_cap + chunk - 1) / chunk + f.n_jobs, queries);
-  hipLaunchKernelGGL(index_decode<true>, grid, dim3(256), 0, stream, a, tpw, f);
+  const int chunks = (a.N_cap + chunk - 1) / chunk;
+  dim3 grid(chunks * queries + f.n_jobs * a.B);
+  if (tpw == 1)
+    hipLaunchKernelGGL((index_decode<true, true>), grid, dim3(256), 0, stream, a, tpw, chunks, f);
+  else
+    hipLaunchKernelGGL((index_decode<true, false>), grid, dim3(256), 0, stream, a, tpw, chunks, f);
   return hipGetLastError();
 }
 
