@@ -250,7 +250,7 @@ def algorithmic(kind, d):
 # measured HBM traffic of the dominant kernel (hardware counters, committed)
 # ---------------------------------------------------------------------------
 DOMINANT_KERNELS = {
-    "index_scores": ["index_decode<false> (decode) / index_prefill (prefill)"],
+    "index_scores": ["index_decode<false, *> (decode) / index_prefill (prefill)"],
     "hca_attn": ["attn_hs<false, true, 4>", "attn_combine<bf16>"],
 }
 KERNEL_SOURCES = {

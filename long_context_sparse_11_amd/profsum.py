@@ -42,7 +42,7 @@ CAL_KERNEL = "bitwise_not"
 UNIT_KERNELS = {
     # decode: the scoring kernel as the bench times it (csa_index_scores); the
     # step runs its variant with the fresh-entry workgroups, index_decode<true>
-    "index_scores": {"decode": ["index_decode<false>"], "prefill": ["index_prefill"]},
+    "index_scores": {"decode": ["index_decode<false,"], "prefill": ["index_prefill"]},
     "hca_attn": {"decode": ["attn_hs<false, true, 4>", "attn_combine"]},
 }
 WORKLOAD_NAME = {"csa64k": "csa_decode_64k", "csa1m": "csa_decode_1m",
