@@ -47,7 +47,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="csa64k", choices=["csa64k", "csa1m", "hca1m", "prefill"])
+    p.add_argument("--workload", default="csa64k",
+                   choices=["csa64k", "csa1m", "hca1m", "prefill", "csa64k_pro"])
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
     p.add_argument("--no-cpu", action="store_true")
@@ -76,26 +77,26 @@ class Step:
         self._cws = {}
         B, D, m = g["B"], g["D"], g["m"]
         self.B = B
-        if kind in ("csa64k", "csa1m"):
+        if kind in ("csa64k", "csa1m", "csa64k_pro"):
             N, K, W = g["N"], g["K"], g["W"]
             self.idx = torch.empty((B, 1, K), dtype=torch.int32, device="cuda")
             self.out = torch.empty_like(g["q"])
-            self.ws_i = torch.empty(L.csa_index_topk_ws_bytes(B, 1, 64, N, K), dtype=torch.uint8,
-                                    device="cuda")
-            n = L.csa_attn_ws_bytes(B, 1, 64, D, K + W)
+            self.ws_i = torch.empty(L.csa_index_topk_ws_bytes(B, 1, g["Hi"], N, K),
+                                    dtype=torch.uint8, device="cuda")
+            n = L.csa_attn_ws_bytes(B, 1, g["H"], D, K + W)
             self.ws_a = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
         elif kind == "hca1m":
             N, W = g["N"], g["W"]
             self.out = torch.empty_like(g["q"])
-            n = L.csa_attn_ws_bytes(B, 1, 64, D, N + W)
+            n = L.csa_attn_ws_bytes(B, 1, g["H"], D, N + W)
             self.ws_a = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
         else:  # prefill
             Tq, N, K, W = g["Tq"], g["N"], g["K"], g["W"]
             self.idx = torch.empty((1, Tq, K), dtype=torch.int32, device="cuda")
             self.out = torch.empty_like(g["q"])
-            self.ws_i = torch.empty(L.csa_index_topk_ws_bytes(1, Tq, 64, N, K), dtype=torch.uint8,
+            self.ws_i = torch.empty(L.csa_index_topk_ws_bytes(1, Tq, g["Hi"], N, K), dtype=torch.uint8,
                                     device="cuda")
-            n = L.csa_attn_ws_bytes(1, Tq, 64, D, K + W)
+            n = L.csa_attn_ws_bytes(1, Tq, g["H"], D, K + W)
             self.ws_a = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
 
     def cws(self, c, m, overlap=True):
@@ -125,7 +126,7 @@ class Step:
         """The step as a list of (name, thunk) library calls."""
         g, L = self.g, self.L
         kind = self.kind
-        if kind in ("csa64k", "csa1m"):
+        if kind in ("csa64k", "csa1m", "csa64k_pro"):
             N, D, Di, m = g["N"], g["D"], g["Di"], g["m"]
             pool, kidx = g["pool"], g["k_idx"]
             return [
@@ -211,7 +212,7 @@ def algorithmic(kind, d):
     B, Tq = d["B"], d["Tq"]
     bf = 2
     out = {}
-    if kind in ("csa64k", "csa1m"):
+    if kind in ("csa64k", "csa1m", "csa64k_pro"):
         N = d["N"]
         comp = B * ((4 * m) * D * bf + D * bf + (4 * m) * Di * bf + Di * bf)
         idx_bytes = B * (N * Di * bf + Hi * Di * bf + Hi * 4 + K * 4)
@@ -514,13 +515,15 @@ def main():
 
     cfgs = {
         "csa64k": dict(workload="csa_decode_64k", batch=4, context=65536, entries=16384),
+        "csa64k_pro": dict(workload="csa_decode_64k_v4pro", batch=4, context=65536,
+                           entries=16384),
         "csa1m": dict(workload="csa_decode_1m", batch=8, context=1048576, entries=262144),
         "hca1m": dict(workload="hca_decode_1m", batch=16, context=1048576, entries=8192),
         "prefill": dict(workload="csa_prefill_4k_on_60k", batch=1, queries=4096, context=65536,
                         entries=16384),
     }[kind]
-    cfgs.update(heads=64, head_dim=512, rope_dims=64, index_heads=64, index_dim=128,
-                index_topk=512, window=128, m=d["m"], step_calls=names,
+    cfgs.update(heads=d["H"], head_dim=d["D"], rope_dims=d["R"], index_heads=d["Hi"],
+                index_dim=d["Di"], index_topk=d["K"], window=d["W"], m=d["m"], step_calls=names,
                 graph=use_graph, steps_per_graph=per_graph, input_copies=n_copies)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,

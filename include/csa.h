@@ -252,7 +252,8 @@ int csa_index_scores(int dt, int B, int Tq, int Hi, int Di, int N_cap, int m,
  *   out     [B, Tq, H, D] dt;  lse [B, Tq, H] f32 natural log (may be NULL)
  *   ws      workspace of csa_attn_ws_bytes(B, Tq, H, D, K + W)
  * Supported: D <= 1024, H <= 128, rope_dims even and <= D; in bf16 with
- * H = 64, D = 512, K + W <= 524288 (else CSA_ERR_UNSUPPORTED).
+ * H = 64 or 128 (Flash, Pro) and D = 512 (the MFMA path), K + W <= 524288
+ * (else CSA_ERR_UNSUPPORTED).
  * ------------------------------------------------------------------------- */
 int csa_sparse_attn(int dt, int B, int Tq, int H, int D, int rope_dims, double rope_base,
                     float scale, const void* q, const void* pool, int N_cap,

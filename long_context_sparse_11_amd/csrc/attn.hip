@@ -157,7 +157,8 @@ __global__ __launch_bounds__(256) void attn_generic(AttnArgs a) {
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr;
 constexpr int kAtD = 512;
-constexpr int kAtH = 64;
+constexpr int kAtH = 64;      // heads per workgroup (NW = 4)
+constexpr int kMaxAtH = 128;  // H: a multiple of kAtH up to this (Flash 64, Pro 128)
 
 // Value of lane (l ^ 32): the two halves of the wave swap through
 // v_permlane32_swap (a VALU move; no LDS round trip).
@@ -262,7 +263,7 @@ void attn_hs(AttnArgs a) {
   const int32_t idx0 = idx_q[has_idx ? min(max(start + (lane & 31), 0), a.K - 1) : 0];
 
   // the lane's query slice: head h, channels 32 ks + 8G .. +7
-  const bf16_t* qrow = (const bf16_t*)a.q + ((int64_t)qi * kAtH + h) * kAtD;
+  const bf16_t* qrow = (const bf16_t*)a.q + ((int64_t)qi * a.H + h) * kAtD;
   bf16x8_t qb[16];
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) qb[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * ks + 8 * G);
@@ -277,7 +278,7 @@ void attn_hs(AttnArgs a) {
   }
   const bf16_t* pool_b = (const bf16_t*)a.pool + (int64_t)b * a.N_cap * kAtD;
   const bf16_t* win_b = (const bf16_t*)a.win + ((int64_t)b * a.L_win + kr.win_r0) * kAtD;
-  const bf16_t* dummy = (const bf16_t*)a.q + (int64_t)qi * kAtH * kAtD;  // 1 KiB always readable
+  const bf16_t* dummy = (const bf16_t*)a.q + (int64_t)qi * a.H * kAtD;  // 1 KiB always readable
 
   // A tile's 32 rows reach LDS in two steps.  resolve_tile: lane l (< 32)
   // turns row j0 + l (sidx_l: its selected index) into a source address with
@@ -506,8 +507,8 @@ void attn_hs(AttnArgs a) {
     const float mf = fmaxf(mrun, skl2);
     const float lf = lrun * exp2f(mrun - mf) + exp2f(skl2 - mf);
     const float fac = exp2f(mrun - mf) / lf;
-    if (G == 0 && a.lse) a.lse[(int64_t)qi * kAtH + h] = (mf + log2f(lf)) * kLn2;
-    bf16_t* op = (bf16_t*)a.out + ((int64_t)qi * kAtH + h) * kAtD;
+    if (G == 0 && a.lse) a.lse[(int64_t)qi * a.H + h] = (mf + log2f(lf)) * kLn2;
+    bf16_t* op = (bf16_t*)a.out + ((int64_t)qi * a.H + h) * kAtD;
 #pragma unroll
     for (int cb = 0; cb < 32; ++cb) {
       float o[4];
@@ -532,7 +533,7 @@ void attn_hs(AttnArgs a) {
       *reinterpret_cast<uint2*>(op + c) = pk;
     }
   } else {
-    const int64_t slot = ((int64_t)qi * S + sp) * kAtH + h;
+    const int64_t slot = ((int64_t)qi * S + sp) * a.H + h;
     if (G == 0) {
       a.part_ml[2 * slot] = mrun;
       a.part_ml[2 * slot + 1] = lrun;
@@ -628,12 +629,13 @@ __global__ __launch_bounds__(128) void attn_combine(AttnArgs a) {
 
 // ------------------------------------------------------------------- launch
 bool attn_uses_mfma(int dt, int H, int D, int R) {
-  return dt == 1 && H == kAtH && D == kAtD && R % 2 == 0 && R <= D;
+  return dt == 1 && H % kAtH == 0 && H <= kMaxAtH && D == kAtD && R % 2 == 0 && R <= D;
 }
 
 int attn_splits(int dt, int B, int Tq, int H, int D, int keys_per_query) {
-  if (!(dt == 1 && H == kAtH && D == kAtD)) return 1;
-  const int64_t q = (int64_t)B * Tq;
+  if (!(dt == 1 && H % kAtH == 0 && H <= kMaxAtH && D == kAtD)) return 1;
+  // a query of H heads is H / 64 workgroups per split
+  const int64_t q = (int64_t)B * Tq * (H / kAtH);
   const int tiles = (keys_per_query + kHsRows - 1) / kHsRows;
   // few queries: spread each one's tiles over splits until there are about
   // as many workgroups as compute units (one tile per split at most)
@@ -669,15 +671,16 @@ static hipError_t launch_generic(const AttnArgs& a, hipStream_t stream) {
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.B * a.Tq == 0) return hipSuccess;
   if (attn_uses_mfma(a.dt, a.H, a.D, a.R)) {
-    dim3 grid(a.splits, a.B * a.Tq);
+    const int hg = a.H / kAtH;  // 64-head groups (grid z)
+    dim3 grid(a.splits, a.B * a.Tq, hg);
     // most rows a split can hold: the list length bound over the split count
     const int wc = (a.W > 0 && a.L_win > 0) ? min(a.W, a.L_win) : 0;
     const int64_t lmax = (a.csa ? (int64_t)a.K : (int64_t)a.N_cap) + wc;
     const bool multi = (lmax + a.splits - 1) / a.splits > kHsRows;
     // single-tile splits in head groups of 32 (two waves, grid z) while the
     // doubled grid still fits the compute units once
-    const bool halves = !multi && 2LL * a.splits * a.B * a.Tq <= kHsHeadSplitBelow;
-    dim3 grid2(a.splits, a.B * a.Tq, 2), block4(256), block2(128);
+    const bool halves = !multi && 2LL * hg * a.splits * a.B * a.Tq <= kHsHeadSplitBelow;
+    dim3 grid2(a.splits, a.B * a.Tq, 2 * hg), block4(256), block2(128);
     if (a.csa) {
       if (multi) hipLaunchKernelGGL((attn_hs<true, true, 4>), grid, block4, 0, stream, a);
       else if (halves) hipLaunchKernelGGL((attn_hs<true, false, 2>), grid2, block2, 0, stream, a);

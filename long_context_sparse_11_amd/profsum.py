@@ -46,7 +46,8 @@ UNIT_KERNELS = {
     "hca_attn": {"decode": ["attn_hs<false, true, 4>", "attn_combine"]},
 }
 WORKLOAD_NAME = {"csa64k": "csa_decode_64k", "csa1m": "csa_decode_1m",
-                 "hca1m": "hca_decode_1m", "prefill": "csa_prefill_4k_on_60k"}
+                 "hca1m": "hca_decode_1m", "prefill": "csa_prefill_4k_on_60k",
+                 "csa64k_pro": "csa_decode_64k_v4pro"}
 
 
 def bench_cmd(workload, steps):

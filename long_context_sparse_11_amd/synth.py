@@ -29,6 +29,10 @@ import zlib
 import numpy as np
 
 FLASH = dict(H=64, D=512, R=64, Hi=64, Di=128, K=512, W=128)
+# V4-Pro's attention and indexer ("DeepSeek-v4 Beyond Basics" section 3.2.2:
+# m = 4, 64 indexer heads x 128, top-k 1024; section 3.3: 128 query heads x
+# 512); RoPE and window as Flash (the page gives no other value)
+PRO = dict(H=128, D=512, R=64, Hi=64, Di=128, K=1024, W=128)
 
 
 # ---------------------------------------------------------------------------
@@ -137,6 +141,7 @@ def toy(seed: int = 0):
 
 DECODE = {  # m, batch, pool entries, heavy-tailed indexer keys
     "csa64k": (4, 4, 16384, False),
+    "csa64k_pro": (4, 4, 16384, False),
     "csa1m": (4, 8, 262144, True),
     "hca1m": (128, 16, 8192, False),
 }
@@ -145,7 +150,8 @@ DECODE = {  # m, batch, pool entries, heavy-tailed indexer keys
 def decode(kind: str, seed: int = 0, B: int | None = None, N: int | None = None,
            heavy_tail: bool | None = None, skip=()):
     """Decode-step inputs (one new query per sequence at the last position of
-    a context of N*m tokens) for 'csa64k', 'csa1m' or 'hca1m'.  ``B`` / ``N``
+    a context of N*m tokens) for 'csa64k', 'csa1m', 'hca1m' or 'csa64k_pro'
+    (V4-Pro shapes).  ``B`` / ``N``
     override batch and pool length for reduced-size cases; ``skip`` names
     arrays not to draw (e.g. the 2 GiB pool when only the indexer is tested).
 
@@ -154,7 +160,7 @@ def decode(kind: str, seed: int = 0, B: int | None = None, N: int | None = None,
     separately so a step can run the compressor too.
     """
     dr = _Draw(seed, kind)
-    F = FLASH
+    F = PRO if kind.endswith("_pro") else FLASH
     H, D, R, Hi, Di, K, W = F["H"], F["D"], F["R"], F["Hi"], F["Di"], F["K"], F["W"]
     m, B0, N0, ht = DECODE[kind]
     B = B0 if B is None else B

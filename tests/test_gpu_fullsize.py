@@ -2,7 +2,8 @@
 run through the C ABI with the same shapes (hence the same kernels, grids
 and key splits) as the benchmark's step, checked against the oracle.
 
-* CSA decode at 64K context (batch 4): every query, whole step.
+* CSA decode at 64K context (batch 4): every query, whole step; also in
+  V4-Pro's shapes (128 heads, top-1024), two sequences checked.
 * CSA decode at 1M context (batch 8, heavy-tailed indexer keys): the whole
   batch runs on the GPU; the oracle checks two sequences (its scores for a
   262,144-entry row are the expensive part).
@@ -94,7 +95,7 @@ def _csa_decode(kind, check_b):
                                            i64(d["q_pos0"]), K, m, jobs,
                                            block_pos0=i64(d["block_pos0"]), ws=ws_i,
                                            want_all_scores=True)
-    ws_a = torch.empty(max(L.csa_attn_ws_bytes(B, 1, 64, D, K + W), 1), dtype=torch.uint8,
+    ws_a = torch.empty(max(L.csa_attn_ws_bytes(B, 1, d["H"], D, K + W), 1), dtype=torch.uint8,
                        device="cuda")
     q, win, sink = dev(d["q"]), dev(d["win"]), dev(d["sink"])
     print(f"[{kind}] sparse_attn", flush=True)
@@ -167,6 +168,11 @@ def test_csa_decode_1m_sampled_sequences():
     _csa_decode("csa1m", check_b=[0, 5])
 
 
+def test_csa_decode_64k_v4pro_shapes():
+    """V4-Pro's attention and selection (128 heads, top-1024) at 64K."""
+    _csa_decode("csa64k_pro", check_b=[0, 3])
+
+
 # ---------------------------------------------------------------------------
 # HCA decode (1M)
 # ---------------------------------------------------------------------------
@@ -179,7 +185,7 @@ def test_hca_decode_1m_sampled_sequences():
     L.csa_compress(dev(d["c_a"]), m, z_a=dev(d["z_a"]), bias_a=dev(d["bias_a"]),
                    gain=dev(d["gain"]), rope_dims=R, pos0=i64(d["block_pos0"]),
                    out=pool[:, N - 1:], out_bstride=N * D)
-    ws_a = torch.empty(max(L.csa_attn_ws_bytes(B, 1, 64, D, N + W), 1), dtype=torch.uint8,
+    ws_a = torch.empty(max(L.csa_attn_ws_bytes(B, 1, d["H"], D, N + W), 1), dtype=torch.uint8,
                        device="cuda")
     out, lse = L.hca_attn(dev(d["q"]), pool, i32(d["n_entries"]), m, dev(d["win"]),
                           i64(d["win_pos0"]), W, dev(d["sink"]), i64(d["q_pos0"]), rope_dims=R,
@@ -268,7 +274,7 @@ def test_csa_prefill_sampled_queries():
 
     # attention with the oracle's index sets on the sampled queries
     print("[prefill] sparse_attn", flush=True)
-    ws_a = torch.empty(max(L.csa_attn_ws_bytes(1, Tq, 64, D, K + W), 1), dtype=torch.uint8,
+    ws_a = torch.empty(max(L.csa_attn_ws_bytes(1, Tq, d["H"], D, K + W), 1), dtype=torch.uint8,
                        device="cuda")
     out, lse = L.csa_sparse_attn(dev(d["q"]), pool, i32(ref_idx_all), dev(d["win"]),
                                  i64(d["win_pos0"]), W, dev(d["sink"]), i64(d["q_pos0"]),

@@ -495,6 +495,36 @@ def test_attn_csa_bf16(N, K, W, Tq, n_empty):
     assert np.abs(host(lse) - rl).max() <= LSE_ATOL_BF16
 
 
+@pytest.mark.parametrize("kind,N,K,Tq", [("csa", 3000, 1024, 1), ("csa", 700, 1024, 3),
+                                          ("hca", 3000, 0, 1), ("hca", 300, 0, 2)])
+def test_attn_128_heads_v4pro(kind, N, K, Tq):
+    """V4-Pro's attention shape (128 heads x 512, top-k 1024): two 64-head
+    groups per query on the MFMA path, splits and head groups as for Flash."""
+    rng = np.random.default_rng(N + Tq + K)
+    B, H, D, R, W, m = 2, 128, 512, 64, 128, 4
+    f = lambda *sh: rng.standard_normal(sh).astype(np.float32)
+    ctx = N * m
+    q_pos0 = np.array([ctx - Tq, ctx - Tq - 3 * m])
+    L_win = Tq + W - 1 + 3 * m
+    win_pos0 = q_pos0 - W + 1 - 3 * m
+    q, pool, win = (synth.Tensor(f(*sh), "bf16") for sh in [(B, Tq, H, D), (B, N, D), (B, L_win, D)])
+    sink = 0.5 * f(H)
+    if kind == "csa":
+        nv = [[O.visible_count(q_pos0[b] + t, m, N) for t in range(Tq)] for b in range(B)]
+        sel = _rand_sel(rng, B, Tq, K, nv, 5)
+        out, lse = _run_attn("csa", dev(q), dev(pool), dev(sel), dev(win), i64(win_pos0), W,
+                             dev(sink), i64(q_pos0), R)
+        ro, rl = _attn_ref("csa", q.f32, pool.f32, sel, win.f32, win_pos0, W, sink, q_pos0, R)
+    else:
+        n_ent = np.array([N, N - 7], np.int32)
+        out, lse = _run_attn("hca", dev(q), dev(pool), None, dev(win), i64(win_pos0), W,
+                             dev(sink), i64(q_pos0), R, m=m, n_entries=i32(n_ent))
+        ro, rl = _attn_ref("hca", q.f32, pool.f32, None, win.f32, win_pos0, W, sink, q_pos0, R,
+                           m=m, n_entries=n_ent)
+    assert rowwise_rel_err(host(out), ro) <= TOL_BF16
+    assert np.abs(host(lse) - rl).max() <= LSE_ATOL_BF16
+
+
 @pytest.mark.parametrize("N,n_ent,Tq,W", [(300, [300, 250, 1], 1, 128), (64, [64, 10, 0], 2, 16),
                                           (2000, [2000, 1999, 1000], 1, 128)])
 def test_attn_hca_bf16(N, n_ent, Tq, W):
