@@ -29,7 +29,10 @@ design notes of the repository):
   * mask first, then top-k; ties go to the lower entry index;
   * selected and window rows are concatenated without de-duplication;
   * an empty key set gives a zero output and lse equal to the sink logit;
-  * all positions are 0-based.
+  * all positions are 0-based;
+  * FP4 indexer keys are stored in the OCP Microscaling (MX) FP4 format:
+    E2M1 elements with one E8M0 power-of-two scale per 32 channels (the
+    pages name FP4 for the indexer and give no format).
 
 Parity status: every function here is pinned by tests/test_oracle_pins.py
 against printed values, closed forms, invariants or library routines, except
@@ -55,6 +58,9 @@ __all__ = [
     "csa_index_topk",
     "csa_sparse_attn",
     "hca_attn",
+    "E2M1_GRID",
+    "mxfp4_quantize",
+    "mxfp4_dequantize",
 ]
 
 
@@ -399,3 +405,66 @@ def hca_attn(q, pool, n_entries, m, win, win_pos0, W, sink, q_pos0, scale,
                                _window_rows(win[b], win_pos0[b], t_pos, W)])
         out[b, t], lse[b, t] = attend(q[b, t], t_pos, rows, sink, scale, rope_dims, rope_base)
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# FP4 storage of the indexer keys (reading)
+# ---------------------------------------------------------------------------
+# [P1] "What does HCA change?" names FP4 for the indexer's cache and gives no
+# format.  Reading: the OCP Microscaling (MX) v1.0 FP4 format, blocks of 32
+# channels.  Element: E2M1 (sign bit 3; 3-bit magnitude code c holding
+# E2M1_GRID[c]).  Block scale: E8M0 byte s meaning 2**(s - 127), with
+# s = floor(log2(max |x|)) - 2 + 127 clamped to [0, 254] (2 is the largest
+# exponent of an E2M1 value); an all-zero block takes s = 0.  Each element is
+# |x| / 2**(s-127) rounded to the nearest grid value, ties to the even code
+# (the one whose lowest bit is 0); the scaled value is below 8, so the top
+# grid value 6 also takes everything in [6, 8).  The sign bit is set for
+# x < 0.  Packing: channel 2i in the low nibble of byte i.
+E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+MX_BLOCK = 32
+
+
+def _e8m0_of_block(v) -> int:
+    amax = max(abs(float(e)) for e in v)
+    if amax == 0.0:
+        return 0
+    _, k = math.frexp(amax)          # amax = f * 2**k with 0.5 <= f < 1
+    return min(max((k - 1) - 2 + 127, 0), 254)
+
+
+def _e2m1_code(x: float, scale: float) -> int:
+    a = abs(x) / scale
+    best = min(range(8), key=lambda c: (abs(a - E2M1_GRID[c]), c & 1))
+    return best | (8 if x < 0 else 0)
+
+
+def mxfp4_quantize(x):
+    """Keys [..., D] (D a multiple of 32) -> (codes uint8 [..., D/2],
+    scales uint8 [..., D/32]) in the MX FP4 reading above.  Plain loops."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    assert D % MX_BLOCK == 0
+    flat = x.reshape(-1, D)
+    codes = np.zeros((flat.shape[0], D // 2), np.uint8)
+    scales = np.zeros((flat.shape[0], D // MX_BLOCK), np.uint8)
+    for r in range(flat.shape[0]):
+        nib = []
+        for blk in range(D // MX_BLOCK):
+            v = flat[r, MX_BLOCK * blk: MX_BLOCK * (blk + 1)]
+            s = _e8m0_of_block(v)
+            scales[r, blk] = s
+            nib += [_e2m1_code(e, 2.0 ** (s - 127)) for e in v]
+        for i in range(D // 2):
+            codes[r, i] = nib[2 * i] | (nib[2 * i + 1] << 4)
+    return codes.reshape(x.shape[:-1] + (D // 2,)), scales.reshape(x.shape[:-1] + (D // MX_BLOCK,))
+
+
+def mxfp4_dequantize(codes, scales) -> np.ndarray:
+    """Exact values (float64 [..., D]) of MX FP4 keys stored as above."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    nib = np.stack([codes & 15, codes >> 4], axis=-1).reshape(codes.shape[:-1] + (-1,))
+    mag = np.asarray(E2M1_GRID, dtype=np.float64)[nib & 7]
+    val = np.where(nib & 8, -mag, mag)
+    scale = np.repeat(np.exp2(scales.astype(np.float64) - 127.0), MX_BLOCK, axis=-1)
+    return val * scale

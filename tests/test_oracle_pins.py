@@ -522,3 +522,83 @@ def test_hca_equals_csa_with_all_visible_selected():
     a, la = O.hca_attn(q, pool, n_ent, m, win, win_pos0, W, sink, q_pos0, 0.25, R)
     c, lc = O.csa_sparse_attn(q, pool, idx, win, win_pos0, W, sink, q_pos0, 0.25, R)
     assert np.allclose(a, c) and np.allclose(la, lc)
+
+
+# ---------------------------------------------------------------------------
+# MX FP4 storage of the indexer keys (reading: OCP Microscaling FP4, E2M1
+# elements, E8M0 scale per 32 channels)
+# ---------------------------------------------------------------------------
+# (value at scale 1, E2M1 code) worked out by hand from the element grid
+# 0, .5, 1, 1.5, 2, 3, 4, 6: exact grid points, the seven midpoints (ties go to
+# the code with a clear lowest bit), points just off a midpoint, saturation.
+_FP4_HAND = [(0.0, 0), (0.5, 1), (1.0, 2), (1.5, 3), (2.0, 4), (3.0, 5), (4.0, 6), (6.0, 7),
+             (0.25, 0), (0.75, 2), (1.25, 2), (1.75, 4), (2.5, 4), (3.5, 6), (5.0, 6),
+             (0.26, 1), (0.74, 1), (1.26, 3), (2.51, 5), (3.49, 5), (5.01, 7), (7.9, 7),
+             (-6.0, 15), (-0.3, 9), (-2.5, 12), (-0.1, 8)]
+
+
+def test_mxfp4_hand_codes():
+    vals = [v for v, _ in _FP4_HAND] + [0.0] * (64 - len(_FP4_HAND))
+    want = [c for _, c in _FP4_HAND] + [0] * (64 - len(_FP4_HAND))
+    # amax 7.9: floor(log2 7.9) = 2, so the block's scale is 2^0 (byte 127)
+    codes, scales = O.mxfp4_quantize(np.array(vals[:32] + vals[32:]).reshape(2, 32))
+    assert scales[0, 0] == 127
+    nib = [int(b) & 15 for b in codes.reshape(-1)]
+    hi = [int(b) >> 4 for b in codes.reshape(-1)]
+    got = [x for pair in zip(nib, hi) for x in pair]
+    assert got[:32] == want[:32]
+
+
+def test_mxfp4_packing_and_dequant_by_hand():
+    x = np.zeros(32)
+    x[0], x[1], x[2], x[3] = 1.0, -0.5, 6.0, -6.0
+    codes, scales = O.mxfp4_quantize(x)
+    assert scales[0] == 127
+    assert codes[0] == (2 | (9 << 4)) and codes[1] == (7 | (15 << 4))
+    assert np.all(codes[2:] == 0)
+    # byte 0x7F with scale byte 129 (x4): channel 0 = -6*4, channel 1 = +6*4
+    d = O.mxfp4_dequantize(np.array([0x7F] + [0] * 15, np.uint8), np.array([129], np.uint8))
+    assert d[0] == -24.0 and d[1] == 24.0 and np.all(d[2:] == 0)
+
+
+@pytest.mark.parametrize("k", [-20, -3, 0, 1, 7, 40])
+def test_mxfp4_scale_exponent(k):
+    # the scale byte is floor(log2 amax) - 2 + 127
+    for amax, want in [(2.0 ** k, k + 125), (2.0 ** k * (1 - 2.0 ** -30), k + 124),
+                       (1.5 * 2.0 ** k, k + 125)]:
+        x = np.zeros(32)
+        x[5] = -amax
+        _, s = O.mxfp4_quantize(x)
+        assert int(s[0]) == want, (amax, int(s[0]), want)
+    z, s = O.mxfp4_quantize(np.zeros(64))
+    assert np.all(s == 0) and np.all(z == 0)
+
+
+def test_mxfp4_grid_values_round_trip_exactly():
+    rng = np.random.default_rng(11)
+    grid = np.array(O.E2M1_GRID)
+    for trial in range(20):
+        k = int(rng.integers(-30, 30))
+        v = grid[rng.integers(0, 8, size=(3, 64))] * np.where(rng.random((3, 64)) < 0.5, -1, 1)
+        v[:, 0], v[:, 32] = 6.0, -4.0   # block maxima fix the scale at 2^k
+        x = v * 2.0 ** k
+        codes, scales = O.mxfp4_quantize(x)
+        assert np.array_equal(O.mxfp4_dequantize(codes, scales), x)
+
+
+def test_mxfp4_error_within_half_grid_gap():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((40, 128)) * np.exp2(rng.integers(-8, 8, size=(40, 1)))
+    codes, scales = O.mxfp4_quantize(x)
+    d = O.mxfp4_dequantize(codes, scales)
+    X = np.repeat(np.exp2(scales.astype(np.float64) - 127), 32, axis=-1)
+    a = np.abs(x) / X
+    assert np.all(a < 8)
+    # half the gap of the grid interval the scaled value falls in (values in
+    # [6, 8) saturate to 6)
+    half = np.where(a <= 2, 0.25, np.where(a <= 4, 0.5, np.where(a <= 6, 1.0, a - 6)))
+    assert np.all(np.abs(d - x) <= half * X * (1 + 1e-12))
+    assert np.all(np.sign(d) * np.sign(x) >= 0)
+    # the block maximum keeps at least 2^(-1) of its value: scale choice sane
+    amax = np.abs(x).reshape(40, 4, 32).max(-1)
+    assert np.all(np.abs(d).reshape(40, 4, 32).max(-1) >= 0.5 * amax)
