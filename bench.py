@@ -10,7 +10,9 @@ scoring), lightning-indexer scores + top-512 selection, sparse gather
 attention with the sink.  Other workloads
 (--workload): csa1m (batch 8, context 1,048,576), hca1m (HCA decode, batch
 16, context 1,048,576: compress + hca_attn), prefill (CSA chunk of 4,096
-queries on a 61,440-token prefix).
+queries on a 61,440-token prefix), csa64k_pro (V4-Pro attention: 128 heads,
+top-1024), csa64k_fp4 / csa1m_fp4 (as csa64k / csa1m with the indexer keys
+stored in MX FP4; the fresh key is quantized inside the step).
 
 Timing: inputs resident in HBM; the step is captured once per input copy in
 a HIP graph and replayed; enough copies of the inputs are rotated that no
@@ -48,7 +50,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="csa64k",
-                   choices=["csa64k", "csa1m", "hca1m", "prefill", "csa64k_pro"])
+                   choices=["csa64k", "csa1m", "hca1m", "prefill", "csa64k_pro", "csa64k_fp4",
+                            "csa1m_fp4"])
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
     p.add_argument("--no-cpu", action="store_true")
@@ -58,6 +61,9 @@ def parse():
 # ---------------------------------------------------------------------------
 # workload setup
 # ---------------------------------------------------------------------------
+CSA_DECODE = ("csa64k", "csa1m", "csa64k_pro", "csa64k_fp4", "csa1m_fp4")
+
+
 def upload(d, torch):
     from long_context_sparse_11_amd.device import to_device
     out = {}
@@ -77,7 +83,7 @@ class Step:
         self._cws = {}
         B, D, m = g["B"], g["D"], g["m"]
         self.B = B
-        if kind in ("csa64k", "csa1m", "csa64k_pro"):
+        if kind in CSA_DECODE:
             N, K, W = g["N"], g["K"], g["W"]
             self.idx = torch.empty((B, 1, K), dtype=torch.int32, device="cuda")
             self.out = torch.empty_like(g["q"])
@@ -118,6 +124,10 @@ class Step:
         if not hasattr(self, "scores"):
             B, Tq, N = g["B"], g["Tq"], g["N"]
             self.scores = self.torch.empty((B, Tq, N), dtype=self.torch.float32, device="cuda")
+        if self.kind.endswith("_fp4"):
+            return ("index_scores", lambda: L.csa_index_scores_mxfp4(
+                g["q_idx"], g["w_idx"], g["k_codes"], g["k_scales"], g["n_entries"], g["q_pos0"],
+                g["m"], out=self.scores))
         return ("index_scores", lambda: L.csa_index_scores(g["q_idx"], g["w_idx"], g["k_idx"],
                                                            g["n_entries"], g["q_pos0"], g["m"],
                                                            out=self.scores))
@@ -126,9 +136,27 @@ class Step:
         """The step as a list of (name, thunk) library calls."""
         g, L = self.g, self.L
         kind = self.kind
-        if kind in ("csa64k", "csa1m", "csa64k_pro"):
+        if kind in CSA_DECODE:
             N, D, Di, m = g["N"], g["D"], g["Di"], g["m"]
-            pool, kidx = g["pool"], g["k_idx"]
+            pool = g["pool"]
+            kv_job = dict(c_a=g["c_a"], z_a=g["z_a"], c_b=g["c_b"], z_b=g["z_b"],
+                          prev_c_b=g["prev_c_b"], prev_z_b=g["prev_z_b"], bias_a=g["bias_a"],
+                          bias_b=g["bias_b"], gain=g["gain"], rope_dims=g["R"], out=pool)
+            attn = ("sparse_attn", lambda: L.csa_sparse_attn(g["q"], pool, self.idx, g["win"],
+                                                             g["win_pos0"], g["W"], g["sink"],
+                                                             g["q_pos0"], rope_dims=g["R"],
+                                                             out=self.out, ws=self.ws_a))
+            if kind.endswith("_fp4"):
+                # indexer keys stored in MX FP4: the fresh key is quantized
+                # by the fused launch into row n_entries - 1
+                key_job = dict(c_a=g["ic_a"], z_a=g["iz_a"], c_b=g["ic_b"], z_b=g["iz_b"],
+                               prev_c_b=g["iprev_c_b"], prev_z_b=g["iprev_z_b"],
+                               bias_a=g["ibias_a"], bias_b=g["ibias_b"])
+                return [("compress_index_topk", lambda: L.csa_decode_index_topk_mxfp4(
+                    g["q_idx"], g["w_idx"], g["k_codes"], g["k_scales"], g["n_entries"],
+                    g["q_pos0"], g["K"], m, [key_job, kv_job], block_pos0=g["block_pos0"],
+                    ws=self.ws_i, idx_out=self.idx)), attn]
+            kidx = g["k_idx"]
             return [
                 # the indexer key and the KV entry of the closing block (row
                 # n_entries - 1 of their pools), then the indexer top-K: the
@@ -212,12 +240,14 @@ def algorithmic(kind, d):
     B, Tq = d["B"], d["Tq"]
     bf = 2
     out = {}
-    if kind in ("csa64k", "csa1m", "csa64k_pro"):
+    if kind in CSA_DECODE:
         N = d["N"]
-        comp = B * ((4 * m) * D * bf + D * bf + (4 * m) * Di * bf + Di * bf)
-        idx_bytes = B * (N * Di * bf + Hi * Di * bf + Hi * 4 + K * 4)
+        # bytes of one stored indexer key: bf16, or MX FP4 codes + scale bytes
+        kb = Di // 2 + Di // 32 if kind.endswith("_fp4") else Di * bf
+        comp = B * ((4 * m) * D * bf + D * bf + (4 * m) * Di * bf + kb)
+        idx_bytes = B * (N * kb + Hi * Di * bf + Hi * 4 + K * 4)
         # the scoring kernel alone: visible keys, query heads and weights
-        out["index_scores"] = {"bytes": B * (N * Di * bf + Hi * Di * bf + Hi * 4),
+        out["index_scores"] = {"bytes": B * (N * kb + Hi * Di * bf + Hi * 4),
                                "flops": B * 2 * Hi * Di * N}
         rows = min(K, N) + W
         attn_bytes = B * (rows * D * bf + 2 * H * D * bf + K * 4)
@@ -348,12 +378,17 @@ def cpu_baseline(kind, d, budget_s):
                 pool[-1] = kv[0]
                 rows = np.concatenate([pool, win[wr]])
             else:
-                O.compress(d["ic_a"].f32[bb], d["iz_a"].f32[bb], d["ibias_a"], m,
+                ik = O.compress(d["ic_a"].f32[bb], d["iz_a"].f32[bb], d["ibias_a"], m,
                            c_b=d["ic_b"].f32[bb], z_b=d["iz_b"].f32[bb], bias_b=d["ibias_b"],
                            prev_c_b=d["iprev_c_b"].f32[bb], prev_z_b=d["iprev_z_b"].f32[bb])
                 nv = O.visible_count(tp, m, d["N"])
+                if kind.endswith("_fp4"):
+                    keys = O.mxfp4_dequantize(d["k_codes"][bb, :nv], d["k_scales"][bb, :nv])
+                    keys[-1] = O.mxfp4_dequantize(*O.mxfp4_quantize(ik[0]))
+                else:
+                    keys = rows_of(d["k_idx"], bb, slice(0, nv))
                 s = O.index_scores(d["q_idx"].f32[bb, 0], d["w_idx"][bb, 0],
-                                   rows_of(d["k_idx"], bb, slice(0, nv))).astype(np.float32)
+                                   keys).astype(np.float32)
                 sel = O.select_topk(s, nv, d["K"])
                 rows = np.concatenate([rows_of(d["pool"], bb, [v for v in sel if v >= 0]), win[wr]])
             O.attend(d["q"].f32[bb, 0], tp, rows, d["sink"], scale, d["R"])
@@ -518,6 +553,10 @@ def main():
         "csa64k_pro": dict(workload="csa_decode_64k_v4pro", batch=4, context=65536,
                            entries=16384),
         "csa1m": dict(workload="csa_decode_1m", batch=8, context=1048576, entries=262144),
+        "csa64k_fp4": dict(workload="csa_decode_64k_mxfp4_keys", batch=4, context=65536,
+                           entries=16384, index_key_format="mxfp4"),
+        "csa1m_fp4": dict(workload="csa_decode_1m_mxfp4_keys", batch=8, context=1048576,
+                          entries=262144, index_key_format="mxfp4"),
         "hca1m": dict(workload="hca_decode_1m", batch=16, context=1048576, entries=8192),
         "prefill": dict(workload="csa_prefill_4k_on_60k", batch=1, queries=4096, context=65536,
                         entries=16384),

@@ -225,6 +225,66 @@ int csa_index_scores(int dt, int B, int Tq, int Hi, int Di, int N_cap, int m,
                      void* stream);
 
 /* ---------------------------------------------------------------------------
+ * MX FP4 indexer keys.
+ *
+ * [P1] "What does HCA change?": the cache holds the indexer's keys in FP4
+ * (and the attention entries in mixed BF16/FP8); the pages give no format.
+ * Format here (the OCP Microscaling FP4 format, converted in hardware on
+ * gfx950): each key of Di channels (Di a multiple of 32) is Di/2 code bytes,
+ * channel 2i in the low nibble of byte i, plus Di/32 scale bytes.  A code is
+ * E2M1: bit 3 the sign, bits 0-2 a magnitude index into {0, 0.5, 1, 1.5, 2,
+ * 3, 4, 6}.  Scale byte s of a 32-channel block multiplies its elements by
+ * 2^(s - 127).
+ *
+ *   k_codes   [B, N_cap, Di/2]  uint8
+ *   k_scales  [B, N_cap, Di/32] uint8
+ * ------------------------------------------------------------------------- */
+
+/* csa_quantize_mxfp4 - rows x D values to MX FP4.  Per 32-channel block,
+ * s = floor(log2(max |x|)) - 2 + 127 clamped to [0, 254] (0 for an all-zero
+ * block); each element is |x| / 2^(s-127) rounded to the nearest magnitude,
+ * ties to the even index (values in [6, 8) give 6), sign bit set for x < 0.
+ *   x       [rows, D] dt, finite
+ *   codes   [rows, D/2] uint8; scales [rows, D/32] uint8 (device, caller-owned)
+ * Errors: CSA_ERR_ARG for a bad dt, rows < 0, D <= 0 or D % 32 != 0, NULL
+ * pointers with rows > 0; CSA_ERR_UNSUPPORTED past rows * D = 2^39. */
+int csa_quantize_mxfp4(int dt, int64_t rows, int D, const void* x, uint8_t* codes,
+                       uint8_t* scales, void* stream);
+
+/* csa_index_topk_mxfp4 / csa_index_scores_mxfp4 - csa_index_topk and
+ * csa_index_scores with the keys in MX FP4 (dt is bf16: q_idx bf16, w_idx
+ * f32).  Each key value is its code's magnitude times its block's scale
+ * (exact in bf16 for scale bytes 2..253), so the results are those of the
+ * bf16 calls on the dequantized keys.  Same shapes, workspace and errors as
+ * those calls; CSA_ERR_ARG also for Di % 32 != 0 or a NULL k_scales. */
+int csa_index_topk_mxfp4(int B, int Tq, int Hi, int Di, int N_cap, int K, int m,
+                         const void* q_idx, const float* w_idx, const uint8_t* k_codes,
+                         const uint8_t* k_scales, const int32_t* n_entries,
+                         const int64_t* q_pos0, int32_t* idx_out, float* score_out,
+                         float* all_scores, void* ws, size_t ws_bytes, void* stream);
+int csa_index_scores_mxfp4(int B, int Tq, int Hi, int Di, int N_cap, int m,
+                           const void* q_idx, const float* w_idx, const uint8_t* k_codes,
+                           const uint8_t* k_scales, const int32_t* n_entries,
+                           const int64_t* q_pos0, float* scores, void* stream);
+
+/* csa_decode_index_topk_mxfp4 - csa_decode_index_topk with the indexer keys
+ * in MX FP4: the key job's fresh entry (pooled in float32 as the compressor
+ * does) is quantized as csa_quantize_mxfp4 and written to row r_b of k_codes
+ * and k_scales; the indexer then reads the FP4 keys (the fresh one scored
+ * from its quantized value).  jobs[0].out must be NULL and its out_bstride
+ * 0; jobs[1] (the KV compressor, if given) writes bf16 as before.  Only the
+ * fused launch writes FP4: bf16 streams, Hi = 64, Di = 128, Tq < 8, job
+ * D <= 512 and at most 16 pooled rows, else CSA_ERR_UNSUPPORTED before any
+ * launch.  Other arguments and errors as csa_decode_index_topk (dt bf16). */
+int csa_decode_index_topk_mxfp4(int B, int Tq, int Hi, int Di, int N_cap, int K, int m,
+                                int overlap, const int64_t* block_pos0,
+                                const csa_compress_job* jobs, int n_jobs, const void* q_idx,
+                                const float* w_idx, uint8_t* k_codes, uint8_t* k_scales,
+                                const int32_t* n_entries, const int64_t* q_pos0,
+                                int32_t* idx_out, float* score_out, float* all_scores,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * csa_sparse_attn - shared-K=V multi-query attention with a per-head sink
  * over the selected pool rows and the sliding-window rows.
  *

@@ -12,6 +12,10 @@ from .binding import (  # noqa: F401
     csa_compress_batch,
     csa_compress_ws_bytes,
     csa_decode_index_topk,
+    csa_decode_index_topk_mxfp4,
+    csa_index_scores_mxfp4,
+    csa_index_topk_mxfp4,
+    csa_quantize_mxfp4,
     csa_index_scores,
     csa_index_topk,
     csa_index_topk_ws_bytes,

@@ -43,6 +43,13 @@ _SIGS = {
     "csa_index_scores": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                      _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                      _c.c_void_p, _c.c_void_p, _c.c_void_p]),
+    "csa_quantize_mxfp4": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_void_p,
+                                      _c.c_void_p, _c.c_void_p]),
+    "csa_index_topk_mxfp4": (_c.c_int, [_c.c_int] * 7 + [_c.c_void_p] * 10 + [_c.c_size_t,
+                                                                               _c.c_void_p]),
+    "csa_index_scores_mxfp4": (_c.c_int, [_c.c_int] * 6 + [_c.c_void_p] * 8),
+    "csa_decode_index_topk_mxfp4": (_c.c_int, [_c.c_int] * 8 + [_c.c_void_p, _c.c_void_p, _c.c_int]
+                                    + [_c.c_void_p] * 10 + [_c.c_size_t, _c.c_void_p]),
     "csa_index_topk_ws_bytes": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int]),
     "csa_sparse_attn": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                    _c.c_double, _c.c_float, _c.c_void_p, _c.c_void_p, _c.c_int,
@@ -169,13 +176,14 @@ class CompressJob(ctypes.Structure):
                 ("rope_base", _c.c_double), ("out", _c.c_void_p), ("out_bstride", _c.c_int64)]
 
 
-def _job_array(jobs, B, T, overlap, out_shape):
+def _job_array(jobs, B, T, overlap, out_shape, first_out_none=False):
     """ctypes array of csa_compress_job from job dicts; out_shape(D) is the
     shape each job's ``out`` must have (row stride D, batch stride
-    ``out_bstride`` or the rows times D)."""
+    ``out_bstride`` or the rows times D).  first_out_none: job 0 has no
+    ``out`` (its entries go elsewhere)."""
     arr = (CompressJob * len(jobs))()
     for k, j in enumerate(jobs):
-        c_a, out = j["c_a"], j["out"]
+        c_a, out = j["c_a"], j.get("out")
         Bj, Tj, D = c_a.shape
         if (Bj, Tj) != (B, T) or (j.get("c_b") is not None) != overlap or c_a.dtype != jobs[0]["c_a"].dtype:
             raise ValueError("jobs must share B, T, dtype and overlap")
@@ -184,7 +192,10 @@ def _job_array(jobs, B, T, overlap, out_shape):
         _f32(j.get("bias_a")), _f32(j.get("bias_b")), _f32(j.get("gain"))
         shape = out_shape(D)
         bs = j.get("out_bstride", 0) or shape[1] * D
-        if (tuple(out.shape) != shape or out.dtype != c_a.dtype or not out.is_cuda
+        if k == 0 and first_out_none:
+            if out is not None or j.get("out_bstride", 0):
+                raise ValueError("job 0 takes no out here")
+        elif (tuple(out.shape) != shape or out.dtype != c_a.dtype or not out.is_cuda
                 or out.stride(2) != 1 or (shape[1] > 1 and out.stride(1) != D)
                 or (B > 1 and out.stride(0) != bs)):
             raise ValueError(f"out must be {list(shape)} with row stride D and batch stride "
@@ -194,7 +205,8 @@ def _job_array(jobs, B, T, overlap, out_shape):
                              p(j.get("prev_c_b")), p(j.get("prev_z_b")), p(j.get("bias_a")),
                              p(j.get("bias_b")), p(j.get("gain")), float(j.get("eps", 1e-6)),
                              int(j.get("rope_dims", 0)), float(j.get("rope_base", 10000.0)),
-                             out.data_ptr(), int(j.get("out_bstride", 0)))
+                             None if out is None else out.data_ptr(),
+                             int(j.get("out_bstride", 0)))
     return arr
 
 
@@ -287,6 +299,107 @@ def csa_decode_index_topk(q_idx, w_idx, n_entries, q_pos0, K, m, jobs, *, block_
                                      _p(score_out), _p(all_scores), _p(ws),
                                      0 if ws is None else ws.numel(), _stream(stream))
     _check(st, "csa_decode_index_topk")
+    return idx_out, score_out, all_scores
+
+
+def _fp4_keys(k_codes, k_scales, Di):
+    B, N_cap, nb = k_codes.shape
+    if (k_codes.dtype != torch.uint8 or k_scales.dtype != torch.uint8 or nb * 2 != Di
+            or tuple(k_scales.shape) != (B, N_cap, Di // 32) or not k_codes.is_contiguous()
+            or not k_scales.is_contiguous()):
+        raise ValueError("k_codes uint8 [B, N_cap, Di/2] and k_scales uint8 [B, N_cap, Di/32], "
+                         "contiguous")
+    return N_cap
+
+
+def csa_quantize_mxfp4(x, *, codes=None, scales=None, stream=None):
+    """[..., D] float32/bf16 -> (codes uint8 [..., D/2], scales uint8
+    [..., D/32]) in MX FP4 (see include/csa.h)."""
+    _dev(x)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    D = x.shape[-1]
+    rows = x.numel() // D if D else 0
+    lead = tuple(x.shape[:-1])
+    if codes is None:
+        codes = torch.empty(lead + (D // 2,), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(lead + (D // 32,), dtype=torch.uint8, device=x.device)
+    st = lib().csa_quantize_mxfp4(_dt(x), rows, D, _p(x), _p(codes), _p(scales), _stream(stream))
+    _check(st, "csa_quantize_mxfp4")
+    return codes, scales
+
+
+def csa_index_topk_mxfp4(q_idx, w_idx, k_codes, k_scales, n_entries, q_pos0, K, m, *,
+                         want_scores=False, want_all_scores=False, ws=None, idx_out=None,
+                         stream=None):
+    """csa_index_topk with MX FP4 keys (q_idx bf16)."""
+    B, Tq, Hi, Di = q_idx.shape
+    _dev(q_idx, w_idx, k_codes, k_scales, n_entries, q_pos0)
+    _f32(w_idx), _i64(q_pos0)
+    N_cap = _fp4_keys(k_codes, k_scales, Di)
+    dev = q_idx.device
+    if idx_out is None:
+        idx_out = torch.empty((B, Tq, K), dtype=torch.int32, device=dev)
+    score_out = torch.empty((B, Tq, K), dtype=torch.float32, device=dev) if want_scores else None
+    all_scores = (torch.empty((B, Tq, N_cap), dtype=torch.float32, device=dev)
+                  if want_all_scores else None)
+    need = csa_index_topk_ws_bytes(B, Tq, Hi, N_cap, K)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = lib().csa_index_topk_mxfp4(B, Tq, Hi, Di, N_cap, K, m, _p(q_idx), _p(w_idx),
+                                    _p(k_codes), _p(k_scales), _p(n_entries), _p(q_pos0),
+                                    _p(idx_out), _p(score_out), _p(all_scores), _p(ws),
+                                    0 if ws is None else ws.numel(), _stream(stream))
+    _check(st, "csa_index_topk_mxfp4")
+    return idx_out, score_out, all_scores
+
+
+def csa_index_scores_mxfp4(q_idx, w_idx, k_codes, k_scales, n_entries, q_pos0, m, *, out=None,
+                           stream=None):
+    """csa_index_scores with MX FP4 keys (q_idx bf16)."""
+    B, Tq, Hi, Di = q_idx.shape
+    _dev(q_idx, w_idx, k_codes, k_scales, n_entries, q_pos0)
+    _f32(w_idx), _i64(q_pos0)
+    N_cap = _fp4_keys(k_codes, k_scales, Di)
+    if out is None:
+        out = torch.empty((B, Tq, N_cap), dtype=torch.float32, device=q_idx.device)
+    st = lib().csa_index_scores_mxfp4(B, Tq, Hi, Di, N_cap, m, _p(q_idx), _p(w_idx), _p(k_codes),
+                                      _p(k_scales), _p(n_entries), _p(q_pos0), _p(out),
+                                      _stream(stream))
+    _check(st, "csa_index_scores_mxfp4")
+    return out
+
+
+def csa_decode_index_topk_mxfp4(q_idx, w_idx, k_codes, k_scales, n_entries, q_pos0, K, m, jobs,
+                                *, block_pos0=None, want_scores=False, want_all_scores=False,
+                                ws=None, idx_out=None, stream=None):
+    """csa_decode_index_topk with the indexer keys in MX FP4: jobs[0] (the
+    key compressor, no ``out``) writes its fresh entry quantized into row
+    min(n_entries[b], N_cap) - 1 of k_codes / k_scales."""
+    B, Tq, Hi, Di = q_idx.shape
+    _dev(q_idx, w_idx, k_codes, k_scales, n_entries, q_pos0, block_pos0)
+    _f32(w_idx), _i64(q_pos0), _i64(block_pos0)
+    N_cap = _fp4_keys(k_codes, k_scales, Di)
+    if jobs[0]["c_a"].shape[1] != m:
+        raise ValueError("the jobs' streams hold one block of m tokens")
+    overlap = jobs[0].get("c_b") is not None
+    arr = _job_array(jobs, B, m, overlap, lambda D: (B, N_cap, D), first_out_none=True)
+    dev = q_idx.device
+    if idx_out is None:
+        idx_out = torch.empty((B, Tq, K), dtype=torch.int32, device=dev)
+    score_out = torch.empty((B, Tq, K), dtype=torch.float32, device=dev) if want_scores else None
+    all_scores = (torch.empty((B, Tq, N_cap), dtype=torch.float32, device=dev)
+                  if want_all_scores else None)
+    need = csa_index_topk_ws_bytes(B, Tq, Hi, N_cap, K)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = lib().csa_decode_index_topk_mxfp4(
+        B, Tq, Hi, Di, N_cap, K, m, int(overlap), _p(block_pos0),
+        ctypes.cast(arr, ctypes.c_void_p), len(jobs), _p(q_idx), _p(w_idx), _p(k_codes),
+        _p(k_scales), _p(n_entries), _p(q_pos0), _p(idx_out), _p(score_out), _p(all_scores),
+        _p(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _check(st, "csa_decode_index_topk_mxfp4")
     return idx_out, score_out, all_scores
 
 

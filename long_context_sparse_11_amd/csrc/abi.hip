@@ -126,7 +126,7 @@ namespace {
 // kernel covers the shape, else a compressor launch first).
 int index_topk_run(int dt, int B, int Tq, int Hi, int Di, int N_cap, int K, int m,
                    const void* q_idx, const float* w_idx, const void* k_idx,
-                   const int32_t* n_entries, const int64_t* q_pos0, int32_t* idx_out,
+                   const uint8_t* k_scales, const int32_t* n_entries, const int64_t* q_pos0, int32_t* idx_out,
                    float* score_out, float* all_scores, void* ws, size_t ws_bytes,
                    const FreshJobs* fresh, hipStream_t s) {
   if (dt != CSA_F32 && dt != CSA_BF16) return CSA_ERR_ARG;
@@ -134,6 +134,7 @@ int index_topk_run(int dt, int B, int Tq, int Hi, int Di, int N_cap, int K, int 
   if (B == 0 || Tq == 0) return CSA_OK;
   if (!q_idx || !w_idx || !n_entries || !q_pos0 || !idx_out) return CSA_ERR_ARG;
   if (N_cap > 0 && !k_idx) return CSA_ERR_ARG;
+  if (k_scales && (dt != CSA_BF16 || Di % 32)) return CSA_ERR_ARG;
   if (Hi > 64 || Di > 256 || Hi * Di > 8192 || K > 4096 || N_cap > (1 << 26))
     return CSA_ERR_UNSUPPORTED;
   if ((int64_t)topk_chunks(N_cap) * K > kTopkCap) return CSA_ERR_UNSUPPORTED;
@@ -145,9 +146,13 @@ int index_topk_run(int dt, int B, int Tq, int Hi, int Di, int N_cap, int K, int 
   w += align256(q * (size_t)N_cap * sizeof(float));
 
   if (N_cap > 0) {
-    IndexArgs ia{dt, B, Tq, Hi, Di, N_cap, m, q_idx, w_idx, k_idx, n_entries, q_pos0, scores};
+    IndexArgs ia{dt, B, Tq, Hi, Di, N_cap, m, q_idx, w_idx, k_idx, n_entries, q_pos0, scores,
+                 k_scales};
     hipError_t e;
-    if (fresh && index_fresh_fused(ia, *fresh)) {
+    const bool fused = fresh && index_fresh_fused(ia, *fresh);
+    // FP4 fresh keys are written only by the fused launch
+    if (fresh && !fused && fresh->job[0].out_scales) return CSA_ERR_UNSUPPORTED;
+    if (fused) {
       e = launch_index_fresh(ia, *fresh, s);
     } else {
       e = fresh ? launch_compress_batch(fresh->job, fresh->n_jobs, s) : hipSuccess;
@@ -193,10 +198,50 @@ CSA_EXPORT int csa_index_topk(int dt, int B, int Tq, int Hi, int Di, int N_cap, 
                               const int32_t* n_entries, const int64_t* q_pos0, int32_t* idx_out,
                               float* score_out, float* all_scores, void* ws, size_t ws_bytes,
                               void* stream) {
-  return index_topk_run(dt, B, Tq, Hi, Di, N_cap, K, m, q_idx, w_idx, k_idx, n_entries, q_pos0,
-                        idx_out, score_out, all_scores, ws, ws_bytes, nullptr,
+  return index_topk_run(dt, B, Tq, Hi, Di, N_cap, K, m, q_idx, w_idx, k_idx, nullptr, n_entries,
+                        q_pos0, idx_out, score_out, all_scores, ws, ws_bytes, nullptr,
                         (hipStream_t)stream);
 }
+
+CSA_EXPORT int csa_index_topk_mxfp4(int B, int Tq, int Hi, int Di, int N_cap, int K, int m,
+                                    const void* q_idx, const float* w_idx, const uint8_t* k_codes,
+                                    const uint8_t* k_scales, const int32_t* n_entries,
+                                    const int64_t* q_pos0, int32_t* idx_out, float* score_out,
+                                    float* all_scores, void* ws, size_t ws_bytes, void* stream) {
+  if (N_cap > 0 && !k_scales) return CSA_ERR_ARG;
+  if (Di <= 0 || Di % 32) return CSA_ERR_ARG;
+  return index_topk_run(CSA_BF16, B, Tq, Hi, Di, N_cap, K, m, q_idx, w_idx, k_codes,
+                        N_cap > 0 ? k_scales : nullptr, n_entries, q_pos0, idx_out, score_out,
+                        all_scores, ws, ws_bytes, nullptr, (hipStream_t)stream);
+}
+
+namespace {
+
+// The fresh-entry jobs of a decode step; key_codes/key_scales replace job
+// 0's output when the indexer keys are stored as MX FP4.  Returns a status.
+int decode_jobs(int dt, int B, int N_cap, int m, int overlap, const int64_t* block_pos0,
+                const csa_compress_job* jobs, int n_jobs, uint8_t* key_codes,
+                uint8_t* key_scales, const int32_t* n_entries, FreshJobs& f) {
+  f = FreshJobs{};
+  f.n_jobs = n_jobs;
+  for (int k = 0; k < n_jobs; ++k) {
+    const csa_compress_job& j = jobs[k];
+    const int64_t pool_stride = (int64_t)N_cap * j.D;
+    if (j.out_bstride != 0 && j.out_bstride != pool_stride) return CSA_ERR_ARG;
+    void* out = (k == 0 && key_codes) ? key_codes : j.out;
+    const int st = compress_args(dt, B, m, j.D, m, overlap, j.c_a, j.z_a, j.c_b, j.z_b,
+                                 j.prev_c_b, j.prev_z_b, j.bias_a, j.bias_b, j.gain, j.eps,
+                                 j.rope_dims, j.rope_base, block_pos0, out, pool_stride, f.job[k]);
+    if (st != CSA_OK) return st == 1 ? CSA_ERR_ARG : st;
+    f.job[k].rows_at = n_entries;
+    f.job[k].rows_cap = N_cap;
+    f.job[k].slices = 1;
+    if (k == 0 && key_codes) f.job[k].out_scales = key_scales;
+  }
+  return CSA_OK;
+}
+
+}  // namespace
 
 CSA_EXPORT int csa_decode_index_topk(int dt, int B, int Tq, int Hi, int Di, int N_cap, int K,
                                      int m, int overlap, const int64_t* block_pos0,
@@ -210,22 +255,35 @@ CSA_EXPORT int csa_decode_index_topk(int dt, int B, int Tq, int Hi, int Di, int 
   if (jobs[0].D != Di) return CSA_ERR_ARG;
   if (B == 0 || Tq == 0) return CSA_OK;
   if (N_cap == 0) return CSA_ERR_ARG;  // the fresh entries need a row
-  FreshJobs f{};
-  f.n_jobs = n_jobs;
-  for (int k = 0; k < n_jobs; ++k) {
-    const csa_compress_job& j = jobs[k];
-    const int64_t pool_stride = (int64_t)N_cap * j.D;
-    if (j.out_bstride != 0 && j.out_bstride != pool_stride) return CSA_ERR_ARG;
-    const int st = compress_args(dt, B, m, j.D, m, overlap, j.c_a, j.z_a, j.c_b, j.z_b,
-                                 j.prev_c_b, j.prev_z_b, j.bias_a, j.bias_b, j.gain, j.eps,
-                                 j.rope_dims, j.rope_base, block_pos0, j.out, pool_stride, f.job[k]);
-    if (st != CSA_OK) return st == 1 ? CSA_ERR_ARG : st;
-    f.job[k].rows_at = n_entries;
-    f.job[k].rows_cap = N_cap;
-    f.job[k].slices = 1;
-  }
-  return index_topk_run(dt, B, Tq, Hi, Di, N_cap, K, m, q_idx, w_idx, jobs[0].out, n_entries,
-                        q_pos0, idx_out, score_out, all_scores, ws, ws_bytes, &f,
+  FreshJobs f;
+  const int st = decode_jobs(dt, B, N_cap, m, overlap, block_pos0, jobs, n_jobs, nullptr, nullptr,
+                             n_entries, f);
+  if (st != CSA_OK) return st;
+  return index_topk_run(dt, B, Tq, Hi, Di, N_cap, K, m, q_idx, w_idx, jobs[0].out, nullptr,
+                        n_entries, q_pos0, idx_out, score_out, all_scores, ws, ws_bytes, &f,
+                        (hipStream_t)stream);
+}
+
+CSA_EXPORT int csa_decode_index_topk_mxfp4(int B, int Tq, int Hi, int Di, int N_cap, int K, int m,
+                                           int overlap, const int64_t* block_pos0,
+                                           const csa_compress_job* jobs, int n_jobs,
+                                           const void* q_idx, const float* w_idx,
+                                           uint8_t* k_codes, uint8_t* k_scales,
+                                           const int32_t* n_entries, const int64_t* q_pos0,
+                                           int32_t* idx_out, float* score_out, float* all_scores,
+                                           void* ws, size_t ws_bytes, void* stream) {
+  if (n_jobs < 1 || n_jobs > 2 || !jobs) return CSA_ERR_ARG;
+  if (B < 0 || Tq < 0 || N_cap < 0 || m <= 0) return CSA_ERR_ARG;
+  if (jobs[0].D != Di || Di <= 0 || Di % 32) return CSA_ERR_ARG;
+  if (jobs[0].out || jobs[0].out_bstride) return CSA_ERR_ARG;  // the key job writes k_codes
+  if (B == 0 || Tq == 0) return CSA_OK;
+  if (N_cap == 0 || !k_codes || !k_scales) return CSA_ERR_ARG;
+  FreshJobs f;
+  const int st = decode_jobs(CSA_BF16, B, N_cap, m, overlap, block_pos0, jobs, n_jobs, k_codes,
+                             k_scales, n_entries, f);
+  if (st != CSA_OK) return st;
+  return index_topk_run(CSA_BF16, B, Tq, Hi, Di, N_cap, K, m, q_idx, w_idx, k_codes, k_scales,
+                        n_entries, q_pos0, idx_out, score_out, all_scores, ws, ws_bytes, &f,
                         (hipStream_t)stream);
 }
 
@@ -240,6 +298,32 @@ CSA_EXPORT int csa_index_scores(int dt, int B, int Tq, int Hi, int Di, int N_cap
   if (Hi > 64 || Di > 256 || Hi * Di > 8192 || N_cap > (1 << 26)) return CSA_ERR_UNSUPPORTED;
   IndexArgs ia{dt, B, Tq, Hi, Di, N_cap, m, q_idx, w_idx, k_idx, n_entries, q_pos0, scores};
   return status_of(launch_index_scores(ia, (hipStream_t)stream));
+}
+
+CSA_EXPORT int csa_index_scores_mxfp4(int B, int Tq, int Hi, int Di, int N_cap, int m,
+                                      const void* q_idx, const float* w_idx,
+                                      const uint8_t* k_codes, const uint8_t* k_scales,
+                                      const int32_t* n_entries, const int64_t* q_pos0,
+                                      float* scores, void* stream) {
+  if (B < 0 || Tq < 0 || Hi <= 0 || Di <= 0 || Di % 32 || N_cap < 0 || m <= 0) return CSA_ERR_ARG;
+  if (B == 0 || Tq == 0 || N_cap == 0) return CSA_OK;
+  if (!q_idx || !w_idx || !k_codes || !k_scales || !n_entries || !q_pos0 || !scores)
+    return CSA_ERR_ARG;
+  if (Hi > 64 || Di > 256 || Hi * Di > 8192 || N_cap > (1 << 26)) return CSA_ERR_UNSUPPORTED;
+  IndexArgs ia{CSA_BF16, B, Tq, Hi, Di, N_cap, m, q_idx, w_idx, k_codes, n_entries, q_pos0,
+               scores, k_scales};
+  return status_of(launch_index_scores(ia, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------------ MX FP4
+CSA_EXPORT int csa_quantize_mxfp4(int dt, int64_t rows, int D, const void* x, uint8_t* codes,
+                                  uint8_t* scales, void* stream) {
+  if (dt != CSA_F32 && dt != CSA_BF16) return CSA_ERR_ARG;
+  if (rows < 0 || D <= 0 || D % 32) return CSA_ERR_ARG;
+  if (rows == 0) return CSA_OK;
+  if (!x || !codes || !scales) return CSA_ERR_ARG;
+  if (rows > ((int64_t)1 << 39) / D) return CSA_ERR_UNSUPPORTED;  // grid bound
+  return status_of(launch_mxfp4_quantize(dt, rows, D, x, codes, scales, (hipStream_t)stream));
 }
 
 // ------------------------------------------------------------------ attention

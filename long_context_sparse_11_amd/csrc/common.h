@@ -220,4 +220,55 @@ __device__ __forceinline__ int visible_entries(int64_t tpos, int m, int n_entrie
   return (int)(x / m);
 }
 
+// ------------------------------------------------------------- MX FP4 keys
+// Indexer keys in the OCP Microscaling FP4 format: E2M1 elements (sign bit 3,
+// magnitude code c in bits 0-2 holding 0, .5, 1, 1.5, 2, 3, 4, 6) and one
+// E8M0 scale byte s = 2^(s - 127) per 32 channels, two channels per byte
+// (the even channel in the low nibble).  The scale is floor(log2 amax) - 2,
+// and each element is rounded to the nearest grid value, ties to the even
+// code.
+
+// E8M0 scale byte of a block with largest magnitude amax (finite, >= 0):
+// the exponent field minus 2, at least 0 (zero and tiny blocks take 0).
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
+  const uint32_t ef = __float_as_uint(amax) >> 23;
+  return ef > 2u ? ef - 2u : 0u;
+}
+
+// 2^(s - 127) as a float (s = 0 is the subnormal 2^-127).
+__device__ __forceinline__ float mx_scale_value(uint32_t s) {
+  return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);
+}
+
+// E2M1 code of x under scale byte s: |x| / 2^(s-127) is below 8 whenever s
+// came from the block's maximum, and the seven comparisons place it between
+// the grid's midpoints (strict at a midpoint whose lower neighbour has the
+// even code, inclusive where the upper one does).
+__device__ __forceinline__ uint32_t e2m1_code(float x, uint32_t s) {
+  const float a = ldexpf(fabsf(x), 127 - (int)s);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return c | (x < 0.f ? 8u : 0u);
+}
+
+// Value of E2M1 code c under scale byte s (exact in float32).
+__device__ __forceinline__ float e2m1_value(uint32_t c, uint32_t s) {
+  const uint32_t k = c & 7u;
+  const float mag = k < 2u ? 0.5f * (float)k : ldexpf(1.0f + 0.5f * (float)(k & 1u), (int)(k >> 1) - 1);
+  const float v = mag * mx_scale_value(s);
+  return (c & 8u) ? -v : v;
+}
+
+// Eight channels (one code dword) to bf16 MFMA operand lanes: byte i gives
+// channels 2i (low nibble) and 2i + 1, scaled by 2^(s-127) in the hardware
+// conversion.
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t codes, float scale) {
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+  return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 }  // namespace csa

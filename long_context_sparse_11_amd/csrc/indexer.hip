@@ -11,6 +11,10 @@
 //  * index_prefill   bf16, 64 heads x 128, many queries: 8 waves = 8 queries
 //                    share 64-key tiles staged in LDS (double buffered).
 //
+// MX FP4 keys (IndexArgs::ks set): every kernel has a variant that reads the
+// codes and scale bytes and turns them into the same bf16 operands (exact:
+// an E2M1 value times a power of two has at most two significant bits).
+//
 // MFMA layout (v_mfma_f32_32x32x16_bf16, C[32x32] += A[32x16] B[16x32]):
 // lane l feeds A row (l % 32) and B column (l % 32) with 8 consecutive K
 // slots starting at 8 * (l / 32); accumulator element r of lane l is
@@ -25,7 +29,7 @@
 namespace csa {
 
 // ------------------------------------------------------------------ generic
-template <typename T>
+template <typename T, bool FP4>
 __global__ __launch_bounds__(256) void index_generic(IndexArgs a) {
   extern __shared__ float sq[];  // [Hi*Di] query, then [Hi] weights
   const int query = blockIdx.y;
@@ -39,11 +43,20 @@ __global__ __launch_bounds__(256) void index_generic(IndexArgs a) {
   __syncthreads();
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= n_vis) return;
-  const T* kp = (const T*)a.k + ((int64_t)b * a.N_cap + s) * a.Di;
+  const int64_t krow = (int64_t)b * a.N_cap + s;
+  const T* kp = (const T*)a.k + krow * a.Di;
+  auto key = [&](int c) -> float {
+    if constexpr (FP4) {
+      const uint32_t byte = ((const uint8_t*)a.k)[krow * (a.Di / 2) + (c >> 1)];
+      return e2m1_value((c & 1) ? byte >> 4 : byte & 15u, a.ks[krow * (a.Di / 32) + (c >> 5)]);
+    } else {
+      return Elem<T>::get(kp + c);
+    }
+  };
   float score = 0.f;
   for (int h = 0; h < a.Hi; ++h) {
     float dot = 0.f;
-    for (int c = 0; c < a.Di; ++c) dot += sq[h * a.Di + c] * Elem<T>::get(kp + c);
+    for (int c = 0; c < a.Di; ++c) dot += sq[h * a.Di + c] * key(c);
     score += sq[HD + h] * fmaxf(dot, 0.f);
   }
   a.scores[(int64_t)query * a.N_cap + s] = score;
@@ -87,6 +100,29 @@ __device__ __forceinline__ float tile_score(const bf16x8_t (&qa)[2][8], const bf
   const uint32_t u = __float_as_uint(sc);
   const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return sc + __uint_as_float(__lane_id() < 32 ? sw[1] : sw[0]);
+}
+
+// A lane's share of one key for the decode kernel: channels 64g .. 64g + 63
+// of key (l % 32), as eight bf16x8 operands, or as MX FP4 codes (32 bytes)
+// with the scale bytes of its two 32-channel blocks, converted when scored.
+template <bool FP4>
+struct KeyTile;
+template <>
+struct KeyTile<false> {
+  bf16x8_t v[8];
+};
+template <>
+struct KeyTile<true> {
+  uint4 c[2];
+  uint32_t s;
+};
+
+__device__ __forceinline__ void fp4_operand(const KeyTile<true>& kt, bf16x8_t (&kb)[8]) {
+  const float s0 = mx_scale_value(kt.s & 255u), s1 = mx_scale_value((kt.s >> 8) & 255u);
+  const uint32_t w[8] = {kt.c[0].x, kt.c[0].y, kt.c[0].z, kt.c[0].w,
+                         kt.c[1].x, kt.c[1].y, kt.c[1].z, kt.c[1].w};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kb[s] = fp4x8_to_bf16(w[s], s < 4 ? s0 : s1);
 }
 
 // ------------------------------------------------------------ fresh entries
@@ -193,18 +229,38 @@ __device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressAr
     y0 = x0 * cs - x1 * sn;
     y1 = x0 * sn + x1 * cs;
   }
-  const uint32_t packed = pack_bf16x2(y0, y1);
-  if (act)
-    *reinterpret_cast<uint32_t*>((bf16_t*)j.out + (int64_t)b * j.out_bstride + (int64_t)row * D +
-                                 c0) = packed;
+  // the stored values, as the scorer sees them
+  float v0, v1;
+  const int64_t at = (int64_t)b * j.out_bstride + (int64_t)row * D;  // channel offset
+  if (j.out_scales) {
+    // MX FP4: the 16 lanes of a 32-channel block share its scale
+    float am = act ? fmaxf(fabsf(y0), fabsf(y1)) : 0.f;
+    am = fmaxf(am, __shfl_xor(am, 1));
+    am = fmaxf(am, __shfl_xor(am, 2));
+    am = fmaxf(am, __shfl_xor(am, 4));
+    am = fmaxf(am, __shfl_xor(am, 8));
+    const uint32_t sb = mx_scale_byte(am);
+    const uint32_t e0 = e2m1_code(y0, sb), e1 = e2m1_code(y1, sb);
+    if (act) {
+      ((uint8_t*)j.out)[at / 2 + tid] = (uint8_t)(e0 | (e1 << 4));
+      if ((tid & 15) == 0) j.out_scales[at / 32 + (tid >> 4)] = (uint8_t)sb;
+    }
+    v0 = e2m1_value(e0, sb);
+    v1 = e2m1_value(e1, sb);
+  } else {
+    const uint32_t packed = pack_bf16x2(y0, y1);
+    if (act) *reinterpret_cast<uint32_t*>((bf16_t*)j.out + at + c0) = packed;
+    v0 = bf16_to_f32(packed & 0xffffu);
+    v1 = bf16_to_f32(packed >> 16);
+  }
   if (!score) return;
 
   // Score the stored entry for every query t of the sequence that sees it:
   // the 4 quarters of a head meet by lane swaps, the 64 heads by a wave sum
   // and the 4 waves through LDS.
   if (act) {
-    skey[c0] = bf16_to_f32(packed & 0xffffu);
-    skey[c0 + 1] = bf16_to_f32(packed >> 16);
+    skey[c0] = v0;
+    skey[c0 + 1] = v1;
   }
   __syncthreads();
   for (int t = 0; t < a.Tq; ++t) {
@@ -250,7 +306,7 @@ __device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressAr
 // ONE: one tile per wave (tiles_per_wave == 1): a single key buffer, so the
 // kernel fits three waves per SIMD (3 workgroups per CU) and a grid of up
 // to 768 workgroups, fresh ones included, runs in one round.
-template <bool FRESH, bool ONE>
+template <bool FRESH, bool ONE, bool FP4>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONE ? 3 : 1, 8)))
 void index_decode(IndexArgs a, int tiles_per_wave, int chunks, FreshJobs f) {
   __shared__ __attribute__((aligned(16))) bf16_t sq[64 * 128];
@@ -279,15 +335,21 @@ void index_decode(IndexArgs a, int tiles_per_wave, int chunks, FreshJobs f) {
   const int tile0 = cx * chunk_tiles;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 31, g = lane >> 5;
-  const bf16_t* kbase = (const bf16_t*)a.k + (int64_t)b * a.N_cap * 128 + g * 64;
   float* out = a.scores + (int64_t)query * a.N_cap;
   // key rows past the visible range are read (every row below N_cap is
   // allocated) but never scored, so no load waits for the visible count
-  auto load = [&](int tl, bf16x8_t(&dst)[8]) {
-    const int key = min(tl * 32 + j, a.N_cap - 1);
-    const bf16_t* kp = kbase + (int64_t)key * 128;
+  auto load = [&](int tl, KeyTile<FP4>& dst) {
+    const int64_t row = (int64_t)b * a.N_cap + min(tl * 32 + j, a.N_cap - 1);
+    if constexpr (FP4) {
+      const uint4* cp = reinterpret_cast<const uint4*>((const uint8_t*)a.k + row * 64 + g * 32);
+      dst.c[0] = cp[0];
+      dst.c[1] = cp[1];
+      dst.s = *reinterpret_cast<const uint16_t*>(a.ks + row * 4 + 2 * g);
+    } else {
+      const bf16_t* kp = (const bf16_t*)a.k + row * 128 + g * 64;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) dst[s] = *reinterpret_cast<const bf16x8_t*>(kp + 8 * s);
+      for (int s = 0; s < 8; ++s) dst.v[s] = *reinterpret_cast<const bf16x8_t*>(kp + 8 * s);
+    }
   };
 
   // the query's 64 x 128 head matrix and head weights, fetched once per
@@ -301,7 +363,7 @@ void index_decode(IndexArgs a, int tiles_per_wave, int chunks, FreshJobs f) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) v[u] = qg[threadIdx.x + 256 * u];
   const f32x4_t wq = reinterpret_cast<const f32x4_t*>(a.w + (int64_t)query * 64)[threadIdx.x & 15];
-  bf16x8_t k0[8];
+  KeyTile<FP4> k0;
   int tile = tile0 + wave;
   load(tile, k0);
 #pragma unroll
@@ -318,8 +380,15 @@ void index_decode(IndexArgs a, int tiles_per_wave, int chunks, FreshJobs f) {
   load_head_weights(sw, lane, wv);
 
   const int tile_end = min(tile0 + chunk_tiles, (n_vis + 31) >> 5);
-  auto score = [&](int tl, const bf16x8_t(&kb)[8]) {
-    const float sc = tile_score(qa, kb, wv);
+  auto score = [&](int tl, const KeyTile<FP4>& kt) {
+    float sc;
+    if constexpr (FP4) {
+      bf16x8_t kb[8];
+      fp4_operand(kt, kb);
+      sc = tile_score(qa, kb, wv);
+    } else {
+      sc = tile_score(qa, kt.v, wv);
+    }
     const int key = tl * 32 + j;
     if (g == 0 && key < n_vis) out[key] = sc;
   };
@@ -329,7 +398,7 @@ void index_decode(IndexArgs a, int tiles_per_wave, int chunks, FreshJobs f) {
   }
   // two key buffers in turn: the next tile's loads are in flight while the
   // current tile is scored, with no register copy between them
-  bf16x8_t k1[8];
+  KeyTile<FP4> k1;
   while (tile < tile_end) {
     const int t1 = tile + 4;
     if (t1 < tile_end) load(t1, k1);
@@ -352,6 +421,7 @@ constexpr int kPfKeys = 64;
 constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kPfPitch = 136;  // bf16 elements per LDS row
 
+template <bool FP4>
 __global__ __launch_bounds__(512) void index_prefill(IndexArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t kt[2][kPfKeys * kPfPitch];
   const int b = blockIdx.y;
@@ -372,25 +442,45 @@ __global__ __launch_bounds__(512) void index_prefill(IndexArgs a) {
   float wv[2][16];
   load_head_weights(a.w + query * 64, lane, wv);
 
-  const bf16_t* kbase = (const bf16_t*)a.k + (int64_t)b * a.N_cap * 128;
+  const int64_t kbase = (int64_t)b * a.N_cap;  // first key row of the sequence
   float* out = a.scores + query * a.N_cap;
 
-  // cooperative tile load: 64 keys x 256 B = 1024 x 16 B pieces, 2 per thread
-  const int p0 = threadIdx.x, p1 = threadIdx.x + 512;
-  auto fetch = [&](int k0, uint4& v0, uint4& v1) {
-    const int r0 = p0 >> 4, r1 = p1 >> 4;
-    const int key0 = min(k0 + r0, max(n_max - 1, 0));
-    const int key1 = min(k0 + r1, max(n_max - 1, 0));
-    v0 = *reinterpret_cast<const uint4*>(kbase + (int64_t)key0 * 128 + (p0 & 15) * 8);
-    v1 = *reinterpret_cast<const uint4*>(kbase + (int64_t)key1 * 128 + (p1 & 15) * 8);
+  // cooperative tile load: 64 keys x 128 channels = 1024 pieces of 8
+  // channels (16 B of bf16, or a code dword and a scale byte), 2 per thread;
+  // FP4 pieces are converted to bf16 on their way into LDS
+  struct Piece {
+    uint4 v;
+    uint32_t s;
   };
-  auto stash = [&](int buf, const uint4& v0, const uint4& v1) {
-    *reinterpret_cast<uint4*>(&kt[buf][(p0 >> 4) * kPfPitch + (p0 & 15) * 8]) = v0;
-    *reinterpret_cast<uint4*>(&kt[buf][(p1 >> 4) * kPfPitch + (p1 & 15) * 8]) = v1;
+  const int p0 = threadIdx.x, p1 = threadIdx.x + 512;
+  auto fetch_one = [&](int k0, int p, Piece& d) {
+    const int64_t row = kbase + min(k0 + (p >> 4), max(n_max - 1, 0));
+    if constexpr (FP4) {
+      d.v.x = reinterpret_cast<const uint32_t*>(a.k)[row * 16 + (p & 15)];
+      d.s = a.ks[row * 4 + ((p & 15) >> 2)];
+    } else {
+      d.v = *reinterpret_cast<const uint4*>((const bf16_t*)a.k + row * 128 + (p & 15) * 8);
+    }
+  };
+  auto fetch = [&](int k0, Piece& v0, Piece& v1) {
+    fetch_one(k0, p0, v0);
+    fetch_one(k0, p1, v1);
+  };
+  auto put = [&](int buf, int p, const Piece& d) {
+    uint4 v = d.v;
+    if constexpr (FP4) {
+      const bf16x8_t x = fp4x8_to_bf16(d.v.x, mx_scale_value(d.s));
+      v = *reinterpret_cast<const uint4*>(&x);
+    }
+    *reinterpret_cast<uint4*>(&kt[buf][(p >> 4) * kPfPitch + (p & 15) * 8]) = v;
+  };
+  auto stash = [&](int buf, const Piece& v0, const Piece& v1) {
+    put(buf, p0, v0);
+    put(buf, p1, v1);
   };
 
   if (n_max <= 0) return;
-  uint4 v0, v1;
+  Piece v0, v1;
   fetch(0, v0, v1);
   stash(0, v0, v1);
   // the query operand has landed before the loop: otherwise the compiler's
@@ -423,10 +513,14 @@ bool index_uses_mfma(const IndexArgs& a) { return a.dt == 1 && a.Hi == 64 && a.D
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream) {
   const int queries = a.B * a.Tq;
   if (queries == 0 || a.N_cap == 0) return hipSuccess;
+  const bool fp4 = a.ks != nullptr;
   if (index_uses_mfma(a)) {
     if (a.Tq >= 8) {
       dim3 grid((a.Tq + 7) / 8, a.B);
-      hipLaunchKernelGGL(index_prefill, grid, dim3(512), 0, stream, a);
+      if (fp4)
+        hipLaunchKernelGGL(index_prefill<true>, grid, dim3(512), 0, stream, a);
+      else
+        hipLaunchKernelGGL(index_prefill<false>, grid, dim3(512), 0, stream, a);
     } else {
       // ~1.5k workgroups in flight: enough to cover 256 CUs several times
       const int64_t keys = (int64_t)queries * a.N_cap;
@@ -435,19 +529,26 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream) {
       const int chunk = 4 * tpw * 32;
       const int chunks = (a.N_cap + chunk - 1) / chunk;
       dim3 grid(chunks * queries);
-      if (tpw == 1)
-        hipLaunchKernelGGL((index_decode<false, true>), grid, dim3(256), 0, stream, a, tpw, chunks, FreshJobs{});
+      const FreshJobs none{};
+      if (fp4 && tpw == 1)
+        hipLaunchKernelGGL((index_decode<false, true, true>), grid, dim3(256), 0, stream, a, tpw, chunks, none);
+      else if (fp4)
+        hipLaunchKernelGGL((index_decode<false, false, true>), grid, dim3(256), 0, stream, a, tpw, chunks, none);
+      else if (tpw == 1)
+        hipLaunchKernelGGL((index_decode<false, true, false>), grid, dim3(256), 0, stream, a, tpw, chunks, none);
       else
-        hipLaunchKernelGGL((index_decode<false, false>), grid, dim3(256), 0, stream, a, tpw, chunks, FreshJobs{});
+        hipLaunchKernelGGL((index_decode<false, false, false>), grid, dim3(256), 0, stream, a, tpw, chunks, none);
     }
     return hipGetLastError();
   }
   const size_t lds = ((size_t)a.Hi * a.Di + a.Hi) * sizeof(float);
   dim3 grid((a.N_cap + 255) / 256, queries);
-  if (a.dt == 1)
-    hipLaunchKernelGGL(index_generic<bf16_t>, grid, dim3(256), lds, stream, a);
+  if (fp4)
+    hipLaunchKernelGGL((index_generic<bf16_t, true>), grid, dim3(256), lds, stream, a);
+  else if (a.dt == 1)
+    hipLaunchKernelGGL((index_generic<bf16_t, false>), grid, dim3(256), lds, stream, a);
   else
-    hipLaunchKernelGGL(index_generic<float>, grid, dim3(256), lds, stream, a);
+    hipLaunchKernelGGL((index_generic<float, false>), grid, dim3(256), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -458,8 +559,11 @@ namespace csa {
 bool index_fresh_fused(const IndexArgs& a, const FreshJobs& f) {
   if (!index_uses_mfma(a) || a.Tq >= 8 || f.n_jobs < 1 || f.n_jobs > 2) return false;
   if (f.job[0].D != a.Di) return false;
+  // MX FP4 keys: the key job stores FP4 (whole 32-channel blocks), others bf16
+  if ((a.ks != nullptr) != (f.job[0].out_scales != nullptr) || (a.ks && a.Di % 32)) return false;
   for (int k = 0; k < f.n_jobs; ++k) {
     const CompressArgs& j = f.job[k];
+    if (k > 0 && j.out_scales) return false;
     const int rows = j.m * ((j.overlap && j.prev_c_b) ? 2 : 1);
     if (j.dt != 1 || j.T != j.m || j.D > 512 || (j.D & 1) || rows > kFreshMaxRows) return false;
   }
@@ -475,10 +579,15 @@ hipError_t launch_index_fresh(const IndexArgs& a, const FreshJobs& f, hipStream_
   const int chunk = 4 * tpw * 32;
   const int chunks = (a.N_cap + chunk - 1) / chunk;
   dim3 grid(chunks * queries + f.n_jobs * a.B);
-  if (tpw == 1)
-    hipLaunchKernelGGL((index_decode<true, true>), grid, dim3(256), 0, stream, a, tpw, chunks, f);
+  const bool fp4 = a.ks != nullptr;
+  if (fp4 && tpw == 1)
+    hipLaunchKernelGGL((index_decode<true, true, true>), grid, dim3(256), 0, stream, a, tpw, chunks, f);
+  else if (fp4)
+    hipLaunchKernelGGL((index_decode<true, false, true>), grid, dim3(256), 0, stream, a, tpw, chunks, f);
+  else if (tpw == 1)
+    hipLaunchKernelGGL((index_decode<true, true, false>), grid, dim3(256), 0, stream, a, tpw, chunks, f);
   else
-    hipLaunchKernelGGL((index_decode<true, false>), grid, dim3(256), 0, stream, a, tpw, chunks, f);
+    hipLaunchKernelGGL((index_decode<true, false, false>), grid, dim3(256), 0, stream, a, tpw, chunks, f);
   return hipGetLastError();
 }
 

@@ -28,6 +28,10 @@ struct CompressArgs {
   // min(rows_at[b], rows_cap) - 1 of out (none when that is negative)
   const int32_t* rows_at;
   int rows_cap;
+  // when set, entries are stored as MX FP4 (fused decode path only): out
+  // holds the codes [B, rows, D/2] bytes and out_scales the scale bytes
+  // [B, rows, D/32]; out_bstride still counts channels (rows * D)
+  uint8_t* out_scales;
 };
 // Workspace the compressor uses for a call of this shape (0 = none); rows:
 // rows pooled per entry (m, or 2m with overlap).
@@ -47,6 +51,9 @@ struct IndexArgs {
   const int32_t* n_entries;
   const int64_t* q_pos0;
   float* scores;        // [B*Tq, N_cap]
+  // MX FP4 keys when set: k holds the codes [B, N_cap, Di/2] bytes and ks the
+  // scale bytes [B, N_cap, Di/32]; q is bf16
+  const uint8_t* ks;
 };
 // True when the MFMA kernels cover this shape (bf16, 64 heads x 128).
 bool index_uses_mfma(const IndexArgs& a);
@@ -63,6 +70,12 @@ struct FreshJobs {
 // and the indexer run as separate launches).
 bool index_fresh_fused(const IndexArgs& a, const FreshJobs& f);
 hipError_t launch_index_fresh(const IndexArgs& a, const FreshJobs& f, hipStream_t stream);
+
+// ---------------------------------------------------------------- MX FP4 keys
+// rows x D values (f32 or bf16, D a multiple of 32) to MX FP4 codes
+// [rows, D/2] and scale bytes [rows, D/32].
+hipError_t launch_mxfp4_quantize(int dt, int64_t rows, int D, const void* x, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t stream);
 
 // --------------------------------------------------------------------- top-k
 // Largest score row that one workgroup selects from in LDS.

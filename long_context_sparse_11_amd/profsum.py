@@ -47,7 +47,9 @@ UNIT_KERNELS = {
 }
 WORKLOAD_NAME = {"csa64k": "csa_decode_64k", "csa1m": "csa_decode_1m",
                  "hca1m": "hca_decode_1m", "prefill": "csa_prefill_4k_on_60k",
-                 "csa64k_pro": "csa_decode_64k_v4pro"}
+                 "csa64k_pro": "csa_decode_64k_v4pro",
+                 "csa64k_fp4": "csa_decode_64k_mxfp4_keys",
+                 "csa1m_fp4": "csa_decode_1m_mxfp4_keys"}
 
 
 def bench_cmd(workload, steps):

@@ -21,6 +21,12 @@ shared K=V head, RoPE on the last 64 channels, indexer 64 heads x 128, top-k
   hca1m      bf16, HCA decode, batch 16 at position 1,048,575, 8,192 entries
   csa1m      bf16, CSA decode, batch 8 at position 1,048,575, 262,144 entries,
              indexer keys with 10% of rows scaled by 4 (heavy-tailed mixture)
+  csa64k_fp4, csa1m_fp4
+             as csa64k / csa1m with the indexer keys stored in MX FP4: code
+             bytes drawn uniformly (every E2M1 code equally likely) and scale
+             bytes uniformly from 125..127 (block scales 1/4, 1/2, 1), the
+             heavy rows of csa1m_fp4 with scale bytes 2 higher (x4).  They
+             are drawn as stored bytes: nothing here quantizes.
 """
 from __future__ import annotations
 
@@ -144,6 +150,8 @@ DECODE = {  # m, batch, pool entries, heavy-tailed indexer keys
     "csa64k_pro": (4, 4, 16384, False),
     "csa1m": (4, 8, 262144, True),
     "hca1m": (128, 16, 8192, False),
+    "csa64k_fp4": (4, 4, 16384, False),
+    "csa1m_fp4": (4, 8, 262144, True),
 }
 
 
@@ -195,7 +203,10 @@ def decode(kind: str, seed: int = 0, B: int | None = None, N: int | None = None,
     d["bias_b"] = dr("bias_b", (m, D), 0.02)
     bf("q_idx", (B, 1, Hi, Di))
     d["w_idx"] = dr("w_idx", (B, 1, Hi), 0.02)
-    if "k_idx" not in skip:
+    if kind.endswith("_fp4"):
+        if "k_idx" not in skip:
+            d["k_codes"], d["k_scales"] = fp4_keys(dr, B, N, Di, ht)
+    elif "k_idx" not in skip:
         kk = dr("k_idx", (B, N, Di))
         if ht:  # exactly floor(0.1 N) rows per sequence scaled by 4
             prng = dr.rng("heavy_rows")
@@ -209,6 +220,21 @@ def decode(kind: str, seed: int = 0, B: int | None = None, N: int | None = None,
     d["ibias_a"] = dr("ibias_a", (m, Di), 0.02)
     d["ibias_b"] = dr("ibias_b", (m, Di), 0.02)
     return d
+
+
+def fp4_keys(dr, B, N, Di, heavy_tail):
+    """MX FP4 indexer keys as stored bytes: codes [B, N, Di/2] uniform over
+    all bytes, scale bytes [B, N, Di/32] uniform over 125..127; with
+    ``heavy_tail`` exactly floor(0.1 N) rows per sequence get scale bytes 2
+    higher (their values x4)."""
+    codes = dr.rng("k_codes").integers(0, 256, size=(B, N, Di // 2), dtype=np.uint8)
+    scales = dr.rng("k_scales").integers(125, 128, size=(B, N, Di // 32), dtype=np.uint8)
+    if heavy_tail:
+        prng = dr.rng("heavy_rows")
+        n_heavy = int(0.1 * N)
+        for b in range(B):
+            scales[b, prng.permutation(N)[:n_heavy]] += np.uint8(2)
+    return codes, scales
 
 
 def prefill(seed: int = 0, Tq: int = 4096, prefix: int = 15360, skip=()):

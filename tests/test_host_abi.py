@@ -33,7 +33,8 @@ def test_header_declares_the_four_calls():
     for n in ("csa_compress", "csa_compress_batch", "csa_index_topk", "csa_index_scores",
               "csa_decode_index_topk", "csa_sparse_attn", "hca_attn",
               "csa_compress_ws_bytes", "csa_index_topk_ws_bytes", "csa_attn_ws_bytes",
-              "csa_status_string"):
+              "csa_status_string", "csa_quantize_mxfp4", "csa_index_topk_mxfp4",
+              "csa_index_scores_mxfp4", "csa_decode_index_topk_mxfp4"):
         assert n in names
 
 
@@ -144,6 +145,40 @@ def test_decode_index_topk_validation(lib):
     assert call([key, _job(D=512, rope_dims=64)]) == CSA_ERR_ARG   # rope, no positions
     assert call([key, kv], ws=N, wsb=0) == CSA_ERR_WORKSPACE
     assert call([key, kv], B=0) == CSA_OK                       # nothing to do
+
+
+def test_mxfp4_validation(lib):
+    """MX FP4 entry points reject bad arguments before any launch."""
+    q = lib.csa_quantize_mxfp4
+    assert q(7, 4, 128, P, P, P, N) == CSA_ERR_ARG            # dtype
+    assert q(1, 4, 48, P, P, P, N) == CSA_ERR_ARG             # not whole 32-channel blocks
+    assert q(1, -1, 128, P, P, P, N) == CSA_ERR_ARG
+    assert q(1, 4, 128, N, P, P, N) == CSA_ERR_ARG
+    assert q(1, 0, 128, N, N, N, N) == CSA_OK                 # nothing to do
+    assert q(0, 1 << 36, 128, P, P, P, N) == CSA_ERR_UNSUPPORTED
+
+    def topk(Di=128, ks=P, ws=P, wsb=1 << 30, B=2, N_cap=64):
+        return lib.csa_index_topk_mxfp4(B, 1, 64, Di, N_cap, 16, 4, P, P, P, ks, P, P, P, N, N,
+                                        ws, wsb, N)
+    assert topk(Di=100) == CSA_ERR_ARG
+    assert topk(ks=N) == CSA_ERR_ARG
+    assert topk(ws=N, wsb=0) == CSA_ERR_WORKSPACE
+    assert topk(B=0) == CSA_OK
+    sc = lib.csa_index_scores_mxfp4
+    assert sc(2, 1, 64, 100, 64, 4, P, P, P, P, P, P, P, N) == CSA_ERR_ARG
+    assert sc(2, 1, 64, 128, 64, 4, P, P, P, N, P, P, P, N) == CSA_ERR_ARG
+
+    from long_context_sparse_11_amd.binding import CompressJob
+    def dec(jobs, Tq=1, kc=P, ks=P):
+        arr = (CompressJob * len(jobs))(*jobs)
+        return lib.csa_decode_index_topk_mxfp4(1, Tq, 64, 128, 64, 16, 4, 1, P,
+                                               ctypes.cast(arr, ctypes.c_void_p), len(jobs), P,
+                                               P, kc, ks, P, P, P, N, N, P, 1 << 30, N)
+    key, kv = _job(D=128, out=None), _job(D=512, out_bstride=64 * 512)
+    assert dec([_job(D=128), kv]) == CSA_ERR_ARG               # the key job takes no out
+    assert dec([key, kv], kc=N) == CSA_ERR_ARG
+    assert dec([key, kv], ks=N) == CSA_ERR_ARG
+    assert dec([key, kv], Tq=8) == CSA_ERR_UNSUPPORTED         # only the fused launch writes FP4
 
 
 def test_compress_job_layout_matches_c():
