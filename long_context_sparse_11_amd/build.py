@@ -30,7 +30,8 @@ FLAGS = [
 # attention keeps its output accumulators in ordinary VGPRs (MFMA VGPR form):
 # the online-softmax rescale touches them with VALU ops, and the AGPR form
 # made the allocator shuttle them between register files on every tile
-SOURCE_FLAGS = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+SOURCE_FLAGS = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+                "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _run(cmd):

@@ -82,6 +82,11 @@ __device__ __forceinline__ void load_head_weights(const float* wp, int lane, flo
     for (int r = 0; r < 16; ++r) wv[mt][r] = wp[mt * 32 + 8 * (r >> 2) + 4 * g + (r & 3)];
 }
 
+// ReLU as an integer max of the float's bits (negative floats are negative
+// integers): one instruction, where fmaxf adds a canonicalisation of the
+// MFMA result first.  -0 maps to +0.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 __device__ __forceinline__ float tile_score(const bf16x8_t (&qa)[2][8], const bf16x8_t (&kb)[8],
                                             const float (&wv)[2][16]) {
   f32x16_t c0 = {}, c1 = {};
@@ -92,9 +97,9 @@ __device__ __forceinline__ float tile_score(const bf16x8_t (&qa)[2][8], const bf
   }
   float sc = 0.f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) sc += wv[0][r] * fmaxf(c0[r], 0.f);
+  for (int r = 0; r < 16; ++r) sc += wv[0][r] * relu(c0[r]);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) sc += wv[1][r] * fmaxf(c1[r], 0.f);
+  for (int r = 0; r < 16; ++r) sc += wv[1][r] * relu(c1[r]);
   // the other half of the heads sits in lane l ^ 32: v_permlane32_swap (a
   // VALU move, no LDS round trip)
   const uint32_t u = __float_as_uint(sc);
@@ -396,18 +401,42 @@ void index_decode(IndexArgs a, int tiles_per_wave, int chunks, FreshJobs f) {
     if (tile < tile_end) score(tile, k0);
     return;
   }
-  // two key buffers in turn: the next tile's loads are in flight while the
-  // current tile is scored, with no register copy between them
-  KeyTile<FP4> k1;
-  while (tile < tile_end) {
-    const int t1 = tile + 4;
-    if (t1 < tile_end) load(t1, k1);
-    score(tile, k0);
-    if (t1 >= tile_end) break;
-    const int t2 = t1 + 4;
-    if (t2 < tile_end) load(t2, k0);
-    score(t1, k1);
-    tile = t2;
+  if constexpr (FP4) {
+    // An MX FP4 tile is a quarter of a bf16 one, so one tile ahead would keep
+    // too few bytes in flight to cover the memory latency: a ring of four
+    // tiles keeps three ahead (as many bytes as the bf16 kernel's one).  The
+    // refills are unconditional (past the chunk they re-read its last tile,
+    // never scored), so the waits before each tile count exactly.
+    if (tile >= tile_end) return;
+    const int last = tile_end - 1;
+    KeyTile<true> r[4];
+    r[0] = k0;
+#pragma unroll
+    for (int i = 1; i < 4; ++i) load(min(tile + 4 * i, last), r[i]);
+    for (;;) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tl = tile + 4 * i;
+        if (tl >= tile_end) return;
+        score(tl, r[i]);
+        load(min(tl + 16, last), r[i]);
+      }
+      tile += 16;
+    }
+  } else {
+    // two key buffers in turn: the next tile's loads are in flight while the
+    // current tile is scored, with no register copy between them
+    KeyTile<false> k1;
+    while (tile < tile_end) {
+      const int t1 = tile + 4;
+      if (t1 < tile_end) load(t1, k1);
+      score(tile, k0);
+      if (t1 >= tile_end) break;
+      const int t2 = t1 + 4;
+      if (t2 < tile_end) load(t2, k0);
+      score(t1, k1);
+      tile = t2;
+    }
   }
 }
 
@@ -510,6 +539,18 @@ __global__ __launch_bounds__(512) void index_prefill(IndexArgs a) {
 
 bool index_uses_mfma(const IndexArgs& a) { return a.dt == 1 && a.Hi == 64 && a.Di == 128; }
 
+// Tiles of 32 keys per wave for the decode kernel.  bf16 keys: ~1.5k
+// workgroups in flight, enough to cover 256 CUs several times with bytes in
+// flight.  MX FP4 keys are a quarter of the bytes and the kernel is bound by
+// its per-tile work, so one round of ~512 workgroups (two per CU) spreads the
+// workgroup prologue (query to LDS and registers) over the most tiles.
+static int decode_tiles_per_wave(const IndexArgs& a) {
+  const int64_t keys = (int64_t)a.B * a.Tq * a.N_cap;
+  const int64_t per = (a.ks ? 512LL : 1536LL) * 128;
+  const int tpw = (int)((keys + per - 1) / per);
+  return max(1, min(tpw, 32));
+}
+
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream) {
   const int queries = a.B * a.Tq;
   if (queries == 0 || a.N_cap == 0) return hipSuccess;
@@ -522,10 +563,7 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream) {
       else
         hipLaunchKernelGGL(index_prefill<false>, grid, dim3(512), 0, stream, a);
     } else {
-      // ~1.5k workgroups in flight: enough to cover 256 CUs several times
-      const int64_t keys = (int64_t)queries * a.N_cap;
-      int tpw = (int)((keys + 1536LL * 128 - 1) / (1536LL * 128));
-      tpw = max(1, min(tpw, 32));
+      const int tpw = decode_tiles_per_wave(a);
       const int chunk = 4 * tpw * 32;
       const int chunks = (a.N_cap + chunk - 1) / chunk;
       dim3 grid(chunks * queries);
@@ -573,9 +611,7 @@ bool index_fresh_fused(const IndexArgs& a, const FreshJobs& f) {
 hipError_t launch_index_fresh(const IndexArgs& a, const FreshJobs& f, hipStream_t stream) {
   const int queries = a.B * a.Tq;
   if (queries == 0) return hipSuccess;
-  const int64_t keys = (int64_t)queries * a.N_cap;
-  int tpw = (int)((keys + 1536LL * 128 - 1) / (1536LL * 128));
-  tpw = max(1, min(tpw, 32));
+  const int tpw = decode_tiles_per_wave(a);
   const int chunk = 4 * tpw * 32;
   const int chunks = (a.N_cap + chunk - 1) / chunk;
   dim3 grid(chunks * queries + f.n_jobs * a.B);

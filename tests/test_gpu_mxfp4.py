@@ -120,10 +120,12 @@ def _check_fp4_index(q, w, codes, scales, n_ent, q_pos0, K, m):
 
 @pytest.mark.parametrize("kind,B,N,n_ent", [("csa64k_fp4", 2, 5000, [5000, 3001]),
                                             ("csa64k_fp4", 3, 700, [700, 513, 0]),
-                                            ("csa1m_fp4", 2, 40000, [40000, 39999])])
+                                            ("csa1m_fp4", 2, 40000, [40000, 39999]),
+                                            ("csa1m_fp4", 2, 262144, [262144, 200001])])
 def test_index_mxfp4_decode(kind, B, N, n_ent):
     """Decode shapes (the streaming MFMA kernel; 40,000 entries take the
-    two-level select), heavy-tailed scales in csa1m_fp4."""
+    two-level select; 2 x 262,144 entries give each wave several tiles, the
+    ring of tiles in flight), heavy-tailed scales in csa1m_fp4."""
     d = synth.decode(kind, 3, B=B, N=N, skip=("pool", "q", "win"))
     n_ent = np.array(n_ent, np.int32)
     q_pos0 = 4 * n_ent.astype(np.int64) - 1
@@ -175,7 +177,7 @@ def _near_rule(x, s):
 
 @pytest.mark.parametrize("N,Tq,n_ent,key_norm_rope", [
     (2000, 1, [2000, 1995], False), (20000, 3, [20000, 20000, 7000], True),
-    (700, 1, [700, 0], False)])
+    (700, 1, [700, 0], False), (262144, 1, [262144, 131071], False)])
 def test_decode_index_topk_mxfp4_fused(N, Tq, n_ent, key_norm_rope):
     """The decode step with FP4 indexer keys: the closing block's key is
     pooled, quantized and written to row n_entries-1 of the codes and scales
