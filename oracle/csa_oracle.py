@@ -420,6 +420,8 @@ def hca_attn(q, pool, n_entries, m, win, win_pos0, W, sink, q_pos0, scale,
 # (the one whose lowest bit is 0); the scaled value is below 8, so the top
 # grid value 6 also takes everything in [6, 8).  The sign bit is set for
 # x < 0.  Packing: channel 2i in the low nibble of byte i.
+# Parity unpinned against the pages (they print no FP4 value): the format is
+# a reading; the functions below are pinned to its definition.
 E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
 MX_BLOCK = 32
 
