@@ -12,7 +12,9 @@ attention with the sink.  Other workloads
 16, context 1,048,576: compress + hca_attn), prefill (CSA chunk of 4,096
 queries on a 61,440-token prefix), csa64k_pro (V4-Pro attention: 128 heads,
 top-1024), csa64k_fp4 / csa1m_fp4 (as csa64k / csa1m with the indexer keys
-stored in MX FP4; the fresh key is quantized inside the step).
+stored in MX FP4; the fresh key is quantized inside the step), swa
+(sliding-window-only layers, batch 16: the new token's window row, then
+attention over the 128-token window alone).
 
 Timing: inputs resident in HBM; the step is captured once per input copy in
 a HIP graph and replayed; enough copies of the inputs are rotated that no
@@ -51,7 +53,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="csa64k",
                    choices=["csa64k", "csa1m", "hca1m", "prefill", "csa64k_pro", "csa64k_fp4",
-                            "csa1m_fp4"])
+                            "csa1m_fp4", "swa"])
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
     p.add_argument("--no-cpu", action="store_true")
@@ -91,6 +93,13 @@ class Step:
                                     dtype=torch.uint8, device="cuda")
             n = L.csa_attn_ws_bytes(B, 1, g["H"], D, K + W)
             self.ws_a = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+        elif kind == "swa":
+            W = g["W"]
+            self.out = torch.empty_like(g["q"])
+            self.pool0 = torch.empty((B, 0, D), dtype=torch.bfloat16, device="cuda")
+            self.idx0 = torch.empty((B, 1, 0), dtype=torch.int32, device="cuda")
+            n = L.csa_attn_ws_bytes(B, 1, g["H"], D, W)
+            self.ws_a = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
         elif kind == "hca1m":
             N, W = g["N"], g["W"]
             self.out = torch.empty_like(g["q"])
@@ -119,7 +128,7 @@ class Step:
         work: the indexer scoring (CSA; one kernel, the scoring half of
         index_topk) or the whole HCA attention call (attention + split merge)."""
         g, L = self.g, self.L
-        if self.kind == "hca1m":
+        if self.kind in ("hca1m", "swa"):
             return self.calls()[1]
         if not hasattr(self, "scores"):
             B, Tq, N = g["B"], g["Tq"], g["N"]
@@ -175,6 +184,20 @@ class Step:
                                                           g["q_pos0"], rope_dims=g["R"],
                                                           out=self.out, ws=self.ws_a)),
             ]
+        if kind == "swa":
+            D, W, win = g["D"], g["W"], g["win"]
+            return [
+                # the new token's window row (m = 1), written over the last
+                # row of the window, then attention over the window alone
+                ("window_row", lambda: L.csa_compress(g["kv"], 1, gain=g["gain"],
+                                                      rope_dims=g["R"], pos0=g["q_pos0"],
+                                                      out=win[:, W - 1:], out_bstride=W * D,
+                                                      ws=self.cws(g["kv"], 1, False))),
+                ("sparse_attn", lambda: L.csa_sparse_attn(g["q"], self.pool0, self.idx0, win,
+                                                          g["win_pos0"], W, g["sink"],
+                                                          g["q_pos0"], rope_dims=g["R"],
+                                                          out=self.out, ws=self.ws_a)),
+            ]
         if kind == "hca1m":
             N, D, m = g["N"], g["D"], g["m"]
             pool = g["pool"]
@@ -217,6 +240,8 @@ def make_inputs(kind):
     from long_context_sparse_11_amd import synth
     if kind == "prefill":
         d = synth.prefill(0)
+    elif kind == "swa":
+        d = synth.swa_decode(0)
     else:
         d = synth.decode(kind, 0)
     return d
@@ -254,6 +279,11 @@ def algorithmic(kind, d):
         out["bytes"] = {"compress_index_topk": comp + idx_bytes, "sparse_attn": attn_bytes}
         out["flops"] = {"compress_index_topk": B * 2 * Hi * Di * N,
                         "sparse_attn": B * 4 * H * D * rows}
+    elif kind == "swa":
+        attn = B * (W * D * bf + 2 * H * D * bf)
+        out["bytes"] = {"window_row": B * 2 * D * bf, "sparse_attn": attn}
+        out["flops"] = {"sparse_attn": B * 4 * H * D * W}
+        out["sparse_attn"] = {"bytes": attn, "flops": out["flops"]["sparse_attn"]}
     elif kind == "hca1m":
         N = d["N"]
         comp = B * (2 * m * D * bf + D * bf)
@@ -283,10 +313,12 @@ def algorithmic(kind, d):
 DOMINANT_KERNELS = {
     "index_scores": ["index_decode<false, *> (decode) / index_prefill (prefill)"],
     "hca_attn": ["attn_hs<false, true, 4>", "attn_combine<bf16>"],
+    "sparse_attn": ["attn_hs<true, *> (+ attn_combine<bf16> when split)"],
 }
 KERNEL_SOURCES = {
     "index_scores": ["indexer.hip", "common.h", "kernels.h"],
     "hca_attn": ["attn.hip", "common.h", "kernels.h"],
+    "sparse_attn": ["attn.hip", "common.h", "kernels.h"],
 }
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
@@ -357,6 +389,18 @@ def cpu_baseline(kind, d, budget_s):
             t += 1
             done += 1
         sample = f"chunk compress + {done} of {Tq} queries"
+    elif kind == "swa":
+        W = d["W"]
+        while time.perf_counter() - t0 < budget_s or done == 0:
+            bb = done % B
+            tp = int(d["q_pos0"][bb])
+            row = O.csa_compress(d["kv"].f32[bb:bb + 1], None, None, 1, gain=d["gain"],
+                                 rope_dims=d["R"], pos0=[tp])[0, 0]
+            rows = d["win"].f32[bb].astype(np.float64)
+            rows[W - 1] = row
+            O.attend(d["q"].f32[bb, 0], tp, rows, d["sink"], scale, d["R"])
+            done += 1
+        sample = f"{done} decode queries (window row + window attention per query) of batch {B}"
     else:
         b = 0
         while time.perf_counter() - t0 < budget_s or done == 0:
@@ -558,6 +602,7 @@ def main():
         "csa1m_fp4": dict(workload="csa_decode_1m_mxfp4_keys", batch=8, context=1048576,
                           entries=262144, index_key_format="mxfp4"),
         "hca1m": dict(workload="hca_decode_1m", batch=16, context=1048576, entries=8192),
+        "swa": dict(workload="swa_decode_1m", batch=16, context=1048576, entries=0),
         "prefill": dict(workload="csa_prefill_4k_on_60k", batch=1, queries=4096, context=65536,
                         entries=16384),
     }[kind]

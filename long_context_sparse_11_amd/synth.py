@@ -237,6 +237,30 @@ def fp4_keys(dr, B, N, Di, heavy_tail):
     return codes, scales
 
 
+def swa_decode(seed: int = 0, B: int = 16, ctx: int = 1 << 20):
+    """Sliding-window-only decode (the layers whose compression ratio is 0,
+    "07 The Model", "The per-layer pattern"): each sequence's new token at
+    position ctx - 1 attends to the raw window of the last W tokens and
+    nothing else.  ``win`` holds window rows for tokens ctx - W .. ctx - 1;
+    the last one is the new token's, which a step rebuilds from its KV row
+    ``kv`` (m = 1: RMSNorm with the gain, RoPE at its position).  Shapes as
+    the Flash decode workloads; no compressed entries (K = 0, N = 0)."""
+    dr = _Draw(seed, "swa")
+    F = FLASH
+    H, D, R, W = F["H"], F["D"], F["R"], F["W"]
+    d = dict(name="swa", dt="bf16", B=B, Tq=1, H=H, D=D, R=R, Hi=F["Hi"], Di=F["Di"], m=1, K=0,
+             W=W, N=0, base=10000.0, eps=1e-6,
+             q_pos0=np.full(B, ctx - 1, np.int64),
+             n_entries=np.zeros(B, np.int32),
+             win_pos0=np.full(B, ctx - W, np.int64))
+    d["q"] = Tensor(dr("q", (B, 1, H, D)), "bf16")
+    d["win"] = Tensor(dr("win", (B, W, D)), "bf16")
+    d["kv"] = Tensor(dr("kv", (B, 1, D)), "bf16")
+    d["gain"] = dr("gain", (D,), 0.02, 1.0)
+    d["sink"] = dr("sink", (H,), 0.02)
+    return d
+
+
 def prefill(seed: int = 0, Tq: int = 4096, prefix: int = 15360, skip=()):
     """CSA chunked prefill: ``Tq`` new tokens after a cached prefix of
     ``prefix`` entries (m = 4).  The chunk's compressor streams carry m extra

@@ -205,6 +205,41 @@ def test_hca_decode_1m_sampled_sequences():
 
 
 # ---------------------------------------------------------------------------
+# Sliding-window-only decode (layers with no compressed entries)
+# ---------------------------------------------------------------------------
+def test_swa_decode_window_only():
+    """The new token's window row (m = 1: RMSNorm, gain, RoPE at its
+    position) written over the window's last row, then attention over the
+    128-token window alone (no pool, K = 0), batch 16 at position 2^20 - 1."""
+    d = synth.swa_decode(0)
+    B, D, W, R = d["B"], d["D"], d["W"], d["R"]
+    win = dev(d["win"])
+    before = win.clone()
+    print(f"[swa] B={B}: window row + window attention", flush=True)
+    L.csa_compress(dev(d["kv"]), 1, gain=dev(d["gain"]), rope_dims=R, pos0=i64(d["q_pos0"]),
+                   out=win[:, W - 1:], out_bstride=W * D)
+    pool0 = torch.empty((B, 0, D), dtype=torch.bfloat16, device="cuda")
+    idx0 = torch.empty((B, 1, 0), dtype=torch.int32, device="cuda")
+    ws_a = torch.empty(max(L.csa_attn_ws_bytes(B, 1, d["H"], D, W), 1), dtype=torch.uint8,
+                       device="cuda")
+    out, lse = L.csa_sparse_attn(dev(d["q"]), pool0, idx0, win, i64(d["win_pos0"]), W,
+                                 dev(d["sink"]), i64(d["q_pos0"]), rope_dims=R, ws=ws_a,
+                                 want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(win[:, : W - 1], before[:, : W - 1])
+    wref = O.csa_compress(d["kv"].f32, None, None, 1, gain=d["gain"], rope_dims=R,
+                          pos0=d["q_pos0"])
+    _check_entries(host(win[:, W - 1]), wref[:, 0])
+    win_o = d["win"].f32.copy()   # older rows + the oracle's own new row
+    win_o[:, W - 1] = synth.Tensor(wref[:, 0].astype(np.float32), "bf16").f32
+    ro, rl = O.csa_sparse_attn(d["q"].f32, np.zeros((B, 0, D)), np.zeros((B, 1, 0), np.int64),
+                               win_o, d["win_pos0"], W, d["sink"], d["q_pos0"],
+                               1.0 / math.sqrt(D), R)
+    assert rowwise_rel_err(host(out), ro) <= TOL_BF16
+    assert np.abs(host(lse) - rl).max() <= 2e-2
+
+
+# ---------------------------------------------------------------------------
 # CSA chunked prefill (4,096 queries on a 61,440-token prefix)
 # ---------------------------------------------------------------------------
 def test_csa_prefill_sampled_queries():
