@@ -61,6 +61,7 @@ __all__ = [
     "E2M1_GRID",
     "mxfp4_quantize",
     "mxfp4_dequantize",
+    "grouped_output_projection",
 ]
 
 
@@ -470,3 +471,34 @@ def mxfp4_dequantize(codes, scales) -> np.ndarray:
     val = np.where(nib & 8, -mag, mag)
     scale = np.repeat(np.exp2(scales.astype(np.float64) - 127.0), MX_BLOCK, axis=-1)
     return val * scale
+
+
+# ---------------------------------------------------------------------------
+# Grouped low-rank output projection
+# ---------------------------------------------------------------------------
+def grouped_output_projection(o, w_a, w_b):
+    """The attention output of one token mapped to the hidden size.
+
+    [P2] section 3.3 (after eq. 26): the concatenated head outputs are too
+    wide, so the heads are split into g groups; each group's outputs,
+    concatenated, are projected to an intermediate vector, and the g
+    intermediates, concatenated, are projected to the final attention
+    output.  [P1] "What does layer 0 sliding-window attention do to p?" (the
+    grouped W_O after the head concat; Flash: 64 heads in 8 groups) and [P4]
+    "Arsitektur" (groups of heads -> a low rank per group -> hidden size).
+    Group j holds heads j*H/g .. (j+1)*H/g - 1, in head order.
+
+    o [H, D]; w_a [g, r, (H/g)*D] (group j's projection, one row per
+    intermediate channel); w_b [d, g*r] -> float64 [d].
+    """
+    o = np.asarray(o, dtype=np.float64)
+    w_a = np.asarray(w_a, dtype=np.float64)
+    w_b = np.asarray(w_b, dtype=np.float64)
+    H, D = o.shape
+    g = w_a.shape[0]
+    per = H // g
+    mids = []
+    for j in range(g):
+        x_j = o[j * per:(j + 1) * per].reshape(-1)   # the group's heads, concatenated
+        mids.append(w_a[j] @ x_j)
+    return w_b @ np.concatenate(mids)

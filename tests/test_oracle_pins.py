@@ -602,3 +602,48 @@ def test_mxfp4_error_within_half_grid_gap():
     # the block maximum keeps at least 2^(-1) of its value: scale choice sane
     amax = np.abs(x).reshape(40, 4, 32).max(-1)
     assert np.all(np.abs(d).reshape(40, 4, 32).max(-1) >= 0.5 * amax)
+
+
+# ---------------------------------------------------------------------------
+# Grouped low-rank output projection
+# ---------------------------------------------------------------------------
+def test_grouped_projection_is_block_diagonal_product():
+    """Grouping = one product with a block-diagonal first matrix over the
+    concatenated heads (scipy's block_diag builds it independently)."""
+    import scipy.linalg
+    rng = np.random.default_rng(31)
+    H, D, g, r, d = 8, 16, 4, 12, 10
+    o = rng.standard_normal((H, D))
+    w_a = rng.standard_normal((g, r, (H // g) * D))
+    w_b = rng.standard_normal((d, g * r))
+    big = scipy.linalg.block_diag(*w_a)                 # [g r, H D]
+    want = w_b @ (big @ o.reshape(-1))
+    assert np.allclose(O.grouped_output_projection(o, w_a, w_b), want, rtol=1e-12, atol=1e-12)
+
+
+def test_grouped_projection_one_group_is_two_plain_products():
+    rng = np.random.default_rng(32)
+    o = rng.standard_normal((4, 8))
+    w_a = rng.standard_normal((1, 6, 32))
+    w_b = rng.standard_normal((5, 6))
+    want = torch.tensor(w_b) @ (torch.tensor(w_a[0]) @ torch.tensor(o).reshape(-1))
+    assert np.allclose(O.grouped_output_projection(o, w_a, w_b), want.numpy(), rtol=1e-12)
+
+
+def test_grouped_projection_group_locality():
+    """Changing one head changes only its group's intermediate: with w_b
+    reading a single group's slot, heads of other groups have no effect."""
+    rng = np.random.default_rng(33)
+    H, D, g, r = 8, 4, 4, 3
+    o = rng.standard_normal((H, D))
+    w_a = rng.standard_normal((g, r, (H // g) * D))
+    w_b = np.zeros((r, g * r))
+    w_b[:, 2 * r:3 * r] = np.eye(r)                    # reads group 2 only
+    base = O.grouped_output_projection(o, w_a, w_b)
+    o2 = o.copy()
+    o2[[0, 1, 2, 3, 6, 7]] += 5.0                       # heads outside group 2 (heads 4, 5)
+    assert np.allclose(O.grouped_output_projection(o2, w_a, w_b), base, rtol=0, atol=1e-12)
+    o3 = o.copy()
+    o3[5, 1] += 1.0                                     # head 5 = second head of group 2
+    delta = O.grouped_output_projection(o3, w_a, w_b) - base
+    assert np.allclose(delta, w_a[2][:, D + 1], atol=1e-12)
