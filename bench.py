@@ -14,7 +14,9 @@ queries on a 61,440-token prefix), csa64k_pro (V4-Pro attention: 128 heads,
 top-1024), csa64k_fp4 / csa1m_fp4 (as csa64k / csa1m with the indexer keys
 stored in MX FP4; the fresh key is quantized inside the step), swa
 (sliding-window-only layers, batch 16: the new token's window row, then
-attention over the 128-token window alone).
+attention over the 128-token window alone), oproj (the grouped low-rank output
+projection of the csa64k batch's 4 tokens: 64 heads in 8 groups -> 8 x 1024
+-> 4096).
 
 Timing: inputs resident in HBM; the step is captured once per input copy in
 a HIP graph and replayed; enough copies of the inputs are rotated that no
@@ -53,7 +55,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="csa64k",
                    choices=["csa64k", "csa1m", "hca1m", "prefill", "csa64k_pro", "csa64k_fp4",
-                            "csa1m_fp4", "swa"])
+                            "csa1m_fp4", "swa", "oproj"])
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
     p.add_argument("--no-cpu", action="store_true")
@@ -93,6 +95,10 @@ class Step:
                                     dtype=torch.uint8, device="cuda")
             n = L.csa_attn_ws_bytes(B, 1, g["H"], D, K + W)
             self.ws_a = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+        elif kind == "oproj":
+            T = g["B"]
+            self.out = torch.empty((T, g["d_model"]), dtype=torch.bfloat16, device="cuda")
+            self.mid = torch.empty((T, g["G"] * g["r"]), dtype=torch.bfloat16, device="cuda")
         elif kind == "swa":
             W = g["W"]
             self.out = torch.empty_like(g["q"])
@@ -130,6 +136,8 @@ class Step:
         g, L = self.g, self.L
         if self.kind in ("hca1m", "swa"):
             return self.calls()[1]
+        if self.kind == "oproj":
+            return self.calls()[0]
         if not hasattr(self, "scores"):
             B, Tq, N = g["B"], g["Tq"], g["N"]
             self.scores = self.torch.empty((B, Tq, N), dtype=self.torch.float32, device="cuda")
@@ -184,6 +192,9 @@ class Step:
                                                           g["q_pos0"], rope_dims=g["R"],
                                                           out=self.out, ws=self.ws_a)),
             ]
+        if kind == "oproj":
+            return [("output_proj", lambda: L.csa_output_proj(g["o"], g["w_a"], g["w_b"],
+                                                              mid=self.mid, out=self.out))]
         if kind == "swa":
             D, W, win = g["D"], g["W"], g["win"]
             return [
@@ -242,6 +253,8 @@ def make_inputs(kind):
         d = synth.prefill(0)
     elif kind == "swa":
         d = synth.swa_decode(0)
+    elif kind == "oproj":
+        d = synth.oproj(0)
     else:
         d = synth.decode(kind, 0)
     return d
@@ -279,6 +292,16 @@ def algorithmic(kind, d):
         out["bytes"] = {"compress_index_topk": comp + idx_bytes, "sparse_attn": attn_bytes}
         out["flops"] = {"compress_index_topk": B * 2 * Hi * Di * N,
                         "sparse_attn": B * 4 * H * D * rows}
+    elif kind == "oproj":
+        G, r, dm = d["G"], d["r"], d["d_model"]
+        ka = (H // G) * D
+        # both weights once, the tokens' outputs in, the intermediates out and
+        # back in, the projected tokens out
+        byt = (G * r * ka + dm * G * r) * bf + B * (H * D + 2 * G * r + dm) * bf
+        fl = 2 * B * (G * r * ka + dm * G * r)
+        out["bytes"] = {"output_proj": byt}
+        out["flops"] = {"output_proj": fl}
+        out["output_proj"] = {"bytes": byt, "flops": fl}
     elif kind == "swa":
         attn = B * (W * D * bf + 2 * H * D * bf)
         out["bytes"] = {"window_row": B * 2 * D * bf, "sparse_attn": attn}
@@ -314,11 +337,13 @@ DOMINANT_KERNELS = {
     "index_scores": ["index_decode<false, *> (decode) / index_prefill (prefill)"],
     "hca_attn": ["attn_hs<false, true, 4>", "attn_combine<bf16>"],
     "sparse_attn": ["attn_hs<true, *> (+ attn_combine<bf16> when split)"],
+    "output_proj": ["proj_rows<4>", "proj_rows<8>"],
 }
 KERNEL_SOURCES = {
     "index_scores": ["indexer.hip", "common.h", "kernels.h"],
     "hca_attn": ["attn.hip", "common.h", "kernels.h"],
     "sparse_attn": ["attn.hip", "common.h", "kernels.h"],
+    "output_proj": ["oproj.hip", "common.h", "kernels.h"],
 }
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
@@ -389,6 +414,12 @@ def cpu_baseline(kind, d, budget_s):
             t += 1
             done += 1
         sample = f"chunk compress + {done} of {Tq} queries"
+    elif kind == "oproj":
+        wa, wb = d["w_a"].f32, d["w_b"].f32
+        while time.perf_counter() - t0 < budget_s or done == 0:
+            O.grouped_output_projection(d["o"].f32[done % B], wa, wb)
+            done += 1
+        sample = f"{done} tokens' projections of batch {B}"
     elif kind == "swa":
         W = d["W"]
         while time.perf_counter() - t0 < budget_s or done == 0:
@@ -603,6 +634,8 @@ def main():
                           entries=262144, index_key_format="mxfp4"),
         "hca1m": dict(workload="hca_decode_1m", batch=16, context=1048576, entries=8192),
         "swa": dict(workload="swa_decode_1m", batch=16, context=1048576, entries=0),
+        "oproj": dict(workload="output_proj_decode", batch=4, groups=8, group_rank=1024,
+                      hidden=4096),
         "prefill": dict(workload="csa_prefill_4k_on_60k", batch=1, queries=4096, context=65536,
                         entries=16384),
     }[kind]

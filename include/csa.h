@@ -285,6 +285,33 @@ int csa_decode_index_topk_mxfp4(int B, int Tq, int Hi, int Di, int N_cap, int K,
                                 void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * csa_output_proj - grouped low-rank output projection of T tokens.
+ *
+ * [P2] section 3.3 (after eq. 26): the concatenated head outputs are split
+ * into G groups, each group projected to an intermediate of r channels, and
+ * the G intermediates, concatenated, projected to the final attention output.
+ * [P1] "What does layer 0 sliding-window attention do to p?" (grouped W_O,
+ * Flash: 64 heads in 8 groups); [P4] "Arsitektur" (groups -> a low rank per
+ * group -> hidden size).  Group j holds heads j*H/G .. (j+1)*H/G - 1.
+ *
+ *   mid[t, j*r + n] = sum_k o[t, j*H/G*D + k] * w_a[j, n, k]   (rounded to bf16)
+ *   out[t, e]       = sum_c mid[t, c] * w_b[e, c]
+ *
+ *   o    [T, H, D] bf16 (attention outputs)
+ *   w_a  [G, r, (H/G)*D] bf16
+ *   w_b  [d_model, G*r] bf16
+ *   mid  [T, G*r] bf16   caller-owned intermediates (written)
+ *   out  [T, d_model] bf16
+ * float32 accumulation; two launches that stream the weights once each.
+ * Supported: 1 <= T <= 16 (decode batches), (H/G)*D a multiple of 512, G*r
+ * a multiple of 1024, r and d_model multiples of 16; else
+ * CSA_ERR_UNSUPPORTED.  CSA_ERR_ARG for nonpositive sizes, H % G != 0 or NULL
+ * pointers (T = 0 does nothing).
+ * ------------------------------------------------------------------------- */
+int csa_output_proj(int T, int H, int D, int G, int r, int d_model, const void* o,
+                    const void* w_a, const void* w_b, void* mid, void* out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * csa_sparse_attn - shared-K=V multi-query attention with a per-head sink
  * over the selected pool rows and the sliding-window rows.
  *

@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     csa_index_scores,
     csa_index_topk,
     csa_index_topk_ws_bytes,
+    csa_output_proj,
     csa_sparse_attn,
     hca_attn,
     lib,

@@ -50,6 +50,7 @@ _SIGS = {
     "csa_index_scores_mxfp4": (_c.c_int, [_c.c_int] * 6 + [_c.c_void_p] * 8),
     "csa_decode_index_topk_mxfp4": (_c.c_int, [_c.c_int] * 8 + [_c.c_void_p, _c.c_void_p, _c.c_int]
                                     + [_c.c_void_p] * 10 + [_c.c_size_t, _c.c_void_p]),
+    "csa_output_proj": (_c.c_int, [_c.c_int] * 6 + [_c.c_void_p] * 6),
     "csa_index_topk_ws_bytes": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int]),
     "csa_sparse_attn": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                    _c.c_double, _c.c_float, _c.c_void_p, _c.c_void_p, _c.c_int,
@@ -421,6 +422,28 @@ def csa_index_scores(q_idx, w_idx, k_idx, n_entries, q_pos0, m, *, out=None, str
                                 _p(k_idx), _p(n_entries), _p(q_pos0), _p(out), _stream(stream))
     _check(st, "csa_index_scores")
     return out
+
+
+def csa_output_proj(o, w_a, w_b, *, mid=None, out=None, stream=None):
+    """Grouped low-rank output projection (see include/csa.h).  o [T, H, D]
+    bf16, w_a [G, r, (H/G) D], w_b [d, G r]; returns (out [T, d], mid [T, G r])."""
+    T, H, D = o.shape
+    G, r, ka = w_a.shape
+    d = w_b.shape[0]
+    _dev(o, w_a, w_b)
+    for t in (o, w_a, w_b):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("o, w_a, w_b are contiguous bf16 tensors")
+    if ka * G != H * D or w_b.shape[1] != G * r:
+        raise ValueError("w_a must be [G, r, (H/G) D] and w_b [d, G r]")
+    if mid is None:
+        mid = torch.empty((T, G * r), dtype=torch.bfloat16, device=o.device)
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.bfloat16, device=o.device)
+    st = lib().csa_output_proj(T, H, D, G, r, d, _p(o), _p(w_a), _p(w_b), _p(mid), _p(out),
+                               _stream(stream))
+    _check(st, "csa_output_proj")
+    return out, mid
 
 
 def csa_attn_ws_bytes(B, Tq, H, D, keys_per_query):

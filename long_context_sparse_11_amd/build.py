@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
-SOURCES = ["abi.hip", "compress.hip", "indexer.hip", "topk.hip", "attn.hip", "mxfp4.hip"]
+SOURCES = ["abi.hip", "compress.hip", "indexer.hip", "topk.hip", "attn.hip", "mxfp4.hip",
+           "oproj.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

@@ -315,6 +315,18 @@ CSA_EXPORT int csa_index_scores_mxfp4(int B, int Tq, int Hi, int Di, int N_cap, 
   return status_of(launch_index_scores(ia, (hipStream_t)stream));
 }
 
+// -------------------------------------------------- grouped output projection
+CSA_EXPORT int csa_output_proj(int T, int H, int D, int G, int r, int d_model, const void* o,
+                               const void* w_a, const void* w_b, void* mid, void* out,
+                               void* stream) {
+  if (T < 0 || H <= 0 || D <= 0 || G <= 0 || r <= 0 || d_model <= 0 || H % G) return CSA_ERR_ARG;
+  if (T == 0) return CSA_OK;
+  if (!o || !w_a || !w_b || !mid || !out) return CSA_ERR_ARG;
+  OprojArgs a{T, H, D, G, r, d_model, o, w_a, w_b, mid, out};
+  if (!out_proj_supported(a)) return CSA_ERR_UNSUPPORTED;
+  return status_of(launch_out_proj(a, (hipStream_t)stream));
+}
+
 // ------------------------------------------------------------------ MX FP4
 CSA_EXPORT int csa_quantize_mxfp4(int dt, int64_t rows, int D, const void* x, uint8_t* codes,
                                   uint8_t* scales, void* stream) {

@@ -261,6 +261,22 @@ def swa_decode(seed: int = 0, B: int = 16, ctx: int = 1 << 20):
     return d
 
 
+def oproj(seed: int = 0, T: int = 4):
+    """Grouped output projection after a decode step (Flash: 64 heads x 512
+    in 8 groups, rank 1024 per group, hidden 4096): T tokens' attention
+    outputs ~N(0, 1) and weights ~N(0, 1/fan_in), bf16."""
+    dr = _Draw(seed, "oproj")
+    F = FLASH
+    H, D, G, r, dm = F["H"], F["D"], 8, 1024, 4096
+    ka = (H // G) * D
+    d = dict(name="oproj", dt="bf16", B=T, Tq=1, H=H, D=D, R=F["R"], Hi=F["Hi"], Di=F["Di"],
+             m=1, K=0, W=0, G=G, r=r, d_model=dm)
+    d["o"] = Tensor(dr("o", (T, H, D)), "bf16")
+    d["w_a"] = Tensor(dr("w_a", (G, r, ka), 1.0 / np.sqrt(ka)), "bf16")
+    d["w_b"] = Tensor(dr("w_b", (dm, G * r), 1.0 / np.sqrt(G * r)), "bf16")
+    return d
+
+
 def prefill(seed: int = 0, Tq: int = 4096, prefix: int = 15360, skip=()):
     """CSA chunked prefill: ``Tq`` new tokens after a cached prefix of
     ``prefix`` entries (m = 4).  The chunk's compressor streams carry m extra

@@ -34,7 +34,7 @@ def test_header_declares_the_four_calls():
               "csa_decode_index_topk", "csa_sparse_attn", "hca_attn",
               "csa_compress_ws_bytes", "csa_index_topk_ws_bytes", "csa_attn_ws_bytes",
               "csa_status_string", "csa_quantize_mxfp4", "csa_index_topk_mxfp4",
-              "csa_index_scores_mxfp4", "csa_decode_index_topk_mxfp4"):
+              "csa_index_scores_mxfp4", "csa_decode_index_topk_mxfp4", "csa_output_proj"):
         assert n in names
 
 
@@ -179,6 +179,18 @@ def test_mxfp4_validation(lib):
     assert dec([key, kv], kc=N) == CSA_ERR_ARG
     assert dec([key, kv], ks=N) == CSA_ERR_ARG
     assert dec([key, kv], Tq=8) == CSA_ERR_UNSUPPORTED         # only the fused launch writes FP4
+
+
+def test_output_proj_validation(lib):
+    f = lib.csa_output_proj
+    assert f(4, 64, 512, 7, 1024, 4096, P, P, P, P, P, N) == CSA_ERR_ARG     # H % G
+    assert f(4, 64, 512, 8, 0, 4096, P, P, P, P, P, N) == CSA_ERR_ARG
+    assert f(4, 64, 512, 8, 1024, 4096, P, N, P, P, P, N) == CSA_ERR_ARG
+    assert f(17, 64, 512, 8, 1024, 4096, P, P, P, P, P, N) == CSA_ERR_UNSUPPORTED  # T > 16
+    assert f(4, 64, 500, 8, 1024, 4096, P, P, P, P, P, N) == CSA_ERR_UNSUPPORTED   # (H/G) D % 512
+    assert f(4, 64, 512, 8, 1000, 4096, P, P, P, P, P, N) == CSA_ERR_UNSUPPORTED   # G r % 1024
+    assert f(4, 64, 512, 8, 1024, 4100, P, P, P, P, P, N) == CSA_ERR_UNSUPPORTED   # d % 16
+    assert f(0, 64, 512, 8, 1024, 4096, N, N, N, N, N, N) == CSA_OK
 
 
 def test_compress_job_layout_matches_c():
