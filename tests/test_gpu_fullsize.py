@@ -160,6 +160,72 @@ def _csa_decode(kind, check_b):
     return e_iso
 
 
+def _csa_decode_fp4(kind, check_b):
+    """The benchmark's FP4-key step at full size: the fused call writes the
+    KV entry (bf16) and the fresh indexer key (MX FP4) of the closing block
+    and selects over the FP4 keys.  The attention that follows reads the bf16
+    pool exactly as in the bf16 workloads (covered by their tests)."""
+    from tests.test_gpu_mxfp4 import _near_rule, _score_bound
+    d = synth.decode(kind, 0, skip=("q", "win"))
+    B, N, D, Di, m, K, R = d["B"], d["N"], d["D"], d["Di"], d["m"], d["K"], d["R"]
+    pool, kc, ks = dev(d["pool"]), dev(d["k_codes"]), dev(d["k_scales"])
+    ws_i = torch.empty(L.csa_index_topk_ws_bytes(B, 1, 64, N, K), dtype=torch.uint8, device="cuda")
+    print(f"[{kind}] B={B} N={N}: compress + index_topk (FP4 keys)", flush=True)
+    jobs = [dict(c_a=dev(d["ic_a"]), z_a=dev(d["iz_a"]), c_b=dev(d["ic_b"]), z_b=dev(d["iz_b"]),
+                 prev_c_b=dev(d["iprev_c_b"]), prev_z_b=dev(d["iprev_z_b"]),
+                 bias_a=dev(d["ibias_a"]), bias_b=dev(d["ibias_b"])),
+            dict(c_a=dev(d["c_a"]), z_a=dev(d["z_a"]), c_b=dev(d["c_b"]), z_b=dev(d["z_b"]),
+                 prev_c_b=dev(d["prev_c_b"]), prev_z_b=dev(d["prev_z_b"]),
+                 bias_a=dev(d["bias_a"]), bias_b=dev(d["bias_b"]), gain=dev(d["gain"]),
+                 rope_dims=R, out=pool)]
+    idx, _, alls = L.csa_decode_index_topk_mxfp4(
+        dev(d["q_idx"]), dev(d["w_idx"]), kc, ks, i32(d["n_entries"]), i64(d["q_pos0"]), K, m,
+        jobs, block_pos0=i64(d["block_pos0"]), ws=ws_i, want_all_scores=True)
+    torch.cuda.synchronize()
+    kv_ref = O.csa_compress(d["c_a"].f32, d["z_a"].f32, d["bias_a"], m, c_b=d["c_b"].f32,
+                            z_b=d["z_b"].f32, bias_b=d["bias_b"], prev_c_b=d["prev_c_b"].f32,
+                            prev_z_b=d["prev_z_b"].f32, gain=d["gain"], rope_dims=R,
+                            pos0=d["block_pos0"])
+    ik_ref = O.csa_compress(d["ic_a"].f32, d["iz_a"].f32, d["ibias_a"], m, c_b=d["ic_b"].f32,
+                            z_b=d["iz_b"].f32, bias_b=d["ibias_b"], prev_c_b=d["iprev_c_b"].f32,
+                            prev_z_b=d["iprev_z_b"].f32)
+    _check_entries(host(pool[:, N - 1]), kv_ref[:, 0])
+    gidx = idx.cpu().numpy().astype(np.int64)
+    gall = alls.cpu().numpy()
+    qf = d["q_idx"].f32
+    for b in range(B):
+        oc, os_ = O.mxfp4_quantize(ik_ref[b, 0])
+        near = _near_rule(ik_ref[b, 0], os_)
+        gq = O.mxfp4_dequantize(host(kc[b, N - 1]), host(ks[b, N - 1]))
+        assert np.array_equal(gq[~near], O.mxfp4_dequantize(oc, os_)[~near]), b
+    for b in check_b:
+        oc, os_ = O.mxfp4_quantize(ik_ref[b, 0])
+        codes, scales = d["k_codes"][b:b + 1].copy(), d["k_scales"][b:b + 1].copy()
+        codes[0, N - 1], scales[0, N - 1] = oc, os_
+        kb = O.mxfp4_dequantize(codes, scales)
+        ridx, rsc = O.csa_index_topk(qf[b:b + 1], d["w_idx"][b:b + 1], kb,
+                                     d["n_entries"][b:b + 1], d["q_pos0"][b:b + 1], K, m)
+        nv = O.visible_count(int(d["q_pos0"][b]), m, int(d["n_entries"][b]))
+        bound = _score_bound(qf[b, 0], d["w_idx"][b, 0], kb[0, :nv])
+        near = _near_rule(ik_ref[b, 0], os_)
+        if near.any():   # a code next to a boundary may sit one step away
+            step = 2 * np.repeat(np.exp2(os_.astype(np.float64) - 126), 32)
+            bound[nv - 1] += float(np.sum(np.abs(d["w_idx"][b, 0]) *
+                                          (np.abs(qf[b, 0]) @ np.where(near, step, 0.0))))
+        err = np.abs(gall[b, 0, :nv].astype(np.float64) - rsc[0, 0, :nv])
+        assert np.all(err <= bound), (b, float((err / bound).max()))
+        check_band(gidx[b, 0], ridx[0, 0], rsc[0, 0], nv, K, band=1e-3 if near.any() else 1e-4)
+        assert np.array_equal(gidx[b, 0], O.select_topk(gall[b, 0, :nv], nv, K)), b
+
+
+def test_csa_decode_1m_fp4_keys_sampled_sequences():
+    _csa_decode_fp4("csa1m_fp4", check_b=[0, 6])
+
+
+def test_csa_decode_64k_fp4_keys_full_step():
+    _csa_decode_fp4("csa64k_fp4", check_b=[0, 1, 2, 3])
+
+
 def test_csa_decode_64k_full_step():
     _csa_decode("csa64k", check_b=[0, 1, 2, 3])
 
