@@ -16,7 +16,8 @@ stored in MX FP4; the fresh key is quantized inside the step), swa
 (sliding-window-only layers, batch 16: the new token's window row, then
 attention over the 128-token window alone), oproj (the grouped low-rank output
 projection of the csa64k batch's 4 tokens: 64 heads in 8 groups -> 8 x 1024
--> 4096).
+-> 4096), oproj_prefill (the same projection for a 4,096-token prefill chunk: a
+tiled GEMM).
 
 Timing: inputs resident in HBM; the step is captured once per input copy in
 a HIP graph and replayed; enough copies of the inputs are rotated that no
@@ -55,7 +56,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="csa64k",
                    choices=["csa64k", "csa1m", "hca1m", "prefill", "csa64k_pro", "csa64k_fp4",
-                            "csa1m_fp4", "swa", "oproj"])
+                            "csa1m_fp4", "swa", "oproj", "oproj_prefill"])
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
     p.add_argument("--no-cpu", action="store_true")
@@ -95,7 +96,7 @@ class Step:
                                     dtype=torch.uint8, device="cuda")
             n = L.csa_attn_ws_bytes(B, 1, g["H"], D, K + W)
             self.ws_a = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
-        elif kind == "oproj":
+        elif kind in ("oproj", "oproj_prefill"):
             T = g["B"]
             self.out = torch.empty((T, g["d_model"]), dtype=torch.bfloat16, device="cuda")
             self.mid = torch.empty((T, g["G"] * g["r"]), dtype=torch.bfloat16, device="cuda")
@@ -136,7 +137,7 @@ class Step:
         g, L = self.g, self.L
         if self.kind in ("hca1m", "swa"):
             return self.calls()[1]
-        if self.kind == "oproj":
+        if self.kind in ("oproj", "oproj_prefill"):
             return self.calls()[0]
         if not hasattr(self, "scores"):
             B, Tq, N = g["B"], g["Tq"], g["N"]
@@ -192,7 +193,7 @@ class Step:
                                                           g["q_pos0"], rope_dims=g["R"],
                                                           out=self.out, ws=self.ws_a)),
             ]
-        if kind == "oproj":
+        if kind in ("oproj", "oproj_prefill"):
             return [("output_proj", lambda: L.csa_output_proj(g["o"], g["w_a"], g["w_b"],
                                                               mid=self.mid, out=self.out))]
         if kind == "swa":
@@ -255,6 +256,8 @@ def make_inputs(kind):
         d = synth.swa_decode(0)
     elif kind == "oproj":
         d = synth.oproj(0)
+    elif kind == "oproj_prefill":
+        d = synth.oproj(0, T=4096)
     else:
         d = synth.decode(kind, 0)
     return d
@@ -292,7 +295,7 @@ def algorithmic(kind, d):
         out["bytes"] = {"compress_index_topk": comp + idx_bytes, "sparse_attn": attn_bytes}
         out["flops"] = {"compress_index_topk": B * 2 * Hi * Di * N,
                         "sparse_attn": B * 4 * H * D * rows}
-    elif kind == "oproj":
+    elif kind in ("oproj", "oproj_prefill"):
         G, r, dm = d["G"], d["r"], d["d_model"]
         ka = (H // G) * D
         # both weights once, the tokens' outputs in, the intermediates out and
@@ -338,6 +341,7 @@ DOMINANT_KERNELS = {
     "hca_attn": ["attn_hs<false, true, 4>", "attn_combine<bf16>"],
     "sparse_attn": ["attn_hs<true, *> (+ attn_combine<bf16> when split)"],
     "output_proj": ["proj_rows<4>", "proj_rows<8>"],
+    "output_proj_gemm": ["proj_gemm<0>", "proj_gemm<1>"],
 }
 KERNEL_SOURCES = {
     "index_scores": ["indexer.hip", "common.h", "kernels.h"],
@@ -414,7 +418,7 @@ def cpu_baseline(kind, d, budget_s):
             t += 1
             done += 1
         sample = f"chunk compress + {done} of {Tq} queries"
-    elif kind == "oproj":
+    elif kind in ("oproj", "oproj_prefill"):
         wa, wb = d["w_a"].f32, d["w_b"].f32
         while time.perf_counter() - t0 < budget_s or done == 0:
             O.grouped_output_projection(d["o"].f32[done % B], wa, wb)
@@ -604,7 +608,7 @@ def main():
         dom_us = float(np.median(timed([(lambda i=i: steps[i % n_copies].dominant()[1]())
                                         for i in range(20)])))
     dw = work[dom]
-    if kind == "prefill":
+    if kind in ("prefill", "oproj_prefill"):
         ach = dw["flops"] / (dom_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
@@ -614,7 +618,7 @@ def main():
                 "frac": round(ach / HBM_PEAK_GBS, 4)}
     roof["traffic"] = measured_traffic(kind, dom)
     roof["kernel"] = dom
-    roof["device_kernels"] = DOMINANT_KERNELS[dom]
+    roof["device_kernels"] = DOMINANT_KERNELS["output_proj_gemm" if kind == "oproj_prefill" else dom]
     roof["algorithmic_bytes_per_launch"] = int(dw["bytes"])
     roof["algorithmic_flops_per_launch"] = int(dw["flops"])
     roof["avg_launch_us"] = round(dom_us, 2)
@@ -636,6 +640,8 @@ def main():
         "swa": dict(workload="swa_decode_1m", batch=16, context=1048576, entries=0),
         "oproj": dict(workload="output_proj_decode", batch=4, groups=8, group_rank=1024,
                       hidden=4096),
+        "oproj_prefill": dict(workload="output_proj_prefill_4k", batch=4096, groups=8,
+                              group_rank=1024, hidden=4096),
         "prefill": dict(workload="csa_prefill_4k_on_60k", batch=1, queries=4096, context=65536,
                         entries=16384),
     }[kind]

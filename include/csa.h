@@ -302,9 +302,10 @@ int csa_decode_index_topk_mxfp4(int B, int Tq, int Hi, int Di, int N_cap, int K,
  *   w_b  [d_model, G*r] bf16
  *   mid  [T, G*r] bf16   caller-owned intermediates (written)
  *   out  [T, d_model] bf16
- * float32 accumulation; two launches that stream the weights once each.
- * Supported: 1 <= T <= 16 (decode batches), (H/G)*D a multiple of 512, G*r
- * a multiple of 1024, r and d_model multiples of 16; else
+ * float32 accumulation; two launches.  Supported: T <= 16 (decode batches,
+ * the weights streamed once) with (H/G)*D a multiple of 512, G*r a multiple
+ * of 1024, r and d_model multiples of 16; or 16 < T <= 2^22 (a tiled GEMM)
+ * with (H/G)*D and G*r multiples of 64, r and d_model multiples of 128; else
  * CSA_ERR_UNSUPPORTED.  CSA_ERR_ARG for nonpositive sizes, H % G != 0 or NULL
  * pointers (T = 0 does nothing).
  * ------------------------------------------------------------------------- */

@@ -7,7 +7,8 @@
 // projected to the hidden size.
 //
 // Decode-sized token counts (T <= 16): every weight is read once, so the two
-// products stream their weights from HBM.  One kernel serves both:
+// products stream their weights from HBM (proj_rows); larger token counts
+// take a tiled GEMM (proj_gemm).  One kernel serves both:
 // y[t, g, n] = sum_k x[t, g, k] w[g, n, k] on v_mfma_f32_16x16x32_bf16 with
 // A = 16 weight rows and B = the (up to 16) tokens; the intermediates are
 // rounded to bf16 between the two launches.
@@ -83,14 +84,116 @@ __global__ __launch_bounds__(64 * NW) void proj_rows(const bf16_t* x, int64_t x_
   }
 }
 
+// ------------------------------------------------------------ many tokens
+// More than 16 tokens (prefill chunks): each weight serves many tokens, so
+// the products are ordinary GEMMs, C[t, g, n] = sum_k X[t, g, k] W[g, n, k].
+// grid (N / 128, ceil(T / 128), G), 4 waves as 2 x 2 quadrants of 64 x 64;
+// v_mfma_f32_32x32x16_bf16 (lane l: A row = token l % 32, B column = weight
+// row l % 32, K slots 8 (l / 32) .. + 7; accumulator element e of lane l is
+// token 8 (e / 4) + 4 (l / 32) + e % 4, row l % 32).  64-channel steps are
+// copied global -> registers -> LDS (double-buffered, one barrier per step);
+// the LDS row pitch of 72 bf16 (144 B) puts the 16 rows a 16-byte read
+// serves in distinct banks.
+constexpr int kGmTile = 128;
+constexpr int kGmK = 64;
+constexpr int kGmPitch = 72;
+
+// STAGE only names the launch (0: grouped product, 1: final product), so the
+// two show up apart in kernel traces.
+template <int STAGE>
+__global__ __launch_bounds__(256) void proj_gemm(const bf16_t* x, int64_t x_tstride,
+                                                 const bf16_t* w, bf16_t* y, int64_t y_tstride,
+                                                 int T, int N, int K) {
+  __shared__ __attribute__((aligned(16))) bf16_t sa[2][kGmTile * kGmPitch];  // tokens x k
+  __shared__ __attribute__((aligned(16))) bf16_t sb[2][kGmTile * kGmPitch];  // weight rows x k
+  const int g = blockIdx.z, n0 = blockIdx.x * kGmTile, t0 = blockIdx.y * kGmTile;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  // copy role: thread tid moves row tid / 2, channels 32 (tid & 1) .. + 31 of
+  // both tiles (tokens past T re-read token T - 1; never stored)
+  const int lr = tid >> 1, lk = (tid & 1) * 32;
+  const bf16_t* xa = x + (int64_t)min(t0 + lr, T - 1) * x_tstride + (int64_t)g * K + lk;
+  const bf16_t* wr = w + ((int64_t)g * N + n0 + lr) * K + lk;
+  // staging registers of one step's copy (named: arrays here went to scratch)
+  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+  auto fetch = [&](int k0) {
+    const uint4* pa = reinterpret_cast<const uint4*>(xa + k0);
+    const uint4* pb = reinterpret_cast<const uint4*>(wr + k0);
+    ra0 = pa[0]; ra1 = pa[1]; ra2 = pa[2]; ra3 = pa[3];
+    rb0 = pb[0]; rb1 = pb[1]; rb2 = pb[2]; rb3 = pb[3];
+  };
+  auto stash = [&](int buf) {
+    uint4* qa = reinterpret_cast<uint4*>(&sa[buf][lr * kGmPitch + lk]);
+    uint4* qb = reinterpret_cast<uint4*>(&sb[buf][lr * kGmPitch + lk]);
+    qa[0] = ra0; qa[1] = ra1; qa[2] = ra2; qa[3] = ra3;
+    qb[0] = rb0; qb[1] = rb1; qb[2] = rb2; qb[3] = rb3;
+  };
+  f32x16_t c00 = {}, c01 = {}, c10 = {}, c11 = {};
+  const int nk = K / kGmK;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  const int ar = lane & 31, ah = 8 * (lane >> 5);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    // unconditional: the last step re-reads itself and fills the idle buffer,
+    // which nothing reads afterwards
+    fetch(min(kt + 1, nk - 1) * kGmK);
+#pragma unroll
+    for (int ks = 0; ks < kGmK / 16; ++ks) {
+      const bf16_t* pa = &sa[buf][(wm * 64 + ar) * kGmPitch + ks * 16 + ah];
+      const bf16_t* pb = &sb[buf][(wn * 64 + ar) * kGmPitch + ks * 16 + ah];
+      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(pa);
+      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(pa + 32 * kGmPitch);
+      const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(pb);
+      const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(pb + 32 * kGmPitch);
+      c00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, c00, 0, 0, 0);
+      c01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, c01, 0, 0, 0);
+      c10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, c10, 0, 0, 0);
+      c11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, c11, 0, 0, 0);
+    }
+    // the other buffer was last read in the previous step, before its barrier
+    stash(buf ^ 1);
+    __syncthreads();
+  }
+  auto store = [&](const f32x16_t& c, int i, int j) {
+    const int n = n0 + wn * 64 + j * 32 + ar;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int t = t0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      if (t < T) y[(int64_t)t * y_tstride + (int64_t)g * N + n] = (bf16_t)f32_to_bf16(c[e]);
+    }
+  };
+  store(c00, 0, 0);
+  store(c01, 0, 1);
+  store(c10, 1, 0);
+  store(c11, 1, 1);
+}
+
 bool out_proj_supported(const OprojArgs& a) {
   const int ka = (a.H / a.G) * a.D, kb = a.G * a.r;
-  return a.T >= 1 && a.T <= kOprojMaxTokens && a.H % a.G == 0 && ka % (4 * kPjStep) == 0 &&
-         kb % (8 * kPjStep) == 0 && a.r % kPjRows == 0 && a.d % kPjRows == 0;
+  if (a.T < 1 || a.H % a.G) return false;
+  if (a.T <= kOprojMaxTokens)
+    return ka % (4 * kPjStep) == 0 && kb % (8 * kPjStep) == 0 && a.r % kPjRows == 0 &&
+           a.d % kPjRows == 0;
+  return a.T <= (1 << 22) && ka % kGmK == 0 && kb % kGmK == 0 && a.r % kGmTile == 0 &&
+         a.d % kGmTile == 0;
 }
 
 hipError_t launch_out_proj(const OprojArgs& a, hipStream_t stream) {
   const int ka = (a.H / a.G) * a.D, kb = a.G * a.r;
+  if (a.T > kOprojMaxTokens) {
+    const unsigned tt = (unsigned)((a.T + kGmTile - 1) / kGmTile);
+    hipLaunchKernelGGL(proj_gemm<0>, dim3(a.r / kGmTile, tt, a.G), dim3(256), 0, stream,
+                       (const bf16_t*)a.o, (int64_t)a.H * a.D, (const bf16_t*)a.w_a,
+                       (bf16_t*)a.mid, (int64_t)kb, a.T, a.r, ka);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(proj_gemm<1>, dim3(a.d / kGmTile, tt, 1), dim3(256), 0, stream,
+                       (const bf16_t*)a.mid, (int64_t)kb, (const bf16_t*)a.w_b, (bf16_t*)a.out,
+                       (int64_t)a.d, a.T, a.d, kb);
+    return hipGetLastError();
+  }
   // o [T, H, D] seen as [T, G, ka] (a group's heads are consecutive)
   hipLaunchKernelGGL(proj_rows<4>, dim3(a.r / kPjRows, a.G), dim3(256), 0, stream,
                      (const bf16_t*)a.o, (int64_t)a.H * a.D, (const bf16_t*)a.w_a, (bf16_t*)a.mid,

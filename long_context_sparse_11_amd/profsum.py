@@ -45,14 +45,16 @@ UNIT_KERNELS = {
     "index_scores": {"decode": ["index_decode<false,"], "prefill": ["index_prefill"]},
     "hca_attn": {"decode": ["attn_hs<false, true, 4>", "attn_combine"]},
     "sparse_attn": {"decode": ["attn_hs<true,"]},
-    "output_proj": {"decode": ["proj_rows<4>", "proj_rows<8>"]},
+    "output_proj": {"decode": ["proj_rows<4>", "proj_rows<8>"],
+                    "prefill": ["proj_gemm<0>", "proj_gemm<1>"]},
 }
 WORKLOAD_NAME = {"csa64k": "csa_decode_64k", "csa1m": "csa_decode_1m",
                  "hca1m": "hca_decode_1m", "prefill": "csa_prefill_4k_on_60k",
                  "csa64k_pro": "csa_decode_64k_v4pro",
                  "csa64k_fp4": "csa_decode_64k_mxfp4_keys",
                  "csa1m_fp4": "csa_decode_1m_mxfp4_keys",
-                 "swa": "swa_decode_1m", "oproj": "output_proj_decode"}
+                 "swa": "swa_decode_1m", "oproj": "output_proj_decode",
+                 "oproj_prefill": "output_proj_prefill_4k"}
 
 
 def bench_cmd(workload, steps):
@@ -151,9 +153,9 @@ def summarize_dirs(workload, out, logs, steps):
     w_scale = CAL_BYTES / (w_kib * 1024.0)
 
     line = _bench_line(logs["stats"]) if logs.get("stats") else None
-    dom = {"hca1m": "hca_attn", "swa": "sparse_attn",
-           "oproj": "output_proj"}.get(workload, "index_scores")
-    phase = "prefill" if workload == "prefill" else "decode"
+    dom = {"hca1m": "hca_attn", "swa": "sparse_attn", "oproj": "output_proj",
+           "oproj_prefill": "output_proj"}.get(workload, "index_scores")
+    phase = "prefill" if workload in ("prefill", "oproj_prefill") else "decode"
     parts = UNIT_KERNELS[dom][phase]
     dom_us, dom_bytes, comp = 0.0, 0.0, []
     for pat in parts:

@@ -1,7 +1,8 @@
 """GPU parity of the grouped low-rank output projection (csa_output_proj)
 against the oracle, at the Flash shape (64 heads x 512 in 8 groups, rank
 1024, hidden 4096), a V4-Pro-like shape (128 heads in 16 groups) and small
-shapes; token counts 1 .. 16 including ragged ones.  Row-wise rule per
+shapes; token counts 1 .. 16 (the weight-streaming kernel) and 40 .. 4,096
+(the tiled GEMM), ragged ones included; sampled tokens at the largest.  Row-wise rule per
 token: ||gpu - oracle||_inf / ||oracle||_inf <= 2e-2 (bf16 operands, bf16
 intermediates, float32 accumulation).
 """
@@ -23,7 +24,7 @@ def _gpu():
     L.lib()
 
 
-def _case(T, H, D, G, r, d, seed):
+def _case(T, H, D, G, r, d, seed, tokens=None):
     rng = np.random.default_rng(seed)
     ka = (H // G) * D
     o = synth.Tensor(rng.standard_normal((T, H, D)).astype(np.float32), "bf16")
@@ -33,7 +34,7 @@ def _case(T, H, D, G, r, d, seed):
     out, mid = L.csa_output_proj(dev(o), dev(w_a), dev(w_b))
     out, mid = host(out), host(mid)
     wa, wb = w_a.f32, w_b.f32
-    for t in range(T):
+    for t in (range(T) if tokens is None else tokens):
         ref = O.grouped_output_projection(o.f32[t], wa, wb)
         assert rowwise_rel_err(out[t][None], ref[None]) <= TOL_BF16, t
         # the intermediates: the grouped product alone (second matrix = I)
@@ -73,3 +74,27 @@ def test_output_proj_tokens_do_not_mix():
     b, _ = L.csa_output_proj(o2, w_a, w_b)
     keep = [0, 1, 3, 4, 5]
     assert torch.equal(a[keep], b[keep]) and not torch.equal(a[2], b[2])
+
+
+@pytest.mark.parametrize("T,tokens", [(40, None), (4096, [0, 1, 127, 128, 2049, 4095])])
+def test_output_proj_many_tokens_flash_shape(T, tokens):
+    """More than 16 tokens take the tiled GEMM (prefill chunks)."""
+    _case(T, 64, 512, 8, 1024, 4096, seed=T, tokens=tokens)
+
+
+def test_output_proj_many_tokens_small_shape_every_token():
+    """A ragged token count (300 = 2 x 128 + 44) with every token checked."""
+    _case(300, 16, 64, 2, 512, 384, seed=300)
+
+
+def test_output_proj_gemm_matches_streaming_kernel():
+    """The same 16 tokens through both kernels (the GEMM sees them among 24)
+    agree to float32 accumulation order."""
+    rng = np.random.default_rng(9)
+    H, D, G, r, d = 64, 512, 8, 1024, 4096
+    mk = lambda *s, sc=1.0: dev(synth.Tensor((rng.standard_normal(s) * sc).astype(np.float32),
+                                             "bf16"))
+    o, w_a, w_b = mk(24, H, D), mk(G, r, 4096, sc=1 / 64), mk(d, G * r, sc=1 / 90.5)
+    many, _ = L.csa_output_proj(o, w_a, w_b)
+    few, _ = L.csa_output_proj(o[:16].contiguous(), w_a, w_b)
+    assert rowwise_rel_err(host(many[:16]), host(few)) <= 1e-2

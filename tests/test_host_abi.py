@@ -186,7 +186,8 @@ def test_output_proj_validation(lib):
     assert f(4, 64, 512, 7, 1024, 4096, P, P, P, P, P, N) == CSA_ERR_ARG     # H % G
     assert f(4, 64, 512, 8, 0, 4096, P, P, P, P, P, N) == CSA_ERR_ARG
     assert f(4, 64, 512, 8, 1024, 4096, P, N, P, P, P, N) == CSA_ERR_ARG
-    assert f(17, 64, 512, 8, 1024, 4096, P, P, P, P, P, N) == CSA_ERR_UNSUPPORTED  # T > 16
+    assert f((1 << 22) + 1, 64, 512, 8, 1024, 4096, P, P, P, P, P, N) == CSA_ERR_UNSUPPORTED
+    assert f(17, 64, 512, 8, 1000, 4096, P, P, P, P, P, N) == CSA_ERR_UNSUPPORTED  # GEMM: r % 128
     assert f(4, 64, 500, 8, 1024, 4096, P, P, P, P, P, N) == CSA_ERR_UNSUPPORTED   # (H/G) D % 512
     assert f(4, 64, 512, 8, 1000, 4096, P, P, P, P, P, N) == CSA_ERR_UNSUPPORTED   # G r % 1024
     assert f(4, 64, 512, 8, 1024, 4100, P, P, P, P, P, N) == CSA_ERR_UNSUPPORTED   # d % 16
