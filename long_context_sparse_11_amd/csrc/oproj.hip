@@ -87,13 +87,21 @@ __global__ __launch_bounds__(64 * NW) void proj_rows(const bf16_t* x, int64_t x_
 // ------------------------------------------------------------ many tokens
 // More than 16 tokens (prefill chunks): each weight serves many tokens, so
 // the products are ordinary GEMMs, C[t, g, n] = sum_k X[t, g, k] W[g, n, k].
-// grid (N / 128, ceil(T / 128), G), 4 waves as 2 x 2 quadrants of 64 x 64;
+// 1-D grid over the tiles of (group, token tile, weight-row tile), 4 waves
+// as 2 x 2 quadrants of 64 x 64;
 // v_mfma_f32_32x32x16_bf16 (lane l: A row = token l % 32, B column = weight
 // row l % 32, K slots 8 (l / 32) .. + 7; accumulator element e of lane l is
 // token 8 (e / 4) + 4 (l / 32) + e % 4, row l % 32).  64-channel steps are
 // copied global -> registers -> LDS (double-buffered, one barrier per step);
 // the LDS row pitch of 72 bf16 (144 B) puts the 16 rows a 16-byte read
 // serves in distinct banks.
+//
+// Tile order.  Workgroup id goes to XCD id % 8, each XCD with its own L2, so
+// XCD x takes the contiguous range x * per .. of the logical tiles; within a
+// group, logical tiles run over 8 token tiles for each weight-row tile in
+// turn, so the workgroups an XCD runs together share their activation and
+// weight tiles through its L2 instead of fetching them from HBM each.
+constexpr int kGmSwizzle = 8;
 constexpr int kGmTile = 128;
 constexpr int kGmK = 64;
 constexpr int kGmPitch = 72;
@@ -103,10 +111,21 @@ constexpr int kGmPitch = 72;
 template <int STAGE>
 __global__ __launch_bounds__(256) void proj_gemm(const bf16_t* x, int64_t x_tstride,
                                                  const bf16_t* w, bf16_t* y, int64_t y_tstride,
-                                                 int T, int N, int K) {
+                                                 int T, int N, int K, int G) {
   __shared__ __attribute__((aligned(16))) bf16_t sa[2][kGmTile * kGmPitch];  // tokens x k
   __shared__ __attribute__((aligned(16))) bf16_t sb[2][kGmTile * kGmPitch];  // weight rows x k
-  const int g = blockIdx.z, n0 = blockIdx.x * kGmTile, t0 = blockIdx.y * kGmTile;
+  const int nt = N / kGmTile, tt = (T + kGmTile - 1) / kGmTile;
+  const int total = nt * tt * G, per = (total + 7) / 8;
+  const int logical = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (logical >= total) return;  // padding of the last XCD's range (whole workgroup)
+  const int g = logical / (nt * tt);
+  const int rest = logical - g * nt * tt;
+  const int band = rest / (kGmSwizzle * nt);          // 8 token tiles x all row tiles
+  const int first_t = band * kGmSwizzle;
+  const int rows_t = min(tt - first_t, kGmSwizzle);
+  const int in_band = rest - band * kGmSwizzle * nt;
+  const int t0 = (first_t + in_band % rows_t) * kGmTile;
+  const int n0 = (in_band / rows_t) * kGmTile;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   // copy role: thread tid moves row tid / 2, channels 32 (tid & 1) .. + 31 of
@@ -183,15 +202,20 @@ bool out_proj_supported(const OprojArgs& a) {
 hipError_t launch_out_proj(const OprojArgs& a, hipStream_t stream) {
   const int ka = (a.H / a.G) * a.D, kb = a.G * a.r;
   if (a.T > kOprojMaxTokens) {
-    const unsigned tt = (unsigned)((a.T + kGmTile - 1) / kGmTile);
-    hipLaunchKernelGGL(proj_gemm<0>, dim3(a.r / kGmTile, tt, a.G), dim3(256), 0, stream,
-                       (const bf16_t*)a.o, (int64_t)a.H * a.D, (const bf16_t*)a.w_a,
-                       (bf16_t*)a.mid, (int64_t)kb, a.T, a.r, ka);
+    const int64_t tt = (a.T + kGmTile - 1) / kGmTile;
+    // grids padded to 8 equal XCD ranges (the kernel maps and drops the rest)
+    auto grid = [&](int N, int G) {
+      const int64_t total = (int64_t)(N / kGmTile) * tt * G;
+      return dim3((unsigned)(8 * ((total + 7) / 8)));
+    };
+    hipLaunchKernelGGL(proj_gemm<0>, grid(a.r, a.G), dim3(256), 0, stream, (const bf16_t*)a.o,
+                       (int64_t)a.H * a.D, (const bf16_t*)a.w_a, (bf16_t*)a.mid, (int64_t)kb,
+                       a.T, a.r, ka, a.G);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(proj_gemm<1>, dim3(a.d / kGmTile, tt, 1), dim3(256), 0, stream,
-                       (const bf16_t*)a.mid, (int64_t)kb, (const bf16_t*)a.w_b, (bf16_t*)a.out,
-                       (int64_t)a.d, a.T, a.d, kb);
+    hipLaunchKernelGGL(proj_gemm<1>, grid(a.d, 1), dim3(256), 0, stream, (const bf16_t*)a.mid,
+                       (int64_t)kb, (const bf16_t*)a.w_b, (bf16_t*)a.out, (int64_t)a.d, a.T,
+                       a.d, kb, 1);
     return hipGetLastError();
   }
   // o [T, H, D] seen as [T, G, ka] (a group's heads are consecutive)
