@@ -347,7 +347,7 @@ KERNEL_SOURCES = {
     "index_scores": ["indexer.hip", "common.h", "kernels.h"],
     "hca_attn": ["attn.hip", "common.h", "kernels.h"],
     "sparse_attn": ["attn.hip", "common.h", "kernels.h"],
-    "output_proj": ["oproj.hip", "common.h", "kernels.h"],
+    "output_proj": ["oproj.hip", "oproj.h", "common.h", "kernels.h"],
 }
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 

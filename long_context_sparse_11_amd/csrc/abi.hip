@@ -3,6 +3,7 @@
 // call allocates, frees or synchronises.
 #include "../../include/csa.h"
 #include "kernels.h"
+#include "oproj.h"
 
 #include <math.h>
 

@@ -71,19 +71,6 @@ struct FreshJobs {
 bool index_fresh_fused(const IndexArgs& a, const FreshJobs& f);
 hipError_t launch_index_fresh(const IndexArgs& a, const FreshJobs& f, hipStream_t stream);
 
-// ---------------------------------------------------- grouped output projection
-constexpr int kOprojMaxTokens = 16;
-struct OprojArgs {
-  int T, H, D, G, r, d;
-  const void* o;     // [T, H, D] bf16
-  const void* w_a;   // [G, r, (H/G) D] bf16
-  const void* w_b;   // [d, G r] bf16
-  void* mid;         // [T, G r] bf16
-  void* out;         // [T, d] bf16
-};
-bool out_proj_supported(const OprojArgs& a);
-hipError_t launch_out_proj(const OprojArgs& a, hipStream_t stream);
-
 // ---------------------------------------------------------------- MX FP4 keys
 // rows x D values (f32 or bf16, D a multiple of 32) to MX FP4 codes
 // [rows, D/2] and scale bytes [rows, D/32].

@@ -13,6 +13,7 @@
 // A = 16 weight rows and B = the (up to 16) tokens; the intermediates are
 // rounded to bf16 between the two launches.
 #include "kernels.h"
+#include "oproj.h"
 
 namespace csa {
 
