@@ -131,7 +131,7 @@ def sink_softmax_weights(z, sink: float):
 # ---------------------------------------------------------------------------
 def compress(c_a, z_a, bias_a, m: int, *, c_b=None, z_b=None, bias_b=None,
              prev_c_b=None, prev_z_b=None, gain=None, eps: float = 1e-6,
-             rope_dims: int = 0, rope_base: float = 10000.0, pos0: int = 0,
+             rope_dims: int = 0, rope_base: float = 10000.0, pos0: int | None = None,
              overlap: bool | None = None) -> np.ndarray:
     """Compress one sequence's token streams into ceil(T/m) entries.
 
@@ -147,9 +147,12 @@ def compress(c_a, z_a, bias_a, m: int, *, c_b=None, z_b=None, bias_b=None,
 
     Entry i (tokens m*i .. m*i+m-1 relative to ``pos0``) takes stream a from
     block i and, when overlapped, stream b from block i-1 (for i == 0 the
-    b rows come from ``prev_*`` if given, otherwise block i has no b rows).
-    ``gain`` None means no RMSNorm; ``rope_dims`` 0 means no RoPE.  The entry
-    is rotated at absolute position pos0 + m*i.
+    b rows come from ``prev_*`` if given, otherwise block i has no b rows;
+    a block that starts before token m is the sequence's first and has no
+    block before it, so ``prev_*`` is not used when pos0 < m).  ``gain`` None
+    means no RMSNorm; ``rope_dims`` 0 means no RoPE.  The entry is rotated at
+    absolute position pos0 + m*i (pos0 None: positions unknown, taken as 0
+    for RoPE, and ``prev_*`` used when given).
 
     Inputs are [T, D] (``prev_*`` [m, D]; biases [m, D]; gain [D]).
     The pages print no pooled value of the real operator, so the pins are
@@ -185,7 +188,9 @@ def compress(c_a, z_a, bias_a, m: int, *, c_b=None, z_b=None, bias_b=None,
                     tok = m * (i - 1) + r
                     logits.append(z_b[tok] + bias_b[r])
                     values.append(c_b[tok])
-                elif prev_c_b is not None:
+                elif prev_c_b is not None and (pos0 is None or pos0 >= m):
+                    # the block before this chunk; a block that starts
+                    # before token m is the first and has none
                     logits.append(np.asarray(prev_z_b[r], dtype=np.float64) + bias_b[r])
                     values.append(np.asarray(prev_c_b[r], dtype=np.float64))
         L = np.stack(logits)            # [rows, D]
@@ -197,7 +202,7 @@ def compress(c_a, z_a, bias_a, m: int, *, c_b=None, z_b=None, bias_b=None,
             g = np.asarray(gain, dtype=np.float64)
             pooled = pooled / np.sqrt(np.mean(pooled * pooled) + eps) * g
         if rope_dims:
-            pooled = rope(pooled, pos0 + m * i, rope_dims, rope_base)
+            pooled = rope(pooled, (pos0 or 0) + m * i, rope_dims, rope_base)
         out[i] = pooled
     return out
 
@@ -318,7 +323,7 @@ def csa_compress(c_a, z_a, bias_a, m, *, c_b=None, z_b=None, bias_b=None,
     """Batched ``compress``: streams [B, T, D], prev [B, m, D] -> [B, ceil(T/m), D]."""
     c_a = np.asarray(c_a)
     B = c_a.shape[0]
-    pos0 = np.zeros(B, dtype=np.int64) if pos0 is None else np.asarray(pos0)
+    pos0 = None if pos0 is None else np.asarray(pos0)
     outs = []
     for b in range(B):
         outs.append(compress(
@@ -328,7 +333,7 @@ def csa_compress(c_a, z_a, bias_a, m, *, c_b=None, z_b=None, bias_b=None,
             prev_c_b=None if prev_c_b is None else prev_c_b[b],
             prev_z_b=None if prev_z_b is None else prev_z_b[b],
             gain=gain, eps=eps, rope_dims=rope_dims, rope_base=rope_base,
-            pos0=int(pos0[b]), overlap=overlap))
+            pos0=None if pos0 is None else int(pos0[b]), overlap=overlap))
     return np.stack(outs)
 
 

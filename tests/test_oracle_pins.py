@@ -647,3 +647,24 @@ def test_grouped_projection_group_locality():
     o3[5, 1] += 1.0                                     # head 5 = second head of group 2
     delta = O.grouped_output_projection(o3, w_a, w_b) - base
     assert np.allclose(delta, w_a[2][:, D + 1], atol=1e-12)
+
+
+def test_compress_first_block_has_no_previous_block():
+    """A block at the start of a sequence has no block before it: a given
+    previous stream is not pooled there ([P2] section 3.2.2, eqs. 9-12 pool
+    block i-1, which the first block lacks), while one block later it is."""
+    rng = np.random.default_rng(41)
+    m, D = 4, 8
+    ca, za, cb, zb = (rng.standard_normal((m, D)) for _ in range(4))
+    pc, pz = rng.standard_normal((m, D)), rng.standard_normal((m, D))
+    bb = 0.1 * rng.standard_normal((m, D))
+    kw = dict(c_b=cb, z_b=zb, bias_b=bb)
+    alone = O.compress(ca, za, None, m, pos0=0, **kw)
+    with_prev_at_0 = O.compress(ca, za, None, m, prev_c_b=pc, prev_z_b=pz, pos0=0, **kw)
+    with_prev_at_m = O.compress(ca, za, None, m, prev_c_b=pc, prev_z_b=pz, pos0=m, **kw)
+    assert np.array_equal(alone, with_prev_at_0)
+    assert not np.allclose(alone, with_prev_at_m)
+    # at pos0 = m the entry is the library softmax over all 2m rows
+    logits = np.concatenate([za, pz + bb])
+    wts = scipy.special.softmax(logits, axis=0)
+    assert np.allclose(with_prev_at_m[0], (wts * np.concatenate([ca, pc])).sum(0), atol=1e-12)
