@@ -66,7 +66,8 @@ typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
  * (c_a/z_a rows m*i .. m*i+m-1; a partial last block pools the rows that
  * exist) and, if overlap != 0, the previous block's m rows of stream b:
  * c_b/z_b rows m*(i-1) .. for i >= 1, prev_c_b/prev_z_b for i == 0 (when
- * prev_c_b is NULL, entry 0 has no b rows, as at the start of a sequence).
+ * prev_c_b is NULL, or the block starts before token m so no block precedes
+ * it, entry 0 has no b rows, as at the start of a sequence).
  * Logit of a row = z + bias[offset in block].  Then, if gain != NULL,
  * y = y / sqrt(mean(y^2) + eps) * gain; then, if rope_dims > 0, RoPE with
  * interleaved pairs on the last rope_dims channels at position pos0[b] + m*i
@@ -283,6 +284,45 @@ int csa_decode_index_topk_mxfp4(int B, int Tq, int Hi, int Di, int N_cap, int K,
                                 const int32_t* n_entries, const int64_t* q_pos0,
                                 int32_t* idx_out, float* score_out, float* all_scores,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Streaming decode state.
+ *
+ * [P4] "Tata letak attention mask" (the cache keeps, per layer, the raw
+ * window and the compressor's pending tokens and overlap state) and [P1]
+ * "How does CSA compress 8 tokens into 4 KV entries?" (an entry exists once
+ * its block of m tokens has closed).  A decode loop keeps every count on
+ * the device, so steps can be captured in a HIP graph and replayed with no
+ * host round trip:
+ *
+ *   - the window is a ring: row p % L_win of win holds token p; pass
+ *     win_pos0 = NULL to csa_sparse_attn / hca_attn for it (L_win >= W);
+ *   - csa_window_row writes the new token's window row into the ring;
+ *   - csa_decode_advance moves q_pos, n_entries and block_pos0 to the next
+ *     token; a block_pos0[b] of -1 tells csa_compress_batch,
+ *     csa_decode_index_topk(_mxfp4) that no block closes for sequence b at
+ *     this step (its caches are left untouched and the indexer ranks the
+ *     entries already stored).
+ * ------------------------------------------------------------------------- */
+
+/* csa_window_row - the window row of each sequence's new token, written into
+ * the ring: win[b, pos[b] % L_win] = RoPE(RMSNorm(kv[b]) * gain, pos[b])
+ * (the compressor with m = 1).
+ *   kv   [B, 1, D] dt;  gain [D] f32 or NULL (no RMSNorm);  pos [B] int64 device
+ *   win  [B, L_win, D] dt (ring)
+ * Errors as csa_compress; CSA_ERR_ARG also for L_win <= 0 or a NULL pos. */
+int csa_window_row(int dt, int B, int D, const void* kv, const float* gain, float eps,
+                   int rope_dims, double rope_base, const int64_t* pos, void* win, int L_win,
+                   void* stream);
+
+/* csa_decode_advance - one token forward for every sequence (device only):
+ * q_pos[b] += 1; with t the new q_pos[b], n_entries[b] = min((t + 1) / m,
+ * N_cap) and block_pos0[b] = t + 1 - m when the block closes at t
+ * ((t + 1) % m == 0), else -1.  Start a sequence at q_pos = -1.
+ *   q_pos, block_pos0 [B] int64;  n_entries [B] int32 (device, in place)
+ * CSA_ERR_ARG for B < 0, m <= 0, N_cap < 0 or NULL pointers. */
+int csa_decode_advance(int B, int m, int N_cap, int64_t* q_pos, int32_t* n_entries,
+                       int64_t* block_pos0, void* stream);
 
 /* ---------------------------------------------------------------------------
  * csa_output_proj - grouped low-rank output projection of T tokens.

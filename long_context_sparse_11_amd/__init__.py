@@ -11,7 +11,9 @@ from .binding import (  # noqa: F401
     csa_compress,
     csa_compress_batch,
     csa_compress_ws_bytes,
+    csa_decode_advance,
     csa_decode_index_topk,
+    csa_window_row,
     csa_decode_index_topk_mxfp4,
     csa_index_scores_mxfp4,
     csa_index_topk_mxfp4,

@@ -51,6 +51,11 @@ _SIGS = {
     "csa_decode_index_topk_mxfp4": (_c.c_int, [_c.c_int] * 8 + [_c.c_void_p, _c.c_void_p, _c.c_int]
                                     + [_c.c_void_p] * 10 + [_c.c_size_t, _c.c_void_p]),
     "csa_output_proj": (_c.c_int, [_c.c_int] * 6 + [_c.c_void_p] * 6),
+    "csa_window_row": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p,
+                                  _c.c_float, _c.c_int, _c.c_double, _c.c_void_p, _c.c_void_p,
+                                  _c.c_int, _c.c_void_p]),
+    "csa_decode_advance": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p,
+                                      _c.c_void_p, _c.c_void_p]),
     "csa_index_topk_ws_bytes": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int]),
     "csa_sparse_attn": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                    _c.c_double, _c.c_float, _c.c_void_p, _c.c_void_p, _c.c_int,
@@ -422,6 +427,32 @@ def csa_index_scores(q_idx, w_idx, k_idx, n_entries, q_pos0, m, *, out=None, str
                                 _p(k_idx), _p(n_entries), _p(q_pos0), _p(out), _stream(stream))
     _check(st, "csa_index_scores")
     return out
+
+
+def csa_window_row(kv, pos, win, *, gain=None, eps=1e-6, rope_dims=0, rope_base=10000.0,
+                   stream=None):
+    """The new token's window row written into the ring win [B, L_win, D]
+    at row pos[b] % L_win (see include/csa.h).  kv [B, 1, D]."""
+    B, _, D = kv.shape
+    _dev(kv, gain, pos, win)
+    _f32(gain), _i64(pos)
+    if win.dtype != kv.dtype or tuple(win.shape[::2]) != (B, D) or not win.is_contiguous():
+        raise ValueError("win must be a contiguous [B, L_win, D] tensor of kv's dtype")
+    st = lib().csa_window_row(_dt(kv), B, D, _p(kv), _p(gain), float(eps), int(rope_dims),
+                              float(rope_base), _p(pos), _p(win), win.shape[1], _stream(stream))
+    _check(st, "csa_window_row")
+    return win
+
+
+def csa_decode_advance(q_pos, n_entries, block_pos0, m, N_cap, *, stream=None):
+    """One token forward on the device (see include/csa.h)."""
+    _dev(q_pos, n_entries, block_pos0)
+    _i64(q_pos), _i64(block_pos0)
+    if n_entries.dtype != torch.int32:
+        raise TypeError("n_entries is int32")
+    st = lib().csa_decode_advance(q_pos.shape[0], int(m), int(N_cap), _p(q_pos), _p(n_entries),
+                                  _p(block_pos0), _stream(stream))
+    _check(st, "csa_decode_advance")
 
 
 def csa_output_proj(o, w_a, w_b, *, mid=None, out=None, stream=None):

@@ -316,6 +316,33 @@ CSA_EXPORT int csa_index_scores_mxfp4(int B, int Tq, int Hi, int Di, int N_cap, 
   return status_of(launch_index_scores(ia, (hipStream_t)stream));
 }
 
+// ------------------------------------------------------------- decode state
+CSA_EXPORT int csa_window_row(int dt, int B, int D, const void* kv, const float* gain, float eps,
+                              int rope_dims, double rope_base, const int64_t* pos, void* win,
+                              int L_win, void* stream) {
+  if (B < 0 || D <= 0 || L_win <= 0) return CSA_ERR_ARG;
+  if (B == 0) return CSA_OK;
+  if (!pos) return CSA_ERR_ARG;
+  CompressArgs a;
+  const int st = compress_args(dt, B, 1, D, 1, 0, kv, nullptr, nullptr, nullptr, nullptr, nullptr,
+                               nullptr, nullptr, gain, eps, rope_dims, rope_base, pos, win,
+                               (int64_t)L_win * D, a);
+  if (st != CSA_OK) return st == 1 ? CSA_OK : st;
+  a.ring_len = L_win;
+  a.ws_y = nullptr;
+  a.ws_bytes = 0;
+  return status_of(launch_compress(a, (hipStream_t)stream));
+}
+
+CSA_EXPORT int csa_decode_advance(int B, int m, int N_cap, int64_t* q_pos, int32_t* n_entries,
+                                  int64_t* block_pos0, void* stream) {
+  if (B < 0 || m <= 0 || N_cap < 0) return CSA_ERR_ARG;
+  if (B == 0) return CSA_OK;
+  if (!q_pos || !n_entries || !block_pos0) return CSA_ERR_ARG;
+  return status_of(launch_decode_advance(B, m, N_cap, q_pos, n_entries, block_pos0,
+                                         (hipStream_t)stream));
+}
+
 // -------------------------------------------------- grouped output projection
 CSA_EXPORT int csa_output_proj(int T, int H, int D, int G, int r, int d_model, const void* o,
                                const void* w_a, const void* w_b, void* mid, void* out,
@@ -355,7 +382,8 @@ int attn_common(AttnArgs& a, double rope_base, int keys_per_query, void* ws, siz
   if (a.B == 0 || a.Tq == 0) return CSA_OK;
   if (!a.q || !a.sink || !a.q_pos0 || !a.out) return CSA_ERR_ARG;
   if (a.N_cap > 0 && !a.pool) return CSA_ERR_ARG;
-  if (a.W > 0 && a.L_win > 0 && (!a.win || !a.win_pos0)) return CSA_ERR_ARG;
+  if (a.W > 0 && a.L_win > 0 && !a.win) return CSA_ERR_ARG;
+  if (a.W > 0 && a.L_win > 0 && !a.win_pos0 && a.L_win < a.W) return CSA_ERR_ARG;  // ring
   if (a.R < 0 || a.R > a.D || (a.R & 1) || (a.R > 0 && !(rope_base > 0.0))) return CSA_ERR_ARG;
   if (a.D > 1024 || a.H > 128 || (a.D & 1)) return CSA_ERR_UNSUPPORTED;
   a.rope_theta1 = a.R > 0 ? pow(rope_base, -2.0 / a.R) : 0.0;

@@ -35,7 +35,13 @@ __device__ __forceinline__ KeyRange key_range(const AttnArgs& a, int b, int qi, 
   k.nsel = a.csa ? a.K : visible_entries(tpos, a.m, min(a.n_entries[b], a.N_cap));
   k.nwin = 0;
   k.win_r0 = 0;
-  if (a.W > 0 && a.L_win > 0) {
+  if (a.W > 0 && a.L_win > 0 && !a.win_pos0) {  // ring: token p at row p % L_win
+    const int64_t p_lo = max((int64_t)0, tpos - a.W + 1);
+    if (tpos >= p_lo) {
+      k.nwin = (int)(tpos - p_lo + 1);
+      k.win_r0 = (int)(p_lo % a.L_win);
+    }
+  } else if (a.W > 0 && a.L_win > 0) {
     const int64_t p_lo = max((int64_t)0, tpos - a.W + 1);
     int64_t r_lo = p_lo - a.win_pos0[b];
     int64_t r_hi = tpos - a.win_pos0[b];
@@ -65,7 +71,9 @@ __device__ __forceinline__ const T* key_row(const AttnArgs& a, int b, int qi, co
     return (const T*)a.pool + ((int64_t)b * a.N_cap + s) * a.D;
   }
   valid = true;
-  return (const T*)a.win + ((int64_t)b * a.L_win + kr.win_r0 + (j - kr.nsel)) * a.D;
+  int r = kr.win_r0 + (j - kr.nsel);  // wraps only in a ring
+  if (r >= a.L_win) r -= a.L_win;
+  return (const T*)a.win + ((int64_t)b * a.L_win + r) * a.D;
 }
 
 // ------------------------------------------------------------------ generic
@@ -277,7 +285,7 @@ void attn_hs(AttnArgs a) {
     end = min(L, start + per);
   }
   const bf16_t* pool_b = (const bf16_t*)a.pool + (int64_t)b * a.N_cap * kAtD;
-  const bf16_t* win_b = (const bf16_t*)a.win + ((int64_t)b * a.L_win + kr.win_r0) * kAtD;
+  const bf16_t* win_b = (const bf16_t*)a.win + (int64_t)b * a.L_win * kAtD;
   const bf16_t* dummy = (const bf16_t*)a.q + (int64_t)qi * a.H * kAtD;  // 1 KiB always readable
 
   // A tile's 32 rows reach LDS in two steps.  resolve_tile: lane l (< 32)
@@ -297,9 +305,10 @@ void attn_hs(AttnArgs a) {
     const int jj = j0 + (lane & 31);
     const bool in_sel = jj < kr.nsel;
     const int srow = CSA ? sidx_l : jj;
-    const int wrow = jj - kr.nsel;
+    int wrow = jj - kr.nsel + kr.win_r0;  // buffer row; wraps only in a ring
+    if (wrow >= a.L_win) wrow -= a.L_win;
     const bool valid =
-        lane < 32 && jj < end && (in_sel ? (srow >= 0 && srow < a.N_cap) : wrow < kr.nwin);
+        lane < 32 && jj < end && (in_sel ? (srow >= 0 && srow < a.N_cap) : jj - kr.nsel < kr.nwin);
     const uint64_t sa = in_sel ? pool_a + (uint64_t)((int64_t)srow * (kAtD * 2))
                                : win_a + (uint64_t)((int64_t)wrow * (kAtD * 2));
     const uint64_t src = valid ? sa : dummy_a;

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a0, Compress
       const int64_t off = ((int64_t)b * a.T + (int64_t)m * (i - 1)) * D;
       cb_base = (const T*)a.c_b + off;
       zb_base = (const T*)a.z_b + off;
-    } else if (a.prev_c_b) {
+    } else if (a.prev_c_b && !(a.pos0 && pos < m)) {  // block 0 has no block before it
       nb = m;
       const int64_t off = (int64_t)b * m * D;
       cb_base = (const T*)a.prev_c_b + off;
@@ -194,11 +194,8 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a0, Compress
   }
 
   const int64_t bstride = a.out_bstride ? a.out_bstride : (int64_t)a.n_out * D;
-  int64_t ent = i;
-  if (a.rows_at) {
-    ent = (int64_t)min(a.rows_at[b], a.rows_cap) - 1;
-    if (ent < 0) return;
-  }
+  const int64_t ent = compress_out_row(a, b, i);
+  if (ent < 0) return;
   T* op = (T*)a.out + (int64_t)b * bstride + ent * D + c0;
   Elem<T>::template store<VEC>(op, y);
 }
@@ -236,7 +233,28 @@ __global__ __launch_bounds__(64) void compress_finish(CompressArgs a) {
     }
   }
   const int64_t bstride = a.out_bstride ? a.out_bstride : (int64_t)a.n_out * D;
-  Elem<T>::template store<VEC>((T*)a.out + (int64_t)b * bstride + (int64_t)i * D + c0, y);
+  const int64_t ent = compress_out_row(a, b, i);
+  if (ent < 0) return;
+  Elem<T>::template store<VEC>((T*)a.out + (int64_t)b * bstride + ent * D + c0, y);
+}
+
+// ------------------------------------------------------------ decode state
+__global__ __launch_bounds__(256) void decode_advance(int B, int m, int N_cap, int64_t* q_pos,
+                                                      int32_t* n_entries, int64_t* block_pos0) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= B) return;
+  const int64_t t = q_pos[b] + 1;
+  q_pos[b] = t;
+  const int64_t n = (t + 1) / m;
+  n_entries[b] = (int32_t)min(n, (int64_t)N_cap);
+  block_pos0[b] = ((t + 1) % m == 0) ? t + 1 - m : -1;
+}
+
+hipError_t launch_decode_advance(int B, int m, int N_cap, int64_t* q_pos, int32_t* n_entries,
+                                 int64_t* block_pos0, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_advance, dim3((B + 255) / 256), dim3(256), 0, stream, B, m, N_cap,
+                     q_pos, n_entries, block_pos0);
+  return hipGetLastError();
 }
 
 // Calls with fewer entries than this split each entry's channels, when an

@@ -149,7 +149,8 @@ __device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressAr
   const int c0 = 2 * tid;
   const bool act = c0 < D;
   const int cc = act ? c0 : 0;
-  const bool prev = j.overlap && j.prev_c_b;
+  // the previous block's stream, when there is a block before this one
+  const bool prev = j.overlap && j.prev_c_b && !(j.pos0 && j.pos0[b] < m);
   const int nr = m + (prev ? m : 0);
   const bf16_t* ca = (const bf16_t*)j.c_a + (int64_t)b * j.T * D;
   const bool hza = j.z_a != nullptr;
@@ -323,7 +324,8 @@ void index_decode(IndexArgs a, int tiles_per_wave, int chunks, FreshJobs f) {
     const int fj = f.n_jobs * a.B;
     if (id < fj) {
       const int fb = id % a.B;
-      const int row = min(a.n_entries[fb], a.N_cap) - 1;
+      const int row = compress_out_row(f.job[0], fb, 0) >= 0 ? min(a.n_entries[fb], a.N_cap) - 1
+                                                             : -1;
       if (row >= 0)
         fresh_entry(a, f.job[id / a.B], fb, row, id < a.B, reinterpret_cast<float*>(sq), sw);
       return;
@@ -375,9 +377,11 @@ void index_decode(IndexArgs a, int tiles_per_wave, int chunks, FreshJobs f) {
   for (int u = 0; u < 4; ++u) reinterpret_cast<uint4*>(sq)[threadIdx.x + 256 * u] = v[u];
   reinterpret_cast<f32x4_t*>(sw)[threadIdx.x] = wq;
   // with fresh entries the last one is scored by its compressing workgroup
-  const int n_vis = FRESH ? max(min(visible_entries(tpos, a.m, min(n_ent, a.N_cap)),
-                                    min(n_ent, a.N_cap) - 1), 0)
-                          : visible_entries(tpos, a.m, min(n_ent, a.N_cap));
+  // (a sequence whose step closes no block, negative block start, has none)
+  const bool fresh_b = FRESH && !(f.job[0].pos0 && f.job[0].pos0[b] < 0);
+  const int n_vis = fresh_b ? max(min(visible_entries(tpos, a.m, min(n_ent, a.N_cap)),
+                                      min(n_ent, a.N_cap) - 1), 0)
+                            : visible_entries(tpos, a.m, min(n_ent, a.N_cap));
   __syncthreads();
   bf16x8_t qa[2][8];
   load_query_operand(sq, lane, qa);

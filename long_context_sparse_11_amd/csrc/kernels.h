@@ -32,7 +32,22 @@ struct CompressArgs {
   // holds the codes [B, rows, D/2] bytes and out_scales the scale bytes
   // [B, rows, D/32]; out_bstride still counts channels (rows * D)
   uint8_t* out_scales;
+  // when > 0: entry i of sequence b goes to row (pos0[b] / m + i) % ring_len
+  // of out (a ring of window rows, m = 1)
+  int ring_len;
 };
+// Row of out that entry i of sequence b goes to, or -1 for none: with
+// rows_at, min(rows_at[b], rows_cap) - 1; a negative pos0[b] means no block
+// closes for b at this step (decode); with ring_len, the ring slot.
+__device__ __forceinline__ int64_t compress_out_row(const CompressArgs& a, int b, int i) {
+  if (a.pos0 && a.pos0[b] < 0) return -1;
+  if (a.rows_at) return (int64_t)min(a.rows_at[b], a.rows_cap) - 1;
+  if (a.ring_len > 0) {
+    const int64_t p = (a.pos0 ? a.pos0[b] / a.m : 0) + i;
+    return p % a.ring_len;
+  }
+  return i;
+}
 // Workspace the compressor uses for a call of this shape (0 = none); rows:
 // rows pooled per entry (m, or 2m with overlap).
 size_t compress_ws_bytes(int dt, int B, int n_out, int D, int rows);
@@ -72,6 +87,11 @@ bool index_fresh_fused(const IndexArgs& a, const FreshJobs& f);
 hipError_t launch_index_fresh(const IndexArgs& a, const FreshJobs& f, hipStream_t stream);
 
 // ---------------------------------------------------------------- MX FP4 keys
+// Decode-state advance: q_pos[b] += 1, then n_entries[b] = min((q_pos + 1)
+// / m, N_cap) and block_pos0[b] = the closing block's first token, or -1.
+hipError_t launch_decode_advance(int B, int m, int N_cap, int64_t* q_pos, int32_t* n_entries,
+                                 int64_t* block_pos0, hipStream_t stream);
+
 // rows x D values (f32 or bf16, D a multiple of 32) to MX FP4 codes
 // [rows, D/2] and scale bytes [rows, D/32].
 hipError_t launch_mxfp4_quantize(int dt, int64_t rows, int D, const void* x, uint8_t* codes,
@@ -111,6 +131,8 @@ struct AttnArgs {
   int m;                     // HCA
   const void* win;      // [B, L_win, D]
   int L_win;
+  // row r of win holds token win_pos0[b] + r; null: a ring, row p % L_win
+  // holds token p (L_win >= W)
   const int64_t* win_pos0;
   int W;
   const float* sink;    // [H]

@@ -34,7 +34,8 @@ def test_header_declares_the_four_calls():
               "csa_decode_index_topk", "csa_sparse_attn", "hca_attn",
               "csa_compress_ws_bytes", "csa_index_topk_ws_bytes", "csa_attn_ws_bytes",
               "csa_status_string", "csa_quantize_mxfp4", "csa_index_topk_mxfp4",
-              "csa_index_scores_mxfp4", "csa_decode_index_topk_mxfp4", "csa_output_proj"):
+              "csa_index_scores_mxfp4", "csa_decode_index_topk_mxfp4", "csa_output_proj",
+              "csa_window_row", "csa_decode_advance"):
         assert n in names
 
 
@@ -192,6 +193,18 @@ def test_output_proj_validation(lib):
     assert f(4, 64, 512, 8, 1000, 4096, P, P, P, P, P, N) == CSA_ERR_UNSUPPORTED   # G r % 1024
     assert f(4, 64, 512, 8, 1024, 4100, P, P, P, P, P, N) == CSA_ERR_UNSUPPORTED   # d % 16
     assert f(0, 64, 512, 8, 1024, 4096, N, N, N, N, N, N) == CSA_OK
+
+
+def test_decode_state_validation(lib):
+    wr = lib.csa_window_row
+    assert wr(1, 2, 512, P, N, 1e-6, 64, 10000.0, N, P, 16, N) == CSA_ERR_ARG     # no positions
+    assert wr(1, 2, 512, P, N, 1e-6, 64, 10000.0, P, P, 0, N) == CSA_ERR_ARG      # L_win 0
+    assert wr(1, 2, 512, N, N, 1e-6, 0, 10000.0, P, P, 16, N) == CSA_ERR_ARG      # no kv
+    assert wr(1, 0, 512, N, N, 1e-6, 0, 10000.0, N, N, 16, N) == CSA_OK
+    adv = lib.csa_decode_advance
+    assert adv(2, 0, 16, P, P, P, N) == CSA_ERR_ARG
+    assert adv(2, 4, 16, P, N, P, N) == CSA_ERR_ARG
+    assert adv(0, 4, 16, N, N, N, N) == CSA_OK
 
 
 def test_compress_job_layout_matches_c():
