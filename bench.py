@@ -16,7 +16,9 @@ stored in MX FP4; the fresh key is quantized inside the step), swa
 (sliding-window-only layers, batch 16: the new token's window row, then
 attention over the 128-token window alone), oproj (the grouped low-rank output
 projection of the csa64k batch's 4 tokens: 64 heads in 8 groups -> 8 x 1024
--> 4096), oproj_prefill (the same projection for a 4,096-token prefill chunk: a
+-> 4096), csa64k_stream (the csa64k step as a streaming loop: positions and
+entry counts advanced on the device, the new token's window row written into
+a ring by the indexer launch, a block closing every 4th step), oproj_prefill (the same projection for a 4,096-token prefill chunk: a
 tiled GEMM).
 
 Timing: inputs resident in HBM; the step is captured once per input copy in
@@ -56,7 +58,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="csa64k",
                    choices=["csa64k", "csa1m", "hca1m", "prefill", "csa64k_pro", "csa64k_fp4",
-                            "csa1m_fp4", "swa", "oproj", "oproj_prefill"])
+                            "csa1m_fp4", "swa", "oproj", "oproj_prefill", "csa64k_stream"])
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
     p.add_argument("--no-cpu", action="store_true")
@@ -66,7 +68,10 @@ def parse():
 # ---------------------------------------------------------------------------
 # workload setup
 # ---------------------------------------------------------------------------
-CSA_DECODE = ("csa64k", "csa1m", "csa64k_pro", "csa64k_fp4", "csa1m_fp4")
+CSA_DECODE = ("csa64k", "csa1m", "csa64k_pro", "csa64k_fp4", "csa1m_fp4", "csa64k_stream")
+# a streaming run starts this many entries below the 16,384-entry cache (a
+# block closes every 4th step, so 2,048 steps fit before the cache is full)
+STREAM_HEADROOM = 512
 
 
 def upload(d, torch):
@@ -96,6 +101,13 @@ class Step:
                                     dtype=torch.uint8, device="cuda")
             n = L.csa_attn_ws_bytes(B, 1, g["H"], D, K + W)
             self.ws_a = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+            if kind == "csa64k_stream":
+                # device state of the loop: the first step is token 4 n - 1
+                n0 = N - STREAM_HEADROOM
+                self.q_pos = torch.full((B,), 4 * n0 - 2, dtype=torch.int64, device="cuda")
+                self.n_ent = torch.full((B,), n0 - 1, dtype=torch.int32, device="cuda")
+                self.blk = torch.full((B,), -1, dtype=torch.int64, device="cuda")
+                self.kv = g["c_a"][:, :1].contiguous()
         elif kind in ("oproj", "oproj_prefill"):
             T = g["B"]
             self.out = torch.empty((T, g["d_model"]), dtype=torch.bfloat16, device="cuda")
@@ -164,6 +176,25 @@ class Step:
                                                              g["win_pos0"], g["W"], g["sink"],
                                                              g["q_pos0"], rope_dims=g["R"],
                                                              out=self.out, ws=self.ws_a))
+            if kind == "csa64k_stream":
+                # the key and KV entries of a closing block and the token's
+                # window row (third job, written to its ring slot) in the
+                # indexer launch
+                st = [dict(c_a=g["ic_a"], z_a=g["iz_a"], c_b=g["ic_b"], z_b=g["iz_b"],
+                           prev_c_b=g["iprev_c_b"], prev_z_b=g["iprev_z_b"],
+                           bias_a=g["ibias_a"], bias_b=g["ibias_b"], out=g["k_idx"]), kv_job,
+                      dict(c_a=self.kv, gain=g["gain"], rope_dims=g["R"], out=g["win"])]
+                return [
+                    ("advance", lambda: L.csa_decode_advance(self.q_pos, self.n_ent, self.blk,
+                                                             m, N)),
+                    ("compress_index_topk", lambda: L.csa_decode_index_topk(
+                        g["q_idx"], g["w_idx"], self.n_ent, self.q_pos, g["K"], m, st,
+                        block_pos0=self.blk, ws=self.ws_i, idx_out=self.idx)),
+                    ("sparse_attn", lambda: L.csa_sparse_attn(g["q"], pool, self.idx, g["win"],
+                                                              None, g["W"], g["sink"],
+                                                              self.q_pos, rope_dims=g["R"],
+                                                              out=self.out, ws=self.ws_a)),
+                ]
             if kind.endswith("_fp4"):
                 # indexer keys stored in MX FP4: the fresh key is quantized
                 # by the fused launch into row n_entries - 1
@@ -258,6 +289,10 @@ def make_inputs(kind):
         d = synth.oproj(0)
     elif kind == "oproj_prefill":
         d = synth.oproj(0, T=4096)
+    elif kind == "csa64k_stream":
+        # the 64K caches; the loop itself starts STREAM_HEADROOM entries lower
+        d = synth.decode("csa64k", 0)
+        d["name"] = kind
     else:
         d = synth.decode(kind, 0)
     return d
@@ -640,6 +675,9 @@ def main():
         "swa": dict(workload="swa_decode_1m", batch=16, context=1048576, entries=0),
         "oproj": dict(workload="output_proj_decode", batch=4, groups=8, group_rank=1024,
                       hidden=4096),
+        "csa64k_stream": dict(workload="csa_decode_64k_streaming", batch=4,
+                              context="63,488 upward (16,384-entry cache)", entries=15872,
+                              window="ring"),
         "oproj_prefill": dict(workload="output_proj_prefill_4k", batch=4096, groups=8,
                               group_rank=1024, hidden=4096),
         "prefill": dict(workload="csa_prefill_4k_on_60k", batch=1, queries=4096, context=65536,

@@ -192,7 +192,13 @@ size_t csa_index_topk_ws_bytes(int B, int Tq, int Hi, int N_cap, int K);
  * (one launch fewer, the fresh key scored by the workgroup that built it),
  * else as a launch of their own.
  *
- *   jobs[n_jobs]   n_jobs 1 or 2, as for csa_compress_batch with T = m:
+ *   jobs[n_jobs]   n_jobs 1 to 3.  jobs[2], if given, is the step token's
+ *                  window row (Tq = 1; the compressor with m = 1, as
+ *                  csa_window_row): c_a = kv [B, 1, D], gain, rope, no b
+ *                  streams; out = the window ring [B, L_win, D] with
+ *                  out_bstride = L_win * D; the row goes to slot
+ *                  q_pos0[b] % L_win (it runs inside the same launch).
+ *                  jobs[0..1] as for csa_compress_batch with T = m:
  *                  c_a, z_a [B, m, D]; prev_c_b, prev_z_b [B, m, D] or NULL
  *                  (overlap: the previous block's second stream; c_b, z_b
  *                  must be given and are not read); bias_a, bias_b [m, D];

@@ -191,6 +191,18 @@ def _job_array(jobs, B, T, overlap, out_shape, first_out_none=False):
     for k, j in enumerate(jobs):
         c_a, out = j["c_a"], j.get("out")
         Bj, Tj, D = c_a.shape
+        if k == 2:   # the step token's window row into its ring
+            if Tj != 1 or Bj != B or out is None or out.dim() != 3 or out.shape[0] != B \
+                    or out.shape[2] != D or not out.is_contiguous() or out.dtype != c_a.dtype:
+                raise ValueError("jobs[2]: c_a [B, 1, D] and out the ring [B, L_win, D]")
+            _dev(c_a, j.get("gain"))
+            _f32(j.get("gain"))
+            p = lambda t: t.data_ptr() if t is not None else None
+            arr[k] = CompressJob(D, p(c_a), None, None, None, None, None, None, None,
+                                 p(j.get("gain")), float(j.get("eps", 1e-6)),
+                                 int(j.get("rope_dims", 0)), float(j.get("rope_base", 10000.0)),
+                                 out.data_ptr(), out.shape[1] * D)
+            continue
         if (Bj, Tj) != (B, T) or (j.get("c_b") is not None) != overlap or c_a.dtype != jobs[0]["c_a"].dtype:
             raise ValueError("jobs must share B, T, dtype and overlap")
         ts = [j.get(n) for n in ("z_a", "c_b", "z_b", "prev_c_b", "prev_z_b", "bias_a", "bias_b", "gain")]

@@ -156,7 +156,8 @@ int index_topk_run(int dt, int B, int Tq, int Hi, int Di, int N_cap, int K, int 
     if (fused) {
       e = launch_index_fresh(ia, *fresh, s);
     } else {
-      e = fresh ? launch_compress_batch(fresh->job, fresh->n_jobs, s) : hipSuccess;
+      e = fresh ? launch_compress_batch(fresh->job, min(fresh->n_jobs, 2), s) : hipSuccess;
+      if (e == hipSuccess && fresh && fresh->n_jobs == 3) e = launch_compress(fresh->job[2], s);
       if (e == hipSuccess) e = launch_index_scores(ia, s);
     }
     if (e != hipSuccess) return CSA_ERR_HIP;
@@ -220,13 +221,25 @@ namespace {
 
 // The fresh-entry jobs of a decode step; key_codes/key_scales replace job
 // 0's output when the indexer keys are stored as MX FP4.  Returns a status.
-int decode_jobs(int dt, int B, int N_cap, int m, int overlap, const int64_t* block_pos0,
+int decode_jobs(int dt, int B, int Tq, int N_cap, int m, int overlap, const int64_t* block_pos0,
                 const csa_compress_job* jobs, int n_jobs, uint8_t* key_codes,
-                uint8_t* key_scales, const int32_t* n_entries, FreshJobs& f) {
+                uint8_t* key_scales, const int32_t* n_entries, const int64_t* q_pos0,
+                FreshJobs& f) {
   f = FreshJobs{};
   f.n_jobs = n_jobs;
   for (int k = 0; k < n_jobs; ++k) {
     const csa_compress_job& j = jobs[k];
+    if (k == 2) {  // the step token's window row: m = 1, ring slot q_pos0[b] % L_win
+      if (Tq != 1 || !q_pos0 || j.D <= 0 || j.out_bstride <= 0 || j.out_bstride % j.D)
+        return CSA_ERR_ARG;
+      const int st = compress_args(dt, B, 1, j.D, 1, 0, j.c_a, j.z_a, j.c_b, j.z_b, j.prev_c_b,
+                                   j.prev_z_b, j.bias_a, j.bias_b, j.gain, j.eps, j.rope_dims,
+                                   j.rope_base, q_pos0, j.out, j.out_bstride, f.job[2]);
+      if (st != CSA_OK) return st == 1 ? CSA_ERR_ARG : st;
+      f.job[2].ring_len = (int)(j.out_bstride / j.D);
+      f.job[2].slices = 1;
+      continue;
+    }
     const int64_t pool_stride = (int64_t)N_cap * j.D;
     if (j.out_bstride != 0 && j.out_bstride != pool_stride) return CSA_ERR_ARG;
     void* out = (k == 0 && key_codes) ? key_codes : j.out;
@@ -251,14 +264,14 @@ CSA_EXPORT int csa_decode_index_topk(int dt, int B, int Tq, int Hi, int Di, int 
                                      const int64_t* q_pos0, int32_t* idx_out, float* score_out,
                                      float* all_scores, void* ws, size_t ws_bytes,
                                      void* stream) {
-  if (n_jobs < 1 || n_jobs > 2 || !jobs) return CSA_ERR_ARG;
+  if (n_jobs < 1 || n_jobs > 3 || !jobs) return CSA_ERR_ARG;
   if (B < 0 || Tq < 0 || N_cap < 0 || m <= 0) return CSA_ERR_ARG;
   if (jobs[0].D != Di) return CSA_ERR_ARG;
   if (B == 0 || Tq == 0) return CSA_OK;
   if (N_cap == 0) return CSA_ERR_ARG;  // the fresh entries need a row
   FreshJobs f;
-  const int st = decode_jobs(dt, B, N_cap, m, overlap, block_pos0, jobs, n_jobs, nullptr, nullptr,
-                             n_entries, f);
+  const int st = decode_jobs(dt, B, Tq, N_cap, m, overlap, block_pos0, jobs, n_jobs, nullptr,
+                             nullptr, n_entries, q_pos0, f);
   if (st != CSA_OK) return st;
   return index_topk_run(dt, B, Tq, Hi, Di, N_cap, K, m, q_idx, w_idx, jobs[0].out, nullptr,
                         n_entries, q_pos0, idx_out, score_out, all_scores, ws, ws_bytes, &f,
@@ -273,15 +286,15 @@ CSA_EXPORT int csa_decode_index_topk_mxfp4(int B, int Tq, int Hi, int Di, int N_
                                            const int32_t* n_entries, const int64_t* q_pos0,
                                            int32_t* idx_out, float* score_out, float* all_scores,
                                            void* ws, size_t ws_bytes, void* stream) {
-  if (n_jobs < 1 || n_jobs > 2 || !jobs) return CSA_ERR_ARG;
+  if (n_jobs < 1 || n_jobs > 3 || !jobs) return CSA_ERR_ARG;
   if (B < 0 || Tq < 0 || N_cap < 0 || m <= 0) return CSA_ERR_ARG;
   if (jobs[0].D != Di || Di <= 0 || Di % 32) return CSA_ERR_ARG;
   if (jobs[0].out || jobs[0].out_bstride) return CSA_ERR_ARG;  // the key job writes k_codes
   if (B == 0 || Tq == 0) return CSA_OK;
   if (N_cap == 0 || !k_codes || !k_scales) return CSA_ERR_ARG;
   FreshJobs f;
-  const int st = decode_jobs(CSA_BF16, B, N_cap, m, overlap, block_pos0, jobs, n_jobs, k_codes,
-                             k_scales, n_entries, f);
+  const int st = decode_jobs(CSA_BF16, B, Tq, N_cap, m, overlap, block_pos0, jobs, n_jobs,
+                             k_codes, k_scales, n_entries, q_pos0, f);
   if (st != CSA_OK) return st;
   return index_topk_run(CSA_BF16, B, Tq, Hi, Di, N_cap, K, m, q_idx, w_idx, k_codes, k_scales,
                         n_entries, q_pos0, idx_out, score_out, all_scores, ws, ws_bytes, &f,

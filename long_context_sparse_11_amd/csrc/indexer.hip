@@ -323,11 +323,14 @@ void index_decode(IndexArgs a, int tiles_per_wave, int chunks, FreshJobs f) {
   if constexpr (FRESH) {
     const int fj = f.n_jobs * a.B;
     if (id < fj) {
-      const int fb = id % a.B;
-      const int row = compress_out_row(f.job[0], fb, 0) >= 0 ? min(a.n_entries[fb], a.N_cap) - 1
+      const int fb = id % a.B, jk = id / a.B;
+      // entries go to row n_entries - 1 (when the step closes a block); the
+      // window row (job 2) to its ring slot
+      const int row = jk == 2 ? (int)compress_out_row(f.job[2], fb, 0)
+                    : compress_out_row(f.job[0], fb, 0) >= 0 ? min(a.n_entries[fb], a.N_cap) - 1
                                                              : -1;
       if (row >= 0)
-        fresh_entry(a, f.job[id / a.B], fb, row, id < a.B, reinterpret_cast<float*>(sq), sw);
+        fresh_entry(a, f.job[jk], fb, row, id < a.B, reinterpret_cast<float*>(sq), sw);
       return;
     }
     id -= fj;
@@ -599,7 +602,7 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream) {
 namespace csa {
 
 bool index_fresh_fused(const IndexArgs& a, const FreshJobs& f) {
-  if (!index_uses_mfma(a) || a.Tq >= 8 || f.n_jobs < 1 || f.n_jobs > 2) return false;
+  if (!index_uses_mfma(a) || a.Tq >= 8 || f.n_jobs < 1 || f.n_jobs > 3) return false;
   if (f.job[0].D != a.Di) return false;
   // MX FP4 keys: the key job stores FP4 (whole 32-channel blocks), others bf16
   if ((a.ks != nullptr) != (f.job[0].out_scales != nullptr) || (a.ks && a.Di % 32)) return false;

@@ -77,8 +77,10 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
 // block per sequence, T = m) run in extra workgroups of the indexer launch
 // and write row min(n_entries[b], N_cap) - 1 of their pools; job 0 is the
 // indexer-key compressor, whose fresh entry those workgroups also score.
+// Job 2, when present, is the step token's window row (m = 1, written to its
+// ring slot, ring_len > 0).
 struct FreshJobs {
-  CompressArgs job[2];
+  CompressArgs job[3];
   int n_jobs;
 };
 // True when launch_index_fresh covers this shape (otherwise the compressors

@@ -54,7 +54,8 @@ WORKLOAD_NAME = {"csa64k": "csa_decode_64k", "csa1m": "csa_decode_1m",
                  "csa64k_fp4": "csa_decode_64k_mxfp4_keys",
                  "csa1m_fp4": "csa_decode_1m_mxfp4_keys",
                  "swa": "swa_decode_1m", "oproj": "output_proj_decode",
-                 "oproj_prefill": "output_proj_prefill_4k"}
+                 "oproj_prefill": "output_proj_prefill_4k",
+                 "csa64k_stream": "csa_decode_64k_streaming"}
 
 
 def bench_cmd(workload, steps):

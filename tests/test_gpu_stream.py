@@ -126,13 +126,14 @@ def test_decode_call_on_a_step_that_closes_no_block():
     assert np.array_equal(host(gidx)[0], host(idx2)[0])
 
 
-def test_streamed_decode_matches_the_full_history():
+@pytest.mark.parametrize("window_in_step", [False, True])
+def test_streamed_decode_matches_the_full_history(window_in_step):
     """40 tokens streamed one decode step at a time from an empty cache (B =
     2, Flash shapes, m = 4, top-4, window 16 in a ring of 16): positions and
-    counts advance on the device, each step writes its window row, closes a
-    block every m tokens (pool and key entries) and attends.  The caches and
-    every step's selection and attention match the oracle on the whole
-    history."""
+    counts advance on the device, each step writes its window row (its own
+    call, or the decode call's third job), closes a block every m tokens
+    (pool and key entries) and attends.  The caches and every step's
+    selection and attention match the oracle on the whole history."""
     rng = np.random.default_rng(50)
     B, T, m, K, W = 2, 40, 4, 4, 16
     H, D, R, Hi, Di = 64, 512, 64, 64, 128
@@ -169,6 +170,9 @@ def test_streamed_decode_matches_the_full_history():
                  prev_c_b=prev["c_b"], prev_z_b=prev["z_b"], bias_a=dev(bias["a"]),
                  bias_b=dev(bias["b"]), gain=dev(gain), rope_dims=R, out=pool)]
     kv_d, q_d, qi_d, w_d = dev(kv), dev(q), dev(q_idx), dev(w_idx)
+    kv_cur = torch.zeros((B, 1, D), dtype=torch.bfloat16, device="cuda")
+    if window_in_step:
+        jobs.append(dict(c_a=kv_cur, gain=dev(wgain), rope_dims=R, out=ring))
 
     # the oracle's caches over the full history (rounded to the caches' bf16)
     pool_ref = O.csa_compress(streams["c_a"].f32, streams["z_a"].f32, bias["a"], m,
@@ -187,7 +191,11 @@ def test_streamed_decode_matches_the_full_history():
         for n in streams:
             cur[n][:, s] = dev_s[n][:, t]
             kcur[n][:, s] = dev_k[n][:, t]
-        L.csa_window_row(kv_d[:, t:t + 1].contiguous(), q_pos, ring, gain=dev(wgain), rope_dims=R)
+        if window_in_step:
+            kv_cur.copy_(kv_d[:, t:t + 1])
+        else:
+            L.csa_window_row(kv_d[:, t:t + 1].contiguous(), q_pos, ring, gain=dev(wgain),
+                             rope_dims=R)
         idx, _, alls = L.csa_decode_index_topk(qi_d[:, t:t + 1].contiguous(),
                                                w_d[:, t:t + 1].contiguous(), n_ent, q_pos, K, m,
                                                jobs, block_pos0=blk, want_all_scores=True)
