@@ -1,6 +1,6 @@
 """rocprofv3 passes over bench.py for one workload, and their summary.
 
-    python3 -m long_context_sparse_11_amd.profsum run --workload csa64k --out gpurun_out/prof
+    python3 -m long_context_sparse_11_amd.profsum run --workload csa64k --out _prof
 
 runs, as child processes from /tmp (TMPDIR=/tmp):
 
@@ -256,7 +256,7 @@ def main():
     p = argparse.ArgumentParser()
     p.add_argument("action", choices=["run", "summarize"])
     p.add_argument("--workload", default="csa64k", choices=sorted(WORKLOAD_NAME))
-    p.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "prof"))
+    p.add_argument("--out", default=os.path.join(ROOT, "_prof"))
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--timeout", type=int, default=300)
     a = p.parse_args()

@@ -38,7 +38,7 @@ def rowwise_rel_err(got, want, axis=-1):
 
 
 def check_band(gpu_idx, ref_idx, ref_scores32, n_vis, K, band=BAND):
-    """North-star rule for one query: equal set sizes and sentinel counts; the
+    """Selection parity rule for one query: equal set sizes and sentinel counts; the
     symmetric difference holds only entries whose float32 oracle score lies
     within `band` of the oracle's K-th score.  Returns the excused count."""
     g = sorted(int(v) for v in gpu_idx if v >= 0)
