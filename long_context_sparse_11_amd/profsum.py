@@ -44,7 +44,7 @@ UNIT_KERNELS = {
     # step runs its variant with the fresh-entry workgroups, index_decode<true>
     "index_scores": {"decode": ["index_decode<false,"], "prefill": ["index_prefill"]},
     "hca_attn": {"decode": ["attn_hs<false, true, 4>", "attn_combine"]},
-    "sparse_attn": {"decode": ["attn_hs<true,"]},
+    "sparse_attn": {"decode": ["attn_hs<true,", "attn_combine"]},
     "output_proj": {"decode": ["proj_rows<4>", "proj_rows<8>"],
                     "prefill": ["proj_gemm<0>", "proj_gemm<1>"]},
 }
