@@ -96,47 +96,35 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkArgs a) {
   const int wave = tid >> 6, lane = tid & 63;
   const int K = a.K;
 
-  // ---- segment geometry
-  int query, n, base_index = 0;
+  // ---- segment geometry from the arguments alone: the scores are requested
+  // before the visible count (two dependent scalar loads) is known.  `cap`
+  // is what the segment's row holds; slots past the visible count are read
+  // (clamped into the row) and take no part.
+  int query, base_index = 0, cap;
   const float* src;
   const int32_t* src_idx = nullptr;
   if (a.mode == 2) {
     query = seg;
-    n = a.nchunks * K;
-    src = a.scores + (int64_t)query * n;
-    src_idx = a.in_idx + (int64_t)query * n;
+    cap = a.nchunks * K;
+    src = a.scores + (int64_t)query * cap;
+    src_idx = a.in_idx + (int64_t)query * cap;
   } else {
     const int c = (a.mode == 1) ? seg % a.nchunks : 0;
     query = (a.mode == 1) ? seg / a.nchunks : seg;
-    const int b = query / a.Tq;
-    const int t = query - b * a.Tq;
-    const int n_vis = visible_entries(a.q_pos0[b] + t, a.m, min(a.n_entries[b], a.N_cap));
     base_index = (a.mode == 1) ? c * a.chunk : 0;
-    n = min(max(n_vis - base_index, 0), a.mode == 1 ? a.chunk : n_vis);
+    cap = (a.mode == 1) ? min(a.chunk, a.N_cap - base_index) : a.N_cap;
     src = a.scores + (int64_t)query * a.N_cap + base_index;
   }
   int32_t* oidx = a.out_idx + (int64_t)seg * K;
   float* osc = a.out_scores ? a.out_scores + (int64_t)seg * K : nullptr;
 
-  // ---- at most K candidates: keep them all (mode 2 always has more than K)
-  if (n <= K) {
-    for (int e = tid; e < K; e += kTkThreads) {
-      const bool v = e < n;
-      oidx[e] = v ? base_index + e : -1;
-      if (osc) osc[e] = v ? src[e] : -INFINITY;
-    }
-    return;
-  }
-
-  // ---- keys in registers; every load issued before any is consumed.  A
-  // slot beyond n, or an empty candidate slot (index -1), takes no part.
+  // ---- keys in registers; every load issued before any is consumed
   uint32_t key[kTkRounds];
   int32_t vi[kTkRounds];  // candidate indices (mode 2)
-  uint32_t live = 0;      // bit i: slot i holds a key
   const int e0 = tid * kTkRounds;
+  float v[kTkRounds];
   {
-    float v[kTkRounds];
-    const bool vec = ((((uintptr_t)src) | ((uintptr_t)src_idx)) & 15) == 0 && e0 + kTkRounds <= n;
+    const bool vec = ((((uintptr_t)src) | ((uintptr_t)src_idx)) & 15) == 0 && e0 + kTkRounds <= cap;
     if (vec) {
 #pragma unroll
       for (int u = 0; u < kTkRounds / 4; ++u) {
@@ -153,20 +141,39 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkArgs a) {
     } else {
 #pragma unroll
       for (int i = 0; i < kTkRounds; ++i) {
-        const int e = e0 + i;
-        v[i] = e < n ? src[e] : 0.f;
-        vi[i] = (src_idx && e < n) ? src_idx[e] : 0;
+        const int e = min(e0 + i, cap - 1);
+        v[i] = src[e];
+        vi[i] = src_idx ? src_idx[e] : 0;
       }
     }
     if (!src_idx) {
 #pragma unroll
       for (int i = 0; i < kTkRounds; ++i) vi[i] = 0;
     }
-#pragma unroll
-    for (int i = 0; i < kTkRounds; ++i) {
-      key[i] = score_key(v[i]);
-      if (e0 + i < n && vi[i] >= 0) live |= 1u << i;
+  }
+  int n = cap;
+  if (a.mode != 2) {
+    const int b = query / a.Tq;
+    const int t = query - b * a.Tq;
+    const int n_vis = visible_entries(a.q_pos0[b] + t, a.m, min(a.n_entries[b], a.N_cap));
+    n = min(max(n_vis - base_index, 0), a.mode == 1 ? a.chunk : n_vis);
+  }
+
+  // ---- at most K candidates: keep them all (mode 2 always has more than K)
+  if (n <= K) {
+    for (int e = tid; e < K; e += kTkThreads) {
+      const bool ok = e < n;
+      oidx[e] = ok ? base_index + e : -1;
+      if (osc) osc[e] = ok ? src[e] : -INFINITY;
     }
+    return;
+  }
+  // a slot beyond n, or an empty candidate slot (index -1), takes no part
+  uint32_t live = 0;  // bit i: slot i holds a key
+#pragma unroll
+  for (int i = 0; i < kTkRounds; ++i) {
+    key[i] = score_key(v[i]);
+    if (e0 + i < n && vi[i] >= 0) live |= 1u << i;
   }
 #pragma unroll
   for (int k = 0; k < kBinsPerThread; ++k) S.hist[tid * kBinsPerThread + k] = 0;
