@@ -546,14 +546,15 @@ __global__ __launch_bounds__(512) void index_prefill(IndexArgs a) {
 
 bool index_uses_mfma(const IndexArgs& a) { return a.dt == 1 && a.Hi == 64 && a.Di == 128; }
 
-// Tiles of 32 keys per wave for the decode kernel.  bf16 keys: ~1.5k
-// workgroups in flight, enough to cover 256 CUs several times with bytes in
-// flight.  MX FP4 keys are a quarter of the bytes and the kernel is bound by
-// its per-tile work, so one round of ~512 workgroups (two per CU) spreads the
-// workgroup prologue (query to LDS and registers) over the most tiles.
+// Tiles of 32 keys per wave for the decode kernel.  Two workgroups fit a CU,
+// so a grid of whole rounds of 512 runs balanced.  bf16 keys: ~1k workgroups
+// (two rounds; at 1M, 16 tiles per wave measured 103.5 us against 109.6 for
+// 2.9 rounds of 11).  MX FP4 keys are a quarter of the bytes and the kernel
+// is bound by its per-tile work, so one round of ~512 spreads the workgroup
+// prologue (query to LDS and registers) over the most tiles.
 static int decode_tiles_per_wave(const IndexArgs& a) {
   const int64_t keys = (int64_t)a.B * a.Tq * a.N_cap;
-  const int64_t per = (a.ks ? 512LL : 1536LL) * 128;
+  const int64_t per = (a.ks ? 512LL : 1024LL) * 128;
   const int tpw = (int)((keys + per - 1) / per);
   return max(1, min(tpw, 32));
 }
