@@ -188,7 +188,7 @@ size_t csa_index_topk_ws_bytes(int B, int Tq, int Hi, int N_cap, int K);
  * the indexer's k_idx.  Then exactly csa_index_topk over k_idx.  The same
  * results as csa_compress_batch (one entry, written at row r_b) followed by
  * csa_index_topk; for bf16 with Hi = 64, Di = 128, Tq < 8, job D <= 512
- * and at most 16 pooled rows the compressors run inside the indexer launch
+ * and at most 8 pooled rows the compressors run inside the indexer launch
  * (one launch fewer, the fresh key scored by the workgroup that built it),
  * else as a launch of their own.
  *
@@ -281,7 +281,7 @@ int csa_index_scores_mxfp4(int B, int Tq, int Hi, int Di, int N_cap, int m,
  * from its quantized value).  jobs[0].out must be NULL and its out_bstride
  * 0; jobs[1] (the KV compressor, if given) writes bf16 as before.  Only the
  * fused launch writes FP4: bf16 streams, Hi = 64, Di = 128, Tq < 8, job
- * D <= 512 and at most 16 pooled rows, else CSA_ERR_UNSUPPORTED before any
+ * D <= 512 and at most 8 pooled rows, else CSA_ERR_UNSUPPORTED before any
  * launch.  Other arguments and errors as csa_decode_index_topk (dt bf16). */
 int csa_decode_index_topk_mxfp4(int B, int Tq, int Hi, int Di, int N_cap, int K, int m,
                                 int overlap, const int64_t* block_pos0,

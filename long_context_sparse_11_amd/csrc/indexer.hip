@@ -140,7 +140,11 @@ __device__ __forceinline__ void fp4_operand(const KeyTile<true>& kt, bf16x8_t (&
 // channels 2t and 2t + 1.  The entry goes to row `row` of the job's pool.
 // For the indexer-key job the entry is then scored against every query of
 // the sequence that sees it, from the bf16 value as stored.
-constexpr int kFreshMaxRows = 16;
+// 8 rows: a CSA block with its overlap (2m, m = 4) or a window row; larger
+// blocks run the compressor as a launch of its own.  The bound sizes the
+// row registers, and with it the fused kernel's occupancy (85 VGPRs at 8
+// rows, 123 at 16).
+constexpr int kFreshMaxRows = 8;
 
 __device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressArgs& j, int b,
                                             int row, bool score, float* skey, float* red) {
