@@ -250,6 +250,16 @@ def test_index_prefill_bf16(Tq, pos0):
     _check_index(q, w, k, np.array([N], np.int32), np.array([pos0]), 512, 4, SCORE_ATOL_BF16)
 
 
+@pytest.mark.parametrize("K,N", [(1, 5000), (4096, 20000), (4096, 9000), (600, 500)])
+def test_index_extreme_k(K, N):
+    """K = 1, K = 4,096 (the largest supported; with 20,000 entries through the
+    two-level select, whose candidate row is then 2 x 4,096), and K above the
+    visible count (every entry kept, -1 padding)."""
+    d = synth.decode("csa64k", 5, B=2, N=N, skip=("pool", "q", "win"))
+    _check_index(d["q_idx"], d["w_idx"], d["k_idx"], d["n_entries"], d["q_pos0"], K, d["m"],
+                 SCORE_ATOL_BF16)
+
+
 def test_index_heavy_tail_two_level_select():
     """Rows longer than one workgroup's LDS go through chunk winners + merge."""
     d = synth.decode("csa1m", 2, B=2, N=40000, skip=("pool", "q", "win"))
