@@ -607,6 +607,31 @@ def test_attn_duplicates_window_clip_and_window_only(dt):
     assert rowwise_rel_err(host(out0), ro) <= tol
 
 
+def test_attn_4096_selected_rows_many_queries():
+    """K = 4,096 selected rows + a 128-row window for 260 queries: more than
+    the 2,048 rows one multi-tile split stages, so every query takes several
+    multi-tile splits and the merge.  Sampled queries against the oracle."""
+    rng = np.random.default_rng(61)
+    H, D, R, W, K, N, Tq = 64, 512, 64, 128, 4096, 8000, 260
+    q = synth.Tensor(rng.standard_normal((1, Tq, H, D)).astype(np.float32), "bf16")
+    pool = synth.Tensor(rng.standard_normal((1, N, D)).astype(np.float32), "bf16")
+    L_win = Tq + W - 1
+    win = synth.Tensor(rng.standard_normal((1, L_win, D)).astype(np.float32), "bf16")
+    sink = (0.02 * rng.standard_normal(H)).astype(np.float32)
+    q_pos0 = np.array([40000])
+    win_pos0 = q_pos0 - W + 1
+    sel = np.sort(rng.integers(0, N, size=(1, Tq, K)), axis=-1).astype(np.int32)
+    sel[0, 7, 4000:] = -1                      # a query with empty slots
+    out, lse = L.csa_sparse_attn(dev(q), dev(pool), dev(sel), dev(win), i64(win_pos0), W,
+                                 dev(sink), i64(q_pos0), rope_dims=R, want_lse=True)
+    pairs = [(0, t) for t in (0, 7, 128, 259)]
+    ro, rl = O.csa_sparse_attn(q.f32, pool.f32, sel, win.f32, win_pos0, W, sink, q_pos0,
+                               1.0 / math.sqrt(D), R, queries=pairs)
+    for b, t in pairs:
+        assert rowwise_rel_err(host(out)[b, t], ro[b, t]) <= TOL_BF16, t
+        assert np.abs(host(lse)[b, t] - rl[b, t]).max() <= 2e-2, t
+
+
 def test_attn_csa_with_all_visible_equals_hca_on_gpu():
     rng = np.random.default_rng(8)
     B, H, D, R, m, N, W = 2, 64, 512, 64, 4, 400, 128
