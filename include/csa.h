@@ -381,7 +381,8 @@ int csa_output_proj(int T, int H, int D, int G, int r, int d_model, const void* 
  *
  *   q       [B, Tq, H, D] dt (RMS-normalised, not rotated)
  *   pool    [B, N_cap, D] dt;  idx [B, Tq, K] int32 (-1 = empty slot)
- *   win     [B, L_win, D] dt;  win_pos0 [B] int64 device (NULL iff W == 0)
+ *   win     [B, L_win, D] dt;  win_pos0 [B] int64 device, or NULL for a
+ *           ring (row p % L_win holds token p; requires L_win >= W)
  *   sink    [H] f32; q_pos0 [B] int64 device
  *   out     [B, Tq, H, D] dt;  lse [B, Tq, H] f32 natural log (may be NULL)
  *   ws      workspace of csa_attn_ws_bytes(B, Tq, H, D, K + W)
