@@ -260,6 +260,15 @@ def test_index_extreme_k(K, N):
                  SCORE_ATOL_BF16)
 
 
+def test_index_largest_supported_pool():
+    """524,288 entries with K = 512 (a 2M-token context): the largest pool the
+    two-level select takes (32 chunk winners of 512 fill the 16,384-score
+    merge row), heavy-tailed keys."""
+    d = synth.decode("csa1m", 6, B=1, N=524288, skip=("pool", "q", "win"))
+    _check_index(d["q_idx"], d["w_idx"], d["k_idx"], d["n_entries"], d["q_pos0"], d["K"], d["m"],
+                 SCORE_ATOL_BF16)
+
+
 def test_index_heavy_tail_two_level_select():
     """Rows longer than one workgroup's LDS go through chunk winners + merge."""
     d = synth.decode("csa1m", 2, B=2, N=40000, skip=("pool", "q", "win"))

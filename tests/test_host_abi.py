@@ -252,6 +252,9 @@ def _index(lib, **kw):
 
 
 def test_index_validation(lib):
+    # the two-level select's merge row holds 16,384 scores: 32 chunks of K = 512
+    assert _index(lib, N=524288 + 1) == CSA_ERR_UNSUPPORTED
+    assert _index(lib, N=524288, wsb=0, ws=N) == CSA_ERR_WORKSPACE   # supported: fails later
     assert _index(lib, K=0) == CSA_ERR_ARG
     assert _index(lib, m=0) == CSA_ERR_ARG
     assert _index(lib, B=0) == CSA_OK
