@@ -232,3 +232,66 @@ def test_streamed_decode_matches_the_full_history(window_in_step):
         assert rowwise_rel_err(host(ring)[:, p % L_win], win_ref[:, p]) <= TOL_BF16
     assert np.array_equal(host(q_pos), [T - 1, T - 1])
     assert np.array_equal(host(n_ent), [n, n])
+
+
+def test_graph_captured_streaming_step_matches_eager():
+    """One streaming step (advance, decode call with the window row as its
+    third job, attention over the ring) captured in a HIP graph and replayed
+    12 times, with eager work and synchronisation between the replays: every
+    replay equals an eager run of the same step on an identical state,
+    bitwise (positions, counts, caches, selection, output)."""
+    rng = np.random.default_rng(71)
+    B, m, K, W, H, D, R, Hi, Di, N_cap = 2, 4, 4, 16, 64, 512, 64, 64, 128, 16
+    f = lambda *s, sc=1.0: (rng.standard_normal(s) * sc).astype(np.float32)
+    bfd = lambda x: dev(synth.Tensor(x, "bf16"))
+
+    def state():
+        st = dict(q_pos=torch.full((B,), 9, dtype=torch.int64, device="cuda"),
+                  n_ent=torch.zeros(B, dtype=torch.int32, device="cuda"),
+                  blk=torch.zeros(B, dtype=torch.int64, device="cuda"),
+                  pool=torch.zeros((B, N_cap, D), dtype=torch.bfloat16, device="cuda"),
+                  kidx=torch.zeros((B, N_cap, Di), dtype=torch.bfloat16, device="cuda"),
+                  ring=torch.zeros((B, W, D), dtype=torch.bfloat16, device="cuda"),
+                  idx=torch.empty((B, 1, K), dtype=torch.int32, device="cuda"),
+                  out=torch.empty((B, 1, H, D), dtype=torch.bfloat16, device="cuda"))
+        st["ws_i"] = torch.empty(L.csa_index_topk_ws_bytes(B, 1, Hi, N_cap, K), dtype=torch.uint8,
+                                 device="cuda")
+        st["ws_a"] = torch.empty(max(L.csa_attn_ws_bytes(B, 1, H, D, K + W), 1),
+                                 dtype=torch.uint8, device="cuda")
+        return st
+
+    s_kv = {n: bfd(f(B, m, D)) for n in ("c_a", "z_a", "c_b", "z_b", "prev_c_b", "prev_z_b")}
+    s_k = {n: bfd(f(B, m, Di)) for n in ("c_a", "z_a", "c_b", "z_b", "prev_c_b", "prev_z_b")}
+    kv_row, q, qi = bfd(f(B, 1, D)), bfd(f(B, 1, H, D)), bfd(f(B, 1, Hi, Di))
+    wi, sink = dev(f(B, 1, Hi, sc=0.02)), dev(f(H, sc=0.02))
+    gain, wgain = dev(1 + f(D, sc=0.02)), dev(1 + f(D, sc=0.02))
+    bk = {n: dev(f(m, Di, sc=0.02)) for n in ("a", "b")}
+    bv = {n: dev(f(m, D, sc=0.02)) for n in ("a", "b")}
+
+    def step(st):
+        L.csa_decode_advance(st["q_pos"], st["n_ent"], st["blk"], m, N_cap)
+        jobs = [dict(**s_k, bias_a=bk["a"], bias_b=bk["b"], out=st["kidx"]),
+                dict(**s_kv, bias_a=bv["a"], bias_b=bv["b"], gain=gain, rope_dims=R,
+                     out=st["pool"]),
+                dict(c_a=kv_row, gain=wgain, rope_dims=R, out=st["ring"])]
+        L.csa_decode_index_topk(qi, wi, st["n_ent"], st["q_pos"], K, m, jobs,
+                                block_pos0=st["blk"], ws=st["ws_i"], idx_out=st["idx"])
+        L.csa_sparse_attn(q, st["pool"], st["idx"], st["ring"], None, W, sink, st["q_pos"],
+                          rope_dims=R, out=st["out"], ws=st["ws_a"])
+
+    eager, graphed = state(), state()
+    step(graphed)                     # warm-up outside the capture, mirrored eagerly
+    step(eager)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(graphed)
+    keys = ("q_pos", "n_ent", "blk", "pool", "kidx", "ring", "idx", "out")
+    for r in range(12):
+        g.replay()
+        step(eager)
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 16, device="cuda").sum()   # eager work between replays
+        for k in keys:
+            assert torch.equal(graphed[k], eager[k]), (r, k)
+    assert int(host(eager["n_ent"])[0]) >= 5 and junk is not None
