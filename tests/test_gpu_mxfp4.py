@@ -250,3 +250,35 @@ def test_decode_mxfp4_rejects_unfused_shapes():
                                       block_pos0=i64(d["block_pos0"]))
     torch.cuda.synchronize()
     assert torch.equal(kc, before)
+
+
+def test_decode_mxfp4_with_window_row_job():
+    """The FP4 decode call with the step token's window row as a third job:
+    the ring row equals csa_window_row's, and the selection and FP4 caches
+    equal those of the two-job call on the same inputs."""
+    d = _fresh_case("bf16", 3000, 1, [3000, 2999], False, seed=23)
+    B, m, K, Di, D, R = d["B"], d["m"], 512, d["Di"], d["D"], d["R"]
+    rng = np.random.default_rng(24)
+    codes, scales = _rand_fp4(rng, B, 3000, Di)
+    kv = dev(synth.Tensor(rng.standard_normal((B, 1, D)).astype(np.float32), "bf16"))
+    wgain = dev((1 + 0.02 * rng.standard_normal(D)).astype(np.float32))
+    L_win = 128
+    outs = []
+    for third in (False, True):
+        kc, ks, pool = dev(codes), dev(scales), dev(d["pool"])
+        ring = torch.zeros((B, L_win, D), dtype=torch.bfloat16, device="cuda")
+        jobs, _ = _fresh_jobs_and_refs(d, None, pool)
+        if third:
+            jobs.append(dict(c_a=kv, gain=wgain, rope_dims=R, out=ring))
+        idx, _, alls = L.csa_decode_index_topk_mxfp4(
+            dev(d["q"]), dev(d["w"]), kc, ks, i32(d["n_ent"]), i64(d["q_pos0"]), K, m, jobs,
+            block_pos0=i64(d["block_pos0"]), want_all_scores=True)
+        outs.append((idx, alls, kc, ks, pool, ring))
+    for k in (0, 2, 3, 4):   # selection and caches
+        assert torch.equal(outs[0][k], outs[1][k]), k
+    for b in range(B):       # scores of the visible entries (later columns are unspecified)
+        nv = O.visible_count(int(d["q_pos0"][b]), m, int(d["n_ent"][b]))
+        assert torch.equal(outs[0][1][b, :, :nv], outs[1][1][b, :, :nv]), b
+    ring_ref = torch.zeros((B, L_win, D), dtype=torch.bfloat16, device="cuda")
+    L.csa_window_row(kv, i64(d["q_pos0"]), ring_ref, gain=wgain, rope_dims=R)
+    assert torch.equal(outs[1][5], ring_ref)
