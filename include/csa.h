@@ -324,7 +324,9 @@ int csa_window_row(int dt, int B, int D, const void* kv, const float* gain, floa
 /* csa_decode_advance - one token forward for every sequence (device only):
  * q_pos[b] += 1; with t the new q_pos[b], n_entries[b] = min((t + 1) / m,
  * N_cap) and block_pos0[b] = t + 1 - m when the block closes at t
- * ((t + 1) % m == 0), else -1.  Start a sequence at q_pos = -1.
+ * ((t + 1) % m == 0), else -1.  Start a sequence at q_pos = -1.  N_cap
+ * must cover the whole context: once n_entries reaches it, a closing step
+ * writes its entry over row N_cap - 1.
  *   q_pos, block_pos0 [B] int64;  n_entries [B] int32 (device, in place)
  * CSA_ERR_ARG for B < 0, m <= 0, N_cap < 0 or NULL pointers. */
 int csa_decode_advance(int B, int m, int N_cap, int64_t* q_pos, int32_t* n_entries,
