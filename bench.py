@@ -368,6 +368,22 @@ def algorithmic(kind, d):
     return out
 
 
+def per_call_rate(kind, work, call_us):
+    out = {}
+    for name, us in call_us.items():
+        if us <= 0:
+            continue
+        r = {}
+        if name in work["bytes"]:
+            r["GB/s"] = round(work["bytes"][name] / (us * 1e-6) / 1e9, 1)
+        fl = work.get("flops", {}).get(name)
+        if fl and kind in ("prefill", "oproj_prefill"):
+            r["TFLOP/s"] = round(fl / (us * 1e-6) / 1e12, 1)
+        if r:
+            out[name] = r
+    return out
+
+
 # ---------------------------------------------------------------------------
 # measured HBM traffic of the dominant kernel (hardware counters, committed)
 # ---------------------------------------------------------------------------
@@ -693,6 +709,10 @@ def main():
         "data": "synthetic", "config": cfgs, "roofline": roof, "cpu_baseline": cpu,
         "device_us_per_step": round(dev_step_us, 2),
         "per_call_us": {k: round(v, 2) for k, v in call_us.items()},
+        # each call's algorithmic rate: HBM GB/s, and TFLOP/s where the call
+        # is a large contraction (the prefill indexer and attention, the
+        # prefill projection)
+        "per_call_rate": per_call_rate(kind, work, call_us),
         "step_algorithmic_bytes": int(step_bytes),
     }
     print(json.dumps(line))
