@@ -117,6 +117,15 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkArgs a) {
   }
   int32_t* oidx = a.out_idx + (int64_t)seg * K;
   float* osc = a.out_scores ? a.out_scores + (int64_t)seg * K : nullptr;
+  // an empty pool (no entry yet, N_cap = 0): nothing to read, every slot
+  // is empty; decided from the arguments before any load
+  if (cap <= 0) {
+    for (int e = tid; e < K; e += kTkThreads) {
+      oidx[e] = -1;
+      if (osc) osc[e] = -INFINITY;
+    }
+    return;
+  }
 
   // ---- keys in registers; every load issued before any is consumed
   uint32_t key[kTkRounds];

@@ -66,6 +66,8 @@ def test_workspace_sizes(lib):
     big = lib.csa_index_topk_ws_bytes(8, 1, 64, 262144, 512)
     assert big >= 8 * 262144 * 4 + 2 * 8 * 16 * 512 * 4 and big > small
     assert lib.csa_index_topk_ws_bytes(0, 1, 64, 10, 5) == 0
+    # an empty pool (N_cap = 0) needs no workspace: the call only fills -1
+    assert lib.csa_index_topk_ws_bytes(4, 1, 64, 0, 512) == 0
     # the MFMA attention splits a few long queries and needs partials
     assert lib.csa_attn_ws_bytes(16, 1, 64, 512, 8320) > 0
     assert lib.csa_attn_ws_bytes(1, 4096, 64, 512, 640) == 0   # many queries: no split
@@ -252,6 +254,8 @@ def _index(lib, **kw):
 
 
 def test_index_validation(lib):
+    assert _index(lib, N=-1) == CSA_ERR_ARG
+    assert _index(lib, N=0, wsb=0, ws=N, K=-1) == CSA_ERR_ARG   # checked before the empty-pool fill
     # the two-level select's merge row holds 16,384 scores: 32 chunks of K = 512
     assert _index(lib, N=524288 + 1) == CSA_ERR_UNSUPPORTED
     assert _index(lib, N=524288, wsb=0, ws=N) == CSA_ERR_WORKSPACE   # supported: fails later
