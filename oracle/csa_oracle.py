@@ -32,7 +32,10 @@ design notes of the repository):
   * all positions are 0-based;
   * FP4 indexer keys are stored in the OCP Microscaling (MX) FP4 format:
     E2M1 elements with one E8M0 power-of-two scale per 32 channels (the
-    pages name FP4 for the indexer and give no format).
+    pages name FP4 for the indexer and give no format);
+  * KV entries stored in mixed precision keep the RoPE channels in bfloat16
+    and the others in the OCP MX FP8 format (E4M3 elements, one E8M0 scale
+    per 32 channels); the pages name BF16 and FP8 and give no format.
 
 Parity status: every function here is pinned by tests/test_oracle_pins.py
 against printed values, closed forms, invariants or library routines, except
@@ -61,6 +64,10 @@ __all__ = [
     "E2M1_GRID",
     "mxfp4_quantize",
     "mxfp4_dequantize",
+    "E4M3_GRID",
+    "kv_fp8_row_bytes",
+    "kv_fp8_quantize",
+    "kv_fp8_dequantize",
     "grouped_output_projection",
 ]
 
@@ -476,6 +483,115 @@ def mxfp4_dequantize(codes, scales) -> np.ndarray:
     val = np.where(nib & 8, -mag, mag)
     scale = np.repeat(np.exp2(scales.astype(np.float64) - 127.0), MX_BLOCK, axis=-1)
     return val * scale
+
+
+# ---------------------------------------------------------------------------
+# Mixed BF16 / FP8 storage of the KV entries (reading)
+# ---------------------------------------------------------------------------
+# [P1] "What does HCA change?" (quoting the paper's section 2.3.4): the KV
+# cache keeps the RoPE channels in BF16 and the other channels in FP8; the
+# pages give no FP8 format.  Reading: the OCP Microscaling (MX) v1.0 FP8
+# format on the D - R non-RoPE channels, blocks of 32 channels (the FP4
+# reading's family).  Element: E4M3 as OCP defines it ("E4M3FN": sign bit 7,
+# exponent field bits 3-6 with bias 7, mantissa bits 0-2; exponent field 0
+# holds the subnormals m * 2**-9; magnitude code 0x7F is NaN, so the largest
+# finite magnitude is 0x7E = 448).  Block scale: E8M0 byte s meaning
+# 2**(s - 127), s = floor(log2(max |x|)) - 8 + 127 clamped to [0, 254] (8 is
+# the largest exponent of an E4M3 value); an all-zero block takes s = 0.
+# Each element is |x| / 2**(s-127) (below 512) rounded to the nearest finite
+# E4M3 magnitude, ties to the even code, which saturates [448, 512) at 448;
+# the sign bit is set for x < 0.  The R RoPE channels are rounded to
+# bfloat16 (nearest, ties to even).  Packed row of one entry:
+#   bytes [0, D-R)            E4M3 codes of channels 0 .. D-R-1
+#   bytes [D-R, D+R)          bfloat16 of channels D-R .. D-1 (little endian)
+#   bytes [D+R, D+R+P)        the (D-R)/32 scale bytes, zero-padded to P, the
+#                             next multiple of 16
+# (592 bytes for D = 512, R = 64, against 1,024 in bfloat16).
+# Parity unpinned against the pages (they print no FP8 value): the format is
+# a reading; the functions below are pinned to its definition.
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code: int) -> float:
+    """Magnitude of E4M3 magnitude code 0..126 (exponent field 0: subnormal)."""
+    e, m = code >> 3, code & 7
+    if e == 0:
+        return m * 2.0 ** -9
+    return (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+E4M3_GRID = tuple(e4m3_value(c) for c in range(127))
+
+
+def kv_fp8_row_bytes(D: int, rope_dims: int) -> int:
+    nb = (D - rope_dims) // MX_BLOCK
+    return (D - rope_dims) + 2 * rope_dims + 16 * ((nb + 15) // 16)
+
+
+def _e8m0_fp8_of_block(v) -> int:
+    amax = max(abs(float(e)) for e in v)
+    if amax == 0.0:
+        return 0
+    _, k = math.frexp(amax)          # amax = f * 2**k with 0.5 <= f < 1
+    return min(max((k - 1) - 8 + 127, 0), 254)
+
+
+def _e4m3_codes(x, scale: float) -> np.ndarray:
+    """Codes of the values x (one block) under one scale: the nearest finite
+    E4M3 magnitude to |x| / scale, ties to the even code, plus the sign bit."""
+    a = np.abs(np.asarray(x, dtype=np.float64)) / scale
+    grid = np.asarray(E4M3_GRID)
+    dist = np.abs(a[:, None] - grid[None, :])
+    best = dist.min(axis=1, keepdims=True)
+    tie_ok = dist == best
+    # among the nearest (at most two adjacent codes) take the even one
+    even = tie_ok & (np.arange(127)[None, :] % 2 == 0)
+    code = np.where(even.any(axis=1), even.argmax(axis=1), tie_ok.argmax(axis=1))
+    return (code | np.where(np.asarray(x) < 0, 0x80, 0)).astype(np.uint8)
+
+
+def _bf16_bits(x) -> np.ndarray:
+    """float64 -> bfloat16 bits, nearest with ties to even (via float32,
+    exact for the float32 values the rows hold)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def kv_fp8_quantize(x, rope_dims: int) -> np.ndarray:
+    """KV entries [..., D] (float values; the RoPE part must be float32
+    values) -> packed rows uint8 [..., kv_fp8_row_bytes(D, R)] as above."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    R = rope_dims
+    assert (D - R) % MX_BLOCK == 0 and 0 <= R <= D
+    nb = (D - R) // MX_BLOCK
+    rb = kv_fp8_row_bytes(D, R)
+    flat = x.reshape(-1, D)
+    out = np.zeros((flat.shape[0], rb), np.uint8)
+    for r in range(flat.shape[0]):
+        for blk in range(nb):
+            v = flat[r, MX_BLOCK * blk: MX_BLOCK * (blk + 1)]
+            s = _e8m0_fp8_of_block(v)
+            out[r, D + R + blk] = s
+            out[r, MX_BLOCK * blk: MX_BLOCK * (blk + 1)] = _e4m3_codes(v, 2.0 ** (s - 127))
+        out[r, D - R: D + R] = _bf16_bits(flat[r, D - R:]).view(np.uint8)
+    return out.reshape(x.shape[:-1] + (rb,))
+
+
+def kv_fp8_dequantize(rows, D: int, rope_dims: int) -> np.ndarray:
+    """Exact values (float64 [..., D]) of packed rows stored as above."""
+    rows = np.asarray(rows, dtype=np.uint8)
+    R = rope_dims
+    nb = (D - R) // MX_BLOCK
+    codes = rows[..., : D - R]
+    mag = np.asarray(E4M3_GRID + (float("nan"),))[codes & 0x7F]
+    val = np.where(codes & 0x80, -mag, mag)
+    scale = np.repeat(np.exp2(rows[..., D + R: D + R + nb].astype(np.float64) - 127.0), MX_BLOCK,
+                      axis=-1)
+    bits = np.ascontiguousarray(rows[..., D - R: D + R]).view(np.uint16)
+    rope = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.concatenate([val * scale, rope], axis=-1)
 
 
 # ---------------------------------------------------------------------------

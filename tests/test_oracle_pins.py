@@ -605,6 +605,125 @@ def test_mxfp4_error_within_half_grid_gap():
 
 
 # ---------------------------------------------------------------------------
+# Mixed BF16 / FP8 storage of the KV entries (reading: OCP Microscaling FP8,
+# E4M3 elements, E8M0 scale per 32 channels; RoPE channels in bfloat16)
+# ---------------------------------------------------------------------------
+# E4M3 magnitudes worked out by hand from the format (bias 7, 3 mantissa bits,
+# exponent field 0 subnormal in units of 2^-9, 0x7F not a number)
+_E4M3_HAND = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6,
+              0x30: 0.5, 0x38: 1.0, 0x39: 1.125, 0x3F: 1.875, 0x40: 2.0, 0x78: 256.0,
+              0x79: 288.0, 0x7E: 448.0}
+# (value at scale 1, code) by hand: grid points, midpoints (ties to the even
+# code), points next to a midpoint, the subnormal range and its top,
+# saturation of [448, 512) and signs
+_FP8_HAND = [(1.0, 0x38), (1.0625, 0x38), (1.0626, 0x39), (1.1875, 0x3A), (1.125, 0x39),
+             (300.0, 0x79), (304.0, 0x7A), (303.9, 0x79), (448.0, 0x7E), (460.0, 0x7E),
+             (511.0, 0x7E), (2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02), (7.5 * 2.0 ** -9, 0x08),
+             (2.0 ** -11, 0x00), (0.0, 0x00), (-1.0, 0xB8), (-300.0, 0xF9), (-2.0 ** -10, 0x80),
+             (1.875, 0x3F), (1.9375, 0x40), (255.0, 0x78)]
+
+
+def test_e4m3_grid_by_hand():
+    for code, v in _E4M3_HAND.items():
+        assert O.E4M3_GRID[code] == v, hex(code)
+    assert len(O.E4M3_GRID) == 127 and all(np.diff(O.E4M3_GRID) > 0)
+
+
+def test_fp8_hand_codes():
+    # block maximum 511 (floor(log2) = 8): scale byte 127, scale 1
+    vals = [v for v, _ in _FP8_HAND]
+    x = np.zeros((1, 96))
+    x[0, :len(vals)] = vals
+    x[0, 32] = 1.0     # second block: amax 1 -> scale byte 119 (2^-8), 1 -> 256 = 0x78
+    x[0, 33] = 2.0 ** -8   # -> 1.0 under that scale = 0x38
+    rows = O.kv_fp8_quantize(x, 32)   # D = 96, R = 32: two FP8 blocks, channels 0-63
+    assert rows.shape == (1, O.kv_fp8_row_bytes(96, 32)) == (1, 64 + 64 + 16)
+    assert [int(c) for c in rows[0, :len(vals)]] == [c for _, c in _FP8_HAND]
+    assert rows[0, 128] == 127 and rows[0, 129] == 119
+    assert rows[0, 32] == 0x78 and rows[0, 33] == 0x38
+    assert np.all(rows[0, 130:] == 0)       # scale padding
+
+
+def test_fp8_codes_match_torch_float8_e4m3fn():
+    """Library special case: at scale 1 (a block whose maximum lies in
+    [256, 448)) the element codes equal torch's float32 -> float8_e4m3fn
+    conversion (nearest, ties to even)."""
+    import torch
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal((50, 32)) * np.exp2(rng.integers(-12, 8, size=(50, 32))))
+    x = np.clip(x, -440, 440).astype(np.float32)
+    x[:, 0] = 300.0
+    rows = O.kv_fp8_quantize(x.astype(np.float64), 0)
+    assert np.all(rows[:, 32] == 127)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(rows[:, :32], want)
+
+
+@pytest.mark.parametrize("k", [-20, -3, 0, 1, 7, 40])
+def test_fp8_scale_exponent(k):
+    # the scale byte is floor(log2 amax) - 8 + 127
+    for amax, want in [(2.0 ** k, k + 119), (2.0 ** k * (1 - 2.0 ** -30), k + 118),
+                       (1.5 * 2.0 ** k, k + 119)]:
+        x = np.zeros(32)
+        x[7] = -amax
+        r = O.kv_fp8_quantize(x, 0)
+        assert int(r[32]) == want, (amax, int(r[32]), want)
+    z = O.kv_fp8_quantize(np.zeros(64), 0)
+    assert np.all(z == 0)
+    tiny = np.zeros(32)
+    tiny[0] = 2.0 ** -130     # below 2^-119: the byte clamps at 0
+    assert O.kv_fp8_quantize(tiny, 0)[32] == 0
+
+
+def test_fp8_row_layout_and_rope_bf16():
+    """D = 512, R = 64: 448 code bytes, the RoPE channels as bfloat16 bits
+    (nearest even), 14 scale bytes padded to 16: 592 bytes."""
+    assert O.kv_fp8_row_bytes(512, 64) == 592
+    x = np.zeros(512)
+    x[448] = 1.0                                  # bf16 0x3F80
+    x[449] = 1.0 + 2.0 ** -8                      # tie -> even: 0x3F80
+    x[450] = 1.0 + 3 * 2.0 ** -8                  # tie -> even: 0x3F82
+    x[511] = -2.0                                 # 0xC000
+    r = O.kv_fp8_quantize(x, 64)
+    bits = r[448:576].view(np.uint16)
+    assert bits[0] == 0x3F80 and bits[1] == 0x3F80 and bits[2] == 0x3F82 and bits[63] == 0xC000
+    assert np.all(r[:448] == 0) and np.all(r[576:] == 0)
+    d = O.kv_fp8_dequantize(r, 512, 64)
+    assert d[448] == 1.0 and d[450] == 1.0 + 2.0 ** -6 and d[511] == -2.0
+
+
+def test_fp8_grid_values_round_trip_exactly():
+    rng = np.random.default_rng(14)
+    grid = np.array(O.E4M3_GRID)
+    for trial in range(20):
+        k = int(rng.integers(-30, 30))
+        v = grid[rng.integers(0, 127, size=(3, 448))] * np.where(rng.random((3, 448)) < 0.5, -1, 1)
+        v[:, ::32] = 448.0          # every block's maximum fixes its scale at 2^k
+        rope = rng.integers(-255, 256, size=(3, 64)) / 8.0    # 8 significant bits: exact in bfloat16
+        x = np.concatenate([v * 2.0 ** k, rope], axis=1)
+        r = O.kv_fp8_quantize(x, 64)
+        assert np.array_equal(O.kv_fp8_dequantize(r, 512, 64), x)
+
+
+def test_fp8_error_within_half_step():
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((40, 512)) * np.exp2(rng.integers(-8, 8, size=(40, 1)))
+    x = x.astype(np.float32).astype(np.float64)
+    r = O.kv_fp8_quantize(x, 64)
+    d = O.kv_fp8_dequantize(r, 512, 64)
+    X = np.repeat(np.exp2(r[:, 576:590].astype(np.float64) - 127), 32, axis=-1)
+    a = np.abs(x[:, :448]) / X
+    assert np.all(a < 512)
+    # half the local step: 2^(e-4) for a normal magnitude of exponent e, 2^-10
+    # in the subnormal range; [448, 512) saturates to 448
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    half = np.where(a >= 448, a - 448, 2.0 ** (e - 4))
+    assert np.all(np.abs(d[:, :448] - x[:, :448]) <= half * X * (1 + 1e-12))
+    # the RoPE channels: bfloat16 rounding (half a unit: relative 2^-8 at most)
+    assert np.all(np.abs(d[:, 448:] - x[:, 448:]) <= np.abs(x[:, 448:]) * 2.0 ** -8)
+
+
+# ---------------------------------------------------------------------------
 # Grouped low-rank output projection
 # ---------------------------------------------------------------------------
 def test_grouped_projection_is_block_diagonal_product():
