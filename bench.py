@@ -58,17 +58,26 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="csa64k",
                    choices=["csa64k", "csa1m", "hca1m", "prefill", "csa64k_pro", "csa64k_fp4",
-                            "csa1m_fp4", "swa", "oproj", "oproj_prefill", "csa64k_stream"])
+                            "csa1m_fp4", "swa", "oproj", "oproj_prefill", "csa64k_stream",
+                            "compress_stream", "csa64k_fp8", "csa1m_fp8", "hca1m_fp8"])
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--only", action="store_true",
+                   help="measure the named workload alone (the default csa64k run also measures "
+                        "the 1M-context decodes, csa1m and hca1m)")
     return p.parse_args()
 
 
 # ---------------------------------------------------------------------------
 # workload setup
 # ---------------------------------------------------------------------------
-CSA_DECODE = ("csa64k", "csa1m", "csa64k_pro", "csa64k_fp4", "csa1m_fp4", "csa64k_stream")
+CSA_DECODE = ("csa64k", "csa1m", "csa64k_pro", "csa64k_fp4", "csa1m_fp4", "csa64k_stream",
+              "csa64k_fp8", "csa1m_fp8")
+# KV pools stored as packed mixed BF16 / FP8 rows (the pool is quantized on
+# the device once, before timing)
+KV_FP8 = ("csa64k_fp8", "csa1m_fp8", "hca1m_fp8")
+HCA = ("hca1m", "hca1m_fp8")
 # a streaming run starts this many entries below the 16,384-entry cache (a
 # block closes every 4th step, so 2,048 steps fit before the cache is full)
 STREAM_HEADROOM = 512
@@ -78,7 +87,9 @@ def upload(d, torch):
     from long_context_sparse_11_amd.device import to_device
     out = {}
     for k, v in d.items():
-        if hasattr(v, "storage") or isinstance(v, np.ndarray):
+        if isinstance(v, torch.Tensor):   # drawn on the device already
+            out[k] = v
+        elif hasattr(v, "storage") or isinstance(v, np.ndarray):
             out[k] = to_device(v)
         else:
             out[k] = v
@@ -119,7 +130,10 @@ class Step:
             self.idx0 = torch.empty((B, 1, 0), dtype=torch.int32, device="cuda")
             n = L.csa_attn_ws_bytes(B, 1, g["H"], D, W)
             self.ws_a = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
-        elif kind == "hca1m":
+        elif kind == "compress_stream":
+            self.pool = torch.empty((B, g["N"], D), dtype=torch.bfloat16, device="cuda")
+            self.keys = torch.empty((B, g["N"], g["Di"]), dtype=torch.bfloat16, device="cuda")
+        elif kind in HCA:
             N, W = g["N"], g["W"]
             self.out = torch.empty_like(g["q"])
             n = L.csa_attn_ws_bytes(B, 1, g["H"], D, N + W)
@@ -143,47 +157,77 @@ class Step:
         return self._cws[key]
 
     def dominant(self):
-        """(name, thunk) of the kernel that carries the step's algorithmic
-        work: the indexer scoring (CSA; one kernel, the scoring half of
-        index_topk) or the whole HCA attention call (attention + split merge)."""
+        """(name, thunk) of the unit that carries most of the step's
+        algorithmic bytes (flops for prefill), launched exactly as inside the
+        step: for CSA decode the fused launch of the closing block's
+        compressors and the indexer scoring (csa_decode_index_scores: the
+        step's first launch without the selection that follows it); for
+        prefill the indexer scoring kernel (csa_index_scores launches the
+        step's index_prefill grid); for HCA and window-only decode the
+        attention call; for the output projection its call."""
         g, L = self.g, self.L
-        if self.kind in ("hca1m", "swa"):
+        if self.kind in HCA or self.kind == "swa":
             return self.calls()[1]
-        if self.kind in ("oproj", "oproj_prefill"):
+        if self.kind in ("oproj", "oproj_prefill", "compress_stream"):
             return self.calls()[0]
         if not hasattr(self, "scores"):
             B, Tq, N = g["B"], g["Tq"], g["N"]
             self.scores = self.torch.empty((B, Tq, N), dtype=self.torch.float32, device="cuda")
+        if self.kind == "prefill":
+            return ("index_scores", lambda: L.csa_index_scores(
+                g["q_idx"], g["w_idx"], g["k_idx"], g["n_entries"], g["q_pos0"], g["m"],
+                out=self.scores))
+        if self.kind == "csa64k_stream":
+            return ("index_decode_fresh", lambda: L.csa_decode_index_scores(
+                g["q_idx"], g["w_idx"], self.n_ent, self.q_pos, g["m"], self.stream_jobs(),
+                block_pos0=self.blk, out=self.scores))
         if self.kind.endswith("_fp4"):
-            return ("index_scores", lambda: L.csa_index_scores_mxfp4(
+            return ("index_decode_fresh", lambda: L.csa_decode_index_scores_mxfp4(
                 g["q_idx"], g["w_idx"], g["k_codes"], g["k_scales"], g["n_entries"], g["q_pos0"],
-                g["m"], out=self.scores))
-        return ("index_scores", lambda: L.csa_index_scores(g["q_idx"], g["w_idx"], g["k_idx"],
-                                                           g["n_entries"], g["q_pos0"], g["m"],
-                                                           out=self.scores))
+                g["m"], self.decode_jobs(fp4=True), block_pos0=g["block_pos0"], out=self.scores))
+        return ("index_decode_fresh", lambda: L.csa_decode_index_scores(
+            g["q_idx"], g["w_idx"], g["n_entries"], g["q_pos0"], g["m"], self.decode_jobs(),
+            block_pos0=g["block_pos0"], out=self.scores))
+
+    def decode_jobs(self, fp4=False):
+        """The closing block's compressor jobs of a CSA decode step: the
+        indexer key (into k_idx, or quantized into the FP4 caches) and the KV
+        entry, both to row n_entries - 1 of their pools."""
+        g = self.g
+        key = dict(c_a=g["ic_a"], z_a=g["iz_a"], c_b=g["ic_b"], z_b=g["iz_b"],
+                   prev_c_b=g["iprev_c_b"], prev_z_b=g["iprev_z_b"], bias_a=g["ibias_a"],
+                   bias_b=g["ibias_b"])
+        if not fp4:
+            key["out"] = g["k_idx"]
+        kv = dict(c_a=g["c_a"], z_a=g["z_a"], c_b=g["c_b"], z_b=g["z_b"], prev_c_b=g["prev_c_b"],
+                  prev_z_b=g["prev_z_b"], bias_a=g["bias_a"], bias_b=g["bias_b"], gain=g["gain"],
+                  rope_dims=g["R"], out=g["pool"], out_kv_fp8=self.kind in KV_FP8)
+        return [key, kv]
+
+    def stream_jobs(self):
+        """The streaming step's jobs: key and KV entries of a closing block
+        and the token's window row (third job, written to its ring slot)."""
+        g = self.g
+        return self.decode_jobs() + [dict(c_a=self.kv, gain=g["gain"], rope_dims=g["R"],
+                                          out=g["win"])]
 
     def calls(self):
         """The step as a list of (name, thunk) library calls."""
         g, L = self.g, self.L
         kind = self.kind
         if kind in CSA_DECODE:
-            N, D, Di, m = g["N"], g["D"], g["Di"], g["m"]
+            N, m = g["N"], g["m"]
             pool = g["pool"]
-            kv_job = dict(c_a=g["c_a"], z_a=g["z_a"], c_b=g["c_b"], z_b=g["z_b"],
-                          prev_c_b=g["prev_c_b"], prev_z_b=g["prev_z_b"], bias_a=g["bias_a"],
-                          bias_b=g["bias_b"], gain=g["gain"], rope_dims=g["R"], out=pool)
-            attn = ("sparse_attn", lambda: L.csa_sparse_attn(g["q"], pool, self.idx, g["win"],
-                                                             g["win_pos0"], g["W"], g["sink"],
-                                                             g["q_pos0"], rope_dims=g["R"],
-                                                             out=self.out, ws=self.ws_a))
+            attn_fn = L.csa_sparse_attn_kvfp8 if kind in KV_FP8 else L.csa_sparse_attn
+            attn = ("sparse_attn", lambda: attn_fn(g["q"], pool, self.idx, g["win"],
+                                                   g["win_pos0"], g["W"], g["sink"],
+                                                   g["q_pos0"], rope_dims=g["R"],
+                                                   out=self.out, ws=self.ws_a))
             if kind == "csa64k_stream":
                 # the key and KV entries of a closing block and the token's
                 # window row (third job, written to its ring slot) in the
                 # indexer launch
-                st = [dict(c_a=g["ic_a"], z_a=g["iz_a"], c_b=g["ic_b"], z_b=g["iz_b"],
-                           prev_c_b=g["iprev_c_b"], prev_z_b=g["iprev_z_b"],
-                           bias_a=g["ibias_a"], bias_b=g["ibias_b"], out=g["k_idx"]), kv_job,
-                      dict(c_a=self.kv, gain=g["gain"], rope_dims=g["R"], out=g["win"])]
+                st = self.stream_jobs()
                 return [
                     ("advance", lambda: L.csa_decode_advance(self.q_pos, self.n_ent, self.blk,
                                                              m, N)),
@@ -198,35 +242,33 @@ class Step:
             if kind.endswith("_fp4"):
                 # indexer keys stored in MX FP4: the fresh key is quantized
                 # by the fused launch into row n_entries - 1
-                key_job = dict(c_a=g["ic_a"], z_a=g["iz_a"], c_b=g["ic_b"], z_b=g["iz_b"],
-                               prev_c_b=g["iprev_c_b"], prev_z_b=g["iprev_z_b"],
-                               bias_a=g["ibias_a"], bias_b=g["ibias_b"])
+                jobs = self.decode_jobs(fp4=True)
                 return [("compress_index_topk", lambda: L.csa_decode_index_topk_mxfp4(
                     g["q_idx"], g["w_idx"], g["k_codes"], g["k_scales"], g["n_entries"],
-                    g["q_pos0"], g["K"], m, [key_job, kv_job], block_pos0=g["block_pos0"],
+                    g["q_pos0"], g["K"], m, jobs, block_pos0=g["block_pos0"],
                     ws=self.ws_i, idx_out=self.idx)), attn]
-            kidx = g["k_idx"]
+            jobs = self.decode_jobs()
             return [
                 # the indexer key and the KV entry of the closing block (row
-                # n_entries - 1 of their pools), then the indexer top-K: the
-                # compressors run inside the indexer launch
+                # n_entries - 1 of their pools; a packed FP8 row for the _fp8
+                # workloads), then the indexer top-K: the compressors run
+                # inside the indexer launch
                 ("compress_index_topk", lambda: L.csa_decode_index_topk(
-                    g["q_idx"], g["w_idx"], g["n_entries"], g["q_pos0"], g["K"], m, [
-                        dict(c_a=g["ic_a"], z_a=g["iz_a"], c_b=g["ic_b"], z_b=g["iz_b"],
-                             prev_c_b=g["iprev_c_b"], prev_z_b=g["iprev_z_b"],
-                             bias_a=g["ibias_a"], bias_b=g["ibias_b"], out=kidx),
-                        dict(c_a=g["c_a"], z_a=g["z_a"], c_b=g["c_b"], z_b=g["z_b"],
-                             prev_c_b=g["prev_c_b"], prev_z_b=g["prev_z_b"], bias_a=g["bias_a"],
-                             bias_b=g["bias_b"], gain=g["gain"], rope_dims=g["R"], out=pool)],
+                    g["q_idx"], g["w_idx"], g["n_entries"], g["q_pos0"], g["K"], m, jobs,
                     block_pos0=g["block_pos0"], ws=self.ws_i, idx_out=self.idx)),
-                ("sparse_attn", lambda: L.csa_sparse_attn(g["q"], pool, self.idx, g["win"],
-                                                          g["win_pos0"], g["W"], g["sink"],
-                                                          g["q_pos0"], rope_dims=g["R"],
-                                                          out=self.out, ws=self.ws_a)),
+                attn,
             ]
         if kind in ("oproj", "oproj_prefill"):
             return [("output_proj", lambda: L.csa_output_proj(g["o"], g["w_a"], g["w_b"],
                                                               mid=self.mid, out=self.out))]
+        if kind == "compress_stream":
+            # both compressors over the whole sequence, one launch
+            jobs = [dict(c_a=g["c_a"], z_a=g["z_a"], c_b=g["c_b"], z_b=g["z_b"],
+                         bias_a=g["bias_a"], bias_b=g["bias_b"], gain=g["gain"],
+                         rope_dims=g["R"], out=self.pool),
+                    dict(c_a=g["ic_a"], z_a=g["iz_a"], c_b=g["ic_b"], z_b=g["iz_b"],
+                         bias_a=g["ibias_a"], bias_b=g["ibias_b"], out=self.keys)]
+            return [("compress", lambda: L.csa_compress_batch(jobs, g["m"], pos0=g["pos0"]))]
         if kind == "swa":
             D, W, win = g["D"], g["W"], g["win"]
             return [
@@ -240,6 +282,19 @@ class Step:
                                                           g["win_pos0"], W, g["sink"],
                                                           g["q_pos0"], rope_dims=g["R"],
                                                           out=self.out, ws=self.ws_a)),
+            ]
+        if kind == "hca1m_fp8":
+            N, m, rb = g["N"], g["m"], g["pool"].shape[2]
+            pool = g["pool"]
+            return [
+                ("compress", lambda: L.csa_compress_kvfp8(
+                    g["c_a"], m, z_a=g["z_a"], bias_a=g["bias_a"], gain=g["gain"],
+                    rope_dims=g["R"], pos0=g["block_pos0"], out=pool[:, N - 1:],
+                    out_bstride=N * rb, ws=self.cws(g["c_a"], m, False))),
+                ("hca_attn", lambda: L.hca_attn_kvfp8(g["q"], pool, g["n_entries"], m, g["win"],
+                                                      g["win_pos0"], g["W"], g["sink"],
+                                                      g["q_pos0"], rope_dims=g["R"],
+                                                      out=self.out, ws=self.ws_a)),
             ]
         if kind == "hca1m":
             N, D, m = g["N"], g["D"], g["m"]
@@ -289,6 +344,12 @@ def make_inputs(kind):
         d = synth.oproj(0)
     elif kind == "oproj_prefill":
         d = synth.oproj(0, T=4096)
+    elif kind == "compress_stream":
+        d = synth.compress_stream(0)
+    elif kind in KV_FP8:
+        # the bf16 workload's inputs; its pool is quantized on the device
+        d = synth.decode(kind[:-4], 0)
+        d["name"] = kind
     elif kind == "csa64k_stream":
         # the 64K caches; the loop itself starts STREAM_HEADROOM entries lower
         d = synth.decode("csa64k", 0)
@@ -316,17 +377,22 @@ def algorithmic(kind, d):
     B, Tq = d["B"], d["Tq"]
     bf = 2
     out = {}
+    # bytes of one stored KV entry: bf16, or a packed mixed BF16 / FP8 row
+    R = d["R"]
+    vb = (D - R) + 2 * R + 16 * (((D - R) // 32 + 15) // 16) if kind in KV_FP8 else D * bf
     if kind in CSA_DECODE:
         N = d["N"]
         # bytes of one stored indexer key: bf16, or MX FP4 codes + scale bytes
         kb = Di // 2 + Di // 32 if kind.endswith("_fp4") else Di * bf
-        comp = B * ((4 * m) * D * bf + D * bf + (4 * m) * Di * bf + kb)
+        comp = B * ((4 * m) * D * bf + vb + (4 * m) * Di * bf + kb)
         idx_bytes = B * (N * kb + Hi * Di * bf + Hi * 4 + K * 4)
-        # the scoring kernel alone: visible keys, query heads and weights
-        out["index_scores"] = {"bytes": B * (N * kb + Hi * Di * bf + Hi * 4),
-                               "flops": B * 2 * Hi * Di * N}
+        # the step's first launch without the selection: the closing block's
+        # compressors (their streams in, the two entries out) and the scoring
+        # (visible keys, query heads and weights)
+        out["index_decode_fresh"] = {"bytes": comp + B * (N * kb + Hi * Di * bf + Hi * 4),
+                                     "flops": B * 2 * Hi * Di * N}
         rows = min(K, N) + W
-        attn_bytes = B * (rows * D * bf + 2 * H * D * bf + K * 4)
+        attn_bytes = B * (min(K, N) * vb + W * D * bf + 2 * H * D * bf + K * 4)
         out["bytes"] = {"compress_index_topk": comp + idx_bytes, "sparse_attn": attn_bytes}
         out["flops"] = {"compress_index_topk": B * 2 * Hi * Di * N,
                         "sparse_attn": B * 4 * H * D * rows}
@@ -340,16 +406,24 @@ def algorithmic(kind, d):
         out["bytes"] = {"output_proj": byt}
         out["flops"] = {"output_proj": fl}
         out["output_proj"] = {"bytes": byt, "flops": fl}
+    elif kind == "compress_stream":
+        T, N = d["T"], d["N"]
+        # four token streams of each compressor in, the entries out
+        byt = 4 * T * (D + Di) * bf + N * (D + Di) * bf
+        out["bytes"] = {"compress": byt}
+        out["flops"] = {}
+        out["compress"] = {"bytes": byt, "flops": 0}
     elif kind == "swa":
         attn = B * (W * D * bf + 2 * H * D * bf)
         out["bytes"] = {"window_row": B * 2 * D * bf, "sparse_attn": attn}
         out["flops"] = {"sparse_attn": B * 4 * H * D * W}
         out["sparse_attn"] = {"bytes": attn, "flops": out["flops"]["sparse_attn"]}
-    elif kind == "hca1m":
+    elif kind in HCA:
         N = d["N"]
-        comp = B * (2 * m * D * bf + D * bf)
+        comp = B * (2 * m * D * bf + vb)
         rows = N + W
-        out["bytes"] = {"compress": comp, "hca_attn": B * (rows * D * bf + 2 * H * D * bf)}
+        out["bytes"] = {"compress": comp,
+                        "hca_attn": B * (N * vb + W * D * bf + 2 * H * D * bf)}
         out["flops"] = {"hca_attn": B * 4 * H * D * rows}
         out["hca_attn"] = {"bytes": out["bytes"]["hca_attn"], "flops": out["flops"]["hca_attn"]}
     else:
@@ -388,17 +462,22 @@ def per_call_rate(kind, work, call_us):
 # measured HBM traffic of the dominant kernel (hardware counters, committed)
 # ---------------------------------------------------------------------------
 DOMINANT_KERNELS = {
-    "index_scores": ["index_decode<false, *> (decode) / index_prefill (prefill)"],
+    "index_decode_fresh": ["index_decode<true, *> (closing-block compressors + scoring, "
+                           "the step's first launch)"],
+    "index_scores": ["index_prefill"],
     "hca_attn": ["attn_hs<false, true, 4>", "attn_combine<bf16>"],
     "sparse_attn": ["attn_hs<true, *> (+ attn_combine<bf16> when split)"],
     "output_proj": ["proj_rows<4>", "proj_rows<8>"],
     "output_proj_gemm": ["proj_gemm<0>", "proj_gemm<1>"],
+    "compress": ["compress_kernel<bf16, 8> (both compressors, one launch)"],
 }
 KERNEL_SOURCES = {
+    "index_decode_fresh": ["indexer.hip", "common.h", "kernels.h"],
     "index_scores": ["indexer.hip", "common.h", "kernels.h"],
     "hca_attn": ["attn.hip", "common.h", "kernels.h"],
     "sparse_attn": ["attn.hip", "common.h", "kernels.h"],
     "output_proj": ["oproj.hip", "oproj.h", "common.h", "kernels.h"],
+    "compress": ["compress.hip", "common.h", "kernels.h"],
 }
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
@@ -469,6 +548,31 @@ def cpu_baseline(kind, d, budget_s):
             t += 1
             done += 1
         sample = f"chunk compress + {done} of {Tq} queries"
+    elif kind == "compress_stream":
+        # entries one block at a time, from host copies of the streams' first
+        # tokens (the device draw), both compressors per entry; the sample
+        # wraps around its first 4,096 entries until the time budget is spent
+        m, n = d["m"], 0
+        T_s = 1 << 14
+        h = {k: d[k][0, :T_s].float().cpu().numpy() for k in
+             ("c_a", "z_a", "c_b", "z_b", "ic_a", "iz_a", "ic_b", "iz_b")}
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s or n == 0:
+            i = n % (T_s // m)
+            lo = max(0, (i - 1) * m)
+            prev = {} if i == 0 else dict(c_b=h["c_b"][lo:i * m], z_b=h["z_b"][lo:i * m])
+            iprev = {} if i == 0 else dict(c_b=h["ic_b"][lo:i * m], z_b=h["iz_b"][lo:i * m])
+            blk = slice(i * m, (i + 1) * m)
+            O.compress(h["c_a"][blk], h["z_a"][blk], d["bias_a"], m, bias_b=d["bias_b"],
+                       prev_c_b=prev.get("c_b"), prev_z_b=prev.get("z_b"),
+                       c_b=h["c_b"][blk], z_b=h["z_b"][blk], gain=d["gain"],
+                       rope_dims=d["R"], pos0=i * m)
+            O.compress(h["ic_a"][blk], h["iz_a"][blk], d["ibias_a"], m, bias_b=d["ibias_b"],
+                       prev_c_b=iprev.get("c_b"), prev_z_b=iprev.get("z_b"),
+                       c_b=h["ic_b"][blk], z_b=h["iz_b"][blk])
+            n += 1
+        done = n * m
+        sample = f"{n} entries of both compressors ({done} tokens) from the sequence start"
     elif kind in ("oproj", "oproj_prefill"):
         wa, wb = d["w_a"].f32, d["w_b"].f32
         while time.perf_counter() - t0 < budget_s or done == 0:
@@ -489,24 +593,29 @@ def cpu_baseline(kind, d, budget_s):
         sample = f"{done} decode queries (window row + window attention per query) of batch {B}"
     else:
         b = 0
+        hca = kind in ("hca1m", "hca1m_fp8")
+        D, R = d["D"], d["R"]
+        # packed mixed BF16 / FP8 pools: the rows the step reads, stored and read back
+        kvq = ((lambda r: O.kv_fp8_dequantize(O.kv_fp8_quantize(r, R), D, R))
+               if kind.endswith("_fp8") else (lambda r: r))
         while time.perf_counter() - t0 < budget_s or done == 0:
             bb = b % B
             m = d["m"]
             tp = int(d["q_pos0"][bb])
             kv = O.compress(d["c_a"].f32[bb], d["z_a"].f32[bb], d["bias_a"], m,
-                            c_b=None if kind == "hca1m" else d["c_b"].f32[bb],
-                            z_b=None if kind == "hca1m" else d["z_b"].f32[bb],
+                            c_b=None if hca else d["c_b"].f32[bb],
+                            z_b=None if hca else d["z_b"].f32[bb],
                             bias_b=d.get("bias_b"),
-                            prev_c_b=None if kind == "hca1m" else d["prev_c_b"].f32[bb],
-                            prev_z_b=None if kind == "hca1m" else d["prev_z_b"].f32[bb],
+                            prev_c_b=None if hca else d["prev_c_b"].f32[bb],
+                            prev_z_b=None if hca else d["prev_z_b"].f32[bb],
                             gain=d["gain"], rope_dims=d["R"], pos0=int(d["block_pos0"][bb]))
             win = d["win"].f32[bb]
             wr = [p - int(d["win_pos0"][bb]) for p in O.window_positions(tp, d["W"])]
-            if kind == "hca1m":
+            if hca:
                 nv = O.visible_count(tp, m, d["N"])
                 pool = rows_of(d["pool"], bb, slice(0, nv)).astype(np.float64)
                 pool[-1] = kv[0]
-                rows = np.concatenate([pool, win[wr]])
+                rows = np.concatenate([kvq(pool), win[wr]])
             else:
                 ik = O.compress(d["ic_a"].f32[bb], d["iz_a"].f32[bb], d["ibias_a"], m,
                            c_b=d["ic_b"].f32[bb], z_b=d["iz_b"].f32[bb], bias_b=d["ibias_b"],
@@ -520,7 +629,8 @@ def cpu_baseline(kind, d, budget_s):
                 s = O.index_scores(d["q_idx"].f32[bb, 0], d["w_idx"][bb, 0],
                                    keys).astype(np.float32)
                 sel = O.select_topk(s, nv, d["K"])
-                rows = np.concatenate([rows_of(d["pool"], bb, [v for v in sel if v >= 0]), win[wr]])
+                rows = np.concatenate([kvq(rows_of(d["pool"], bb, [v for v in sel if v >= 0])
+                                           .astype(np.float64)), win[wr]])
             O.attend(d["q"].f32[bb, 0], tp, rows, d["sink"], scale, d["R"])
             done += 1
             b += 1
@@ -532,20 +642,43 @@ def cpu_baseline(kind, d, budget_s):
 
 
 # ---------------------------------------------------------------------------
-def main():
-    a = parse()
-    if a.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for {a.gpus}); the path shards by sequence "
-              "across GPUs with no exchange, so the whole-job rate is N times this line", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    import long_context_sparse_11_amd as L
-    L.lib()
-    if not torch.cuda.is_available():
-        print("no GPU", file=sys.stderr)
-        sys.exit(1)
+WORKLOAD_CONFIG = {
+    "csa64k": dict(workload="csa_decode_64k", batch=4, context=65536, entries=16384),
+    "csa64k_pro": dict(workload="csa_decode_64k_v4pro", batch=4, context=65536, entries=16384),
+    "csa1m": dict(workload="csa_decode_1m", batch=8, context=1048576, entries=262144),
+    "csa64k_fp4": dict(workload="csa_decode_64k_mxfp4_keys", batch=4, context=65536,
+                       entries=16384, index_key_format="mxfp4"),
+    "csa1m_fp4": dict(workload="csa_decode_1m_mxfp4_keys", batch=8, context=1048576,
+                      entries=262144, index_key_format="mxfp4"),
+    "hca1m": dict(workload="hca_decode_1m", batch=16, context=1048576, entries=8192),
+    "swa": dict(workload="swa_decode_1m", batch=16, context=1048576, entries=0),
+    "oproj": dict(workload="output_proj_decode", batch=4, groups=8, group_rank=1024, hidden=4096),
+    "csa64k_stream": dict(workload="csa_decode_64k_streaming", batch=4,
+                          context="63,488 upward (16,384-entry cache)", entries=15872,
+                          window="ring"),
+    "oproj_prefill": dict(workload="output_proj_prefill_4k", batch=4096, groups=8,
+                          group_rank=1024, hidden=4096),
+    "prefill": dict(workload="csa_prefill_4k_on_60k", batch=1, queries=4096, context=65536,
+                    entries=16384),
+    "compress_stream": dict(workload="compress_stream_1m", batch=1, tokens=1048576,
+                            entries=262144, key_width=128),
+    "csa64k_fp8": dict(workload="csa_decode_64k_fp8_kv", batch=4, context=65536, entries=16384,
+                       kv_format="bf16 rope + mx fp8"),
+    "csa1m_fp8": dict(workload="csa_decode_1m_fp8_kv", batch=8, context=1048576, entries=262144,
+                      kv_format="bf16 rope + mx fp8"),
+    "hca1m_fp8": dict(workload="hca_decode_1m_fp8_kv", batch=16, context=1048576, entries=8192,
+                      kv_format="bf16 rope + mx fp8"),
+}
+# workloads measured after the headline in the default run (the metric's 1M
+# context), with their timed steps capped so the whole run stays short
+ALSO = ("csa1m", "hca1m")
+ALSO_STEPS = 20
 
-    kind = a.workload
+
+def measure(kind, steps, warmup, use_graph, cpu_seconds, torch, L):
+    """Run one workload: warmup + timed steps (graph replays), per-call and
+    dominant-unit timing with HIP events, the roofline fields and, when
+    cpu_seconds is set, the CPU oracle's rate.  Returns the result dict."""
     d = make_inputs(kind)
     work = algorithmic(kind, d)
     step_bytes = sum(work["bytes"].values())
@@ -555,6 +688,9 @@ def main():
     base = upload({k: v for k, v in d.items() if k not in ("name", "dt")}, torch)
     if kind == "prefill":
         prefill_buffers(base, torch)
+    if kind in KV_FP8:
+        base["pool"] = L.csa_quantize_kv_fp8(base["pool"], d["R"])
+        torch.cuda.synchronize()
     copies = [base]
     big = [k for k, v in base.items() if isinstance(v, torch.Tensor) and v.numel() * v.element_size() > 4096]
     for _ in range(n_copies - 1):
@@ -562,7 +698,7 @@ def main():
         for k in big:
             c[k] = base[k].clone()
         copies.append(c)
-    steps = [Step(kind, c, L, torch) for c in copies]
+    steps_l = [Step(kind, c, L, torch) for c in copies]
 
     # calibration kernel of known traffic for the hardware byte counters
     # (reads and writes 512 MiB; also flushes the Infinity Cache)
@@ -570,18 +706,18 @@ def main():
     cal_dst = torch.empty_like(cal_src)
     torch.bitwise_not(cal_src, out=cal_dst)
     torch.cuda.synchronize()
+    del cal_src, cal_dst
 
     stream = torch.cuda.current_stream()
-    names = [n for n, _ in steps[0].calls()]
-    use_graph = not a.no_graph
+    names = [n for n, _ in steps_l[0].calls()]
     # eager warm-up (loads the code objects)
-    for st in steps[:2]:
+    for st in steps_l[:2]:
         for _, f in st.calls():
             f()
     torch.cuda.synchronize()
     # steps per graph replay: several decode steps are captured together
     # (each on its own input copy), as a serving loop would capture them
-    per_graph = next(p for p in (10, 8, 5, 4, 2, 1) if a.steps % p == 0 and a.warmup % p == 0) \
+    per_graph = next(p for p in (10, 8, 5, 4, 2, 1) if steps % p == 0 and warmup % p == 0) \
         if use_graph else 1
     reps_call = 20  # repetitions of one call per timing graph (distinct copies)
     graphs, call_graphs = [], []
@@ -590,42 +726,42 @@ def main():
             gph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gph):
                 for r in range(per_graph):
-                    for _, f in steps[(gi * per_graph + r) % n_copies].calls():
+                    for _, f in steps_l[(gi * per_graph + r) % n_copies].calls():
                         f()
             graphs.append(gph)
         for k in range(len(names)):
             cg = torch.cuda.CUDAGraph()
             with torch.cuda.graph(cg):
                 for r in range(reps_call):
-                    steps[r % n_copies].calls()[k][1]()
+                    steps_l[r % n_copies].calls()[k][1]()
             call_graphs.append(cg)
         dom_graph = torch.cuda.CUDAGraph()
-        for st in steps[:2]:
+        for st in steps_l[:2]:
             st.dominant()[1]()   # allocates its output before capture
         torch.cuda.synchronize()
         with torch.cuda.graph(dom_graph):
             for r in range(reps_call):
-                steps[r % n_copies].dominant()[1]()
+                steps_l[r % n_copies].dominant()[1]()
         torch.cuda.synchronize()
 
     def run(i):  # replay i covers steps i*per_graph .. (i+1)*per_graph-1
         if use_graph:
             graphs[i % n_copies].replay()
         else:
-            for _, f in steps[i % n_copies].calls():
+            for _, f in steps_l[i % n_copies].calls():
                 f()
 
-    for i in range(a.warmup // per_graph):
+    for i in range(warmup // per_graph):
         run(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(a.steps // per_graph):
-        run(a.warmup // per_graph + i)
+    for i in range(steps // per_graph):
+        run(warmup // per_graph + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / a.steps
+    ms_per_step = elapsed * 1e3 / steps
     tokens = d["B"] * d["Tq"]
-    value = tokens * a.steps / elapsed
+    value = tokens * steps / elapsed
 
     # device time per step and per library call: HIP events on the library's
     # stream around graph replays, queued behind a spin kernel so the device
@@ -646,17 +782,17 @@ def main():
                    for k, n in enumerate(names)}
     else:
         dev_step_us = float(np.median(timed([(lambda i=i: run(i)) for i in range(20)])))
-        call_us = {n: float(np.median(timed([(lambda i=i, k=k: steps[i % n_copies].calls()[k][1]())
+        call_us = {n: float(np.median(timed([(lambda i=i, k=k: steps_l[i % n_copies].calls()[k][1]())
                                              for i in range(20)]))) for k, n in enumerate(names)}
 
-    # roofline of the dominant kernel: its per-launch duration from HIP
-    # events around replays of a graph of reps_call launches (rotating input
+    # roofline of the dominant unit: its per-launch duration from HIP events
+    # around replays of a graph of reps_call launches (rotating input
     # copies), on the library's stream
-    dom = steps[0].dominant()[0]
+    dom = steps_l[0].dominant()[0]
     if use_graph:
         dom_us = float(np.median(timed([dom_graph.replay] * 10))) / reps_call
     else:
-        dom_us = float(np.median(timed([(lambda i=i: steps[i % n_copies].dominant()[1]())
+        dom_us = float(np.median(timed([(lambda i=i: steps_l[i % n_copies].dominant()[1]())
                                         for i in range(20)])))
     dw = work[dom]
     if kind in ("prefill", "oproj_prefill"):
@@ -674,47 +810,75 @@ def main():
     roof["algorithmic_flops_per_launch"] = int(dw["flops"])
     roof["avg_launch_us"] = round(dom_us, 2)
 
-    cpu = None
-    if not a.no_cpu:
-        cpu = cpu_baseline(kind, d, a.cpu_seconds)
+    # the whole step against the HBM roofline: its algorithmic bytes over the
+    # wall-clock time per step (and over the device time per step)
+    step_roof = {"algorithmic_bytes": int(step_bytes),
+                 "achieved_GBs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                 "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "frac_device_time": round(step_bytes / (dev_step_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                           4)}
 
-    cfgs = {
-        "csa64k": dict(workload="csa_decode_64k", batch=4, context=65536, entries=16384),
-        "csa64k_pro": dict(workload="csa_decode_64k_v4pro", batch=4, context=65536,
-                           entries=16384),
-        "csa1m": dict(workload="csa_decode_1m", batch=8, context=1048576, entries=262144),
-        "csa64k_fp4": dict(workload="csa_decode_64k_mxfp4_keys", batch=4, context=65536,
-                           entries=16384, index_key_format="mxfp4"),
-        "csa1m_fp4": dict(workload="csa_decode_1m_mxfp4_keys", batch=8, context=1048576,
-                          entries=262144, index_key_format="mxfp4"),
-        "hca1m": dict(workload="hca_decode_1m", batch=16, context=1048576, entries=8192),
-        "swa": dict(workload="swa_decode_1m", batch=16, context=1048576, entries=0),
-        "oproj": dict(workload="output_proj_decode", batch=4, groups=8, group_rank=1024,
-                      hidden=4096),
-        "csa64k_stream": dict(workload="csa_decode_64k_streaming", batch=4,
-                              context="63,488 upward (16,384-entry cache)", entries=15872,
-                              window="ring"),
-        "oproj_prefill": dict(workload="output_proj_prefill_4k", batch=4096, groups=8,
-                              group_rank=1024, hidden=4096),
-        "prefill": dict(workload="csa_prefill_4k_on_60k", batch=1, queries=4096, context=65536,
-                        entries=16384),
-    }[kind]
-    cfgs.update(heads=d["H"], head_dim=d["D"], rope_dims=d["R"], index_heads=d["Hi"],
-                index_dim=d["Di"], index_topk=d["K"], window=d["W"], m=d["m"], step_calls=names,
-                graph=use_graph, steps_per_graph=per_graph, input_copies=n_copies)
+    cpu = cpu_baseline(kind, d, cpu_seconds) if cpu_seconds else None
+
+    cfg = dict(WORKLOAD_CONFIG[kind])
+    cfg.update(heads=d["H"], head_dim=d["D"], rope_dims=d["R"], index_heads=d["Hi"],
+               index_dim=d["Di"], index_topk=d["K"], window=d["W"], m=d["m"], step_calls=names,
+               graph=use_graph, steps_per_graph=per_graph, input_copies=n_copies)
+    res = dict(value=round(value, 1), ms_per_step=round(ms_per_step, 5), config=cfg,
+               roofline=roof, step_roofline=step_roof, cpu_baseline=cpu,
+               device_us_per_step=round(dev_step_us, 2),
+               per_call_us={k: round(v, 2) for k, v in call_us.items()},
+               # each call's algorithmic rate: HBM GB/s, and TFLOP/s where the
+               # call is a large contraction (the prefill indexer and
+               # attention, the prefill projection)
+               per_call_rate=per_call_rate(kind, work, call_us),
+               step_algorithmic_bytes=int(step_bytes))
+    del graphs, call_graphs, steps_l, copies, base
+    if use_graph:
+        del dom_graph
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {a.gpus}); the path shards by sequence "
+              "across GPUs with no exchange, so the whole-job rate is N times this line", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import long_context_sparse_11_amd as L
+    L.lib()
+    if not torch.cuda.is_available():
+        print("no GPU", file=sys.stderr)
+        sys.exit(1)
+
+    use_graph = not a.no_graph
+    kind = a.workload
+    r = measure(kind, a.steps, a.warmup, use_graph, None if a.no_cpu else a.cpu_seconds, torch, L)
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 5),
+        "metric": METRIC, "value": r["value"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": r["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic", "config": cfgs, "roofline": roof, "cpu_baseline": cpu,
-        "device_us_per_step": round(dev_step_us, 2),
-        "per_call_us": {k: round(v, 2) for k, v in call_us.items()},
-        # each call's algorithmic rate: HBM GB/s, and TFLOP/s where the call
-        # is a large contraction (the prefill indexer and attention, the
-        # prefill projection)
-        "per_call_rate": per_call_rate(kind, work, call_us),
-        "step_algorithmic_bytes": int(step_bytes),
+        "data": "synthetic", "config": r["config"], "roofline": r["roofline"],
+        "step_roofline": r["step_roofline"], "cpu_baseline": r["cpu_baseline"],
+        "device_us_per_step": r["device_us_per_step"], "per_call_us": r["per_call_us"],
+        "per_call_rate": r["per_call_rate"], "step_algorithmic_bytes": r["step_algorithmic_bytes"],
     }
+    # the metric's 1M-context decode workloads, measured in the same run
+    if kind == "csa64k" and not a.only:
+        also = {}
+        for k in ALSO:
+            n, w = max(min(a.steps, ALSO_STEPS), 1), min(a.warmup, ALSO_STEPS)
+            ra = measure(k, n, w, use_graph, None, torch, L)
+            also[ra["config"]["workload"]] = {
+                "value": ra["value"], "unit": "tokens/s", "steps": n, "warmup": w,
+                "ms_per_step": ra["ms_per_step"], "device_us_per_step": ra["device_us_per_step"],
+                "per_call_us": ra["per_call_us"], "per_call_rate": ra["per_call_rate"],
+                "roofline": ra["roofline"], "step_roofline": ra["step_roofline"],
+                "config": ra["config"]}
+        line["also"] = also
     print(json.dumps(line))
 
 

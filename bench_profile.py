@@ -1,26 +1,34 @@
 """rocprofv3 passes over bench.py for one workload, and their summary.
 
-    python3 -m long_context_sparse_11_amd.profsum run --workload csa64k --out _prof
+    python3 bench_profile.py run --workload csa64k --out $OUT
 
-runs, as child processes from /tmp (TMPDIR=/tmp):
+runs, as child processes from /tmp (TMPDIR=/tmp), each under its own time
+limit:
 
-  1. rocprofv3 --kernel-trace --stats  -- python3 bench.py --workload W ...
-  2. rocprofv3 --pmc FETCH_SIZE        -- python3 bench.py --workload W ...
-  3. rocprofv3 --pmc WRITE_SIZE        -- python3 bench.py --workload W ...
+  1. rocprofv3 --kernel-trace --stats  -- python3 bench.py --workload W --only ...
+  2. rocprofv3 --pmc FETCH_SIZE        -- python3 bench.py --workload W --only ...
+  3. rocprofv3 --pmc WRITE_SIZE        -- python3 bench.py --workload W --only ...
+  4. rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16
+                     SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE
+                                       -- python3 bench.py --workload W --only ...
 
-(each counter in a run of its own), then writes profiles/<kernel>_<workload>.md
-(per-kernel durations, per-dispatch byte counters, the calibration, the
-dominant kernel's duration next to the one bench.py measured in the same run)
+then writes profiles/<unit>_<workload>.md (per-kernel durations, per-dispatch
+byte counters scaled by the calibration kernel, MFMA and LDS counters, the
+dominant unit's duration next to the one bench.py measured in the same run)
 and the workload's record in profiles/counters.json, which bench.py reads
 for the ``traffic`` field of its roofline.
 
 The byte counters are scaled by what they read for the calibration kernel
 (bench.py's bitwise_not over 512 MiB: 512 MiB read, 512 MiB written).  A
-record carries a hash of the dominant kernel's sources; bench.py ignores it
-once they change.
+record carries a hash of the dominant unit's sources; bench.py ignores it
+once they change.  MFMA utilisation is the busy-cycle count over the
+dispatch's active cycles (GRBM_GUI_ACTIVE, which reads the sum over the 8
+XCDs, divided by 8) times the 1,024 SIMDs (256 CUs x 4): the fraction of the
+MFMA peak at the clock the kernel ran at; the bf16 MFMA operation count is
+SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flops.
 
 ``summarize`` re-runs only the summary step on existing output directories.
-This module never touches the GPU itself.
+This script never touches the GPU itself.
 """
 from __future__ import annotations
 
@@ -34,20 +42,29 @@ import statistics
 import subprocess
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
 CAL_BYTES = 512 << 20
 CAL_KERNEL = "bitwise_not"
+SIMDS = 256 * 4
+# GRBM_GUI_ACTIVE comes back summed over the 8 XCDs (per dispatch it reads
+# about 8 x 2.1 GHz x the traced duration), so one XCD's active cycles are a
+# eighth of it
+XCDS = 8
+MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                 "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE"]
 # device kernels of each dominant unit (substrings of rocprof kernel names)
 UNIT_KERNELS = {
-    # decode: the scoring kernel as the bench times it (csa_index_scores); the
-    # step runs its variant with the fresh-entry workgroups, index_decode<true>
-    "index_scores": {"decode": ["index_decode<false,"], "prefill": ["index_prefill"]},
-    "hca_attn": {"decode": ["attn_hs<false, true, 4>", "attn_combine"]},
-    "sparse_attn": {"decode": ["attn_hs<true,", "attn_combine"]},
-    "output_proj": {"decode": ["proj_rows<4>", "proj_rows<8>"],
-                    "prefill": ["proj_gemm<0>", "proj_gemm<1>"]},
+    # CSA decode: the step's first launch, compressors + scoring
+    "index_decode_fresh": ["index_decode<true,"],
+    # prefill: the scoring kernel of the step's index_topk call
+    "index_scores": ["index_prefill"],
+    "hca_attn": ["attn_hs<false,", "attn_combine"],
+    "sparse_attn": ["attn_hs<true,", "attn_combine"],
+    "output_proj": ["proj_rows<", "proj_gemm<"],
 }
+DOMINANT = {"hca1m": "hca_attn", "swa": "sparse_attn", "oproj": "output_proj",
+            "oproj_prefill": "output_proj", "prefill": "index_scores"}
 WORKLOAD_NAME = {"csa64k": "csa_decode_64k", "csa1m": "csa_decode_1m",
                  "hca1m": "hca_decode_1m", "prefill": "csa_prefill_4k_on_60k",
                  "csa64k_pro": "csa_decode_64k_v4pro",
@@ -55,11 +72,17 @@ WORKLOAD_NAME = {"csa64k": "csa_decode_64k", "csa1m": "csa_decode_1m",
                  "csa1m_fp4": "csa_decode_1m_mxfp4_keys",
                  "swa": "swa_decode_1m", "oproj": "output_proj_decode",
                  "oproj_prefill": "output_proj_prefill_4k",
-                 "csa64k_stream": "csa_decode_64k_streaming"}
+                 "csa64k_stream": "csa_decode_64k_streaming",
+                 "compress_stream": "compress_stream_1m"}
+
+
+def dominant(workload):
+    return DOMINANT.get(workload, "compress" if workload == "compress_stream"
+                        else "index_decode_fresh")
 
 
 def bench_cmd(workload, steps):
-    return ["python3", os.path.join(ROOT, "bench.py"), "--workload", workload,
+    return ["python3", os.path.join(ROOT, "bench.py"), "--workload", workload, "--only",
             "--steps", str(steps), "--warmup", str(steps), "--no-cpu"]
 
 
@@ -72,6 +95,8 @@ def passes(workload, out, steps):
                    "-d", os.path.join(out, f"{w}_fetch"), "-o", "run", "--"] + bench_cmd(w, 10)),
         ("write", ["rocprofv3", "--pmc", "WRITE_SIZE", "--output-format", "csv",
                    "-d", os.path.join(out, f"{w}_write"), "-o", "run", "--"] + bench_cmd(w, 10)),
+        ("mfma", ["rocprofv3", "--pmc", *MFMA_COUNTERS, "--output-format", "csv",
+                  "-d", os.path.join(out, f"{w}_mfma"), "-o", "run", "--"] + bench_cmd(w, 10)),
     ]
 
 
@@ -82,23 +107,24 @@ def run(args):
     logs = {}
     for name, cmd in passes(args.workload, out, args.steps):
         log = os.path.join(out, f"{args.workload}_{name}.log")
-        print(f"[profsum] {args.workload} {name}: {' '.join(cmd)}", flush=True)
+        print(f"[bench_profile] {args.workload} {name}: {' '.join(cmd)}", flush=True)
         with open(log, "w") as fh:
             try:
                 rc = subprocess.run(["timeout", "-s", "KILL", str(args.timeout)] + cmd, cwd="/tmp",
                                     env=env, stdout=fh, stderr=subprocess.STDOUT).returncode
             except OSError as e:
-                print(f"[profsum] could not start: {e}", flush=True)
+                print(f"[bench_profile] could not start: {e}", flush=True)
                 return 1
         logs[name] = log
         if rc != 0:
             # rocprofv3 may itself end with a fault after a complete run
             tail = open(log).read().splitlines()[-5:]
             done = any(line.startswith("{\"metric\"") for line in open(log))
-            print(f"[profsum] {name} exited {rc}; bench line printed: {done}", flush=True)
+            print(f"[bench_profile] {name} exited {rc}; bench line printed: {done}", flush=True)
             print("\n".join(tail), flush=True)
             if not done:
                 return rc
+        print(f"[bench_profile] {args.workload} {name} done", flush=True)
     return summarize_dirs(args.workload, out, logs, args.steps)
 
 
@@ -144,6 +170,8 @@ def summarize_dirs(workload, out, logs, steps):
                          float(r["MaxNs"]) / 1e3, float(r["Percentage"])) for r in rows}
     fetch = _counter(os.path.join(out, f"{workload}_fetch"), "FETCH_SIZE")
     write = _counter(os.path.join(out, f"{workload}_write"), "WRITE_SIZE")
+    mdir = os.path.join(out, f"{workload}_mfma")
+    mf = {c: _counter(mdir, c) for c in MFMA_COUNTERS} if os.path.isdir(mdir) else None
     cal_f = _match(fetch, CAL_KERNEL)
     cal_w = _match(write, CAL_KERNEL)
     if not cal_f or not cal_w:
@@ -154,23 +182,27 @@ def summarize_dirs(workload, out, logs, steps):
     w_scale = CAL_BYTES / (w_kib * 1024.0)
 
     line = _bench_line(logs["stats"]) if logs.get("stats") else None
-    dom = {"hca1m": "hca_attn", "swa": "sparse_attn", "oproj": "output_proj",
-           "oproj_prefill": "output_proj"}.get(workload, "index_scores")
-    phase = "prefill" if workload in ("prefill", "oproj_prefill") else "decode"
-    parts = UNIT_KERNELS[dom][phase]
+    dom = dominant(workload)
     dom_us, dom_bytes, comp = 0.0, 0.0, []
-    for pat in parts:
+    for pat in UNIT_KERNELS[dom]:
         sk = _match(stats, pat)
+        if not sk:
+            continue
         fk = _match(fetch, pat)
         wk = _match(write, pat)
-        if not (sk and fk and wk):
-            raise RuntimeError(f"kernel {pat} missing from the profiles")
-        us = stats[sk[0]][1]
-        fb = statistics.median(fetch[fk[0]]) * 1024.0 * f_scale
-        wb = statistics.median(write[wk[0]]) * 1024.0 * w_scale
-        dom_us += us
-        dom_bytes += fb + wb
-        comp.append((_short(sk[0]), us, fb, wb))
+        if not (fk and wk):
+            raise RuntimeError(f"kernel {pat} missing from the counter runs")
+        for name in sk:
+            us = stats[name][1]
+            f_n = [n for n in fk if _short(n) == _short(name)]
+            w_n = [n for n in wk if _short(n) == _short(name)]
+            fb = statistics.median(fetch[f_n[0]]) * 1024.0 * f_scale if f_n else float("nan")
+            wb = statistics.median(write[w_n[0]]) * 1024.0 * w_scale if w_n else float("nan")
+            dom_us += us
+            dom_bytes += fb + wb
+            comp.append((_short(name), us, fb, wb))
+    if not comp:
+        raise RuntimeError(f"no kernel of unit {dom} in the profiles")
 
     rec = {
         "kernel": dom,
@@ -203,9 +235,9 @@ def summarize_dirs(workload, out, logs, steps):
           "Commands (from /tmp with TMPDIR=/tmp; $REPO is the repository root, $OUT any "
           "output directory):", "", "```"]
     md += cmds
-    md += [f"python3 -m long_context_sparse_11_amd.profsum summarize --workload {workload} "
-           f"--out $OUT --steps {steps}", "```", "",
-           "All of it at once: `python3 -m long_context_sparse_11_amd.profsum run "
+    md += [f"python3 $REPO/bench_profile.py summarize --workload {workload} --out $OUT "
+           f"--steps {steps}", "```", "",
+           "All of it at once: `python3 $REPO/bench_profile.py run "
            f"--workload {workload} --out $OUT --steps {steps}`.", "",
            "## Kernel durations (kernel trace, whole bench run)", "",
            "| kernel | calls | avg µs | min µs | max µs | % time |", "|---|---|---|---|---|---|"]
@@ -226,7 +258,37 @@ def summarize_dirs(workload, out, logs, steps):
         wk = statistics.median(write[name]) if name in write else float("nan")
         md.append(f"| `{_short(name)}` | {fk:.1f} | {wk:.1f} | {fk * 1024 * f_scale:.0f} | "
                   f"{wk * 1024 * w_scale:.0f} |")
-    md += ["", "## Dominant kernel", "",
+    if mf is not None:
+        md += ["", "## MFMA and LDS counters per dispatch (median)", "",
+               "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1,024 SIMDs), "
+               "the fraction of the MFMA peak at the clock the kernel ran at (GRBM_GUI_ACTIVE "
+               "reads the sum over the 8 XCDs; the clock column is that sum / 8 over the traced "
+               "duration); bf16 MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, their rate over "
+               "the kernel's traced average duration, against the published 2.5 PFLOP/s; LDS bank "
+               "conflicts per access = SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - "
+               "SQ_LDS_BANK_CONFLICT).", "",
+               "| kernel | MFMA busy % | clock GHz | bf16 MFMA flops | bf16 MFMA TFLOP/s "
+               "| % of 2.5 PFLOP/s | LDS conflict cycles | LDS conflicts / access |",
+               "|---|---|---|---|---|---|---|---|"]
+        names = sorted(mf["GRBM_GUI_ACTIVE"])
+        for name in names:
+            if CAL_KERNEL in name or "spin_kernel" in name or "elementwise" in name \
+                    or "copyBuffer" in name:
+                continue
+            med = {c: statistics.median(mf[c][name]) if name in mf[c] else float("nan")
+                   for c in MFMA_COUNTERS}
+            active = med["GRBM_GUI_ACTIVE"] / XCDS
+            busy = 100.0 * med["SQ_VALU_MFMA_BUSY_CYCLES"] / max(active * SIMDS, 1)
+            flops = med["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+            st = [v for k, v in stats.items() if _short(k) == _short(name)]
+            us = st[0][1] if st else float("nan")
+            tf = flops / (us * 1e-6) / 1e12 if us > 0 else float("nan")
+            ghz = active / (us * 1e3) if us > 0 else float("nan")
+            acc = med["SQ_LDS_IDX_ACTIVE"] - med["SQ_LDS_BANK_CONFLICT"]
+            cpa = med["SQ_LDS_BANK_CONFLICT"] / acc if acc > 0 else float("nan")
+            md.append(f"| `{_short(name)}` | {busy:.1f} | {ghz:.2f} | {flops:.4g} | {tf:.1f} | "
+                      f"{100 * tf / 2500:.1f} | {med['SQ_LDS_BANK_CONFLICT']:.4g} | {cpa:.4f} |")
+    md += ["", "## Dominant unit", "",
            f"- unit: `{dom}` = " + " + ".join(f"`{c[0]}`" for c in comp),
            f"- average duration per launch, rocprofv3: {dom_us:.2f} µs"
            + ("" if line is None else
@@ -240,7 +302,7 @@ def summarize_dirs(workload, out, logs, steps):
     path = os.path.join(PROFILES, f"{dom}_{WORKLOAD_NAME[workload]}.md")
     with open(path, "w") as fh:
         fh.write("\n".join(md) + "\n")
-    print(f"[profsum] wrote {path} and the {workload} record of {cpath}", flush=True)
+    print(f"[bench_profile] wrote {path} and the {workload} record of {cpath}", flush=True)
     return 0
 
 
@@ -256,9 +318,9 @@ def main():
     p = argparse.ArgumentParser()
     p.add_argument("action", choices=["run", "summarize"])
     p.add_argument("--workload", default="csa64k", choices=sorted(WORKLOAD_NAME))
-    p.add_argument("--out", default=os.path.join(ROOT, "_prof"))
+    p.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "prof"))
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--timeout", type=int, default=300)
+    p.add_argument("--timeout", type=int, default=240)
     a = p.parse_args()
     sys.exit(run(a) if a.action == "run" else summarize(a))
 

@@ -104,6 +104,60 @@ int csa_compress(int dt, int B, int T, int D, int m, int overlap,
 size_t csa_compress_ws_bytes(int dt, int B, int T, int D, int m, int overlap);
 
 /* ---------------------------------------------------------------------------
+ * Mixed BF16 / FP8 storage of the KV entries.
+ *
+ * [P1] "What does HCA change?" (quoting the paper's section 2.3.4): the KV
+ * cache keeps the RoPE channels in BF16 and the other channels in FP8; the
+ * pages give no format.  Format here (the OCP Microscaling FP8 format,
+ * converted in hardware on gfx950): per entry of D = 512 channels with R
+ * RoPE channels (R a multiple of 32), one packed row of
+ * csa_kv_fp8_row_bytes(D, R) bytes (592 for R = 64):
+ *   bytes [0, D-R)       E4M3 codes of channels 0 .. D-R-1: bit 7 the sign,
+ *                        bits 3-6 the exponent field (bias 7), bits 0-2 the
+ *                        mantissa; field 0 is subnormal (m * 2^-9); largest
+ *                        finite magnitude 0x7E = 448
+ *   bytes [D-R, D+R)     the R RoPE channels in bfloat16
+ *   bytes [D+R, ...)     one E8M0 scale byte per 32 code channels, value
+ *                        2^(s-127), zero-padded to a multiple of 16 bytes
+ * Quantization: per 32-channel block s = floor(log2(max |x|)) - 8 + 127
+ * clamped to [0, 254] (0 for an all-zero block); each element is
+ * |x| / 2^(s-127) rounded to the nearest E4M3 magnitude, ties to the even
+ * code, saturating at 448; sign bit set for x < 0.  The RoPE channels are
+ * rounded to bfloat16 (nearest even).  Window rows stay bf16.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of one packed row; 0 for a shape the format does not cover (D must
+ * be 512, R a multiple of 32 in [0, D]). */
+size_t csa_kv_fp8_row_bytes(int D, int rope_dims);
+
+/* rows x D values (dt f32 or bf16, finite) -> packed rows [rows, row_bytes]
+ * uint8 (device, caller-owned).  Errors: CSA_ERR_ARG for a bad dt, rows < 0
+ * or NULL pointers with rows > 0; CSA_ERR_UNSUPPORTED for another shape or
+ * past rows * D = 2^39. */
+int csa_quantize_kv_fp8(int dt, int64_t rows, int D, int rope_dims, const void* x, void* out,
+                        void* stream);
+
+/* Packed rows -> their exact values as bf16 [rows, D] (an E4M3 value times
+ * a power of two is exact in bf16 for scale bytes 9..246), with the same
+ * hardware conversion the attention uses.  Errors as csa_quantize_kv_fp8. */
+int csa_dequantize_kv_fp8(int64_t rows, int D, int rope_dims, const void* rows_in, void* out,
+                          void* stream);
+
+/* csa_compress_kvfp8 - csa_compress writing each entry as a packed row
+ * (pooled, normalised and rotated in float32 exactly as csa_compress does,
+ * then quantized as csa_quantize_kv_fp8).  out [B, n_out rows] of
+ * csa_kv_fp8_row_bytes(D, rope_dims) bytes, batch stride out_bstride bytes
+ * (0: n_out rows).  Other arguments, workspace and errors as csa_compress;
+ * CSA_ERR_UNSUPPORTED for a shape the row format does not cover. */
+int csa_compress_kvfp8(int dt, int B, int T, int D, int m, int overlap,
+                       const void* c_a, const void* z_a, const void* c_b, const void* z_b,
+                       const void* prev_c_b, const void* prev_z_b,
+                       const float* bias_a, const float* bias_b,
+                       const float* gain, float eps,
+                       int rope_dims, double rope_base, const int64_t* pos0,
+                       void* out, int64_t out_bstride, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * csa_compress_batch - up to two compressors over the same token block in
  * one launch.
  *
@@ -136,6 +190,11 @@ typedef struct csa_compress_job {
   double rope_base;
   void* out;
   int64_t out_bstride;
+  /* 0: out holds entries of dt.  1: out holds packed mixed BF16 / FP8 rows
+   * (csa_kv_fp8_row_bytes(D, rope_dims) bytes each, see csa_compress_kvfp8)
+   * and out_bstride counts bytes; D = 512 only, and in the decode calls only
+   * for the KV job jobs[1]. */
+  int out_kv_fp8;
 } csa_compress_job;
 
 int csa_compress_batch(int dt, int B, int T, int m, int overlap, const int64_t* pos0,
@@ -291,11 +350,34 @@ int csa_decode_index_topk_mxfp4(int B, int Tq, int Hi, int Di, int N_cap, int K,
                                 int32_t* idx_out, float* score_out, float* all_scores,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/* csa_decode_index_scores(_mxfp4) - the scoring half of
+ * csa_decode_index_topk(_mxfp4): the closing block's fresh entries are
+ * written exactly as there (the same launch: for the shapes listed there the
+ * compressors run inside the indexer launch), then every visible entry is
+ * scored into scores [B, Tq, N_cap] f32 (later columns unspecified); no
+ * selection, no workspace.  [P2] section 3.2.2 (eqs. 9-16).  A caller that
+ * selects elsewhere uses it: a pool split over several devices scores each
+ * slice and merges the per-slice winners; it also times the fused launch on
+ * its own.  Arguments and errors as csa_decode_index_topk(_mxfp4) without
+ * K, idx_out, score_out and the workspace; CSA_ERR_ARG for a NULL scores. */
+int csa_decode_index_scores(int dt, int B, int Tq, int Hi, int Di, int N_cap, int m, int overlap,
+                            const int64_t* block_pos0, const csa_compress_job* jobs, int n_jobs,
+                            const void* q_idx, const float* w_idx, const int32_t* n_entries,
+                            const int64_t* q_pos0, float* scores, void* stream);
+int csa_decode_index_scores_mxfp4(int B, int Tq, int Hi, int Di, int N_cap, int m, int overlap,
+                                  const int64_t* block_pos0, const csa_compress_job* jobs,
+                                  int n_jobs, const void* q_idx, const float* w_idx,
+                                  uint8_t* k_codes, uint8_t* k_scales,
+                                  const int32_t* n_entries, const int64_t* q_pos0,
+                                  float* scores, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Streaming decode state.
  *
- * [P4] "Tata letak attention mask" (the cache keeps, per layer, the raw
- * window and the compressor's pending tokens and overlap state) and [P1]
+ * [P4] "Lapisan cache" (the per-layer caches, DeepseekV4CSACache and
+ * DeepseekV4HCACache, keep the raw sliding window and, for the compressor
+ * and the indexer, the pending tokens, the pool, the entry count and the
+ * overlap state) and [P1]
  * "How does CSA compress 8 tokens into 4 KV entries?" (an entry exists once
  * its block of m tokens has closed).  A decode loop keeps every count on
  * the device, so steps can be captured in a HIP graph and replayed with no
@@ -418,6 +500,27 @@ int hca_attn(int dt, int B, int Tq, int H, int D, int rope_dims, double rope_bas
              const int64_t* win_pos0, int W, const float* sink,
              const int64_t* q_pos0, void* out, float* lse,
              void* ws, size_t ws_bytes, void* stream);
+
+/* csa_sparse_attn_kvfp8 / hca_attn_kvfp8 - csa_sparse_attn and hca_attn
+ * over a pool of packed mixed BF16 / FP8 rows (see csa_kv_fp8_row_bytes):
+ * pool [B, N_cap, row_bytes] uint8.  q, the window and out are bf16 (no dt
+ * argument); each pool row's values are its exact dequantization, so the
+ * result is that of the bf16 call on the dequantized pool.  Other arguments,
+ * workspace and errors as those calls; CSA_ERR_UNSUPPORTED outside the
+ * bf16 MFMA shape (H a multiple of 64 up to 128, D = 512, R a multiple of
+ * 32). */
+int csa_sparse_attn_kvfp8(int B, int Tq, int H, int D, int rope_dims, double rope_base,
+                          float scale, const void* q, const void* pool, int N_cap,
+                          const int32_t* idx, int K, const void* win, int L_win,
+                          const int64_t* win_pos0, int W, const float* sink,
+                          const int64_t* q_pos0, void* out, float* lse,
+                          void* ws, size_t ws_bytes, void* stream);
+int hca_attn_kvfp8(int B, int Tq, int H, int D, int rope_dims, double rope_base,
+                   float scale, const void* q, const void* pool, int N_cap,
+                   const int32_t* n_entries, int m, const void* win, int L_win,
+                   const int64_t* win_pos0, int W, const float* sink,
+                   const int64_t* q_pos0, void* out, float* lse,
+                   void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace (bytes) for csa_sparse_attn / hca_attn with at most
  * keys_per_query rows per query (K + W, or N_cap + W). */

@@ -10,8 +10,16 @@ from .binding import (  # noqa: F401
     csa_attn_ws_bytes,
     csa_compress,
     csa_compress_batch,
+    csa_compress_kvfp8,
+    csa_dequantize_kv_fp8,
+    csa_kv_fp8_row_bytes,
+    csa_quantize_kv_fp8,
+    csa_sparse_attn_kvfp8,
+    hca_attn_kvfp8,
     csa_compress_ws_bytes,
     csa_decode_advance,
+    csa_decode_index_scores,
+    csa_decode_index_scores_mxfp4,
     csa_decode_index_topk,
     csa_window_row,
     csa_decode_index_topk_mxfp4,

@@ -50,7 +50,34 @@ _SIGS = {
     "csa_index_scores_mxfp4": (_c.c_int, [_c.c_int] * 6 + [_c.c_void_p] * 8),
     "csa_decode_index_topk_mxfp4": (_c.c_int, [_c.c_int] * 8 + [_c.c_void_p, _c.c_void_p, _c.c_int]
                                     + [_c.c_void_p] * 10 + [_c.c_size_t, _c.c_void_p]),
+    "csa_decode_index_scores": (_c.c_int, [_c.c_int] * 8 + [_c.c_void_p, _c.c_void_p, _c.c_int]
+                                + [_c.c_void_p] * 6),
+    "csa_decode_index_scores_mxfp4": (_c.c_int, [_c.c_int] * 7
+                                      + [_c.c_void_p, _c.c_void_p, _c.c_int]
+                                      + [_c.c_void_p] * 8),
     "csa_output_proj": (_c.c_int, [_c.c_int] * 6 + [_c.c_void_p] * 6),
+    "csa_kv_fp8_row_bytes": (_c.c_size_t, [_c.c_int, _c.c_int]),
+    "csa_quantize_kv_fp8": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int, _c.c_int, _c.c_void_p,
+                                       _c.c_void_p, _c.c_void_p]),
+    "csa_dequantize_kv_fp8": (_c.c_int, [_c.c_int64, _c.c_int, _c.c_int, _c.c_void_p,
+                                         _c.c_void_p, _c.c_void_p]),
+    "csa_compress_kvfp8": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                      _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                      _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                      _c.c_void_p, _c.c_float, _c.c_int, _c.c_double,
+                                      _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p,
+                                      _c.c_size_t, _c.c_void_p]),
+    "csa_sparse_attn_kvfp8": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                         _c.c_double, _c.c_float, _c.c_void_p, _c.c_void_p,
+                                         _c.c_int, _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int,
+                                         _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_void_p,
+                                         _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_size_t,
+                                         _c.c_void_p]),
+    "hca_attn_kvfp8": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_double,
+                                  _c.c_float, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p,
+                                  _c.c_int, _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int,
+                                  _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                  _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "csa_window_row": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p,
                                   _c.c_float, _c.c_int, _c.c_double, _c.c_void_p, _c.c_void_p,
                                   _c.c_int, _c.c_void_p]),
@@ -179,7 +206,8 @@ class CompressJob(ctypes.Structure):
                 ("c_b", _c.c_void_p), ("z_b", _c.c_void_p), ("prev_c_b", _c.c_void_p),
                 ("prev_z_b", _c.c_void_p), ("bias_a", _c.c_void_p), ("bias_b", _c.c_void_p),
                 ("gain", _c.c_void_p), ("eps", _c.c_float), ("rope_dims", _c.c_int),
-                ("rope_base", _c.c_double), ("out", _c.c_void_p), ("out_bstride", _c.c_int64)]
+                ("rope_base", _c.c_double), ("out", _c.c_void_p), ("out_bstride", _c.c_int64),
+                ("out_kv_fp8", _c.c_int)]
 
 
 def _job_array(jobs, B, T, overlap, out_shape, first_out_none=False):
@@ -209,8 +237,21 @@ def _job_array(jobs, B, T, overlap, out_shape, first_out_none=False):
         _dev(c_a, *ts)
         _f32(j.get("bias_a")), _f32(j.get("bias_b")), _f32(j.get("gain"))
         shape = out_shape(D)
-        bs = j.get("out_bstride", 0) or shape[1] * D
-        if k == 0 and first_out_none:
+        fp8 = bool(j.get("out_kv_fp8", False))
+        if fp8:   # packed mixed BF16 / FP8 rows: [B, rows, row_bytes] uint8
+            rb = csa_kv_fp8_row_bytes(D, int(j.get("rope_dims", 0)))
+            shape = (shape[0], shape[1], rb)
+            bs = j.get("out_bstride", 0) or shape[1] * rb
+            if (out is None or tuple(out.shape) != shape or out.dtype != torch.uint8
+                    or not out.is_cuda or out.stride(2) != 1
+                    or (shape[1] > 1 and out.stride(1) != rb) or (B > 1 and out.stride(0) != bs)):
+                raise ValueError(f"out must be uint8 {list(shape)} with row stride {rb} and "
+                                 "batch stride out_bstride (bytes)")
+        else:
+            bs = j.get("out_bstride", 0) or shape[1] * D
+        if fp8:
+            pass
+        elif k == 0 and first_out_none:
             if out is not None or j.get("out_bstride", 0):
                 raise ValueError("job 0 takes no out here")
         elif (tuple(out.shape) != shape or out.dtype != c_a.dtype or not out.is_cuda
@@ -224,7 +265,7 @@ def _job_array(jobs, B, T, overlap, out_shape, first_out_none=False):
                              p(j.get("bias_b")), p(j.get("gain")), float(j.get("eps", 1e-6)),
                              int(j.get("rope_dims", 0)), float(j.get("rope_base", 10000.0)),
                              None if out is None else out.data_ptr(),
-                             int(j.get("out_bstride", 0)))
+                             int(j.get("out_bstride", 0)), int(fp8))
     return arr
 
 
@@ -421,6 +462,59 @@ def csa_decode_index_topk_mxfp4(q_idx, w_idx, k_codes, k_scales, n_entries, q_po
     return idx_out, score_out, all_scores
 
 
+def csa_decode_index_scores(q_idx, w_idx, n_entries, q_pos0, m, jobs, *, block_pos0=None,
+                            out=None, stream=None):
+    """The scoring half of csa_decode_index_topk: the closing block's fresh
+    entries (jobs as there), then the scores [B, Tq, N_cap] float32 of every
+    visible entry (later columns as they were).  Returns the scores."""
+    B, Tq, Hi, Di = q_idx.shape
+    N_cap = jobs[0]["out"].shape[1]
+    overlap = jobs[0].get("c_b") is not None
+    _dev(q_idx, w_idx, n_entries, q_pos0, block_pos0)
+    _f32(w_idx), _i64(q_pos0), _i64(block_pos0)
+    if n_entries.dtype != torch.int32:
+        raise TypeError("n_entries is int32")
+    if jobs[0]["c_a"].shape[1] != m:
+        raise ValueError("the jobs' streams hold one block of m tokens")
+    arr = _job_array(jobs, B, m, overlap, lambda D: (B, N_cap, D))
+    out = _scores_out(out, B, Tq, N_cap, q_idx.device)
+    st = lib().csa_decode_index_scores(_dt(q_idx), B, Tq, Hi, Di, N_cap, m, int(overlap),
+                                       _p(block_pos0), ctypes.cast(arr, ctypes.c_void_p),
+                                       len(jobs), _p(q_idx), _p(w_idx), _p(n_entries),
+                                       _p(q_pos0), _p(out), _stream(stream))
+    _check(st, "csa_decode_index_scores")
+    return out
+
+
+def csa_decode_index_scores_mxfp4(q_idx, w_idx, k_codes, k_scales, n_entries, q_pos0, m, jobs,
+                                  *, block_pos0=None, out=None, stream=None):
+    """csa_decode_index_scores with the indexer keys in MX FP4 (jobs[0] has
+    no ``out``; its fresh entry goes quantized into k_codes / k_scales)."""
+    B, Tq, Hi, Di = q_idx.shape
+    _dev(q_idx, w_idx, k_codes, k_scales, n_entries, q_pos0, block_pos0)
+    _f32(w_idx), _i64(q_pos0), _i64(block_pos0)
+    N_cap = _fp4_keys(k_codes, k_scales, Di)
+    if jobs[0]["c_a"].shape[1] != m:
+        raise ValueError("the jobs' streams hold one block of m tokens")
+    overlap = jobs[0].get("c_b") is not None
+    arr = _job_array(jobs, B, m, overlap, lambda D: (B, N_cap, D), first_out_none=True)
+    out = _scores_out(out, B, Tq, N_cap, q_idx.device)
+    st = lib().csa_decode_index_scores_mxfp4(
+        B, Tq, Hi, Di, N_cap, m, int(overlap), _p(block_pos0), ctypes.cast(arr, ctypes.c_void_p),
+        len(jobs), _p(q_idx), _p(w_idx), _p(k_codes), _p(k_scales), _p(n_entries), _p(q_pos0),
+        _p(out), _stream(stream))
+    _check(st, "csa_decode_index_scores_mxfp4")
+    return out
+
+
+def _scores_out(out, B, Tq, N_cap, device):
+    if out is None:
+        return torch.empty((B, Tq, N_cap), dtype=torch.float32, device=device)
+    if tuple(out.shape) != (B, Tq, N_cap) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out is a contiguous float32 [B, Tq, N_cap] tensor")
+    return out
+
+
 def csa_index_scores(q_idx, w_idx, k_idx, n_entries, q_pos0, m, *, out=None, stream=None):
     """Indexer scores of the visible entries (no selection).  Returns scores
     [B, Tq, N_cap] float32; columns past a query's visible count are left as
@@ -537,4 +631,137 @@ def hca_attn(q, pool, n_entries, m, win, win_pos0, W, sink, q_pos0, *, rope_dims
                         int(W), _p(sink), _p(q_pos0), _p(out), _p(lse), _p(ws),
                         0 if ws is None else ws.numel(), _stream(stream))
     _check(st, "hca_attn")
+    return out, lse
+
+
+# ------------------------------------------------- mixed BF16 / FP8 KV rows
+def csa_kv_fp8_row_bytes(D, rope_dims):
+    """Bytes of one packed mixed BF16 / FP8 KV row (0: shape not covered)."""
+    return int(lib().csa_kv_fp8_row_bytes(int(D), int(rope_dims)))
+
+
+def _fp8_pool(pool, D, rope_dims):
+    rb = csa_kv_fp8_row_bytes(D, rope_dims)
+    if rb == 0:
+        raise ValueError("packed FP8 rows need D = 512 and rope_dims a multiple of 32")
+    if pool.dtype != torch.uint8 or pool.dim() != 3 or pool.shape[2] != rb or not pool.is_contiguous():
+        raise ValueError(f"pool must be contiguous uint8 [B, N_cap, {rb}]")
+    return rb
+
+
+def csa_quantize_kv_fp8(x, rope_dims, *, out=None, stream=None):
+    """[..., D] float32/bf16 KV entries -> packed rows uint8 [..., row_bytes]."""
+    _dev(x)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    D = x.shape[-1]
+    rb = csa_kv_fp8_row_bytes(D, rope_dims)
+    rows = x.numel() // D if D else 0
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (rb,), dtype=torch.uint8, device=x.device)
+    st = lib().csa_quantize_kv_fp8(_dt(x), rows, D, int(rope_dims), _p(x), _p(out),
+                                   _stream(stream))
+    _check(st, "csa_quantize_kv_fp8")
+    return out
+
+
+def csa_dequantize_kv_fp8(rows_in, D, rope_dims, *, out=None, stream=None):
+    """Packed rows [..., row_bytes] -> their values as bf16 [..., D]."""
+    _dev(rows_in)
+    rb = csa_kv_fp8_row_bytes(D, rope_dims)
+    if rows_in.dtype != torch.uint8 or rows_in.shape[-1] != rb or not rows_in.is_contiguous():
+        raise ValueError(f"rows must be contiguous uint8 [..., {rb}]")
+    n = rows_in.numel() // rb
+    if out is None:
+        out = torch.empty(tuple(rows_in.shape[:-1]) + (D,), dtype=torch.bfloat16,
+                          device=rows_in.device)
+    st = lib().csa_dequantize_kv_fp8(n, int(D), int(rope_dims), _p(rows_in), _p(out),
+                                     _stream(stream))
+    _check(st, "csa_dequantize_kv_fp8")
+    return out
+
+
+def csa_compress_kvfp8(c_a, m, *, z_a=None, c_b=None, z_b=None, prev_c_b=None, prev_z_b=None,
+                       bias_a=None, bias_b=None, gain=None, eps=1e-6, rope_dims=0,
+                       rope_base=10000.0, pos0=None, out=None, out_bstride=0, ws=None,
+                       stream=None):
+    """csa_compress writing packed mixed BF16 / FP8 rows: returns out uint8
+    [B, ceil(T/m), row_bytes] (or writes the caller's ``out``, batch stride
+    ``out_bstride`` bytes)."""
+    B, T, D = c_a.shape
+    overlap = c_b is not None
+    _dev(c_a, z_a, c_b, z_b, prev_c_b, prev_z_b, bias_a, bias_b, gain, pos0)
+    _f32(bias_a), _f32(bias_b), _f32(gain), _i64(pos0)
+    n_out = -(-T // m)
+    rb = csa_kv_fp8_row_bytes(D, rope_dims)
+    if out is None:
+        out = torch.empty((B, n_out, rb), dtype=torch.uint8, device=c_a.device)
+    else:
+        bs = out_bstride if out_bstride else n_out * rb
+        if (tuple(out.shape) != (B, n_out, rb) or out.dtype != torch.uint8 or not out.is_cuda
+                or out.stride(2) != 1 or (n_out > 1 and out.stride(1) != rb)
+                or (B > 1 and out.stride(0) != bs)):
+            raise ValueError(f"out must be uint8 [B, ceil(T/m), {rb}] with batch stride "
+                             "out_bstride (bytes)")
+    need = csa_compress_ws_bytes(_dt(c_a), B, T, D, m, overlap)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=c_a.device)
+    if ws is not None and ws.numel() == 0:
+        ws = None
+    st = lib().csa_compress_kvfp8(_dt(c_a), B, T, D, m, int(overlap), _p(c_a), _p(z_a), _p(c_b),
+                                  _p(z_b), _p(prev_c_b), _p(prev_z_b), _p(bias_a), _p(bias_b),
+                                  _p(gain), float(eps), int(rope_dims), float(rope_base),
+                                  _p(pos0), _p(out), int(out_bstride), _p(ws),
+                                  0 if ws is None else ws.numel(), _stream(stream))
+    _check(st, "csa_compress_kvfp8")
+    return out
+
+
+def csa_sparse_attn_kvfp8(q, pool, idx, win, win_pos0, W, sink, q_pos0, *, rope_dims,
+                          rope_base=10000.0, scale=None, want_lse=False, out=None, ws=None,
+                          stream=None):
+    """csa_sparse_attn over packed mixed BF16 / FP8 pool rows."""
+    B, Tq, H, D = q.shape
+    _fp8_pool(pool, D, rope_dims)
+    N_cap = pool.shape[1]
+    K = idx.shape[2]
+    L_win = 0 if win is None else win.shape[1]
+    _dev(q, pool, idx, win, win_pos0, sink, q_pos0)
+    _f32(sink), _i64(q_pos0), _i64(win_pos0)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device) if want_lse else None
+    need = csa_attn_ws_bytes(B, Tq, H, D, K + W)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib().csa_sparse_attn_kvfp8(B, Tq, H, D, int(rope_dims), float(rope_base), float(scale),
+                                     _p(q), _p(pool), N_cap, _p(idx), K, _p(win), L_win,
+                                     _p(win_pos0), int(W), _p(sink), _p(q_pos0), _p(out), _p(lse),
+                                     _p(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _check(st, "csa_sparse_attn_kvfp8")
+    return out, lse
+
+
+def hca_attn_kvfp8(q, pool, n_entries, m, win, win_pos0, W, sink, q_pos0, *, rope_dims,
+                   rope_base=10000.0, scale=None, want_lse=False, out=None, ws=None, stream=None):
+    """hca_attn over packed mixed BF16 / FP8 pool rows."""
+    B, Tq, H, D = q.shape
+    _fp8_pool(pool, D, rope_dims)
+    N_cap = pool.shape[1]
+    L_win = 0 if win is None else win.shape[1]
+    _dev(q, pool, n_entries, win, win_pos0, sink, q_pos0)
+    _f32(sink), _i64(q_pos0), _i64(win_pos0)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device) if want_lse else None
+    need = csa_attn_ws_bytes(B, Tq, H, D, N_cap + W)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib().hca_attn_kvfp8(B, Tq, H, D, int(rope_dims), float(rope_base), float(scale), _p(q),
+                              _p(pool), N_cap, _p(n_entries), int(m), _p(win), L_win,
+                              _p(win_pos0), int(W), _p(sink), _p(q_pos0), _p(out), _p(lse),
+                              _p(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _check(st, "hca_attn_kvfp8")
     return out, lse

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
 SOURCES = ["abi.hip", "compress.hip", "indexer.hip", "topk.hip", "attn.hip", "mxfp4.hip",
-           "oproj.hip"]
+           "kvfp8.hip", "oproj.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

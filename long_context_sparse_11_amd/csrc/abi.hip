@@ -38,11 +38,15 @@ namespace {
 
 // Checks one compressor's arguments and fills its launch arguments.
 // Returns CSA_OK, an error, or 1 for "nothing to do" (B or T zero).
+// out_fp8: entries as packed mixed BF16 / FP8 rows (out_bstride in bytes).
+bool kv_fp8_shape_ok(int D, int R) { return D == 512 && R >= 0 && R <= D && R % 32 == 0; }
+
 int compress_args(int dt, int B, int T, int D, int m, int overlap, const void* c_a,
                   const void* z_a, const void* c_b, const void* z_b, const void* prev_c_b,
                   const void* prev_z_b, const float* bias_a, const float* bias_b,
                   const float* gain, float eps, int rope_dims, double rope_base,
-                  const int64_t* pos0, void* out, int64_t out_bstride, CompressArgs& a) {
+                  const int64_t* pos0, void* out, int64_t out_bstride, CompressArgs& a,
+                  int out_fp8 = 0) {
   if (dt != CSA_F32 && dt != CSA_BF16) return CSA_ERR_ARG;
   if (B < 0 || T < 0 || D <= 0 || m <= 0) return CSA_ERR_ARG;
   if (B == 0 || T == 0) return 1;
@@ -57,12 +61,15 @@ int compress_args(int dt, int B, int T, int D, int m, int overlap, const void* c
   if (rope_dims > 0 && (!pos0 || !(rope_base > 0.0))) return CSA_ERR_ARG;
   if (gain && !(eps >= 0.f)) return CSA_ERR_ARG;
   const int n_out = (T + m - 1) / m;
-  if (out_bstride != 0 && out_bstride < (int64_t)n_out * D) return CSA_ERR_ARG;
+  if (out_fp8 && !kv_fp8_shape_ok(D, rope_dims)) return CSA_ERR_UNSUPPORTED;
+  const int64_t row = out_fp8 ? kv_fp8_row_bytes_host(D, rope_dims) : D;
+  if (out_bstride != 0 && out_bstride < (int64_t)n_out * row) return CSA_ERR_ARG;
   if (m > 1024 || !is_pow2(D) || D > 1024 || D < (dt == CSA_BF16 ? 8 : 4)) return CSA_ERR_UNSUPPORTED;
   const double theta1 = rope_dims > 0 ? pow(rope_base, -2.0 / rope_dims) : 0.0;
   a = CompressArgs{dt, B, T, D, m, overlap ? 1 : 0, n_out, c_a, z_a, c_b, z_b, prev_c_b, prev_z_b,
                    bias_a, bias_b, gain, eps, rope_dims, theta1, pos0, out, out_bstride,
                    1, nullptr, 0};
+  a.out_fp8_row = out_fp8 ? (int)row : 0;
   return CSA_OK;
 }
 
@@ -87,6 +94,26 @@ CSA_EXPORT int csa_compress(int dt, int B, int T, int D, int m, int overlap, con
   return status_of(launch_compress(a, (hipStream_t)stream));
 }
 
+CSA_EXPORT int csa_compress_kvfp8(int dt, int B, int T, int D, int m, int overlap,
+                                  const void* c_a, const void* z_a, const void* c_b,
+                                  const void* z_b, const void* prev_c_b, const void* prev_z_b,
+                                  const float* bias_a, const float* bias_b, const float* gain,
+                                  float eps, int rope_dims, double rope_base, const int64_t* pos0,
+                                  void* out, int64_t out_bstride, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  CompressArgs a;
+  const int st = compress_args(dt, B, T, D, m, overlap, c_a, z_a, c_b, z_b, prev_c_b, prev_z_b,
+                               bias_a, bias_b, gain, eps, rope_dims, rope_base, pos0, out,
+                               out_bstride, a, 1);
+  if (st == 1) return CSA_OK;
+  if (st != CSA_OK) return st;
+  if (ws && ws_bytes < compress_ws_bytes(dt, B, a.n_out, D, m * (overlap ? 2 : 1)))
+    return CSA_ERR_WORKSPACE;
+  a.ws_y = (float*)ws;
+  a.ws_bytes = ws ? ws_bytes : 0;
+  return status_of(launch_compress(a, (hipStream_t)stream));
+}
+
 CSA_EXPORT int csa_compress_batch(int dt, int B, int T, int m, int overlap, const int64_t* pos0,
                                   const csa_compress_job* jobs, int n_jobs, void* stream) {
   if (n_jobs < 1 || n_jobs > 2 || !jobs) return CSA_ERR_ARG;
@@ -96,7 +123,8 @@ CSA_EXPORT int csa_compress_batch(int dt, int B, int T, int m, int overlap, cons
     const csa_compress_job& j = jobs[k];
     const int st = compress_args(dt, B, T, j.D, m, overlap, j.c_a, j.z_a, j.c_b, j.z_b,
                                  j.prev_c_b, j.prev_z_b, j.bias_a, j.bias_b, j.gain, j.eps,
-                                 j.rope_dims, j.rope_base, pos0, j.out, j.out_bstride, a[k]);
+                                 j.rope_dims, j.rope_base, pos0, j.out, j.out_bstride, a[k],
+                                 j.out_kv_fp8 ? 1 : 0);
     if (st == 1) nothing = 1;
     else if (st != CSA_OK) return st;
   }
@@ -122,9 +150,32 @@ CSA_EXPORT size_t csa_index_topk_ws_bytes(int B, int Tq, int Hi, int N_cap, int 
 
 namespace {
 
+// Indexer scores of every visible entry, optionally preceded by the
+// fresh-entry compressors of a decode step (fused into the indexer launch
+// when its kernel covers the shape, else a compressor launch first).
+// Arguments already validated; N_cap > 0.
+int index_scores_run(int dt, int B, int Tq, int Hi, int Di, int N_cap, int m, const void* q_idx,
+                     const float* w_idx, const void* k_idx, const uint8_t* k_scales,
+                     const int32_t* n_entries, const int64_t* q_pos0, float* scores,
+                     const FreshJobs* fresh, hipStream_t s) {
+  IndexArgs ia{dt, B, Tq, Hi, Di, N_cap, m, q_idx, w_idx, k_idx, n_entries, q_pos0, scores,
+               k_scales};
+  hipError_t e;
+  const bool fused = fresh && index_fresh_fused(ia, *fresh);
+  // FP4 fresh keys are written only by the fused launch
+  if (fresh && !fused && fresh->job[0].out_scales) return CSA_ERR_UNSUPPORTED;
+  if (fused) {
+    e = launch_index_fresh(ia, *fresh, s);
+  } else {
+    e = fresh ? launch_compress_batch(fresh->job, min(fresh->n_jobs, 2), s) : hipSuccess;
+    if (e == hipSuccess && fresh && fresh->n_jobs == 3) e = launch_compress(fresh->job[2], s);
+    if (e == hipSuccess) e = launch_index_scores(ia, s);
+  }
+  return status_of(e);
+}
+
 // Indexer scores and top-K, optionally preceded by the fresh-entry
-// compressors of a decode step (fused into the indexer launch when its
-// kernel covers the shape, else a compressor launch first).
+// compressors of a decode step (index_scores_run), then the selection.
 int index_topk_run(int dt, int B, int Tq, int Hi, int Di, int N_cap, int K, int m,
                    const void* q_idx, const float* w_idx, const void* k_idx,
                    const uint8_t* k_scales, const int32_t* n_entries, const int64_t* q_pos0, int32_t* idx_out,
@@ -147,20 +198,9 @@ int index_topk_run(int dt, int B, int Tq, int Hi, int Di, int N_cap, int K, int 
   w += align256(q * (size_t)N_cap * sizeof(float));
 
   if (N_cap > 0) {
-    IndexArgs ia{dt, B, Tq, Hi, Di, N_cap, m, q_idx, w_idx, k_idx, n_entries, q_pos0, scores,
-                 k_scales};
-    hipError_t e;
-    const bool fused = fresh && index_fresh_fused(ia, *fresh);
-    // FP4 fresh keys are written only by the fused launch
-    if (fresh && !fused && fresh->job[0].out_scales) return CSA_ERR_UNSUPPORTED;
-    if (fused) {
-      e = launch_index_fresh(ia, *fresh, s);
-    } else {
-      e = fresh ? launch_compress_batch(fresh->job, min(fresh->n_jobs, 2), s) : hipSuccess;
-      if (e == hipSuccess && fresh && fresh->n_jobs == 3) e = launch_compress(fresh->job[2], s);
-      if (e == hipSuccess) e = launch_index_scores(ia, s);
-    }
-    if (e != hipSuccess) return CSA_ERR_HIP;
+    const int st = index_scores_run(dt, B, Tq, Hi, Di, N_cap, m, q_idx, w_idx, k_idx, k_scales,
+                                    n_entries, q_pos0, scores, fresh, s);
+    if (st != CSA_OK) return st;
   }
   const int nc = topk_chunks(N_cap);
   TopkArgs ta{};
@@ -230,7 +270,8 @@ int decode_jobs(int dt, int B, int Tq, int N_cap, int m, int overlap, const int6
   for (int k = 0; k < n_jobs; ++k) {
     const csa_compress_job& j = jobs[k];
     if (k == 2) {  // the step token's window row: m = 1, ring slot q_pos0[b] % L_win
-      if (Tq != 1 || !q_pos0 || j.D <= 0 || j.out_bstride <= 0 || j.out_bstride % j.D)
+      if (Tq != 1 || !q_pos0 || j.D <= 0 || j.out_bstride <= 0 || j.out_bstride % j.D ||
+          j.out_kv_fp8)
         return CSA_ERR_ARG;
       const int st = compress_args(dt, B, 1, j.D, 1, 0, j.c_a, j.z_a, j.c_b, j.z_b, j.prev_c_b,
                                    j.prev_z_b, j.bias_a, j.bias_b, j.gain, j.eps, j.rope_dims,
@@ -240,12 +281,17 @@ int decode_jobs(int dt, int B, int Tq, int N_cap, int m, int overlap, const int6
       f.job[2].slices = 1;
       continue;
     }
-    const int64_t pool_stride = (int64_t)N_cap * j.D;
+    // the KV job (jobs[1]) may store packed mixed BF16 / FP8 rows
+    if (j.out_kv_fp8 && k != 1) return CSA_ERR_ARG;
+    if (j.out_kv_fp8 && !kv_fp8_shape_ok(j.D, j.rope_dims)) return CSA_ERR_UNSUPPORTED;
+    const int64_t pool_stride =
+        (int64_t)N_cap * (j.out_kv_fp8 ? kv_fp8_row_bytes_host(j.D, j.rope_dims) : j.D);
     if (j.out_bstride != 0 && j.out_bstride != pool_stride) return CSA_ERR_ARG;
     void* out = (k == 0 && key_codes) ? key_codes : j.out;
     const int st = compress_args(dt, B, m, j.D, m, overlap, j.c_a, j.z_a, j.c_b, j.z_b,
                                  j.prev_c_b, j.prev_z_b, j.bias_a, j.bias_b, j.gain, j.eps,
-                                 j.rope_dims, j.rope_base, block_pos0, out, pool_stride, f.job[k]);
+                                 j.rope_dims, j.rope_base, block_pos0, out, pool_stride, f.job[k],
+                                 j.out_kv_fp8 ? 1 : 0);
     if (st != CSA_OK) return st == 1 ? CSA_ERR_ARG : st;
     f.job[k].rows_at = n_entries;
     f.job[k].rows_cap = N_cap;
@@ -299,6 +345,64 @@ CSA_EXPORT int csa_decode_index_topk_mxfp4(int B, int Tq, int Hi, int Di, int N_
   return index_topk_run(CSA_BF16, B, Tq, Hi, Di, N_cap, K, m, q_idx, w_idx, k_codes, k_scales,
                         n_entries, q_pos0, idx_out, score_out, all_scores, ws, ws_bytes, &f,
                         (hipStream_t)stream);
+}
+
+namespace {
+
+// Shape and pointer checks shared by the two decode-scores calls.
+int decode_scores_args(int B, int Tq, int Hi, int Di, int N_cap, int m, const void* q_idx,
+                       const float* w_idx, const int32_t* n_entries, const int64_t* q_pos0,
+                       const float* scores) {
+  if (B < 0 || Tq < 0 || Hi <= 0 || Di <= 0 || N_cap < 0 || m <= 0) return CSA_ERR_ARG;
+  if (B == 0 || Tq == 0) return 1;
+  if (N_cap == 0) return CSA_ERR_ARG;  // the fresh entries need a row
+  if (!q_idx || !w_idx || !n_entries || !q_pos0 || !scores) return CSA_ERR_ARG;
+  if (Hi > 64 || Di > 256 || Hi * Di > 8192 || N_cap > (1 << 26)) return CSA_ERR_UNSUPPORTED;
+  return CSA_OK;
+}
+
+}  // namespace
+
+CSA_EXPORT int csa_decode_index_scores(int dt, int B, int Tq, int Hi, int Di, int N_cap, int m,
+                                       int overlap, const int64_t* block_pos0,
+                                       const csa_compress_job* jobs, int n_jobs,
+                                       const void* q_idx, const float* w_idx,
+                                       const int32_t* n_entries, const int64_t* q_pos0,
+                                       float* scores, void* stream) {
+  if (dt != CSA_F32 && dt != CSA_BF16) return CSA_ERR_ARG;
+  if (n_jobs < 1 || n_jobs > 3 || !jobs) return CSA_ERR_ARG;
+  if (jobs[0].D != Di) return CSA_ERR_ARG;
+  const int st0 = decode_scores_args(B, Tq, Hi, Di, N_cap, m, q_idx, w_idx, n_entries, q_pos0,
+                                     scores);
+  if (st0 != CSA_OK) return st0 == 1 ? CSA_OK : st0;
+  FreshJobs f;
+  const int st = decode_jobs(dt, B, Tq, N_cap, m, overlap, block_pos0, jobs, n_jobs, nullptr,
+                             nullptr, n_entries, q_pos0, f);
+  if (st != CSA_OK) return st;
+  return index_scores_run(dt, B, Tq, Hi, Di, N_cap, m, q_idx, w_idx, jobs[0].out, nullptr,
+                          n_entries, q_pos0, scores, &f, (hipStream_t)stream);
+}
+
+CSA_EXPORT int csa_decode_index_scores_mxfp4(int B, int Tq, int Hi, int Di, int N_cap, int m,
+                                             int overlap, const int64_t* block_pos0,
+                                             const csa_compress_job* jobs, int n_jobs,
+                                             const void* q_idx, const float* w_idx,
+                                             uint8_t* k_codes, uint8_t* k_scales,
+                                             const int32_t* n_entries, const int64_t* q_pos0,
+                                             float* scores, void* stream) {
+  if (n_jobs < 1 || n_jobs > 3 || !jobs) return CSA_ERR_ARG;
+  if (jobs[0].D != Di || Di <= 0 || Di % 32) return CSA_ERR_ARG;
+  if (jobs[0].out || jobs[0].out_bstride) return CSA_ERR_ARG;  // the key job writes k_codes
+  const int st0 = decode_scores_args(B, Tq, Hi, Di, N_cap, m, q_idx, w_idx, n_entries, q_pos0,
+                                     scores);
+  if (st0 != CSA_OK) return st0 == 1 ? CSA_OK : st0;
+  if (!k_codes || !k_scales) return CSA_ERR_ARG;
+  FreshJobs f;
+  const int st = decode_jobs(CSA_BF16, B, Tq, N_cap, m, overlap, block_pos0, jobs, n_jobs,
+                             k_codes, k_scales, n_entries, q_pos0, f);
+  if (st != CSA_OK) return st;
+  return index_scores_run(CSA_BF16, B, Tq, Hi, Di, N_cap, m, q_idx, w_idx, k_codes, k_scales,
+                          n_entries, q_pos0, scores, &f, (hipStream_t)stream);
 }
 
 CSA_EXPORT int csa_index_scores(int dt, int B, int Tq, int Hi, int Di, int N_cap, int m,
@@ -379,6 +483,34 @@ CSA_EXPORT int csa_quantize_mxfp4(int dt, int64_t rows, int D, const void* x, ui
   return status_of(launch_mxfp4_quantize(dt, rows, D, x, codes, scales, (hipStream_t)stream));
 }
 
+// -------------------------------------------------- mixed BF16 / FP8 KV rows
+CSA_EXPORT size_t csa_kv_fp8_row_bytes(int D, int rope_dims) {
+  if (!kv_fp8_shape_ok(D, rope_dims)) return 0;
+  return (size_t)kv_fp8_row_bytes_host(D, rope_dims);
+}
+
+CSA_EXPORT int csa_quantize_kv_fp8(int dt, int64_t rows, int D, int rope_dims, const void* x,
+                                   void* out, void* stream) {
+  if (dt != CSA_F32 && dt != CSA_BF16) return CSA_ERR_ARG;
+  if (rows < 0 || D <= 0 || rope_dims < 0 || rope_dims > D) return CSA_ERR_ARG;
+  if (!kv_fp8_shape_ok(D, rope_dims)) return CSA_ERR_UNSUPPORTED;
+  if (rows == 0) return CSA_OK;
+  if (!x || !out) return CSA_ERR_ARG;
+  if (rows > ((int64_t)1 << 39) / D) return CSA_ERR_UNSUPPORTED;  // grid bound
+  return status_of(launch_kv_fp8_quantize(dt, rows, D, rope_dims, x, out, (hipStream_t)stream));
+}
+
+CSA_EXPORT int csa_dequantize_kv_fp8(int64_t rows, int D, int rope_dims, const void* rows_in,
+                                     void* out, void* stream) {
+  if (rows < 0 || D <= 0 || rope_dims < 0 || rope_dims > D) return CSA_ERR_ARG;
+  if (!kv_fp8_shape_ok(D, rope_dims)) return CSA_ERR_UNSUPPORTED;
+  if (rows == 0) return CSA_OK;
+  if (!rows_in || !out) return CSA_ERR_ARG;
+  if (rows > ((int64_t)1 << 39) / D) return CSA_ERR_UNSUPPORTED;
+  return status_of(launch_kv_fp8_dequantize(rows, D, rope_dims, rows_in, out,
+                                            (hipStream_t)stream));
+}
+
 // ------------------------------------------------------------------ attention
 CSA_EXPORT size_t csa_attn_ws_bytes(int B, int Tq, int H, int D, int keys_per_query) {
   if (B <= 0 || Tq <= 0 || H <= 0 || D <= 0 || keys_per_query <= 0) return 0;
@@ -400,6 +532,10 @@ int attn_common(AttnArgs& a, double rope_base, int keys_per_query, void* ws, siz
   if (a.R < 0 || a.R > a.D || (a.R & 1) || (a.R > 0 && !(rope_base > 0.0))) return CSA_ERR_ARG;
   if (a.D > 1024 || a.H > 128 || (a.D & 1)) return CSA_ERR_UNSUPPORTED;
   a.rope_theta1 = a.R > 0 ? pow(rope_base, -2.0 / a.R) : 0.0;
+  // packed mixed BF16 / FP8 pool rows: the bf16 MFMA kernels only
+  if (a.pool_row_bytes > 0 &&
+      (!attn_uses_mfma(a.dt, a.H, a.D, a.R) || !kv_fp8_shape_ok(a.D, a.R)))
+    return CSA_ERR_UNSUPPORTED;
   if (attn_uses_mfma(a.dt, a.H, a.D, a.R)) {
     if (a.csa && (int64_t)keys_per_query > attn_max_csa_keys()) return CSA_ERR_UNSUPPORTED;
     a.splits = attn_splits(a.dt, a.B, a.Tq, a.H, a.D, keys_per_query);
@@ -433,6 +569,45 @@ CSA_EXPORT int csa_sparse_attn(int dt, int B, int Tq, int H, int D, int rope_dim
   a.win = win; a.L_win = L_win; a.win_pos0 = win_pos0; a.W = W;
   a.sink = sink; a.q_pos0 = q_pos0; a.out = out; a.lse = lse;
   return attn_common(a, rope_base, K + W, ws, ws_bytes, (hipStream_t)stream);
+}
+
+CSA_EXPORT int csa_sparse_attn_kvfp8(int B, int Tq, int H, int D, int rope_dims,
+                                     double rope_base, float scale, const void* q,
+                                     const void* pool, int N_cap, const int32_t* idx, int K,
+                                     const void* win, int L_win, const int64_t* win_pos0, int W,
+                                     const float* sink, const int64_t* q_pos0, void* out,
+                                     float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (K < 0) return CSA_ERR_ARG;
+  if (K > 0 && !idx) return CSA_ERR_ARG;
+  if (!kv_fp8_shape_ok(D, rope_dims)) return CSA_ERR_UNSUPPORTED;
+  AttnArgs a{};
+  a.dt = CSA_BF16; a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.R = rope_dims;
+  a.scale = scale;
+  a.q = q; a.pool = pool; a.N_cap = N_cap; a.csa = 1; a.idx = idx; a.K = K;
+  a.n_entries = nullptr; a.m = 1;
+  a.win = win; a.L_win = L_win; a.win_pos0 = win_pos0; a.W = W;
+  a.sink = sink; a.q_pos0 = q_pos0; a.out = out; a.lse = lse;
+  a.pool_row_bytes = kv_fp8_row_bytes_host(D, rope_dims);
+  return attn_common(a, rope_base, K + W, ws, ws_bytes, (hipStream_t)stream);
+}
+
+CSA_EXPORT int hca_attn_kvfp8(int B, int Tq, int H, int D, int rope_dims, double rope_base,
+                              float scale, const void* q, const void* pool, int N_cap,
+                              const int32_t* n_entries, int m, const void* win, int L_win,
+                              const int64_t* win_pos0, int W, const float* sink,
+                              const int64_t* q_pos0, void* out, float* lse, void* ws,
+                              size_t ws_bytes, void* stream) {
+  if (m <= 0 || !n_entries) return CSA_ERR_ARG;
+  if (!kv_fp8_shape_ok(D, rope_dims)) return CSA_ERR_UNSUPPORTED;
+  AttnArgs a{};
+  a.dt = CSA_BF16; a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.R = rope_dims;
+  a.scale = scale;
+  a.q = q; a.pool = pool; a.N_cap = N_cap; a.csa = 0; a.idx = nullptr; a.K = 0;
+  a.n_entries = n_entries; a.m = m;
+  a.win = win; a.L_win = L_win; a.win_pos0 = win_pos0; a.W = W;
+  a.sink = sink; a.q_pos0 = q_pos0; a.out = out; a.lse = lse;
+  a.pool_row_bytes = kv_fp8_row_bytes_host(D, rope_dims);
+  return attn_common(a, rope_base, N_cap + W, ws, ws_bytes, (hipStream_t)stream);
 }
 
 CSA_EXPORT int hca_attn(int dt, int B, int Tq, int H, int D, int rope_dims, double rope_base,

@@ -232,7 +232,16 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 // is the head group: half the query slice and half the partial output per
 // workgroup, twice the workgroups.  A workgroup's rows and partials go
 // through one compute unit, whose own rate bounds these short workgroups.
-template <bool CSA, bool MULTI, int NW>
+//
+// FP8: the pool rows are packed mixed BF16 / FP8 rows (pool_row_bytes each:
+// the non-RoPE channels as E4M3 codes with one E8M0 scale per 32 channels,
+// the RoPE channels in bf16).  A pool row is copied raw into a staging row
+// of LDS (the same buffer loads into LDS, 16 bytes per lane), and each wave,
+// once its own copies have landed, converts its rows into the bf16 tile with
+// v_cvt_scalef32_pk_bf16_fp8 (exact: an E4M3 value times a power of two fits
+// bf16); window rows stay bf16 and are copied as before.  Everything after
+// the tile copy is unchanged.
+template <bool CSA, bool MULTI, int NW, bool FP8>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_hs(AttnArgs a) {
   constexpr int RPW = kHsRows / NW;  // tile rows each wave copies
@@ -243,6 +252,9 @@ void attn_hs(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t s_rows1[kHsRows * kAtD];
   __shared__ float s_cos[kAtD / 2], s_sin[kAtD / 2];
   __shared__ __attribute__((aligned(16))) int32_t s_idx[MULTI && CSA ? kHsMaxSplitRows : 4];
+  // FP8: raw pool rows, one 1 KiB slot per tile row (a row's copy fills its
+  // first pool_row_bytes; the lanes past it read nothing)
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[FP8 ? kHsRows * 1024 : 16];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -284,7 +296,6 @@ void attn_hs(AttnArgs a) {
     start = min(L, sp * per);
     end = min(L, start + per);
   }
-  const bf16_t* pool_b = (const bf16_t*)a.pool + (int64_t)b * a.N_cap * kAtD;
   const bf16_t* win_b = (const bf16_t*)a.win + (int64_t)b * a.L_win * kAtD;
   const bf16_t* dummy = (const bf16_t*)a.q + (int64_t)qi * a.H * kAtD;  // 1 KiB always readable
 
@@ -296,10 +307,14 @@ void attn_hs(AttnArgs a) {
   // its lane into scalar registers and lane i fetches the 16-byte chunk that
   // belongs at position i (i ^ hs_swz(row)).
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const uint64_t pool_a = (uint64_t)pool_b, win_a = (uint64_t)win_b, dummy_a = (uint64_t)dummy;
+  const uint64_t pool_a = (uint64_t)((const uint8_t*)a.pool +
+                                     (int64_t)b * a.N_cap * (FP8 ? a.pool_row_bytes : kAtD * 2));
+  const uint64_t win_a = (uint64_t)win_b, dummy_a = (uint64_t)dummy;
+  const int64_t pool_rb = FP8 ? a.pool_row_bytes : kAtD * 2;
   struct TileSrc {
     int lo, hi;  // this lane's row address
     uint32_t mask;
+    uint32_t fp8;  // FP8: rows read from the pool (converted after the copy)
   };
   auto resolve_tile = [&](int j0, int sidx_l) -> TileSrc {
     const int jj = j0 + (lane & 31);
@@ -309,15 +324,26 @@ void attn_hs(AttnArgs a) {
     if (wrow >= a.L_win) wrow -= a.L_win;
     const bool valid =
         lane < 32 && jj < end && (in_sel ? (srow >= 0 && srow < a.N_cap) : jj - kr.nsel < kr.nwin);
-    const uint64_t sa = in_sel ? pool_a + (uint64_t)((int64_t)srow * (kAtD * 2))
+    const uint64_t sa = in_sel ? pool_a + (uint64_t)((int64_t)srow * pool_rb)
                                : win_a + (uint64_t)((int64_t)wrow * (kAtD * 2));
     const uint64_t src = valid ? sa : dummy_a;
-    return TileSrc{(int)(uint32_t)src, (int)(uint32_t)(src >> 32), (uint32_t)__ballot(valid)};
+    return TileSrc{(int)(uint32_t)src, (int)(uint32_t)(src >> 32), (uint32_t)__ballot(valid),
+                   FP8 ? (uint32_t)__ballot(valid && in_sel) : 0u};
   };
   auto issue_row = [&](const TileSrc& ts, int u, bf16_t* dst) {
     const int r = RPW * wv + u;
     const uint64_t rs = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(ts.hi, r) << 32) |
                         (uint32_t)__builtin_amdgcn_readlane(ts.lo, r);
+    if (FP8 && ((ts.fp8 >> r) & 1u)) {
+      // a packed pool row, raw into its staging slot: lane i copies bytes
+      // 16 i .. 16 i + 15; lanes past the row's end fall outside the
+      // descriptor's range and read nothing
+      const __amdgpu_buffer_rsrc_t rsrc =
+          __builtin_amdgcn_make_buffer_rsrc((void*)rs, (short)0, a.pool_row_bytes, kRawBufferWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)(s_stage + r * 1024), 16,
+                                               16 * lane, 0, 0, 0);
+      return;
+    }
     // a buffer load (not a global one): it counts on vmcnt only, so the
     // LDS reads issued around it keep exact lgkmcnt waits
     const __amdgpu_buffer_rsrc_t rsrc =
@@ -325,14 +351,61 @@ void attn_hs(AttnArgs a) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)(dst + r * kAtD), 16,
                                              16 * (lane ^ hs_swz(r)), 0, 0, 0);
   };
+  // FP8: this wave's staged pool rows into the bf16 tile (after its copies
+  // have landed: the caller waits on vmcnt).  Lane l < nc holds channels
+  // 8l .. 8l+7 (8 code bytes, the scale of their 32-channel block); the
+  // other lanes one 16-byte chunk of the bf16 RoPE channels.  Each lane
+  // writes its 16-byte chunk l of the row at the tile's swizzled position.
+  // The reads of a batch of rows are all issued before the first conversion
+  // (the LDS latency is paid once per batch, not once per row); every lane
+  // reads 16 bytes of its row (codes in the low half), its scale byte, and
+  // rows that are not staged are read and dropped.
+  const int nc = (kAtD - R) >> 3;
+  const int src_off = lane < nc ? 8 * lane : (kAtD - R) + 16 * (lane - nc);
+  const int scl_off = kAtD + R + (lane < nc ? lane >> 2 : 0);
+  auto convert_rows = [&](uint32_t fp8_rows, bf16_t* dst) {
+    constexpr int BATCH = RPW < 4 ? RPW : 4;
+#pragma unroll
+    for (int u0 = 0; u0 < RPW; u0 += BATCH) {
+      u32x4_t raw[BATCH];
+      uint32_t sb[BATCH];
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) {
+        const uint8_t* st = s_stage + (RPW * wv + u0 + k) * 1024;
+        if (lane < nc) {
+          const uint2 c8 = *reinterpret_cast<const uint2*>(st + src_off);
+          raw[k] = u32x4_t{c8.x, c8.y, 0u, 0u};
+        } else {
+          raw[k] = *reinterpret_cast<const u32x4_t*>(st + src_off);
+        }
+        sb[k] = st[scl_off];
+      }
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) {
+        const int r = RPW * wv + u0 + k;
+        if (!((fp8_rows >> r) & 1u)) continue;
+        u32x4_t w = raw[k];
+        if (lane < nc) {
+          const float sc = mx_scale_value(sb[k]);
+          const uint32_t lo = raw[k][0], hi = raw[k][1];
+          w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, false));
+          w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, true));
+          w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, false));
+          w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, true));
+        }
+        *reinterpret_cast<u32x4_t*>(dst + r * kAtD + 8 * (lane ^ hs_swz(r))) = w;
+      }
+    }
+  };
 
   // ---- prologue: tile 0's rows, the rope table, the split's later indices
-  uint32_t vmask;
+  uint32_t vmask, fp8_0 = 0;
   {
     const TileSrc t0 = resolve_tile(start, idx0);
 #pragma unroll
     for (int u = 0; u < RPW; ++u) issue_row(t0, u, s_rows0);
     vmask = t0.mask;
+    fp8_0 = t0.fp8;
   }
   for (int p = tid; p < R / 2; p += 64 * NW) rope_cos_sin(tpos, p, a.rope_theta1, s_cos[p], s_sin[p]);
   if constexpr (MULTI && CSA) {
@@ -341,6 +414,7 @@ void attn_hs(AttnArgs a) {
       s_idx[jj - start] = a.idx[(int64_t)qi * a.K + jj];
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (FP8) convert_rows(fp8_0, s_rows0);
   __syncthreads();
 
   // rotate the query slice's rope channels at +tpos (each lane its own pairs)
@@ -374,7 +448,7 @@ void attn_hs(AttnArgs a) {
     // multi-tile splits request the next tile while this one is used; past
     // the split's end every row is invalid and the copy reads the harmless
     // row into the idle buffer, so the request is unconditional
-    TileSrc nt{0, 0, 0u};
+    TileSrc nt{0, 0, 0u, 0u};
     if constexpr (MULTI) {
       const int jn = j0 + kHsRows;
       int sidx_l = 0;
@@ -499,6 +573,7 @@ void attn_hs(AttnArgs a) {
     if constexpr (MULTI) {
       // the next tile's rows have landed and every wave is done with this one
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if constexpr (FP8) convert_rows(nt.fp8, next);
       __syncthreads();
       vmask = nt.mask;
     }
@@ -677,6 +752,21 @@ static hipError_t launch_generic(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <bool FP8>
+static void launch_hs(const AttnArgs& a, bool multi, bool halves, dim3 grid, dim3 grid2,
+                      hipStream_t stream) {
+  const dim3 block4(256), block2(128);
+  if (a.csa) {
+    if (multi) hipLaunchKernelGGL((attn_hs<true, true, 4, FP8>), grid, block4, 0, stream, a);
+    else if (halves) hipLaunchKernelGGL((attn_hs<true, false, 2, FP8>), grid2, block2, 0, stream, a);
+    else hipLaunchKernelGGL((attn_hs<true, false, 4, FP8>), grid, block4, 0, stream, a);
+  } else {
+    if (multi) hipLaunchKernelGGL((attn_hs<false, true, 4, FP8>), grid, block4, 0, stream, a);
+    else if (halves) hipLaunchKernelGGL((attn_hs<false, false, 2, FP8>), grid2, block2, 0, stream, a);
+    else hipLaunchKernelGGL((attn_hs<false, false, 4, FP8>), grid, block4, 0, stream, a);
+  }
+}
+
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.B * a.Tq == 0) return hipSuccess;
   if (attn_uses_mfma(a.dt, a.H, a.D, a.R)) {
@@ -689,16 +779,11 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
     // single-tile splits in head groups of 32 (two waves, grid z) while the
     // doubled grid still fits the compute units once
     const bool halves = !multi && 2LL * hg * a.splits * a.B * a.Tq <= kHsHeadSplitBelow;
-    dim3 grid2(a.splits, a.B * a.Tq, 2 * hg), block4(256), block2(128);
-    if (a.csa) {
-      if (multi) hipLaunchKernelGGL((attn_hs<true, true, 4>), grid, block4, 0, stream, a);
-      else if (halves) hipLaunchKernelGGL((attn_hs<true, false, 2>), grid2, block2, 0, stream, a);
-      else hipLaunchKernelGGL((attn_hs<true, false, 4>), grid, block4, 0, stream, a);
-    } else {
-      if (multi) hipLaunchKernelGGL((attn_hs<false, true, 4>), grid, block4, 0, stream, a);
-      else if (halves) hipLaunchKernelGGL((attn_hs<false, false, 2>), grid2, block2, 0, stream, a);
-      else hipLaunchKernelGGL((attn_hs<false, false, 4>), grid, block4, 0, stream, a);
-    }
+    dim3 grid2(a.splits, a.B * a.Tq, 2 * hg);
+    if (a.pool_row_bytes > 0)
+      launch_hs<true>(a, multi, halves, grid, grid2, stream);
+    else
+      launch_hs<false>(a, multi, halves, grid, grid2, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
     hipLaunchKernelGGL(attn_combine<bf16_t>, dim3(a.B * a.Tq, a.H), dim3(128), 0, stream, a);

@@ -138,15 +138,21 @@ __device__ __forceinline__ double rope_theta(double theta1, int j) {
   return th;
 }
 
-__device__ __forceinline__ void rope_cos_sin(int64_t pos, int j, double theta1, float& c, float& s) {
+// cos / sin of pos * theta (theta_j from rope_theta), the angle reduced in
+// float64 as above.
+__device__ __forceinline__ void rope_cos_sin_theta(int64_t pos, double theta, float& c, float& s) {
   constexpr double kTwoPiHi = 6.283185307179586;        // nearest double to 2*pi
   constexpr double kTwoPiLo = 2.4492935982947064e-16;   // 2*pi - kTwoPiHi
   constexpr double kInvTwoPi = 0.15915494309189535;
-  const double phi = (double)pos * rope_theta(theta1, j);
+  const double phi = (double)pos * theta;
   const double k = rint(phi * kInvTwoPi);
   double r = fma(-k, kTwoPiHi, phi);
   r = fma(-k, kTwoPiLo, r);
   sincosf((float)r, &s, &c);
+}
+
+__device__ __forceinline__ void rope_cos_sin(int64_t pos, int j, double theta1, float& c, float& s) {
+  rope_cos_sin_theta(pos, rope_theta(theta1, j), c, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -269,6 +275,41 @@ __device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t codes, float scale) {
   const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
   const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
   return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// ------------------------------------------------------ MX FP8 KV entries
+// KV entries in mixed precision: the R RoPE channels in bfloat16, the other
+// D - R channels in the OCP Microscaling FP8 format (E4M3 elements: sign bit
+// 7, exponent field bits 3-6 with bias 7, mantissa bits 0-2, exponent field
+// 0 subnormal in units of 2^-9, largest finite magnitude 448; one E8M0 scale
+// byte s = 2^(s - 127) per 32 channels, s = floor(log2 amax) - 8).  Packed
+// row: D - R code bytes, then the 2R bytes of the bfloat16 channels, then the
+// (D - R) / 32 scale bytes zero-padded to a multiple of 16.
+
+__device__ __forceinline__ int kv_fp8_scale_pad(int D, int R) {
+  return 16 * ((((D - R) / 32) + 15) / 16);
+}
+
+// E8M0 scale byte of a block with largest magnitude amax (finite, >= 0):
+// the exponent field minus 8, at least 0.
+__device__ __forceinline__ uint32_t mx8_scale_byte(float amax) {
+  const uint32_t ef = __float_as_uint(amax) >> 23;
+  return ef > 8u ? ef - 8u : 0u;
+}
+
+// E4M3 code of x under scale byte s: a = |x| / 2^(s-127) lies below 512.
+// With e = max(floor(log2 a), -6) (-6: the subnormal range shares the
+// smallest normal exponent's step), a * 2^(3-e) is exact and its rounding to
+// an integer q in [0, 16] (nearest, ties to even) is the rounding of the
+// mantissa to 3 bits; the code is 8 (e + 7) + q - 8, which carries into the
+// exponent when q = 16 and equals q itself in the subnormal range.  Codes
+// above 0x7E (448) saturate there.
+__device__ __forceinline__ uint32_t e4m3_code(float x, uint32_t s) {
+  const float a = ldexpf(fabsf(x), 127 - (int)s);
+  const int e = max((int)(__float_as_uint(a) >> 23) - 127, -6);
+  const float q = rintf(ldexpf(a, 3 - e));
+  const uint32_t c = min((uint32_t)(8 * (e + 7) + (int)q - 8), 126u);
+  return c | (x < 0.f ? 0x80u : 0u);
 }
 
 }  // namespace csa

@@ -193,9 +193,16 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a0, Compress
     }
   }
 
-  const int64_t bstride = a.out_bstride ? a.out_bstride : (int64_t)a.n_out * D;
   const int64_t ent = compress_out_row(a, b, i);
   if (ent < 0) return;
+  if constexpr (VEC == 8) {
+    if (a.out_fp8_row > 0) {  // packed mixed BF16 / FP8 row (D = 512: one wave)
+      const int64_t bs = a.out_bstride ? a.out_bstride : (int64_t)a.n_out * a.out_fp8_row;
+      store_kv_fp8_row((uint8_t*)a.out + (int64_t)b * bs + ent * a.out_fp8_row, lane, y, R);
+      return;
+    }
+  }
+  const int64_t bstride = a.out_bstride ? a.out_bstride : (int64_t)a.n_out * D;
   T* op = (T*)a.out + (int64_t)b * bstride + ent * D + c0;
   Elem<T>::template store<VEC>(op, y);
 }
@@ -232,10 +239,183 @@ __global__ __launch_bounds__(64) void compress_finish(CompressArgs a) {
       }
     }
   }
-  const int64_t bstride = a.out_bstride ? a.out_bstride : (int64_t)a.n_out * D;
   const int64_t ent = compress_out_row(a, b, i);
   if (ent < 0) return;
+  if constexpr (VEC == 8) {
+    if (a.out_fp8_row > 0) {  // packed mixed BF16 / FP8 row (D = 512)
+      const int64_t bs = a.out_bstride ? a.out_bstride : (int64_t)a.n_out * a.out_fp8_row;
+      store_kv_fp8_row((uint8_t*)a.out + (int64_t)b * bs + ent * a.out_fp8_row, lane, y, R);
+      return;
+    }
+  }
+  const int64_t bstride = a.out_bstride ? a.out_bstride : (int64_t)a.n_out * D;
   Elem<T>::template store<VEC>((T*)a.out + (int64_t)b * bstride + ent * D + c0, y);
+}
+
+// ------------------------------------------------------ short-block streaming
+// Many entries of short blocks (CSA m = 4 with its overlap, window rows
+// m = 1): a sub-group of L = D / VEC lanes owns one entry, lane l of it
+// channels VEC l .. VEC l + VEC - 1, and holds all of the entry's rows for
+// them, so the per-channel softmax, the weighted sum, the RMSNorm (a
+// sub-group sum), the gain and RoPE need no LDS merge and no barrier.  A
+// wave takes 64 / L entries at once and strides over the call's entries.
+// The block shape (M rows per stream, the overlap) is a template argument,
+// so every row address is a branch-free select and all 2M (or M) row loads
+// of an entry are issued back to back before any arithmetic (16 KiB in
+// flight per wave for a 512-channel CSA entry).  The biases sit in LDS in
+// base-2 logit units; the lane's gain and RoPE frequencies are loaded once.
+constexpr int kRowsMaxD = 512;   // widest row the kernel's bias table holds
+
+template <typename T, int VEC, int M, bool OVERLAP>
+__global__ __launch_bounds__(256) void compress_rows_kernel(CompressArgs a0, CompressArgs a1) {
+  constexpr int ROWS = M * (OVERLAP ? 2 : 1);
+  __shared__ __attribute__((aligned(16))) float s_bias[ROWS * kRowsMaxD];
+  const CompressArgs a = blockIdx.y ? a1 : a0;
+  const int D = a.D;
+  const int L = D / VEC;                // lanes per entry (a power of two <= 64)
+  const int lane = threadIdx.x & 63;
+  const int sub = lane / L, l = lane - sub * L;
+  const int per_wave = 64 / L;
+  const int c0 = l * VEC;
+  constexpr int NW = VEC * (int)sizeof(T) / 16;  // 16-byte words per lane per row
+  for (int x = threadIdx.x; x < ROWS * D; x += blockDim.x) {
+    const int r = x / D, c = x - r * D;
+    const bool in_a = r < M;
+    const float* bp = in_a ? a.bias_a : a.bias_b;
+    s_bias[x] = bp ? bp[(int64_t)(in_a ? r : r - M) * D + c] * kLog2e : 0.f;
+  }
+  __syncthreads();
+  float gv[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) gv[e] = a.gain ? a.gain[c0 + e] : 1.f;
+  const int R = a.rope_dims;
+  const bool rot = R > 0 && c0 + VEC > D - R;
+  double theta[VEC / 2];
+#pragma unroll
+  for (int k = 0; k < VEC / 2; ++k) {
+    const int c = c0 + 2 * k;
+    theta[k] = (rot && c >= D - R) ? rope_theta(a.rope_theta1, (c - (D - R)) >> 1) : 0.0;
+  }
+  const bool has_z = a.z_a != nullptr;
+  const T* za_base = has_z ? (const T*)a.z_a : (const T*)a.c_a;  // read and ignored without z
+
+  const int64_t entries = (int64_t)a.B * a.n_out;
+  const int64_t wave0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 64;
+  const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / 64;
+  for (int64_t e0 = wave0 * per_wave; e0 < entries; e0 += nwaves * per_wave) {
+    const int64_t ent = e0 + sub;
+    const bool live = ent < entries;
+    const int64_t ec = live ? ent : entries - 1;     // a dead lane reads a live entry's rows
+    const int b = (int)(ec / a.n_out);
+    const int i = (int)(ec - (int64_t)b * a.n_out);
+    const int64_t a_row0 = (int64_t)M * i;
+    const int na = (int)min((int64_t)M, (int64_t)a.T - a_row0);
+    // the sequence's first position, requested before the rows: waiting for
+    // it (the b-stream choice of entry 0) then leaves the rows in flight
+    const int64_t p0 = a.pos0 ? a.pos0[b] : 0;
+    // stream a: rows a_row0 + r, clamped into the block (a partial last block
+    // re-reads its last row; masked below)
+    const int64_t a_off = ((int64_t)b * a.T + a_row0) * D + c0;
+    u32x4_t cw[ROWS][NW], zw[ROWS][NW];
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
+      const int64_t ro = a_off + (int64_t)min(r, na - 1) * D;
+      Elem<T>::template load_raw<VEC>((const T*)a.c_a + ro, cw[r]);
+      Elem<T>::template load_raw<VEC>(za_base + ro, zw[r]);
+    }
+    int nb = 0;
+    if constexpr (OVERLAP) {
+      // stream b: block i - 1, or for entry 0 the block before the call
+      // (given, and not at the sequence start); otherwise no b rows
+      const bool use_prev = i == 0 && a.prev_c_b && (!a.pos0 || p0 >= M);
+      nb = (i >= 1 || use_prev) ? M : 0;
+      const T* cb = i >= 1 ? (const T*)a.c_b + ((int64_t)b * a.T + a_row0 - M) * D
+                           : (use_prev ? (const T*)a.prev_c_b + (int64_t)b * M * D
+                                       : (const T*)a.c_a + ((int64_t)b * a.T + a_row0) * D);
+      const T* zb = i >= 1 ? (const T*)a.z_b + ((int64_t)b * a.T + a_row0 - M) * D
+                           : (use_prev ? (const T*)a.prev_z_b + (int64_t)b * M * D
+                                       : za_base + ((int64_t)b * a.T + a_row0) * D);
+#pragma unroll
+      for (int r = 0; r < M; ++r) {
+        Elem<T>::template load_raw<VEC>(cb + (int64_t)r * D + c0, cw[M + r]);
+        Elem<T>::template load_raw<VEC>(zb + (int64_t)r * D + c0, zw[M + r]);
+      }
+    }
+    const int64_t pos = p0 + a_row0;
+    // base-2 logit of row slot r, channel e; -inf for a row the block lacks
+    auto logit = [&](int r, int e, const float* zv) {
+      const bool ok = r < M ? r < na : r - M < nb;
+      return ok ? (has_z ? zv[e] * kLog2e : 0.f) + s_bias[r * D + c0 + e] : -INFINITY;
+    };
+    // online softmax over the row slots in order (slot 0, the block's first
+    // row, always exists, so the running maximum starts finite); each row's
+    // raw words are converted only when its turn comes
+    float mx[VEC], den[VEC], acc[VEC];
+    {
+      float zv[VEC], cv[VEC];
+      Elem<T>::template from_raw<VEC>(zw[0], zv);
+      Elem<T>::template from_raw<VEC>(cw[0], cv);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        mx[e] = logit(0, e, zv);
+        den[e] = 1.f;
+        acc[e] = cv[e];
+      }
+    }
+#pragma unroll
+    for (int r = 1; r < ROWS; ++r) {
+      float zv[VEC], cv[VEC];
+      Elem<T>::template from_raw<VEC>(zw[r], zv);
+      Elem<T>::template from_raw<VEC>(cw[r], cv);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float lg = logit(r, e, zv);          // -inf for a missing row
+        const float mn = fmaxf(mx[e], lg);
+        const float sc = exp2f(mx[e] - mn);
+        const float p = exp2f(lg - mn);
+        den[e] = den[e] * sc + p;
+        acc[e] = acc[e] * sc + p * cv[e];
+        mx[e] = mn;
+      }
+    }
+    float y[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) y[e] = acc[e] / den[e];
+    if (a.gain) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) ss += y[e] * y[e];
+      for (int off = L >> 1; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+      const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) y[e] = y[e] * inv * gv[e];
+    }
+    if (rot) {
+#pragma unroll
+      for (int k = 0; k < VEC / 2; ++k) {
+        if (c0 + 2 * k < D - R) continue;
+        float cs, sn;
+        rope_cos_sin_theta(pos, theta[k], cs, sn);
+        const float x0 = y[2 * k], x1 = y[2 * k + 1];
+        y[2 * k] = x0 * cs - x1 * sn;
+        y[2 * k + 1] = x0 * sn + x1 * cs;
+      }
+    }
+    const int64_t row = live ? compress_out_row(a, b, i) : -1;
+    if constexpr (VEC == 8) {
+      if (a.out_fp8_row > 0) {  // packed mixed BF16 / FP8 row (D = 512: the whole wave)
+        if (row >= 0) {
+          const int64_t bs = a.out_bstride ? a.out_bstride : (int64_t)a.n_out * a.out_fp8_row;
+          store_kv_fp8_row((uint8_t*)a.out + (int64_t)b * bs + row * a.out_fp8_row, lane, y, R);
+        }
+        continue;
+      }
+    }
+    if (row >= 0) {
+      const int64_t bstride = a.out_bstride ? a.out_bstride : (int64_t)a.n_out * D;
+      Elem<T>::template store<VEC>((T*)a.out + (int64_t)b * bstride + row * D + c0, y);
+    }
+  }
 }
 
 // ------------------------------------------------------------ decode state
@@ -275,6 +455,9 @@ static int compress_vec(int dt, int D) {
 static int compress_slices(const CompressArgs& a) {
   const int64_t entries = (int64_t)a.B * a.n_out;
   if (entries >= kCompressSplitBelow || a.m * (a.overlap ? 2 : 1) < kCompressSplitRows) return 1;
+  // packed FP8 rows are stored by one wave holding the whole row: the
+  // slices' finisher (which needs the gain) or the single workgroup
+  if (a.out_fp8_row > 0 && !a.gain) return 1;
   if (a.gain && (a.D % 512 != 0 || !a.ws_y ||
                  a.ws_bytes < (size_t)entries * a.D * sizeof(float)))
     return 1;
@@ -307,8 +490,45 @@ static int compress_threads(const CompressArgs& a, int L) {
 
 // One launch for n (1 or 2) jobs of one VEC; the block is the largest any
 // job asks for, and each job spreads its rows over blockDim / L groups.
+// The short-block streaming kernel covers a call whose jobs pool at most
+// kRowsMax rows per entry, keep whole entries (no channel slices) and have
+// many entries: a short block's cost is its bytes, not the merge.
+constexpr int64_t kRowsKernelMinEntries = 256;
+
+// Block shapes the kernel is instantiated for: CSA (m = 4, overlap) and
+// window rows (m = 1).
+static bool rows_kernel_covers(const CompressArgs& a, int vec) {
+  const int L = a.D / vec;
+  const bool shape = (a.m == 4 && a.overlap) || (a.m == 1 && !a.overlap);
+  return shape && a.slices == 1 && L >= 1 && L <= 64 && vec <= 8 && a.D <= kRowsMaxD &&
+         (int64_t)a.B * a.n_out >= kRowsKernelMinEntries &&
+         (a.out_fp8_row == 0 || L == 64);
+}
+
 template <typename T, int VEC>
 static hipError_t launch_compress_t(const CompressArgs* jobs, int n, hipStream_t stream) {
+  bool rows_ok = true;
+  int64_t most = 0;
+  for (int k = 0; k < n; ++k) {
+    rows_ok = rows_ok && rows_kernel_covers(jobs[k], VEC);
+    const int64_t waves = ((int64_t)jobs[k].B * jobs[k].n_out + (64 / (jobs[k].D / VEC)) - 1) /
+                          (64 / (jobs[k].D / VEC));
+    most = max(most, waves);
+  }
+  if (rows_ok && (n == 1 || (jobs[1].m == jobs[0].m && jobs[1].overlap == jobs[0].overlap))) {
+    // about 12 waves per compute unit, each striding over its entries
+    const int64_t wgs = min((most + 3) / 4, (int64_t)256 * 3);
+    const dim3 grid((unsigned)wgs, n);
+    if constexpr (VEC <= 8) {
+      if (jobs[0].m == 4)
+        hipLaunchKernelGGL((compress_rows_kernel<T, VEC, 4, true>), grid, dim3(256), 0, stream,
+                           jobs[0], n > 1 ? jobs[1] : jobs[0]);
+      else
+        hipLaunchKernelGGL((compress_rows_kernel<T, VEC, 1, false>), grid, dim3(256), 0, stream,
+                           jobs[0], n > 1 ? jobs[1] : jobs[0]);
+      return hipGetLastError();
+    }
+  }
   int threads = 0;
   for (int k = 0; k < n; ++k)
     threads = max(threads, compress_threads(jobs[k], jobs[k].D / jobs[k].slices / VEC));

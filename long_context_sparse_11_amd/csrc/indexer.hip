@@ -63,15 +63,23 @@ __global__ __launch_bounds__(256) void index_generic(IndexArgs a) {
 }
 
 // --------------------------------------------------------------- MFMA common
-// Query operand: lane (g, j) holds heads j and 32+j, channels 64g + 8s .. +7.
+// Query operand: lane (g, j) holds heads j and 32+j, channels 64g + 8s .. +7;
+// head h's row starts at qp + h * pitch.
+template <int PITCH>
 __device__ __forceinline__ void load_query_operand(const bf16_t* qp, int lane, bf16x8_t (&qa)[2][8]) {
   const int j = lane & 31, g = lane >> 5;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      qa[mt][s] = *reinterpret_cast<const bf16x8_t*>(qp + (mt * 32 + j) * 128 + g * 64 + 8 * s);
+      qa[mt][s] = *reinterpret_cast<const bf16x8_t*>(qp + (mt * 32 + j) * PITCH + g * 64 + 8 * s);
 }
+
+// Row pitch (bf16) of the query heads staged in LDS by the decode kernel:
+// 272 bytes, so the 16-byte reads of consecutive heads (one per lane) spread
+// over the banks instead of all landing on one (a 256-byte pitch did: 5.2
+// conflict cycles per access measured).
+constexpr int kSqPitch = 136;
 
 // Head weights matching the accumulator rows held by this lane.
 __device__ __forceinline__ void load_head_weights(const float* wp, int lane, float (&wv)[2][16]) {
@@ -242,6 +250,29 @@ __device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressAr
   // the stored values, as the scorer sees them
   float v0, v1;
   const int64_t at = (int64_t)b * j.out_bstride + (int64_t)row * D;  // channel offset
+  if (j.out_fp8_row > 0) {
+    // packed mixed BF16 / FP8 row (the KV job, D = 512; never scored): the
+    // 16 threads of a 32-channel block share its scale
+    const int Dr = D - j.rope_dims;
+    const bool f8 = act && c0 < Dr;
+    float am = f8 ? fmaxf(fabsf(y0), fabsf(y1)) : 0.f;
+    am = fmaxf(am, __shfl_xor(am, 1));
+    am = fmaxf(am, __shfl_xor(am, 2));
+    am = fmaxf(am, __shfl_xor(am, 4));
+    am = fmaxf(am, __shfl_xor(am, 8));
+    const uint32_t sb = mx8_scale_byte(am);
+    uint8_t* rp = (uint8_t*)j.out + (int64_t)b * j.out_bstride + (int64_t)row * j.out_fp8_row;
+    if (f8) {
+      *reinterpret_cast<uint16_t*>(rp + c0) = (uint16_t)(e4m3_code(y0, sb) | (e4m3_code(y1, sb) << 8));
+      if ((tid & 15) == 0) rp[D + j.rope_dims + (c0 >> 5)] = (uint8_t)sb;
+    } else if (act) {
+      *reinterpret_cast<uint32_t*>(rp + Dr + 2 * (c0 - Dr)) = pack_bf16x2(y0, y1);
+    }
+    if (tid == 0) {
+      for (int p = D + j.rope_dims + Dr / 32; p < j.out_fp8_row; ++p) rp[p] = 0;
+    }
+    return;
+  }
   if (j.out_scales) {
     // MX FP4: the 16 lanes of a 32-channel block share its scale
     float am = act ? fmaxf(fabsf(y0), fabsf(y1)) : 0.f;
@@ -319,7 +350,7 @@ __device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressAr
 template <bool FRESH, bool ONE, bool FP4>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONE ? 3 : 1, 8)))
 void index_decode(IndexArgs a, int tiles_per_wave, int chunks, FreshJobs f) {
-  __shared__ __attribute__((aligned(16))) bf16_t sq[64 * 128];
+  __shared__ __attribute__((aligned(16))) bf16_t sq[64 * kSqPitch];
   // head weights: thread i stores a copy of weights 4(i%16) .. +3 in slot i
   // (a store in every thread: a branch around it would drag its load along)
   __shared__ __attribute__((aligned(16))) float sw[256 * 4];
@@ -381,7 +412,10 @@ void index_decode(IndexArgs a, int tiles_per_wave, int chunks, FreshJobs f) {
   int tile = tile0 + wave;
   load(tile, k0);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) reinterpret_cast<uint4*>(sq)[threadIdx.x + 256 * u] = v[u];
+  for (int u = 0; u < 4; ++u) {
+    const int c = threadIdx.x + 256 * u;  // 16-byte chunk c: head c / 16, channels 8 (c % 16)
+    *reinterpret_cast<uint4*>(sq + (c >> 4) * kSqPitch + 8 * (c & 15)) = v[u];
+  }
   reinterpret_cast<f32x4_t*>(sw)[threadIdx.x] = wq;
   // with fresh entries the last one is scored by its compressing workgroup
   // (a sequence whose step closes no block, negative block start, has none)
@@ -391,7 +425,7 @@ void index_decode(IndexArgs a, int tiles_per_wave, int chunks, FreshJobs f) {
                             : visible_entries(tpos, a.m, min(n_ent, a.N_cap));
   __syncthreads();
   bf16x8_t qa[2][8];
-  load_query_operand(sq, lane, qa);
+  load_query_operand<kSqPitch>(sq, lane, qa);
   float wv[2][16];
   load_head_weights(sw, lane, wv);
 
@@ -478,7 +512,7 @@ __global__ __launch_bounds__(512) void index_prefill(IndexArgs a) {
   const int64_t query = (int64_t)b * a.Tq + (live ? t : t_last);
 
   bf16x8_t qa[2][8];
-  load_query_operand((const bf16_t*)a.q + query * 64 * 128, lane, qa);
+  load_query_operand<128>((const bf16_t*)a.q + query * 64 * 128, lane, qa);
   float wv[2][16];
   load_head_weights(a.w + query * 64, lane, wv);
 
@@ -614,6 +648,7 @@ bool index_fresh_fused(const IndexArgs& a, const FreshJobs& f) {
   for (int k = 0; k < f.n_jobs; ++k) {
     const CompressArgs& j = f.job[k];
     if (k > 0 && j.out_scales) return false;
+    if (j.out_fp8_row > 0 && (k != 1 || j.D != 512)) return false;
     const int rows = j.m * ((j.overlap && j.prev_c_b) ? 2 : 1);
     if (j.dt != 1 || j.T != j.m || j.D > 512 || (j.D & 1) || rows > kFreshMaxRows) return false;
   }

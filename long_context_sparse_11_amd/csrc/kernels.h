@@ -35,6 +35,10 @@ struct CompressArgs {
   // when > 0: entry i of sequence b goes to row (pos0[b] / m + i) % ring_len
   // of out (a ring of window rows, m = 1)
   int ring_len;
+  // when > 0: entries are stored as packed mixed BF16 / FP8 rows of this
+  // many bytes (D = 512, rope_dims a multiple of 32); out_bstride then counts
+  // bytes
+  int out_fp8_row;
 };
 // Row of out that entry i of sequence b goes to, or -1 for none: with
 // rows_at, min(rows_at[b], rows_cap) - 1; a negative pos0[b] means no block
@@ -47,6 +51,44 @@ __device__ __forceinline__ int64_t compress_out_row(const CompressArgs& a, int b
     return p % a.ring_len;
   }
   return i;
+}
+// Stores one KV entry (D = 512) as a packed mixed BF16 / FP8 row from the 64
+// lanes of a wave, lane l holding channels 8l .. 8l+7: the lanes of the
+// D - R non-RoPE channels write 8 E4M3 codes each (the 4 lanes of a
+// 32-channel block meet by lane swaps for its scale, the first writes the
+// scale byte), the others their bf16 channels; lane 0 zeroes the padding.
+__device__ __forceinline__ void store_kv_fp8_row(uint8_t* row, int lane, const float (&y)[8],
+                                                 int R) {
+  constexpr int D = 512;
+  const int nc = (D - R) >> 3;
+  const bool fp8 = lane < nc;
+  float am = 0.f;
+  if (fp8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(y[e]));
+  }
+  am = fmaxf(am, __shfl_xor(am, 1));
+  am = fmaxf(am, __shfl_xor(am, 2));
+  const uint32_t s = mx8_scale_byte(am);
+  if (fp8) {
+    uint2 w;
+    w.x = e4m3_code(y[0], s) | (e4m3_code(y[1], s) << 8) | (e4m3_code(y[2], s) << 16) |
+          (e4m3_code(y[3], s) << 24);
+    w.y = e4m3_code(y[4], s) | (e4m3_code(y[5], s) << 8) | (e4m3_code(y[6], s) << 16) |
+          (e4m3_code(y[7], s) << 24);
+    *reinterpret_cast<uint2*>(row + 8 * lane) = w;
+    if ((lane & 3) == 0) row[D + R + (lane >> 2)] = (uint8_t)s;
+  } else {
+    uint4 pk;
+    pk.x = pack_bf16x2(y[0], y[1]);
+    pk.y = pack_bf16x2(y[2], y[3]);
+    pk.z = pack_bf16x2(y[4], y[5]);
+    pk.w = pack_bf16x2(y[6], y[7]);
+    *reinterpret_cast<uint4*>(row + (D - R) + 16 * (lane - nc)) = pk;
+  }
+  if (lane == 0) {
+    for (int p = D + R + (D - R) / 32; p < D + R + kv_fp8_scale_pad(D, R); ++p) row[p] = 0;
+  }
 }
 // Workspace the compressor uses for a call of this shape (0 = none); rows:
 // rows pooled per entry (m, or 2m with overlap).
@@ -99,6 +141,13 @@ hipError_t launch_decode_advance(int B, int m, int N_cap, int64_t* q_pos, int32_
 hipError_t launch_mxfp4_quantize(int dt, int64_t rows, int D, const void* x, uint8_t* codes,
                                  uint8_t* scales, hipStream_t stream);
 
+// ------------------------------------------------- mixed BF16 / FP8 KV rows
+int kv_fp8_row_bytes_host(int D, int R);
+hipError_t launch_kv_fp8_quantize(int dt, int64_t rows, int D, int R, const void* x, void* out,
+                                  hipStream_t stream);
+hipError_t launch_kv_fp8_dequantize(int64_t rows, int D, int R, const void* in, void* out,
+                                    hipStream_t stream);
+
 // --------------------------------------------------------------------- top-k
 // Largest score row that one workgroup selects from in LDS.
 constexpr int kTopkCap = 16384;
@@ -141,6 +190,9 @@ struct AttnArgs {
   const int64_t* q_pos0;
   void* out;            // [B, Tq, H, D]
   float* lse;           // [B, Tq, H] or null
+  // 0: pool rows are D elements of dt; > 0: packed mixed BF16 / FP8 rows of
+  // this many bytes (kv_fp8_row_bytes; bf16 MFMA shape only)
+  int pool_row_bytes;
   int splits;           // key-range splits per query (1 = no combine pass)
   float* part_o;        // [B*Tq, splits, H, D] when splits > 1
   float* part_ml;       // [B*Tq, splits, H, 2]

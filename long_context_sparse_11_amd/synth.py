@@ -21,6 +21,10 @@ shared K=V head, RoPE on the last 64 channels, indexer 64 heads x 128, top-k
   hca1m      bf16, HCA decode, batch 16 at position 1,048,575, 8,192 entries
   csa1m      bf16, CSA decode, batch 8 at position 1,048,575, 262,144 entries,
              indexer keys with 10% of rows scaled by 4 (heavy-tailed mixture)
+  compress_stream
+             bf16, the compressors alone over one 1,048,576-token sequence
+             (KV entries 512 wide with RMSNorm + RoPE, indexer keys 128
+             wide): 5.4 GiB of token streams, drawn on the device
   csa64k_fp4, csa1m_fp4
              as csa64k / csa1m with the indexer keys stored in MX FP4: code
              bytes drawn uniformly (every E2M1 code equally likely) and scale
@@ -312,4 +316,36 @@ def prefill(seed: int = 0, Tq: int = 4096, prefix: int = 15360, skip=()):
     bf("q_idx", (1, Tq, Hi, Di))
     d["w_idx"] = dr("w_idx", (1, Tq, Hi), 0.02)
     d["sink"] = dr("sink", (H,), 0.02)
+    return d
+
+
+def compress_stream(seed: int = 0, T: int = 1 << 20, device: str = "cuda"):
+    """The compressors alone over one long sequence (a prefill's compressor
+    pass, or the standalone streaming measurement): T tokens from position 0,
+    the KV compressor (D = 512, overlap, RMSNorm gain, RoPE 64) and the
+    indexer-key compressor (Di = 128, overlap) over the same blocks.  The
+    eight token streams [1, T, D] / [1, T, Di] (5.4 GiB at T = 2^20) are drawn
+    on the device, N(0, 1) in bfloat16 from torch's generator seeded with
+    (seed, crc32 of the stream name): a host draw of that size would take
+    minutes.  Biases and gain follow the host recipe (N(0, 0.02), 1 +
+    N(0, 0.02)).  ``device=None`` skips the streams (their parameters only)."""
+    dr = _Draw(seed, "compress_stream")
+    F = FLASH
+    D, R, Di, m = F["D"], F["R"], F["Di"], 4
+    d = dict(name="compress_stream", dt="bf16", B=1, Tq=T, T=T, H=F["H"], D=D, R=R, Hi=F["Hi"],
+             Di=Di, m=m, K=F["K"], W=F["W"], N=T // m, base=10000.0, eps=1e-6,
+             pos0=np.array([0], np.int64))
+    d["bias_a"] = dr("bias_a", (m, D), 0.02)
+    d["bias_b"] = dr("bias_b", (m, D), 0.02)
+    d["gain"] = dr("gain", (D,), 0.02, 1.0)
+    d["ibias_a"] = dr("ibias_a", (m, Di), 0.02)
+    d["ibias_b"] = dr("ibias_b", (m, Di), 0.02)
+    if device is None:
+        return d
+    import torch
+    for name, width in (("c_a", D), ("z_a", D), ("c_b", D), ("z_b", D),
+                        ("ic_a", Di), ("iz_a", Di), ("ic_b", Di), ("iz_b", Di)):
+        g = torch.Generator(device=device)
+        g.manual_seed(int(seed) * 1000003 + zlib.crc32(name.encode()))
+        d[name] = torch.randn((1, T, width), generator=g, device=device, dtype=torch.bfloat16)
     return d

@@ -100,6 +100,47 @@ def test_compress_bf16(D, m, T, overlap, prev, normrope, pos):
     assert rowwise_rel_err(host(out), ref) <= TOL_BF16
 
 
+# calls with many entries of short blocks (at most 8 pooled rows) take the
+# streaming kernel (one sub-group of lanes per entry)
+MANY = [  # dt, D, m, T, overlap, prev, norm+rope, pos0
+    ("bf16", 512, 4, 4099, True, True, True, [61440, 8]),     # CSA KV chunk, ragged tail
+    ("bf16", 128, 4, 2050, True, False, False, [0, 400]),     # indexer keys, sequence start
+    ("bf16", 512, 1, 600, False, False, True, [77, 1000]),    # window rows
+    ("bf16", 64, 8, 2400, False, False, True, [16, 0]),       # 8 lanes per entry
+    ("f32", 256, 4, 1030, True, True, True, [4, 4096]),
+]
+
+
+@pytest.mark.parametrize("dt,D,m,T,overlap,prev,normrope,pos", MANY)
+def test_compress_many_entries(dt, D, m, T, overlap, prev, normrope, pos):
+    rng = np.random.default_rng(D * 5 + m * 11 + T)
+    B = 2
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)
+    Tn = lambda x: synth.Tensor(x, dt)
+    c_a, z_a = Tn(f(B, T, D)), Tn(f(B, T, D))
+    bias_a = 0.02 * f(m, D)
+    kw, okw = {}, {}
+    if overlap:
+        c_b, z_b = Tn(f(B, T, D)), Tn(f(B, T, D))
+        bias_b = 0.02 * f(m, D)
+        kw.update(c_b=dev(c_b), z_b=dev(z_b), bias_b=dev(bias_b))
+        okw.update(c_b=c_b.f32, z_b=z_b.f32, bias_b=bias_b)
+        if prev:
+            pc, pz = Tn(f(B, m, D)), Tn(f(B, m, D))
+            kw.update(prev_c_b=dev(pc), prev_z_b=dev(pz))
+            okw.update(prev_c_b=pc.f32, prev_z_b=pz.f32)
+    if normrope:
+        gain = (1 + 0.02 * f(D)).astype(np.float32)
+        R = min(64, D // 4)
+        kw.update(gain=dev(gain), rope_dims=R)
+        okw.update(gain=gain, rope_dims=R)
+    got = L.csa_compress(dev(c_a), m, z_a=dev(z_a), bias_a=dev(bias_a), pos0=i64(pos), **kw)
+    ref = O.csa_compress(c_a.f32, z_a.f32, bias_a, m, pos0=pos, **okw)
+    assert got.shape == ref.shape
+    tol = TOL_BF16 if dt == "bf16" else TOL_F32
+    assert rowwise_rel_err(host(got), ref) <= tol
+
+
 @pytest.mark.parametrize("D,m,T,overlap", [(512, 128, 256, False), (512, 16, 32, True)])
 def test_compress_without_workspace(D, m, T, overlap):
     """A call with few entries and a gain splits each entry over several
@@ -301,6 +342,29 @@ def test_index_nothing_visible():
     assert np.all(gidx == -1) and np.all(np.isneginf(gsc))
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_index_empty_pool(dt):
+    """A pool with no entry yet (N_cap = 0: fewer than m tokens so far): the
+    call needs no workspace, reads no score and fills every slot with -1
+    (score -inf), for the bf16 and the MX FP4 keys alike."""
+    rng = np.random.default_rng(6)
+    Hi, Di = (64, 128) if dt == "bf16" else (4, 32)
+    q = synth.Tensor(rng.standard_normal((2, 3, Hi, Di)).astype(np.float32), dt)
+    w = rng.standard_normal((2, 3, Hi)).astype(np.float32)
+    k = torch.empty((2, 0, Di), dtype=torch.bfloat16 if dt == "bf16" else torch.float32,
+                    device="cuda")
+    assert L.csa_index_topk_ws_bytes(2, 3, Hi, 0, 16) == 0
+    gidx, gsc, _ = L.csa_index_topk(dev(q), dev(w), k, i32([0, 0]), i64([2, 0]), 16, 4,
+                                    want_scores=True)
+    assert np.all(host(gidx) == -1) and np.all(np.isneginf(host(gsc)))
+    if dt == "bf16":
+        kc = torch.empty((2, 0, Di // 2), dtype=torch.uint8, device="cuda")
+        ks = torch.empty((2, 0, Di // 32), dtype=torch.uint8, device="cuda")
+        fidx, fsc, _ = L.csa_index_topk_mxfp4(dev(q), dev(w), kc, ks, i32([0, 0]), i64([2, 0]),
+                                              16, 4, want_scores=True)
+        assert np.all(host(fidx) == -1) and np.all(np.isneginf(host(fsc)))
+
+
 def _fresh_case(dt, N, Tq, n_ent, key_norm_rope, seed):
     """Inputs of a decode step whose last query closes a block: the closing
     block's streams for the indexer-key and KV compressors, pools holding the
@@ -420,8 +484,44 @@ def test_decode_index_topk_matches_separate_calls():
     # may differ by a bf16 rounding step, and it is scored on another path
     assert np.array_equal(host(gall)[:, :, : N - 1], host(all2)[:, :, : N - 1])
     assert np.abs(host(gall)[:, :, N - 1] - host(all2)[:, :, N - 1]).max() <= 1e-2
+    # each path's selection is exactly the oracle's select on its own scores
     for b in range(2):
-        check_band(host(gidx)[b, 0], host(idx2)[b, 0], host(all2)[b, 0], N, K, band=2e-3)
+        assert np.array_equal(host(gidx)[b, 0], O.select_topk(host(gall)[b, 0, :N], N, K))
+        assert np.array_equal(host(idx2)[b, 0], O.select_topk(host(all2)[b, 0, :N], N, K))
+
+
+@pytest.mark.parametrize("n_jobs", [2, 3])
+def test_decode_index_scores_is_the_scoring_half(n_jobs):
+    """csa_decode_index_scores writes the same fresh entries (and window row)
+    and the same scores, bitwise, as csa_decode_index_topk: it is the same
+    launch without the selection."""
+    d = _fresh_case("bf16", 3000, 1, [3000, 2001], False, seed=31)
+    m, K, D, R = d["m"], 512, d["D"], d["R"]
+    rng = np.random.default_rng(32)
+    kv = dev(synth.Tensor(rng.standard_normal((2, 1, D)).astype(np.float32), "bf16"))
+    wgain = dev((1 + 0.02 * rng.standard_normal(D)).astype(np.float32))
+    res = []
+    for scores_only in (False, True):
+        kidx, pool = dev(d["k_idx"]), dev(d["pool"])
+        ring = torch.zeros((2, 128, D), dtype=torch.bfloat16, device="cuda")
+        jobs, _ = _fresh_jobs_and_refs(d, kidx, pool)
+        if n_jobs == 3:
+            jobs.append(dict(c_a=kv, gain=wgain, rope_dims=R, out=ring))
+        if scores_only:
+            alls = L.csa_decode_index_scores(dev(d["q"]), dev(d["w"]), i32(d["n_ent"]),
+                                             i64(d["q_pos0"]), m, jobs,
+                                             block_pos0=i64(d["block_pos0"]))
+        else:
+            _, _, alls = L.csa_decode_index_topk(dev(d["q"]), dev(d["w"]), i32(d["n_ent"]),
+                                                 i64(d["q_pos0"]), K, m, jobs,
+                                                 block_pos0=i64(d["block_pos0"]),
+                                                 want_all_scores=True)
+        res.append((alls, kidx, pool, ring))
+    for k in (1, 2, 3):
+        assert torch.equal(res[0][k], res[1][k]), k
+    for b in range(2):
+        nv = O.visible_count(int(d["q_pos0"][b]), m, int(d["n_ent"][b]))
+        assert torch.equal(res[0][0][b, :, :nv], res[1][0][b, :, :nv]), b
 
 
 def test_index_p4_sentinel_example():

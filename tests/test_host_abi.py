@@ -312,3 +312,54 @@ def test_attn_validation(lib):
     assert _attn(lib, "hca_attn", m=0) == CSA_ERR_ARG
     assert _attn(lib, "hca_attn", n_ent=N) == CSA_ERR_ARG
     assert _attn(lib, "hca_attn", wsb=1) == CSA_ERR_WORKSPACE
+
+
+def test_kv_fp8_validation(lib):
+    assert lib.csa_kv_fp8_row_bytes(512, 64) == 592
+    assert lib.csa_kv_fp8_row_bytes(512, 0) == 528 and lib.csa_kv_fp8_row_bytes(512, 512) == 1024
+    assert lib.csa_kv_fp8_row_bytes(256, 64) == 0 and lib.csa_kv_fp8_row_bytes(512, 48) == 0
+    assert lib.csa_quantize_kv_fp8(3, 4, 512, 64, P, P, N) == CSA_ERR_ARG
+    assert lib.csa_quantize_kv_fp8(1, 4, 256, 64, P, P, N) == CSA_ERR_UNSUPPORTED
+    assert lib.csa_quantize_kv_fp8(1, 4, 512, 64, N, P, N) == CSA_ERR_ARG
+    assert lib.csa_quantize_kv_fp8(1, 0, 512, 64, N, N, N) == CSA_OK
+    assert lib.csa_dequantize_kv_fp8(-1, 512, 64, P, P, N) == CSA_ERR_ARG
+    assert lib.csa_dequantize_kv_fp8(4, 512, 40, P, P, N) == CSA_ERR_UNSUPPORTED
+    # the attention over packed rows: the bf16 MFMA shape only
+    args = (4, 1, 64, 256, 64, 10000.0, 0.04, P, P, 100, P, 16, P, 128, P, 128, P, P, P, N, N, 0,
+            N)
+    assert lib.csa_sparse_attn_kvfp8(*args) == CSA_ERR_UNSUPPORTED
+    assert lib.hca_attn_kvfp8(4, 1, 64, 512, 48, 10000.0, 0.04, P, P, 100, P, 4, P, 128, P, 128,
+                              P, P, P, N, N, 0, N) == CSA_ERR_UNSUPPORTED
+    assert lib.hca_attn_kvfp8(4, 1, 64, 512, 64, 10000.0, 0.04, P, P, 100, N, 4, P, 128, P, 128,
+                              P, P, P, N, N, 0, N) == CSA_ERR_ARG
+    # the compressor writing packed rows: D = 512, R a multiple of 32
+    kw = dict(D=256, rope=64, base=10000.0, pos0=P)
+    a = dict(dt=1, B=2, T=8, m=4, overlap=1, c_a=P, z_a=P, c_b=P, z_b=P, prev_c_b=N, prev_z_b=N,
+             bias_a=N, bias_b=N, gain=N, eps=1e-6, out=P, ostride=0, ws=N, wsb=0)
+    a.update(kw)
+    st = lib.csa_compress_kvfp8(a["dt"], a["B"], a["T"], a["D"], a["m"], a["overlap"], a["c_a"],
+                                a["z_a"], a["c_b"], a["z_b"], a["prev_c_b"], a["prev_z_b"],
+                                a["bias_a"], a["bias_b"], a["gain"], a["eps"], a["rope"],
+                                a["base"], a["pos0"], a["out"], a["ostride"], a["ws"], a["wsb"], N)
+    assert st == CSA_ERR_UNSUPPORTED
+
+
+def test_decode_index_scores_validation(lib):
+    from long_context_sparse_11_amd.binding import CompressJob
+    key = CompressJob(128, P, P, P, P, N, N, N, N, N, 1e-6, 0, 10000.0, P, 0, 0)
+    kv = CompressJob(512, P, P, P, P, N, N, N, N, P, 1e-6, 64, 10000.0, P, 0, 0)
+    arr = (CompressJob * 2)(key, kv)
+
+    def call(n=2, N_cap=64, Di=128, scores=P, m=4, B=2):
+        return lib.csa_decode_index_scores(1, B, 1, 64, Di, N_cap, m, 1, P,
+                                           ctypes.cast(arr, ctypes.c_void_p), n, P, P, P, P,
+                                           scores, N)
+    assert call(n=0) == CSA_ERR_ARG
+    assert call(N_cap=0) == CSA_ERR_ARG          # no row for the fresh entry
+    assert call(Di=64) == CSA_ERR_ARG            # jobs[0].D != Di
+    assert call(scores=N) == CSA_ERR_ARG
+    assert call(m=0) == CSA_ERR_ARG
+    assert call(B=0) == CSA_OK
+    # the key job cannot store packed FP8 rows
+    arr[0].out_kv_fp8 = 1
+    assert call() == CSA_ERR_ARG
