@@ -26,7 +26,9 @@
  *     the buffers described by the arguments; data that violates a stated
  *     precondition gives unspecified values, never an out-of-bounds access.
  *   - The library is stateless and re-entrant; results are deterministic
- *     (same inputs, same bits).
+ *     (same inputs, same bits).  The one exception is
+ *     csa_decode_index_topk_noalloc, which works in a scratch array the
+ *     library holds on each device.
  */
 #ifndef CSA_H
 #define CSA_H
@@ -43,7 +45,8 @@ typedef enum {
   CSA_ERR_ARG = -1,         /* null pointer, negative size, inconsistent sizes */
   CSA_ERR_UNSUPPORTED = -2, /* shape outside what the kernels implement      */
   CSA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required     */
-  CSA_ERR_HIP = -4          /* a kernel launch failed                          */
+  CSA_ERR_HIP = -4,         /* a kernel launch failed                          */
+  CSA_ERR_SCRATCH = -5      /* the call needs more than the library's scratch  */
 } csa_status;
 
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
@@ -349,6 +352,28 @@ int csa_decode_index_topk_mxfp4(int B, int Tq, int Hi, int Di, int N_cap, int K,
                                 const int32_t* n_entries, const int64_t* q_pos0,
                                 int32_t* idx_out, float* score_out, float* all_scores,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/* csa_decode_index_topk_noalloc - csa_decode_index_topk for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  The workspace is not an
+ * argument: the call works in a scratch array of CSA_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each device (a static device array, present
+ * while the library is loaded; its address is looked up once per device,
+ * on the first call there, with that device current).  The call allocates
+ * and frees nothing.  Calls that overlap in time on one device share that
+ * device's array and race: order them on one stream.  The array keeps the
+ * last call's contents; nothing in it needs to start at zero (the scores
+ * the selection reads are written by the same call).  Arguments, results
+ * and errors as csa_decode_index_topk without ws / ws_bytes; CSA_ERR_SCRATCH
+ * when csa_index_topk_ws_bytes(B, Tq, Hi, N_cap, K) exceeds the scratch
+ * (decode of 8 sequences at 1,048,576 tokens needs 8.9 MB). */
+#define CSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int csa_decode_index_topk_noalloc(int dt, int B, int Tq, int Hi, int Di, int N_cap, int K, int m,
+                                  int overlap, const int64_t* block_pos0,
+                                  const csa_compress_job* jobs, int n_jobs, const void* q_idx,
+                                  const float* w_idx, const int32_t* n_entries,
+                                  const int64_t* q_pos0, int32_t* idx_out, float* score_out,
+                                  float* all_scores, void* stream);
 
 /* csa_decode_index_scores(_mxfp4) - the scoring half of
  * csa_decode_index_topk(_mxfp4): the closing block's fresh entries are

@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     csa_decode_index_scores,
     csa_decode_index_scores_mxfp4,
     csa_decode_index_topk,
+    csa_decode_index_topk_noalloc,
     csa_window_row,
     csa_decode_index_topk_mxfp4,
     csa_index_scores_mxfp4,

@@ -50,6 +50,9 @@ _SIGS = {
     "csa_index_scores_mxfp4": (_c.c_int, [_c.c_int] * 6 + [_c.c_void_p] * 8),
     "csa_decode_index_topk_mxfp4": (_c.c_int, [_c.c_int] * 8 + [_c.c_void_p, _c.c_void_p, _c.c_int]
                                     + [_c.c_void_p] * 10 + [_c.c_size_t, _c.c_void_p]),
+    "csa_decode_index_topk_noalloc": (_c.c_int, [_c.c_int] * 9 + [_c.c_void_p, _c.c_void_p,
+                                                                    _c.c_int]
+                                      + [_c.c_void_p] * 8),
     "csa_decode_index_scores": (_c.c_int, [_c.c_int] * 8 + [_c.c_void_p, _c.c_void_p, _c.c_int]
                                 + [_c.c_void_p] * 6),
     "csa_decode_index_scores_mxfp4": (_c.c_int, [_c.c_int] * 7
@@ -358,6 +361,38 @@ def csa_decode_index_topk(q_idx, w_idx, n_entries, q_pos0, K, m, jobs, *, block_
                                      _p(score_out), _p(all_scores), _p(ws),
                                      0 if ws is None else ws.numel(), _stream(stream))
     _check(st, "csa_decode_index_topk")
+    return idx_out, score_out, all_scores
+
+
+def csa_decode_index_topk_noalloc(q_idx, w_idx, n_entries, q_pos0, K, m, jobs, *,
+                                  block_pos0=None, want_scores=False, want_all_scores=False,
+                                  idx_out=None, stream=None):
+    """csa_decode_index_topk working in the library's own device scratch
+    (no workspace argument; see include/csa.h).  The outputs are allocated
+    here unless given: pass idx_out (and nothing else to allocate) where the
+    caller must not allocate."""
+    B, Tq, Hi, Di = q_idx.shape
+    k_idx = jobs[0]["out"]
+    N_cap = k_idx.shape[1]
+    overlap = jobs[0].get("c_b") is not None
+    _dev(q_idx, w_idx, n_entries, q_pos0, block_pos0)
+    _f32(w_idx), _i64(q_pos0), _i64(block_pos0)
+    if n_entries.dtype != torch.int32:
+        raise TypeError("n_entries is int32")
+    if jobs[0]["c_a"].shape[1] != m:
+        raise ValueError("the jobs' streams hold one block of m tokens")
+    arr = _job_array(jobs, B, m, overlap, lambda D: (B, N_cap, D))
+    dev = q_idx.device
+    if idx_out is None:
+        idx_out = torch.empty((B, Tq, K), dtype=torch.int32, device=dev)
+    score_out = torch.empty((B, Tq, K), dtype=torch.float32, device=dev) if want_scores else None
+    all_scores = (torch.empty((B, Tq, N_cap), dtype=torch.float32, device=dev)
+                  if want_all_scores else None)
+    st = lib().csa_decode_index_topk_noalloc(
+        _dt(q_idx), B, Tq, Hi, Di, N_cap, K, m, int(overlap), _p(block_pos0),
+        ctypes.cast(arr, ctypes.c_void_p), len(jobs), _p(q_idx), _p(w_idx), _p(n_entries),
+        _p(q_pos0), _p(idx_out), _p(score_out), _p(all_scores), _stream(stream))
+    _check(st, "csa_decode_index_topk_noalloc")
     return idx_out, score_out, all_scores
 
 

@@ -7,6 +7,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #define CSA_EXPORT extern "C" __attribute__((visibility("default")))
 
 using namespace csa;
@@ -29,6 +31,9 @@ CSA_EXPORT const char* csa_status_string(int status) {
     case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED: shape not implemented";
     case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE: workspace missing or too small";
     case CSA_ERR_HIP: return "CSA_ERR_HIP: kernel launch failed";
+    case CSA_ERR_SCRATCH:
+      return "CSA_ERR_SCRATCH: the call needs more than the library's scratch "
+             "(CSA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown csa_status";
   }
 }
@@ -345,6 +350,57 @@ CSA_EXPORT int csa_decode_index_topk_mxfp4(int B, int Tq, int Hi, int Di, int N_
   return index_topk_run(CSA_BF16, B, Tq, Hi, Di, N_cap, K, m, q_idx, w_idx, k_codes, k_scales,
                         n_entries, q_pos0, idx_out, score_out, all_scores, ws, ws_bytes, &f,
                         (hipStream_t)stream);
+}
+
+// ------------------------------------------------- no-allocation decode call
+// The scratch of csa_decode_index_topk_noalloc: a file-scope device array
+// (one copy on every device the library runs on, allocated with the code
+// object).  In host code `scratch` is a host-side stand-in, not a device
+// address; the device address comes from hipGetSymbolAddress, once per
+// device, and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[CSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on its first use), or
+// nullptr if the lookup fails.
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+CSA_EXPORT int csa_decode_index_topk_noalloc(int dt, int B, int Tq, int Hi, int Di, int N_cap,
+                                             int K, int m, int overlap,
+                                             const int64_t* block_pos0,
+                                             const csa_compress_job* jobs, int n_jobs,
+                                             const void* q_idx, const float* w_idx,
+                                             const int32_t* n_entries, const int64_t* q_pos0,
+                                             int32_t* idx_out, float* score_out,
+                                             float* all_scores, void* stream) {
+  if (B < 0 || Tq < 0 || Hi <= 0 || N_cap < 0 || K <= 0) return CSA_ERR_ARG;
+  const size_t need = csa_index_topk_ws_bytes(B, Tq, Hi, N_cap, K);
+  if (need > (size_t)CSA_NOALLOC_SCRATCH_BYTES) return CSA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = device_scratch();
+    if (!ws) return CSA_ERR_HIP;
+  }
+  return csa_decode_index_topk(dt, B, Tq, Hi, Di, N_cap, K, m, overlap, block_pos0, jobs, n_jobs,
+                               q_idx, w_idx, n_entries, q_pos0, idx_out, score_out, all_scores,
+                               ws, need > 0 ? (size_t)CSA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 namespace {
