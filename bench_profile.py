@@ -62,9 +62,10 @@ UNIT_KERNELS = {
     "hca_attn": ["attn_hs<false,", "attn_combine"],
     "sparse_attn": ["attn_hs<true,", "attn_combine"],
     "output_proj": ["proj_rows<", "proj_gemm<"],
+    "compress": ["compress_rows_kernel<"],
 }
-DOMINANT = {"hca1m": "hca_attn", "swa": "sparse_attn", "oproj": "output_proj",
-            "oproj_prefill": "output_proj", "prefill": "index_scores"}
+DOMINANT = {"hca1m": "hca_attn", "hca1m_fp8": "hca_attn", "swa": "sparse_attn",
+            "oproj": "output_proj", "oproj_prefill": "output_proj", "prefill": "index_scores"}
 WORKLOAD_NAME = {"csa64k": "csa_decode_64k", "csa1m": "csa_decode_1m",
                  "hca1m": "hca_decode_1m", "prefill": "csa_prefill_4k_on_60k",
                  "csa64k_pro": "csa_decode_64k_v4pro",
@@ -73,7 +74,9 @@ WORKLOAD_NAME = {"csa64k": "csa_decode_64k", "csa1m": "csa_decode_1m",
                  "swa": "swa_decode_1m", "oproj": "output_proj_decode",
                  "oproj_prefill": "output_proj_prefill_4k",
                  "csa64k_stream": "csa_decode_64k_streaming",
-                 "compress_stream": "compress_stream_1m"}
+                 "compress_stream": "compress_stream_1m",
+                 "csa64k_fp8": "csa_decode_64k_fp8_kv", "csa1m_fp8": "csa_decode_1m_fp8_kv",
+                 "hca1m_fp8": "hca_decode_1m_fp8_kv"}
 
 
 def dominant(workload):

@@ -356,45 +356,25 @@ void attn_hs(AttnArgs a) {
   // 8l .. 8l+7 (8 code bytes, the scale of their 32-channel block); the
   // other lanes one 16-byte chunk of the bf16 RoPE channels.  Each lane
   // writes its 16-byte chunk l of the row at the tile's swizzled position.
-  // The reads of a batch of rows are all issued before the first conversion
-  // (the LDS latency is paid once per batch, not once per row); every lane
-  // reads 16 bytes of its row (codes in the low half), its scale byte, and
-  // rows that are not staged are read and dropped.
   const int nc = (kAtD - R) >> 3;
-  const int src_off = lane < nc ? 8 * lane : (kAtD - R) + 16 * (lane - nc);
-  const int scl_off = kAtD + R + (lane < nc ? lane >> 2 : 0);
   auto convert_rows = [&](uint32_t fp8_rows, bf16_t* dst) {
-    constexpr int BATCH = RPW < 4 ? RPW : 4;
 #pragma unroll
-    for (int u0 = 0; u0 < RPW; u0 += BATCH) {
-      u32x4_t raw[BATCH];
-      uint32_t sb[BATCH];
-#pragma unroll
-      for (int k = 0; k < BATCH; ++k) {
-        const uint8_t* st = s_stage + (RPW * wv + u0 + k) * 1024;
-        if (lane < nc) {
-          const uint2 c8 = *reinterpret_cast<const uint2*>(st + src_off);
-          raw[k] = u32x4_t{c8.x, c8.y, 0u, 0u};
-        } else {
-          raw[k] = *reinterpret_cast<const u32x4_t*>(st + src_off);
-        }
-        sb[k] = st[scl_off];
+    for (int u = 0; u < RPW; ++u) {
+      const int r = RPW * wv + u;
+      if (!((fp8_rows >> r) & 1u)) continue;
+      const uint8_t* st = s_stage + r * 1024;
+      u32x4_t w;
+      if (lane < nc) {
+        const uint2 c8 = *reinterpret_cast<const uint2*>(st + 8 * lane);
+        const float sc = mx_scale_value(st[kAtD + R + (lane >> 2)]);
+        w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.x, sc, false));
+        w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.x, sc, true));
+        w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.y, sc, false));
+        w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.y, sc, true));
+      } else {
+        w = *reinterpret_cast<const u32x4_t*>(st + (kAtD - R) + 16 * (lane - nc));
       }
-#pragma unroll
-      for (int k = 0; k < BATCH; ++k) {
-        const int r = RPW * wv + u0 + k;
-        if (!((fp8_rows >> r) & 1u)) continue;
-        u32x4_t w = raw[k];
-        if (lane < nc) {
-          const float sc = mx_scale_value(sb[k]);
-          const uint32_t lo = raw[k][0], hi = raw[k][1];
-          w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, false));
-          w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, true));
-          w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, false));
-          w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, true));
-        }
-        *reinterpret_cast<u32x4_t*>(dst + r * kAtD + 8 * (lane ^ hs_swz(r))) = w;
-      }
+      *reinterpret_cast<u32x4_t*>(dst + r * kAtD + 8 * (lane ^ hs_swz(r))) = w;
     }
   };
 
