@@ -266,7 +266,10 @@ def summarize_dirs(workload, out, logs, steps):
                "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1,024 SIMDs), "
                "the fraction of the MFMA peak at the clock the kernel ran at (GRBM_GUI_ACTIVE "
                "reads the sum over the 8 XCDs; the clock column is that sum / 8 over the traced "
-               "duration); bf16 MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, their rate over "
+               "duration; a value above the 2.4 GHz peak clock means the counter window ran longer "
+               "than the kernel, which happens for kernels of tens of microseconds, and their "
+               "busy % is then a lower bound); bf16 MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x "
+               "512, their rate over "
                "the kernel's traced average duration, against the published 2.5 PFLOP/s; LDS bank "
                "conflicts per access = SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - "
                "SQ_LDS_BANK_CONFLICT).", "",
