@@ -422,100 +422,90 @@ void attn_hs(AttnArgs a) {
   for (int cb = 0; cb < 32; ++cb) oacc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.scale * kLog2e;
 
-  // One tile: logits, softmax, PV from `rows`; in multi-tile splits the
-  // next tile's rows are first requested into `next` (the other buffer).
-  auto tile_step = [&](int j0, const bf16_t* rows, bf16_t* next) {
-    // multi-tile splits request the next tile while this one is used; past
-    // the split's end every row is invalid and the copy reads the harmless
-    // row into the idle buffer, so the request is unconditional
-    TileSrc nt{0, 0, 0u, 0u};
-    if constexpr (MULTI) {
-      const int jn = j0 + kHsRows;
-      int sidx_l = 0;
-      // row jn + l's selected index; entries past the selected part (or the
-      // split) are never used, the clamp only keeps the read inside s_idx
-      if constexpr (CSA) sidx_l = s_idx[min(jn - start + (lane & 31), kHsMaxSplitRows - 1)];
-      nt = resolve_tile(jn, sidx_l);
-    }
-
-    // logits S^T[key][head] over all 512 channels for two 16-key blocks (two
-    // independent accumulator chains, interleaved).  The order is pinned:
-    // with one wave per SIMD nothing else hides the LDS latency, so the 32
-    // operand reads run 8 ahead of their MFMAs, and the next tile's 8 row
-    // copies are spread between them instead of stalling issue up front.
-    f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    {
-      const bf16_t* rpk[2] = {rows + c16 * kAtD, rows + (16 + c16) * kAtD};
-      const int swk[2] = {hs_swz(c16), hs_swz(16 + c16)};
-      // step f reads block f % 2, channel slice f / 2
-      auto qk_read = [&](int f) {
-        const int kb = f & 1, ks = f >> 1;
-        return *reinterpret_cast<const bf16x8_t*>(rpk[kb] + 128 * (ks >> 2) +
-                                                  8 * ((4 * (ks & 3) + G) ^ swk[kb]));
-      };
-      bf16x8_t av[8];
+  // Logits S^T[key][head] of one tile over all 512 channels for two 16-key
+  // blocks (two independent accumulator chains, interleaved).  The order is
+  // pinned: with one wave per SIMD nothing else hides the LDS latency, so the
+  // 32 operand reads run 8 ahead of their MFMAs.  hook(f) runs after MFMA
+  // step f: in multi-tile splits it issues the next tile's copies, spread
+  // between the reads instead of stalling issue up front.
+  auto qk = [&](const bf16_t* rows, f32x4_t (&acc)[2], auto&& hook) {
+    acc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    acc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const bf16_t* rpk[2] = {rows + c16 * kAtD, rows + (16 + c16) * kAtD};
+    const int swk[2] = {hs_swz(c16), hs_swz(16 + c16)};
+    // step f reads block f % 2, channel slice f / 2
+    auto qk_read = [&](int f) {
+      const int kb = f & 1, ks = f >> 1;
+      return *reinterpret_cast<const bf16x8_t*>(rpk[kb] + 128 * (ks >> 2) +
+                                                8 * ((4 * (ks & 3) + G) ^ swk[kb]));
+    };
+    bf16x8_t av[8];
 #pragma unroll
-      for (int f = 0; f < 8; ++f) av[f] = qk_read(f);
+    for (int f = 0; f < 8; ++f) av[f] = qk_read(f);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < 32; ++f) {
+      acc[f & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[f & 7], qb[f >> 1], acc[f & 1], 0, 0, 0);
+      if (f + 8 < 32) av[f & 7] = qk_read(f + 8);
+      hook(f);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int f = 0; f < 32; ++f) {
-        sacc[f & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[f & 7], qb[f >> 1], sacc[f & 1], 0, 0, 0);
-        if (f + 8 < 32) av[f & 7] = qk_read(f + 8);
-        if constexpr (MULTI) {
-          if (f % (32 / RPW) == 32 / RPW - 1) issue_row(nt, f / (32 / RPW), next);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
     }
+  };
 
-    // online softmax of head h over this tile's 32 keys: lane (G, c16) holds
-    // keys 16kb + 4G + r; the other three row groups hold the rest
+  // Online softmax of head h over a tile's 32 keys (lane (G, c16) holds keys
+  // 16kb + 4G + r; the other three row groups hold the rest), branch-free
+  // but for the rare rescale.  The reference maximum moves lazily: only when
+  // the tile maximum exceeds it by more than 2^8 (log2 units); the first tile
+  // with a valid key moves it.  The exponentials are v_exp_f32 itself: the
+  // arguments are at most 8, results below 2^-126 do not matter here, and a
+  // masked key (-inf) or a head with no valid key yet (reference -inf) gives
+  // 0.  Returns the bf16 PV operand.
+  auto softmax = [&](const f32x4_t (&sc)[2], uint32_t vm) -> bf16x8_t {
+    const uint32_t vg = vm >> (4 * G);  // bit 16 kb + r: key 16 kb + 4G + r
     float p[2][4];
     float tmx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = 16 * kb + 4 * G + r;
-        p[kb][r] = ((vmask >> key) & 1) ? sacc[kb][r] * sl2 : -INFINITY;
+        p[kb][r] = ((vg >> (16 * kb + r)) & 1) ? sc[kb][r] * sl2 : -INFINITY;
         tmx = fmaxf(tmx, p[kb][r]);
       }
     tmx = fmaxf(tmx, row_swap16(tmx));
     tmx = fmaxf(tmx, half_swap(tmx));
-    // lazily moved reference: rescale only when the tile max exceeds it by
-    // more than 2^8 (log2 units); the first tile with a valid key moves it
-    if (__ballot(tmx > mrun + 8.f)) {
-      const float mnew = fmaxf(mrun, tmx);
-      if (mnew > mrun) {
-        const float alpha = exp2f(mrun - mnew);
-        lrun *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < 32; ++cb) oacc[cb] *= alpha;
-        mrun = mnew;
-      }
-    }
-    const bool none = mrun == -INFINITY;
+    const bool move = __ballot(tmx > mrun + 8.f) != 0;
+    const float mnew = move ? fmaxf(mrun, tmx) : mrun;
+    const bool none = mnew == -INFINITY;
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[kb][r] = none ? 0.f : exp2f(p[kb][r] - mrun);
+        p[kb][r] = __builtin_amdgcn_exp2f(none ? -INFINITY : p[kb][r] - mnew);
         rs += p[kb][r];
       }
     rs += row_swap16(rs);
     rs += half_swap(rs);
+    if (__ballot(mnew > mrun)) {
+      const float alpha = mnew > mrun ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.f;
+      lrun *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < 32; ++cb) oacc[cb] *= alpha;
+      mrun = mnew;
+    }
     lrun += rs;
     u32x4_t pk;
     pk.x = pack_bf16x2(p[0][0], p[0][1]);
     pk.y = pack_bf16x2(p[0][2], p[0][3]);
     pk.z = pack_bf16x2(p[1][0], p[1][1]);
     pk.w = pack_bf16x2(p[1][2], p[1][3]);
-    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk);
+    return __builtin_bit_cast(bf16x8_t, pk);
+  };
 
-    // O^T[ch][head] += R^T[ch][key] P^T[key][head]: in each 16-lane group,
-    // lane i points at key row 4G + i/4 (and 16 + 4G + i/4), channels
-    // 16cb + 4(i % 4) .. +3, and receives channel 16cb + i of the 4 rows.
+  // O^T[ch][head] += R^T[ch][key] P^T[key][head]: in each 16-lane group,
+  // lane i points at key row 4G + i/4 (and 16 + 4G + i/4), channels
+  // 16cb + 4(i % 4) .. +3, and receives channel 16cb + i of the 4 rows.
+  auto pv = [&](const bf16_t* rows, bf16x8_t pb) {
     const int kr0 = 4 * G + (c16 >> 2);
     const int kr1 = kr0 + 16;
     const bf16_t* rp0 = rows + kr0 * kAtD;
@@ -549,20 +539,47 @@ void attn_hs(AttnArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
+  };
 
-    if constexpr (MULTI) {
+  // the copies of the tile at row j0 into `dst`, one row per (32 / RPW) QK
+  // steps; past the split's end every row is invalid and the copy reads the
+  // harmless row into the idle buffer, so the request is unconditional
+  auto next_tile = [&](int j0) -> TileSrc {
+    int sidx_l = 0;
+    // row j0 + l's selected index; entries past the selected part (or the
+    // split) are never used, the clamp only keeps the read inside s_idx
+    if constexpr (MULTI && CSA) sidx_l = s_idx[min(j0 - start + (lane & 31), kHsMaxSplitRows - 1)];
+    return resolve_tile(j0, sidx_l);
+  };
+
+  if constexpr (!MULTI) {
+    // a single tile: logits, softmax, PV
+    if (start < end) {
+      f32x4_t sc[2];
+      qk(s_rows0, sc, [](int) {});
+      pv(s_rows0, softmax(sc, vmask));
+    }
+  } else {
+    // multi-tile splits: the next tile's rows are copied into the other
+    // buffer while this one is used; one barrier per tile
+    auto tile = [&](int j0, const bf16_t* rows, bf16_t* next) {
+      const TileSrc nt = next_tile(j0 + kHsRows);
+      f32x4_t sc[2];
+      qk(rows, sc, [&](int f) {
+        if (f % (32 / RPW) == 32 / RPW - 1) issue_row(nt, f / (32 / RPW), next);
+      });
+      pv(rows, softmax(sc, vmask));
       // the next tile's rows have landed and every wave is done with this one
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if constexpr (FP8) convert_rows(nt.fp8, next);
       __syncthreads();
       vmask = nt.mask;
+    };
+    for (int j0 = start; j0 < end; j0 += 2 * kHsRows) {
+      tile(j0, s_rows0, s_rows1);
+      if (j0 + kHsRows >= end) break;
+      tile(j0 + kHsRows, s_rows1, s_rows0);
     }
-  };
-
-  for (int j0 = start; j0 < end; j0 += 2 * kHsRows) {
-    tile_step(j0, s_rows0, s_rows1);
-    if (j0 + kHsRows >= end) break;
-    tile_step(j0 + kHsRows, s_rows1, s_rows0);
   }
 
   // ---- epilogue: lane (G, c16) holds channels 16cb + 4G + r of head h
