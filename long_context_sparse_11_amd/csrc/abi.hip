@@ -598,8 +598,8 @@ int attn_common(AttnArgs& a, double rope_base, int keys_per_query, void* ws, siz
     if (a.splits > 1) {
       const size_t need = attn_ws_bytes(a.dt, a.B, a.Tq, a.H, a.D, keys_per_query);
       if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
-      a.part_o = (float*)ws;
-      a.part_ml = a.part_o + (size_t)a.B * a.Tq * a.splits * a.H * a.D;
+      a.part_ml = (float*)ws;
+      a.part_o = (bf16_t*)(a.part_ml + (size_t)a.B * a.Tq * a.splits * a.H * 2);
     }
   } else {
     a.splits = 1;

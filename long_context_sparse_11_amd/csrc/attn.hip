@@ -620,8 +620,11 @@ void attn_hs(AttnArgs a) {
       a.part_ml[2 * slot + 1] = lrun;
     }
     // the output's rope slice is rotated back by -tpos here (the rotation is
-    // linear, so the merge of the splits commutes with it)
-    float* po = a.part_o + slot * kAtD;
+    // linear, so the merge of the splits commutes with it); the split
+    // outputs are stored in bf16, halving the bytes this epilogue writes and
+    // the merge reads (each is unnormalised against its own maximum, so the
+    // rounding is relative to the values themselves)
+    bf16_t* po = a.part_o + slot * kAtD;
 #pragma unroll
     for (int cb = 0; cb < 32; ++cb) {
       float o[4] = {oacc[cb][0], oacc[cb][1], oacc[cb][2], oacc[cb][3]};
@@ -638,14 +641,17 @@ void attn_hs(AttnArgs a) {
           }
         }
       }
-      *reinterpret_cast<f32x4_t*>(po + c) = f32x4_t{o[0], o[1], o[2], o[3]};
+      uint2 pk;
+      pk.x = pack_bf16x2(o[0], o[1]);
+      pk.y = pack_bf16x2(o[2], o[3]);
+      *reinterpret_cast<uint2*>(po + c) = pk;
     }
   }
 }
 
 // Merge of the key-range splits: partial maxima are in log2 units of the
-// scaled logits, partial sums and outputs unnormalised (outputs already
-// rotated back by -tpos on their rope slice).  grid (B*Tq, H),
+// scaled logits, partial sums and outputs unnormalised (outputs in bf16,
+// already rotated back by -tpos on their rope slice).  grid (B*Tq, H),
 // 128 threads of 4 channels each (the 512-wide Flash rows).  The partial
 // outputs of the first kCbPre splits are requested before the per-split
 // weights are known, so the two dependent reads overlap; the weights go
@@ -661,12 +667,17 @@ __global__ __launch_bounds__(128) void attn_combine(AttnArgs a) {
   const int S = a.splits;
   const int64_t slot0 = (int64_t)qi * S * a.H + h;
   const int c = threadIdx.x * 4;
-  const float* po = a.part_o + slot0 * kAtD + c;
+  const bf16_t* po = a.part_o + slot0 * kAtD + c;
   const int64_t sstride = (int64_t)a.H * kAtD;
-  f32x4_t v[kCbPre];
+  // four bf16 split-output channels to f32
+  auto widen = [](uint2 w) {
+    return f32x4_t{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                   __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+  };
+  uint2 v[kCbPre];
 #pragma unroll
   for (int u = 0; u < kCbPre; ++u)
-    v[u] = u < S ? *reinterpret_cast<const f32x4_t*>(po + u * sstride) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    v[u] = u < S ? *reinterpret_cast<const uint2*>(po + u * sstride) : uint2{0u, 0u};
   if (threadIdx.x < 64) {  // one wave merges the (max, sum) pairs
     const int lane = threadIdx.x;
     const float skl2 = a.sink[h] * kLog2e;
@@ -692,15 +703,15 @@ __global__ __launch_bounds__(128) void attn_combine(AttnArgs a) {
   f32x4_t o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < kCbPre; ++u)
-    if (u < S) o += s_w[u] * v[u];
+    if (u < S) o += s_w[u] * widen(v[u]);
   for (int s = kCbPre; s < S; s += 8) {
-    f32x4_t w8[8];
+    uint2 w8[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      w8[u] = s + u < S ? *reinterpret_cast<const f32x4_t*>(po + (s + u) * sstride) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      w8[u] = s + u < S ? *reinterpret_cast<const uint2*>(po + (s + u) * sstride) : uint2{0u, 0u};
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (s + u < S) o += s_w[s + u] * w8[u];
+      if (s + u < S) o += s_w[s + u] * widen(w8[u]);
   }
   float r[4] = {o[0], o[1], o[2], o[3]};
   T* op = (T*)a.out + ((int64_t)qi * a.H + h) * kAtD + c;
@@ -735,7 +746,8 @@ int64_t attn_max_csa_keys() { return (int64_t)kMaxSplits * kHsMaxSplitRows; }
 size_t attn_ws_bytes(int dt, int B, int Tq, int H, int D, int keys_per_query) {
   const int s = attn_splits(dt, B, Tq, H, D, keys_per_query);
   if (s <= 1) return 0;
-  return (size_t)B * Tq * s * H * ((size_t)D + 2) * sizeof(float);
+  // (max, sum) pairs in f32, then the split outputs in bf16
+  return (size_t)B * Tq * s * H * (2 * sizeof(float) + (size_t)D * sizeof(bf16_t));
 }
 
 template <typename T>

@@ -194,8 +194,8 @@ struct AttnArgs {
   // this many bytes (kv_fp8_row_bytes; bf16 MFMA shape only)
   int pool_row_bytes;
   int splits;           // key-range splits per query (1 = no combine pass)
-  float* part_o;        // [B*Tq, splits, H, D] when splits > 1
-  float* part_ml;       // [B*Tq, splits, H, 2]
+  float* part_ml;       // [B*Tq, splits, H, 2] when splits > 1: (max, sum)
+  bf16_t* part_o;       // [B*Tq, splits, H, D] unnormalised split outputs
 };
 bool attn_uses_mfma(int dt, int H, int D, int R);
 int attn_splits(int dt, int B, int Tq, int H, int D, int keys_per_query);
