@@ -145,36 +145,42 @@ __device__ __forceinline__ void fp4_operand(const KeyTile<true>& kt, bf16x8_t (&
 // z + bias (with overlap, also the previous block's second-stream rows)
 // weights the rows of c; then RMSNorm with the gain, and RoPE of the last
 // rope_dims channels at the block's position.  One workgroup; thread t holds
-// channels 2t and 2t + 1.  The entry goes to row `row` of the job's pool.
-// For the indexer-key job the entry is then scored against every query of
-// the sequence that sees it, from the bf16 value as stored.
+// channels 2t and 2t + 1.  The entry goes to row n_entries - 1 of the job's
+// pool when the step closes a block for the sequence (the rule of job jrow),
+// or with `ring` to the window ring's slot.  For the indexer-key job the
+// entry is then scored against every query of the sequence that sees it,
+// from the bf16 value as stored.
 // 8 rows: a CSA block with its overlap (2m, m = 4) or a window row; larger
 // blocks run the compressor as a launch of its own.  The bound sizes the
 // row registers, and with it the fused kernel's occupancy (85 VGPRs at 8
 // rows, 123 at 16).
 constexpr int kFreshMaxRows = 8;
 
-__device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressArgs& j, int b,
-                                            int row, bool score, float* skey, float* red) {
+__device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressArgs& j,
+                                            const CompressArgs& jrow, bool ring, int b,
+                                            bool score, float* skey, float* red) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int D = j.D, m = j.m;
   const int c0 = 2 * tid;
   const bool act = c0 < D;
   const int cc = act ? c0 : 0;
-  // the previous block's stream, when there is a block before this one
-  const bool prev = j.overlap && j.prev_c_b && !(j.pos0 && j.pos0[b] < m);
-  const int nr = m + (prev ? m : 0);
+  // The row addresses come from the arguments alone, so every load is issued
+  // before the first scalar load (the block's start, the entry count) has
+  // returned: the previous block's stream is read whenever it is given and
+  // pooled only when there is a block before this one (nr rows); rows past
+  // the block re-read row 0 and are dropped.
+  const bool has_prev = j.overlap && j.prev_c_b;
+  const int nr_max = m + (has_prev ? m : 0);
   const bf16_t* ca = (const bf16_t*)j.c_a + (int64_t)b * j.T * D;
   const bool hza = j.z_a != nullptr;
   const bf16_t* za = hza ? (const bf16_t*)j.z_a + (int64_t)b * j.T * D : ca;
-  const bf16_t* cb = prev ? (const bf16_t*)j.prev_c_b + (int64_t)b * m * D : ca;
-  const bf16_t* zb = prev ? (const bf16_t*)j.prev_z_b + (int64_t)b * m * D : za;
-  // every load first: rows past the block re-read row 0 and are dropped
+  const bf16_t* cb = has_prev ? (const bf16_t*)j.prev_c_b + (int64_t)b * m * D : ca;
+  const bf16_t* zb = has_prev ? (const bf16_t*)j.prev_z_b + (int64_t)b * m * D : za;
   uint32_t cw[kFreshMaxRows], zw[kFreshMaxRows];
   float2 bw[kFreshMaxRows];
 #pragma unroll
   for (int r = 0; r < kFreshMaxRows; ++r) {
-    const int rr = r < nr ? r : 0;
+    const int rr = r < nr_max ? r : 0;
     const bool in_a = rr < m;
     const int64_t ro = (int64_t)(in_a ? rr : rr - m) * D + cc;
     cw[r] = *reinterpret_cast<const uint32_t*>((in_a ? ca : cb) + ro);
@@ -184,6 +190,8 @@ __device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressAr
   }
   const float2 gn = j.gain ? *reinterpret_cast<const float2*>(j.gain + cc) : make_float2(1.f, 1.f);
   const int64_t pos = j.pos0 ? j.pos0[b] : 0;
+  const bool prev = has_prev && !(j.pos0 && pos < m);
+  const int nr = m + (prev ? m : 0);
   // scoring (indexer-key job): thread (h = tid / 4, quarter qq = tid % 4)
   // takes head h over channels 32 qq .. 32 qq + 31; the first query's slice
   // and weight are requested with the rows
@@ -203,6 +211,17 @@ __device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressAr
   // the sequence's entry count and first query position, requested early too
   const int n_ent = min(a.n_entries[b], a.N_cap);
   const int64_t qpos = a.q_pos0[b];
+  // the output row, decided once the loads are in flight: an entry goes to
+  // row n_entries - 1 of its pool when the step closes a block (the rule of
+  // the key job, jrow), a window row to its ring slot; -1: nothing is stored
+  const int row = ring ? (int)compress_out_row(j, b, 0)
+                       : (compress_out_row(jrow, b, 0) >= 0 ? n_ent - 1 : -1);
+  // the RoPE angle of this thread's channel pair depends on the position
+  // alone: computed while the rows are in flight
+  const int R = j.rope_dims;
+  const bool rot = R > 0 && act && c0 >= D - R;
+  float cs = 1.f, sn = 0.f;
+  if (rot) rope_cos_sin(pos, (c0 - (D - R)) >> 1, j.rope_theta1, cs, sn);
 
   auto logit = [&](int r, int e) {  // base-2 logit of row r, channel c0 + e
     const bool in_a = r < m;
@@ -217,11 +236,14 @@ __device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressAr
       mx1 = fmaxf(mx1, logit(r, 1));
     }
   }
+  // v_exp_f32 directly: the arguments are at most 0, and weights below
+  // 2^-126 next to the maximum's weight of 1 do not change the sums
   float den0 = 0.f, den1 = 0.f, acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
   for (int r = 0; r < kFreshMaxRows; ++r) {
     if (r < nr) {
-      const float p0 = exp2f(logit(r, 0) - mx0), p1 = exp2f(logit(r, 1) - mx1);
+      const float p0 = __builtin_amdgcn_exp2f(logit(r, 0) - mx0);
+      const float p1 = __builtin_amdgcn_exp2f(logit(r, 1) - mx1);
       den0 += p0;
       den1 += p1;
       acc0 += p0 * bf16_to_f32(cw[r] & 0xffffu);
@@ -239,10 +261,7 @@ __device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressAr
     y0 = y0 * inv * gn.x;
     y1 = y1 * inv * gn.y;
   }
-  const int R = j.rope_dims;
-  if (R > 0 && act && c0 >= D - R) {
-    float cs, sn;
-    rope_cos_sin(pos, (c0 - (D - R)) >> 1, j.rope_theta1, cs, sn);
+  if (rot) {
     const float x0 = y0, x1 = y1;
     y0 = x0 * cs - x1 * sn;
     y1 = x0 * sn + x1 * cs;
@@ -262,6 +281,7 @@ __device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressAr
     am = fmaxf(am, __shfl_xor(am, 8));
     const uint32_t sb = mx8_scale_byte(am);
     uint8_t* rp = (uint8_t*)j.out + (int64_t)b * j.out_bstride + (int64_t)row * j.out_fp8_row;
+    if (row < 0) return;
     if (f8) {
       *reinterpret_cast<uint16_t*>(rp + c0) = (uint16_t)(e4m3_code(y0, sb) | (e4m3_code(y1, sb) << 8));
       if ((tid & 15) == 0) rp[D + j.rope_dims + (c0 >> 5)] = (uint8_t)sb;
@@ -282,7 +302,7 @@ __device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressAr
     am = fmaxf(am, __shfl_xor(am, 8));
     const uint32_t sb = mx_scale_byte(am);
     const uint32_t e0 = e2m1_code(y0, sb), e1 = e2m1_code(y1, sb);
-    if (act) {
+    if (act && row >= 0) {
       ((uint8_t*)j.out)[at / 2 + tid] = (uint8_t)(e0 | (e1 << 4));
       if ((tid & 15) == 0) j.out_scales[at / 32 + (tid >> 4)] = (uint8_t)sb;
     }
@@ -290,11 +310,11 @@ __device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressAr
     v1 = e2m1_value(e1, sb);
   } else {
     const uint32_t packed = pack_bf16x2(y0, y1);
-    if (act) *reinterpret_cast<uint32_t*>((bf16_t*)j.out + at + c0) = packed;
+    if (act && row >= 0) *reinterpret_cast<uint32_t*>((bf16_t*)j.out + at + c0) = packed;
     v0 = bf16_to_f32(packed & 0xffffu);
     v1 = bf16_to_f32(packed >> 16);
   }
-  if (!score) return;
+  if (!score || row < 0) return;
 
   // Score the stored entry for every query t of the sequence that sees it:
   // the 4 quarters of a head meet by lane swaps, the 64 heads by a wave sum
@@ -320,11 +340,14 @@ __device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressAr
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const uint32_t wd[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+      const float* kc = skey + 32 * qq + 8 * u;
+      const f32x4_t k0 = *reinterpret_cast<const f32x4_t*>(kc);
+      const f32x4_t k1 = *reinterpret_cast<const f32x4_t*>(kc + 4);
+      const float kv[8] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int c = 32 * qq + 8 * u + 2 * e;
-        dot += bf16_to_f32(wd[e] & 0xffffu) * skey[c];
-        dot += bf16_to_f32(wd[e] >> 16) * skey[c + 1];
+        dot += bf16_to_f32(wd[e] & 0xffffu) * kv[2 * e];
+        dot += bf16_to_f32(wd[e] >> 16) * kv[2 * e + 1];
       }
     }
     dot += __shfl_xor(dot, 1);
@@ -361,11 +384,15 @@ void index_decode(IndexArgs a, int tiles_per_wave, int chunks, FreshJobs f) {
       const int fb = id % a.B, jk = id / a.B;
       // entries go to row n_entries - 1 (when the step closes a block); the
       // window row (job 2) to its ring slot
-      const int row = jk == 2 ? (int)compress_out_row(f.job[2], fb, 0)
-                    : compress_out_row(f.job[0], fb, 0) >= 0 ? min(a.n_entries[fb], a.N_cap) - 1
-                                                             : -1;
-      if (row >= 0)
-        fresh_entry(a, f.job[jk], fb, row, id < a.B, reinterpret_cast<float*>(sq), sw);
+      // (-1: no block closes for the sequence at this step; the entry is
+      // still pooled, as its loads do not wait for this, but not stored).
+      // One call per job index, so that each reads its job's fields at fixed
+      // argument offsets (with a computed index the fields came through a
+      // chain of dependent scalar loads ahead of the first row load).
+      float* skey = reinterpret_cast<float*>(sq);
+      if (jk == 0) fresh_entry(a, f.job[0], f.job[0], false, fb, true, skey, sw);
+      else if (jk == 1) fresh_entry(a, f.job[1], f.job[0], false, fb, false, skey, sw);
+      else fresh_entry(a, f.job[2], f.job[2], true, fb, false, skey, sw);
       return;
     }
     id -= fj;
