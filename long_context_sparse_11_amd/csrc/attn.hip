@@ -456,10 +456,9 @@ void attn_hs(AttnArgs a) {
   // 16kb + 4G + r; the other three row groups hold the rest), branch-free
   // but for the rare rescale.  The reference maximum moves lazily: only when
   // the tile maximum exceeds it by more than 2^8 (log2 units); the first tile
-  // with a valid key moves it.  The exponentials are v_exp_f32 itself: the
-  // arguments are at most 8, results below 2^-126 do not matter here, and a
-  // masked key (-inf) or a head with no valid key yet (reference -inf) gives
-  // 0.  Returns the bf16 PV operand.
+  // with a valid key moves it.  The weights come from v_exp_f32 alone
+  // (exp2_weight; arguments at most 8): a masked key (-inf) or a head with
+  // no valid key yet (reference -inf) gives 0.  Returns the bf16 PV operand.
   auto softmax = [&](const f32x4_t (&sc)[2], uint32_t vm) -> bf16x8_t {
     const uint32_t vg = vm >> (4 * G);  // bit 16 kb + r: key 16 kb + 4G + r
     float p[2][4];
@@ -481,13 +480,13 @@ void attn_hs(AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[kb][r] = __builtin_amdgcn_exp2f(none ? -INFINITY : p[kb][r] - mnew);
+        p[kb][r] = exp2_weight(none ? -INFINITY : p[kb][r] - mnew);
         rs += p[kb][r];
       }
     rs += row_swap16(rs);
     rs += half_swap(rs);
     if (__ballot(mnew > mrun)) {
-      const float alpha = mnew > mrun ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.f;
+      const float alpha = mnew > mrun ? exp2_weight(mrun - mnew) : 1.f;
       lrun *= alpha;
 #pragma unroll
       for (int cb = 0; cb < 32; ++cb) oacc[cb] *= alpha;

@@ -16,6 +16,12 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+// 2^x by v_exp_f32 alone (about 1 ulp; results below 2^-126 flush to 0,
+// -inf gives 0).  For softmax weights taken against the running maximum,
+// where a weight below 2^-126 next to the maximum's weight of 1 cannot
+// change a sum; exp2f adds a rescaling around the instruction to keep such
+// results, seven instructions in place of one.
+__device__ __forceinline__ float exp2_weight(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------------------

@@ -116,8 +116,8 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a0, Compress
       for (int e = 0; e < VEC; ++e) {
         const float l = ((hz[u] ? zv[e] : 0.f) + (hb[u] ? bv[e] : 0.f)) * kLog2e;  // base 2
         const float nm = fmaxf(mx[e], l);
-        const float sc = exp2f(mx[e] - nm);
-        const float p = exp2f(l - nm);
+        const float sc = exp2_weight(mx[e] - nm);
+        const float p = exp2_weight(l - nm);
         den[e] = den[e] * sc + p;
         acc[e] = acc[e] * sc + p * cv[e];
         mx[e] = nm;
@@ -146,8 +146,8 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a0, Compress
       for (int e = 0; e < VEC; ++e) {
         const float om = s_mx[o + e];
         const float M = fmaxf(mx[e], om);
-        const float w0 = mx[e] == -INFINITY ? 0.f : exp2f(mx[e] - M);
-        const float w1 = om == -INFINITY ? 0.f : exp2f(om - M);
+        const float w0 = mx[e] == -INFINITY ? 0.f : exp2_weight(mx[e] - M);
+        const float w1 = om == -INFINITY ? 0.f : exp2_weight(om - M);
         den[e] = den[e] * w0 + s_den[o + e] * w1;
         acc[e] = acc[e] * w0 + s_acc[o + e] * w1;
         mx[e] = M;
@@ -371,8 +371,8 @@ __global__ __launch_bounds__(256) void compress_rows_kernel(CompressArgs a0, Com
       for (int e = 0; e < VEC; ++e) {
         const float lg = logit(r, e, zv);          // -inf for a missing row
         const float mn = fmaxf(mx[e], lg);
-        const float sc = exp2f(mx[e] - mn);
-        const float p = exp2f(lg - mn);
+        const float sc = exp2_weight(mx[e] - mn);
+        const float p = exp2_weight(lg - mn);
         den[e] = den[e] * sc + p;
         acc[e] = acc[e] * sc + p * cv[e];
         mx[e] = mn;

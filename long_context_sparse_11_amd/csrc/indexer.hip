@@ -236,14 +236,12 @@ __device__ __forceinline__ void fresh_entry(const IndexArgs& a, const CompressAr
       mx1 = fmaxf(mx1, logit(r, 1));
     }
   }
-  // v_exp_f32 directly: the arguments are at most 0, and weights below
-  // 2^-126 next to the maximum's weight of 1 do not change the sums
   float den0 = 0.f, den1 = 0.f, acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
   for (int r = 0; r < kFreshMaxRows; ++r) {
     if (r < nr) {
-      const float p0 = __builtin_amdgcn_exp2f(logit(r, 0) - mx0);
-      const float p1 = __builtin_amdgcn_exp2f(logit(r, 1) - mx1);
+      const float p0 = exp2_weight(logit(r, 0) - mx0);
+      const float p1 = exp2_weight(logit(r, 1) - mx1);
       den0 += p0;
       den1 += p1;
       acc0 += p0 * bf16_to_f32(cw[r] & 0xffffu);
