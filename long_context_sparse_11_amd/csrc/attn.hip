@@ -241,8 +241,17 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 // v_cvt_scalef32_pk_bf16_fp8 (exact: an E4M3 value times a power of two fits
 // bf16); window rows stay bf16 and are copied as before.  Everything after
 // the tile copy is unchanged.
+//
+// Waves per SIMD: the bf16 multi-tile kernel is held to two (256 registers
+// each), so that two workgroups share a compute unit and hide each other's
+// copy, softmax and barrier waits; to fit, its operand reads run 4 ahead of
+// the MFMAs (not 8 and 16) and its LDS addresses are recomputed per tile.
+// Prefill attention: 579 -> 469 us.  The others keep one wave per SIMD: a
+// single-tile split is one short workgroup per compute unit, and the FP8
+// kernel's staging area leaves LDS for one workgroup.
 template <bool CSA, bool MULTI, int NW, bool FP8>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(MULTI && !FP8 ? 2 : 1, MULTI && !FP8 ? 2 : 1)))
 void attn_hs(AttnArgs a) {
   constexpr int RPW = kHsRows / NW;  // tile rows each wave copies
   // two row buffers as distinct objects: with every access naming a fixed
@@ -425,28 +434,36 @@ void attn_hs(AttnArgs a) {
   // Logits S^T[key][head] of one tile over all 512 channels for two 16-key
   // blocks (two independent accumulator chains, interleaved).  The order is
   // pinned: with one wave per SIMD nothing else hides the LDS latency, so the
-  // 32 operand reads run 8 ahead of their MFMAs.  hook(f) runs after MFMA
-  // step f: in multi-tile splits it issues the next tile's copies, spread
-  // between the reads instead of stalling issue up front.
+  // 32 operand reads run 8 ahead of their MFMAs (4 at two waves per SIMD).
+  // hook(f) runs after MFMA step f: in multi-tile splits it issues the next
+  // tile's copies, spread between the reads instead of stalling issue up
+  // front.  At two waves per SIMD the lane index is made opaque per tile, so
+  // the read addresses are recomputed (a few VALU ops) rather than held in
+  // registers across the tile loop.
+  constexpr bool kTwoWaves = MULTI && !FP8;
+  constexpr int kQkAhead = kTwoWaves ? 4 : 8;
   auto qk = [&](const bf16_t* rows, f32x4_t (&acc)[2], auto&& hook) {
     acc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     acc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const bf16_t* rpk[2] = {rows + c16 * kAtD, rows + (16 + c16) * kAtD};
-    const int swk[2] = {hs_swz(c16), hs_swz(16 + c16)};
+    int ln = lane;
+    if constexpr (kTwoWaves) asm volatile("" : "+v"(ln));
+    const int lc16 = ln & 15, lG = ln >> 4;
+    const bf16_t* rpk[2] = {rows + lc16 * kAtD, rows + (16 + lc16) * kAtD};
+    const int swk[2] = {hs_swz(lc16), hs_swz(16 + lc16)};
     // step f reads block f % 2, channel slice f / 2
     auto qk_read = [&](int f) {
       const int kb = f & 1, ks = f >> 1;
       return *reinterpret_cast<const bf16x8_t*>(rpk[kb] + 128 * (ks >> 2) +
-                                                8 * ((4 * (ks & 3) + G) ^ swk[kb]));
+                                                8 * ((4 * (ks & 3) + lG) ^ swk[kb]));
     };
-    bf16x8_t av[8];
+    bf16x8_t av[kQkAhead];
 #pragma unroll
-    for (int f = 0; f < 8; ++f) av[f] = qk_read(f);
+    for (int f = 0; f < kQkAhead; ++f) av[f] = qk_read(f);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int f = 0; f < 32; ++f) {
-      acc[f & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[f & 7], qb[f >> 1], acc[f & 1], 0, 0, 0);
-      if (f + 8 < 32) av[f & 7] = qk_read(f + 8);
+      acc[f & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[f % kQkAhead], qb[f >> 1], acc[f & 1], 0, 0, 0);
+      if (f + kQkAhead < 32) av[f % kQkAhead] = qk_read(f + kQkAhead);
       hook(f);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -505,12 +522,15 @@ void attn_hs(AttnArgs a) {
   // lane i points at key row 4G + i/4 (and 16 + 4G + i/4), channels
   // 16cb + 4(i % 4) .. +3, and receives channel 16cb + i of the 4 rows.
   auto pv = [&](const bf16_t* rows, bf16x8_t pb) {
-    const int kr0 = 4 * G + (c16 >> 2);
+    int ln = lane;
+    if constexpr (kTwoWaves) asm volatile("" : "+v"(ln));
+    const int lc16 = ln & 15, lG = ln >> 4;
+    const int kr0 = 4 * lG + (lc16 >> 2);
     const int kr1 = kr0 + 16;
     const bf16_t* rp0 = rows + kr0 * kAtD;
     const bf16_t* rp1 = rows + kr1 * kAtD;
     const int sw0 = hs_swz(kr0), sw1 = hs_swz(kr1);
-    const int q4 = c16 & 3;
+    const int q4 = lc16 & 3;
 #pragma unroll
     for (int c8 = 0; c8 < 4; ++c8) {
       bf16x8_t av[8];
@@ -530,14 +550,16 @@ void attn_hs(AttnArgs a) {
       for (int k = 0; k < 8; ++k)
         oacc[8 * c8 + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k], pb, oacc[8 * c8 + k], 0, 0, 0);
     }
-    // 16 transposing reads (8 channel blocks) ahead, then one MFMA per two
-    __builtin_amdgcn_sched_group_barrier(0x100, 16, 1);
+    // kPvAhead transposing reads (two per channel block) ahead, then one
+    // MFMA per two
+    constexpr int kPvAhead = kTwoWaves ? 4 : 16;
+    __builtin_amdgcn_sched_group_barrier(0x100, kPvAhead, 1);
 #pragma unroll
-    for (int i = 0; i < 24; ++i) {
+    for (int i = 0; i < 32 - kPvAhead / 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, kPvAhead / 2, 1);
   };
 
   // the copies of the tile at row j0 into `dst`, one row per (32 / RPW) QK
