@@ -89,7 +89,17 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t x, uint32_t& total, 
   return before;
 }
 
-__global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkArgs a) {
+// CAND: the segment is a merge of chunk winners (mode 2), whose candidate
+// indices come with the scores; otherwise indices are positions.  WIDE: held
+// to 64 VGPRs so that two workgroups share a compute unit, for launches of
+// many segments (a prefill chunk's queries: 4,096 selects took 132 us at one
+// workgroup per compute unit, 101 us at two); what that spills costs a
+// latency-bound decode select ~0.4 us, so few segments keep the unconstrained
+// instance.
+template <bool CAND, bool WIDE>
+__global__ __launch_bounds__(kTkThreads)
+__attribute__((amdgpu_waves_per_eu(WIDE ? 8 : 1, WIDE ? 8 : 4)))
+void topk_kernel(TopkArgs a) {
   __shared__ TkShared S;
   const int seg = blockIdx.x;
   const int tid = threadIdx.x;
@@ -103,7 +113,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkArgs a) {
   int query, base_index = 0, cap;
   const float* src;
   const int32_t* src_idx = nullptr;
-  if (a.mode == 2) {
+  if (CAND) {
     query = seg;
     cap = a.nchunks * K;
     src = a.scores + (int64_t)query * cap;
@@ -129,7 +139,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkArgs a) {
 
   // ---- keys in registers; every load issued before any is consumed
   uint32_t key[kTkRounds];
-  int32_t vi[kTkRounds];  // candidate indices (mode 2)
+  int32_t vi[CAND ? kTkRounds : 1];  // candidate indices (mode 2)
   const int e0 = tid * kTkRounds;
   float v[kTkRounds];
   {
@@ -140,7 +150,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkArgs a) {
         const f32x4_t x = reinterpret_cast<const f32x4_t*>(src + e0)[u];
         v[4 * u] = x[0]; v[4 * u + 1] = x[1]; v[4 * u + 2] = x[2]; v[4 * u + 3] = x[3];
       }
-      if (src_idx) {
+      if constexpr (CAND) {
 #pragma unroll
         for (int u = 0; u < kTkRounds / 4; ++u) {
           const int4 x = reinterpret_cast<const int4*>(src_idx + e0)[u];
@@ -152,16 +162,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkArgs a) {
       for (int i = 0; i < kTkRounds; ++i) {
         const int e = min(e0 + i, cap - 1);
         v[i] = src[e];
-        vi[i] = src_idx ? src_idx[e] : 0;
+        if constexpr (CAND) vi[i] = src_idx[e];
       }
     }
-    if (!src_idx) {
-#pragma unroll
-      for (int i = 0; i < kTkRounds; ++i) vi[i] = 0;
-    }
+
   }
   int n = cap;
-  if (a.mode != 2) {
+  if (!CAND) {
     const int b = query / a.Tq;
     const int t = query - b * a.Tq;
     const int n_vis = visible_entries(a.q_pos0[b] + t, a.m, min(a.n_entries[b], a.N_cap));
@@ -182,7 +189,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkArgs a) {
 #pragma unroll
   for (int i = 0; i < kTkRounds; ++i) {
     key[i] = score_key(v[i]);
-    if (e0 + i < n && vi[i] >= 0) live |= 1u << i;
+    if (e0 + i < n && (!CAND || vi[CAND ? i : 0] >= 0)) live |= 1u << i;
   }
 #pragma unroll
   for (int k = 0; k < kBinsPerThread; ++k) S.hist[tid * kBinsPerThread + k] = 0;
@@ -308,11 +315,14 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkArgs a) {
       if (osc) osc[e] = -INFINITY;
     }
   } else if (linear) {
-    uint32_t dg[kTkRounds];
+    // the linear first digit (recomputed where it is used again: held in
+    // registers it would cost 16 per thread)
+    auto digit = [&](int i) {
+      return (uint32_t)fminf((key_score(key[i]) - fmn) * scale, (float)(kBins - 1));
+    };
 #pragma unroll
     for (int i = 0; i < kTkRounds; ++i) {
-      dg[i] = (uint32_t)fminf((key_score(key[i]) - fmn) * scale, (float)(kBins - 1));
-      if ((live >> i) & 1) atomicAdd(&S.hist[dg[i]], 1u);
+      if ((live >> i) & 1) atomicAdd(&S.hist[digit(i)], 1u);
     }
     __syncthreads();
     uint32_t h[kBinsPerThread], local = 0;
@@ -341,8 +351,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkArgs a) {
 #pragma unroll
     for (int i = 0; i < kTkRounds; ++i) {
       const bool v = (live >> i) & 1;
-      above_m |= (v && dg[i] > d1) ? (1u << i) : 0u;
-      in_bin |= (v && dg[i] == d1) ? (1u << i) : 0u;
+      const uint32_t d = digit(i);
+      above_m |= (v && d > d1) ? (1u << i) : 0u;
+      in_bin |= (v && d == d1) ? (1u << i) : 0u;
     }
     __syncthreads();  // sel_* are rewritten below
 
@@ -486,16 +497,24 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkArgs a) {
     const bool c = g || (e && seen_eq < take);
     seen_eq += e ? 1u : 0u;
     if (c) {
-      oidx[p] = src_idx ? vi[i] : base_index + e0 + i;
+      oidx[p] = CAND ? vi[CAND ? i : 0] : base_index + e0 + i;
       if (osc) osc[p] = key_score(key[i]);
       ++p;
     }
   }
 }
 
+// launches of at least this many segments take the two-per-CU instance
+constexpr int kTkWideSegments = 1024;
+
 hipError_t launch_topk(const TopkArgs& a, int segments, hipStream_t stream) {
   if (segments == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(segments), dim3(kTkThreads), 0, stream, a);
+  if (a.mode == 2)
+    hipLaunchKernelGGL((topk_kernel<true, false>), dim3(segments), dim3(kTkThreads), 0, stream, a);
+  else if (segments >= kTkWideSegments)
+    hipLaunchKernelGGL((topk_kernel<false, true>), dim3(segments), dim3(kTkThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((topk_kernel<false, false>), dim3(segments), dim3(kTkThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -260,6 +260,29 @@ def _check_index(q_idx, w_idx, k_idx, n_entries, q_pos0, K, m, score_atol):
     return excused
 
 
+@pytest.mark.parametrize("ties", [False, True])
+@pytest.mark.parametrize("early", [False, True])
+def test_index_topk_many_queries_wide_select(ties, early):
+    """A launch of 1,100 selects (at least 1,024 segments takes the top-k
+    instance that runs two workgroups per compute unit): every query's
+    selection equals the oracle's select on the GPU's own scores, within the
+    band of the oracle's, with and without heavy ties (keys on a coarse
+    grid). Causal visibility is ragged: 2,225 .. 2,500 entries per query, or
+    (early) 0 .. 275, so that queries with nothing visible and with at most
+    K visible are in the launch too."""
+    rng = np.random.default_rng(1100 + int(ties) + 2 * int(early))
+    B, Tq, Hi, Di, N, K, m = 1, 1100, 4, 32, 2500, 64, 4
+    q = rng.standard_normal((B, Tq, Hi, Di)).astype(np.float32)
+    w = np.abs(rng.standard_normal((B, Tq, Hi))).astype(np.float32)
+    k = rng.standard_normal((B, N, Di)).astype(np.float32)
+    if ties:
+        k = np.round(k * 2.0) / 2.0
+        q = np.round(q * 2.0) / 2.0
+    n_ent = np.array([N], np.int32)
+    q_pos0 = np.array([0 if early else 4 * N - Tq])
+    _check_index(q, w, k, n_ent, q_pos0, K, m, score_atol=1e-4)
+
+
 def test_index_toy_fp32():
     d = synth.toy(0)
     keys = O.csa_compress(d["ic_a"].f32, d["iz_a"].f32, d["ibias_a"], 4, c_b=d["ic_b"].f32,
