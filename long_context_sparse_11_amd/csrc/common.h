@@ -68,6 +68,13 @@ struct Elem<float> {
 #pragma unroll
     for (int c = 0; c < VEC / 4; ++c) w[c] = reinterpret_cast<const u32x4_t*>(p)[c];
   }
+  // the same, for data read once: streamed past the caches (non-temporal)
+  template <int VEC>
+  __device__ __forceinline__ static void load_raw_stream(const float* p, u32x4_t* w) {
+#pragma unroll
+    for (int c = 0; c < VEC / 4; ++c)
+      w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p) + c);
+  }
   template <int VEC>
   __device__ __forceinline__ static void from_raw(const u32x4_t* w, float* v) {
 #pragma unroll
@@ -111,6 +118,12 @@ struct Elem<bf16_t> {
   __device__ __forceinline__ static void load_raw(const bf16_t* p, u32x4_t* w) {
 #pragma unroll
     for (int c = 0; c < VEC / 8; ++c) w[c] = reinterpret_cast<const u32x4_t*>(p)[c];
+  }
+  template <int VEC>
+  __device__ __forceinline__ static void load_raw_stream(const bf16_t* p, u32x4_t* w) {
+#pragma unroll
+    for (int c = 0; c < VEC / 8; ++c)
+      w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p) + c);
   }
   template <int VEC>
   __device__ __forceinline__ static void from_raw(const u32x4_t* w, float* v) {

@@ -262,8 +262,10 @@ __global__ __launch_bounds__(64) void compress_finish(CompressArgs a) {
 // The block shape (M rows per stream, the overlap) is a template argument,
 // so every row address is a branch-free select and all 2M (or M) row loads
 // of an entry are issued back to back before any arithmetic (16 KiB in
-// flight per wave for a 512-channel CSA entry).  The biases sit in LDS in
-// base-2 logit units; the lane's gain and RoPE frequencies are loaded once.
+// flight per wave for a 512-channel CSA entry).  Each row is read once, so
+// the loads stream past the caches (non-temporal: the 1M-token pass 1141 ->
+// 1117 us).  The biases sit in LDS in base-2 logit units; the lane's gain
+// and RoPE frequencies are loaded once.
 constexpr int kRowsMaxD = 512;   // widest row the kernel's bias table holds
 
 template <typename T, int VEC, int M, bool OVERLAP>
@@ -320,8 +322,8 @@ __global__ __launch_bounds__(256) void compress_rows_kernel(CompressArgs a0, Com
 #pragma unroll
     for (int r = 0; r < M; ++r) {
       const int64_t ro = a_off + (int64_t)min(r, na - 1) * D;
-      Elem<T>::template load_raw<VEC>((const T*)a.c_a + ro, cw[r]);
-      Elem<T>::template load_raw<VEC>(za_base + ro, zw[r]);
+      Elem<T>::template load_raw_stream<VEC>((const T*)a.c_a + ro, cw[r]);
+      Elem<T>::template load_raw_stream<VEC>(za_base + ro, zw[r]);
     }
     int nb = 0;
     if constexpr (OVERLAP) {
@@ -337,8 +339,8 @@ __global__ __launch_bounds__(256) void compress_rows_kernel(CompressArgs a0, Com
                                        : za_base + ((int64_t)b * a.T + a_row0) * D);
 #pragma unroll
       for (int r = 0; r < M; ++r) {
-        Elem<T>::template load_raw<VEC>(cb + (int64_t)r * D + c0, cw[M + r]);
-        Elem<T>::template load_raw<VEC>(zb + (int64_t)r * D + c0, zw[M + r]);
+        Elem<T>::template load_raw_stream<VEC>(cb + (int64_t)r * D + c0, cw[M + r]);
+        Elem<T>::template load_raw_stream<VEC>(zb + (int64_t)r * D + c0, zw[M + r]);
       }
     }
     const int64_t pos = p0 + a_row0;
