@@ -9,7 +9,8 @@ indexer key, written in place into the caches; one launch with the indexer
 scoring), lightning-indexer scores + top-512 selection, sparse gather
 attention with the sink.  Other workloads
 (--workload): csa1m (batch 8, context 1,048,576), hca1m (HCA decode, batch
-16, context 1,048,576: compress + hca_attn), prefill (CSA chunk of 4,096
+16, context 1,048,576: one hca_decode_attn call, the closing block's entry
+and the attention), prefill (CSA chunk of 4,096
 queries on a 61,440-token prefix), csa64k_pro (V4-Pro attention: 128 heads,
 top-1024), csa64k_fp4 / csa1m_fp4 (as csa64k / csa1m with the indexer keys
 stored in MX FP4; the fresh key is quantized inside the step), swa
@@ -136,7 +137,8 @@ class Step:
         elif kind in HCA:
             N, W = g["N"], g["W"]
             self.out = torch.empty_like(g["q"])
-            n = L.csa_attn_ws_bytes(B, 1, g["H"], D, N + W)
+            n = (L.hca_decode_attn_ws_bytes(B, g["H"], D, N + W) if kind == "hca1m"
+                 else L.csa_attn_ws_bytes(B, 1, g["H"], D, N + W))
             self.ws_a = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
         else:  # prefill
             Tq, N, K, W = g["Tq"], g["N"], g["K"], g["W"]
@@ -167,7 +169,7 @@ class Step:
         attention call; for the output projection its call."""
         g, L = self.g, self.L
         if self.kind in HCA or self.kind == "swa":
-            return self.calls()[1]
+            return self.calls()[-1]
         if self.kind in ("oproj", "oproj_prefill", "compress_stream"):
             return self.calls()[0]
         if not hasattr(self, "scores"):
@@ -297,17 +299,14 @@ class Step:
                                                       out=self.out, ws=self.ws_a)),
             ]
         if kind == "hca1m":
-            N, D, m = g["N"], g["D"], g["m"]
-            pool = g["pool"]
+            # one call: the closing block's entry (pooled by the attention
+            # launch's last split, stored to row N - 1) and the attention
+            m, pool = g["m"], g["pool"]
             return [
-                ("compress", lambda: L.csa_compress(g["c_a"], m, z_a=g["z_a"], bias_a=g["bias_a"],
-                                                    gain=g["gain"], rope_dims=g["R"],
-                                                    pos0=g["block_pos0"], out=pool[:, N - 1:],
-                                                    out_bstride=N * D,
-                                                    ws=self.cws(g["c_a"], m, False))),
-                ("hca_attn", lambda: L.hca_attn(g["q"], pool, g["n_entries"], m, g["win"],
-                                                g["win_pos0"], g["W"], g["sink"], g["q_pos0"],
-                                                rope_dims=g["R"], out=self.out, ws=self.ws_a)),
+                ("hca_step", lambda: L.hca_decode_attn(
+                    g["q"], pool, g["n_entries"], m, g["c_a"], g["z_a"], g["bias_a"], g["gain"],
+                    g["block_pos0"], g["win"], g["win_pos0"], g["W"], g["sink"], g["q_pos0"],
+                    rope_dims=g["R"], out=self.out, ws=self.ws_a)),
             ]
         # prefill
         N, D, Di, m, P = g["N"], g["D"], g["Di"], g["m"], g["prefix"]
@@ -420,12 +419,20 @@ def algorithmic(kind, d):
         out["sparse_attn"] = {"bytes": attn, "flops": out["flops"]["sparse_attn"]}
     elif kind in HCA:
         N = d["N"]
+        # the closing block's two streams in, its entry out (the bias, shared
+        # by the batch, is not counted)
         comp = B * (2 * m * D * bf + vb)
         rows = N + W
-        out["bytes"] = {"compress": comp,
-                        "hca_attn": B * (N * vb + W * D * bf + 2 * H * D * bf)}
-        out["flops"] = {"hca_attn": B * 4 * H * D * rows}
-        out["hca_attn"] = {"bytes": out["bytes"]["hca_attn"], "flops": out["flops"]["hca_attn"]}
+        attn = B * (N * vb + W * D * bf + 2 * H * D * bf)
+        fl = B * 4 * H * D * rows
+        if kind == "hca1m":  # one call does both
+            out["bytes"] = {"hca_step": comp + attn}
+            out["flops"] = {"hca_step": fl}
+            out["hca_step"] = {"bytes": comp + attn, "flops": fl}
+        else:
+            out["bytes"] = {"compress": comp, "hca_attn": attn}
+            out["flops"] = {"hca_attn": fl}
+            out["hca_attn"] = {"bytes": attn, "flops": fl}
     else:
         N, P = d["N"], d["prefix"]
         T = Tq + m
@@ -466,6 +473,8 @@ DOMINANT_KERNELS = {
                            "the step's first launch)"],
     "index_scores": ["index_prefill"],
     "hca_attn": ["attn_hs<false, true, 4>", "attn_combine<bf16>"],
+    "hca_step": ["attn_hs<false, true, 4> (its last split pools the closing block)",
+                 "attn_combine<bf16>"],
     "sparse_attn": ["attn_hs<true, *> (+ attn_combine<bf16> when split)"],
     "output_proj": ["proj_rows<4>", "proj_rows<8>"],
     "output_proj_gemm": ["proj_gemm<0>", "proj_gemm<1>"],
@@ -475,6 +484,7 @@ KERNEL_SOURCES = {
     "index_decode_fresh": ["indexer.hip", "common.h", "kernels.h"],
     "index_scores": ["indexer.hip", "common.h", "kernels.h"],
     "hca_attn": ["attn.hip", "common.h", "kernels.h"],
+    "hca_step": ["attn.hip", "common.h", "kernels.h"],
     "sparse_attn": ["attn.hip", "common.h", "kernels.h"],
     "output_proj": ["oproj.hip", "oproj.h", "common.h", "kernels.h"],
     "compress": ["compress.hip", "common.h", "kernels.h"],

@@ -551,6 +551,50 @@ int hca_attn_kvfp8(int B, int Tq, int H, int D, int rope_dims, double rope_base,
  * keys_per_query rows per query (K + W, or N_cap + W). */
 size_t csa_attn_ws_bytes(int B, int Tq, int H, int D, int keys_per_query);
 
+/* ---------------------------------------------------------------------------
+ * hca_decode_attn - one HCA decode step in one call: the closing block's
+ * entry is pooled, stored and attended together with the entries already in
+ * the pool.  The result is that of csa_compress (HCA: m-row blocks, no
+ * overlap, one block per sequence, entry to row min(n_entries[b], N_cap) - 1
+ * of pool) followed by hca_attn with Tq = 1, up to rounding order.
+ *
+ * [P2] section 3.3 (eqs. 20-23): the new entry is the softmax-weighted pool
+ * of the block's m rows per channel (logits z + bias), then RMSNorm with
+ * gain and RoPE at the block's first position block_pos0[b]; [P2] section
+ * 3.3 (eqs. 24-26) and [P4] "Tata letak attention mask": the query at t
+ * attends to every entry w < min(n_entries[b], (t + 1) / m), the new one
+ * included, and to its window.
+ *
+ *   c, z        [B, m, D] bf16: the block's rows and logits (z may be NULL:
+ *               logits from the bias alone)
+ *   bias        [m, D] f32 or NULL (zero);  gain [D] f32 or NULL (no RMSNorm)
+ *   block_pos0  [B] int64 device: the closing block's first position, or -1
+ *               when no block closes for sequence b (nothing is pooled or
+ *               stored, and the call is hca_attn)
+ *   pool        [B, N_cap, D] bf16, written at the new entry's row only;
+ *               n_entries[b] counts the entries including the new one
+ *   q [B, 1, H, D], q_pos0 [B] (the query's position), out [B, 1, H, D]:
+ *   bf16; rope_dims applies to the query, the output and the new entry.
+ *   Other arguments as hca_attn (dt = bf16, Tq = 1).
+ *   ws          workspace of hca_decode_attn_ws_bytes(B, H, D, N_cap + W)
+ * The last key-range split of each query computes the entry (its workgroup
+ * pools the rows while the other splits stream the pool) and the others
+ * leave its row out, so no launch waits for the compressor.
+ * CSA_ERR_UNSUPPORTED outside the bf16 MFMA shape (H a multiple of 64 up to
+ * 128, D = 512, even rope_dims) or for m > 1024; CSA_ERR_ARG for m <= 0 or
+ * NULL c, n_entries, block_pos0; otherwise errors as hca_attn.
+ * ------------------------------------------------------------------------- */
+int hca_decode_attn(int B, int H, int D, int rope_dims, double rope_base, float scale,
+                    const void* q, void* pool, int N_cap, const int32_t* n_entries, int m,
+                    const void* c, const void* z, const float* bias, const float* gain,
+                    float eps, const int64_t* block_pos0, const void* win, int L_win,
+                    const int64_t* win_pos0, int W, const float* sink, const int64_t* q_pos0,
+                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace (bytes) for hca_decode_attn with at most keys_per_query rows per
+ * query (N_cap + W); 0 for shapes it does not take. */
+size_t hca_decode_attn_ws_bytes(int B, int H, int D, int keys_per_query);
+
 /* Human-readable name of a csa_status value (static string). */
 const char* csa_status_string(int status);
 

@@ -33,5 +33,7 @@ from .binding import (  # noqa: F401
     csa_output_proj,
     csa_sparse_attn,
     hca_attn,
+    hca_decode_attn,
+    hca_decode_attn_ws_bytes,
     lib,
 )

@@ -594,9 +594,11 @@ int attn_common(AttnArgs& a, double rope_base, int keys_per_query, void* ws, siz
     return CSA_ERR_UNSUPPORTED;
   if (attn_uses_mfma(a.dt, a.H, a.D, a.R)) {
     if (a.csa && (int64_t)keys_per_query > attn_max_csa_keys()) return CSA_ERR_UNSUPPORTED;
-    a.splits = attn_splits(a.dt, a.B, a.Tq, a.H, a.D, keys_per_query);
+    a.splits = a.fresh ? attn_fresh_splits(a.B, a.H, a.D, keys_per_query)
+                       : attn_splits(a.dt, a.B, a.Tq, a.H, a.D, keys_per_query);
     if (a.splits > 1) {
-      const size_t need = attn_ws_bytes(a.dt, a.B, a.Tq, a.H, a.D, keys_per_query);
+      const size_t need = a.fresh ? attn_fresh_ws_bytes(a.B, a.H, a.D, keys_per_query)
+                                  : attn_ws_bytes(a.dt, a.B, a.Tq, a.H, a.D, keys_per_query);
       if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
       a.part_ml = (float*)ws;
       a.part_o = (bf16_t*)(a.part_ml + (size_t)a.B * a.Tq * a.splits * a.H * 2);
@@ -679,5 +681,35 @@ CSA_EXPORT int hca_attn(int dt, int B, int Tq, int H, int D, int rope_dims, doub
   a.n_entries = n_entries; a.m = m;
   a.win = win; a.L_win = L_win; a.win_pos0 = win_pos0; a.W = W;
   a.sink = sink; a.q_pos0 = q_pos0; a.out = out; a.lse = lse;
+  return attn_common(a, rope_base, N_cap + W, ws, ws_bytes, (hipStream_t)stream);
+}
+
+CSA_EXPORT size_t hca_decode_attn_ws_bytes(int B, int H, int D, int keys_per_query) {
+  if (B <= 0 || keys_per_query <= 0 || !attn_uses_mfma(CSA_BF16, H, D, 0)) return 0;
+  return attn_fresh_ws_bytes(B, H, D, keys_per_query);
+}
+
+CSA_EXPORT int hca_decode_attn(int B, int H, int D, int rope_dims, double rope_base, float scale,
+                               const void* q, void* pool, int N_cap, const int32_t* n_entries,
+                               int m, const void* c, const void* z, const float* bias,
+                               const float* gain, float eps, const int64_t* block_pos0,
+                               const void* win, int L_win, const int64_t* win_pos0, int W,
+                               const float* sink, const int64_t* q_pos0, void* out, float* lse,
+                               void* ws, size_t ws_bytes, void* stream) {
+  if (m <= 0 || !n_entries || !block_pos0 || !c) return CSA_ERR_ARG;
+  if (gain && !(eps >= 0.f)) return CSA_ERR_ARG;
+  if (rope_dims < 0 || rope_dims > D || (rope_dims & 1)) return CSA_ERR_ARG;
+  if (!attn_uses_mfma(CSA_BF16, H, D, rope_dims) || m > 1024) return CSA_ERR_UNSUPPORTED;
+  AttnArgs a{};
+  a.dt = CSA_BF16; a.B = B; a.Tq = 1; a.H = H; a.D = D; a.R = rope_dims;
+  a.scale = scale;
+  a.q = q; a.pool = pool; a.N_cap = N_cap; a.csa = 0; a.idx = nullptr; a.K = 0;
+  a.n_entries = n_entries; a.m = m;
+  a.win = win; a.L_win = L_win; a.win_pos0 = win_pos0; a.W = W;
+  a.sink = sink; a.q_pos0 = q_pos0; a.out = out; a.lse = lse;
+  a.fresh = 1;
+  a.fj.dt = CSA_BF16; a.fj.B = B; a.fj.T = m; a.fj.D = D; a.fj.m = m; a.fj.n_out = 1;
+  a.fj.c_a = c; a.fj.z_a = z; a.fj.bias_a = bias; a.fj.gain = gain; a.fj.eps = eps;
+  a.fj.rope_dims = rope_dims; a.fj.pos0 = block_pos0;
   return attn_common(a, rope_base, N_cap + W, ws, ws_bytes, (hipStream_t)stream);
 }

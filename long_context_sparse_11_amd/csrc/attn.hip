@@ -226,6 +226,208 @@ __device__ __forceinline__ float row_swap16(float x) {
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
+// ------------------------------------------- HCA decode step: the new entry
+// Row of the pool that a decode step's closing block fills (the entry count
+// already includes it), or -1 when no block closes for sequence b.
+__device__ __forceinline__ int fresh_entry_row(const AttnArgs& a, int b) {
+  return a.fj.pos0[b] >= 0 ? min(a.n_entries[b], a.N_cap) - 1 : -1;
+}
+
+// The closing block of an HCA decode step, handled by the last split of its
+// query inside the attention launch (hca_decode_attn): the block is pooled
+// beside the other splits' tile loops instead of in launches of its own ahead
+// of them.  "DeepSeek-v4 Beyond Basics" section 3.3 (eqs. 20-23): the entry
+// is the softmax-weighted pool of the block's m rows per channel, then
+// RMSNorm with its gain and RoPE at the block's first position; the same
+// section (eq. 26): it is attended like every other visible entry.
+//
+// Wave w pools rows w, w + NW, ... with an online softmax per channel (lane l
+// holds channels 8l .. 8l + 7; eight rows' loads in flight per wave); the
+// waves' partials merge through LDS and wave 0 finishes the entry:
+// normalises, applies the gain, rotates, rounds to bf16, stores it to the
+// pool (head group 0 only) and leaves it in LDS.  The split's partial is
+// that one row: per head, the logit q'.row (q' the query rotated at tpos and
+// rounded to bf16, as the tile loop uses it) as the running maximum, a sum
+// of 1, and the row with its rope slice rotated back by -tpos as the
+// unnormalised output.  With no closing block, or an entry the query does
+// not see, the partial is empty (maximum -inf, sum 0, zero output); the
+// other splits leave the entry's row out when the query sees it.
+template <int NW>
+__device__ __forceinline__ void hca_fresh_split(const AttnArgs& a, int b, int qi, int sp, int S,
+                                                float* s_f, bf16_t* s_row, bf16_t* s_out,
+                                                float* s_cos, float* s_sin) {
+  const CompressArgs& f = a.fj;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int R = a.R, rope0 = kAtD - R;
+  const int64_t tpos = a.q_pos0[b];  // one query per sequence
+  const int64_t bp = f.pos0[b];
+  const int row = fresh_entry_row(a, b);
+  const bool vis = row >= 0 && row == key_range(a, b, qi, tpos).nsel - 1;
+  for (int p = tid; p < R / 2; p += 64 * NW) rope_cos_sin(tpos, p, a.rope_theta1, s_cos[p], s_sin[p]);
+
+  if (row >= 0) {
+    const int m = f.m, c0 = 8 * lane;
+    const bool hz = f.z_a != nullptr, hb = f.bias_a != nullptr;
+    const bf16_t* cbase = (const bf16_t*)f.c_a + (int64_t)b * m * kAtD + c0;
+    const bf16_t* zbase = hz ? (const bf16_t*)f.z_a + (int64_t)b * m * kAtD + c0 : cbase;
+    float mx[8], den[8], acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { mx[e] = -INFINITY; den[e] = 0.f; acc[e] = 0.f; }
+    // the optional streams' words start at zero once (a skipped load leaves
+    // them defined), and every load of a batch goes out before any arithmetic
+    u32x4_t cw[8], zw[8], bw[8][2];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      zw[u] = u32x4_t{0u, 0u, 0u, 0u};
+      bw[u][0] = bw[u][1] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    for (int r0 = wave; r0 < m; r0 += 8 * NW) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = r0 + u * NW;
+        const int64_t ro = (int64_t)(r < m ? r : r0) * kAtD;
+        Elem<bf16_t>::template load_raw_stream<8>(cbase + ro, &cw[u]);
+        if (hz) Elem<bf16_t>::template load_raw_stream<8>(zbase + ro, &zw[u]);
+        if (hb) Elem<float>::template load_raw<8>(f.bias_a + ro + c0, bw[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (r0 + u * NW >= m) break;
+        float cv[8], zv[8], bv[8];
+        Elem<bf16_t>::template from_raw<8>(&cw[u], cv);
+        Elem<bf16_t>::template from_raw<8>(&zw[u], zv);
+        Elem<float>::template from_raw<8>(bw[u], bv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float l = (zv[e] + bv[e]) * kLog2e;  // base 2; absent streams read 0
+          const float nm = fmaxf(mx[e], l);
+          const float sc = exp2_weight(mx[e] - nm);
+          const float p = exp2_weight(l - nm);
+          den[e] = den[e] * sc + p;
+          acc[e] = acc[e] * sc + p * cv[e];
+          mx[e] = nm;
+        }
+      }
+    }
+    float* mine = s_f + wave * 3 * kAtD;  // [NW][3][512]: max, sum, weighted sum
+#pragma unroll
+    for (int e = 0; e < 8; e += 4) {
+      *reinterpret_cast<f32x4_t*>(mine + c0 + e) = f32x4_t{mx[e], mx[e + 1], mx[e + 2], mx[e + 3]};
+      *reinterpret_cast<f32x4_t*>(mine + kAtD + c0 + e) =
+          f32x4_t{den[e], den[e + 1], den[e + 2], den[e + 3]};
+      *reinterpret_cast<f32x4_t*>(mine + 2 * kAtD + c0 + e) =
+          f32x4_t{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+    }
+    __syncthreads();
+    if (wave == 0) {
+      for (int w = 1; w < NW; ++w) {
+        const float* o = s_f + w * 3 * kAtD;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float om = o[c0 + e];
+          const float M = fmaxf(mx[e], om);
+          const float w0 = mx[e] == -INFINITY ? 0.f : exp2_weight(mx[e] - M);
+          const float w1 = om == -INFINITY ? 0.f : exp2_weight(om - M);
+          den[e] = den[e] * w0 + o[kAtD + c0 + e] * w1;
+          acc[e] = acc[e] * w0 + o[2 * kAtD + c0 + e] * w1;
+          mx[e] = M;
+        }
+      }
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = acc[e] / den[e];
+      if (f.gain) {
+        float gv[8];
+        Elem<float>::template load<8>(f.gain + c0, gv);
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += y[e] * y[e];
+        ss = wave_sum(ss);
+        const float inv = 1.0f / sqrtf(ss / (float)kAtD + f.eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = y[e] * inv * gv[e];
+      }
+      u32x4_t ent, outw;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c = c0 + 2 * k;
+        float x0 = y[2 * k], x1 = y[2 * k + 1];
+        if (c >= rope0) {  // the entry's rotation, at the block's first position
+          float cs, sn;
+          rope_cos_sin(bp, (c - rope0) >> 1, a.rope_theta1, cs, sn);
+          const float r0v = x0 * cs - x1 * sn, r1v = x0 * sn + x1 * cs;
+          x0 = r0v;
+          x1 = r1v;
+        }
+        ent[k] = pack_bf16x2(x0, x1);
+        // the stored (bf16) values, rotated back by -tpos for the output
+        float o0 = __uint_as_float(ent[k] << 16), o1 = __uint_as_float(ent[k] & 0xffff0000u);
+        if (c >= rope0) {
+          const int pj = (c - rope0) >> 1;
+          const float cs = s_cos[pj], sn = s_sin[pj];
+          const float t0 = o0 * cs + o1 * sn, t1 = -o0 * sn + o1 * cs;
+          o0 = t0;
+          o1 = t1;
+        }
+        outw[k] = pack_bf16x2(o0, o1);
+      }
+      if (blockIdx.z == 0)
+        *reinterpret_cast<u32x4_t*>((bf16_t*)a.pool + ((int64_t)b * a.N_cap + row) * kAtD + c0) = ent;
+      *reinterpret_cast<u32x4_t*>(s_row + c0) = ent;
+      *reinterpret_cast<u32x4_t*>(s_out + c0) = outw;
+    }
+  }
+  __syncthreads();
+
+  // per head: thread (head hl, channel quarter qt)
+  const int hl = tid >> 2, qt = tid & 3;
+  const int h = 16 * NW * (int)blockIdx.z + hl;
+  const int64_t slot = ((int64_t)qi * S + sp) * a.H + h;
+  u32x4_t* po = reinterpret_cast<u32x4_t*>(a.part_o + slot * kAtD + 128 * qt);
+  if (!vis) {
+    if (qt == 0) {
+      a.part_ml[2 * slot] = -INFINITY;
+      a.part_ml[2 * slot + 1] = 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) po[k] = u32x4_t{0u, 0u, 0u, 0u};
+    return;
+  }
+  const u32x4_t* qp =
+      reinterpret_cast<const u32x4_t*>((const bf16_t*)a.q + ((int64_t)qi * a.H + h) * kAtD + 128 * qt);
+  u32x4_t qw[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) qw[k] = qp[k];
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int c8 = 128 * qt + 8 * k;
+    const u32x4_t rw = *reinterpret_cast<const u32x4_t*>(s_row + c8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = c8 + 2 * j;
+      uint32_t qj = qw[k][j];
+      if (c >= rope0) {
+        const int pj = (c - rope0) >> 1;
+        const float cs = s_cos[pj], sn = s_sin[pj];
+        const float x0 = __uint_as_float(qj << 16), x1 = __uint_as_float(qj & 0xffff0000u);
+        qj = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+      }
+      s += __uint_as_float(qj << 16) * __uint_as_float(rw[j] << 16) +
+           __uint_as_float(qj & 0xffff0000u) * __uint_as_float(rw[j] & 0xffff0000u);
+    }
+  }
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  if (qt == 0) {
+    a.part_ml[2 * slot] = s * a.scale * kLog2e;
+    a.part_ml[2 * slot + 1] = 1.f;
+  }
+  const u32x4_t* so = reinterpret_cast<const u32x4_t*>(s_out + 128 * qt);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) po[k] = so[k];
+}
+
 // NW: waves per workgroup, 16 heads each.  With NW = 4 the workgroup takes
 // all 64 heads and four waves share each copied tile; with NW = 2 (single-
 // tile splits of few queries, i.e. decode) it takes 32 heads and blockIdx.z
@@ -273,6 +475,16 @@ void attn_hs(AttnArgs a) {
   const int b = qi / a.Tq, t = qi - b * a.Tq;
   const int R = a.R;
   const int rope0 = kAtD - R;
+  // HCA decode step: the last split pools the closing block's entry; the
+  // others divide the key list among themselves
+  if constexpr (!CSA && !FP8) {
+    if (a.fresh && sp == S - 1) {
+      hca_fresh_split<NW>(a, b, qi, sp, S, reinterpret_cast<float*>(s_rows0), s_rows1,
+                          s_rows1 + kAtD, s_cos, s_sin);
+      return;
+    }
+  }
+  const int Sa = S - a.fresh;
 
   // ---- split bounds (CSA: a fixed range of [K selected, up to
   // min(W, L_win) window rows], known before the position)
@@ -280,7 +492,7 @@ void attn_hs(AttnArgs a) {
   if (CSA) {
     const int wc = (a.W > 0 && a.L_win > 0) ? min(a.W, a.L_win) : 0;
     const int Lmax = a.K + wc;
-    const int per = (((Lmax + S - 1) / S) + kHsRows - 1) / kHsRows * kHsRows;
+    const int per = (((Lmax + Sa - 1) / Sa) + kHsRows - 1) / kHsRows * kHsRows;
     start = min(Lmax, sp * per);
     end = min(Lmax, start + per);
   }
@@ -298,10 +510,17 @@ void attn_hs(AttnArgs a) {
   for (int ks = 0; ks < 16; ++ks) qb[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * ks + 8 * G);
 
   const int64_t tpos = a.q_pos0[b] + t;
-  const KeyRange kr = key_range(a, b, qi, tpos);
+  KeyRange kr = key_range(a, b, qi, tpos);
+  if constexpr (!CSA && !FP8) {
+    // the closing block's entry, when the query sees it, is the last split's
+    if (a.fresh) {
+      const int row = fresh_entry_row(a, b);
+      if (row >= 0 && row == kr.nsel - 1) kr.nsel -= 1;
+    }
+  }
   if (!CSA) {
     const int L = kr.nsel + kr.nwin;
-    const int per = (((L + S - 1) / S) + kHsRows - 1) / kHsRows * kHsRows;
+    const int per = (((L + Sa - 1) / Sa) + kHsRows - 1) / kHsRows * kHsRows;
     start = min(L, sp * per);
     end = min(L, start + per);
   }
@@ -776,6 +995,20 @@ size_t attn_ws_bytes(int dt, int B, int Tq, int H, int D, int keys_per_query) {
   return (size_t)B * Tq * s * H * (2 * sizeof(float) + (size_t)D * sizeof(bf16_t));
 }
 
+// HCA decode step with the closing block's entry (bf16, the Flash shape,
+// one query per sequence): as many splits as hca_attn takes, the last one
+// given to the entry, so the grid keeps its one workgroup per compute unit.
+// (One split more per query, 272 workgroups at batch 16, put two on some
+// compute units: the 1M-token step took 59 us against 48.)
+int attn_fresh_splits(int B, int H, int D, int keys_per_query) {
+  return max(2, attn_splits(1, B, 1, H, D, keys_per_query));
+}
+
+size_t attn_fresh_ws_bytes(int B, int H, int D, int keys_per_query) {
+  const int s = attn_fresh_splits(B, H, D, keys_per_query);
+  return (size_t)B * s * H * (2 * sizeof(float) + (size_t)D * sizeof(bf16_t));
+}
+
 template <typename T>
 static hipError_t launch_generic(const AttnArgs& a, hipStream_t stream) {
   dim3 grid((a.H + 3) / 4, a.B * a.Tq), block(256);
@@ -810,7 +1043,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
     // most rows a split can hold: the list length bound over the split count
     const int wc = (a.W > 0 && a.L_win > 0) ? min(a.W, a.L_win) : 0;
     const int64_t lmax = (a.csa ? (int64_t)a.K : (int64_t)a.N_cap) + wc;
-    const bool multi = (lmax + a.splits - 1) / a.splits > kHsRows;
+    const int sa = a.splits - a.fresh;  // splits over the key list
+    const bool multi = (lmax + sa - 1) / sa > kHsRows;
     // single-tile splits in head groups of 32 (two waves, grid z) while the
     // doubled grid still fits the compute units once
     const bool halves = !multi && 2LL * hg * a.splits * a.B * a.Tq <= kHsHeadSplitBelow;

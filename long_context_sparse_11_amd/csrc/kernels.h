@@ -196,12 +196,21 @@ struct AttnArgs {
   int splits;           // key-range splits per query (1 = no combine pass)
   float* part_ml;       // [B*Tq, splits, H, 2] when splits > 1: (max, sum)
   bf16_t* part_o;       // [B*Tq, splits, H, D] unnormalised split outputs
+  // HCA decode step (hca_decode_attn; Tq = 1, bf16, the MFMA shape): the
+  // last split of each query is the closing block's new entry, pooled by
+  // that split's workgroup from job fj (T = m, one entry per sequence, to
+  // row min(n_entries[b], N_cap) - 1 when fj.pos0[b] >= 0) and counted as a
+  // split of one row; the other splits leave that row out
+  int fresh;
+  CompressArgs fj;
 };
 bool attn_uses_mfma(int dt, int H, int D, int R);
 int attn_splits(int dt, int B, int Tq, int H, int D, int keys_per_query);
 // most selected + window rows per query the MFMA path takes (CSA)
 int64_t attn_max_csa_keys();
 size_t attn_ws_bytes(int dt, int B, int Tq, int H, int D, int keys_per_query);
+int attn_fresh_splits(int B, int H, int D, int keys_per_query);
+size_t attn_fresh_ws_bytes(int B, int H, int D, int keys_per_query);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace csa

@@ -688,6 +688,120 @@ def test_attn_hca_bf16(N, n_ent, Tq, W):
     assert np.abs(host(lse) - rl).max() <= LSE_ATOL_BF16
 
 
+# ----------------------------------------------- HCA decode step in one call
+def _hca_step_case(kinds, H, N, W, m, seed, with_z=True, with_gain=True):
+    """Per-sequence decode situations: 'close' (a block closes and the query
+    sees its entry), 'open' (no block closes), 'clamp' (the entry count is
+    past N_cap: the entry goes to row N_cap - 1), 'first' (the first block),
+    'unseen' (a block closes after the query's position, so the query does
+    not see it), 'empty' (no entries yet)."""
+    rng = np.random.default_rng(seed)
+    B, D, R = len(kinds), 512, 64
+    n_ent, bp, qp = [], [], []
+    for b, k in enumerate(kinds):
+        n = {"close": N - b, "open": N - 2, "clamp": N + 3, "first": 1, "unseen": N - 4,
+             "empty": 0}[k]
+        tpos = {"open": n * m + 17, "unseen": (n - 1) * m + 5, "empty": 50}.get(k, n * m - 1)
+        n_ent.append(n)
+        bp.append((n - 1) * m if k in ("close", "clamp", "first", "unseen") else -1)
+        qp.append(tpos)
+    n_ent, bp, qp = (np.array(x, dt) for x, dt in ((n_ent, np.int32), (bp, np.int64), (qp, np.int64)))
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)
+    d = dict(B=B, H=H, D=D, R=R, m=m, W=W, N=N, n_ent=n_ent, block_pos0=bp, q_pos0=qp,
+             win_pos0=qp - W + 1)
+    for name, shape in (("q", (B, 1, H, D)), ("pool", (B, N, D)), ("win", (B, W, D)),
+                        ("c", (B, m, D)), ("z", (B, m, D))):
+        d[name] = synth.Tensor(f(*shape), "bf16")
+    if not with_z:
+        d["z"] = None
+    d["bias"] = 0.02 * f(m, D)
+    d["gain"] = (1.0 + 0.02 * f(D)).astype(np.float32) if with_gain else None
+    d["sink"] = 0.5 * f(H)
+    # the oracle: the entry from the compressor, then attention over the pool
+    ref_pool = d["pool"].f32.astype(np.float64)
+    rows = {}
+    for b in range(B):
+        row = min(int(n_ent[b]), N) - 1
+        if bp[b] >= 0 and row >= 0:
+            ent = O.csa_compress(d["c"].f32[b:b + 1], None if d["z"] is None else d["z"].f32[b:b + 1],
+                                 d["bias"], m, gain=d["gain"], rope_dims=R, pos0=[bp[b]])[0, 0]
+            ref_pool[b, row] = ent
+            rows[b] = (row, ent)
+    d["rows"] = rows
+    d["ref"] = O.hca_attn(d["q"].f32, ref_pool, n_ent, m, d["win"].f32, d["win_pos0"], W,
+                          d["sink"], qp, 1 / math.sqrt(D), R)
+    return d
+
+
+def _run_hca_step(d, pool):
+    return L.hca_decode_attn(dev(d["q"]), pool, i32(d["n_ent"]), d["m"], dev(d["c"]),
+                             None if d["z"] is None else dev(d["z"]), dev(d["bias"]),
+                             None if d["gain"] is None else dev(d["gain"]), i64(d["block_pos0"]),
+                             dev(d["win"]), i64(d["win_pos0"]), d["W"], dev(d["sink"]),
+                             i64(d["q_pos0"]), rope_dims=d["R"], want_lse=True)
+
+
+ALL_KINDS = ["close", "open", "clamp", "first", "unseen", "empty"]
+
+
+@pytest.mark.parametrize("H,N,W,m,kinds,with_z,with_gain", [
+    (64, 300, 128, 128, ALL_KINDS, True, True),
+    (64, 3000, 128, 128, ["close", "clamp", "open", "close", "unseen", "close", "first",
+                          "close"], True, True),        # long splits
+    (128, 500, 128, 128, ["close", "open"], True, True),    # two 64-head groups
+    (128, 3000, 128, 128, ["close", "clamp"], True, True),
+    (64, 700, 16, 200, ["close", "unseen", "open"], False, False),  # m not a power of two
+    (64, 90, 128, 16, ["close", "first", "empty"], True, True),     # short blocks
+    # at most 32 keys: one single-tile split beside the entry's (32-head groups)
+    (64, 12, 16, 16, ["close", "first", "empty", "open"], True, True),
+    (128, 12, 16, 16, ["close", "clamp"], True, True),
+])
+def test_hca_decode_step_fused(H, N, W, m, kinds, with_z, with_gain):
+    """hca_decode_attn: the closing block's entry (compressor, stored into the
+    pool) and the attention over every visible entry + window in one call,
+    against the oracle's compressor followed by its HCA attention."""
+    d = _hca_step_case(kinds, H, N, W, m, seed=N + H + m, with_z=with_z, with_gain=with_gain)
+    pool = dev(d["pool"])
+    before = host(pool)
+    out, lse = _run_hca_step(d, pool)
+    ro, rl = d["ref"]
+    assert rowwise_rel_err(host(out), ro) <= TOL_BF16
+    assert np.abs(host(lse) - rl).max() <= LSE_ATOL_BF16
+    after = host(pool)
+    for b in range(d["B"]):
+        if b in d["rows"]:
+            row, ent = d["rows"][b]
+            assert rowwise_rel_err(after[b, row:row + 1], ent[None]) <= TOL_BF16
+            keep = np.ones(d["N"], bool)
+            keep[row] = False
+            assert np.array_equal(after[b, keep], before[b, keep])
+        else:
+            assert np.array_equal(after[b], before[b])
+
+
+@pytest.mark.parametrize("H,N", [(64, 3000), (64, 300)])
+def test_hca_decode_step_matches_separate_calls(H, N):
+    """The fused step against csa_compress (the entry written into the pool)
+    followed by hca_attn on the same inputs: the stored entries and the
+    outputs agree to the rounding of the entry's last bf16 bit."""
+    kinds = ["close", "close", "open", "clamp"]
+    d = _hca_step_case(kinds, H, N, 128, 128, seed=7 + N)
+    pool_f = dev(d["pool"])
+    out_f, lse_f = _run_hca_step(d, pool_f)
+    pool_s = dev(d["pool"])
+    bp = d["block_pos0"]
+    ents = L.csa_compress(dev(d["c"]), d["m"], z_a=dev(d["z"]), bias_a=dev(d["bias"]),
+                          gain=dev(d["gain"]), rope_dims=d["R"], pos0=i64(np.maximum(bp, 0)))
+    for b, (row, _) in d["rows"].items():
+        pool_s[b, row] = ents[b, 0]
+    out_s, lse_s = L.hca_attn(dev(d["q"]), pool_s, i32(d["n_ent"]), d["m"], dev(d["win"]),
+                              i64(d["win_pos0"]), d["W"], dev(d["sink"]), i64(d["q_pos0"]),
+                              rope_dims=d["R"], want_lse=True)
+    assert rowwise_rel_err(host(pool_f), host(pool_s).astype(np.float64)) <= 1e-2
+    assert rowwise_rel_err(host(out_f), host(out_s).astype(np.float64)) <= 1e-2
+    assert np.abs(host(lse_f) - host(lse_s)).max() <= 1e-2
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_attn_empty_key_set_is_sink_only(dt):
     """No selected rows and no window: output 0, lse = sink."""

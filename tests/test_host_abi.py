@@ -35,7 +35,8 @@ def test_header_declares_the_four_calls():
               "csa_compress_ws_bytes", "csa_index_topk_ws_bytes", "csa_attn_ws_bytes",
               "csa_status_string", "csa_quantize_mxfp4", "csa_index_topk_mxfp4",
               "csa_index_scores_mxfp4", "csa_decode_index_topk_mxfp4", "csa_output_proj",
-              "csa_window_row", "csa_decode_advance"):
+              "csa_window_row", "csa_decode_advance", "hca_decode_attn",
+              "hca_decode_attn_ws_bytes"):
         assert n in names
 
 
@@ -312,6 +313,35 @@ def test_attn_validation(lib):
     assert _attn(lib, "hca_attn", m=0) == CSA_ERR_ARG
     assert _attn(lib, "hca_attn", n_ent=N) == CSA_ERR_ARG
     assert _attn(lib, "hca_attn", wsb=1) == CSA_ERR_WORKSPACE
+
+
+def _hca_step(lib, **kw):
+    a = dict(B=16, H=64, D=512, R=64, base=10000.0, scale=0.044, N=8192, n_ent=P, m=128, c=P,
+             gain=N, eps=1e-6, bp=P, L_win=128, W=128, ws=P, wsb=1 << 40)
+    a.update(kw)
+    return lib.hca_decode_attn(a["B"], a["H"], a["D"], a["R"], a["base"], a["scale"], P, P,
+                               a["N"], a["n_ent"], a["m"], a["c"], P, N, a["gain"], a["eps"],
+                               a["bp"], P, a["L_win"], P, a["W"], P, P, P, N, a["ws"], a["wsb"],
+                               N)
+
+
+def test_hca_decode_step_validation(lib):
+    assert _hca_step(lib, m=0) == CSA_ERR_ARG
+    assert _hca_step(lib, c=N) == CSA_ERR_ARG
+    assert _hca_step(lib, n_ent=N) == CSA_ERR_ARG
+    assert _hca_step(lib, bp=N) == CSA_ERR_ARG
+    assert _hca_step(lib, gain=P, eps=-1.0) == CSA_ERR_ARG
+    assert _hca_step(lib, R=63) == CSA_ERR_ARG
+    assert _hca_step(lib, H=32) == CSA_ERR_UNSUPPORTED     # the MFMA shape only
+    assert _hca_step(lib, D=256) == CSA_ERR_UNSUPPORTED
+    assert _hca_step(lib, m=2048) == CSA_ERR_UNSUPPORTED
+    assert _hca_step(lib, ws=N) == CSA_ERR_WORKSPACE
+    assert _hca_step(lib, B=0) == CSA_OK
+    # hca_attn's splits (one of them the new entry's), at least two
+    s_attn = lib.csa_attn_ws_bytes(16, 1, 64, 512, 8192 + 128)
+    assert lib.hca_decode_attn_ws_bytes(16, 64, 512, 8192 + 128) == s_attn > 0
+    assert lib.hca_decode_attn_ws_bytes(1, 64, 512, 10) == 2 * 64 * (8 + 2 * 512)
+    assert lib.hca_decode_attn_ws_bytes(1, 32, 512, 10) == 0
 
 
 def test_kv_fp8_validation(lib):
