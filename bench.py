@@ -137,8 +137,7 @@ class Step:
         elif kind in HCA:
             N, W = g["N"], g["W"]
             self.out = torch.empty_like(g["q"])
-            n = (L.hca_decode_attn_ws_bytes(B, g["H"], D, N + W) if kind == "hca1m"
-                 else L.csa_attn_ws_bytes(B, 1, g["H"], D, N + W))
+            n = L.hca_decode_attn_ws_bytes(B, g["H"], D, N + W)
             self.ws_a = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
         else:  # prefill
             Tq, N, K, W = g["Tq"], g["N"], g["K"], g["W"]
@@ -285,25 +284,14 @@ class Step:
                                                           g["q_pos0"], rope_dims=g["R"],
                                                           out=self.out, ws=self.ws_a)),
             ]
-        if kind == "hca1m_fp8":
-            N, m, rb = g["N"], g["m"], g["pool"].shape[2]
-            pool = g["pool"]
-            return [
-                ("compress", lambda: L.csa_compress_kvfp8(
-                    g["c_a"], m, z_a=g["z_a"], bias_a=g["bias_a"], gain=g["gain"],
-                    rope_dims=g["R"], pos0=g["block_pos0"], out=pool[:, N - 1:],
-                    out_bstride=N * rb, ws=self.cws(g["c_a"], m, False))),
-                ("hca_attn", lambda: L.hca_attn_kvfp8(g["q"], pool, g["n_entries"], m, g["win"],
-                                                      g["win_pos0"], g["W"], g["sink"],
-                                                      g["q_pos0"], rope_dims=g["R"],
-                                                      out=self.out, ws=self.ws_a)),
-            ]
-        if kind == "hca1m":
+        if kind in HCA:
             # one call: the closing block's entry (pooled by the attention
-            # launch's last split, stored to row N - 1) and the attention
+            # launch's last split, stored to row N - 1: bf16, or a packed
+            # BF16 / FP8 row) and the attention
             m, pool = g["m"], g["pool"]
+            fn = L.hca_decode_attn_kvfp8 if kind == "hca1m_fp8" else L.hca_decode_attn
             return [
-                ("hca_step", lambda: L.hca_decode_attn(
+                ("hca_step", lambda: fn(
                     g["q"], pool, g["n_entries"], m, g["c_a"], g["z_a"], g["bias_a"], g["gain"],
                     g["block_pos0"], g["win"], g["win_pos0"], g["W"], g["sink"], g["q_pos0"],
                     rope_dims=g["R"], out=self.out, ws=self.ws_a)),
@@ -425,14 +413,10 @@ def algorithmic(kind, d):
         rows = N + W
         attn = B * (N * vb + W * D * bf + 2 * H * D * bf)
         fl = B * 4 * H * D * rows
-        if kind == "hca1m":  # one call does both
-            out["bytes"] = {"hca_step": comp + attn}
-            out["flops"] = {"hca_step": fl}
-            out["hca_step"] = {"bytes": comp + attn, "flops": fl}
-        else:
-            out["bytes"] = {"compress": comp, "hca_attn": attn}
-            out["flops"] = {"hca_attn": fl}
-            out["hca_attn"] = {"bytes": attn, "flops": fl}
+        # one call does both
+        out["bytes"] = {"hca_step": comp + attn}
+        out["flops"] = {"hca_step": fl}
+        out["hca_step"] = {"bytes": comp + attn, "flops": fl}
     else:
         N, P = d["N"], d["prefix"]
         T = Tq + m
@@ -472,7 +456,6 @@ DOMINANT_KERNELS = {
     "index_decode_fresh": ["index_decode<true, *> (closing-block compressors + scoring, "
                            "the step's first launch)"],
     "index_scores": ["index_prefill"],
-    "hca_attn": ["attn_hs<false, true, 4>", "attn_combine<bf16>"],
     "hca_step": ["attn_hs<false, true, 4> (its last split pools the closing block)",
                  "attn_combine<bf16>"],
     "sparse_attn": ["attn_hs<true, *> (+ attn_combine<bf16> when split)"],
@@ -483,7 +466,6 @@ DOMINANT_KERNELS = {
 KERNEL_SOURCES = {
     "index_decode_fresh": ["indexer.hip", "common.h", "kernels.h"],
     "index_scores": ["indexer.hip", "common.h", "kernels.h"],
-    "hca_attn": ["attn.hip", "common.h", "kernels.h"],
     "hca_step": ["attn.hip", "common.h", "kernels.h"],
     "sparse_attn": ["attn.hip", "common.h", "kernels.h"],
     "output_proj": ["oproj.hip", "oproj.h", "common.h", "kernels.h"],

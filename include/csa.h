@@ -591,8 +591,24 @@ int hca_decode_attn(int B, int H, int D, int rope_dims, double rope_base, float 
                     const int64_t* win_pos0, int W, const float* sink, const int64_t* q_pos0,
                     void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace (bytes) for hca_decode_attn with at most keys_per_query rows per
- * query (N_cap + W); 0 for shapes it does not take. */
+/* hca_decode_attn_kvfp8 - hca_decode_attn over a pool of packed mixed
+ * BF16 / FP8 rows (see csa_kv_fp8_row_bytes): pool [B, N_cap, row_bytes]
+ * uint8.  The new entry is stored as a packed row (as csa_compress_kvfp8
+ * stores it) and attended as the values read back from that row, so the
+ * result is that of csa_compress_kvfp8 followed by hca_attn_kvfp8 with
+ * Tq = 1, up to rounding order.  Other arguments, workspace and errors as
+ * hca_decode_attn; CSA_ERR_UNSUPPORTED also for rope_dims not a multiple of
+ * 32. */
+int hca_decode_attn_kvfp8(int B, int H, int D, int rope_dims, double rope_base, float scale,
+                          const void* q, void* pool, int N_cap, const int32_t* n_entries, int m,
+                          const void* c, const void* z, const float* bias, const float* gain,
+                          float eps, const int64_t* block_pos0, const void* win, int L_win,
+                          const int64_t* win_pos0, int W, const float* sink,
+                          const int64_t* q_pos0, void* out, float* lse, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Workspace (bytes) for hca_decode_attn(_kvfp8) with at most keys_per_query
+ * rows per query (N_cap + W); 0 for shapes it does not take. */
 size_t hca_decode_attn_ws_bytes(int B, int H, int D, int keys_per_query);
 
 /* Human-readable name of a csa_status value (static string). */

@@ -34,6 +34,7 @@ from .binding import (  # noqa: F401
     csa_sparse_attn,
     hca_attn,
     hca_decode_attn,
+    hca_decode_attn_kvfp8,
     hca_decode_attn_ws_bytes,
     lib,
 )

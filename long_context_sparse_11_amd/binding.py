@@ -105,6 +105,13 @@ _SIGS = {
                                    _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_void_p,
                                    _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_size_t,
                                    _c.c_void_p]),
+    "hca_decode_attn_kvfp8": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_double,
+                                   _c.c_float, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p,
+                                   _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                   _c.c_void_p, _c.c_float, _c.c_void_p, _c.c_void_p, _c.c_int,
+                                   _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_void_p,
+                                   _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_size_t,
+                                   _c.c_void_p]),
     "hca_decode_attn_ws_bytes": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int, _c.c_int]),
     "csa_status_string": (_c.c_char_p, [_c.c_int]),
 }
@@ -683,7 +690,7 @@ def hca_decode_attn_ws_bytes(B, H, D, keys_per_query):
 
 def hca_decode_attn(q, pool, n_entries, m, c, z, bias, gain, block_pos0, win, win_pos0, W, sink,
                     q_pos0, *, rope_dims, rope_base=10000.0, eps=1e-6, scale=None,
-                    want_lse=False, out=None, ws=None, stream=None):
+                    want_lse=False, out=None, ws=None, stream=None, _fn="hca_decode_attn"):
     """One HCA decode step (see include/csa.h): the closing block c, z [B, m, D]
     is pooled into pool row min(n_entries, N_cap) - 1 where block_pos0 >= 0,
     and the query q [B, 1, H, D] attends to every visible entry + window.
@@ -691,13 +698,17 @@ def hca_decode_attn(q, pool, n_entries, m, c, z, bias, gain, block_pos0, win, wi
     B, Tq, H, D = q.shape
     if Tq != 1:
         raise ValueError("hca_decode_attn takes one query per sequence")
+    if _fn == "hca_decode_attn_kvfp8":
+        _fp8_pool(pool, D, rope_dims)
+    elif pool.dtype != torch.bfloat16:
+        raise TypeError("pool is bf16")
     N_cap = pool.shape[1]
     L_win = 0 if win is None else win.shape[1]
     _dev(q, pool, n_entries, c, z, bias, gain, block_pos0, win, win_pos0, sink, q_pos0)
     _f32(sink), _f32(bias), _f32(gain), _i64(q_pos0), _i64(win_pos0), _i64(block_pos0)
-    for t in (q, pool, c, z):
+    for t in (q, c, z):
         if t is not None and t.dtype != torch.bfloat16:
-            raise TypeError("q, pool, c and z are bf16")
+            raise TypeError("q, c and z are bf16")
     if tuple(c.shape) != (B, m, D) or (z is not None and tuple(z.shape) != (B, m, D)):
         raise ValueError("c and z must be [B, m, D]")
     scale = 1.0 / math.sqrt(D) if scale is None else scale
@@ -707,13 +718,22 @@ def hca_decode_attn(q, pool, n_entries, m, c, z, bias, gain, block_pos0, win, wi
     need = hca_decode_attn_ws_bytes(B, H, D, N_cap + W)
     if ws is None and need:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-    st = lib().hca_decode_attn(B, H, D, int(rope_dims), float(rope_base), float(scale), _p(q),
-                               _p(pool), N_cap, _p(n_entries), int(m), _p(c), _p(z), _p(bias),
-                               _p(gain), float(eps), _p(block_pos0), _p(win), L_win,
-                               _p(win_pos0), int(W), _p(sink), _p(q_pos0), _p(out), _p(lse),
-                               _p(ws), 0 if ws is None else ws.numel(), _stream(stream))
-    _check(st, "hca_decode_attn")
+    st = getattr(lib(), _fn)(B, H, D, int(rope_dims), float(rope_base), float(scale), _p(q),
+                             _p(pool), N_cap, _p(n_entries), int(m), _p(c), _p(z), _p(bias),
+                             _p(gain), float(eps), _p(block_pos0), _p(win), L_win,
+                             _p(win_pos0), int(W), _p(sink), _p(q_pos0), _p(out), _p(lse),
+                             _p(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _check(st, _fn)
     return out, lse
+
+
+def hca_decode_attn_kvfp8(q, pool, n_entries, m, c, z, bias, gain, block_pos0, win, win_pos0, W,
+                          sink, q_pos0, **kw):
+    """hca_decode_attn with the pool as packed mixed BF16 / FP8 rows (uint8
+    [B, N_cap, row_bytes]): the new entry is stored packed and attended as
+    the values read back from its row."""
+    return hca_decode_attn(q, pool, n_entries, m, c, z, bias, gain, block_pos0, win, win_pos0, W,
+                           sink, q_pos0, _fn="hca_decode_attn_kvfp8", **kw)
 
 
 # ------------------------------------------------- mixed BF16 / FP8 KV rows

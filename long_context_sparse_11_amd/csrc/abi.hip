@@ -689,17 +689,20 @@ CSA_EXPORT size_t hca_decode_attn_ws_bytes(int B, int H, int D, int keys_per_que
   return attn_fresh_ws_bytes(B, H, D, keys_per_query);
 }
 
-CSA_EXPORT int hca_decode_attn(int B, int H, int D, int rope_dims, double rope_base, float scale,
-                               const void* q, void* pool, int N_cap, const int32_t* n_entries,
-                               int m, const void* c, const void* z, const float* bias,
-                               const float* gain, float eps, const int64_t* block_pos0,
-                               const void* win, int L_win, const int64_t* win_pos0, int W,
-                               const float* sink, const int64_t* q_pos0, void* out, float* lse,
-                               void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+int hca_decode_common(int B, int H, int D, int rope_dims, double rope_base, float scale,
+                      const void* q, void* pool, int N_cap, const int32_t* n_entries, int m,
+                      const void* c, const void* z, const float* bias, const float* gain,
+                      float eps, const int64_t* block_pos0, const void* win, int L_win,
+                      const int64_t* win_pos0, int W, const float* sink, const int64_t* q_pos0,
+                      void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream,
+                      bool fp8) {
   if (m <= 0 || !n_entries || !block_pos0 || !c) return CSA_ERR_ARG;
   if (gain && !(eps >= 0.f)) return CSA_ERR_ARG;
   if (rope_dims < 0 || rope_dims > D || (rope_dims & 1)) return CSA_ERR_ARG;
   if (!attn_uses_mfma(CSA_BF16, H, D, rope_dims) || m > 1024) return CSA_ERR_UNSUPPORTED;
+  if (fp8 && !kv_fp8_shape_ok(D, rope_dims)) return CSA_ERR_UNSUPPORTED;
   AttnArgs a{};
   a.dt = CSA_BF16; a.B = B; a.Tq = 1; a.H = H; a.D = D; a.R = rope_dims;
   a.scale = scale;
@@ -707,9 +710,37 @@ CSA_EXPORT int hca_decode_attn(int B, int H, int D, int rope_dims, double rope_b
   a.n_entries = n_entries; a.m = m;
   a.win = win; a.L_win = L_win; a.win_pos0 = win_pos0; a.W = W;
   a.sink = sink; a.q_pos0 = q_pos0; a.out = out; a.lse = lse;
+  if (fp8) a.pool_row_bytes = kv_fp8_row_bytes_host(D, rope_dims);
   a.fresh = 1;
   a.fj.dt = CSA_BF16; a.fj.B = B; a.fj.T = m; a.fj.D = D; a.fj.m = m; a.fj.n_out = 1;
   a.fj.c_a = c; a.fj.z_a = z; a.fj.bias_a = bias; a.fj.gain = gain; a.fj.eps = eps;
   a.fj.rope_dims = rope_dims; a.fj.pos0 = block_pos0;
-  return attn_common(a, rope_base, N_cap + W, ws, ws_bytes, (hipStream_t)stream);
+  return attn_common(a, rope_base, N_cap + W, ws, ws_bytes, stream);
+}
+
+}  // namespace
+
+CSA_EXPORT int hca_decode_attn(int B, int H, int D, int rope_dims, double rope_base, float scale,
+                               const void* q, void* pool, int N_cap, const int32_t* n_entries,
+                               int m, const void* c, const void* z, const float* bias,
+                               const float* gain, float eps, const int64_t* block_pos0,
+                               const void* win, int L_win, const int64_t* win_pos0, int W,
+                               const float* sink, const int64_t* q_pos0, void* out, float* lse,
+                               void* ws, size_t ws_bytes, void* stream) {
+  return hca_decode_common(B, H, D, rope_dims, rope_base, scale, q, pool, N_cap, n_entries, m, c,
+                           z, bias, gain, eps, block_pos0, win, L_win, win_pos0, W, sink, q_pos0,
+                           out, lse, ws, ws_bytes, (hipStream_t)stream, false);
+}
+
+CSA_EXPORT int hca_decode_attn_kvfp8(int B, int H, int D, int rope_dims, double rope_base,
+                                     float scale, const void* q, void* pool, int N_cap,
+                                     const int32_t* n_entries, int m, const void* c,
+                                     const void* z, const float* bias, const float* gain,
+                                     float eps, const int64_t* block_pos0, const void* win,
+                                     int L_win, const int64_t* win_pos0, int W, const float* sink,
+                                     const int64_t* q_pos0, void* out, float* lse, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  return hca_decode_common(B, H, D, rope_dims, rope_base, scale, q, pool, N_cap, n_entries, m, c,
+                           z, bias, gain, eps, block_pos0, win, L_win, win_pos0, W, sink, q_pos0,
+                           out, lse, ws, ws_bytes, (hipStream_t)stream, true);
 }

@@ -244,15 +244,16 @@ __device__ __forceinline__ int fresh_entry_row(const AttnArgs& a, int b) {
 // Wave w pools rows w, w + NW, ... with an online softmax per channel (lane l
 // holds channels 8l .. 8l + 7; eight rows' loads in flight per wave); the
 // waves' partials merge through LDS and wave 0 finishes the entry:
-// normalises, applies the gain, rotates, rounds to bf16, stores it to the
-// pool (head group 0 only) and leaves it in LDS.  The split's partial is
+// normalises, applies the gain, rotates, stores it to the pool (head group
+// 0 only; bf16, or a packed mixed BF16 / FP8 row) and leaves in LDS the bf16
+// values a reader of the stored row gets back.  The split's partial is
 // that one row: per head, the logit q'.row (q' the query rotated at tpos and
 // rounded to bf16, as the tile loop uses it) as the running maximum, a sum
 // of 1, and the row with its rope slice rotated back by -tpos as the
 // unnormalised output.  With no closing block, or an entry the query does
 // not see, the partial is empty (maximum -inf, sum 0, zero output); the
 // other splits leave the entry's row out when the query sees it.
-template <int NW>
+template <int NW, bool FP8>
 __device__ __forceinline__ void hca_fresh_split(const AttnArgs& a, int b, int qi, int sp, int S,
                                                 float* s_f, bf16_t* s_row, bf16_t* s_out,
                                                 float* s_cos, float* s_sin) {
@@ -347,20 +348,35 @@ __device__ __forceinline__ void hca_fresh_split(const AttnArgs& a, int b, int qi
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = y[e] * inv * gv[e];
       }
-      u32x4_t ent, outw;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {  // the entry's rotation, at the block's first position
+        const int c = c0 + 2 * k;
+        if (c >= rope0) {
+          float cs, sn;
+          rope_cos_sin(bp, (c - rope0) >> 1, a.rope_theta1, cs, sn);
+          const float x0 = y[2 * k], x1 = y[2 * k + 1];
+          y[2 * k] = x0 * cs - x1 * sn;
+          y[2 * k + 1] = x0 * sn + x1 * cs;
+        }
+      }
+      // the row as stored, and the bf16 values a reader of it gets back
+      u32x4_t ent;
+      if constexpr (FP8) {
+        if (blockIdx.z == 0)
+          store_kv_fp8_row((uint8_t*)a.pool + ((int64_t)b * a.N_cap + row) * a.pool_row_bytes,
+                           lane, y, R);
+        ent = kv_fp8_row_values(lane, y, R);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ent[k] = pack_bf16x2(y[2 * k], y[2 * k + 1]);
+        if (blockIdx.z == 0)
+          *reinterpret_cast<u32x4_t*>((bf16_t*)a.pool + ((int64_t)b * a.N_cap + row) * kAtD + c0) = ent;
+      }
+      // those values, rotated back by -tpos, are the split's output
+      u32x4_t outw;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int c = c0 + 2 * k;
-        float x0 = y[2 * k], x1 = y[2 * k + 1];
-        if (c >= rope0) {  // the entry's rotation, at the block's first position
-          float cs, sn;
-          rope_cos_sin(bp, (c - rope0) >> 1, a.rope_theta1, cs, sn);
-          const float r0v = x0 * cs - x1 * sn, r1v = x0 * sn + x1 * cs;
-          x0 = r0v;
-          x1 = r1v;
-        }
-        ent[k] = pack_bf16x2(x0, x1);
-        // the stored (bf16) values, rotated back by -tpos for the output
         float o0 = __uint_as_float(ent[k] << 16), o1 = __uint_as_float(ent[k] & 0xffff0000u);
         if (c >= rope0) {
           const int pj = (c - rope0) >> 1;
@@ -371,8 +387,6 @@ __device__ __forceinline__ void hca_fresh_split(const AttnArgs& a, int b, int qi
         }
         outw[k] = pack_bf16x2(o0, o1);
       }
-      if (blockIdx.z == 0)
-        *reinterpret_cast<u32x4_t*>((bf16_t*)a.pool + ((int64_t)b * a.N_cap + row) * kAtD + c0) = ent;
       *reinterpret_cast<u32x4_t*>(s_row + c0) = ent;
       *reinterpret_cast<u32x4_t*>(s_out + c0) = outw;
     }
@@ -477,10 +491,10 @@ void attn_hs(AttnArgs a) {
   const int rope0 = kAtD - R;
   // HCA decode step: the last split pools the closing block's entry; the
   // others divide the key list among themselves
-  if constexpr (!CSA && !FP8) {
+  if constexpr (!CSA) {
     if (a.fresh && sp == S - 1) {
-      hca_fresh_split<NW>(a, b, qi, sp, S, reinterpret_cast<float*>(s_rows0), s_rows1,
-                          s_rows1 + kAtD, s_cos, s_sin);
+      hca_fresh_split<NW, FP8>(a, b, qi, sp, S, reinterpret_cast<float*>(s_rows0), s_rows1,
+                               s_rows1 + kAtD, s_cos, s_sin);
       return;
     }
   }
@@ -511,7 +525,7 @@ void attn_hs(AttnArgs a) {
 
   const int64_t tpos = a.q_pos0[b] + t;
   KeyRange kr = key_range(a, b, qi, tpos);
-  if constexpr (!CSA && !FP8) {
+  if constexpr (!CSA) {
     // the closing block's entry, when the query sees it, is the last split's
     if (a.fresh) {
       const int row = fresh_entry_row(a, b);

@@ -90,6 +90,38 @@ __device__ __forceinline__ void store_kv_fp8_row(uint8_t* row, int lane, const f
     for (int p = D + R + (D - R) / 32; p < D + R + kv_fp8_scale_pad(D, R); ++p) row[p] = 0;
   }
 }
+// The values a reader of that packed row gets back for the lane's 8
+// channels, as bf16 pairs: the E4M3 codes times their block's scale (exact
+// in bf16, converted as the attention converts a staged row), or the bf16
+// RoPE channels.  All 64 lanes take part (the block scale's lane swaps).
+__device__ __forceinline__ u32x4_t kv_fp8_row_values(int lane, const float (&y)[8], int R) {
+  constexpr int D = 512;
+  const bool fp8 = lane < ((D - R) >> 3);
+  float am = 0.f;
+  if (fp8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(y[e]));
+  }
+  am = fmaxf(am, __shfl_xor(am, 1));
+  am = fmaxf(am, __shfl_xor(am, 2));
+  const uint32_t s = mx8_scale_byte(am);
+  u32x4_t v;
+  if (fp8) {
+    const uint32_t lo = e4m3_code(y[0], s) | (e4m3_code(y[1], s) << 8) |
+                        (e4m3_code(y[2], s) << 16) | (e4m3_code(y[3], s) << 24);
+    const uint32_t hi = e4m3_code(y[4], s) | (e4m3_code(y[5], s) << 8) |
+                        (e4m3_code(y[6], s) << 16) | (e4m3_code(y[7], s) << 24);
+    const float sc = mx_scale_value(s);
+    v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, false));
+    v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, true));
+    v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, false));
+    v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, true));
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = pack_bf16x2(y[2 * k], y[2 * k + 1]);
+  }
+  return v;
+}
 // Workspace the compressor uses for a call of this shape (0 = none); rows:
 // rows pooled per entry (m, or 2m with overlap).
 size_t compress_ws_bytes(int dt, int B, int n_out, int D, int rows);
@@ -196,7 +228,7 @@ struct AttnArgs {
   int splits;           // key-range splits per query (1 = no combine pass)
   float* part_ml;       // [B*Tq, splits, H, 2] when splits > 1: (max, sum)
   bf16_t* part_o;       // [B*Tq, splits, H, D] unnormalised split outputs
-  // HCA decode step (hca_decode_attn; Tq = 1, bf16, the MFMA shape): the
+  // HCA decode step (hca_decode_attn(_kvfp8); Tq = 1, the MFMA shape): the
   // last split of each query is the closing block's new entry, pooled by
   // that split's workgroup from job fj (T = m, one entry per sequence, to
   // row min(n_entries[b], N_cap) - 1 when fj.pos0[b] >= 0) and counted as a

@@ -22,7 +22,8 @@ import long_context_sparse_11_amd as L
 from long_context_sparse_11_amd import synth
 from oracle import csa_oracle as O
 from tests.helpers import TOL_BF16, dev, host, rowwise_rel_err
-from tests.test_gpu_parity import _fresh_case, _fresh_jobs_and_refs, _rand_sel, i32, i64
+from tests.test_gpu_parity import (ALL_KINDS, _fresh_case, _fresh_jobs_and_refs, _hca_step_case,
+                                   _rand_sel, i32, i64)
 
 pytestmark = pytest.mark.gpu
 
@@ -233,6 +234,52 @@ def test_attn_kvfp8_equals_bf16_on_dequantized_pool_and_oracle(kind, N, K, W, Tq
     assert torch.equal(o8, ob) and torch.equal(l8, lb)
     assert rowwise_rel_err(host(o8), ro) <= TOL_BF16
     assert np.abs(host(l8) - rl).max() <= 2e-2
+
+
+def _run_hca_step_fp8(d, p8):
+    return L.hca_decode_attn_kvfp8(dev(d["q"]), p8, i32(d["n_ent"]), d["m"], dev(d["c"]),
+                                   dev(d["z"]), dev(d["bias"]), dev(d["gain"]),
+                                   i64(d["block_pos0"]), dev(d["win"]), i64(d["win_pos0"]),
+                                   d["W"], dev(d["sink"]), i64(d["q_pos0"]), rope_dims=R,
+                                   want_lse=True)
+
+
+@pytest.mark.parametrize("H,N,W,m,kinds", [
+    (64, 300, 128, 128, ALL_KINDS),
+    (64, 3000, 128, 128, ["close", "clamp", "open", "close"]),
+    (128, 500, 128, 128, ["close", "open"]),
+    (64, 12, 16, 16, ["close", "first", "empty", "open"]),   # one single-tile key split
+])
+def test_hca_decode_step_fused_fp8(H, N, W, m, kinds):
+    """hca_decode_attn_kvfp8: the closing block's entry stored as a packed row
+    (codes against the oracle's quantization of its exact entry) and the
+    attention over the dequantized pool with it, against the oracle; and the
+    same output as hca_attn_kvfp8 over the pool the call wrote."""
+    d = _hca_step_case(kinds, H, N, W, m, seed=N + H + m + 1)
+    pool8 = O.kv_fp8_quantize(d["pool"].f32.astype(np.float64), R)
+    p8 = dev(pool8)
+    out, lse = _run_hca_step_fp8(d, p8)
+    got = host(p8)
+    ref_pool = O.kv_fp8_dequantize(pool8, D, R)
+    for b in range(d["B"]):
+        if b in d["rows"]:
+            row, ent = d["rows"][b]
+            _check_fp8_entries(got[b, row][None], ent[None])
+            keep = np.ones(N, bool)
+            keep[row] = False
+            assert np.array_equal(got[b, keep], pool8[b, keep])
+            ref_pool[b, row] = O.kv_fp8_dequantize(O.kv_fp8_quantize(ent[None], R), D, R)[0]
+        else:
+            assert np.array_equal(got[b], pool8[b])
+    ro, rl = O.hca_attn(d["q"].f32, ref_pool, d["n_ent"], m, d["win"].f32, d["win_pos0"], W,
+                        d["sink"], d["q_pos0"], 1 / math.sqrt(D), R)
+    assert rowwise_rel_err(host(out), ro) <= TOL_BF16
+    assert np.abs(host(lse) - rl).max() <= 2e-2
+    o2, l2 = L.hca_attn_kvfp8(dev(d["q"]), p8, i32(d["n_ent"]), m, dev(d["win"]),
+                              i64(d["win_pos0"]), W, dev(d["sink"]), i64(d["q_pos0"]),
+                              rope_dims=R, want_lse=True)
+    assert rowwise_rel_err(host(out), host(o2).astype(np.float64)) <= 1e-2
+    assert np.abs(host(lse) - host(l2)).max() <= 1e-2
 
 
 def test_kvfp8_rejects_uncovered_shapes():

@@ -342,6 +342,10 @@ def test_hca_decode_step_validation(lib):
     assert lib.hca_decode_attn_ws_bytes(16, 64, 512, 8192 + 128) == s_attn > 0
     assert lib.hca_decode_attn_ws_bytes(1, 64, 512, 10) == 2 * 64 * (8 + 2 * 512)
     assert lib.hca_decode_attn_ws_bytes(1, 32, 512, 10) == 0
+    # packed FP8 pools: R a multiple of 32
+    assert lib.hca_decode_attn_kvfp8(16, 64, 512, 48, 10000.0, 0.044, P, P, 8192, P, 128, P, P,
+                                     N, N, 1e-6, P, P, 128, P, 128, P, P, P, N, P, 1 << 40,
+                                     N) == CSA_ERR_UNSUPPORTED
 
 
 def test_kv_fp8_validation(lib):
