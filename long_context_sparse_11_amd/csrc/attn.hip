@@ -914,9 +914,10 @@ void attn_hs(AttnArgs a) {
 // 128 threads of 4 channels each (the 512-wide Flash rows).  The partial
 // outputs of the first kCbPre splits are requested before the per-split
 // weights are known, so the two dependent reads overlap; the weights go
-// through LDS.
+// through LDS.  32 covers the decode grids (20 splits at 64K: 12.6 ->
+// 12.4 us per call against 16, whose last 4 splits waited for the weights).
 constexpr int kMaxSplits = 256;
-constexpr int kCbPre = 16;
+constexpr int kCbPre = 32;
 
 template <typename T>
 __global__ __launch_bounds__(128) void attn_combine(AttnArgs a) {
