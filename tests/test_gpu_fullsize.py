@@ -6,8 +6,10 @@ and key splits) as the benchmark's step, checked against the oracle.
   V4-Pro's shapes (128 heads, top-1024), two sequences checked.
 * CSA decode at 1M context (batch 8, heavy-tailed indexer keys): the whole
   batch runs on the GPU; the oracle checks two sequences (its scores for a
-  262,144-entry row are the expensive part).
-* HCA decode at 1M context (batch 16): three sequences checked.
+  262,144-entry row are the expensive part).  Both CSA decodes also with
+  the KV pool in packed BF16 / FP8 rows.
+* HCA decode at 1M context (batch 16): the one-call step (bf16 and packed
+  BF16 / FP8 pools) and the two-call form; three sequences checked.
 * CSA chunked prefill (4,096 queries after a 15,360-entry prefix): the
   compressor over the whole chunk; indexer and attention on a sample of
   queries (first 64, last 64, every 16th).
@@ -77,11 +79,25 @@ def _check_selection(gidx, gall, ref_idx, ref_sc, n_vis, K):
 # ---------------------------------------------------------------------------
 # CSA decode (64K and 1M)
 # ---------------------------------------------------------------------------
-def _csa_decode(kind, check_b):
+def _deq_rows(rows_b, idx_lists, D, R):
+    """Packed FP8 rows of one sequence -> a compact float64 pool of the rows
+    the index lists name, and the lists remapped into it (-1 kept)."""
+    used = np.unique(np.concatenate([np.asarray(x).ravel() for x in idx_lists]))
+    used = used[used >= 0]
+    remap = np.full(rows_b.shape[0], -1, np.int64)
+    remap[used] = np.arange(len(used))
+    pool = O.kv_fp8_dequantize(rows_b[used], D, R)
+    return pool, [np.where(np.asarray(x) >= 0, remap[np.maximum(x, 0)], -1) for x in idx_lists]
+
+
+def _csa_decode(kind, check_b, fp8=False):
     d = synth.decode(kind, 0)
     B, N, D, Di, m, K, W, R = d["B"], d["N"], d["D"], d["Di"], d["m"], d["K"], d["W"], d["R"]
     scale = 1.0 / math.sqrt(D)
     pool, kidx = dev(d["pool"]), dev(d["k_idx"])
+    if fp8:   # the pool in packed BF16 / FP8 rows, quantized on the device
+        pool = L.csa_quantize_kv_fp8(pool, R)
+        before = host(pool[:, : N - 1])
     # the benchmark's step: the closing block's key and KV entries (row N-1
     # of the caches) and the indexer top-K in one call, then the attention
     ws_i = torch.empty(L.csa_index_topk_ws_bytes(B, 1, 64, N, K), dtype=torch.uint8, device="cuda")
@@ -92,7 +108,8 @@ def _csa_decode(kind, check_b):
             dict(c_a=dev(d["c_a"]), z_a=dev(d["z_a"]), c_b=dev(d["c_b"]), z_b=dev(d["z_b"]),
                  prev_c_b=dev(d["prev_c_b"]), prev_z_b=dev(d["prev_z_b"]),
                  bias_a=dev(d["bias_a"]), bias_b=dev(d["bias_b"]), gain=dev(d["gain"]),
-                 rope_dims=R, out=pool)]
+                 rope_dims=R, out=pool, out_kv_fp8=fp8)]
+    attn = L.csa_sparse_attn_kvfp8 if fp8 else L.csa_sparse_attn
     idx, _, alls = L.csa_decode_index_topk(dev(d["q_idx"]), dev(d["w_idx"]), i32(d["n_entries"]),
                                            i64(d["q_pos0"]), K, m, jobs,
                                            block_pos0=i64(d["block_pos0"]), ws=ws_i,
@@ -101,8 +118,8 @@ def _csa_decode(kind, check_b):
                        device="cuda")
     q, win, sink = dev(d["q"]), dev(d["win"]), dev(d["sink"])
     print(f"[{kind}] sparse_attn", flush=True)
-    out_step, _ = L.csa_sparse_attn(q, pool, idx, win, i64(d["win_pos0"]), W, sink,
-                                    i64(d["q_pos0"]), rope_dims=R, ws=ws_a)
+    out_step, _ = attn(q, pool, idx, win, i64(d["win_pos0"]), W, sink, i64(d["q_pos0"]),
+                       rope_dims=R, ws=ws_a)
     torch.cuda.synchronize()
 
     # compressed entries (every sequence)
@@ -113,7 +130,12 @@ def _csa_decode(kind, check_b):
     ik_ref = O.csa_compress(d["ic_a"].f32, d["iz_a"].f32, d["ibias_a"], m, c_b=d["ic_b"].f32,
                             z_b=d["iz_b"].f32, bias_b=d["ibias_b"], prev_c_b=d["iprev_c_b"].f32,
                             prev_z_b=d["iprev_z_b"].f32)
-    _check_entries(host(pool[:, N - 1]), kv_ref[:, 0])
+    if fp8:
+        from tests.test_gpu_kvfp8 import _check_fp8_entries
+        _check_fp8_entries(host(pool[:, N - 1]), kv_ref[:, 0])
+        assert np.array_equal(host(pool[:, : N - 1]), before)
+    else:
+        _check_entries(host(pool[:, N - 1]), kv_ref[:, 0])
     _check_entries(host(kidx[:, N - 1]), ik_ref[:, 0])
 
     # indexer + selection on the sampled sequences.  Stage isolation: the
@@ -139,11 +161,30 @@ def _csa_decode(kind, check_b):
 
     # attention with the oracle's index sets (stage isolation), same launch shape
     print(f"[{kind}] sparse_attn on the oracle's index sets", flush=True)
-    out_iso, lse_iso = L.csa_sparse_attn(q, pool, i32(ref_idx_all), win, i64(d["win_pos0"]), W,
-                                         sink, i64(d["q_pos0"]), rope_dims=R, ws=ws_a,
-                                         want_lse=True)
+    out_iso, lse_iso = attn(q, pool, i32(ref_idx_all), win, i64(d["win_pos0"]), W, sink,
+                            i64(d["q_pos0"]), rope_dims=R, ws=ws_a, want_lse=True)
     torch.cuda.synchronize()
     sel = np.asarray(check_b)
+    if fp8:
+        # per sequence, over the dequantized rows the index sets name: the
+        # cached rows as stored and, at N - 1, the oracle's quantization of
+        # its own entry (isolated run) or the GPU's stored row (the step)
+        for i, b in enumerate(check_b):
+            rows_b = host(pool[b])
+            own = rows_b.copy()
+            own[N - 1] = O.kv_fp8_quantize(kv_ref[b, 0][None], R)[0]
+            for rows, ix, o, l in ((own, ref_idx_all, out_iso, lse_iso),
+                                   (rows_b, gidx, out_step, None)):
+                pc, (ic,) = _deq_rows(rows, [ix[b]], D, R)
+                ro, rl = O.csa_sparse_attn(_f32(d["q"], slice(b, b + 1)), pc[None], ic[None],
+                                           _f32(d["win"], slice(b, b + 1)),
+                                           d["win_pos0"][b:b + 1], W, d["sink"],
+                                           d["q_pos0"][b:b + 1], scale, R)
+                e = rowwise_rel_err(host(o)[b:b + 1], ro)
+                assert e <= TOL_BF16, (b, e)
+                if l is not None:
+                    assert np.abs(host(l)[b:b + 1] - rl).max() <= 2e-2
+        return None
     pool_s = _f32(d["pool"], sel).copy()
     pool_s[:, N - 1] = synth.Tensor(kv_ref[sel, 0].astype(np.float32), "bf16").f32
     ro, rl = O.csa_sparse_attn(_f32(d["q"], sel), pool_s, ref_idx_all[sel], _f32(d["win"], sel),
@@ -231,6 +272,16 @@ def test_csa_decode_1m_sampled_sequences():
     _csa_decode("csa1m", check_b=[0, 5])
 
 
+def test_csa_decode_64k_fp8_kv_full_step():
+    """The benchmark's FP8-KV step at 64K: the fused call writes the closing
+    block's KV entry as a packed row, the attention reads the packed pool."""
+    _csa_decode("csa64k", check_b=[0, 1, 2, 3], fp8=True)
+
+
+def test_csa_decode_1m_fp8_kv_sampled_sequences():
+    _csa_decode("csa1m", check_b=[0, 5], fp8=True)
+
+
 def test_csa_decode_64k_v4pro_shapes():
     """V4-Pro's attention and selection (128 heads, top-1024) at 64K."""
     _csa_decode("csa64k_pro", check_b=[0, 3])
@@ -239,27 +290,57 @@ def test_csa_decode_64k_v4pro_shapes():
 # ---------------------------------------------------------------------------
 # HCA decode (1M)
 # ---------------------------------------------------------------------------
-def test_hca_decode_1m_sampled_sequences():
+@pytest.mark.parametrize("mode", ["one_call", "two_calls", "one_call_fp8"])
+def test_hca_decode_1m_sampled_sequences(mode):
+    """The HCA step at 1M context (batch 16): hca_decode_attn as the benchmark
+    times it (the closing block's entry pooled by the attention launch),
+    csa_compress + hca_attn, and hca_decode_attn_kvfp8 over the pool in
+    packed BF16 / FP8 rows (quantized on the device, as the benchmark does).
+    The new entries of every sequence are checked against the oracle's
+    compressor; the outputs of three sequences against the oracle's
+    attention over the cached entries plus the oracle's new entry (for FP8:
+    the dequantized rows and the oracle's quantization of that entry)."""
     d = synth.decode("hca1m", 0)
     B, N, D, m, W, R = d["B"], d["N"], d["D"], d["m"], d["W"], d["R"]
     scale = 1.0 / math.sqrt(D)
     pool = dev(d["pool"])
-    print(f"[hca1m] B={B} N={N}: compress + attention", flush=True)
-    L.csa_compress(dev(d["c_a"]), m, z_a=dev(d["z_a"]), bias_a=dev(d["bias_a"]),
-                   gain=dev(d["gain"]), rope_dims=R, pos0=i64(d["block_pos0"]),
-                   out=pool[:, N - 1:], out_bstride=N * D)
-    ws_a = torch.empty(max(L.csa_attn_ws_bytes(B, 1, d["H"], D, N + W), 1), dtype=torch.uint8,
-                       device="cuda")
-    out, lse = L.hca_attn(dev(d["q"]), pool, i32(d["n_entries"]), m, dev(d["win"]),
-                          i64(d["win_pos0"]), W, dev(d["sink"]), i64(d["q_pos0"]), rope_dims=R,
-                          ws=ws_a, want_lse=True)
+    q, win, sink = dev(d["q"]), dev(d["win"]), dev(d["sink"])
+    args = (dev(d["c_a"]), dev(d["z_a"]), dev(d["bias_a"]), dev(d["gain"]), i64(d["block_pos0"]),
+            win, i64(d["win_pos0"]), W, sink, i64(d["q_pos0"]))
+    ws_f = torch.empty(max(L.hca_decode_attn_ws_bytes(B, d["H"], D, N + W), 1),
+                       dtype=torch.uint8, device="cuda")
+    print(f"[hca1m] B={B} N={N}: {mode}", flush=True)
+    if mode == "one_call":
+        out, lse = L.hca_decode_attn(q, pool, i32(d["n_entries"]), m, *args, rope_dims=R, ws=ws_f,
+                                     want_lse=True)
+    elif mode == "two_calls":
+        L.csa_compress(dev(d["c_a"]), m, z_a=dev(d["z_a"]), bias_a=dev(d["bias_a"]),
+                       gain=dev(d["gain"]), rope_dims=R, pos0=i64(d["block_pos0"]),
+                       out=pool[:, N - 1:], out_bstride=N * D)
+        ws_a = torch.empty(max(L.csa_attn_ws_bytes(B, 1, d["H"], D, N + W), 1),
+                           dtype=torch.uint8, device="cuda")
+        out, lse = L.hca_attn(q, pool, i32(d["n_entries"]), m, win, i64(d["win_pos0"]), W, sink,
+                              i64(d["q_pos0"]), rope_dims=R, ws=ws_a, want_lse=True)
+    else:
+        pool = L.csa_quantize_kv_fp8(pool, R)
+        before = host(pool[:, : N - 1])
+        out, lse = L.hca_decode_attn_kvfp8(q, pool, i32(d["n_entries"]), m, *args, rope_dims=R,
+                                           ws=ws_f, want_lse=True)
     torch.cuda.synchronize()
     kv_ref = O.csa_compress(d["c_a"].f32, d["z_a"].f32, d["bias_a"], m, gain=d["gain"],
                             rope_dims=R, pos0=d["block_pos0"])
-    _check_entries(host(pool[:, N - 1]), kv_ref[:, 0])
     sel = np.array([0, 7, 15])
-    pool_s = _f32(d["pool"], sel).copy()   # cached entries + the oracle's own new entry
-    pool_s[:, N - 1] = synth.Tensor(kv_ref[sel, 0].astype(np.float32), "bf16").f32
+    if mode == "one_call_fp8":
+        from tests.test_gpu_kvfp8 import _check_fp8_entries
+        rows = host(pool)
+        _check_fp8_entries(rows[:, N - 1], kv_ref[:, 0])
+        assert np.array_equal(rows[:, : N - 1], before)
+        pool_s = O.kv_fp8_dequantize(rows[sel], D, R)
+        pool_s[:, N - 1] = O.kv_fp8_dequantize(O.kv_fp8_quantize(kv_ref[sel, 0], R), D, R)
+    else:
+        _check_entries(host(pool[:, N - 1]), kv_ref[:, 0])
+        pool_s = _f32(d["pool"], sel).copy()   # cached entries + the oracle's own new entry
+        pool_s[:, N - 1] = synth.Tensor(kv_ref[sel, 0].astype(np.float32), "bf16").f32
     ro, rl = O.hca_attn(_f32(d["q"], sel), pool_s, d["n_entries"][sel], m, _f32(d["win"], sel),
                         d["win_pos0"][sel], W, d["sink"], d["q_pos0"][sel], scale, R)
     e = rowwise_rel_err(host(out)[sel], ro)
