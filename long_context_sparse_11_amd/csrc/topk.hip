@@ -71,7 +71,10 @@ __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, TkShare
 }
 
 // Exclusive block prefix of x (all threads take part); also returns the
-// block total.  Uses S.red[0] and two barriers.
+// block total.  Uses S.red[0] and two barriers; TRAIL false drops the second
+// (which keeps S.red[0] from being rewritten while others still read it) where
+// a barrier comes before the next write of S.red anyway.
+template <bool TRAIL = true>
 __device__ __forceinline__ uint32_t block_excl_sum(uint32_t x, uint32_t& total, TkShared& S,
                                                    int wave, int lane) {
   const uint32_t incl = wave_incl_sum(x);
@@ -85,7 +88,7 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t x, uint32_t& total, 
     tot += t;
   }
   total = tot;
-  __syncthreads();
+  if (TRAIL) __syncthreads();
   return before;
 }
 
@@ -293,13 +296,16 @@ void topk_kernel(TopkArgs a) {
       kmx = max(kmx, S.red[1][w]);
       n_live += S.red[2][w];
     }
-    __syncthreads();
   }
   const float fmn = key_score(kmn), fmx = key_score(kmx);
   const float range = fmx - fmn;
   const float scale = (float)kBins / range;
   const bool linear = kmn < kmx && isfinite(fmn) && isfinite(fmx) && isfinite(range) &&
                       isfinite(scale) && scale > 0.f;
+  // S.red is read above and rewritten next: by the linear path only after
+  // the histogram's barrier, by the other two paths at once (the values
+  // every thread read are equal, so the branch is uniform)
+  if (!linear || n_live <= (uint32_t)K) __syncthreads();
 
   uint32_t prefix = 0, mask = 0;   // threshold among the keys of in_bin
   int remaining = K;
@@ -332,7 +338,8 @@ void topk_kernel(TopkArgs a) {
       local += h[k];
     }
     uint32_t total;
-    const uint32_t below = block_excl_sum(local, total, S, wave, lane);
+    // S.red is next written after the selection's barrier below
+    const uint32_t below = block_excl_sum<false>(local, total, S, wave, lane);
     uint32_t above = total - below - local;
 #pragma unroll
     for (int k = kBinsPerThread - 1; k >= 0; --k) {
@@ -355,7 +362,9 @@ void topk_kernel(TopkArgs a) {
       above_m |= (v && d > d1) ? (1u << i) : 0u;
       in_bin |= (v && d == d1) ? (1u << i) : 0u;
     }
-    __syncthreads();  // sel_* are rewritten below
+    // sel_* are rewritten below only after a barrier (the compaction's, or
+    // those of the block-level select), which every thread reaches after
+    // its reads above
 
     if (c1 == (uint32_t)remaining) {
       // the whole bin is taken: every key of in_bin is "equal" and all fit
@@ -483,7 +492,7 @@ void topk_kernel(TopkArgs a) {
   }
   const uint32_t ngt = __popc(gt_m), neq = __popc(eq_m);
   uint32_t total;  // counts packed as gt | eq << 16 (each at most kTopkCap)
-  const uint32_t before = block_excl_sum(ngt | (neq << 16), total, S, wave, lane);
+  const uint32_t before = block_excl_sum<false>(ngt | (neq << 16), total, S, wave, lane);
   const uint32_t before_gt = before & 0xffffu, before_eq = before >> 16;
   // the first `take` of this thread's equal keys are chosen; the clamp comes
   // before the subtraction so that no intermediate can wrap
