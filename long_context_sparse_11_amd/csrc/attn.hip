@@ -644,21 +644,23 @@ void attn_hs(AttnArgs a) {
   if constexpr (FP8) convert_rows(fp8_0, s_rows0);
   __syncthreads();
 
-  // rotate the query slice's rope channels at +tpos (each lane its own pairs)
+  // rotate the query slice's rope channels at +tpos (each lane its own
+  // pairs).  Which 32-channel slices hold rope channels is the same for every
+  // lane, so the skip is a uniform branch; inside a slice each pair is
+  // rotated or passed through by a select (no per-lane branches)
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) {
+    if (32 * ks + 32 <= rope0) continue;
     const int c0 = 32 * ks + 8 * G;
-    if (c0 + 8 <= rope0) continue;
     const u32x4_t w = __builtin_bit_cast(u32x4_t, qb[ks]);
     u32x4_t pk;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int c = c0 + 2 * k;
-      const bool rot = c >= rope0;
       const int pj = max(c - rope0, 0) >> 1;
-      const float cs = rot ? s_cos[pj] : 1.f, sn = rot ? s_sin[pj] : 0.f;
+      const float cs = s_cos[pj], sn = s_sin[pj];
       const float x0 = __uint_as_float(w[k] << 16), x1 = __uint_as_float(w[k] & 0xffff0000u);
-      pk[k] = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+      pk[k] = c >= rope0 ? pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs) : w[k];
     }
     qb[ks] = __builtin_bit_cast(bf16x8_t, pk);
   }
@@ -842,6 +844,41 @@ void attn_hs(AttnArgs a) {
   }
 
   // ---- epilogue: lane (G, c16) holds channels 16cb + 4G + r of head h
+  // rotate_back: channels c .. c + 3 (block cb) rotated by -tpos where they
+  // are rope channels.  In the straight-line single-tile kernels the block
+  // test is uniform and each pair is rotated or passed through by a select
+  // (per-lane branches there cost hundreds of exec-mask moves: the 64K decode
+  // kernel shrank from 6,110 to 5,194 instructions).  The multi-tile kernels
+  // keep per-lane branches: with the selects their tile loop no longer fit
+  // its registers.
+  auto rotate_back = [&](float (&o)[4], int c, int cb) {
+    if constexpr (MULTI) {
+      if (c + 4 > rope0) {
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          if (c + e >= rope0) {
+            const int pj = (c + e - rope0) >> 1;
+            const float cs = s_cos[pj], sn = s_sin[pj];
+            const float x0 = o[e], x1 = o[e + 1];
+            o[e] = x0 * cs + x1 * sn;
+            o[e + 1] = -x0 * sn + x1 * cs;
+          }
+        }
+      }
+    } else {
+      if (16 * cb + 16 > rope0) {
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const bool rot = c + e >= rope0;
+          const int pj = max(c + e - rope0, 0) >> 1;
+          const float cs = s_cos[pj], sn = s_sin[pj];
+          const float x0 = o[e], x1 = o[e + 1];
+          o[e] = rot ? x0 * cs + x1 * sn : x0;
+          o[e + 1] = rot ? -x0 * sn + x1 * cs : x1;
+        }
+      }
+    }
+  };
   if (S == 1) {
     const float skl2 = a.sink[h] * kLog2e;
     const float mf = fmaxf(mrun, skl2);
@@ -855,18 +892,7 @@ void attn_hs(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[r] = oacc[cb][r] * fac;
       const int c = 16 * cb + 4 * G;
-      if (c + 4 > rope0) {
-#pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          if (c + e >= rope0) {
-            const int pj = (c + e - rope0) >> 1;
-            const float cs = s_cos[pj], sn = s_sin[pj];
-            const float x0 = o[e], x1 = o[e + 1];
-            o[e] = x0 * cs + x1 * sn;
-            o[e + 1] = -x0 * sn + x1 * cs;
-          }
-        }
-      }
+      rotate_back(o, c, cb);
       uint2 pk;
       pk.x = pack_bf16x2(o[0], o[1]);
       pk.y = pack_bf16x2(o[2], o[3]);
@@ -888,18 +914,7 @@ void attn_hs(AttnArgs a) {
     for (int cb = 0; cb < 32; ++cb) {
       float o[4] = {oacc[cb][0], oacc[cb][1], oacc[cb][2], oacc[cb][3]};
       const int c = 16 * cb + 4 * G;
-      if (c + 4 > rope0) {
-#pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          if (c + e >= rope0) {
-            const int pj = (c + e - rope0) >> 1;
-            const float cs = s_cos[pj], sn = s_sin[pj];
-            const float x0 = o[e], x1 = o[e + 1];
-            o[e] = x0 * cs + x1 * sn;
-            o[e + 1] = -x0 * sn + x1 * cs;
-          }
-        }
-      }
+      rotate_back(o, c, cb);
       uint2 pk;
       pk.x = pack_bf16x2(o[0], o[1]);
       pk.y = pack_bf16x2(o[2], o[3]);
