@@ -465,7 +465,7 @@ __device__ __forceinline__ void hca_fresh_split(const AttnArgs& a, int b, int qi
 // Prefill attention: 579 -> 469 us.  The others keep one wave per SIMD: a
 // single-tile split is one short workgroup per compute unit, and the FP8
 // kernel's staging area leaves LDS for one workgroup.
-template <bool CSA, bool MULTI, int NW, bool FP8>
+template <bool CSA, bool MULTI, int NW, bool FP8, int RC = 0>
 __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(MULTI && !FP8 ? 2 : 1, MULTI && !FP8 ? 2 : 1)))
 void attn_hs(AttnArgs a) {
@@ -487,7 +487,7 @@ void attn_hs(AttnArgs a) {
   const int h = 16 * (NW * (int)blockIdx.z + wave) + c16;  // this lane's head
   const int qi = blockIdx.y, sp = blockIdx.x, S = gridDim.x;
   const int b = qi / a.Tq, t = qi - b * a.Tq;
-  const int R = a.R;
+  const int R = RC > 0 ? RC : a.R;  // RC: rope width fixed at compile time
   const int rope0 = kAtD - R;
   // HCA decode step: the last split pools the closing block's entry; the
   // others divide the key list among themselves
@@ -1050,18 +1050,36 @@ static hipError_t launch_generic(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The single-tile kernels run their code once, straight through, so their
+// size is part of their time: for the Flash and Pro rope width (64 channels)
+// an instance with it fixed at compile time drops every rope test on the
+// other 448 channels (the query rotation, the epilogue).
+constexpr int kRopeFixed = 64;
+
+template <bool FP8, int RC>
+static void launch_hs_single(const AttnArgs& a, bool halves, dim3 grid, dim3 grid2,
+                             hipStream_t stream) {
+  const dim3 block4(256), block2(128);
+  if (a.csa) {
+    if (halves) hipLaunchKernelGGL((attn_hs<true, false, 2, FP8, RC>), grid2, block2, 0, stream, a);
+    else hipLaunchKernelGGL((attn_hs<true, false, 4, FP8, RC>), grid, block4, 0, stream, a);
+  } else {
+    if (halves) hipLaunchKernelGGL((attn_hs<false, false, 2, FP8, RC>), grid2, block2, 0, stream, a);
+    else hipLaunchKernelGGL((attn_hs<false, false, 4, FP8, RC>), grid, block4, 0, stream, a);
+  }
+}
+
 template <bool FP8>
 static void launch_hs(const AttnArgs& a, bool multi, bool halves, dim3 grid, dim3 grid2,
                       hipStream_t stream) {
-  const dim3 block4(256), block2(128);
-  if (a.csa) {
-    if (multi) hipLaunchKernelGGL((attn_hs<true, true, 4, FP8>), grid, block4, 0, stream, a);
-    else if (halves) hipLaunchKernelGGL((attn_hs<true, false, 2, FP8>), grid2, block2, 0, stream, a);
-    else hipLaunchKernelGGL((attn_hs<true, false, 4, FP8>), grid, block4, 0, stream, a);
+  if (multi) {
+    const dim3 block4(256);
+    if (a.csa) hipLaunchKernelGGL((attn_hs<true, true, 4, FP8>), grid, block4, 0, stream, a);
+    else hipLaunchKernelGGL((attn_hs<false, true, 4, FP8>), grid, block4, 0, stream, a);
+  } else if (a.R == kRopeFixed) {
+    launch_hs_single<FP8, kRopeFixed>(a, halves, grid, grid2, stream);
   } else {
-    if (multi) hipLaunchKernelGGL((attn_hs<false, true, 4, FP8>), grid, block4, 0, stream, a);
-    else if (halves) hipLaunchKernelGGL((attn_hs<false, false, 2, FP8>), grid2, block2, 0, stream, a);
-    else hipLaunchKernelGGL((attn_hs<false, false, 4, FP8>), grid, block4, 0, stream, a);
+    launch_hs_single<FP8, 0>(a, halves, grid, grid2, stream);
   }
 }
 

@@ -667,6 +667,40 @@ def test_attn_128_heads_v4pro(kind, N, K, Tq):
     assert np.abs(host(lse) - rl).max() <= LSE_ATOL_BF16
 
 
+@pytest.mark.parametrize("kind,R,Tq,N", [
+    ("csa", 0, 1, 2000), ("csa", 32, 1, 2000), ("csa", 128, 1, 2000),   # two-wave single tiles
+    ("csa", 32, 24, 2000),                                              # multi-tile splits
+    ("hca", 32, 1, 3000), ("hca", 128, 1, 3000), ("hca", 0, 2, 300)])   # four-wave single tiles
+def test_attn_other_rope_widths(kind, R, Tq, N):
+    """Rope widths other than 64 (the width the single-tile kernels also have
+    an instance for with it fixed at compile time): no rotation, a narrower
+    and a wider rope slice, through the instances that read it at run time."""
+    rng = np.random.default_rng(1000 + R + Tq + N)
+    B, H, D, W = 2, 64, 512, 128
+    m = 4 if kind == "csa" else 128
+    ctx = N * m
+    q_pos0 = np.array([ctx - Tq, ctx - Tq - 3 * m])
+    L_win = Tq + W - 1 + 3 * m
+    win_pos0 = q_pos0 - W + 1 - 3 * m
+    f = lambda *sh: rng.standard_normal(sh).astype(np.float32)
+    q, pool, win = (synth.Tensor(f(*sh), "bf16") for sh in [(B, Tq, H, D), (B, N, D), (B, L_win, D)])
+    sink = 0.5 * f(H)
+    if kind == "csa":
+        nv = [[O.visible_count(q_pos0[b] + t, m, N) for t in range(Tq)] for b in range(B)]
+        sel = _rand_sel(rng, B, Tq, 512, nv, 3)
+        out, lse = _run_attn("csa", dev(q), dev(pool), dev(sel), dev(win), i64(win_pos0), W,
+                             dev(sink), i64(q_pos0), R)
+        ro, rl = _attn_ref("csa", q.f32, pool.f32, sel, win.f32, win_pos0, W, sink, q_pos0, R)
+    else:
+        n_ent = np.array([N, N - 5], np.int32)
+        out, lse = _run_attn("hca", dev(q), dev(pool), None, dev(win), i64(win_pos0), W,
+                             dev(sink), i64(q_pos0), R, m=m, n_entries=i32(n_ent))
+        ro, rl = _attn_ref("hca", q.f32, pool.f32, None, win.f32, win_pos0, W, sink, q_pos0, R,
+                           m=m, n_entries=n_ent)
+    assert rowwise_rel_err(host(out), ro) <= TOL_BF16
+    assert np.abs(host(lse) - rl).max() <= LSE_ATOL_BF16
+
+
 @pytest.mark.parametrize("N,n_ent,Tq,W", [(300, [300, 250, 1], 1, 128), (64, [64, 10, 0], 2, 16),
                                           (2000, [2000, 1999, 1000], 1, 128)])
 def test_attn_hca_bf16(N, n_ent, Tq, W):
