@@ -954,23 +954,37 @@ __global__ __launch_bounds__(128) void attn_combine(AttnArgs a) {
   for (int u = 0; u < kCbPre; ++u)
     v[u] = u < S ? *reinterpret_cast<const uint2*>(po + u * sstride) : uint2{0u, 0u};
   if (threadIdx.x < 64) {  // one wave merges the (max, sum) pairs
+    // lane l holds the pairs of splits l, l + 64, ... in registers: one
+    // round of loads (a second pass over them in memory was a second,
+    // dependent round trip)
     const int lane = threadIdx.x;
     const float skl2 = a.sink[h] * kLog2e;
+    constexpr int kPer = kMaxSplits / 64;
+    float2 ml[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int s = lane + 64 * k;
+      ml[k] = s < S ? *reinterpret_cast<const float2*>(a.part_ml + 2 * (slot0 + (int64_t)s * a.H))
+                    : make_float2(-INFINITY, 0.f);
+    }
     float M = skl2;
-    for (int s = lane; s < S; s += 64) M = fmaxf(M, a.part_ml[2 * (slot0 + (int64_t)s * a.H)]);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) M = fmaxf(M, ml[k].x);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float Ls = 0.f;
-    for (int s = lane; s < S; s += 64) {
-      const int64_t sl = slot0 + (int64_t)s * a.H;
-      Ls += a.part_ml[2 * sl + 1] * exp2f(a.part_ml[2 * sl] - M);
+    float Ls = 0.f, w[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      w[k] = exp2f(ml[k].x - M);  // 0 for an absent split (max -inf)
+      Ls += ml[k].y * w[k];
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) Ls += __shfl_xor(Ls, off);
     Ls += exp2f(skl2 - M);
     const float inv = 1.f / Ls;
-    for (int s = lane; s < S; s += 64)
-      s_w[s] = exp2f(a.part_ml[2 * (slot0 + (int64_t)s * a.H)] - M) * inv;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+      if (lane + 64 * k < S) s_w[lane + 64 * k] = w[k] * inv;
     if (lane == 0) s_lse = (M + log2f(Ls)) * kLn2;
   }
   __syncthreads();
