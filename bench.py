@@ -14,8 +14,8 @@ and the attention), prefill (CSA chunk of 4,096
 queries on a 61,440-token prefix), csa64k_pro (V4-Pro attention: 128 heads,
 top-1024), csa64k_fp4 / csa1m_fp4 (as csa64k / csa1m with the indexer keys
 stored in MX FP4; the fresh key is quantized inside the step), swa
-(sliding-window-only layers, batch 16: the new token's window row, then
-attention over the 128-token window alone), oproj (the grouped low-rank output
+(sliding-window-only layers, batch 16: one swa_decode_attn call, the new
+token's window row and the attention over the 128-token window alone), oproj (the grouped low-rank output
 projection of the csa64k batch's 4 tokens: 64 heads in 8 groups -> 8 x 1024
 -> 4096), csa64k_stream (the csa64k step as a streaming loop: positions and
 entry counts advanced on the device, the new token's window row written into
@@ -127,9 +127,7 @@ class Step:
         elif kind == "swa":
             W = g["W"]
             self.out = torch.empty_like(g["q"])
-            self.pool0 = torch.empty((B, 0, D), dtype=torch.bfloat16, device="cuda")
-            self.idx0 = torch.empty((B, 1, 0), dtype=torch.int32, device="cuda")
-            n = L.csa_attn_ws_bytes(B, 1, g["H"], D, W)
+            n = L.swa_decode_attn_ws_bytes(B, g["H"], D, W)
             self.ws_a = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
         elif kind == "compress_stream":
             self.pool = torch.empty((B, g["N"], D), dtype=torch.bfloat16, device="cuda")
@@ -271,18 +269,15 @@ class Step:
                          bias_a=g["ibias_a"], bias_b=g["ibias_b"], out=self.keys)]
             return [("compress", lambda: L.csa_compress_batch(jobs, g["m"], pos0=g["pos0"]))]
         if kind == "swa":
-            D, W, win = g["D"], g["W"], g["win"]
+            # one call: the new token's window row (m = 1), written over the
+            # last row of the window by the attention launch's last split,
+            # and the attention over the window alone
+            W, win = g["W"], g["win"]
             return [
-                # the new token's window row (m = 1), written over the last
-                # row of the window, then attention over the window alone
-                ("window_row", lambda: L.csa_compress(g["kv"], 1, gain=g["gain"],
-                                                      rope_dims=g["R"], pos0=g["q_pos0"],
-                                                      out=win[:, W - 1:], out_bstride=W * D,
-                                                      ws=self.cws(g["kv"], 1, False))),
-                ("sparse_attn", lambda: L.csa_sparse_attn(g["q"], self.pool0, self.idx0, win,
-                                                          g["win_pos0"], W, g["sink"],
-                                                          g["q_pos0"], rope_dims=g["R"],
-                                                          out=self.out, ws=self.ws_a)),
+                ("swa_step", lambda: L.swa_decode_attn(g["q"], g["kv"], g["gain"], win,
+                                                       g["win_pos0"], W, g["sink"], g["q_pos0"],
+                                                       rope_dims=g["R"], out=self.out,
+                                                       ws=self.ws_a)),
             ]
         if kind in HCA:
             # one call: the closing block's entry (pooled by the attention
@@ -401,10 +396,13 @@ def algorithmic(kind, d):
         out["flops"] = {}
         out["compress"] = {"bytes": byt, "flops": 0}
     elif kind == "swa":
-        attn = B * (W * D * bf + 2 * H * D * bf)
-        out["bytes"] = {"window_row": B * 2 * D * bf, "sparse_attn": attn}
-        out["flops"] = {"sparse_attn": B * 4 * H * D * W}
-        out["sparse_attn"] = {"bytes": attn, "flops": out["flops"]["sparse_attn"]}
+        # the token's kv row in and its window row out, then the window, the
+        # query and the output (one call does both)
+        byt = B * 2 * D * bf + B * (W * D * bf + 2 * H * D * bf)
+        fl = B * 4 * H * D * W
+        out["bytes"] = {"swa_step": byt}
+        out["flops"] = {"swa_step": fl}
+        out["swa_step"] = {"bytes": byt, "flops": fl}
     elif kind in HCA:
         N = d["N"]
         # the closing block's two streams in, its entry out (the bias, shared
@@ -458,6 +456,8 @@ DOMINANT_KERNELS = {
     "index_scores": ["index_prefill"],
     "hca_step": ["attn_hs<false, true, 4> (its last split pools the closing block)",
                  "attn_combine<bf16>"],
+    "swa_step": ["attn_hs<false, false, 2> (its last split builds the token's window row)",
+                 "attn_combine<bf16>"],
     "sparse_attn": ["attn_hs<true, *> (+ attn_combine<bf16> when split)"],
     "output_proj": ["proj_rows<4>", "proj_rows<8>"],
     "output_proj_gemm": ["proj_gemm<0>", "proj_gemm<1>"],
@@ -467,6 +467,7 @@ KERNEL_SOURCES = {
     "index_decode_fresh": ["indexer.hip", "common.h", "kernels.h"],
     "index_scores": ["indexer.hip", "common.h", "kernels.h"],
     "hca_step": ["attn.hip", "common.h", "kernels.h"],
+    "swa_step": ["attn.hip", "common.h", "kernels.h"],
     "sparse_attn": ["attn.hip", "common.h", "kernels.h"],
     "output_proj": ["oproj.hip", "oproj.h", "common.h", "kernels.h"],
     "compress": ["compress.hip", "common.h", "kernels.h"],

@@ -60,11 +60,12 @@ UNIT_KERNELS = {
     # prefill: the scoring kernel of the step's index_topk call
     "index_scores": ["index_prefill"],
     "hca_step": ["attn_hs<false,", "attn_combine"],
+    "swa_step": ["attn_hs<false,", "attn_combine"],
     "sparse_attn": ["attn_hs<true,", "attn_combine"],
     "output_proj": ["proj_rows<", "proj_gemm<"],
     "compress": ["compress_rows_kernel<"],
 }
-DOMINANT = {"hca1m": "hca_step", "hca1m_fp8": "hca_step", "swa": "sparse_attn",
+DOMINANT = {"hca1m": "hca_step", "hca1m_fp8": "hca_step", "swa": "swa_step",
             "oproj": "output_proj", "oproj_prefill": "output_proj", "prefill": "index_scores"}
 WORKLOAD_NAME = {"csa64k": "csa_decode_64k", "csa1m": "csa_decode_1m",
                  "hca1m": "hca_decode_1m", "prefill": "csa_prefill_4k_on_60k",

@@ -611,6 +611,46 @@ int hca_decode_attn_kvfp8(int B, int H, int D, int rope_dims, double rope_base, 
  * rows per query (N_cap + W); 0 for shapes it does not take. */
 size_t hca_decode_attn_ws_bytes(int B, int H, int D, int keys_per_query);
 
+/* ---------------------------------------------------------------------------
+ * swa_decode_attn - one decode step of a sliding-window-only layer in one
+ * call: the query token's window row is built and stored, and the query
+ * attends to its window.  The result is that of csa_window_row (or
+ * csa_compress with m = 1 into the window buffer) followed by
+ * csa_sparse_attn with K = 0 and no pool, up to rounding order.
+ *
+ * [P3] "The per-layer pattern" and [P1] "What does layer 0 sliding-window
+ * attention do to p?": the first layers attend to the raw window only, the
+ * query's own token included, with the sink in the softmax (eq. 27 of
+ * [P1]); [P2] section 3.2.2: the window holds the most recent uncompressed
+ * tokens.  The window row of token t is built as csa_compress builds one
+ * with m = 1: RMSNorm(kv) * gain, RoPE at t.
+ *
+ *   q [B, 1, H, D], out [B, 1, H, D], kv [B, 1, D]: bf16
+ *   gain [D] f32 or NULL (no RMSNorm); q_pos0 [B] int64 device: the token's
+ *   position t (the row's RoPE position too)
+ *   win [B, L_win, D] bf16: a ring (win_pos0 NULL, L_win >= W; row
+ *   t % L_win is written) or a linear buffer with win[b, r] the token at
+ *   win_pos0[b] + r (row t - win_pos0[b] is written when it lies in the
+ *   buffer; otherwise nothing is written and the window holds what the
+ *   buffer holds).  Other arguments as csa_sparse_attn.
+ *   ws          workspace of swa_decode_attn_ws_bytes(B, H, D, W)
+ * The last key-range split of each query builds and stores the row and
+ * attends to it alone; the others leave it out.
+ * CSA_ERR_UNSUPPORTED outside the bf16 MFMA shape (H a multiple of 64 up to
+ * 128, D = 512); CSA_ERR_ARG for NULL kv or win, L_win <= 0, W <= 0, a ring
+ * shorter than W, odd or out-of-range rope_dims, a negative eps with a
+ * gain; CSA_ERR_WORKSPACE as csa_sparse_attn.
+ * ------------------------------------------------------------------------- */
+int swa_decode_attn(int B, int H, int D, int rope_dims, double rope_base, float scale,
+                    const void* q, const void* kv, const float* gain, float eps, void* win,
+                    int L_win, const int64_t* win_pos0, int W, const float* sink,
+                    const int64_t* q_pos0, void* out, float* lse, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* Workspace (bytes) for swa_decode_attn over a window of W rows; 0 for
+ * shapes it does not take. */
+size_t swa_decode_attn_ws_bytes(int B, int H, int D, int W);
+
 /* Human-readable name of a csa_status value (static string). */
 const char* csa_status_string(int status);
 

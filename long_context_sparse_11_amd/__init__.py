@@ -36,5 +36,7 @@ from .binding import (  # noqa: F401
     hca_decode_attn,
     hca_decode_attn_kvfp8,
     hca_decode_attn_ws_bytes,
+    swa_decode_attn,
+    swa_decode_attn_ws_bytes,
     lib,
 )

@@ -113,6 +113,12 @@ _SIGS = {
                                    _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_size_t,
                                    _c.c_void_p]),
     "hca_decode_attn_ws_bytes": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int, _c.c_int]),
+    "swa_decode_attn": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_double,
+                                   _c.c_float, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                   _c.c_float, _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int,
+                                   _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                   _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "swa_decode_attn_ws_bytes": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int, _c.c_int]),
     "csa_status_string": (_c.c_char_p, [_c.c_int]),
 }
 
@@ -734,6 +740,43 @@ def hca_decode_attn_kvfp8(q, pool, n_entries, m, c, z, bias, gain, block_pos0, w
     the values read back from its row."""
     return hca_decode_attn(q, pool, n_entries, m, c, z, bias, gain, block_pos0, win, win_pos0, W,
                            sink, q_pos0, _fn="hca_decode_attn_kvfp8", **kw)
+
+
+def swa_decode_attn_ws_bytes(B, H, D, W):
+    return int(lib().swa_decode_attn_ws_bytes(B, H, D, W))
+
+
+def swa_decode_attn(q, kv, gain, win, win_pos0, W, sink, q_pos0, *, rope_dims,
+                    rope_base=10000.0, eps=1e-6, scale=None, want_lse=False, out=None, ws=None,
+                    stream=None):
+    """One window-only decode step (see include/csa.h): the token's window
+    row from kv [B, 1, D] is written into win (its ring slot when win_pos0 is
+    None, else row q_pos0 - win_pos0), and q [B, 1, H, D] attends to the
+    window.  Returns (out, lse)."""
+    B, Tq, H, D = q.shape
+    if Tq != 1:
+        raise ValueError("swa_decode_attn takes one query per sequence")
+    L_win = win.shape[1]
+    _dev(q, kv, gain, win, win_pos0, sink, q_pos0)
+    _f32(sink), _f32(gain), _i64(q_pos0), _i64(win_pos0)
+    for t in (q, kv, win):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("q, kv and win are bf16")
+    if tuple(kv.shape) != (B, 1, D):
+        raise ValueError("kv must be [B, 1, D]")
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device) if want_lse else None
+    need = swa_decode_attn_ws_bytes(B, H, D, W)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib().swa_decode_attn(B, H, D, int(rope_dims), float(rope_base), float(scale), _p(q),
+                               _p(kv), _p(gain), float(eps), _p(win), L_win, _p(win_pos0),
+                               int(W), _p(sink), _p(q_pos0), _p(out), _p(lse), _p(ws),
+                               0 if ws is None else ws.numel(), _stream(stream))
+    _check(st, "swa_decode_attn")
+    return out, lse
 
 
 # ------------------------------------------------- mixed BF16 / FP8 KV rows

@@ -744,3 +744,36 @@ CSA_EXPORT int hca_decode_attn_kvfp8(int B, int H, int D, int rope_dims, double 
                            z, bias, gain, eps, block_pos0, win, L_win, win_pos0, W, sink, q_pos0,
                            out, lse, ws, ws_bytes, (hipStream_t)stream, true);
 }
+
+// The window-only decode step in one call: the query token's window row
+// (the compressor with m = 1) and the attention over the window, through
+// the kernels of the HCA path (no pool, no selected indices: with csa set,
+// the key list is the K = 0 selection plus the window).
+CSA_EXPORT size_t swa_decode_attn_ws_bytes(int B, int H, int D, int W) {
+  if (B <= 0 || W <= 0 || !attn_uses_mfma(CSA_BF16, H, D, 0)) return 0;
+  return attn_fresh_ws_bytes(B, H, D, W);
+}
+
+CSA_EXPORT int swa_decode_attn(int B, int H, int D, int rope_dims, double rope_base, float scale,
+                               const void* q, const void* kv, const float* gain, float eps,
+                               void* win, int L_win, const int64_t* win_pos0, int W,
+                               const float* sink, const int64_t* q_pos0, void* out, float* lse,
+                               void* ws, size_t ws_bytes, void* stream) {
+  if (!kv || !win || L_win <= 0 || W <= 0) return CSA_ERR_ARG;
+  if (gain && !(eps >= 0.f)) return CSA_ERR_ARG;
+  if (rope_dims < 0 || rope_dims > D || (rope_dims & 1)) return CSA_ERR_ARG;
+  if (!win_pos0 && L_win < W) return CSA_ERR_ARG;  // a ring holds the whole window
+  if (!attn_uses_mfma(CSA_BF16, H, D, rope_dims)) return CSA_ERR_UNSUPPORTED;
+  AttnArgs a{};
+  a.dt = CSA_BF16; a.B = B; a.Tq = 1; a.H = H; a.D = D; a.R = rope_dims;
+  a.scale = scale;
+  a.q = q; a.pool = nullptr; a.N_cap = 0; a.csa = 1; a.idx = nullptr; a.K = 0;
+  a.n_entries = nullptr; a.m = 1;
+  a.win = win; a.L_win = L_win; a.win_pos0 = win_pos0; a.W = W;
+  a.sink = sink; a.q_pos0 = q_pos0; a.out = out; a.lse = lse;
+  a.fresh = 2;
+  a.fj.dt = CSA_BF16; a.fj.B = B; a.fj.T = 1; a.fj.D = D; a.fj.m = 1; a.fj.n_out = 1;
+  a.fj.c_a = kv; a.fj.gain = gain; a.fj.eps = eps; a.fj.rope_dims = rope_dims;
+  a.fj.pos0 = q_pos0;
+  return attn_common(a, rope_base, W, ws, ws_bytes, (hipStream_t)stream);
+}

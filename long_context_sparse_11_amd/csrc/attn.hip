@@ -233,64 +233,128 @@ __device__ __forceinline__ int fresh_entry_row(const AttnArgs& a, int b) {
   return a.fj.pos0[b] >= 0 ? min(a.n_entries[b], a.N_cap) - 1 : -1;
 }
 
-// The closing block of an HCA decode step, handled by the last split of its
-// query inside the attention launch (hca_decode_attn): the block is pooled
-// beside the other splits' tile loops instead of in launches of its own ahead
-// of them.  "DeepSeek-v4 Beyond Basics" section 3.3 (eqs. 20-23): the entry
-// is the softmax-weighted pool of the block's m rows per channel, then
-// RMSNorm with its gain and RoPE at the block's first position; the same
-// section (eq. 26): it is attended like every other visible entry.
+// Row of the window buffer that holds the token at tpos (its ring slot, or
+// its offset from win_pos0[b]), or -1 when the buffer does not hold it.
+__device__ __forceinline__ int window_slot(const AttnArgs& a, int b, int64_t tpos) {
+  if (a.L_win <= 0 || tpos < 0) return -1;
+  if (!a.win_pos0) return (int)(tpos % a.L_win);
+  const int64_t r = tpos - a.win_pos0[b];
+  return (r >= 0 && r < a.L_win) ? (int)r : -1;
+}
+
+// The new row of a decode step, handled by the last split of its query
+// inside the attention launch: hca_decode_attn's closing block, pooled
+// beside the other splits' tile loops instead of in launches of its own
+// ahead of them, or swa_decode_attn's token row.  "DeepSeek-v4 Beyond
+// Basics" section 3.3 (eqs. 20-23): an HCA entry is the softmax-weighted
+// pool of the block's m rows per channel, then RMSNorm with its gain and
+// RoPE at the block's first position; a window row is the same with m = 1
+// (its one row, normalised and rotated at its own position); the same
+// section (eq. 26): the row is attended like every other visible one.
 //
 // Wave w pools rows w, w + NW, ... with an online softmax per channel (lane l
-// holds channels 8l .. 8l + 7; eight rows' loads in flight per wave); the
-// waves' partials merge through LDS and wave 0 finishes the entry:
-// normalises, applies the gain, rotates, stores it to the pool (head group
-// 0 only; bf16, or a packed mixed BF16 / FP8 row) and leaves in LDS the bf16
-// values a reader of the stored row gets back.  The split's partial is
-// that one row: per head, the logit q'.row (q' the query rotated at tpos and
-// rounded to bf16, as the tile loop uses it) as the running maximum, a sum
-// of 1, and the row with its rope slice rotated back by -tpos as the
-// unnormalised output.  With no closing block, or an entry the query does
-// not see, the partial is empty (maximum -inf, sum 0, zero output); the
-// other splits leave the entry's row out when the query sees it.
+// holds channels 8l .. 8l + 7; eight rows' loads in flight per wave, the
+// first batch issued before anything else, since its addresses depend on
+// nothing); the waves' partials merge through LDS and wave 0 finishes the
+// row: normalises, applies the gain, rotates, and passes the bf16 values a
+// reader of the stored row gets back to the other waves through LDS.  The
+// split's partial is that one row: per head, the logit q'.row (q' the query
+// rotated at tpos and rounded to bf16, as the tile loop uses it) as the
+// running maximum, a sum of 1, and the row with its rope slice rotated back
+// by -tpos as the unnormalised output, the same for every head.  Lane l
+// keeps its 16-byte chunk l of everything, so each head's query load and
+// partial store is one contiguous 1 KB access per wave, and the 16 heads'
+// logits reduce across the wave in 17 shuffles.  With NW = 2 the query
+// slices go straight into LDS at the start (buffer loads into LDS: no
+// registers held while the rows arrive).  The row is stored (head group 0
+// only; bf16, or a packed mixed BF16 / FP8 row) after the partial.  With
+// no new row, or one the query does not see, the partial is empty (maximum
+// -inf, sum 0, zero output); the other splits leave the row out when the
+// query sees it.
 template <int NW, bool FP8>
-__device__ __forceinline__ void hca_fresh_split(const AttnArgs& a, int b, int qi, int sp, int S,
-                                                float* s_f, bf16_t* s_row, bf16_t* s_out,
-                                                float* s_cos, float* s_sin) {
+__device__ __forceinline__ void fresh_split(const AttnArgs& a, int b, int qi, int sp, int S,
+                                            bf16_t* s_q, bf16_t* s_buf) {
+  // s_buf (32 KB) holds the waves' pooling partials, the row and four rope
+  // tables; the barriers below order every LDS hand-over, so NW > 1
+  static_assert(NW > 1 && NW * 6144 + 5120 <= kHsRows * kAtD * 2, "fresh split LDS layout");
   const CompressArgs& f = a.fj;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m = f.m, c0 = 8 * lane;
+  const bool hz = f.z_a != nullptr, hb = f.bias_a != nullptr;
+  const bf16_t* cbase = (const bf16_t*)f.c_a + (int64_t)b * m * kAtD + c0;
+  const bf16_t* zbase = hz ? (const bf16_t*)f.z_a + (int64_t)b * m * kAtD + c0 : cbase;
+  // the optional streams' words start at zero once (a skipped load leaves
+  // them defined), and every load of a batch goes out before any arithmetic
+  u32x4_t cw[8], zw[8], bw[8][2];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    zw[u] = u32x4_t{0u, 0u, 0u, 0u};
+    bw[u][0] = bw[u][1] = u32x4_t{0u, 0u, 0u, 0u};
+  }
+  auto issue = [&](int r0) {  // rows r0, r0 + NW, ... (8 of them; past m, r0 again)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = r0 + u * NW;
+      const int64_t ro = (int64_t)(r < m ? r : r0) * kAtD;
+      Elem<bf16_t>::template load_raw_stream<8>(cbase + ro, &cw[u]);
+      if (hz) Elem<bf16_t>::template load_raw_stream<8>(zbase + ro, &zw[u]);
+      if (hb) Elem<float>::template load_raw<8>(f.bias_a + ro + c0, bw[u]);
+    }
+  };
+  if (wave < m) issue(wave);  // [B, m, D] rows: in bounds whether or not a row is new
+
+  // this wave's 16 heads: head 16 (NW z + wave) + k, its query slice at
+  // q + (qi H + h) D; with NW = 2, k-th slice into LDS row 16 wave + k
+  const int hw = 16 * (NW * (int)blockIdx.z + wave);
+  const bf16_t* qbase = (const bf16_t*)a.q + ((int64_t)qi * a.H + hw) * kAtD;
+  constexpr bool kQLds = NW == 2;  // 32 heads x 1 KB: the 32 KB s_q holds them
+  if constexpr (kQLds) {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)qbase, (short)0, 16 * kAtD * 2, kRawBufferWord3);
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)(s_q + (16 * wave + k) * kAtD),
+                                               16, 16 * lane + 1024 * k, 0, 0, 0);
+  }
+
   const int R = a.R, rope0 = kAtD - R;
   const int64_t tpos = a.q_pos0[b];  // one query per sequence
   const int64_t bp = f.pos0[b];
-  const int row = fresh_entry_row(a, b);
-  const bool vis = row >= 0 && row == key_range(a, b, qi, tpos).nsel - 1;
-  for (int p = tid; p < R / 2; p += 64 * NW) rope_cos_sin(tpos, p, a.rope_theta1, s_cos[p], s_sin[p]);
+  // the new row: a pool entry (the closing block's), or the query token's
+  // own window row (always the last of its window)
+  const bool win_row = a.fresh == 2;
+  const int row = win_row ? window_slot(a, b, tpos) : fresh_entry_row(a, b);
+  // whether the query sees the row: a window row whenever there is a window
+  // (it is the window's last token), a pool entry once the query's position
+  // reaches the entry's last token (all row + 1 entries visible)
+  const bool vis =
+      row >= 0 && (win_row ? a.W > 0 : tpos + 1 >= (int64_t)a.m * (int64_t)(row + 1));
+  // rope tables (one pair per thread, the rows' loads in flight): at tpos
+  // for the query and the rotation back, at bp for the row (a window row's
+  // own position is tpos)
+  float* s_f = reinterpret_cast<float*>(s_buf);  // [NW][3][512]: max, sum, weighted sum
+  bf16_t* s_row = s_buf + NW * 3 * kAtD * 2;     // the row's bf16 values
+  float* s_tc = reinterpret_cast<float*>(s_row + kAtD);
+  float* s_ts = s_tc + kAtD / 2;
+  float* s_ec = win_row ? s_tc : s_ts + kAtD / 2;
+  float* s_es = win_row ? s_ts : s_ec + kAtD / 2;
+  for (int p = tid; p < R / 2; p += 64 * NW) {
+    rope_cos_sin(tpos, p, a.rope_theta1, s_tc[p], s_ts[p]);
+    if (!win_row) rope_cos_sin(bp, p, a.rope_theta1, s_ec[p], s_es[p]);
+  }
+  float gv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gv[e] = 1.f;
+  if (wave == 0 && f.gain) Elem<float>::template load<8>(f.gain + c0, gv);
 
+  float y[8];
+  u32x4_t ent = u32x4_t{0u, 0u, 0u, 0u};
   if (row >= 0) {
-    const int m = f.m, c0 = 8 * lane;
-    const bool hz = f.z_a != nullptr, hb = f.bias_a != nullptr;
-    const bf16_t* cbase = (const bf16_t*)f.c_a + (int64_t)b * m * kAtD + c0;
-    const bf16_t* zbase = hz ? (const bf16_t*)f.z_a + (int64_t)b * m * kAtD + c0 : cbase;
     float mx[8], den[8], acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) { mx[e] = -INFINITY; den[e] = 0.f; acc[e] = 0.f; }
-    // the optional streams' words start at zero once (a skipped load leaves
-    // them defined), and every load of a batch goes out before any arithmetic
-    u32x4_t cw[8], zw[8], bw[8][2];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      zw[u] = u32x4_t{0u, 0u, 0u, 0u};
-      bw[u][0] = bw[u][1] = u32x4_t{0u, 0u, 0u, 0u};
-    }
     for (int r0 = wave; r0 < m; r0 += 8 * NW) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int r = r0 + u * NW;
-        const int64_t ro = (int64_t)(r < m ? r : r0) * kAtD;
-        Elem<bf16_t>::template load_raw_stream<8>(cbase + ro, &cw[u]);
-        if (hz) Elem<bf16_t>::template load_raw_stream<8>(zbase + ro, &zw[u]);
-        if (hb) Elem<float>::template load_raw<8>(f.bias_a + ro + c0, bw[u]);
-      }
+      if (r0 != wave) issue(r0);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (r0 + u * NW >= m) break;
@@ -310,18 +374,20 @@ __device__ __forceinline__ void hca_fresh_split(const AttnArgs& a, int b, int qi
         }
       }
     }
-    float* mine = s_f + wave * 3 * kAtD;  // [NW][3][512]: max, sum, weighted sum
+    if constexpr (NW > 1) {
+      float* mine = s_f + wave * 3 * kAtD;
 #pragma unroll
-    for (int e = 0; e < 8; e += 4) {
-      *reinterpret_cast<f32x4_t*>(mine + c0 + e) = f32x4_t{mx[e], mx[e + 1], mx[e + 2], mx[e + 3]};
-      *reinterpret_cast<f32x4_t*>(mine + kAtD + c0 + e) =
-          f32x4_t{den[e], den[e + 1], den[e + 2], den[e + 3]};
-      *reinterpret_cast<f32x4_t*>(mine + 2 * kAtD + c0 + e) =
-          f32x4_t{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+      for (int e = 0; e < 8; e += 4) {
+        *reinterpret_cast<f32x4_t*>(mine + c0 + e) = f32x4_t{mx[e], mx[e + 1], mx[e + 2], mx[e + 3]};
+        *reinterpret_cast<f32x4_t*>(mine + kAtD + c0 + e) =
+            f32x4_t{den[e], den[e + 1], den[e + 2], den[e + 3]};
+        *reinterpret_cast<f32x4_t*>(mine + 2 * kAtD + c0 + e) =
+            f32x4_t{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+      }
+      __syncthreads();
     }
-    __syncthreads();
     if (wave == 0) {
-      for (int w = 1; w < NW; ++w) {
+      for (int w = 1; w < NW && w < m; ++w) {
         const float* o = s_f + w * 3 * kAtD;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -334,12 +400,9 @@ __device__ __forceinline__ void hca_fresh_split(const AttnArgs& a, int b, int qi
           mx[e] = M;
         }
       }
-      float y[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[e] = acc[e] / den[e];
       if (f.gain) {
-        float gv[8];
-        Elem<float>::template load<8>(f.gain + c0, gv);
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss += y[e] * y[e];
@@ -349,97 +412,110 @@ __device__ __forceinline__ void hca_fresh_split(const AttnArgs& a, int b, int qi
         for (int e = 0; e < 8; ++e) y[e] = y[e] * inv * gv[e];
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {  // the entry's rotation, at the block's first position
+      for (int k = 0; k < 4; ++k) {  // the row's rotation, at its own position
         const int c = c0 + 2 * k;
         if (c >= rope0) {
-          float cs, sn;
-          rope_cos_sin(bp, (c - rope0) >> 1, a.rope_theta1, cs, sn);
+          const float cs = s_ec[(c - rope0) >> 1], sn = s_es[(c - rope0) >> 1];
           const float x0 = y[2 * k], x1 = y[2 * k + 1];
           y[2 * k] = x0 * cs - x1 * sn;
           y[2 * k + 1] = x0 * sn + x1 * cs;
         }
       }
-      // the row as stored, and the bf16 values a reader of it gets back
-      u32x4_t ent;
+      // the bf16 values a reader of the stored row gets back
       if constexpr (FP8) {
-        if (blockIdx.z == 0)
-          store_kv_fp8_row((uint8_t*)a.pool + ((int64_t)b * a.N_cap + row) * a.pool_row_bytes,
-                           lane, y, R);
-        ent = kv_fp8_row_values(lane, y, R);
+        ent = win_row ? u32x4_t{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                                pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])}
+                      : kv_fp8_row_values(lane, y, R);
       } else {
 #pragma unroll
         for (int k = 0; k < 4; ++k) ent[k] = pack_bf16x2(y[2 * k], y[2 * k + 1]);
-        if (blockIdx.z == 0)
-          *reinterpret_cast<u32x4_t*>((bf16_t*)a.pool + ((int64_t)b * a.N_cap + row) * kAtD + c0) = ent;
       }
-      // those values, rotated back by -tpos, are the split's output
-      u32x4_t outw;
+      if constexpr (NW > 1) *reinterpret_cast<u32x4_t*>(s_row + c0) = ent;
+    }
+  }
+  if constexpr (kQLds) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the query slices
+  if constexpr (NW > 1) __syncthreads();
+  if (row >= 0 && wave != 0) ent = *reinterpret_cast<const u32x4_t*>(s_row + c0);
+
+  // the row rotated back by -tpos: this lane's chunk of every head's output
+  u32x4_t outw = u32x4_t{0u, 0u, 0u, 0u};
+  float s[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) s[k] = 0.f;
+  if (vis) {
+    float tcs[4], tsn[4];  // this lane's rope pairs at tpos
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int pj = max(0, (c0 + 2 * k - rope0) >> 1);
+      tcs[k] = c0 + 2 * k >= rope0 ? s_tc[pj] : 1.f;
+      tsn[k] = c0 + 2 * k >= rope0 ? s_ts[pj] : 0.f;
+    }
+    // the query slices (NW = 4: loaded now), one 16-byte chunk per head
+    u32x4_t qc[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if constexpr (kQLds)
+        qc[k] = *reinterpret_cast<const u32x4_t*>(s_q + (16 * wave + k) * kAtD + c0);
+      else
+        qc[k] = *reinterpret_cast<const u32x4_t*>(qbase + k * kAtD + c0);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float o0 = __uint_as_float(ent[k] << 16), o1 = __uint_as_float(ent[k] & 0xffff0000u);
+      if (c0 + 2 * k >= rope0) {
+        const float t0 = o0 * tcs[k] + o1 * tsn[k], t1 = -o0 * tsn[k] + o1 * tcs[k];
+        o0 = t0;
+        o1 = t1;
+      }
+      outw[k] = pack_bf16x2(o0, o1);
+    }
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int c = c0 + 2 * k;
-        float o0 = __uint_as_float(ent[k] << 16), o1 = __uint_as_float(ent[k] & 0xffff0000u);
-        if (c >= rope0) {
-          const int pj = (c - rope0) >> 1;
-          const float cs = s_cos[pj], sn = s_sin[pj];
-          const float t0 = o0 * cs + o1 * sn, t1 = -o0 * sn + o1 * cs;
-          o0 = t0;
-          o1 = t1;
+        uint32_t qj = qc[h][k];
+        if (c0 + 2 * k >= rope0) {
+          const float x0 = __uint_as_float(qj << 16), x1 = __uint_as_float(qj & 0xffff0000u);
+          qj = pack_bf16x2(x0 * tcs[k] - x1 * tsn[k], x0 * tsn[k] + x1 * tcs[k]);
         }
-        outw[k] = pack_bf16x2(o0, o1);
+        s[h] += __uint_as_float(qj << 16) * __uint_as_float(ent[k] << 16) +
+                __uint_as_float(qj & 0xffff0000u) * __uint_as_float(ent[k] & 0xffff0000u);
       }
-      *reinterpret_cast<u32x4_t*>(s_row + c0) = ent;
-      *reinterpret_cast<u32x4_t*>(s_out + c0) = outw;
     }
   }
-  __syncthreads();
+  // 16 sums over 64 lanes: each xor step halves the values a lane keeps
+  // (bit j of the lane picks the half), then two plain steps; lane l ends
+  // with head l & 15's logit
+#pragma unroll
+  for (int j = 0, n = 16; n > 1; ++j, n >>= 1) {
+    const bool hi = (lane >> j) & 1;
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) {
+      const float keep = hi ? s[2 * i + 1] : s[2 * i], give = hi ? s[2 * i] : s[2 * i + 1];
+      s[i] = keep + __shfl_xor(give, 1 << j);
+    }
+  }
+  s[0] += __shfl_xor(s[0], 16);
+  s[0] += __shfl_xor(s[0], 32);
+  const int64_t slot0 = ((int64_t)qi * S + sp) * a.H + hw;
+  if (lane < 16)
+    *reinterpret_cast<float2*>(a.part_ml + 2 * (slot0 + lane)) =
+        vis ? make_float2(s[0] * a.scale * kLog2e, 1.f) : make_float2(-INFINITY, 0.f);
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    *reinterpret_cast<u32x4_t*>(a.part_o + (slot0 + k) * kAtD + c0) = outw;
 
-  // per head: thread (head hl, channel quarter qt)
-  const int hl = tid >> 2, qt = tid & 3;
-  const int h = 16 * NW * (int)blockIdx.z + hl;
-  const int64_t slot = ((int64_t)qi * S + sp) * a.H + h;
-  u32x4_t* po = reinterpret_cast<u32x4_t*>(a.part_o + slot * kAtD + 128 * qt);
-  if (!vis) {
-    if (qt == 0) {
-      a.part_ml[2 * slot] = -INFINITY;
-      a.part_ml[2 * slot + 1] = 0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) po[k] = u32x4_t{0u, 0u, 0u, 0u};
-    return;
-  }
-  const u32x4_t* qp =
-      reinterpret_cast<const u32x4_t*>((const bf16_t*)a.q + ((int64_t)qi * a.H + h) * kAtD + 128 * qt);
-  u32x4_t qw[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) qw[k] = qp[k];
-  float s = 0.f;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int c8 = 128 * qt + 8 * k;
-    const u32x4_t rw = *reinterpret_cast<const u32x4_t*>(s_row + c8);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = c8 + 2 * j;
-      uint32_t qj = qw[k][j];
-      if (c >= rope0) {
-        const int pj = (c - rope0) >> 1;
-        const float cs = s_cos[pj], sn = s_sin[pj];
-        const float x0 = __uint_as_float(qj << 16), x1 = __uint_as_float(qj & 0xffff0000u);
-        qj = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
-      }
-      s += __uint_as_float(qj << 16) * __uint_as_float(rw[j] << 16) +
-           __uint_as_float(qj & 0xffff0000u) * __uint_as_float(rw[j] & 0xffff0000u);
+  // the row itself, last: nothing in this launch reads it back
+  if (row >= 0 && wave == 0 && blockIdx.z == 0) {
+    if (win_row) {
+      *reinterpret_cast<u32x4_t*>((bf16_t*)a.win + ((int64_t)b * a.L_win + row) * kAtD + c0) = ent;
+    } else if constexpr (FP8) {
+      store_kv_fp8_row((uint8_t*)a.pool + ((int64_t)b * a.N_cap + row) * a.pool_row_bytes, lane,
+                       y, R);
+    } else {
+      *reinterpret_cast<u32x4_t*>((bf16_t*)a.pool + ((int64_t)b * a.N_cap + row) * kAtD + c0) = ent;
     }
   }
-  s += __shfl_xor(s, 1);
-  s += __shfl_xor(s, 2);
-  if (qt == 0) {
-    a.part_ml[2 * slot] = s * a.scale * kLog2e;
-    a.part_ml[2 * slot + 1] = 1.f;
-  }
-  const u32x4_t* so = reinterpret_cast<const u32x4_t*>(s_out + 128 * qt);
-#pragma unroll
-  for (int k = 0; k < 16; ++k) po[k] = so[k];
 }
 
 // NW: waves per workgroup, 16 heads each.  With NW = 4 the workgroup takes
@@ -493,12 +569,11 @@ void attn_hs(AttnArgs a) {
   // others divide the key list among themselves
   if constexpr (!CSA) {
     if (a.fresh && sp == S - 1) {
-      hca_fresh_split<NW, FP8>(a, b, qi, sp, S, reinterpret_cast<float*>(s_rows0), s_rows1,
-                               s_rows1 + kAtD, s_cos, s_sin);
+      fresh_split<NW, FP8>(a, b, qi, sp, S, s_rows0, s_rows1);
       return;
     }
   }
-  const int Sa = S - a.fresh;
+  const int Sa = S - ((!CSA && a.fresh) ? 1 : 0);  // splits over the key list
 
   // ---- split bounds (CSA: a fixed range of [K selected, up to
   // min(W, L_win) window rows], known before the position)
@@ -527,9 +602,11 @@ void attn_hs(AttnArgs a) {
   KeyRange kr = key_range(a, b, qi, tpos);
   if constexpr (!CSA) {
     // the closing block's entry, when the query sees it, is the last split's
-    if (a.fresh) {
+    if (a.fresh == 1) {
       const int row = fresh_entry_row(a, b);
       if (row >= 0 && row == kr.nsel - 1) kr.nsel -= 1;
+    } else if (a.fresh == 2) {  // the token's own window row: the last one
+      if (window_slot(a, b, tpos) >= 0 && kr.nwin > 0) kr.nwin -= 1;
     }
   }
   if (!CSA) {
@@ -1039,13 +1116,17 @@ size_t attn_ws_bytes(int dt, int B, int Tq, int H, int D, int keys_per_query) {
   return (size_t)B * Tq * s * H * (2 * sizeof(float) + (size_t)D * sizeof(bf16_t));
 }
 
-// HCA decode step with the closing block's entry (bf16, the Flash shape,
-// one query per sequence): as many splits as hca_attn takes, the last one
-// given to the entry, so the grid keeps its one workgroup per compute unit.
-// (One split more per query, 272 workgroups at batch 16, put two on some
-// compute units: the 1M-token step took 59 us against 48.)
+// Decode steps with a new row (bf16, the Flash shape, one query per
+// sequence): the key list's splits plus one for the new row while the grid
+// still fits the compute units once (the window-only decode: 4 + 1 splits
+// of 16 queries); past that, as many splits as without it, the last one
+// given to the new row, so the grid keeps its one workgroup per compute
+// unit (one split more per query, 272 workgroups for the 1M-token HCA step
+// at batch 16, put two on some compute units: 59 us against 48).
 int attn_fresh_splits(int B, int H, int D, int keys_per_query) {
-  return max(2, attn_splits(1, B, 1, H, D, keys_per_query));
+  const int s = attn_splits(1, B, 1, H, D, keys_per_query);
+  if ((int64_t)B * (H / kAtH) * (s + 1) <= 256) return min(s + 1, kMaxSplits);
+  return max(2, s);
 }
 
 size_t attn_fresh_ws_bytes(int B, int H, int D, int keys_per_query) {
@@ -1074,7 +1155,7 @@ template <bool FP8, int RC>
 static void launch_hs_single(const AttnArgs& a, bool halves, dim3 grid, dim3 grid2,
                              hipStream_t stream) {
   const dim3 block4(256), block2(128);
-  if (a.csa) {
+  if (a.csa && !a.fresh) {
     if (halves) hipLaunchKernelGGL((attn_hs<true, false, 2, FP8, RC>), grid2, block2, 0, stream, a);
     else hipLaunchKernelGGL((attn_hs<true, false, 4, FP8, RC>), grid, block4, 0, stream, a);
   } else {
@@ -1088,7 +1169,7 @@ static void launch_hs(const AttnArgs& a, bool multi, bool halves, dim3 grid, dim
                       hipStream_t stream) {
   if (multi) {
     const dim3 block4(256);
-    if (a.csa) hipLaunchKernelGGL((attn_hs<true, true, 4, FP8>), grid, block4, 0, stream, a);
+    if (a.csa && !a.fresh) hipLaunchKernelGGL((attn_hs<true, true, 4, FP8>), grid, block4, 0, stream, a);
     else hipLaunchKernelGGL((attn_hs<false, true, 4, FP8>), grid, block4, 0, stream, a);
   } else if (a.R == kRopeFixed) {
     launch_hs_single<FP8, kRopeFixed>(a, halves, grid, grid2, stream);
@@ -1097,6 +1178,9 @@ static void launch_hs(const AttnArgs& a, bool multi, bool halves, dim3 grid, dim
   }
 }
 
+// A step with a new row runs the kernels without selected indices (the ones
+// with the new-row split); the window-only step sets csa with K = 0, so that
+// their key list is the window alone.
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.B * a.Tq == 0) return hipSuccess;
   if (attn_uses_mfma(a.dt, a.H, a.D, a.R)) {
@@ -1105,7 +1189,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
     // most rows a split can hold: the list length bound over the split count
     const int wc = (a.W > 0 && a.L_win > 0) ? min(a.W, a.L_win) : 0;
     const int64_t lmax = (a.csa ? (int64_t)a.K : (int64_t)a.N_cap) + wc;
-    const int sa = a.splits - a.fresh;  // splits over the key list
+    const int sa = a.splits - (a.fresh ? 1 : 0);  // splits over the key list
     const bool multi = (lmax + sa - 1) / sa > kHsRows;
     // single-tile splits in head groups of 32 (two waves, grid z) while the
     // doubled grid still fits the compute units once

@@ -228,11 +228,13 @@ struct AttnArgs {
   int splits;           // key-range splits per query (1 = no combine pass)
   float* part_ml;       // [B*Tq, splits, H, 2] when splits > 1: (max, sum)
   bf16_t* part_o;       // [B*Tq, splits, H, D] unnormalised split outputs
-  // HCA decode step (hca_decode_attn(_kvfp8); Tq = 1, the MFMA shape): the
-  // last split of each query is the closing block's new entry, pooled by
-  // that split's workgroup from job fj (T = m, one entry per sequence, to
-  // row min(n_entries[b], N_cap) - 1 when fj.pos0[b] >= 0) and counted as a
-  // split of one row; the other splits leave that row out
+  // Decode steps with a new row (Tq = 1, the MFMA shape; the kernels without
+  // selected indices): the last split of each query computes the row from
+  // job fj and counts as a split of that one row, the other splits leave it
+  // out.  fresh 1 (hca_decode_attn(_kvfp8)): the closing block's entry
+  // (T = m, one entry per sequence), to pool row min(n_entries[b], N_cap) - 1
+  // when fj.pos0[b] >= 0.  fresh 2 (swa_decode_attn): the query token's own
+  // window row (m = 1, at fj.pos0[b] = q_pos0[b]), to its window buffer row.
   int fresh;
   CompressArgs fj;
 };

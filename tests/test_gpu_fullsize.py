@@ -351,24 +351,31 @@ def test_hca_decode_1m_sampled_sequences(mode):
 # ---------------------------------------------------------------------------
 # Sliding-window-only decode (layers with no compressed entries)
 # ---------------------------------------------------------------------------
-def test_swa_decode_window_only():
+@pytest.mark.parametrize("one_call", [True, False])
+def test_swa_decode_window_only(one_call):
     """The new token's window row (m = 1: RMSNorm, gain, RoPE at its
     position) written over the window's last row, then attention over the
-    128-token window alone (no pool, K = 0), batch 16 at position 2^20 - 1."""
+    128-token window alone (no pool, K = 0), batch 16 at position 2^20 - 1:
+    as the benchmark times it (swa_decode_attn, one call) and as two calls."""
     d = synth.swa_decode(0)
     B, D, W, R = d["B"], d["D"], d["W"], d["R"]
     win = dev(d["win"])
     before = win.clone()
-    print(f"[swa] B={B}: window row + window attention", flush=True)
-    L.csa_compress(dev(d["kv"]), 1, gain=dev(d["gain"]), rope_dims=R, pos0=i64(d["q_pos0"]),
-                   out=win[:, W - 1:], out_bstride=W * D)
-    pool0 = torch.empty((B, 0, D), dtype=torch.bfloat16, device="cuda")
-    idx0 = torch.empty((B, 1, 0), dtype=torch.int32, device="cuda")
-    ws_a = torch.empty(max(L.csa_attn_ws_bytes(B, 1, d["H"], D, W), 1), dtype=torch.uint8,
-                       device="cuda")
-    out, lse = L.csa_sparse_attn(dev(d["q"]), pool0, idx0, win, i64(d["win_pos0"]), W,
-                                 dev(d["sink"]), i64(d["q_pos0"]), rope_dims=R, ws=ws_a,
-                                 want_lse=True)
+    print(f"[swa] B={B}: window row + window attention, one call {one_call}", flush=True)
+    if one_call:
+        out, lse = L.swa_decode_attn(dev(d["q"]), dev(d["kv"]), dev(d["gain"]), win,
+                                     i64(d["win_pos0"]), W, dev(d["sink"]), i64(d["q_pos0"]),
+                                     rope_dims=R, want_lse=True)
+    else:
+        L.csa_compress(dev(d["kv"]), 1, gain=dev(d["gain"]), rope_dims=R,
+                       pos0=i64(d["q_pos0"]), out=win[:, W - 1:], out_bstride=W * D)
+        pool0 = torch.empty((B, 0, D), dtype=torch.bfloat16, device="cuda")
+        idx0 = torch.empty((B, 1, 0), dtype=torch.int32, device="cuda")
+        ws_a = torch.empty(max(L.csa_attn_ws_bytes(B, 1, d["H"], D, W), 1), dtype=torch.uint8,
+                           device="cuda")
+        out, lse = L.csa_sparse_attn(dev(d["q"]), pool0, idx0, win, i64(d["win_pos0"]), W,
+                                     dev(d["sink"]), i64(d["q_pos0"]), rope_dims=R, ws=ws_a,
+                                     want_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(win[:, : W - 1], before[:, : W - 1])
     wref = O.csa_compress(d["kv"].f32, None, None, 1, gain=d["gain"], rope_dims=R,

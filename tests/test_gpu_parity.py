@@ -836,6 +836,78 @@ def test_hca_decode_step_matches_separate_calls(H, N):
     assert np.abs(host(lse_f) - host(lse_s)).max() <= 1e-2
 
 
+# ------------------------------------------- window-only decode in one call
+@pytest.mark.parametrize("ring,H,B,pos", [
+    (True, 64, 16, None),                 # the benchmark's shape, deep in the sequence
+    (False, 64, 3, [1000, 50, 0]),        # linear buffer; a short window; the first token
+    (True, 128, 2, [5, 300]),             # two head groups; a window not yet full
+    (False, 64, 2, [400, 9000]),          # linear buffer not holding the token: no row
+])
+def test_swa_decode_step_fused(ring, H, B, pos):
+    """swa_decode_attn: the token's window row (the compressor with m = 1)
+    stored into the window buffer and the attention over the window, against
+    the oracle's compressor and attention, and against the two calls."""
+    rng = np.random.default_rng(77 + H + B)
+    D, R, W = 512, 64, 128
+    q_pos0 = np.array(pos if pos is not None else [(1 << 20) - 1 - 3 * b for b in range(B)],
+                      np.int64)
+    f = lambda *sh: rng.standard_normal(sh).astype(np.float32)
+    q, kv = synth.Tensor(f(B, 1, H, D), "bf16"), synth.Tensor(f(B, 1, D), "bf16")
+    gain = (1.0 + 0.02 * f(D)).astype(np.float32)
+    sink = 0.5 * f(H)
+    if ring:
+        L_win, win_pos0 = W + 8, None
+    else:
+        L_win = W + 5
+        win_pos0 = q_pos0 - W - 2                     # the token sits at row W + 2
+        if pos == [400, 9000]:
+            win_pos0 = q_pos0 - L_win - 2             # past the buffer's end: nothing stored
+    win0 = synth.Tensor(f(B, L_win, D), "bf16")
+    win = dev(win0)
+    out, lse = L.swa_decode_attn(dev(q), dev(kv), dev(gain), win,
+                                 None if win_pos0 is None else i64(win_pos0), W, dev(sink),
+                                 i64(q_pos0), rope_dims=R, want_lse=True)
+    got = host(win)
+    wref = O.csa_compress(kv.f32, None, None, 1, gain=gain, rope_dims=R, pos0=q_pos0)[:, 0]
+    # the oracle: the window positions the buffer holds (all of them for a
+    # ring), the token's own row replaced by the oracle's when it is held
+    ref_win = win0.f32.astype(np.float64)
+    ro = np.zeros((B, 1, H, D))
+    rl = np.zeros((B, 1, H))
+    for b in range(B):
+        t = int(q_pos0[b])
+        slot = t % L_win if ring else t - int(win_pos0[b])
+        keep = np.ones(L_win, bool)
+        if 0 <= slot < L_win:
+            keep[slot] = False
+            assert rowwise_rel_err(got[b, slot:slot + 1], wref[b][None]) <= TOL_BF16
+            ref_win[b, slot] = wref[b]
+        assert np.array_equal(got[b, keep], win0.f32[b, keep])
+        rs = [p % L_win if ring else p - int(win_pos0[b]) for p in O.window_positions(t, W)]
+        rs = [r for r in rs if 0 <= r < L_win]
+        o1, l1 = O.attend(q.f32[b, 0], t, ref_win[b, rs], sink, 1 / math.sqrt(D), R)
+        ro[b, 0], rl[b, 0] = o1, l1
+    assert rowwise_rel_err(host(out), ro) <= TOL_BF16
+    assert np.abs(host(lse) - rl).max() <= LSE_ATOL_BF16
+    # the same step as two calls: the row, then the window-only attention
+    win2 = dev(win0)
+    for b in range(B):
+        t = int(q_pos0[b])
+        slot = t % L_win if ring else t - int(win_pos0[b])
+        if 0 <= slot < L_win:
+            row = L.csa_compress(dev(kv)[b:b + 1], 1, gain=dev(gain), rope_dims=R,
+                                 pos0=i64(q_pos0[b:b + 1]))
+            win2[b, slot] = row[0, 0]
+    o2, l2 = L.csa_sparse_attn(dev(q), torch.empty((B, 0, D), dtype=torch.bfloat16,
+                                                   device="cuda"),
+                               torch.empty((B, 1, 0), dtype=torch.int32, device="cuda"), win2,
+                               None if win_pos0 is None else i64(win_pos0), W, dev(sink),
+                               i64(q_pos0), rope_dims=R, want_lse=True)
+    assert rowwise_rel_err(host(win), host(win2).astype(np.float64)) <= 1e-2
+    assert rowwise_rel_err(host(out), host(o2).astype(np.float64)) <= 1e-2
+    assert np.abs(host(lse) - host(l2)).max() <= 1e-2
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_attn_empty_key_set_is_sink_only(dt):
     """No selected rows and no window: output 0, lse = sink."""

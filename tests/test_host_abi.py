@@ -36,7 +36,7 @@ def test_header_declares_the_four_calls():
               "csa_status_string", "csa_quantize_mxfp4", "csa_index_topk_mxfp4",
               "csa_index_scores_mxfp4", "csa_decode_index_topk_mxfp4", "csa_output_proj",
               "csa_window_row", "csa_decode_advance", "hca_decode_attn",
-              "hca_decode_attn_ws_bytes"):
+              "hca_decode_attn_ws_bytes", "swa_decode_attn", "swa_decode_attn_ws_bytes"):
         assert n in names
 
 
@@ -346,6 +346,30 @@ def test_hca_decode_step_validation(lib):
     assert lib.hca_decode_attn_kvfp8(16, 64, 512, 48, 10000.0, 0.044, P, P, 8192, P, 128, P, P,
                                      N, N, 1e-6, P, P, 128, P, 128, P, P, P, N, P, 1 << 40,
                                      N) == CSA_ERR_UNSUPPORTED
+
+
+def _swa_step(lib, **kw):
+    a = dict(B=16, H=64, D=512, R=64, base=10000.0, scale=0.044, kv=P, gain=N, eps=1e-6, win=P,
+             L_win=128, wp=P, W=128, ws=P, wsb=1 << 40)
+    a.update(kw)
+    return lib.swa_decode_attn(a["B"], a["H"], a["D"], a["R"], a["base"], a["scale"], P, a["kv"],
+                               a["gain"], a["eps"], a["win"], a["L_win"], a["wp"], a["W"], P, P,
+                               P, N, a["ws"], a["wsb"], N)
+
+
+def test_swa_decode_step_validation(lib):
+    assert _swa_step(lib, kv=N) == CSA_ERR_ARG
+    assert _swa_step(lib, win=N) == CSA_ERR_ARG
+    assert _swa_step(lib, L_win=0) == CSA_ERR_ARG
+    assert _swa_step(lib, W=0) == CSA_ERR_ARG
+    assert _swa_step(lib, wp=N, L_win=100) == CSA_ERR_ARG     # a ring shorter than the window
+    assert _swa_step(lib, gain=P, eps=-1.0) == CSA_ERR_ARG
+    assert _swa_step(lib, R=63) == CSA_ERR_ARG
+    assert _swa_step(lib, H=32) == CSA_ERR_UNSUPPORTED
+    assert _swa_step(lib, ws=N) == CSA_ERR_WORKSPACE
+    assert _swa_step(lib, B=0) == CSA_OK
+    # 4 window splits of 16 queries plus the new row's
+    assert lib.swa_decode_attn_ws_bytes(16, 64, 512, 128) == 16 * 5 * 64 * (8 + 2 * 512)
 
 
 def test_kv_fp8_validation(lib):
