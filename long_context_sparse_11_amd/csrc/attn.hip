@@ -258,12 +258,15 @@ __device__ __forceinline__ int window_slot(const AttnArgs& a, int b, int64_t tpo
 // nothing); the waves' partials merge through LDS and wave 0 finishes the
 // row: normalises, applies the gain, rotates, and passes the bf16 values a
 // reader of the stored row gets back to the other waves through LDS.  The
-// split's partial is that one row: per head, the logit q'.row (q' the query
-// rotated at tpos and rounded to bf16, as the tile loop uses it) as the
-// running maximum, a sum of 1, and the row with its rope slice rotated back
-// by -tpos as the unnormalised output, the same for every head.  Lane l
-// keeps its 16-byte chunk l of everything, so each head's query load and
-// partial store is one contiguous 1 KB access per wave, and the 16 heads'
+// split's partial is that one row: the row with its rope slice rotated back
+// by -tpos (rounded to bf16) as the unnormalised output, the same for every
+// head, and per head a sum of 1 and the logit as the running maximum.  The
+// logit q'.row (q' the query rotated at tpos) equals q.(the row rotated back
+// by -tpos): a rotation moves to the other operand of a dot product, so it
+// is the query's dot with that output chunk; it differs from the tile loop's
+// q' rounded to bf16 by rounding alone.  Lane l keeps its 16-byte chunk l of
+// everything, so each head's query load and partial store is one contiguous
+// 1 KB access per wave, the logits are bf16 pair dots, and the 16 heads'
 // logits reduce across the wave in 17 shuffles.  With NW = 2 the query
 // slices go straight into LDS at the start (buffer loads into LDS: no
 // registers held while the rows arrive).  The row is stored (head group 0
@@ -443,12 +446,13 @@ __device__ __forceinline__ void fresh_split(const AttnArgs& a, int b, int qi, in
 #pragma unroll
   for (int k = 0; k < 16; ++k) s[k] = 0.f;
   if (vis) {
-    float tcs[4], tsn[4];  // this lane's rope pairs at tpos
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int pj = max(0, (c0 + 2 * k - rope0) >> 1);
-      tcs[k] = c0 + 2 * k >= rope0 ? s_tc[pj] : 1.f;
-      tsn[k] = c0 + 2 * k >= rope0 ? s_ts[pj] : 0.f;
+    for (int k = 0; k < 4; ++k) {  // this lane's pairs: rotated back where they are rope pairs
+      const int c = c0 + 2 * k, pj = max(0, (c - rope0) >> 1);
+      const float cs = s_tc[pj], sn = s_ts[pj];
+      const float o0 = __uint_as_float(ent[k] << 16), o1 = __uint_as_float(ent[k] & 0xffff0000u);
+      const uint32_t r = pack_bf16x2(o0 * cs + o1 * sn, -o0 * sn + o1 * cs);
+      outw[k] = c >= rope0 ? r : ent[k];
     }
     // the query slices (NW = 4: loaded now), one 16-byte chunk per head
     u32x4_t qc[16];
@@ -459,27 +463,17 @@ __device__ __forceinline__ void fresh_split(const AttnArgs& a, int b, int qi, in
       else
         qc[k] = *reinterpret_cast<const u32x4_t*>(qbase + k * kAtD + c0);
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float o0 = __uint_as_float(ent[k] << 16), o1 = __uint_as_float(ent[k] & 0xffff0000u);
-      if (c0 + 2 * k >= rope0) {
-        const float t0 = o0 * tcs[k] + o1 * tsn[k], t1 = -o0 * tsn[k] + o1 * tcs[k];
-        o0 = t0;
-        o1 = t1;
-      }
-      outw[k] = pack_bf16x2(o0, o1);
-    }
+    // the rotation of the rope pairs moves from the query to the row:
+    // q'.row = q.(row rotated back by -tpos), the output chunk itself, so
+    // each head's logit is 4 two-product bf16 dots per lane
 #pragma unroll
     for (int h = 0; h < 16; ++h) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        uint32_t qj = qc[h][k];
-        if (c0 + 2 * k >= rope0) {
-          const float x0 = __uint_as_float(qj << 16), x1 = __uint_as_float(qj & 0xffff0000u);
-          qj = pack_bf16x2(x0 * tcs[k] - x1 * tsn[k], x0 * tsn[k] + x1 * tcs[k]);
-        }
-        s[h] += __uint_as_float(qj << 16) * __uint_as_float(ent[k] << 16) +
-                __uint_as_float(qj & 0xffff0000u) * __uint_as_float(ent[k] & 0xffff0000u);
+        // copies first: a bit cast of a vector's element would read element 0
+        const uint32_t qj = qc[h][k], oj = outw[k];
+        s[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qj),
+                                               __builtin_bit_cast(bf16x2_t, oj), s[h], false);
       }
     }
   }
