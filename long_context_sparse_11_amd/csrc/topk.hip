@@ -44,9 +44,17 @@ constexpr int kBinsPerThread = kBins / kTkThreads;
 constexpr int kBinCap = 2048;  // most keys of the threshold bin one wave resolves
 static_assert(kTkRounds <= 32, "slot masks are 32 bits");
 
+constexpr int kMaxTopK = 4096;  // largest K a segment selects
 struct TkShared {
-  uint32_t hist[kBins];
-  uint32_t bin[kBinCap];
+  union {
+    struct {
+      uint32_t hist[kBins];
+      uint32_t bin[kBinCap];
+    };
+    // the chosen (index, score) pairs at their output positions, written
+    // once the selection no longer reads hist or bin
+    int2 out[kMaxTopK];
+  };
   uint32_t red[3][kTkWaves];
   uint32_t sel_digit, sel_above, sel_count, fill;
 };
@@ -108,6 +116,8 @@ void topk_kernel(TopkArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int K = a.K;
+  // the scores stay in registers for the first digit where registers allow
+  constexpr bool KEEP_V = !WIDE;
 
   // ---- segment geometry from the arguments alone: the scores are requested
   // before the visible count (two dependent scalar loads) is known.  `cap`
@@ -321,14 +331,29 @@ void topk_kernel(TopkArgs a) {
       if (osc) osc[e] = -INFINITY;
     }
   } else if (linear) {
-    // the linear first digit (recomputed where it is used again: held in
-    // registers it would cost 16 per thread)
+    // the linear first digit, recomputed where it is used again (held in
+    // registers it would cost 16 per thread): one FMA on the score, which
+    // the unconstrained instance keeps in registers (the other converts the
+    // key back).  Monotone in the score: the FMA rounds its exact value
+    // once, and the conversion truncates (a value just below 0 gives 0).
+    const float off = -fmn * scale;
     auto digit = [&](int i) {
-      return (uint32_t)fminf((key_score(key[i]) - fmn) * scale, (float)(kBins - 1));
+      const float x = KEEP_V ? v[i] : key_score(key[i]);
+      return min((uint32_t)fmaf(x, scale, off), (uint32_t)(kBins - 1));
     };
+    if (!CAND && !WIDE) {
+      // a decode select: every slot adds its live bit (0 for a dead slot,
+      // whose digit is any bin), in straight-line code (19.2 -> 18.8 us per
+      // 64K decode call).  The merge of chunk winners and the two-per-CU
+      // instance keep the branch per slot: without it they measured slower
+      // (the 1M merge by ~5 us, a prefill chunk's selects by ~45 us).
 #pragma unroll
-    for (int i = 0; i < kTkRounds; ++i) {
-      if ((live >> i) & 1) atomicAdd(&S.hist[digit(i)], 1u);
+      for (int i = 0; i < kTkRounds; ++i) atomicAdd(&S.hist[digit(i)], (live >> i) & 1u);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kTkRounds; ++i) {
+        if ((live >> i) & 1) atomicAdd(&S.hist[digit(i)], 1u);
+      }
     }
     __syncthreads();
     uint32_t h[kBinsPerThread], local = 0;
@@ -500,16 +525,35 @@ void topk_kernel(TopkArgs a) {
   const uint32_t take = min(neq, (uint32_t)remaining - eq_before);
   uint32_t p = before_gt + eq_before;
   uint32_t seen_eq = 0;
+  // the unconstrained instance gathers the chosen pairs in LDS at their
+  // output positions (hist and bin are no longer read: every thread passed
+  // the prefix count's barrier after its last read), then stores them
+  // coalesced; the two-per-CU instance stores each pair where it is chosen
+  // (the staging's registers cost it spills)
 #pragma unroll
   for (int i = 0; i < kTkRounds; ++i) {
     const bool g = (gt_m >> i) & 1, e = (eq_m >> i) & 1;
     const bool c = g || (e && seen_eq < take);
     seen_eq += e ? 1u : 0u;
     if (c) {
-      oidx[p] = CAND ? vi[CAND ? i : 0] : base_index + e0 + i;
-      if (osc) osc[p] = key_score(key[i]);
+      const int32_t ix = CAND ? vi[CAND ? i : 0] : base_index + e0 + i;
+      const float sc = key_score(key[i]);
+      if (WIDE) {
+        oidx[p] = ix;
+        if (osc) osc[p] = sc;
+      } else {
+        S.out[p] = make_int2(ix, (int)__float_as_uint(sc));
+      }
       ++p;
     }
+  }
+  if (WIDE) return;
+  const int chosen = (int)((total & 0xffffu) + min(total >> 16, (uint32_t)remaining));
+  __syncthreads();
+  for (int e = tid; e < chosen; e += kTkThreads) {
+    const int2 o = S.out[e];
+    oidx[e] = o.x;
+    if (osc) osc[e] = __uint_as_float((uint32_t)o.y);
   }
 }
 
