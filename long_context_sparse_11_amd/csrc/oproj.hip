@@ -89,7 +89,7 @@ __global__ __launch_bounds__(64 * NW) void proj_rows(const bf16_t* x, int64_t x_
 // More than 16 tokens (prefill chunks): each weight serves many tokens, so
 // the products are ordinary GEMMs, C[t, g, n] = sum_k X[t, g, k] W[g, n, k].
 // 1-D grid over the tiles of (group, token tile, weight-row tile), 4 waves
-// as 2 x 2 quadrants of 64 x 64;
+// as 2 x 2 quadrants of (32 MI) tokens x (32 NJ) weight rows;
 // v_mfma_f32_32x32x16_bf16 (lane l: A row = token l % 32, B column = weight
 // row l % 32, K slots 8 (l / 32) .. + 7; accumulator element e of lane l is
 // token 8 (e / 4) + 4 (l / 32) + e % 4, row l % 32).  64-channel steps are
@@ -97,25 +97,33 @@ __global__ __launch_bounds__(64 * NW) void proj_rows(const bf16_t* x, int64_t x_
 // the LDS row pitch of 72 bf16 (144 B) puts the 16 rows a 16-byte read
 // serves in distinct banks.
 //
+// Operand reuse.  Per 16 channels a wave reads MI + NJ 16-byte operands from
+// LDS for MI x NJ MFMAs.  At MI = NJ = 2 (128 x 128 tiles) that is one read
+// per MFMA, more than the LDS delivers to four waves running MFMAs back to
+// back; 256 x 256 tiles (MI = NJ = 4, 256 accumulators per lane, 144 KiB of
+// LDS, one workgroup per compute unit) halve it.
+//
 // Tile order.  Workgroup id goes to XCD id % 8, each XCD with its own L2, so
 // XCD x takes the contiguous range x * per .. of the logical tiles; within a
 // group, logical tiles run over 8 token tiles for each weight-row tile in
 // turn, so the workgroups an XCD runs together share their activation and
 // weight tiles through its L2 instead of fetching them from HBM each.
 constexpr int kGmSwizzle = 8;
-constexpr int kGmTile = 128;
+constexpr int kGmTile = 128;  // the smallest tile (both sides)
 constexpr int kGmK = 64;
 constexpr int kGmPitch = 72;
 
 // STAGE only names the launch (0: grouped product, 1: final product), so the
 // two show up apart in kernel traces.
-template <int STAGE>
+template <int STAGE, int MI, int NJ>
 __global__ __launch_bounds__(256) void proj_gemm(const bf16_t* x, int64_t x_tstride,
                                                  const bf16_t* w, bf16_t* y, int64_t y_tstride,
                                                  int T, int N, int K, int G) {
-  __shared__ __attribute__((aligned(16))) bf16_t sa[2][kGmTile * kGmPitch];  // tokens x k
-  __shared__ __attribute__((aligned(16))) bf16_t sb[2][kGmTile * kGmPitch];  // weight rows x k
-  const int nt = N / kGmTile, tt = (T + kGmTile - 1) / kGmTile;
+  constexpr int TT = 64 * MI, TR = 64 * NJ;  // workgroup tile: tokens x weight rows
+  constexpr int CA = TT * 8 / 256, CB = TR * 8 / 256;  // 16-byte chunks per thread and step
+  __shared__ __attribute__((aligned(16))) bf16_t sa[2][TT * kGmPitch];  // tokens x k
+  __shared__ __attribute__((aligned(16))) bf16_t sb[2][TR * kGmPitch];  // weight rows x k
+  const int nt = N / TR, tt = (T + TT - 1) / TT;
   const int total = nt * tt * G, per = (total + 7) / 8;
   const int logical = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
   if (logical >= total) return;  // padding of the last XCD's range (whole workgroup)
@@ -125,30 +133,53 @@ __global__ __launch_bounds__(256) void proj_gemm(const bf16_t* x, int64_t x_tstr
   const int first_t = band * kGmSwizzle;
   const int rows_t = min(tt - first_t, kGmSwizzle);
   const int in_band = rest - band * kGmSwizzle * nt;
-  const int t0 = (first_t + in_band % rows_t) * kGmTile;
-  const int n0 = (in_band / rows_t) * kGmTile;
+  const int t0 = (first_t + in_band % rows_t) * TT;
+  const int n0 = (in_band / rows_t) * TR;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  // copy role: thread tid moves row tid / 2, channels 32 (tid & 1) .. + 31 of
-  // both tiles (tokens past T re-read token T - 1; never stored)
-  const int lr = tid >> 1, lk = (tid & 1) * 32;
-  const bf16_t* xa = x + (int64_t)min(t0 + lr, T - 1) * x_tstride + (int64_t)g * K + lk;
-  const bf16_t* wr = w + ((int64_t)g * N + n0 + lr) * K + lk;
-  // staging registers of one step's copy (named: arrays here went to scratch)
-  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+  // copy role: chunk q = tid + 256 i of a tile is row q / 8, channels
+  // 8 (q % 8) .. + 7 of the step (one 128-byte row segment per 8 threads).
+  // Addresses are a uniform base per chunk plus one 32-bit lane offset per
+  // operand (the global loads' scalar-base form: two address registers in
+  // all).  Tokens past T re-read token T - 1 and are never stored; the
+  // 256 x 256 instance runs only where T divides into its tiles.
+  const int ck = (tid & 7) * 8;
+  const int rc = tid >> 3;
+  const uint32_t la = (uint32_t)(((int64_t)rc * x_tstride + ck) * 2);
+  const uint32_t lb = (uint32_t)(((int64_t)rc * K + ck) * 2);
+  const char* xbase = reinterpret_cast<const char*>(x + (int64_t)t0 * x_tstride + (int64_t)g * K);
+  const char* wbase = reinterpret_cast<const char*>(w + ((int64_t)g * N + n0) * K);
+  u32x4_t ra[CA], rb[CB];
   auto fetch = [&](int k0) {
-    const uint4* pa = reinterpret_cast<const uint4*>(xa + k0);
-    const uint4* pb = reinterpret_cast<const uint4*>(wr + k0);
-    ra0 = pa[0]; ra1 = pa[1]; ra2 = pa[2]; ra3 = pa[3];
-    rb0 = pb[0]; rb1 = pb[1]; rb2 = pb[2]; rb3 = pb[3];
+    if constexpr (MI == 2) {
+      // the 128-tile instance serves ragged token counts: clamped rows
+#pragma unroll
+      for (int i = 0; i < CA; ++i)
+        ra[i] = *reinterpret_cast<const u32x4_t*>(
+            x + (int64_t)min(t0 + rc + 32 * i, T - 1) * x_tstride + (int64_t)g * K + ck + k0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < CA; ++i)
+        ra[i] = *reinterpret_cast<const u32x4_t*>(xbase + (int64_t)32 * i * x_tstride * 2 +
+                                                  (int64_t)k0 * 2 + la);
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+      rb[i] = *reinterpret_cast<const u32x4_t*>(wbase + (int64_t)32 * i * K * 2 + (int64_t)k0 * 2 + lb);
   };
   auto stash = [&](int buf) {
-    uint4* qa = reinterpret_cast<uint4*>(&sa[buf][lr * kGmPitch + lk]);
-    uint4* qb = reinterpret_cast<uint4*>(&sb[buf][lr * kGmPitch + lk]);
-    qa[0] = ra0; qa[1] = ra1; qa[2] = ra2; qa[3] = ra3;
-    qb[0] = rb0; qb[1] = rb1; qb[2] = rb2; qb[3] = rb3;
+#pragma unroll
+    for (int i = 0; i < CA; ++i)
+      *reinterpret_cast<u32x4_t*>(&sa[buf][((tid >> 3) + 32 * i) * kGmPitch + ck]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+      *reinterpret_cast<u32x4_t*>(&sb[buf][((tid >> 3) + 32 * i) * kGmPitch + ck]) = rb[i];
   };
-  f32x16_t c00 = {}, c01 = {}, c10 = {}, c11 = {};
+  f32x16_t c[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) c[i][j] = f32x16_t{};
   const int nk = K / kGmK;
   fetch(0);
   stash(0);
@@ -161,33 +192,36 @@ __global__ __launch_bounds__(256) void proj_gemm(const bf16_t* x, int64_t x_tstr
     fetch(min(kt + 1, nk - 1) * kGmK);
 #pragma unroll
     for (int ks = 0; ks < kGmK / 16; ++ks) {
-      const bf16_t* pa = &sa[buf][(wm * 64 + ar) * kGmPitch + ks * 16 + ah];
-      const bf16_t* pb = &sb[buf][(wn * 64 + ar) * kGmPitch + ks * 16 + ah];
-      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(pa);
-      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(pa + 32 * kGmPitch);
-      const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(pb);
-      const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(pb + 32 * kGmPitch);
-      c00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, c00, 0, 0, 0);
-      c01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, c01, 0, 0, 0);
-      c10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, c10, 0, 0, 0);
-      c11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, c11, 0, 0, 0);
+      const bf16_t* pa = &sa[buf][(wm * 32 * MI + ar) * kGmPitch + ks * 16 + ah];
+      const bf16_t* pb = &sb[buf][(wn * 32 * NJ + ar) * kGmPitch + ks * 16 + ah];
+      bf16x8_t av[MI], bv[NJ];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) av[i] = *reinterpret_cast<const bf16x8_t*>(pa + 32 * i * kGmPitch);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bv[j] = *reinterpret_cast<const bf16x8_t*>(pb + 32 * j * kGmPitch);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], c[i][j], 0, 0, 0);
     }
     // the other buffer was last read in the previous step, before its barrier
     stash(buf ^ 1);
     __syncthreads();
   }
-  auto store = [&](const f32x16_t& c, int i, int j) {
-    const int n = n0 + wn * 64 + j * 32 + ar;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int t = t0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-      if (t < T) y[(int64_t)t * y_tstride + (int64_t)g * N + n] = (bf16_t)f32_to_bf16(c[e]);
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int n = n0 + wn * 32 * NJ + j * 32 + ar;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int t = t0 + wm * 32 * MI + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        // the 256-tile instance runs only where T fills its tiles
+        if (MI != 2 || t < T)
+          y[(int64_t)t * y_tstride + (int64_t)g * N + n] = (bf16_t)f32_to_bf16(c[i][j][e]);
+      }
     }
-  };
-  store(c00, 0, 0);
-  store(c01, 0, 1);
-  store(c10, 1, 0);
-  store(c11, 1, 1);
 }
 
 bool out_proj_supported(const OprojArgs& a) {
@@ -203,21 +237,29 @@ bool out_proj_supported(const OprojArgs& a) {
 hipError_t launch_out_proj(const OprojArgs& a, hipStream_t stream) {
   const int ka = (a.H / a.G) * a.D, kb = a.G * a.r;
   if (a.T > kOprojMaxTokens) {
-    const int64_t tt = (a.T + kGmTile - 1) / kGmTile;
     // grids padded to 8 equal XCD ranges (the kernel maps and drops the rest)
-    auto grid = [&](int N, int G) {
-      const int64_t total = (int64_t)(N / kGmTile) * tt * G;
+    auto grid = [&](int N, int G, int TT, int TR) {
+      const int64_t total = (int64_t)(N / TR) * ((a.T + TT - 1) / TT) * G;
       return dim3((unsigned)(8 * ((total + 7) / 8)));
     };
-    hipLaunchKernelGGL(proj_gemm<0>, grid(a.r, a.G), dim3(256), 0, stream, (const bf16_t*)a.o,
-                       (int64_t)a.H * a.D, (const bf16_t*)a.w_a, (bf16_t*)a.mid, (int64_t)kb,
-                       a.T, a.r, ka, a.G);
-    hipError_t e = hipGetLastError();
+    // 256 x 256 tiles where the weight rows divide into them, else 128 x 128
+    auto run = [&](auto stage, const bf16_t* x, int64_t xs, const bf16_t* w, bf16_t* y,
+                   int64_t ys, int N, int K, int G) {
+      constexpr int S = decltype(stage)::value;
+      if (N % 256 == 0 && a.T % 256 == 0 && (int64_t)31 * xs + K < (1LL << 30) &&
+          (int64_t)31 * K + K < (1LL << 30))
+        hipLaunchKernelGGL((proj_gemm<S, 4, 4>), grid(N, G, 256, 256), dim3(256), 0, stream, x, xs,
+                           w, y, ys, a.T, N, K, G);
+      else
+        hipLaunchKernelGGL((proj_gemm<S, 2, 2>), grid(N, G, 128, 128), dim3(256), 0, stream, x, xs,
+                           w, y, ys, a.T, N, K, G);
+      return hipGetLastError();
+    };
+    hipError_t e = run(std::integral_constant<int, 0>{}, (const bf16_t*)a.o, (int64_t)a.H * a.D,
+                       (const bf16_t*)a.w_a, (bf16_t*)a.mid, (int64_t)kb, a.r, ka, a.G);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(proj_gemm<1>, grid(a.d, 1), dim3(256), 0, stream, (const bf16_t*)a.mid,
-                       (int64_t)kb, (const bf16_t*)a.w_b, (bf16_t*)a.out, (int64_t)a.d, a.T,
-                       a.d, kb, 1);
-    return hipGetLastError();
+    return run(std::integral_constant<int, 1>{}, (const bf16_t*)a.mid, (int64_t)kb,
+               (const bf16_t*)a.w_b, (bf16_t*)a.out, (int64_t)a.d, a.d, kb, 1);
   }
   // o [T, H, D] seen as [T, G, ka] (a group's heads are consecutive)
   hipLaunchKernelGGL(proj_rows<4>, dim3(a.r / kPjRows, a.G), dim3(256), 0, stream,

@@ -76,9 +76,13 @@ def test_output_proj_tokens_do_not_mix():
     assert torch.equal(a[keep], b[keep]) and not torch.equal(a[2], b[2])
 
 
-@pytest.mark.parametrize("T,tokens", [(40, None), (4096, [0, 1, 127, 128, 2049, 4095])])
+@pytest.mark.parametrize("T,tokens", [(40, None),
+                                      (4096, [0, 1, 37, 70, 127, 128, 200, 255, 256, 2049, 3333,
+                                              4095])])
 def test_output_proj_many_tokens_flash_shape(T, tokens):
-    """More than 16 tokens take the tiled GEMM (prefill chunks)."""
+    """More than 16 tokens take the tiled GEMM (prefill chunks); at 4,096
+    tokens the 256 x 256 tiles, sampled in every 32-token block of a tile
+    and in both halves of its waves' token range."""
     _case(T, 64, 512, 8, 1024, 4096, seed=T, tokens=tokens)
 
 
