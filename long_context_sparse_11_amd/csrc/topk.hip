@@ -107,10 +107,13 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t x, uint32_t& total, 
 // workgroup per compute unit, 101 us at two); what that spills costs a
 // latency-bound decode select ~0.4 us, so few segments keep the unconstrained
 // instance.
-template <bool CAND, bool WIDE>
+// RND: keys per thread (the segment's capacity is kTkThreads * RND); the
+// merge of at most 8,192 chunk winners takes 8, so every wave holds keys.
+template <bool CAND, bool WIDE, int RND = kTkRounds>
 __global__ __launch_bounds__(kTkThreads)
 __attribute__((amdgpu_waves_per_eu(WIDE ? 8 : 1, WIDE ? 8 : 4)))
 void topk_kernel(TopkArgs a) {
+  static_assert(RND % 4 == 0 && RND <= kTkRounds, "keys per thread");
   __shared__ TkShared S;
   const int seg = blockIdx.x;
   const int tid = threadIdx.x;
@@ -151,28 +154,28 @@ void topk_kernel(TopkArgs a) {
   }
 
   // ---- keys in registers; every load issued before any is consumed
-  uint32_t key[kTkRounds];
-  int32_t vi[CAND ? kTkRounds : 1];  // candidate indices (mode 2)
-  const int e0 = tid * kTkRounds;
-  float v[kTkRounds];
+  uint32_t key[RND];
+  int32_t vi[CAND ? RND : 1];  // candidate indices (mode 2)
+  const int e0 = tid * RND;
+  float v[RND];
   {
-    const bool vec = ((((uintptr_t)src) | ((uintptr_t)src_idx)) & 15) == 0 && e0 + kTkRounds <= cap;
+    const bool vec = ((((uintptr_t)src) | ((uintptr_t)src_idx)) & 15) == 0 && e0 + RND <= cap;
     if (vec) {
 #pragma unroll
-      for (int u = 0; u < kTkRounds / 4; ++u) {
+      for (int u = 0; u < RND / 4; ++u) {
         const f32x4_t x = reinterpret_cast<const f32x4_t*>(src + e0)[u];
         v[4 * u] = x[0]; v[4 * u + 1] = x[1]; v[4 * u + 2] = x[2]; v[4 * u + 3] = x[3];
       }
       if constexpr (CAND) {
 #pragma unroll
-        for (int u = 0; u < kTkRounds / 4; ++u) {
+        for (int u = 0; u < RND / 4; ++u) {
           const int4 x = reinterpret_cast<const int4*>(src_idx + e0)[u];
           vi[4 * u] = x.x; vi[4 * u + 1] = x.y; vi[4 * u + 2] = x.z; vi[4 * u + 3] = x.w;
         }
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < kTkRounds; ++i) {
+      for (int i = 0; i < RND; ++i) {
         const int e = min(e0 + i, cap - 1);
         v[i] = src[e];
         if constexpr (CAND) vi[i] = src_idx[e];
@@ -200,7 +203,7 @@ void topk_kernel(TopkArgs a) {
   // a slot beyond n, or an empty candidate slot (index -1), takes no part
   uint32_t live = 0;  // bit i: slot i holds a key
 #pragma unroll
-  for (int i = 0; i < kTkRounds; ++i) {
+  for (int i = 0; i < RND; ++i) {
     key[i] = score_key(v[i]);
     if (e0 + i < n && (!CAND || vi[CAND ? i : 0] >= 0)) live |= 1u << i;
   }
@@ -221,7 +224,7 @@ void topk_kernel(TopkArgs a) {
     for (;;) {
       uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
-      for (int i = 0; i < kTkRounds; ++i) {
+      for (int i = 0; i < RND; ++i) {
         if (((act >> i) & 1) && (key[i] & mask) == prefix) {
           mn = min(mn, key[i]);
           mx = max(mx, key[i]);
@@ -241,7 +244,7 @@ void topk_kernel(TopkArgs a) {
       const int shift = max(hb + 1 - kDigitBits, 0);
       const uint32_t dmask = (1u << (hb + 1 - shift)) - 1u;
 #pragma unroll
-      for (int i = 0; i < kTkRounds; ++i) {
+      for (int i = 0; i < RND; ++i) {
         if (((act >> i) & 1) && (key[i] & mask) == prefix)
           atomicAdd(&S.hist[(key[i] >> shift) & dmask], 1u);
       }
@@ -282,7 +285,7 @@ void topk_kernel(TopkArgs a) {
   // first digit
   uint32_t kmn = 0xffffffffu, kmx = 0u;
 #pragma unroll
-  for (int i = 0; i < kTkRounds; ++i) {
+  for (int i = 0; i < RND; ++i) {
     if ((live >> i) & 1) {
       kmn = min(kmn, key[i]);
       kmx = max(kmx, key[i]);
@@ -348,10 +351,10 @@ void topk_kernel(TopkArgs a) {
       // instance keep the branch per slot: without it they measured slower
       // (the 1M merge by ~5 us, a prefill chunk's selects by ~45 us).
 #pragma unroll
-      for (int i = 0; i < kTkRounds; ++i) atomicAdd(&S.hist[digit(i)], (live >> i) & 1u);
+      for (int i = 0; i < RND; ++i) atomicAdd(&S.hist[digit(i)], (live >> i) & 1u);
     } else {
 #pragma unroll
-      for (int i = 0; i < kTkRounds; ++i) {
+      for (int i = 0; i < RND; ++i) {
         if ((live >> i) & 1) atomicAdd(&S.hist[digit(i)], 1u);
       }
     }
@@ -381,7 +384,7 @@ void topk_kernel(TopkArgs a) {
     remaining = K - (int)S.sel_above;
     in_bin = 0;
 #pragma unroll
-    for (int i = 0; i < kTkRounds; ++i) {
+    for (int i = 0; i < RND; ++i) {
       const bool v = (live >> i) & 1;
       const uint32_t d = digit(i);
       above_m |= (v && d > d1) ? (1u << i) : 0u;
@@ -401,7 +404,7 @@ void topk_kernel(TopkArgs a) {
       if (lane == 63) base = atomicAdd(&S.fill, incl);
       uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)base, 63) + incl - mine;
 #pragma unroll
-      for (int i = 0; i < kTkRounds; ++i) {
+      for (int i = 0; i < RND; ++i) {
         if ((in_bin >> i) & 1) S.bin[pos++] = key[i];
       }
       __syncthreads();
@@ -509,7 +512,7 @@ void topk_kernel(TopkArgs a) {
   // of the output, starting after everything chosen by lower threads.
   uint32_t gt_m = above_m, eq_m = 0;
 #pragma unroll
-  for (int i = 0; i < kTkRounds; ++i) {
+  for (int i = 0; i < RND; ++i) {
     const bool v = (in_bin >> i) & 1;
     const uint32_t k = key[i] & mask;
     gt_m |= (v && k > prefix) ? (1u << i) : 0u;
@@ -531,7 +534,7 @@ void topk_kernel(TopkArgs a) {
   // coalesced; the two-per-CU instance stores each pair where it is chosen
   // (the staging's registers cost it spills)
 #pragma unroll
-  for (int i = 0; i < kTkRounds; ++i) {
+  for (int i = 0; i < RND; ++i) {
     const bool g = (gt_m >> i) & 1, e = (eq_m >> i) & 1;
     const bool c = g || (e && seen_eq < take);
     seen_eq += e ? 1u : 0u;
@@ -562,7 +565,10 @@ constexpr int kTkWideSegments = 1024;
 
 hipError_t launch_topk(const TopkArgs& a, int segments, hipStream_t stream) {
   if (segments == 0) return hipSuccess;
-  if (a.mode == 2)
+  if (a.mode == 2 && (int64_t)a.nchunks * a.K <= kTkThreads * (kTkRounds / 2))
+    hipLaunchKernelGGL((topk_kernel<true, false, kTkRounds / 2>), dim3(segments), dim3(kTkThreads), 0,
+                       stream, a);
+  else if (a.mode == 2)
     hipLaunchKernelGGL((topk_kernel<true, false>), dim3(segments), dim3(kTkThreads), 0, stream, a);
   else if (segments >= kTkWideSegments)
     hipLaunchKernelGGL((topk_kernel<false, true>), dim3(segments), dim3(kTkThreads), 0, stream, a);
