@@ -340,12 +340,15 @@ def test_index_heavy_tail_two_level_select():
                  SCORE_ATOL_BF16)
 
 
+@pytest.mark.parametrize("N", [3000, 40000])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_index_all_zero_scores_take_lowest_indices(dt):
-    """Every dot negative -> every score 0 -> ties -> the K lowest indices."""
+def test_index_all_zero_scores_take_lowest_indices(dt, N):
+    """Every dot negative -> every score 0 -> ties -> the K lowest indices;
+    at 40,000 entries through the chunk selects and the merge of their
+    1,536 winners (ties resolved in index order across chunks)."""
     rng = np.random.default_rng(3)
     Hi, Di = (64, 128) if dt == "bf16" else (4, 32)
-    N, K = 3000, 512
+    K = 512
     q = np.abs(rng.standard_normal((1, 1, Hi, Di))).astype(np.float32)
     k = -np.abs(rng.standard_normal((1, N, Di))).astype(np.float32)
     w = rng.standard_normal((1, 1, Hi)).astype(np.float32)   # mixed signs: -0 and +0 scores
